@@ -1,0 +1,133 @@
+"""Seeded synthetic inputs for GEMM tests and benchmarks.
+
+This module holds no GEMM arithmetic.  It only draws matrices, and both the
+GPU path's tests and the CPU oracle's tests take their inputs from it.
+
+Generator: a counter-based stream built on the SplitMix64 output function
+(Steele, Lea and Flood, "Fast splittable pseudorandom number generators",
+OOPSLA 2014; the 64-bit finaliser with shifts 30, 27, 31 and multipliers
+0xBF58476D1CE4E5B9, 0x94D049BB133111EB, stepping by the golden-ratio
+increment 0x9E3779B97F4A7C15).
+
+* ``splitmix64(state, n)`` is the plain sequential generator: it adds the
+  increment to the state and returns the finalised state, n times.
+* A matrix stream ``(seed, stream)`` has key
+  ``k = mix64((seed ^ (stream << 56)) + GAMMA)``: the first SplitMix64 output
+  from that state.  Element ``t`` of the stream (flat row-major index of the
+  packed matrix) is ``u_t = mix64(k + (t + 1) * GAMMA)``, so any element can
+  be regenerated on its own.
+* ``uniform[-1, 1)``: ``(u_t >> 40) * 2**-23 - 1``, a 24-bit grid value that
+  is exact in FP32.  FP16 inputs are the round-to-nearest-even FP16 value of
+  that FP32 number (numpy's ``astype(np.float16)``).
+
+Streams: A uses stream 0 and B stream 1.  The workloads draw i.i.d.
+uniform[-1, 1) entries from seed 0, the synthetic square and rectangular
+random matrices the GEMM articles time (4096^3 and 2048^3 FP32).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+MASK64 = (1 << 64) - 1
+GAMMA = 0x9E3779B97F4A7C15
+_C1 = 0xBF58476D1CE4E5B9
+_C2 = 0x94D049BB133111EB
+
+STREAM_A = 0
+STREAM_B = 1
+
+
+def mix64_int(z: int) -> int:
+    """SplitMix64 finaliser on a Python int (mod 2**64)."""
+    z &= MASK64
+    z = ((z ^ (z >> 30)) * _C1) & MASK64
+    z = ((z ^ (z >> 27)) * _C2) & MASK64
+    return z ^ (z >> 31)
+
+
+def mix64(z: np.ndarray) -> np.ndarray:
+    """SplitMix64 finaliser, element-wise on a uint64 array (wrapping).
+    Works in place on a private copy."""
+    z = np.array(z, dtype=np.uint64, copy=True)
+    tmp = np.empty_like(z)
+    with np.errstate(over="ignore"):
+        for shift, mul in ((30, _C1), (27, _C2)):
+            np.right_shift(z, np.uint64(shift), out=tmp)
+            np.bitwise_xor(z, tmp, out=z)
+            np.multiply(z, np.uint64(mul), out=z)
+        np.right_shift(z, np.uint64(31), out=tmp)
+        np.bitwise_xor(z, tmp, out=z)
+    return z
+
+
+def splitmix64(state: int, n: int) -> list[int]:
+    """The sequential generator: n outputs starting from ``state``."""
+    out = []
+    for _ in range(n):
+        state = (state + GAMMA) & MASK64
+        out.append(mix64_int(state))
+    return out
+
+
+def stream_key(seed: int, stream: int) -> int:
+    return mix64_int(((seed ^ (stream << 56)) + GAMMA) & MASK64)
+
+
+def stream_u64(seed: int, stream: int, count: int, start: int = 0) -> np.ndarray:
+    """Raw 64-bit draws ``u_t`` for t = start .. start + count - 1."""
+    key = np.uint64(stream_key(seed, stream))
+    t = np.arange(start + 1, start + count + 1, dtype=np.uint64)
+    with np.errstate(over="ignore"):
+        np.multiply(t, np.uint64(GAMMA), out=t)
+        np.add(t, key, out=t)
+    return mix64(t)
+
+
+def u64_to_uniform(u: np.ndarray) -> np.ndarray:
+    """Map draws to the 24-bit grid in [-1, 1 - 2**-23] (float32, exact)."""
+    top = (np.asarray(u, dtype=np.uint64) >> np.uint64(40)).astype(np.float64)
+    return (top * 2.0 ** -23 - 1.0).astype(np.float32)
+
+
+def uniform_f32(seed: int, stream: int, rows: int, cols: int) -> np.ndarray:
+    """rows x cols float32 matrix, i.i.d. uniform[-1, 1) on a 2**-23 grid."""
+    n = rows * cols
+    if n == 0:
+        return np.zeros((rows, cols), dtype=np.float32)
+    return u64_to_uniform(stream_u64(seed, stream, n)).reshape(rows, cols)
+
+
+def uniform_f16(seed: int, stream: int, rows: int, cols: int) -> np.ndarray:
+    """The FP32 matrix of :func:`uniform_f32` rounded to FP16 (RNE)."""
+    return uniform_f32(seed, stream, rows, cols).astype(np.float16)
+
+
+def small_int(seed: int, stream: int, rows: int, cols: int, lo: int = -2,
+              hi: int = 2, dtype=np.float32) -> np.ndarray:
+    """Integers in [lo, hi] (as ``dtype``): with |a|, |b| <= 2 and K <= 512
+    every partial sum of a GEMM is an integer below 2**11, exact in FP32 and
+    FP16, so the product has one correct answer."""
+    n = rows * cols
+    if n == 0:
+        return np.zeros((rows, cols), dtype=dtype)
+    u = stream_u64(seed, stream, n) >> np.uint64(32)
+    span = np.uint64(hi - lo + 1)
+    v = ((u * span) >> np.uint64(32)).astype(np.int64) + lo
+    return v.reshape(rows, cols).astype(dtype)
+
+
+def permutation(seed: int, stream: int, n: int) -> np.ndarray:
+    """A permutation of 0..n-1: the order that sorts n stream draws."""
+    if n == 0:
+        return np.zeros(0, dtype=np.int64)
+    return np.argsort(stream_u64(seed, stream, n), kind="stable").astype(np.int64)
+
+
+def workload(M: int, N: int, K: int, dtype: str, seed: int = 0):
+    """The benchmark and parity inputs: A (M x K) and B (K x N), packed
+    row-major, i.i.d. uniform[-1, 1) from ``seed`` (A stream 0, B stream 1)."""
+    if dtype == "f32":
+        return (uniform_f32(seed, STREAM_A, M, K), uniform_f32(seed, STREAM_B, K, N))
+    if dtype == "f16":
+        return (uniform_f16(seed, STREAM_A, M, K), uniform_f16(seed, STREAM_B, K, N))
+    raise ValueError(f"unknown dtype {dtype!r}")

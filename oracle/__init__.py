@@ -1,0 +1,231 @@
+"""CPU oracle for dense row-major GEMM (FP64 accumulation).
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, ``__graft_entry__.smoke()``
+and the CPU-baseline leg of ``bench.py`` may import this package.  The GPU
+library never imports it and shares no code with it.
+
+The arithmetic lives in ``oracle.c`` (plain C, built with gcc, no HIP
+header).  This module only builds that file, loads it with ctypes and
+marshals numpy arrays:
+
+* :func:`gemm_rows` -- rows of ``C_ref = A @ B`` and of ``D = |A| @ |B|``,
+  accumulated in double over k ascending (the naive kernel's per-output K
+  loop in "sgemm - beyond cuBLAS", section 1, and the one-thread-per-output
+  kernel in "GEMM: from naive to shared memory tiling and register
+  blocking", section 1).
+* :func:`gemm_entries` -- the same quantities for single (i, j) pairs.
+* :func:`check` -- ``max_ij |C_gpu - C_ref| / D`` plus counts.
+* :func:`f16_to_f64` -- exact IEEE binary16 decoding.
+
+Parity status: pinned (see the oracle tests in ``tests/``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+# No -ffast-math: the summation order is the definition's, k ascending.
+CFLAGS = ["-O3", "-std=c11", "-fPIC", "-shared", "-pthread",
+          "-fno-fast-math", "-ffp-contract=off", "-Wall", "-Wextra"]
+
+_lock = threading.Lock()
+_lib = None
+
+SGEMM_TOL = 1e-5
+HGEMM_TOL = 2e-3
+
+
+def build(src: str = _SRC, out: str = _LIB, extra_flags=()) -> str:
+    """Compile ``src`` into the shared library ``out`` with gcc."""
+    cmd = ["gcc", *CFLAGS, *extra_flags, src, "-o", out + ".tmp", "-lm"]
+    subprocess.run(cmd, check=True, capture_output=True, text=True)
+    os.replace(out + ".tmp", out)
+    return out
+
+
+def _declare(lib):
+    i64, p = ctypes.c_int64, ctypes.c_void_p
+    lib.oracle_version.restype = ctypes.c_int
+    lib.oracle_f16_to_f64.argtypes = [ctypes.c_uint16]
+    lib.oracle_f16_to_f64.restype = ctypes.c_double
+    lib.oracle_f16_array_to_f64.argtypes = [p, p, i64]
+    lib.oracle_f16_array_to_f64.restype = None
+    for name in ("oracle_gemm_rows_f32", "oracle_gemm_rows_f16"):
+        fn = getattr(lib, name)
+        fn.argtypes = [i64, i64, i64, p, i64, p, i64, p, p, i64, p, i64, ctypes.c_int]
+        fn.restype = ctypes.c_int
+    for name in ("oracle_gemm_entries_f32", "oracle_gemm_entries_f16"):
+        fn = getattr(lib, name)
+        fn.argtypes = [i64, p, i64, p, i64, p, p, i64, p, p]
+        fn.restype = ctypes.c_int
+    for name in ("oracle_check_f32", "oracle_check_f16"):
+        fn = getattr(lib, name)
+        fn.argtypes = [i64, i64, p, i64, p, i64, p, i64, ctypes.c_double, p, p]
+        fn.restype = None
+    return lib
+
+
+def load(path: str | None = None):
+    """Load (building first if needed) the oracle library.  With ``path``,
+    load that file instead (used by the tests' planted-mistake builds)."""
+    global _lib
+    if path is not None:
+        return _declare(ctypes.CDLL(path))
+    with _lock:
+        if _lib is None:
+            if (not os.path.exists(_LIB)
+                    or os.path.getmtime(_LIB) < os.path.getmtime(_SRC)):
+                build()
+            _lib = _declare(ctypes.CDLL(_LIB))
+    return _lib
+
+
+def default_threads() -> int:
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def _ptr(a: np.ndarray) -> int:
+    return a.ctypes.data
+
+
+def _as_matrix(x: np.ndarray, dtype) -> tuple[np.ndarray, int]:
+    """Return (array, leading dimension in elements).  Row-major views with
+    unit column stride keep their row stride; anything else is copied."""
+    if x.ndim != 2:
+        raise ValueError("expected a 2-D array")
+    if x.dtype != dtype:
+        raise TypeError(f"expected dtype {np.dtype(dtype)}, got {x.dtype}")
+    item = x.dtype.itemsize
+    if x.strides[1] != item or x.strides[0] % item or x.strides[0] < x.shape[1] * item:
+        x = np.ascontiguousarray(x)
+    ld = x.strides[0] // item if x.shape[0] > 0 else max(1, x.shape[1])
+    return x, max(ld, 1)
+
+
+def _kind(a: np.ndarray) -> str:
+    if a.dtype == np.float32:
+        return "f32"
+    if a.dtype == np.float16 or a.dtype == np.uint16:
+        return "f16"
+    raise TypeError(f"unsupported dtype {a.dtype}")
+
+
+def _bits16(a: np.ndarray) -> np.ndarray:
+    return a.view(np.uint16) if a.dtype == np.float16 else a
+
+
+def gemm_rows(A: np.ndarray, B: np.ndarray, rows=None, threads: int | None = None,
+              lib=None):
+    """C_ref and D (both float64) for the rows ``rows`` of C (all rows when
+    None).  A is M x K, B is K x N; float32, or float16 (or uint16 binary16
+    bit patterns)."""
+    lib = lib or load()
+    kind = _kind(A)
+    if _kind(B) != kind:
+        raise TypeError("A and B must have the same element type")
+    dt = np.float32 if kind == "f32" else np.uint16
+    if kind == "f16":
+        A, B = _bits16(A), _bits16(B)
+    A, lda = _as_matrix(A, dt)
+    B, ldb = _as_matrix(B, dt)
+    M, K = A.shape
+    K2, N = B.shape
+    if K2 != K:
+        raise ValueError(f"inner dimensions differ: {K} vs {K2}")
+    if rows is None:
+        nrows, rows_arr, rp = M, None, None
+    else:
+        rows_arr = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        if rows_arr.size and (rows_arr.min() < 0 or rows_arr.max() >= M):
+            raise IndexError("row index out of range")
+        nrows, rp = rows_arr.size, _ptr(rows_arr)
+    C = np.zeros((nrows, N), dtype=np.float64)
+    D = np.zeros((nrows, N), dtype=np.float64)
+    if nrows == 0 or N == 0:
+        return C, D
+    fn = lib.oracle_gemm_rows_f32 if kind == "f32" else lib.oracle_gemm_rows_f16
+    # A dummy one-element buffer stands in for A or B when K == 0.
+    a_ptr = _ptr(A) if A.size else _ptr(np.zeros(1, dt))
+    b_ptr = _ptr(B) if B.size else _ptr(np.zeros(1, dt))
+    rc = fn(nrows, N, K, a_ptr, lda, b_ptr, ldb, rp, _ptr(C), N, _ptr(D), N,
+            int(threads or default_threads()))
+    if rc != 0:
+        raise RuntimeError(f"oracle_gemm_rows failed with code {rc}")
+    return C, D
+
+
+def gemm_entries(A: np.ndarray, B: np.ndarray, ii, jj, lib=None):
+    """C_ref[ii[t], jj[t]] and D[ii[t], jj[t]] as float64 vectors."""
+    lib = lib or load()
+    kind = _kind(A)
+    dt = np.float32 if kind == "f32" else np.uint16
+    if kind == "f16":
+        A, B = _bits16(A), _bits16(B)
+    A, lda = _as_matrix(A, dt)
+    B, ldb = _as_matrix(B, dt)
+    M, K = A.shape
+    N = B.shape[1]
+    ii = np.ascontiguousarray(np.asarray(ii, dtype=np.int64))
+    jj = np.ascontiguousarray(np.asarray(jj, dtype=np.int64))
+    if ii.shape != jj.shape:
+        raise ValueError("ii and jj differ in length")
+    if ii.size and (ii.min() < 0 or ii.max() >= M or jj.min() < 0 or jj.max() >= N):
+        raise IndexError("entry index out of range")
+    c = np.zeros(ii.size, dtype=np.float64)
+    d = np.zeros(ii.size, dtype=np.float64)
+    if ii.size == 0:
+        return c, d
+    fn = lib.oracle_gemm_entries_f32 if kind == "f32" else lib.oracle_gemm_entries_f16
+    a_ptr = _ptr(A) if A.size else _ptr(np.zeros(1, dt))
+    b_ptr = _ptr(B) if B.size else _ptr(np.zeros(1, dt))
+    rc = fn(K, a_ptr, lda, b_ptr, ldb, _ptr(ii), _ptr(jj), ii.size, _ptr(c), _ptr(d))
+    if rc != 0:
+        raise RuntimeError(f"oracle_gemm_entries failed with code {rc}")
+    return c, d
+
+
+def check(C_gpu: np.ndarray, C_ref: np.ndarray, D: np.ndarray, tol: float,
+          lib=None) -> dict:
+    """Element-wise error ratio |C_gpu - C_ref| / D, maximised.  C_gpu is
+    float32 or float16 / uint16 bit patterns (judged after FP16 rounding)."""
+    lib = lib or load()
+    kind = _kind(C_gpu)
+    dt = np.float32 if kind == "f32" else np.uint16
+    if kind == "f16":
+        C_gpu = _bits16(C_gpu)
+    C_gpu, ldc = _as_matrix(C_gpu, dt)
+    R, ldr = _as_matrix(np.asarray(C_ref, dtype=np.float64), np.float64)
+    Dm, ldd = _as_matrix(np.asarray(D, dtype=np.float64), np.float64)
+    M, N = C_gpu.shape
+    if R.shape != (M, N) or Dm.shape != (M, N):
+        raise ValueError("shape mismatch between C_gpu, C_ref and D")
+    out = np.zeros(4, dtype=np.float64)
+    cnt = np.zeros(2, dtype=np.int64)
+    if M and N:
+        fn = lib.oracle_check_f32 if kind == "f32" else lib.oracle_check_f16
+        fn(M, N, _ptr(C_gpu), ldc, _ptr(R), ldr, _ptr(Dm), ldd, float(tol),
+           _ptr(out), _ptr(cnt))
+    return {"max_rel": float(out[0]), "max_abs": float(out[1]),
+            "worst": (int(out[2]), int(out[3])), "n_bad": int(cnt[0]),
+            "n_nonfinite": int(cnt[1]), "tol": float(tol),
+            "ok": bool(cnt[0] == 0 and cnt[1] == 0)}
+
+
+def f16_to_f64(bits) -> np.ndarray:
+    """Exact decode of binary16 bit patterns (uint16 or float16 array)."""
+    lib = load()
+    b = np.ascontiguousarray(_bits16(np.asarray(bits)).astype(np.uint16, copy=False))
+    out = np.empty(b.shape, dtype=np.float64)
+    if b.size:
+        lib.oracle_f16_array_to_f64(_ptr(b), _ptr(out), b.size)
+    return out

@@ -1,0 +1,305 @@
+/*
+ * CPU oracle for dense row-major GEMM, C[M x N] = A[M x K] * B[K x N].
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the slow, obviously correct
+ * reference that the GPU library is checked against.  Only the test suite,
+ * the smoke check and the benchmark's CPU-baseline leg may load it.  It
+ * shares no code, header, table or helper with the GPU library and includes
+ * no HIP header.
+ *
+ * What it computes (plain definition, no blocking, no reordering):
+ *   C_ref[i][j] = sum_{k=0}^{K-1} A[i][k] * B[k][j]          (k ascending)
+ *   D[i][j]     = sum_{k=0}^{K-1} |A[i][k]| * |B[k][j]|      (error scale)
+ * Sources: the row-major problem statement C = A x B with 2MNK flops in
+ * "GEMM: from naive to shared memory tiling and register blocking"
+ * (quant67.com, introduction and section 1, the one-thread-per-output
+ * kernel); the per-element K loop of the naive kernel in "sgemm - beyond
+ * cuBLAS" (wingedge777.com, section 1); the 2MNK operation count in the
+ * lqnn.cn SGEMM article (section 1.1); C = A x B with A of size M x K in
+ * "hgemm_naive_kernel explained" (yuyanqi.com, section 1.1).
+ *
+ * Arithmetic: every input is widened to double before use.  An FP32 x FP32
+ * product carries at most 48 significant bits and an FP16 x FP16 product at
+ * most 22, so each product is exact in double and only the K-1 additions
+ * round.  The loop order is i, k, j with k ascending for every element, so
+ * each C_ref[i][j] is accumulated in exactly the order of the textbook
+ * i-j-k triple loop; FMA contraction cannot change a bit because the product
+ * is exact.  Build without -ffast-math (no reassociation).
+ *
+ * FP16 inputs arrive as IEEE binary16 bit patterns and are decoded by this
+ * file's own bit-level decoder (exact, including subnormals, signed zeros,
+ * infinities and NaN).
+ *
+ * Parity status: pinned.  The pins (identity, permutation, all-ones closed
+ * form C_ij = K, rank-1 outer products, K = 0 and K = 1, brute force against
+ * exact rational arithmetic on tiny shapes, float64 library matmul, the
+ * exhaustive binary16 decode table) live in the test suite.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_VERSION 1
+
+int oracle_version(void) { return ORACLE_VERSION; }
+
+/* ---------------------------------------------------------------------- */
+/* IEEE 754 binary16 -> binary64, exact.                                   */
+/* Layout: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits.        */
+/* ---------------------------------------------------------------------- */
+double oracle_f16_to_f64(uint16_t h)
+{
+    const int sign = (h >> 15) & 1;
+    const int expo = (h >> 10) & 0x1f;
+    const int frac = h & 0x3ff;
+    double mag;
+    if (expo == 0) {
+        /* zero or subnormal: frac * 2^(1 - 15 - 10) */
+        mag = ldexp((double)frac, -24);
+    } else if (expo == 0x1f) {
+        mag = frac ? NAN : INFINITY;
+    } else {
+        /* normal: (1024 + frac) * 2^(expo - 15 - 10) */
+        mag = ldexp((double)(0x400 | frac), expo - 25);
+    }
+    return sign ? -mag : mag;
+}
+
+void oracle_f16_array_to_f64(const uint16_t *src, double *dst, int64_t n)
+{
+    for (int64_t t = 0; t < n; ++t)
+        dst[t] = oracle_f16_to_f64(src[t]);
+}
+
+/* ---------------------------------------------------------------------- */
+/* Input access: element (i, k) of a row-major matrix with leading         */
+/* dimension ld lives at base[i * ld + k].                                  */
+/* ---------------------------------------------------------------------- */
+enum { ORACLE_F32 = 0, ORACLE_F16 = 1 };
+
+static double load_elem(const void *base, int dtype, int64_t idx)
+{
+    if (dtype == ORACLE_F32)
+        return (double)((const float *)base)[idx];
+    return oracle_f16_to_f64(((const uint16_t *)base)[idx]);
+}
+
+typedef struct {
+    int dtype;
+    int64_t N, K;
+    const void *A; int64_t lda;
+    const void *B; int64_t ldb;
+    const int64_t *rows;   /* which rows of C to produce (NULL: 0..nrows-1) */
+    int64_t r_begin, r_end; /* slice of the row list this worker owns */
+    double *C; int64_t ldr; /* output row t of the list goes to C + t*ldr   */
+    double *D; int64_t ldd; /* same for the error scale                      */
+} rows_job;
+
+/* One worker: for each owned row i of C, acc[:] = 0, then for k ascending
+ * acc[j] += A[i][k] * B[k][j] and den[j] += |A[i][k]| * |B[k][j]|. */
+static void *rows_worker(void *arg)
+{
+    const rows_job *jb = (const rows_job *)arg;
+    for (int64_t t = jb->r_begin; t < jb->r_end; ++t) {
+        const int64_t i = jb->rows ? jb->rows[t] : t;
+        double *acc = jb->C + t * jb->ldr;
+        double *den = jb->D + t * jb->ldd;
+        for (int64_t j = 0; j < jb->N; ++j) {
+            acc[j] = 0.0;
+            den[j] = 0.0;
+        }
+        for (int64_t k = 0; k < jb->K; ++k) {
+            const double a = load_elem(jb->A, jb->dtype, i * jb->lda + k);
+            const double abs_a = fabs(a);
+            const int64_t brow = k * jb->ldb;
+            for (int64_t j = 0; j < jb->N; ++j) {
+                const double b = load_elem(jb->B, jb->dtype, brow + j);
+                acc[j] += a * b;
+                den[j] += abs_a * fabs(b);
+            }
+        }
+    }
+    return NULL;
+}
+
+static int run_rows(int dtype, int64_t nrows, int64_t N, int64_t K,
+                    const void *A, int64_t lda, const void *B, int64_t ldb,
+                    const int64_t *rows, double *C, int64_t ldr,
+                    double *D, int64_t ldd, int nthreads)
+{
+    if (nrows < 0 || N < 0 || K < 0 || ldr < N || ldd < N)
+        return -1;
+    if (nrows == 0 || N == 0)
+        return 0;
+    if (nthreads < 1)
+        nthreads = 1;
+    if (nthreads > nrows)
+        nthreads = (int)nrows;
+    rows_job *jobs = (rows_job *)calloc((size_t)nthreads, sizeof(rows_job));
+    pthread_t *tids = (pthread_t *)calloc((size_t)nthreads, sizeof(pthread_t));
+    if (!jobs || !tids) {
+        free(jobs);
+        free(tids);
+        return -2;
+    }
+    int rc = 0;
+    int started = 0;
+    for (int w = 0; w < nthreads; ++w) {
+        rows_job *jb = &jobs[w];
+        jb->dtype = dtype;
+        jb->N = N; jb->K = K;
+        jb->A = A; jb->lda = lda;
+        jb->B = B; jb->ldb = ldb;
+        jb->rows = rows;
+        jb->r_begin = nrows * w / nthreads;
+        jb->r_end = nrows * (w + 1) / nthreads;
+        jb->C = C; jb->ldr = ldr;
+        jb->D = D; jb->ldd = ldd;
+        if (w == 0)
+            continue; /* worker 0 runs on the calling thread */
+        if (pthread_create(&tids[w], NULL, rows_worker, jb) != 0) {
+            rc = -3;
+            break;
+        }
+        started = w;
+    }
+    if (rc == 0)
+        rows_worker(&jobs[0]);
+    for (int w = 1; w <= started; ++w)
+        pthread_join(tids[w], NULL);
+    free(jobs);
+    free(tids);
+    return rc;
+}
+
+/*
+ * Rows of C_ref and D.
+ *   rows == NULL : produce rows 0..nrows-1 (nrows is then M)
+ *   rows != NULL : produce rows rows[0..nrows-1]; output row t is rows[t]
+ * C and D are caller-owned double arrays with leading dimensions ldr, ldd.
+ * Returns 0 on success, a negative value on bad arguments or thread failure.
+ */
+int oracle_gemm_rows_f32(int64_t nrows, int64_t N, int64_t K,
+                         const float *A, int64_t lda, const float *B, int64_t ldb,
+                         const int64_t *rows, double *C, int64_t ldr,
+                         double *D, int64_t ldd, int nthreads)
+{
+    return run_rows(ORACLE_F32, nrows, N, K, A, lda, B, ldb, rows, C, ldr, D, ldd,
+                    nthreads);
+}
+
+int oracle_gemm_rows_f16(int64_t nrows, int64_t N, int64_t K,
+                         const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb,
+                         const int64_t *rows, double *C, int64_t ldr,
+                         double *D, int64_t ldd, int nthreads)
+{
+    return run_rows(ORACLE_F16, nrows, N, K, A, lda, B, ldb, rows, C, ldr, D, ldd,
+                    nthreads);
+}
+
+/*
+ * Single entries C_ref[ii[t]][jj[t]] and D[ii[t]][jj[t]], each one a plain
+ * dot product over k ascending (the same order as the row routine).
+ */
+static int run_entries(int dtype, int64_t K, const void *A, int64_t lda,
+                       const void *B, int64_t ldb, const int64_t *ii,
+                       const int64_t *jj, int64_t n, double *c, double *d)
+{
+    if (K < 0 || n < 0)
+        return -1;
+    for (int64_t t = 0; t < n; ++t) {
+        double acc = 0.0, den = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            const double a = load_elem(A, dtype, ii[t] * lda + k);
+            const double b = load_elem(B, dtype, k * ldb + jj[t]);
+            acc += a * b;
+            den += fabs(a) * fabs(b);
+        }
+        c[t] = acc;
+        d[t] = den;
+    }
+    return 0;
+}
+
+int oracle_gemm_entries_f32(int64_t K, const float *A, int64_t lda,
+                            const float *B, int64_t ldb, const int64_t *ii,
+                            const int64_t *jj, int64_t n, double *c, double *d)
+{
+    return run_entries(ORACLE_F32, K, A, lda, B, ldb, ii, jj, n, c, d);
+}
+
+int oracle_gemm_entries_f16(int64_t K, const uint16_t *A, int64_t lda,
+                            const uint16_t *B, int64_t ldb, const int64_t *ii,
+                            const int64_t *jj, int64_t n, double *c, double *d)
+{
+    return run_entries(ORACLE_F16, K, A, lda, B, ldb, ii, jj, n, c, d);
+}
+
+/* ---------------------------------------------------------------------- */
+/* Error metric.                                                           */
+/*   r_ij = |C_gpu[i][j] - C_ref[i][j]| / D[i][j]                           */
+/*   r_ij = 0 when numerator and D are both 0; +inf when only D is 0.      */
+/*   e = max r_ij.  A NaN or Inf in C_gpu is counted as non-finite.         */
+/* C_gpu is widened exactly (FP32) or decoded exactly (FP16 bit patterns),  */
+/* i.e. the FP16 result is judged after its own output rounding.           */
+/* out[0] = e, out[1] = max |C_gpu - C_ref|, out[2] = i of e, out[3] = j.   */
+/* cnt[0] = #(r_ij > tol), cnt[1] = #non-finite C_gpu entries.              */
+/* ---------------------------------------------------------------------- */
+static void check_common(int dtype, int64_t M, int64_t N, const void *C, int64_t ldc,
+                         const double *R, int64_t ldr, const double *D, int64_t ldd,
+                         double tol, double *out, int64_t *cnt)
+{
+    double worst = 0.0, worst_abs = 0.0;
+    int64_t wi = -1, wj = -1, n_bad = 0, n_nonfinite = 0;
+    for (int64_t i = 0; i < M; ++i) {
+        for (int64_t j = 0; j < N; ++j) {
+            const double g = load_elem(C, dtype, i * ldc + j);
+            const double ref = R[i * ldr + j];
+            const double den = D[i * ldd + j];
+            double r;
+            if (!isfinite(g)) {
+                ++n_nonfinite;
+                r = INFINITY;
+            } else {
+                const double diff = fabs(g - ref);
+                if (diff > worst_abs)
+                    worst_abs = diff;
+                if (den == 0.0)
+                    r = (diff == 0.0) ? 0.0 : INFINITY;
+                else
+                    r = diff / den;
+            }
+            if (r > tol)
+                ++n_bad;
+            if (r > worst || wi < 0) {
+                if (r > worst || (wi < 0 && r >= worst)) {
+                    worst = r;
+                    wi = i;
+                    wj = j;
+                }
+            }
+        }
+    }
+    out[0] = worst;
+    out[1] = worst_abs;
+    out[2] = (double)wi;
+    out[3] = (double)wj;
+    cnt[0] = n_bad;
+    cnt[1] = n_nonfinite;
+}
+
+void oracle_check_f32(int64_t M, int64_t N, const float *C, int64_t ldc,
+                      const double *R, int64_t ldr, const double *D, int64_t ldd,
+                      double tol, double *out, int64_t *cnt)
+{
+    check_common(ORACLE_F32, M, N, C, ldc, R, ldr, D, ldd, tol, out, cnt);
+}
+
+void oracle_check_f16(int64_t M, int64_t N, const uint16_t *C, int64_t ldc,
+                      const double *R, int64_t ldr, const double *D, int64_t ldd,
+                      double tol, double *out, int64_t *cnt)
+{
+    check_common(ORACLE_F16, M, N, C, ldc, R, ldr, D, ldd, tol, out, cnt);
+}

@@ -1,0 +1,252 @@
+"""Pins for the CPU oracle: facts fixed by the mathematics of C = A x B, not
+by the oracle itself.
+
+Each pin takes an oracle library handle (``oracle.load()`` or a build of a
+planted-mistake copy of ``oracle.c``) and raises AssertionError when the
+oracle disagrees with the fact.  ``run_all`` collects the failures.
+
+The problem is the row-major product C[M x N] = A[M x K] x B[K x N] of the
+GEMM articles ("GEMM: from naive to shared memory tiling and register
+blocking", quant67.com, introduction; "hgemm_naive_kernel explained",
+yuyanqi.com, section 1.1).  The pages print no worked matrices, so the pins
+are closed forms (identity, permutation, all-ones C_ij = K, rank-1 outer
+products, K = 0, K = 1), brute force against exact rational arithmetic, a
+float64 library matmul, and the exhaustive binary16 table.
+"""
+from __future__ import annotations
+
+import random
+from fractions import Fraction
+
+import numpy as np
+
+import oracle
+from dense_gemm_row_amd import synth
+
+U64 = 2.0 ** -53  # unit roundoff of binary64
+
+
+def _padded(x: np.ndarray, pad: int) -> np.ndarray:
+    """A row-major view of ``x`` whose leading dimension is cols + pad; the
+    pad columns hold NaN so that reading them poisons the result."""
+    rows, cols = x.shape
+    big = np.full((rows, cols + pad), np.nan, dtype=x.dtype)
+    big[:, :cols] = x
+    return big[:, :cols]
+
+
+def _dtypes():
+    return (np.float32, np.float16)
+
+
+def _rand(dtype, seed, stream, r, c):
+    if dtype == np.float32:
+        return synth.uniform_f32(seed, stream, r, c)
+    return synth.uniform_f16(seed, stream, r, c)
+
+
+def pin_identity(lib):
+    """A = I gives C = B; B = I gives C = A (bit-exact), with padded ld."""
+    for dt in _dtypes():
+        for (M, N, K) in [(5, 7, 5), (1, 9, 1), (12, 3, 12)]:
+            B = _rand(dt, 11, 1, K, N)
+            A = np.eye(M, K, dtype=dt)
+            C, D = oracle.gemm_rows(_padded(A, 3), _padded(B, 5), lib=lib)
+            assert np.array_equal(C, B.astype(np.float64)), "A=I must give C=B"
+            assert np.array_equal(D, np.abs(B.astype(np.float64))), "A=I: D=|B|"
+        for (M, N, K) in [(7, 5, 5), (9, 1, 1), (3, 12, 12)]:
+            A = _rand(dt, 12, 0, M, K)
+            B = np.eye(K, N, dtype=dt)
+            C, D = oracle.gemm_rows(_padded(A, 2), _padded(B, 4), lib=lib)
+            assert np.array_equal(C, A.astype(np.float64)), "B=I must give C=A"
+
+
+def pin_permutation(lib):
+    """A = P (row i has its single 1 in column p[i]) gives C[i] = B[p[i]];
+    B = Q (row k has its 1 in column q[k]) gives C[:, q[k]] = A[:, k]."""
+    for dt in _dtypes():
+        K, N = 9, 6
+        p = synth.permutation(3, 2, K)
+        A = np.zeros((K, K), dtype=dt)
+        A[np.arange(K), p] = 1
+        B = _rand(dt, 13, 1, K, N)
+        C, _ = oracle.gemm_rows(_padded(A, 1), _padded(B, 3), lib=lib)
+        assert np.array_equal(C, B[p].astype(np.float64)), "C = P B"
+        M, K = 4, 7
+        q = synth.permutation(4, 2, K)
+        Bq = np.zeros((K, K), dtype=dt)
+        Bq[np.arange(K), q] = 1
+        A2 = _rand(dt, 14, 0, M, K)
+        C2, _ = oracle.gemm_rows(A2, Bq, lib=lib)
+        expect = np.zeros((M, K))
+        expect[:, q] = A2.astype(np.float64)
+        assert np.array_equal(C2, expect), "C = A Q"
+
+
+def pin_all_ones(lib):
+    """All-ones A and B: C_ij = K and D_ij = K exactly."""
+    for dt in _dtypes():
+        for (M, N, K) in [(1, 1, 1), (2, 3, 5), (7, 1, 9), (33, 17, 64), (3, 4, 1000)]:
+            A = np.ones((M, K), dtype=dt)
+            B = np.ones((K, N), dtype=dt)
+            C, D = oracle.gemm_rows(_padded(A, 1), B, lib=lib)
+            assert np.all(C == K) and np.all(D == K), f"all-ones must give K={K}"
+            c, d = oracle.gemm_entries(A, B, [M - 1, 0], [0, N - 1], lib=lib)
+            assert np.all(c == K) and np.all(d == K), "entries: all-ones"
+
+
+def pin_rank1(lib):
+    """Only column c of A and row c of B are nonzero: C = u v^T exactly.
+    When B's nonzero row is a different one, C = 0."""
+    for dt in _dtypes():
+        M, N, K = 6, 5, 8
+        u = synth.small_int(5, 0, M, 1, -3, 3).ravel()
+        v = synth.small_int(5, 1, 1, N, -3, 3).ravel()
+        for c in (0, 3, K - 1):
+            A = np.zeros((M, K), dtype=dt)
+            B = np.zeros((K, N), dtype=dt)
+            A[:, c] = u
+            B[c, :] = v
+            C, D = oracle.gemm_rows(A, _padded(B, 2), lib=lib)
+            assert np.array_equal(C, np.outer(u, v)), "rank-1: C = u v^T"
+            assert np.array_equal(D, np.abs(np.outer(u, v))), "rank-1: D"
+            B2 = np.zeros((K, N), dtype=dt)
+            B2[(c + 1) % K, :] = v
+            C2, _ = oracle.gemm_rows(A, B2, lib=lib)
+            assert not np.any(C2), "mismatched k must give C = 0"
+
+
+def pin_k0_k1(lib):
+    """K = 0 is the empty sum (C = 0, D = 0); K = 1 gives C_ij = a_i b_j,
+    exact in double."""
+    for dt in _dtypes():
+        A = np.zeros((4, 0), dtype=dt)
+        B = np.zeros((0, 3), dtype=dt)
+        C, D = oracle.gemm_rows(A, B, lib=lib)
+        assert C.shape == (4, 3) and not np.any(C) and not np.any(D), "K=0"
+        A = _rand(dt, 21, 0, 5, 1)
+        B = _rand(dt, 21, 1, 1, 7)
+        C, _ = oracle.gemm_rows(A, B, lib=lib)
+        expect = np.outer(A.astype(np.float64).ravel(), B.astype(np.float64).ravel())
+        assert np.array_equal(C, expect), "K=1: C = a b^T"
+
+
+def _exact_fraction(x) -> Fraction:
+    return Fraction(float(x))
+
+
+def pin_bruteforce_fractions(lib, trials: int = 60):
+    """Tiny random shapes against exact rational arithmetic: the double
+    result lies within K * 2**-53 * D of the exact sum (each product exact,
+    K - 1 rounded additions), and D within the same relative bound of the
+    exact sum of |a||b|."""
+    rng = random.Random(1234)
+    for trial in range(trials):
+        dt = np.float32 if trial % 2 == 0 else np.float16
+        M, N, K = rng.randint(1, 6), rng.randint(1, 6), rng.randint(1, 6)
+        A = _rand(dt, 100 + trial, 0, M, K)
+        B = _rand(dt, 100 + trial, 1, K, N)
+        A = A * dt(2.0 ** rng.randint(-6, 6))  # vary magnitudes
+        C, D = oracle.gemm_rows(_padded(A, rng.randint(0, 3)),
+                                _padded(B, rng.randint(0, 3)), lib=lib)
+        ce, de = oracle.gemm_entries(A, B, [M - 1], [N - 1], lib=lib)
+        for i in range(M):
+            for j in range(N):
+                exact = sum(_exact_fraction(A[i, k]) * _exact_fraction(B[k, j])
+                            for k in range(K))
+                den = sum(abs(_exact_fraction(A[i, k]) * _exact_fraction(B[k, j]))
+                          for k in range(K))
+                bound = Fraction(K) * Fraction(U64) * den
+                assert abs(Fraction(C[i, j]) - exact) <= bound, (
+                    f"C[{i},{j}] off the exact sum (M,N,K={M},{N},{K})")
+                assert abs(Fraction(D[i, j]) - den) <= bound, "D off the exact sum"
+                if i == M - 1 and j == N - 1:
+                    assert abs(Fraction(ce[0]) - exact) <= bound, "entry off"
+
+
+def pin_numpy_matmul(lib):
+    """float64 matmul of the same (exactly widened) inputs at 256^3: every
+    element within 1e-12 * D of the oracle, and D matches |A| @ |B|."""
+    for dt in _dtypes():
+        A = _rand(dt, 0, 0, 256, 256)
+        B = _rand(dt, 0, 1, 256, 256)
+        A64, B64 = A.astype(np.float64), B.astype(np.float64)
+        C, D = oracle.gemm_rows(A, B, threads=4, lib=lib)
+        ref = A64 @ B64
+        den = np.abs(A64) @ np.abs(B64)
+        assert np.all(np.abs(C - ref) <= 1e-12 * den), "oracle vs float64 matmul"
+        assert np.all(np.abs(D - den) <= 1e-12 * den), "D vs |A| @ |B|"
+        # Row subsets and single entries agree with the full result.
+        rows = [255, 0, 17, 17]
+        Cs, Ds = oracle.gemm_rows(A, B, rows=rows, threads=2, lib=lib)
+        assert np.all(np.abs(Cs - ref[rows]) <= 1e-12 * den[rows]), "row subset"
+        ii, jj = [3, 200, 255], [255, 0, 128]
+        ce, de = oracle.gemm_entries(A, B, ii, jj, lib=lib)
+        assert np.all(np.abs(ce - ref[ii, jj]) <= 1e-12 * den[ii, jj]), "entries"
+
+
+def pin_f16_decode(lib):
+    """Exhaustive binary16 decode against numpy's float16 -> float64, plus
+    closed values: 0x3C00 = 1, 0x7BFF = 65504, 0x0001 = 2**-24,
+    0x0400 = 2**-14, 0x8000 = -0, 0x7C00 = +inf, 0x7E00 = NaN."""
+    bits = np.arange(65536, dtype=np.uint16)
+    mine = _decode(lib, bits)
+    ref = bits.view(np.float16).astype(np.float64)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(mine), nan), "NaN patterns"
+    assert np.array_equal(mine[~nan], ref[~nan]), "decoded values"
+    assert np.array_equal(np.signbit(mine[~nan]), np.signbit(ref[~nan])), "signs"
+    closed = {0x3C00: 1.0, 0x7BFF: 65504.0, 0x0001: 2.0 ** -24, 0x0400: 2.0 ** -14,
+              0x3555: 0.333251953125, 0xC000: -2.0, 0x7C00: float("inf")}
+    for b, v in closed.items():
+        assert lib.oracle_f16_to_f64(b) == v, f"decode 0x{b:04x}"
+    neg0 = lib.oracle_f16_to_f64(0x8000)
+    assert neg0 == 0.0 and np.signbit(neg0), "decode -0"
+
+
+def _decode(lib, bits):
+    out = np.empty(bits.shape, dtype=np.float64)
+    lib.oracle_f16_array_to_f64(bits.ctypes.data, out.ctypes.data, bits.size)
+    return out
+
+
+def pin_error_metric(lib):
+    """The check routine on hand-made cases: r = |g - ref| / D; 0/0 is 0;
+    x/0 is +inf; NaN and Inf in the GPU result are counted non-finite; the
+    FP16 result is judged after decoding."""
+    R = np.array([[1.0, 2.0, 0.0], [4.0, -1.0, 0.0]])
+    D = np.array([[2.0, 4.0, 0.0], [8.0, 1.0, 0.0]])
+    G = np.array([[1.5, 2.0, 0.0], [4.0, -1.0, 0.0]], dtype=np.float32)
+    rep = oracle.check(G, R, D, 0.3, lib=lib)
+    assert rep["max_rel"] == 0.25 and rep["worst"] == (0, 0), "ratio 0.5/2"
+    assert rep["max_abs"] == 0.5 and rep["ok"], "abs error / pass"
+    rep = oracle.check(G, R, D, 0.2, lib=lib)
+    assert rep["n_bad"] == 1 and not rep["ok"], "one element above tol"
+    G2 = G.copy()
+    G2[1, 2] = 1e-30
+    rep = oracle.check(G2, R, D, 1.0, lib=lib)
+    assert rep["max_rel"] == float("inf") and rep["worst"] == (1, 2), "x/0 = inf"
+    G3 = G.copy()
+    G3[0, 1] = np.nan
+    G3[1, 0] = np.inf
+    rep = oracle.check(G3, R, D, 1.0, lib=lib)
+    assert rep["n_nonfinite"] == 2 and not rep["ok"], "non-finite"
+    H = np.array([[1.0, 2.0, 0.0], [4.0, -1.0, 0.0]], dtype=np.float16)
+    H[0, 0] = np.float16(1.5)
+    rep = oracle.check(H, R, D, 0.3, lib=lib)
+    assert rep["max_rel"] == 0.25, "f16 decoded before comparing"
+
+
+PINS = [pin_identity, pin_permutation, pin_all_ones, pin_rank1, pin_k0_k1,
+        pin_bruteforce_fractions, pin_numpy_matmul, pin_f16_decode,
+        pin_error_metric]
+
+
+def run_all(lib) -> list[str]:
+    failures = []
+    for pin in PINS:
+        try:
+            pin(lib)
+        except AssertionError as e:
+            failures.append(f"{pin.__name__}: {e}")
+    return failures

@@ -1,0 +1,71 @@
+"""Planted mistakes in the oracle must fail at least one pin.
+
+Each case copies oracle.c, applies one textual change (a dropped term, a
+wrong sign or index, a transposed operand, a wrong decode constant, a
+broken error ratio), builds the copy with gcc and runs all pins against it
+in a child process.  The anchors are checked first, so a refactor of
+oracle.c that removes one fails loudly instead of silently passing."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "oracle.c")
+
+MUTANTS = {
+    "drop_last_k": ("for (int64_t k = 0; k < jb->K; ++k)",
+                    "for (int64_t k = 0; k < jb->K - 1; ++k)"),
+    "skip_first_k": ("for (int64_t k = 0; k < jb->K; ++k)",
+                     "for (int64_t k = 1; k < jb->K; ++k)"),
+    "wrong_sign": ("acc[j] += a * b;", "acc[j] -= a * b;"),
+    "transposed_b": ("const double b = load_elem(jb->B, jb->dtype, brow + j);",
+                     "const double b = load_elem(jb->B, jb->dtype, j * jb->ldb + k);"),
+    "transposed_a": ("load_elem(jb->A, jb->dtype, i * jb->lda + k)",
+                     "load_elem(jb->A, jb->dtype, k * jb->lda + i)"),
+    "b_uses_lda": ("const int64_t brow = k * jb->ldb;",
+                   "const int64_t brow = k * jb->lda;"),
+    "a_ignores_lda": ("load_elem(jb->A, jb->dtype, i * jb->lda + k)",
+                      "load_elem(jb->A, jb->dtype, i * jb->K + k)"),
+    "den_signed": ("den[j] += abs_a * fabs(b);", "den[j] += a * b;"),
+    "f16_bias": ("mag = ldexp((double)(0x400 | frac), expo - 25);",
+                 "mag = ldexp((double)(0x400 | frac), expo - 24);"),
+    "f16_no_hidden_bit": ("mag = ldexp((double)(0x400 | frac), expo - 25);",
+                          "mag = ldexp((double)frac, expo - 25);"),
+    "f16_subnormal": ("mag = ldexp((double)frac, -24);",
+                      "mag = ldexp((double)frac, -25);"),
+    "f16_sign": ("return sign ? -mag : mag;", "return mag;"),
+    "entries_drop_k": ("for (int64_t k = 0; k < K; ++k) {",
+                       "for (int64_t k = 0; k + 1 < K; ++k) {"),
+    "metric_absolute": ("r = diff / den;", "r = diff;"),
+    "metric_zero_den_hidden": ("r = (diff == 0.0) ? 0.0 : INFINITY;", "r = 0.0;"),
+    "metric_nan_ignored": ("++n_nonfinite;\n                r = INFINITY;",
+                           "r = 0.0;"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_is_caught(name, tmp_path):
+    old, new = MUTANTS[name]
+    text = open(SRC).read()
+    assert old in text, f"anchor for {name} not found in oracle.c"
+    src = tmp_path / "oracle_mutant.c"
+    src.write_text(text.replace(old, new))
+    lib = str(tmp_path / "liboracle_mutant.so")
+    oracle.build(str(src), lib)
+    res = subprocess.run([sys.executable, os.path.join(ROOT, "tests", "_pin_runner.py"), lib],
+                         capture_output=True, text=True, timeout=600)
+    assert res.returncode != 0, f"mutant {name} passed every pin:\n{res.stdout}"
+
+
+def test_unmutated_copy_passes(tmp_path):
+    src = tmp_path / "oracle_copy.c"
+    src.write_text(open(SRC).read())
+    lib = str(tmp_path / "liboracle_copy.so")
+    oracle.build(str(src), lib)
+    res = subprocess.run([sys.executable, os.path.join(ROOT, "tests", "_pin_runner.py"), lib],
+                         capture_output=True, text=True, timeout=600)
+    assert res.returncode == 0, res.stdout + res.stderr

@@ -1,0 +1,61 @@
+"""The seeded input generator.  CPU only."""
+import numpy as np
+
+from dense_gemm_row_amd import synth
+
+
+def test_splitmix64_published_sequence():
+    # First outputs of SplitMix64 started from state 0, as printed by the
+    # reference implementation (Vigna's splitmix64.c; Java SplittableRandom
+    # with seed 0 yields the same stream).
+    assert synth.splitmix64(0, 4) == [0xE220A8397B1DCDAF, 0x6E789E6AA1B965F4,
+                                      0x06C45D188009454F, 0xF88BB8A8724C81EC]
+
+
+def test_vector_and_scalar_finaliser_agree():
+    z = synth.stream_u64(7, 3, 1000) ^ np.uint64(0x1234)
+    vec = synth.mix64(z)
+    assert [int(x) for x in vec[:50]] == [synth.mix64_int(int(x)) for x in z[:50]]
+
+
+def test_stream_is_counter_based():
+    key = synth.stream_key(0, 1)
+    full = synth.stream_u64(0, 1, 100)
+    assert int(full[0]) == synth.mix64_int(key + synth.GAMMA)
+    assert np.array_equal(synth.stream_u64(0, 1, 10, start=90), full[90:])
+
+
+def test_uniform_grid_and_range():
+    a = synth.uniform_f32(0, 0, 300, 301)
+    assert a.dtype == np.float32 and a.shape == (300, 301)
+    assert a.min() >= -1.0 and a.max() <= 1.0 - 2.0 ** -23
+    grid = (a.astype(np.float64) + 1.0) * 2.0 ** 23
+    assert np.array_equal(grid, np.round(grid)), "values sit on the 2^-23 grid"
+    assert abs(a.mean()) < 0.01 and abs(a.var() - 1 / 3) < 0.01
+
+
+def test_streams_differ_and_repeat():
+    a0 = synth.uniform_f32(0, 0, 8, 8)
+    assert np.array_equal(a0, synth.uniform_f32(0, 0, 8, 8))
+    assert not np.array_equal(a0, synth.uniform_f32(0, 1, 8, 8))
+    assert not np.array_equal(a0, synth.uniform_f32(1, 0, 8, 8))
+
+
+def test_f16_is_rne_of_f32():
+    a = synth.uniform_f32(5, 0, 64, 64)
+    h = synth.uniform_f16(5, 0, 64, 64)
+    assert h.dtype == np.float16
+    assert np.array_equal(h, a.astype(np.float16))
+    err = np.abs(h.astype(np.float64) - a.astype(np.float64))
+    ulp = np.spacing(np.abs(h)).astype(np.float64)
+    assert np.all(err <= ulp / 2)
+
+
+def test_small_int_range():
+    v = synth.small_int(0, 0, 200, 200)
+    assert set(np.unique(v).tolist()) == {-2.0, -1.0, 0.0, 1.0, 2.0}
+
+
+def test_permutation_valid():
+    p = synth.permutation(0, 2, 1000)
+    assert np.array_equal(np.sort(p), np.arange(1000))
