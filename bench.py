@@ -1,0 +1,256 @@
+#!/usr/bin/env python3
+"""Benchmark: dense row-major GEMM at M = N = K = 4096 on one MI355X.
+
+One step is the whole path once: an FP32 SGEMM (C = A x B, FP32 in/out) and
+an FP16 HGEMM (FP16 in, FP32 accumulate, FP16 out), both 4096^3, through the
+libgemm C-ABI on the current torch stream, inputs resident in HBM.  `value`
+is the step's throughput, 2 * (2 * 4096^3) flops / step time, in TFLOP/s;
+the JSON line also carries each kernel's own TFLOP/s and fraction of the
+MI355X matrix peak (FP32 157.3 TFLOP/s, FP16 2516.6 TFLOP/s dense).
+
+Before timing, sampled rows and entries of both products are checked
+against the CPU oracle.  After timing, the oracle itself is timed on a
+bounded sample of the same workload (``cpu_baseline``).
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"f32": 157.3, "f16": 2516.6}  # MI355X dense matrix peaks
+HBM_PEAK_GBS = 8000.0
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--size", type=int, default=4096, help="M = N = K")
+    ap.add_argument("--dtypes", default="f32,f16", help="kernels in one step")
+    ap.add_argument("--f32-config", default=None, help="force an FP32 variant by name")
+    ap.add_argument("--f16-config", default=None, help="force an FP16 variant by name")
+    ap.add_argument("--order", type=int, default=None, help="force the tile order")
+    ap.add_argument("--group-m", type=int, default=None, help="force the band height")
+    ap.add_argument("--cpu-budget", type=float, default=20.0,
+                    help="seconds of oracle work for the CPU baseline (0 = skip)")
+    ap.add_argument("--cpu-threads", type=int, default=16)
+    ap.add_argument("--no-check", action="store_true", help="skip the oracle check")
+    return ap.parse_args()
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "dense_gemm_row_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel: str, digest: str):
+    """HBM bytes per launch measured by rocprofv3 counters for this kernel
+    and this exact kernel source, or None."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    for line in open(path):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        kv = dict(tok.split("=", 1) for tok in line.split() if "=" in tok)
+        if kv.get("variant") == kernel and kv.get("source") == digest:
+            try:
+                return float(kv["bytes_per_launch"])
+            except (KeyError, ValueError):
+                return None
+    return None
+
+
+def main():
+    args = parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on one GPU only: this library has no multi-GPU path "
+              "(see DESIGN.md for how the GEMM would shard). Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from dense_gemm_row_amd import gemm, synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    gemm.lib()  # fails loudly if libgemm.so is missing
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    n = args.size
+    kinds = [k for k in args.dtypes.split(",") if k]
+    flops = 2.0 * n * n * n
+
+    # Inputs: i.i.d. uniform[-1, 1) from seed 0 (A stream 0, B stream 1); the
+    # FP16 operands are the RNE roundings of the FP32 ones.
+    t0 = time.time()
+    A32 = synth.uniform_f32(0, synth.STREAM_A, n, n)
+    B32 = synth.uniform_f32(0, synth.STREAM_B, n, n)
+    host = {"f32": (A32, B32), "f16": (A32.astype(np.float16), B32.astype(np.float16))}
+    gen_s = time.time() - t0
+    tdt = {"f32": torch.float32, "f16": torch.float16}
+    devbuf = {}
+    for k in kinds:
+        A, B = host[k]
+        devbuf[k] = (torch.from_numpy(A).to(dev), torch.from_numpy(B).to(dev),
+                     torch.empty((n, n), dtype=tdt[k], device=dev))
+    cfgs = {}
+    for k in kinds:
+        dt = gemm.DTYPE_F32 if k == "f32" else gemm.DTYPE_F16
+        name = args.f32_config if k == "f32" else args.f16_config
+        c = gemm.config_by_name(dt, name) if name else gemm.gemm_select_config(dt, n, n, n)
+        if args.order is not None:
+            c.order = args.order
+        if args.group_m is not None:
+            c.group_m = args.group_m
+        cfgs[k] = c
+    stream = torch.cuda.current_stream(dev)
+    sptr = stream.cuda_stream
+
+    def launch(k):
+        a, b, c = devbuf[k]
+        fn = gemm.gemm_f32_ex if k == "f32" else gemm.gemm_f16_ex
+        st = fn(n, n, n, a.data_ptr(), n, b.data_ptr(), n, c.data_ptr(), n, sptr, cfgs[k])
+        if st != gemm.GEMM_OK:
+            raise gemm.GemmError(st, f"gemm_{k}")
+
+    for _ in range(max(args.warmup, 1)):
+        for k in kinds:
+            launch(k)
+    torch.cuda.synchronize()
+
+    parity = {}
+    if not args.no_check:
+        import oracle
+        rng = np.random.default_rng(1)
+        for k in kinds:
+            A, B = host[k]
+            C = devbuf[k][2].cpu().numpy()
+            rows = sorted(set([0, n - 1] + rng.integers(0, n, 6).tolist()))
+            ref, den = oracle.gemm_rows(A, B, rows=rows, threads=min(args.cpu_threads, 16))
+            tol = oracle.SGEMM_TOL if k == "f32" else oracle.HGEMM_TOL
+            rep = oracle.check(np.ascontiguousarray(C[rows]), ref, den, tol)
+            ii, jj = rng.integers(0, n, 512), rng.integers(0, n, 512)
+            ce, de = oracle.gemm_entries(A, B, ii, jj)
+            rep2 = oracle.check(C[ii, jj].reshape(1, -1), ce.reshape(1, -1), de.reshape(1, -1), tol)
+            parity[k] = {"rows": len(rows), "entries": 512, "tol": tol,
+                         "max_rel": max(rep["max_rel"], rep2["max_rel"]),
+                         "ok": rep["ok"] and rep2["ok"]}
+        if not all(p["ok"] for p in parity.values()):
+            print(json.dumps({"error": "parity check failed", "parity": parity}), flush=True)
+            sys.exit(1)
+
+    # Timed region: K steps, events around every launch on the launch stream.
+    ev = {k: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)] for k in kinds}
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for s in range(args.steps):
+        for k in kinds:
+            ev[k][s][0].record(stream)
+            launch(k)
+            ev[k][s][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    ms_per_step = wall * 1e3 / args.steps
+
+    kernels = {}
+    for k in kinds:
+        times = sorted(e0.elapsed_time(e1) for e0, e1 in ev[k])
+        mean = sum(times) / len(times)
+        med = times[len(times) // 2]
+        kernels[k] = {
+            "variant": cfgs[k].name.decode(), "order": cfgs[k].order, "group_m": cfgs[k].group_m,
+            "ms_mean": round(mean, 5), "ms_median": round(med, 5), "ms_min": round(times[0], 5),
+            "tflops": round(flops / (mean * 1e-3) / 1e12, 2),
+            "tflops_median": round(flops / (med * 1e-3) / 1e12, 2),
+            "pct_peak": round(100.0 * flops / (mean * 1e-3) / 1e12 / PEAK_TFLOPS[k], 2),
+            "peak_tflops": PEAK_TFLOPS[k],
+        }
+
+    digest = source_digest()
+    dom = max(kinds, key=lambda k: kernels[k]["ms_mean"])
+
+    def roofline(k):
+        kk = kernels[k]
+        achieved = flops / (kk["ms_mean"] * 1e-3) / 1e12
+        traffic = load_traffic(kk["variant"], digest)
+        return {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS[k],
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS[k], 4),
+                "traffic": traffic, "kernel": kk["variant"],
+                "algorithmic_flops_per_launch": flops}
+
+    cpu = None
+    if args.cpu_budget > 0:
+        import oracle
+        threads = max(1, min(args.cpu_threads, len(os.sched_getaffinity(0))))
+        spent, done_flops, parts = 0.0, 0.0, []
+        for k in kinds:
+            A, B = host[k]
+            # Calibrate on a few rows, then fill this kind's share of the budget.
+            t1 = time.perf_counter()
+            oracle.gemm_rows(A, B, rows=list(range(threads)), threads=threads)
+            per_row = (time.perf_counter() - t1) / threads
+            share = args.cpu_budget / len(kinds)
+            rows = max(threads, int(share / max(per_row, 1e-6) // threads) * threads)
+            rows = min(rows, n)
+            t1 = time.perf_counter()
+            oracle.gemm_rows(A, B, rows=list(range(rows)), threads=threads)
+            dt = time.perf_counter() - t1
+            spent += dt
+            done_flops += 2.0 * rows * n * n
+            parts.append(f"{rows} rows of the {n}^3 {'SGEMM' if k == 'f32' else 'HGEMM'}")
+        cpu = {"value": round(done_flops / spent / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+               "kind": "oracle", "seconds": round(spent, 2),
+               "sample": " + ".join(parts) + " (FP64 i-k-j oracle, all columns of each row)"}
+
+    total_flops = flops * len(kinds)
+    value = total_flops / (ms_per_step * 1e-3) / 1e12
+    out = {
+        "metric": "TFLOP/s (2MNK/t) and % of MI355X peak, SGEMM & HGEMM at M=N=K=4096",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "+".join(kinds),
+        "data": "synthetic",
+        "config": {"workload": f"sgemm+hgemm {n}x{n}x{n} row-major, uniform[-1,1) seed 0",
+                   "M": n, "N": n, "K": n, "step": " then ".join(
+                       "SGEMM fp32" if k == "f32" else "HGEMM fp16-in fp32-acc fp16-out" for k in kinds)},
+        "kernels": kernels,
+        "roofline": roofline(dom),
+        "roofline_all": {k: roofline(k) for k in kinds},
+        "cpu_baseline": cpu,
+        "parity": parity,
+        "source_digest": digest,
+        "input_gen_s": round(gen_s, 2),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

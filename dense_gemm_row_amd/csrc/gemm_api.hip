@@ -1,0 +1,353 @@
+// C-ABI entry points of libgemm (declared in include/gemm.h): argument
+// validation, variant selection (tuning table, then shape heuristic),
+// launch on the caller's stream, and the host-only checks.
+//
+// The user-facing call mirrors the bindings of the GEMM articles
+// ("sgemm - beyond cuBLAS", section 1 and 2 bindings: infer M, K, N from the
+// operands, compute the grid, launch on the current stream) with explicit
+// sizes and leading dimensions instead of tensors.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "gemm_internal.h"
+
+namespace gemm {
+
+int lds_conflicts(const int* addr, int width, int banks) {
+  const int group = (banks * 4) / width < 64 ? (banks * 4) / width : 64;
+  int extra = 0;
+  for (int g0 = 0; g0 < 64; g0 += group) {
+    // For each bank, the distinct word addresses touched by this group.
+    int worst = 0;
+    for (int bank = 0; bank < banks; ++bank) {
+      int words[64 * 4];
+      int n = 0;
+      for (int l = g0; l < g0 + group && l < 64; ++l) {
+        if (addr[l] < 0) continue;
+        for (int w = 0; w < width / 4; ++w) {
+          const int word = addr[l] / 4 + w;
+          if (word % banks != bank) continue;
+          bool seen = false;
+          for (int t = 0; t < n; ++t) seen = seen || words[t] == word;
+          if (!seen) words[n++] = word;
+        }
+      }
+      if (n > worst) worst = n;
+    }
+    if (worst > 1) extra += worst - 1;
+  }
+  return extra;
+}
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+gemm_status_t fail(gemm_status_t st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+gemm_status_t fail(gemm_status_t st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+struct Table {
+  std::vector<Variant> v[2];  // per dtype
+  Table() {
+    int n = 0;
+    const Variant* p = sgemm_mfma_variants(&n);
+    v[0].insert(v[0].end(), p, p + n);
+    p = sgemm_simt_variants(&n);
+    v[0].insert(v[0].end(), p, p + n);
+    p = hgemm_mfma_variants(&n);
+    v[1].insert(v[1].end(), p, p + n);
+    for (int d = 0; d < 2; ++d)
+      for (size_t i = 0; i < v[d].size(); ++i) v[d][i].desc.id = (int32_t)i;
+  }
+};
+
+const Table& table() {
+  static Table t;
+  return t;
+}
+
+struct TuneEntry {
+  int dtype;
+  int64_t M, N, K;
+  int id, order, group_m;
+};
+std::vector<TuneEntry> g_tuning;
+std::mutex g_tuning_mu;
+
+int find_by_name(int dtype, const char* name) {
+  const auto& v = table().v[dtype];
+  for (size_t i = 0; i < v.size(); ++i)
+    if (strcmp(v[i].desc.name, name) == 0) return (int)i;
+  return -1;
+}
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Heuristic: among the MFMA variants, prefer the largest tile area that
+// still gives at least one workgroup per CU (256 CUs); otherwise the one
+// with the most workgroups.  Ties go to the earlier table entry.
+gemm_config_t heuristic(int dtype, int64_t M, int64_t N, int64_t K) {
+  (void)K;
+  const auto& v = table().v[dtype];
+  const int64_t kCUs = 256;
+  int best = -1;
+  int64_t best_area = -1, best_tiles = -1;
+  for (size_t i = 0; i < v.size(); ++i) {
+    const gemm_config_t& d = v[i].desc;
+    if (d.family != GEMM_FAMILY_MFMA) continue;
+    const int64_t tiles = cdiv(M, d.bm) * cdiv(N, d.bn);
+    const int64_t area = (int64_t)d.bm * d.bn;
+    if (tiles >= kCUs) {
+      if (best_tiles < kCUs || area > best_area) {
+        best = (int)i;
+        best_area = area;
+        best_tiles = tiles;
+      }
+    } else if (best_tiles < kCUs && (tiles > best_tiles || (tiles == best_tiles && area > best_area))) {
+      best = (int)i;
+      best_area = area;
+      best_tiles = tiles;
+    }
+  }
+  return v[best < 0 ? 0 : best].desc;
+}
+
+gemm_config_t select(int dtype, int64_t M, int64_t N, int64_t K) {
+  {
+    std::lock_guard<std::mutex> lk(g_tuning_mu);
+    for (const auto& e : g_tuning)
+      if (e.dtype == dtype && e.M == M && e.N == N && e.K == K) {
+        gemm_config_t d = table().v[dtype][e.id].desc;
+        d.order = e.order;
+        d.group_m = e.group_m;
+        return d;
+      }
+  }
+  return heuristic(dtype, M, N, K);
+}
+
+TileMap make_map(const gemm_config_t& c, int64_t M, int64_t N) {
+  TileMap t;
+  t.tiles_m = (int)cdiv(M, c.bm);
+  t.tiles_n = (int)cdiv(N, c.bn);
+  t.order = c.order;
+  t.group_m = c.group_m;
+  t.xcds = kXcds;
+  return t;
+}
+
+bool overlap(const void* a, size_t abytes, const void* b, size_t bbytes) {
+  if (!a || !b || abytes == 0 || bbytes == 0) return false;
+  const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  return a0 < b0 + bbytes && b0 < a0 + abytes;
+}
+
+size_t span_bytes(int64_t rows, int64_t cols, int64_t ld, size_t es) {
+  if (rows <= 0 || cols <= 0) return 0;
+  return ((size_t)(rows - 1) * (size_t)ld + (size_t)cols) * es;
+}
+
+gemm_status_t validate(int dtype, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                       const void* B, int64_t ldb, const void* C, int64_t ldc) {
+  if (M < 0 || N < 0 || K < 0) return fail(GEMM_ERR_INVALID_ARG, "negative dimension");
+  const int64_t lim = 0x7fffffff;
+  if (M > lim || N > lim || K > lim) return fail(GEMM_ERR_INVALID_ARG, "dimension above 2^31-1");
+  if (lda < (K > 1 ? K : 1)) return fail(GEMM_ERR_INVALID_ARG, "lda < max(1, K)");
+  if (ldb < (N > 1 ? N : 1)) return fail(GEMM_ERR_INVALID_ARG, "ldb < max(1, N)");
+  if (ldc < (N > 1 ? N : 1)) return fail(GEMM_ERR_INVALID_ARG, "ldc < max(1, N)");
+  if (M > 0 && K > 0 && !A) return fail(GEMM_ERR_INVALID_ARG, "A is NULL");
+  if (K > 0 && N > 0 && !B) return fail(GEMM_ERR_INVALID_ARG, "B is NULL");
+  if (M > 0 && N > 0 && !C) return fail(GEMM_ERR_INVALID_ARG, "C is NULL");
+  const int64_t tiles_lim = 0x7fffffff;
+  if (cdiv(M, 64) * cdiv(N, 64) > tiles_lim) return fail(GEMM_ERR_INVALID_ARG, "output too large");
+  const size_t es = dtype == GEMM_DTYPE_F32 ? 4 : 2;
+  const size_t cb = span_bytes(M, N, ldc, es);
+  if (overlap(C, cb, A, span_bytes(M, K, lda, es)) || overlap(C, cb, B, span_bytes(K, N, ldb, es)))
+    return fail(GEMM_ERR_ALIAS, "C overlaps A or B");
+  return GEMM_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+gemm_status_t run(int dtype, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                  const void* B, int64_t ldb, void* C, int64_t ldc, void* stream,
+                  const gemm_config_t* forced) {
+  g_err[0] = 0;
+  gemm_status_t st = validate(dtype, M, N, K, A, lda, B, ldb, C, ldc);
+  if (st != GEMM_OK) return st;
+  gemm_config_t cfg;
+  const auto& v = table().v[dtype];
+  if (forced) {
+    if (forced->id < 0 || forced->id >= (int32_t)v.size())
+      return fail(GEMM_ERR_UNSUPPORTED, "config id %d not in the %s table", forced->id,
+                  dtype == GEMM_DTYPE_F32 ? "f32" : "f16");
+    if (forced->order < GEMM_ORDER_ROW || forced->order > GEMM_ORDER_XCD || forced->group_m < 1)
+      return fail(GEMM_ERR_UNSUPPORTED, "bad tile order %d / group_m %d", forced->order,
+                  forced->group_m);
+    cfg = v[forced->id].desc;
+    cfg.order = forced->order;
+    cfg.group_m = forced->group_m;
+  } else {
+    cfg = select(dtype, M, N, K);
+  }
+  if (M == 0 || N == 0) return GEMM_OK;
+
+  Params p;
+  p.A = A;
+  p.B = B;
+  p.C = C;
+  p.lda = lda;
+  p.ldb = ldb;
+  p.ldc = ldc;
+  p.M = (int)M;
+  p.N = (int)N;
+  p.K = (int)K;
+  const int w = dtype == GEMM_DTYPE_F32 ? 4 : 8;  // elements per 16 bytes
+  const bool vec = aligned16(A) && aligned16(B) && aligned16(C) && lda % w == 0 &&
+                   ldb % w == 0 && ldc % w == 0 && K % w == 0 && N % w == 0;
+  const TileMap map = make_map(cfg, M, N);
+  const hipError_t e = v[cfg.id].launch(p, map, vec, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(GEMM_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+  return GEMM_OK;
+}
+
+}  // namespace
+}  // namespace gemm
+
+using namespace gemm;
+
+extern "C" {
+
+gemm_status_t gemm_f32(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
+                       const float* B, int64_t ldb, float* C, int64_t ldc, void* stream) {
+  return run(GEMM_DTYPE_F32, M, N, K, A, lda, B, ldb, C, ldc, stream, nullptr);
+}
+
+gemm_status_t gemm_f16(int64_t M, int64_t N, int64_t K, const gemm_f16_t* A, int64_t lda,
+                       const gemm_f16_t* B, int64_t ldb, gemm_f16_t* C, int64_t ldc,
+                       void* stream) {
+  return run(GEMM_DTYPE_F16, M, N, K, A, lda, B, ldb, C, ldc, stream, nullptr);
+}
+
+gemm_status_t gemm_f32_ex(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
+                          const float* B, int64_t ldb, float* C, int64_t ldc, void* stream,
+                          const gemm_config_t* cfg) {
+  if (!cfg) return fail(GEMM_ERR_INVALID_ARG, "cfg is NULL");
+  return run(GEMM_DTYPE_F32, M, N, K, A, lda, B, ldb, C, ldc, stream, cfg);
+}
+
+gemm_status_t gemm_f16_ex(int64_t M, int64_t N, int64_t K, const gemm_f16_t* A, int64_t lda,
+                          const gemm_f16_t* B, int64_t ldb, gemm_f16_t* C, int64_t ldc,
+                          void* stream, const gemm_config_t* cfg) {
+  if (!cfg) return fail(GEMM_ERR_INVALID_ARG, "cfg is NULL");
+  return run(GEMM_DTYPE_F16, M, N, K, A, lda, B, ldb, C, ldc, stream, cfg);
+}
+
+int32_t gemm_num_configs(int32_t dtype) {
+  if (dtype != GEMM_DTYPE_F32 && dtype != GEMM_DTYPE_F16) return 0;
+  return (int32_t)table().v[dtype].size();
+}
+
+gemm_status_t gemm_get_config(int32_t dtype, int32_t idx, gemm_config_t* out) {
+  if (dtype != GEMM_DTYPE_F32 && dtype != GEMM_DTYPE_F16)
+    return fail(GEMM_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  if (!out) return fail(GEMM_ERR_INVALID_ARG, "out is NULL");
+  const auto& v = table().v[dtype];
+  if (idx < 0 || idx >= (int32_t)v.size()) return fail(GEMM_ERR_INVALID_ARG, "index out of range");
+  *out = v[idx].desc;
+  return GEMM_OK;
+}
+
+gemm_status_t gemm_select_config(int32_t dtype, int64_t M, int64_t N, int64_t K,
+                                 gemm_config_t* out) {
+  if (dtype != GEMM_DTYPE_F32 && dtype != GEMM_DTYPE_F16)
+    return fail(GEMM_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  if (!out || M < 0 || N < 0 || K < 0) return fail(GEMM_ERR_INVALID_ARG, "bad arguments");
+  *out = select(dtype, M, N, K);
+  return GEMM_OK;
+}
+
+gemm_status_t gemm_tile_of_block(const gemm_config_t* cfg, int64_t M, int64_t N, int64_t block,
+                                 int64_t* tile_m, int64_t* tile_n) {
+  if (!cfg || !tile_m || !tile_n || M <= 0 || N <= 0 || cfg->bm <= 0 || cfg->bn <= 0)
+    return fail(GEMM_ERR_INVALID_ARG, "bad arguments");
+  const TileMap map = make_map(*cfg, M, N);
+  if (block < 0 || block >= (int64_t)map.tiles_m * map.tiles_n)
+    return fail(GEMM_ERR_INVALID_ARG, "block out of range");
+  int tm, tn;
+  tile_of_block((int)block, map, tm, tn);
+  *tile_m = tm;
+  *tile_n = tn;
+  return GEMM_OK;
+}
+
+gemm_status_t gemm_layout_check(int32_t dtype, int32_t idx, int32_t banks, int64_t out[2]) {
+  if (dtype != GEMM_DTYPE_F32 && dtype != GEMM_DTYPE_F16)
+    return fail(GEMM_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  const auto& v = table().v[dtype];
+  if (idx < 0 || idx >= (int32_t)v.size() || !out || banks <= 0 || banks > 64 || (banks & (banks - 1)))
+    return fail(GEMM_ERR_INVALID_ARG, "bad arguments");
+  const int rc = v[idx].layout_check(banks, out);
+  if (rc != 0) return fail(GEMM_ERR_UNSUPPORTED, "layout check %s failed with code %d", v[idx].desc.name, rc);
+  return GEMM_OK;
+}
+
+gemm_status_t gemm_load_tuning(const char* path) {
+  std::vector<TuneEntry> entries;
+  if (path) {
+    FILE* f = fopen(path, "r");
+    if (!f) return fail(GEMM_ERR_INVALID_ARG, "cannot open %s", path);
+    char line[512];
+    int lineno = 0;
+    while (fgets(line, sizeof line, f)) {
+      ++lineno;
+      if (line[0] == '#' || line[0] == '\n') continue;
+      char dt[16], name[64];
+      long long M, N, K;
+      int order, gm;
+      if (sscanf(line, "%15s %lld %lld %lld %63s %d %d", dt, &M, &N, &K, name, &order, &gm) != 7) {
+        fclose(f);
+        return fail(GEMM_ERR_INVALID_ARG, "%s:%d: expected 'dtype M N K name order group_m'", path, lineno);
+      }
+      const int dtype = strcmp(dt, "f32") == 0 ? 0 : strcmp(dt, "f16") == 0 ? 1 : -1;
+      const int id = dtype < 0 ? -1 : find_by_name(dtype, name);
+      if (id < 0 || order < GEMM_ORDER_ROW || order > GEMM_ORDER_XCD || gm < 1) {
+        fclose(f);
+        return fail(GEMM_ERR_INVALID_ARG, "%s:%d: unknown dtype/variant or bad order", path, lineno);
+      }
+      entries.push_back(TuneEntry{dtype, M, N, K, id, order, gm});
+    }
+    fclose(f);
+  }
+  std::lock_guard<std::mutex> lk(g_tuning_mu);
+  g_tuning.swap(entries);
+  return GEMM_OK;
+}
+
+const char* gemm_status_string(gemm_status_t s) {
+  switch (s) {
+    case GEMM_OK: return "GEMM_OK";
+    case GEMM_ERR_INVALID_ARG: return "GEMM_ERR_INVALID_ARG";
+    case GEMM_ERR_UNSUPPORTED: return "GEMM_ERR_UNSUPPORTED";
+    case GEMM_ERR_HIP: return "GEMM_ERR_HIP";
+    case GEMM_ERR_ALIAS: return "GEMM_ERR_ALIAS";
+  }
+  return "unknown gemm_status_t";
+}
+
+const char* gemm_last_error(void) { return g_err; }
+
+const char* gemm_version(void) { return "libgemm 0.1.0 (gfx950)"; }
+
+}  // extern "C"

@@ -1,0 +1,141 @@
+// Internal declarations shared by the libgemm kernels and the C-ABI layer.
+//
+// Everything in this header is either plain data passed to kernels or an
+// integer index map marked __host__ __device__, so that the host-side checks
+// (tile map bijection, LDS layout bijection and bank-conflict counts) run the
+// very functions the kernels run.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gemm.h"
+
+namespace gemm {
+
+// ---------------------------------------------------------------------------
+// Kernel arguments.
+// ---------------------------------------------------------------------------
+struct Params {
+  const void* A;
+  const void* B;
+  void* C;
+  int64_t lda, ldb, ldc;
+  int M, N, K;
+};
+
+// Workgroup -> output tile order.  See gemm_order_t in gemm.h.
+struct TileMap {
+  int tiles_m, tiles_n;
+  int order;    // gemm_order_t
+  int group_m;  // band height for GROUPED / XCD
+  int xcds;     // number of XCDs the dispatcher deals workgroups over
+};
+
+// Number of XCDs on MI355X; the command processor hands consecutive
+// workgroup ids of a dispatch to the XCDs in round-robin order.
+constexpr int kXcds = 8;
+
+// Tile computed by workgroup `b`.  A bijection from [0, tiles_m*tiles_n)
+// onto the tile grid for every order (checked on the host for every
+// variant and shape in the tests).
+__host__ __device__ inline void tile_of_block(int b, const TileMap& t, int& tm, int& tn) {
+  const int G = t.tiles_m * t.tiles_n;
+  if (t.order == GEMM_ORDER_ROW) {
+    tm = b / t.tiles_n;
+    tn = b - tm * t.tiles_n;
+    return;
+  }
+  int bb = b;
+  if (t.order == GEMM_ORDER_XCD && t.xcds > 1) {
+    // Workgroup b runs on XCD x = b % xcds as that XCD's (b / xcds)-th
+    // workgroup.  XCD x owns q + (x < r) workgroups (q = G / xcds,
+    // r = G % xcds); give it the contiguous run of linear tile ids starting
+    // at x*q + min(x, r) so that its workgroups share operand panels in
+    // that XCD's L2.
+    const int x = b % t.xcds;
+    const int q = G / t.xcds, r = G % t.xcds;
+    bb = x * q + (x < r ? x : r) + b / t.xcds;
+  }
+  const int gm = t.group_m < 1 ? 1 : t.group_m;
+  const int width = gm * t.tiles_n;  // tiles in one band
+  const int band = bb / width;
+  const int first_m = band * gm;
+  const int rows = (t.tiles_m - first_m) < gm ? (t.tiles_m - first_m) : gm;
+  const int in = bb - band * width;
+  tm = first_m + in % rows;
+  tn = in / rows;
+}
+
+// ---------------------------------------------------------------------------
+// LDS model used by the layout derivations (measured on gfx950): 64 banks of
+// 4 bytes.  A wave's ds_read/ds_write of W bytes per lane is serviced in
+// groups of 256/W consecutive lanes (16 lanes for 16-byte accesses); an
+// access group is conflict-free when its lanes touch distinct banks (equal
+// addresses broadcast).
+// ---------------------------------------------------------------------------
+constexpr int kLdsBanks = 64;
+
+// XOR swizzle for a row-major LDS tile whose rows are `row_bytes` long and
+// are read or written in 16-byte chunks.  Chunk q of row r is stored at
+// chunk position q ^ swz_row(r).  With R = 256 / row_bytes rows per 256-byte
+// bank line and CPR = row_bytes / 16 chunks per row, swz_row(r) =
+// (r / R) % CPR makes
+//   * 16 consecutive rows read at one chunk index land on 16 distinct
+//     16-byte bank slots (fragment reads), and
+//   * one row written chunk by chunk by consecutive lanes stays a
+//     permutation of its own slots (staging writes),
+// which is the wave64 / 64-bank re-derivation of the column XOR used for
+// the transposed A tile in "sgemm - beyond cuBLAS" (section 4).
+__host__ __device__ constexpr int swz_row(int r, int row_bytes) {
+  return row_bytes >= 256 ? (r % (row_bytes / 16))
+                          : ((r / (256 / row_bytes)) % (row_bytes / 16));
+}
+
+// Byte offset of 16-byte chunk q of row r in a swizzled tile.
+__host__ __device__ constexpr int swz_off(int r, int q, int row_bytes) {
+  return r * row_bytes + 16 * (q ^ swz_row(r, row_bytes));
+}
+
+// FP16 B tile (stored transposed, one LDS row per output column): the LDS
+// row that holds tile column n.  Columns are interleaved so that, for a
+// wave tile of WN columns split into NB = WN/32 MFMA blocks, block nb's lane
+// i owns column NB*i + nb (the epilogue then writes NB adjacent columns per
+// lane); sigma flips the row parity between neighbouring 8-column staging
+// blocks so that two such blocks written by one 16-lane group use different
+// halves of the 256-byte bank line.
+__host__ __device__ constexpr int log2i(int v) { return v <= 1 ? 0 : 1 + log2i(v / 2); }
+
+__host__ __device__ constexpr int bt_sigma(int i, int NB) {
+  return i ^ ((i >> (3 - log2i(NB))) & 1);
+}
+
+__host__ __device__ constexpr int bt_row(int n, int WN) {
+  const int NB = WN / 32;
+  const int wn = n / WN, np = n % WN;
+  return wn * WN + 32 * (np % NB) + bt_sigma(np / NB, NB);
+}
+
+// ---------------------------------------------------------------------------
+// Variant table.
+// ---------------------------------------------------------------------------
+using LaunchFn = hipError_t (*)(const Params&, const TileMap&, bool vec, hipStream_t);
+using LayoutFn = int (*)(int banks, int64_t out[2]);
+
+struct Variant {
+  gemm_config_t desc;  // id / order / group_m are defaults, filled at init
+  LaunchFn launch;
+  LayoutFn layout_check;
+};
+
+// Per-family registration (each kernel file defines its table).
+const Variant* sgemm_mfma_variants(int* count);
+const Variant* sgemm_simt_variants(int* count);
+const Variant* hgemm_mfma_variants(int* count);
+
+// Host bank-conflict accounting for one wave-wide LDS access: `addr[64]`
+// byte addresses of `width` bytes each.  Returns the extra passes over the
+// conflict-free minimum.
+int lds_conflicts(const int* addr, int width, int banks);
+
+}  // namespace gemm

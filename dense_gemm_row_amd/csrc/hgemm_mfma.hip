@@ -1,0 +1,369 @@
+// FP16 HGEMM on the gfx950 matrix cores: C = A x B with binary16 inputs,
+// FP32 accumulation and one round-to-nearest-even conversion per output.
+// (The HGEMM of "hgemm_naive_kernel explained", whose kernels accumulate in
+// FP16; here the accumulator is FP32.)
+//
+// * v_mfma_f32_32x32x16_f16 lane maps (checked on the device): lane l
+//   supplies A[l%32][8*(l/32) .. +7] and B[8*(l/32) .. +7][l%32], eight
+//   consecutive k per lane; accumulator register r of lane l holds row
+//   8*(r/4) + 4*(l/32) + r%4, column l%32.
+// * Both operands must therefore be K-contiguous per lane.  A is (row-major
+//   A has k contiguous): its LDS tile is BM rows of BK = 64 halves (128
+//   bytes) and a lane's fragment is one 16-byte read.  B is row-major with n
+//   contiguous, so the staging step transposes it: each thread loads an
+//   8 (k) x 8 (n) block with eight 16-byte loads, transposes it in
+//   registers with byte permutes, and writes eight 16-byte rows of the
+//   transposed LDS tile (one LDS row per output column).  This is the
+//   transposed-operand idea of "sgemm - beyond cuBLAS" (section 3) and of
+//   the s_a[BK][BM] tile in "hgemm_naive_kernel explained" (section 7.1),
+//   applied to the operand that the matrix core needs transposed.
+// * LDS rows use the chunk XOR swizzle swz_row (128-byte rows), and the B
+//   rows are permuted by bt_row (column interleave + parity flip), which
+//   keeps the staging writes and fragment reads conflict-free in 16-lane
+//   groups over 64 banks.
+// * Column interleave as in the FP32 kernel: block nb of a wave tile covers
+//   columns wn0 + NB*j + nb, so each lane stores NB adjacent FP16 outputs
+//   (2*NB bytes) per row, 32 lanes writing 64*NB contiguous bytes.
+// * Two LDS stages, global loads of slice t+1 in flight while slice t feeds
+//   the MFMAs, one barrier per slice (the double buffer of section 8 of the
+//   HGEMM article, with the buffer index computed, not fixed).
+// * VEC=true: A, B, C 16-byte aligned and K, N, lda, ldb, ldc multiples of
+//   8 (whole 16-byte chunks in or out of range).  VEC=false: element loads
+//   and stores with per-element masks.
+#include "gemm_internal.h"
+
+namespace gemm {
+namespace {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int BK = 64;         // halves per K slice
+constexpr int ROW_BYTES = 128; // one LDS row = BK halves
+
+template <int BM, int BN, int WM, int WN>
+struct Shape {
+  static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
+  static constexpr int NT = WAVES_M * WAVES_N * 64;
+  static constexpr int MB = WM / 32, NB = WN / 32;
+  static constexpr int A_CHUNKS = BM * (BK / 8);      // 16-byte chunks
+  static constexpr int B_BLOCKS = (BK / 8) * (BN / 8); // 8x8 blocks
+  static constexpr int CA = A_CHUNKS / NT;
+  static constexpr int CB = (B_BLOCKS + NT - 1) / NT;
+  static constexpr int A_STAGE = BM * ROW_BYTES, B_STAGE = BN * ROW_BYTES;  // bytes
+  static constexpr int STAGE = A_STAGE + B_STAGE;
+  static constexpr int LDS_BYTES = 2 * STAGE;
+  static_assert(BM % WM == 0 && BN % WN == 0, "wave grid");
+  static_assert(WM % 32 == 0 && (NB == 1 || NB == 2 || NB == 4), "wave tile");
+  static_assert(A_CHUNKS % NT == 0, "A staging split");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS");
+
+  // A chunk q (8 halves) of tile row r.
+  __host__ __device__ static constexpr int a_chunk(int r, int q) { return swz_off(r, q, ROW_BYTES); }
+  // Transposed B: k-chunk q of tile column n.
+  __host__ __device__ static constexpr int b_chunk(int n, int q) {
+    return A_STAGE + swz_off(bt_row(n, WN), q, ROW_BYTES);
+  }
+  // Fragment reads: A row r, B LDS row for (wave column origin wn0, block nb,
+  // lane row j), both at k-chunk q.
+  __host__ __device__ static constexpr int b_frag(int wn0, int nb, int j, int q) {
+    return A_STAGE + swz_off(wn0 + 32 * nb + bt_sigma(j, NB), q, ROW_BYTES);
+  }
+};
+
+__device__ inline f32x16 mfma(f16x8 a, f16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ inline unsigned short f16_bits(float x) {
+  // v_cvt_f16_f32: round to nearest even (checked on the device).
+  return __builtin_bit_cast(unsigned short, static_cast<_Float16>(x));
+}
+
+template <int BM, int BN, int WM, int WN, bool VEC>
+__global__ void __launch_bounds__((Shape<BM, BN, WM, WN>::NT))
+hgemm_mfma_kernel(Params p, TileMap map) {
+  using S = Shape<BM, BN, WM, WN>;
+  constexpr int NT = S::NT, MB = S::MB, NB = S::NB, CA = S::CA, CB = S::CB;
+
+  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * S::STAGE];
+
+  int tm, tn;
+  tile_of_block(blockIdx.x, map, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int M = p.M, N = p.N, K = p.K;
+  const unsigned short* __restrict__ A = static_cast<const unsigned short*>(p.A);
+  const unsigned short* __restrict__ B = static_cast<const unsigned short*>(p.B);
+  unsigned short* __restrict__ C = static_cast<unsigned short*>(p.C);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int lrow = lane & 31, h = lane >> 5;
+  const int wm0 = (wave / S::WAVES_N) * WM, wn0 = (wave % S::WAVES_N) * WN;
+
+  // A staging: chunk (row r, k-chunk q) per slot.
+  const unsigned short* a_src[CA];
+  bool a_row_ok[CA];
+  int a_k[CA], a_dst[CA];
+#pragma unroll
+  for (int i = 0; i < CA; ++i) {
+    const int id = tid + i * NT;
+    const int r = id / (BK / 8), q = id % (BK / 8);
+    a_row_ok[i] = (m0 + r) < M;
+    a_src[i] = A + (int64_t)(a_row_ok[i] ? m0 + r : 0) * p.lda + 8 * q;
+    a_k[i] = 8 * q;
+    a_dst[i] = S::a_chunk(r, q);
+  }
+  // B staging: 8x8 block (k-group r, column chunk c) per slot.
+  const unsigned short* b_src[CB];
+  bool b_on[CB];
+  int b_k[CB], b_col[CB], b_c[CB], b_r[CB];
+#pragma unroll
+  for (int i = 0; i < CB; ++i) {
+    const int id = tid + i * NT;
+    b_on[i] = id < S::B_BLOCKS;
+    const int r = id % (BK / 8), c = id / (BK / 8);
+    b_r[i] = r;
+    b_c[i] = c;
+    b_k[i] = 8 * r;
+    b_col[i] = n0 + 8 * c;
+    b_src[i] = B + (int64_t)(8 * r) * p.ldb + (b_col[i] < N ? b_col[i] : 0);
+  }
+
+  u32x4 ra[CA];
+  u32x4 rb[CB][8];
+
+  auto load_slice = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < CA; ++i) {
+      const int kg = k0 + a_k[i];
+      if (VEC) {
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (a_row_ok[i] && kg < K) v = *reinterpret_cast<const u32x4*>(a_src[i] + k0);
+        ra[i] = v;
+      } else {
+        unsigned short e[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) e[t] = (a_row_ok[i] && kg + t < K) ? a_src[i][k0 + t] : 0;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) ra[i][d] = e[2 * d] | ((unsigned)e[2 * d + 1] << 16);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < CB; ++i) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int kg = k0 + b_k[i] + e;
+        const unsigned short* src = b_src[i] + (int64_t)(k0 + e) * p.ldb;
+        if (VEC) {
+          u32x4 v = {0u, 0u, 0u, 0u};
+          if (b_on[i] && kg < K && b_col[i] < N) v = *reinterpret_cast<const u32x4*>(src);
+          rb[i][e] = v;
+        } else {
+          unsigned short x[8];
+#pragma unroll
+          for (int t = 0; t < 8; ++t) x[t] = (b_on[i] && kg < K && b_col[i] + t < N) ? src[t] : 0;
+#pragma unroll
+          for (int d = 0; d < 4; ++d) rb[i][e][d] = x[2 * d] | ((unsigned)x[2 * d + 1] << 16);
+        }
+      }
+    }
+  };
+
+  auto store_slice = [&](int stage) {
+    unsigned char* base = smem + stage * S::STAGE;
+#pragma unroll
+    for (int i = 0; i < CA; ++i) *reinterpret_cast<u32x4*>(base + a_dst[i]) = ra[i];
+#pragma unroll
+    for (int i = 0; i < CB; ++i) {
+      if (!b_on[i]) continue;
+      // rb[i][e] holds row k = 8r+e, columns 8c..8c+7 as 4 dwords of 2
+      // halves.  Column j of the transposed block: dword d gathers rows
+      // 2d (low half) and 2d+1 (high half) of column j.
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const unsigned sel = (j & 1) ? 0x07060302u : 0x05040100u;
+        u32x4 t;
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+          t[d] = __builtin_amdgcn_perm(rb[i][2 * d + 1][j >> 1], rb[i][2 * d][j >> 1], sel);
+        *reinterpret_cast<u32x4*>(base + S::b_chunk(8 * b_c[i] + j, b_r[i])) = t;
+      }
+    }
+  };
+
+  f32x16 acc[MB][NB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[mb][nb][r] = 0.f;
+
+  const int T = (K + BK - 1) / BK;
+  if (T > 0) {
+    load_slice(0);
+    store_slice(0);
+    __syncthreads();
+    for (int t = 0; t < T; ++t) {
+      const int cur = t & 1;
+      if (t + 1 < T) load_slice((t + 1) * BK);
+      const unsigned char* base = smem + cur * S::STAGE;
+#pragma unroll
+      for (int kk = 0; kk < BK; kk += 16) {
+        const int q = kk / 8 + h;
+        f16x8 a[MB], b[NB];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+          a[mb] = *reinterpret_cast<const f16x8*>(base + S::a_chunk(wm0 + 32 * mb + lrow, q));
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+          b[nb] = *reinterpret_cast<const f16x8*>(base + S::b_frag(wn0, nb, lrow, q));
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = mfma(a[mb], b[nb], acc[mb][nb]);
+      }
+      if (t + 1 < T) store_slice(cur ^ 1);
+      __syncthreads();
+    }
+  }
+
+  // Epilogue: FP32 -> FP16 (RNE), NB adjacent columns per lane and row.
+  const int col = n0 + wn0 + NB * lrow;
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = m0 + wm0 + 32 * mb + 8 * (r / 4) + 4 * h + (r % 4);
+      if (row >= M) continue;
+      unsigned short* dst = C + (int64_t)row * p.ldc + col;
+      if (VEC) {
+        if (col < N) {
+          if constexpr (NB == 4) {
+            uint2 v;
+            v.x = f16_bits(acc[mb][0][r]) | ((unsigned)f16_bits(acc[mb][1][r]) << 16);
+            v.y = f16_bits(acc[mb][2][r]) | ((unsigned)f16_bits(acc[mb][3][r]) << 16);
+            *reinterpret_cast<uint2*>(dst) = v;
+          } else if constexpr (NB == 2) {
+            *reinterpret_cast<unsigned*>(dst) =
+                f16_bits(acc[mb][0][r]) | ((unsigned)f16_bits(acc[mb][1][r]) << 16);
+          } else {
+            *dst = f16_bits(acc[mb][0][r]);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+          if (col + nb < N) dst[nb] = f16_bits(acc[mb][nb][r]);
+      }
+    }
+  }
+}
+
+template <int BM, int BN, int WM, int WN>
+hipError_t launch(const Params& p, const TileMap& map, bool vec, hipStream_t stream) {
+  using S = Shape<BM, BN, WM, WN>;
+  const dim3 grid(map.tiles_m * map.tiles_n), block(S::NT);
+  if (vec)
+    hipLaunchKernelGGL((hgemm_mfma_kernel<BM, BN, WM, WN, true>), grid, block, 0, stream, p, map);
+  else
+    hipLaunchKernelGGL((hgemm_mfma_kernel<BM, BN, WM, WN, false>), grid, block, 0, stream, p, map);
+  return hipGetLastError();
+}
+
+// Host replay of one K slice's LDS accesses (see the FP32 kernel).
+template <int BM, int BN, int WM, int WN>
+int layout_check(int banks, int64_t out[2]) {
+  using S = Shape<BM, BN, WM, WN>;
+  int64_t wconf = 0, rconf = 0;
+  static unsigned char cover[S::STAGE];
+  for (int i = 0; i < S::STAGE; ++i) cover[i] = 0;
+  int addr[64];
+  for (int i = 0; i < S::CA; ++i)
+    for (int w = 0; w < S::NT / 64; ++w) {
+      for (int l = 0; l < 64; ++l) {
+        const int id = w * 64 + l + i * S::NT;
+        const int off = S::a_chunk(id / (BK / 8), id % (BK / 8));
+        if (off < 0 || off + 16 > S::A_STAGE) return 1;
+        for (int b = 0; b < 16; ++b) cover[off + b]++;
+        addr[l] = off;
+      }
+      wconf += lds_conflicts(addr, 16, banks);
+    }
+  for (int i = 0; i < S::CB; ++i)
+    for (int w = 0; w < S::NT / 64; ++w) {
+      for (int j = 0; j < 8; ++j) {
+        int active = 0;
+        for (int l = 0; l < 64; ++l) {
+          const int id = w * 64 + l + i * S::NT;
+          if (id >= S::B_BLOCKS) { addr[l] = -1; continue; }
+          ++active;
+          const int r = id % (BK / 8), c = id / (BK / 8);
+          const int off = S::b_chunk(8 * c + j, r);
+          if (off < S::A_STAGE || off + 16 > S::STAGE) return 2;
+          for (int b = 0; b < 16; ++b) cover[off + b]++;
+          addr[l] = off;
+        }
+        if (active) wconf += lds_conflicts(addr, 16, banks);
+      }
+    }
+  for (int i = 0; i < S::STAGE; ++i)
+    if (cover[i] != 1) return 3;
+  for (int w = 0; w < S::NT / 64; ++w) {
+    const int wm0 = (w / S::WAVES_N) * WM, wn0 = (w % S::WAVES_N) * WN;
+    for (int kk = 0; kk < BK; kk += 16) {
+      for (int mb = 0; mb < S::MB; ++mb) {
+        for (int l = 0; l < 64; ++l) {
+          const int off = S::a_chunk(wm0 + 32 * mb + (l & 31), kk / 8 + (l >> 5));
+          if (off < 0 || off + 16 > S::A_STAGE) return 4;
+          addr[l] = off;
+        }
+        rconf += lds_conflicts(addr, 16, banks);
+      }
+      for (int nb = 0; nb < S::NB; ++nb) {
+        for (int l = 0; l < 64; ++l) {
+          const int off = S::b_frag(wn0, nb, l & 31, kk / 8 + (l >> 5));
+          if (off < S::A_STAGE || off + 16 > S::STAGE) return 5;
+          addr[l] = off;
+        }
+        rconf += lds_conflicts(addr, 16, banks);
+      }
+    }
+  }
+  // The fragment read of (wn0, nb, j) must be the row the staging wrote for
+  // the column the epilogue assigns to that lane: wn0 + NB*j + nb.
+  for (int n = 0; n < BN; ++n) {
+    const int wn0 = (n / WN) * WN, np = n % WN;
+    if (S::b_frag(wn0, np % S::NB, np / S::NB, 0) != S::b_chunk(n, 0)) return 6;
+  }
+  out[0] = wconf;
+  out[1] = rconf;
+  return 0;
+}
+
+#define HGEMM_MFMA_VARIANT(BM, BN, WM, WN)                                                   \
+  Variant {                                                                                  \
+    gemm_config_t{0, GEMM_DTYPE_F16, GEMM_FAMILY_MFMA, BM, BN, BK, WM, WN,                   \
+                  Shape<BM, BN, WM, WN>::NT, 2, Shape<BM, BN, WM, WN>::LDS_BYTES,            \
+                  GEMM_ORDER_XCD, 4, "mfma_f16_" #BM "x" #BN "x64_w" #WM "x" #WN},           \
+        &launch<BM, BN, WM, WN>, &layout_check<BM, BN, WM, WN>                               \
+  }
+
+const Variant kVariants[] = {
+    HGEMM_MFMA_VARIANT(256, 256, 128, 128),
+    HGEMM_MFMA_VARIANT(256, 128, 128, 64),
+    HGEMM_MFMA_VARIANT(128, 256, 64, 128),
+    HGEMM_MFMA_VARIANT(128, 128, 64, 64),
+    HGEMM_MFMA_VARIANT(64, 64, 32, 32),
+};
+
+}  // namespace
+
+const Variant* hgemm_mfma_variants(int* count) {
+  *count = sizeof(kVariants) / sizeof(kVariants[0]);
+  return kVariants;
+}
+
+}  // namespace gemm

@@ -1,0 +1,241 @@
+"""ctypes binding of libgemm (include/gemm.h).
+
+The functions carry the C names and only marshal arguments: every step of
+the GEMM runs in the HIP kernels of ``libgemm.so``.  There is no fallback:
+if the library is missing, loading raises.
+
+``matmul`` is a convenience for torch tensors on the GPU: it reads shapes,
+strides, data pointers and the current stream and calls ``gemm_f32`` /
+``gemm_f16`` (or the ``_ex`` forms).  Torch provides memory and streams
+only.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libgemm.so")
+
+GEMM_OK = 0
+GEMM_ERR_INVALID_ARG = -1
+GEMM_ERR_UNSUPPORTED = -2
+GEMM_ERR_HIP = -3
+GEMM_ERR_ALIAS = -4
+
+DTYPE_F32 = 0
+DTYPE_F16 = 1
+FAMILY_MFMA = 0
+FAMILY_SIMT = 1
+ORDER_ROW = 0
+ORDER_GROUPED = 1
+ORDER_XCD = 2
+
+EXPORTS = ["gemm_f32", "gemm_f16", "gemm_f32_ex", "gemm_f16_ex", "gemm_num_configs",
+           "gemm_get_config", "gemm_select_config", "gemm_tile_of_block",
+           "gemm_layout_check", "gemm_load_tuning", "gemm_status_string",
+           "gemm_last_error", "gemm_version"]
+
+
+class GemmConfig(ctypes.Structure):
+    _fields_ = [("id", ctypes.c_int32), ("dtype", ctypes.c_int32), ("family", ctypes.c_int32),
+                ("bm", ctypes.c_int32), ("bn", ctypes.c_int32), ("bk", ctypes.c_int32),
+                ("wm", ctypes.c_int32), ("wn", ctypes.c_int32), ("threads", ctypes.c_int32),
+                ("stages", ctypes.c_int32), ("lds_bytes", ctypes.c_int32),
+                ("order", ctypes.c_int32), ("group_m", ctypes.c_int32),
+                ("name", ctypes.c_char * 48)]
+
+    def as_dict(self) -> dict:
+        d = {f: getattr(self, f) for f, _ in self._fields_}
+        d["name"] = self.name.decode()
+        return d
+
+    def __repr__(self) -> str:  # pragma: no cover
+        return f"GemmConfig({self.as_dict()})"
+
+
+class GemmError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = gemm_status_string(status)
+        detail = gemm_last_error()
+        super().__init__(f"{where}: {msg}" + (f" ({detail})" if detail else ""))
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def _declare(lib):
+    i64, i32, p = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
+    cfgp = ctypes.POINTER(GemmConfig)
+    gemm_args = [i64, i64, i64, p, i64, p, i64, p, i64, p]
+    for name in ("gemm_f32", "gemm_f16"):
+        getattr(lib, name).argtypes = gemm_args
+        getattr(lib, name).restype = ctypes.c_int
+    for name in ("gemm_f32_ex", "gemm_f16_ex"):
+        getattr(lib, name).argtypes = gemm_args + [cfgp]
+        getattr(lib, name).restype = ctypes.c_int
+    lib.gemm_num_configs.argtypes = [i32]
+    lib.gemm_num_configs.restype = i32
+    lib.gemm_get_config.argtypes = [i32, i32, cfgp]
+    lib.gemm_get_config.restype = ctypes.c_int
+    lib.gemm_select_config.argtypes = [i32, i64, i64, i64, cfgp]
+    lib.gemm_select_config.restype = ctypes.c_int
+    lib.gemm_tile_of_block.argtypes = [cfgp, i64, i64, i64, ctypes.POINTER(i64), ctypes.POINTER(i64)]
+    lib.gemm_tile_of_block.restype = ctypes.c_int
+    lib.gemm_layout_check.argtypes = [i32, i32, i32, ctypes.POINTER(i64)]
+    lib.gemm_layout_check.restype = ctypes.c_int
+    lib.gemm_load_tuning.argtypes = [ctypes.c_char_p]
+    lib.gemm_load_tuning.restype = ctypes.c_int
+    lib.gemm_status_string.argtypes = [ctypes.c_int]
+    lib.gemm_status_string.restype = ctypes.c_char_p
+    lib.gemm_last_error.argtypes = []
+    lib.gemm_last_error.restype = ctypes.c_char_p
+    lib.gemm_version.argtypes = []
+    lib.gemm_version.restype = ctypes.c_char_p
+    return lib
+
+
+def lib():
+    """The loaded libgemm (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        with _lock:
+            if _lib is None:
+                if not os.path.exists(LIB_PATH):
+                    raise ImportError(
+                        f"{LIB_PATH} is missing: build it with "
+                        "`python -m dense_gemm_row_amd.build` (needs hipcc)")
+                _lib = _declare(ctypes.CDLL(LIB_PATH))
+    return _lib
+
+
+# --------------------------------------------------------------------------
+# The C entry points, one Python function each.
+# --------------------------------------------------------------------------
+def gemm_f32(M, N, K, A, lda, B, ldb, C, ldc, stream=None) -> int:
+    return lib().gemm_f32(M, N, K, A, lda, B, ldb, C, ldc, stream)
+
+
+def gemm_f16(M, N, K, A, lda, B, ldb, C, ldc, stream=None) -> int:
+    return lib().gemm_f16(M, N, K, A, lda, B, ldb, C, ldc, stream)
+
+
+def gemm_f32_ex(M, N, K, A, lda, B, ldb, C, ldc, stream, cfg: GemmConfig) -> int:
+    return lib().gemm_f32_ex(M, N, K, A, lda, B, ldb, C, ldc, stream,
+                             ctypes.byref(cfg) if cfg is not None else None)
+
+
+def gemm_f16_ex(M, N, K, A, lda, B, ldb, C, ldc, stream, cfg: GemmConfig) -> int:
+    return lib().gemm_f16_ex(M, N, K, A, lda, B, ldb, C, ldc, stream,
+                             ctypes.byref(cfg) if cfg is not None else None)
+
+
+def gemm_num_configs(dtype: int) -> int:
+    return lib().gemm_num_configs(dtype)
+
+
+def gemm_get_config(dtype: int, idx: int) -> GemmConfig:
+    out = GemmConfig()
+    st = lib().gemm_get_config(dtype, idx, ctypes.byref(out))
+    if st != GEMM_OK:
+        raise GemmError(st, "gemm_get_config")
+    return out
+
+
+def gemm_select_config(dtype: int, M: int, N: int, K: int) -> GemmConfig:
+    out = GemmConfig()
+    st = lib().gemm_select_config(dtype, M, N, K, ctypes.byref(out))
+    if st != GEMM_OK:
+        raise GemmError(st, "gemm_select_config")
+    return out
+
+
+def gemm_tile_of_block(cfg: GemmConfig, M: int, N: int, block: int) -> tuple[int, int]:
+    tm, tn = ctypes.c_int64(), ctypes.c_int64()
+    st = lib().gemm_tile_of_block(ctypes.byref(cfg), M, N, block, ctypes.byref(tm), ctypes.byref(tn))
+    if st != GEMM_OK:
+        raise GemmError(st, "gemm_tile_of_block")
+    return tm.value, tn.value
+
+
+def gemm_layout_check(dtype: int, idx: int, banks: int = 64) -> tuple[int, int]:
+    out = (ctypes.c_int64 * 2)()
+    st = lib().gemm_layout_check(dtype, idx, banks, out)
+    if st != GEMM_OK:
+        raise GemmError(st, "gemm_layout_check")
+    return out[0], out[1]
+
+
+def gemm_load_tuning(path: str | None) -> int:
+    return lib().gemm_load_tuning(path.encode() if path else None)
+
+
+def gemm_status_string(status: int) -> str:
+    return lib().gemm_status_string(status).decode()
+
+
+def gemm_last_error() -> str:
+    return lib().gemm_last_error().decode()
+
+
+def gemm_version() -> str:
+    return lib().gemm_version().decode()
+
+
+def configs(dtype: int) -> list[GemmConfig]:
+    return [gemm_get_config(dtype, i) for i in range(gemm_num_configs(dtype))]
+
+
+def config_by_name(dtype: int, name: str, order: int | None = None,
+                   group_m: int | None = None) -> GemmConfig:
+    for c in configs(dtype):
+        if c.name.decode() == name:
+            if order is not None:
+                c.order = order
+            if group_m is not None:
+                c.group_m = group_m
+            return c
+    raise KeyError(name)
+
+
+# --------------------------------------------------------------------------
+# Torch convenience: shapes, strides, pointers and the current stream.
+# --------------------------------------------------------------------------
+def _ld(t) -> int:
+    if t.dim() != 2:
+        raise ValueError("expected a 2-D tensor")
+    if t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError("rows must be contiguous (unit column stride)")
+    return max(int(t.stride(0)), 1) if t.shape[0] > 1 else max(int(t.shape[1]), 1)
+
+
+def matmul(a, b, out=None, config: GemmConfig | None = None, stream=None):
+    """C = a @ b on the GPU through libgemm.  a: M x K, b: K x N, both
+    float32 or both float16, row-major (any row stride).  Returns ``out``
+    (allocated when None).  Raises GemmError on a non-OK status."""
+    import torch
+    if a.dtype != b.dtype or a.dtype not in (torch.float32, torch.float16):
+        raise TypeError("a and b must both be float32 or both float16")
+    if not (a.is_cuda and b.is_cuda):
+        raise ValueError("a and b must be GPU tensors")
+    M, K = a.shape
+    K2, N = b.shape
+    if K2 != K:
+        raise ValueError(f"inner dimensions differ: {K} vs {K2}")
+    if out is None:
+        out = torch.empty((M, N), dtype=a.dtype, device=a.device)
+    if out.shape != (M, N) or out.dtype != a.dtype:
+        raise ValueError("out has the wrong shape or dtype")
+    if stream is None:
+        stream = torch.cuda.current_stream(a.device).cuda_stream
+    args = (M, N, K, a.data_ptr(), _ld(a), b.data_ptr(), _ld(b), out.data_ptr(), _ld(out), stream)
+    if a.dtype == torch.float32:
+        st = gemm_f32(*args) if config is None else gemm_f32_ex(*args, config)
+    else:
+        st = gemm_f16(*args) if config is None else gemm_f16_ex(*args, config)
+    if st != GEMM_OK:
+        raise GemmError(st, "gemm_f32" if a.dtype == torch.float32 else "gemm_f16")
+    return out

@@ -1,0 +1,171 @@
+/*
+ * libgemm -- dense row-major GEMM on AMD Instinct MI355X (gfx950).
+ *
+ * Operation (every compute entry point):
+ *     C[i][j] = sum_{k=0}^{K-1} A[i][k] * B[k][j],   0 <= i < M, 0 <= j < N
+ * i.e. C[M x N] = A[M x K] x B[K x N] in row-major storage, 2*M*N*K flops.
+ * This is the problem statement of "GEMM: from naive to shared memory tiling
+ * and register blocking" (quant67.com, introduction) and of the naive kernel
+ * in "sgemm - beyond cuBLAS" (wingedge777.com, section 1); the FP16 variant
+ * is the HGEMM of "hgemm_naive_kernel explained" (yuyanqi.com, section 1.1),
+ * here with FP32 accumulation instead of the page's FP16 accumulator.
+ *
+ * Conventions shared by all entry points
+ * --------------------------------------
+ * Layout     Row-major.  Element (i, k) of A is A[i*lda + k], (k, j) of B is
+ *            B[k*ldb + j], (i, j) of C is C[i*ldc + j].  Leading dimensions
+ *            are counted in elements.
+ * Memory     A, B and C are device pointers owned by the caller.  The library
+ *            never allocates, frees or retains them.  C is overwritten (no
+ *            alpha/beta); its columns [N, ldc) are never written.
+ * Streams    `stream` is a hipStream_t passed as void* (NULL = the default
+ *            stream).  Calls only enqueue work and return; the caller
+ *            synchronises.  Concurrent calls on different streams are safe.
+ * Degenerate M == 0 or N == 0: no work, GEMM_OK.  K == 0: C[0:M, 0:N] = 0
+ *            (the empty sum).
+ * Alignment  None required.  Operands whose pointers are 16-byte aligned and
+ *            whose K, N and leading dimensions are multiples of 4 (FP32) or 8
+ *            (FP16) take the 128-bit vector path; others a scalar path with
+ *            the same results.
+ * Rounding   FP32: products and sums in FP32 on the matrix cores; the order
+ *            of the K-sum is the kernel's (results agree with the exact sum
+ *            within |C - C_exact| <= 1e-5 * sum_k |A_ik||B_kj| for the
+ *            supported sizes).  FP16: FP16 inputs, FP32 accumulation, one
+ *            round-to-nearest-even conversion to FP16 per output.
+ * Errors     No exception or abort crosses this interface.  Argument errors
+ *            are detected on the host before any GPU work is enqueued:
+ *              M, N or K < 0                              -> INVALID_ARG
+ *              lda < max(1,K), ldb < max(1,N), ldc < max(1,N) -> INVALID_ARG
+ *              NULL A (M,K > 0), B (K,N > 0) or C (M,N > 0) -> INVALID_ARG
+ *              byte range of C overlapping that of A or B   -> ALIAS
+ *              forced configuration unknown / wrong dtype   -> UNSUPPORTED
+ *              launch failure reported by the HIP runtime   -> HIP
+ *            gemm_last_error() returns a message for the calling thread's
+ *            most recent failure.
+ */
+#ifndef DENSE_GEMM_ROW_AMD_GEMM_H
+#define DENSE_GEMM_ROW_AMD_GEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum gemm_status {
+    GEMM_OK = 0,
+    GEMM_ERR_INVALID_ARG = -1,
+    GEMM_ERR_UNSUPPORTED = -2,
+    GEMM_ERR_HIP = -3,
+    GEMM_ERR_ALIAS = -4
+} gemm_status_t;
+
+/* IEEE 754 binary16 bit pattern. */
+typedef uint16_t gemm_f16_t;
+
+typedef enum gemm_dtype { GEMM_DTYPE_F32 = 0, GEMM_DTYPE_F16 = 1 } gemm_dtype_t;
+
+/* Kernel families. */
+typedef enum gemm_family {
+    GEMM_FAMILY_MFMA = 0, /* matrix-core kernels (v_mfma_f32_32x32x2_f32,
+                             v_mfma_f32_32x32x16_f16)                     */
+    GEMM_FAMILY_SIMT = 1  /* vector-FMA kernel, kept as an ablation (FP32) */
+} gemm_family_t;
+
+/* Workgroup-to-tile order. */
+typedef enum gemm_order {
+    GEMM_ORDER_ROW = 0,     /* tile (bid / tiles_n, bid % tiles_n)             */
+    GEMM_ORDER_GROUPED = 1, /* column sweep inside bands of group_m tile rows  */
+    GEMM_ORDER_XCD = 2      /* GROUPED after gathering the workgroups that the
+                               dispatcher sends to one XCD (round robin over
+                               8) into one contiguous run of tiles            */
+} gemm_order_t;
+
+/*
+ * One compiled kernel variant plus its launch order.  gemm_get_config fills
+ * every field; gemm_*_ex reads `id` (which variant) and `order`/`group_m`
+ * (how workgroups map to tiles) and ignores the descriptive fields.
+ */
+typedef struct gemm_config {
+    int32_t id;         /* index in the variant table of this dtype          */
+    int32_t dtype;      /* gemm_dtype_t                                      */
+    int32_t family;     /* gemm_family_t                                     */
+    int32_t bm, bn, bk; /* macro tile: rows, columns, K-slice depth          */
+    int32_t wm, wn;     /* per-wave tile (SIMT: per-thread tile rows, cols)  */
+    int32_t threads;    /* workgroup size (multiple of the 64-lane wave)     */
+    int32_t stages;     /* LDS buffers in the K pipeline                     */
+    int32_t lds_bytes;  /* LDS per workgroup                                 */
+    int32_t order;      /* gemm_order_t                                      */
+    int32_t group_m;    /* band height in tile rows for GROUPED/XCD orders   */
+    char name[48];      /* e.g. "mfma_f32_128x128x32_w64x64"                 */
+} gemm_config_t;
+
+/*
+ * FP32 GEMM, C = A x B (FP32 in, FP32 out).  Chooses the variant from the
+ * tuning table (gemm_load_tuning) or a shape heuristic.
+ */
+gemm_status_t gemm_f32(int64_t M, int64_t N, int64_t K,
+                       const float *A, int64_t lda,
+                       const float *B, int64_t ldb,
+                       float *C, int64_t ldc, void *stream);
+
+/*
+ * FP16 GEMM, C = A x B: binary16 inputs, FP32 accumulation, binary16 output
+ * rounded to nearest even (overflow gives +-Inf, subnormals are kept).
+ */
+gemm_status_t gemm_f16(int64_t M, int64_t N, int64_t K,
+                       const gemm_f16_t *A, int64_t lda,
+                       const gemm_f16_t *B, int64_t ldb,
+                       gemm_f16_t *C, int64_t ldc, void *stream);
+
+/* As gemm_f32 / gemm_f16 with a forced variant and tile order (tests,
+ * tuner, ablation).  cfg->id must name a variant of the matching dtype. */
+gemm_status_t gemm_f32_ex(int64_t M, int64_t N, int64_t K,
+                          const float *A, int64_t lda,
+                          const float *B, int64_t ldb,
+                          float *C, int64_t ldc, void *stream,
+                          const gemm_config_t *cfg);
+gemm_status_t gemm_f16_ex(int64_t M, int64_t N, int64_t K,
+                          const gemm_f16_t *A, int64_t lda,
+                          const gemm_f16_t *B, int64_t ldb,
+                          gemm_f16_t *C, int64_t ldc, void *stream,
+                          const gemm_config_t *cfg);
+
+/* Variant table: count per dtype, and the description of variant idx. */
+int32_t gemm_num_configs(int32_t dtype);
+gemm_status_t gemm_get_config(int32_t dtype, int32_t idx, gemm_config_t *out);
+
+/* The configuration gemm_f32 / gemm_f16 would use for this shape (host
+ * only; no GPU work). */
+gemm_status_t gemm_select_config(int32_t dtype, int64_t M, int64_t N, int64_t K,
+                                 gemm_config_t *out);
+
+/* Workgroup-to-tile map of a configuration (host only): the tile
+ * (tile_m, tile_n) that workgroup `block` computes for an M x N output.
+ * The kernels use the same function on the device. */
+gemm_status_t gemm_tile_of_block(const gemm_config_t *cfg, int64_t M, int64_t N,
+                                 int64_t block, int64_t *tile_m, int64_t *tile_n);
+
+/* Host check of a variant's LDS layouts: every staging write and fragment
+ * read stays inside the stage, writes cover the stage exactly once, and the
+ * bank-conflict count under `banks` 4-byte banks is reported per access
+ * class (out[0] staging writes, out[1] fragment reads, in extra passes over
+ * the minimum).  Returns GEMM_OK when the layout is a bijection in bounds. */
+gemm_status_t gemm_layout_check(int32_t dtype, int32_t idx, int32_t banks,
+                                int64_t out[2]);
+
+/* Tuning table: a text file of lines "dtype M N K name order group_m"
+ * (dtype f32|f16).  Exact-shape matches override the heuristic.  Loading
+ * replaces the previous table; NULL clears it.  Not safe to call
+ * concurrently with GEMM calls. */
+gemm_status_t gemm_load_tuning(const char *path);
+
+const char *gemm_status_string(gemm_status_t status);
+const char *gemm_last_error(void); /* thread-local; "" when none */
+const char *gemm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DENSE_GEMM_ROW_AMD_GEMM_H */

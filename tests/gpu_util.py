@@ -1,0 +1,121 @@
+"""Helpers for the GPU parity tests: device operands with guard bands, calls
+through the C-ABI binding, comparison with the oracle.
+
+Every operand lives inside a larger device buffer: `guard` canary elements
+before and after it, and `pad` canary columns at the end of each row (so the
+leading dimension exceeds the column count).  After a call the canaries
+must be intact: the kernel wrote nothing outside C[0:M, 0:N].
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+from dense_gemm_row_amd import gemm
+
+CANARY_F32 = np.uint32(0x7FC0DEAD)  # a quiet NaN payload nobody computes
+CANARY_F16 = np.uint16(0x7E5A)
+
+
+def log(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+class DevMatrix:
+    """rows x cols matrix at element offset `offset` of a flat device buffer
+    with leading dimension cols + pad and `guard` elements on both sides."""
+
+    def __init__(self, host: np.ndarray | None, rows: int, cols: int, kind: str,
+                 pad: int = 0, guard: int = 64, offset: int = 0):
+        self.rows, self.cols, self.kind = rows, cols, kind
+        self.ld = max(cols + pad, 1)
+        self.guard = guard + offset
+        self.bits = np.uint32 if kind == "f32" else np.uint16
+        self.es = 4 if kind == "f32" else 2
+        canary = CANARY_F32 if kind == "f32" else CANARY_F16
+        n = self.guard + rows * self.ld + guard
+        flat = np.full(n, canary, dtype=self.bits)
+        if host is not None and rows and cols:
+            view = flat[self.guard:self.guard + rows * self.ld].reshape(rows, self.ld)
+            view[:, :cols] = host.view(self.bits)
+        tdt = torch.int32 if kind == "f32" else torch.int16
+        self.flat_host = flat
+        self.dev = torch.from_numpy(flat.view(np.int32 if kind == "f32" else np.int16)).to("cuda")
+        assert self.dev.dtype == tdt
+
+    @property
+    def ptr(self) -> int:
+        return self.dev.data_ptr() + self.guard * self.es
+
+    def fetch(self) -> np.ndarray:
+        return self.dev.cpu().numpy().view(self.bits)
+
+    def matrix(self, flat: np.ndarray | None = None) -> np.ndarray:
+        flat = self.fetch() if flat is None else flat
+        if self.rows == 0:
+            return np.zeros((0, self.cols), dtype=np.float32 if self.kind == "f32" else np.float16)
+        view = flat[self.guard:self.guard + self.rows * self.ld].reshape(self.rows, self.ld)
+        out = np.ascontiguousarray(view[:, :self.cols])
+        return out.view(np.float32 if self.kind == "f32" else np.float16)
+
+    def untouched_outside(self, flat: np.ndarray | None = None) -> bool:
+        """Canaries intact before, after and in the row padding."""
+        flat = self.fetch() if flat is None else flat
+        canary = CANARY_F32 if self.kind == "f32" else CANARY_F16
+        body = flat[self.guard:self.guard + self.rows * self.ld]
+        ok = np.all(flat[:self.guard] == canary) and np.all(flat[self.guard + self.rows * self.ld:] == canary)
+        if self.rows and self.ld > self.cols:
+            ok = ok and np.all(body.reshape(self.rows, self.ld)[:, self.cols:] == canary)
+        return bool(ok)
+
+
+def run(A: np.ndarray, B: np.ndarray, cfg=None, pad=(0, 0, 0), offset=(0, 0, 0),
+        repeat: int = 1):
+    """Compute A @ B through libgemm.  Returns (C as numpy, C DevMatrix)."""
+    kind = "f32" if A.dtype == np.float32 else "f16"
+    M, K = A.shape
+    N = B.shape[1]
+    dA = DevMatrix(A, M, K, kind, pad=pad[0], offset=offset[0])
+    dB = DevMatrix(B, K, N, kind, pad=pad[1], offset=offset[1])
+    dC = DevMatrix(None, M, N, kind, pad=pad[2], offset=offset[2])
+    stream = torch.cuda.current_stream().cuda_stream
+    for _ in range(repeat):
+        args = (M, N, K, dA.ptr, dA.ld, dB.ptr, dB.ld, dC.ptr, dC.ld, stream)
+        if kind == "f32":
+            st = gemm.gemm_f32(*args) if cfg is None else gemm.gemm_f32_ex(*args, cfg)
+        else:
+            st = gemm.gemm_f16(*args) if cfg is None else gemm.gemm_f16_ex(*args, cfg)
+        if st != gemm.GEMM_OK:
+            raise gemm.GemmError(st, "gemm call")
+    torch.cuda.synchronize()
+    flat = dC.fetch()
+    assert dC.untouched_outside(flat), "kernel wrote outside C[0:M, 0:N]"
+    return dC.matrix(flat), dC
+
+
+def tol_for(kind: str) -> float:
+    return oracle.SGEMM_TOL if kind == "f32" else oracle.HGEMM_TOL
+
+
+def check_full(A, B, C, tol=None) -> dict:
+    kind = "f32" if A.dtype == np.float32 else "f16"
+    ref, den = oracle.gemm_rows(A, B)
+    return oracle.check(C, ref, den, tol_for(kind) if tol is None else tol)
+
+
+def check_rows(A, B, C, rows, tol=None) -> dict:
+    kind = "f32" if A.dtype == np.float32 else "f16"
+    ref, den = oracle.gemm_rows(A, B, rows=rows)
+    return oracle.check(np.ascontiguousarray(C[rows]), ref, den, tol_for(kind) if tol is None else tol)
+
+
+def exact_equal(A, B, C) -> bool:
+    """Bit-exact agreement with the oracle (for inputs whose product is
+    exactly representable): compare the decoded output to C_ref."""
+    ref, _ = oracle.gemm_rows(A, B)
+    got = C.astype(np.float64)
+    return bool(np.array_equal(got, ref))

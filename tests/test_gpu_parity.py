@@ -1,0 +1,198 @@
+"""GPU parity: libgemm (through the C-ABI) against the CPU oracle.
+
+* Exact inputs (small integers, identity, permutation, the FP16 rounding
+  probe): the product has one representable answer, so every kernel
+  variant must match the oracle bit for bit, on edge shapes, padded leading
+  dimensions and misaligned operands.
+* Random uniform[-1, 1) inputs at the benchmark shapes: max_ij
+  |C - C_ref| / sum_k |A_ik||B_kj| <= 1e-5 (FP32) or <= 2e-3 (FP16, judged
+  after the output's FP16 rounding), in full up to 2048^3 and on sampled
+  rows and entries at the full sizes.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from dense_gemm_row_amd import gemm, synth
+from tests.gpu_util import check_full, check_rows, exact_equal, log, run
+
+pytestmark = pytest.mark.gpu
+
+F32_CFGS = list(range(7))
+F16_CFGS = list(range(5))
+
+EDGE_SHAPES = [(1, 1, 1), (2, 3, 5), (31, 33, 17), (64, 64, 64), (127, 129, 65),
+               (130, 257, 96), (257, 130, 200), (65, 300, 512)]
+
+
+def _cfg(kind, idx, order=None, group_m=None):
+    c = gemm.gemm_get_config(gemm.DTYPE_F32 if kind == "f32" else gemm.DTYPE_F16, idx)
+    if order is not None:
+        c.order = order
+    if group_m is not None:
+        c.group_m = group_m
+    return c
+
+
+def _ints(M, N, K, kind, seed=7):
+    dt = np.float32 if kind == "f32" else np.float16
+    return (synth.small_int(seed, 0, M, K, dtype=dt), synth.small_int(seed, 1, K, N, dtype=dt))
+
+
+def test_configs_present():
+    assert gemm.gemm_num_configs(gemm.DTYPE_F32) == len(F32_CFGS)
+    assert gemm.gemm_num_configs(gemm.DTYPE_F16) == len(F16_CFGS)
+
+
+@pytest.mark.parametrize("idx", F32_CFGS)
+@pytest.mark.parametrize("shape", EDGE_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_f32_exact_small_int(idx, shape):
+    M, N, K = shape
+    A, B = _ints(M, N, K, "f32")
+    cfg = _cfg("f32", idx)
+    log(f"f32 exact cfg={cfg.name.decode()} shape={shape}")
+    C, _ = run(A, B, cfg)
+    assert exact_equal(A, B, C)
+
+
+@pytest.mark.parametrize("idx", F16_CFGS)
+@pytest.mark.parametrize("shape", EDGE_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_f16_exact_small_int(idx, shape):
+    M, N, K = shape
+    A, B = _ints(M, N, K, "f16")
+    cfg = _cfg("f16", idx)
+    log(f"f16 exact cfg={cfg.name.decode()} shape={shape}")
+    C, _ = run(A, B, cfg)
+    assert exact_equal(A, B, C)
+
+
+@pytest.mark.parametrize("kind", ["f32", "f16"])
+@pytest.mark.parametrize("order", [gemm.ORDER_ROW, gemm.ORDER_GROUPED, gemm.ORDER_XCD])
+def test_tile_orders_exact(kind, order):
+    # 300 x 520 output: ragged in both dimensions for every tile size.
+    M, N, K = 300, 520, 136
+    A, B = _ints(M, N, K, kind, seed=11)
+    n = len(F32_CFGS if kind == "f32" else F16_CFGS)
+    for idx in range(n):
+        cfg = _cfg(kind, idx, order=order, group_m=3)
+        log(f"{kind} order={order} cfg={cfg.name.decode()}")
+        C, _ = run(A, B, cfg)
+        assert exact_equal(A, B, C), cfg.name
+
+
+@pytest.mark.parametrize("kind", ["f32", "f16"])
+@pytest.mark.parametrize("pad,offset", [((3, 5, 7), (0, 0, 0)),    # ld > cols, scalar path
+                                        ((8, 8, 8), (0, 0, 0)),    # ld > cols, vector path
+                                        ((0, 0, 0), (1, 0, 0)),    # misaligned A
+                                        ((0, 0, 0), (0, 1, 0)),    # misaligned B
+                                        ((0, 0, 0), (0, 0, 1))])   # misaligned C
+def test_ld_and_alignment(kind, pad, offset):
+    M, N, K = 129, 200, 264
+    A, B = _ints(M, N, K, kind, seed=3)
+    n = len(F32_CFGS if kind == "f32" else F16_CFGS)
+    for idx in range(n):
+        cfg = _cfg(kind, idx)
+        log(f"{kind} pad={pad} offset={offset} cfg={cfg.name.decode()}")
+        C, _ = run(A, B, cfg, pad=pad, offset=offset)
+        assert exact_equal(A, B, C), cfg.name
+
+
+@pytest.mark.parametrize("kind", ["f32", "f16"])
+def test_k_zero_writes_zeros(kind):
+    A = np.zeros((70, 0), np.float32 if kind == "f32" else np.float16)
+    B = np.zeros((0, 90), A.dtype)
+    log(f"{kind} K=0")
+    C, _ = run(A, B)
+    assert C.shape == (70, 90) and np.all(C == 0) and not np.any(np.signbit(C))
+
+
+@pytest.mark.parametrize("kind", ["f32", "f16"])
+def test_empty_m_n(kind):
+    dt = np.float32 if kind == "f32" else np.float16
+    log(f"{kind} M=0 / N=0")
+    C, _ = run(np.zeros((0, 5), dt), np.ones((5, 7), dt))
+    assert C.shape == (0, 7)
+    C, _ = run(np.ones((6, 5), dt), np.zeros((5, 0), dt))
+    assert C.shape == (6, 0)
+
+
+def test_f16_output_rounds_to_nearest_even():
+    # Exact FP32 sums that fall halfway between two FP16 neighbours:
+    #   (1 + 2^-10) * 1.5   = 1.5 + 1.5 ulp : ties-to-even 0x3E02, truncation 0x3E01
+    #   1 + 2^-11           = 1 + 0.5 ulp   : ties-to-even 0x3C00, half-up 0x3C01
+    #   1 + 2^-10 + 2^-11   = 1 + 1.5 ulp   : ties-to-even 0x3C02, truncation 0x3C01
+    h = np.float16
+    A = np.array([[1 + 2 ** -10, 0], [1, 2 ** -11], [1 + 2 ** -10, 2 ** -11]], h)
+    B = np.array([[1.5, 1], [0, 1]], h)
+    expect = np.array([[0x3E02, 0x3C01], [0x3E00, 0x3C00], [0x3E02, 0x3C02]], np.uint16)
+    for idx in F16_CFGS:
+        log(f"f16 RNE probe cfg={idx}")
+        C, _ = run(A, B, _cfg("f16", idx))
+        assert np.array_equal(C.view(np.uint16), expect), C.view(np.uint16)
+
+
+@pytest.mark.parametrize("kind", ["f32", "f16"])
+def test_identity_and_permutation_4096(kind):
+    n = 4096
+    dt = np.float32 if kind == "f32" else np.float16
+    B = synth.uniform_f32(5, 1, n, n).astype(dt)
+    eye = np.eye(n, dtype=dt)
+    log(f"{kind} identity 4096")
+    C, _ = run(eye, B)
+    assert np.array_equal(C.view(np.uint16 if kind == "f16" else np.uint32),
+                          B.view(np.uint16 if kind == "f16" else np.uint32))
+    p = synth.permutation(9, 2, n)
+    P = np.zeros((n, n), dt)
+    P[np.arange(n), p] = 1
+    log(f"{kind} permutation 4096")
+    C, _ = run(P, B)
+    assert np.array_equal(C, B[p])
+
+
+@pytest.mark.parametrize("kind", ["f32", "f16"])
+def test_deterministic(kind):
+    A, B = synth.workload(1000, 1000, 1000, kind, seed=4)
+    log(f"{kind} determinism")
+    C1, _ = run(A, B)
+    C2, _ = run(A, B, repeat=3)
+    assert np.array_equal(C1.view(np.uint8), C2.view(np.uint8))
+
+
+@pytest.mark.parametrize("kind", ["f32", "f16"])
+@pytest.mark.parametrize("n", [256, 2048])
+def test_random_full_check(kind, n):
+    A, B = synth.workload(n, n, n, kind)
+    n_cfg = len(F32_CFGS if kind == "f32" else F16_CFGS)
+    for idx in range(n_cfg) if n == 256 else [None]:
+        cfg = None if idx is None else _cfg(kind, idx)
+        log(f"{kind} random {n}^3 cfg={'auto' if cfg is None else cfg.name.decode()}")
+        C, _ = run(A, B, cfg)
+        rep = check_full(A, B, C)
+        log(f"  max_rel={rep['max_rel']:.3e} max_abs={rep['max_abs']:.3e}")
+        assert rep["ok"], rep
+
+
+SWEEP = [(4096, 4096, 4096), (8192, 8192, 1024), (1024, 1024, 8192), (4096, 11008, 4096),
+         (4000, 4000, 4000)]
+
+
+@pytest.mark.parametrize("kind", ["f32", "f16"])
+@pytest.mark.parametrize("shape", SWEEP, ids=lambda s: "x".join(map(str, s)))
+def test_random_sampled_full_size(kind, shape):
+    M, N, K = shape
+    A, B = synth.workload(M, N, K, kind)
+    log(f"{kind} random {shape} (auto config)")
+    C, _ = run(A, B)
+    rng = np.random.default_rng(0)
+    rows = sorted(set([0, M - 1, M // 2] + rng.integers(0, M, 40).tolist()))
+    rep = check_rows(A, B, C, rows)
+    log(f"  rows: max_rel={rep['max_rel']:.3e}")
+    assert rep["ok"], rep
+    ii = rng.integers(0, M, 2000)
+    jj = rng.integers(0, N, 2000)
+    ii[:2], jj[:2] = [M - 1, 0], [N - 1, N - 1]
+    ref, den = oracle.gemm_entries(A, B, ii, jj)
+    rep = oracle.check(C[ii, jj].reshape(1, -1), ref.reshape(1, -1), den.reshape(1, -1),
+                       oracle.SGEMM_TOL if kind == "f32" else oracle.HGEMM_TOL)
+    log(f"  entries: max_rel={rep['max_rel']:.3e}")
+    assert rep["ok"], rep
