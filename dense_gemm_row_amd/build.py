@@ -20,7 +20,7 @@ BUILD_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libgemm.so")
 ARCH = "gfx950"
 
-SOURCES = ["gemm_api.hip", "sgemm_mfma.hip", "hgemm_mfma.hip", "sgemm_simt.hip"]
+SOURCES = ["gemm_api.hip", "sgemm_mfma.hip", "hgemm_mfma.hip", "hgemm_pipe.hip", "hgemm_tr.hip", "sgemm_simt.hip"]
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
@@ -54,7 +54,10 @@ def build(extra_flags=(), jobs: int | None = None, verbose: bool = False) -> str
     with cf.ThreadPoolExecutor(jobs) as ex:
         objs = list(ex.map(lambda s: _compile(s, list(extra_flags)), SOURCES))
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    # --no-undefined: a kernel whose host-side launch stub went missing must
+    # fail the build, not the first dlopen.
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,--no-undefined", *objs,
+           "-o", tmp, "-L/opt/rocm/lib", "-lamdhip64"]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stdout}\n{res.stderr}")

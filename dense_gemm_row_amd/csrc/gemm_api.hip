@@ -65,6 +65,10 @@ struct Table {
     v[0].insert(v[0].end(), p, p + n);
     p = sgemm_simt_variants(&n);
     v[0].insert(v[0].end(), p, p + n);
+    p = hgemm_tr_variants(&n);
+    v[1].insert(v[1].end(), p, p + n);
+    p = hgemm_pipe_variants(&n);
+    v[1].insert(v[1].end(), p, p + n);
     p = hgemm_mfma_variants(&n);
     v[1].insert(v[1].end(), p, p + n);
     for (int d = 0; d < 2; ++d)

@@ -132,6 +132,14 @@ struct Variant {
 const Variant* sgemm_mfma_variants(int* count);
 const Variant* sgemm_simt_variants(int* count);
 const Variant* hgemm_mfma_variants(int* count);
+const Variant* hgemm_pipe_variants(int* count);
+const Variant* hgemm_tr_variants(int* count);
+
+// Launch the general FP16 kernel (any alignment, 64-bit addressing) with
+// the given workgroup tile (and the given wave tile when it has one); used
+// by the pipelined variants for operands they do not take.
+hipError_t hgemm_launch_shape(int bm, int bn, int wm, int wn, const Params& p, const TileMap& map,
+                              bool vec, hipStream_t stream);
 
 // Host bank-conflict accounting for one wave-wide LDS access: `addr[64]`
 // byte addresses of `width` bytes each.  Returns the extra passes over the

@@ -361,6 +361,17 @@ const Variant kVariants[] = {
 
 }  // namespace
 
+hipError_t hgemm_launch_shape(int bm, int bn, int wm, int wn, const Params& p, const TileMap& map,
+                              bool vec, hipStream_t stream) {
+  // The tile map depends on the workgroup tile only: any wave split of the
+  // same bm x bn tile computes the same tiles.  Prefer the same wave tile.
+  const Variant* pick = nullptr;
+  for (const Variant& v : kVariants)
+    if (v.desc.bm == bm && v.desc.bn == bn && (!pick || (v.desc.wm == wm && v.desc.wn == wn)))
+      pick = &v;
+  return pick ? pick->launch(p, map, vec, stream) : hipErrorInvalidValue;
+}
+
 const Variant* hgemm_mfma_variants(int* count) {
   *count = sizeof(kVariants) / sizeof(kVariants[0]);
   return kVariants;

@@ -1,0 +1,495 @@
+// FP16 HGEMM for aligned operands, built around gfx950's LDS-direct loads and
+// LDS transpose reads: binary16 A and B, FP32 accumulation on
+// v_mfma_f32_32x32x16_f16, one round-to-nearest-even conversion per output.
+//
+// Data path per K slice of 64 (no VGPR staging, no VALU in the main loop):
+// * A and B move from global memory straight into LDS with
+//   buffer_load_dwordx4 ... lds: one instruction fills 1 KB of LDS per wave,
+//   lane l writing bytes [16l, 16l+16) of the wave's block, so each lane
+//   fetches the 16-byte global chunk whose (swizzled) LDS position is 16l.
+//   The A tile is row-major (k contiguous, 128-byte rows, chunk XOR
+//   swz_row); the B tile is row-major as in memory (n contiguous, BN*2-byte
+//   rows) with the 16-byte chunk index XORed by 4*(k%4).
+// * The matrix core needs B down columns (8 consecutive k per lane).  The
+//   transpose read ds_read_b64_tr_b16 provides that: within each group of
+//   16 lanes, output lane j receives element j%4 of the 8-byte pieces
+//   addressed by lanes j/4, 4+j/4, 8+j/4 and 12+j/4 (lane-map checked on the
+//   device), so pointing lane 4t+q at row k+t, columns c+4q..c+4q+3 hands
+//   lane j the four values B[k..k+3][c+j].  Two such reads give the eight k
+//   values of one MFMA operand.
+// * Operands are swapped in the MFMA: it computes blocks of C^T = B^T A^T,
+//   so an accumulator register group holds four consecutive output columns
+//   of one output row.  This is the transposed-operand idea of "sgemm -
+//   beyond cuBLAS" (section 3) and of "hgemm_naive_kernel explained"
+//   (section 7.1), done by the hardware transpose read instead of a
+//   transposed store.
+// * K advances by moving the buffer descriptors' base address and shrinking
+//   their range (scalar adds); loads outside the matrix (rows past M or K,
+//   columns past N) are range-checked by the hardware and return zeros.  The
+//   last, partial K slice of A is masked per lane.  Fragment addresses are
+//   per-lane constants plus immediate offsets.
+// * Two LDS stages, one barrier per slice; the copy of slice t+2 is issued
+//   right after the barrier that frees its stage, and the last k step's
+//   MFMAs (registers only) run after the barrier, covering the first
+//   fragment reads of the next stage (the double buffer of "sgemm - beyond
+//   cuBLAS", section 6, with the asynchronous copies that the lqnn.cn SGEMM
+//   article adds in section 3.5).
+// * Epilogue through LDS: each wave stores its FP16 tile row-major into LDS
+//   (rows padded by 8 bytes: conflict-free 8-byte writes), then reads whole
+//   16-byte row chunks back and writes C with 16 lanes per 256-byte row
+//   segment (the coalesced write-back of section 5).
+#include "gemm_internal.h"
+
+namespace gemm {
+namespace {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) f16x8 lds_f16x8;
+
+constexpr int BK = 64;
+constexpr int A_ROW = 128;             // bytes per A tile row (BK halves)
+constexpr unsigned OOB = 0x80000000u;  // offset past every buffer's range
+
+template <int BM, int BN, int WM, int WN>
+struct Shape {
+  static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN, NW = WAVES_M * WAVES_N;
+  static constexpr int NT = NW * 64;
+  static constexpr int MB = WM / 32, NB = WN / 32;
+  static constexpr int B_ROW = BN * 2;            // bytes per B tile row
+  static constexpr int B_CPR = B_ROW / 16;        // 16-byte chunks per B row
+  static constexpr int A_STAGE = BM * A_ROW, B_STAGE = BK * B_ROW;
+  // LDS: four arrays, A stage 0/1 and B stage 0/1 (separate objects, so
+  // the compiler can tell the copies into one stage from reads of the
+  // other).  In the epilogue wave w stages its FP16 tile in array w.
+  static constexpr int LDS_BYTES = 2 * (A_STAGE + B_STAGE);
+  static constexpr int EPI_ROW = WN * 2;          // bytes per staged FP16 row
+  static constexpr int EPI_SPR = WN / 4;          // 8-byte slots per row
+  static constexpr int EPI_WAVE = WM * EPI_ROW;
+  static constexpr int IA = A_STAGE / 1024 / NW, IB = B_STAGE / 1024 / NW;
+  static_assert(NW == 4 && EPI_WAVE <= A_STAGE && EPI_WAVE <= B_STAGE, "epilogue staging");
+  static_assert(BM % WM == 0 && BN % WN == 0, "wave grid");
+  static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile");
+  static_assert(A_STAGE % (1024 * NW) == 0 && B_STAGE % (1024 * NW) == 0, "direct-load split");
+  static_assert(B_CPR >= 16, "B rows of at least 256 bytes (the k%4 chunk XOR)");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS");
+  // Fragment reads use a per-lane base plus immediate offsets (< 64 KB).
+  static_assert((MB - 1) * 32 * A_ROW < 65536 && 52 * B_ROW < 65536, "immediate offsets");
+
+  // B tile: physical chunk of logical chunk c in row k.
+  __host__ __device__ static constexpr int b_phys(int k, int c) { return c ^ (4 * (k % 4)); }
+  // Byte offsets within one stage array.
+  __host__ __device__ static constexpr int a_byte(int r, int q) { return swz_off(r, q, A_ROW); }
+  __host__ __device__ static constexpr int b_byte(int k, int n) {
+    return k * B_ROW + 16 * b_phys(k, n / 8) + 2 * (n % 8);
+  }
+  // Direct loads: lane l of wave w, instruction i.
+  __host__ __device__ static constexpr int a_dl_row(int i, int w, int l) { return 8 * (i * NW + w) + l / 8; }
+  __host__ __device__ static constexpr int a_dl_q(int i, int w, int l) {
+    return (l % 8) ^ swz_row(a_dl_row(i, w, l), A_ROW);
+  }
+  __host__ __device__ static constexpr int b_dl_k(int i, int w, int l) {
+    return (1024 * (i * NW + w) + 16 * l) / B_ROW;
+  }
+  __host__ __device__ static constexpr int b_dl_c(int i, int w, int l) {
+    return ((1024 * (i * NW + w) + 16 * l) % B_ROW / 16) ^ (4 * (b_dl_k(i, w, l) % 4));
+  }
+  // Fragment reads for k step j of a slice.
+  //  B_op (A values): lane reads row wm0 + 32mb + l%32, chunk 2j + l/32.
+  __host__ __device__ static constexpr int a_frag(int wm0, int mb, int j, int l) {
+    return a_byte(wm0 + 32 * mb + l % 32, 2 * j + l / 32);
+  }
+  //  A_op (B values, transpose read j2 of 2): lane 4t+q of 16-lane group g
+  //  points at row 16j + 8h + 4j2 + t, columns wn0 + 32nb + 16(g%2) + 4q.
+  __host__ __device__ static constexpr int b_frag(int wn0, int nb, int j, int j2, int l) {
+    return b_byte(16 * j + 8 * (l / 32) + 4 * j2 + (l % 16) / 4,
+                  wn0 + 32 * nb + 16 * ((l / 16) % 2) + 4 * (l % 4));
+  }
+  // Epilogue staging: 8-byte slot s (columns 4s..4s+3) of tile row m, XOR
+  // swizzled by the row so that the 32 rows written by one instruction hit
+  // 32 different bank pairs; read back 8 bytes at a time.
+  __host__ __device__ static constexpr int epi_byte(int m, int s) {
+    return m * EPI_ROW + 8 * (s ^ (m % EPI_SPR));
+  }
+};
+
+__device__ inline f32x16 mfma(f16x8 a, f16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ inline unsigned short f16_bits(float x) {
+  return __builtin_bit_cast(unsigned short, static_cast<_Float16>(x));
+}
+
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const unsigned char* base, int64_t bytes) {
+  // Raw buffer (stride 0); num_records in bytes; loads past it return 0.
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(base), 0,
+                                           (int)(bytes > 0 ? bytes : 0), 0x00020000);
+}
+
+constexpr int SG_MFMA = 0x008, SG_VMEM_RD = 0x020, SG_DS_RD = 0x100;
+
+// s_waitcnt immediate: vmcnt(n) (6 bits, split 4 + 2) with expcnt and
+// lgkmcnt left at their maximum (no wait).
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
+#define SGB(mask, n) __builtin_amdgcn_sched_group_barrier((mask), (n), 0)
+
+// Issue the LDS-direct copies of K slice s into `stage`.  The buffer
+// descriptors start at the slice (base moved by s*BK along k) and end at the
+// matrix end, so rows past K (and anything past the last element) load as
+// zeros.  A device function rather than a kernel lambda: lambdas of a kernel
+// are also compiled for the host, and a descriptor value there makes the
+// host pass drop the kernel's launch stub.
+template <class S>
+__device__ __forceinline__ void issue_slice(const unsigned char* Ab, const unsigned char* Bb,
+                                            int64_t a_bytes, int64_t b_bytes, int s,
+                                            const unsigned* a_vo, const unsigned* b_vo,
+                                            unsigned char* lds_a, unsigned char* lds_b, int wave,
+                                            int ldb) {
+  const int64_t ka = 2 * (int64_t)s * BK, kb = (int64_t)s * BK * ldb * 2;
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(Ab + ka, a_bytes - ka);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bb + kb, b_bytes - kb);
+#pragma unroll
+  for (int i = 0; i < S::IA; ++i) {
+    lds_void* dst = (lds_void*)(lds_a + 1024 * (i * S::NW + wave));
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, dst, 16, a_vo[i], 0, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < S::IB; ++i) {
+    lds_void* dst = (lds_void*)(lds_b + 1024 * (i * S::NW + wave));
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, dst, 16, b_vo[i], 0, 0, 0);
+  }
+}
+
+template <int BM, int BN, int WM, int WN>
+__global__ void __launch_bounds__((Shape<BM, BN, WM, WN>::NT))
+hgemm_tr_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
+  using S = Shape<BM, BN, WM, WN>;
+  constexpr int NW = S::NW, MB = S::MB, NB = S::NB, IA = S::IA, IB = S::IB;
+
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_a0[S::A_STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_a1[S::A_STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_b0[S::B_STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_b1[S::B_STAGE];
+
+  int tm, tn;
+  tile_of_block(blockIdx.x, map, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int M = p.M, N = p.N, K = p.K;
+  const int lda = (int)p.lda, ldb = (int)p.ldb;
+  const unsigned char* Ab = static_cast<const unsigned char*>(p.A);
+  const unsigned char* Bb = static_cast<const unsigned char*>(p.B);
+
+  const int tid = threadIdx.x;
+  const int l = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm0 = (wave / S::WAVES_N) * WM, wn0 = (wave % S::WAVES_N) * WN;
+  const int T = (K + BK - 1) / BK;
+
+  // Direct-load offsets (relative to the slice's descriptor base).
+  unsigned a_vo[IA], a_vo_tail[IA], b_vo[IB];
+#pragma unroll
+  for (int i = 0; i < IA; ++i) {
+    const int r = S::a_dl_row(i, wave, l), q = S::a_dl_q(i, wave, l);
+    const bool ok = (m0 + r) < M;
+    a_vo[i] = ok ? 2u * ((unsigned)(m0 + r) * (unsigned)lda + 8u * q) : OOB;
+    a_vo_tail[i] = ((T - 1) * BK + 8 * q < K) ? a_vo[i] : OOB;
+  }
+#pragma unroll
+  for (int i = 0; i < IB; ++i) {
+    const int k = S::b_dl_k(i, wave, l), c = S::b_dl_c(i, wave, l);
+    const bool ok = (n0 + 8 * c) < N;
+    b_vo[i] = ok ? 2u * ((unsigned)k * (unsigned)ldb + (unsigned)(n0 + 8 * c)) : OOB;
+  }
+  // Fragment byte offsets: k step j of A and block nb of B; other blocks
+  // and k steps are immediate offsets.
+  int a_fb[4], b_fb[NB];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) a_fb[j] = S::a_frag(wm0, 0, j, l);
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) b_fb[nb] = S::b_frag(wn0, nb, 0, 0, l);
+
+  auto issue = [&](int s, unsigned char* la, unsigned char* lb) {
+    issue_slice<S>(Ab, Bb, a_bytes, b_bytes, s, s == T - 1 ? a_vo_tail : a_vo, b_vo, la, lb, wave, ldb);
+  };
+
+  f16x8 fa[2][MB], fb[2][NB];
+  auto load_frags = [&](int buf, const unsigned char* la, const unsigned char* lb, int j) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+      fa[buf][mb] = *(const lds_f16x8*)(la + a_fb[j] + mb * 32 * A_ROW);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const unsigned char* b = lb + b_fb[nb] + 16 * j * S::B_ROW;
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)b);
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(b + 4 * S::B_ROW));
+      fb[buf][nb] = __builtin_bit_cast(f16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+  };
+
+  // acc[nb][mb]: block of C^T (rows n, columns m).
+  f32x16 acc[NB][MB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[nb][mb][r] = 0.f;
+  auto mma = [&](int buf) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) acc[nb][mb] = mfma(fb[buf][nb], fa[buf][mb], acc[nb][mb]);
+  };
+
+  constexpr int NMMA = MB * NB;     // MFMAs per k step
+  constexpr int NRD = MB + 2 * NB;  // LDS reads per k step
+  // One slice: k steps 0-2 on the current stage with the next step's
+  // fragments in flight; wait for the next stage's copies; barrier; issue
+  // slice t+2 into the freed stage; k step 3 (registers only) under the
+  // first fragment reads of the next stage.  The stage arrays are named
+  // statically (the loop is unrolled by two) so that the copies into one
+  // stage do not make the compiler wait before reads of the other.
+  auto slice = [&](int t, unsigned char* ca, unsigned char* cb, unsigned char* na, unsigned char* nb_) {
+    load_frags(1, ca, cb, 1);
+    mma(0);
+#pragma unroll
+    for (int i = 0; i < NRD; ++i) { SGB(SG_MFMA, 1); SGB(SG_DS_RD, 1); }
+    SGB(SG_MFMA, NMMA - NRD);
+    __builtin_amdgcn_sched_barrier(0);
+    load_frags(0, ca, cb, 2);
+    mma(1);
+#pragma unroll
+    for (int i = 0; i < NRD; ++i) { SGB(SG_MFMA, 1); SGB(SG_DS_RD, 1); }
+    SGB(SG_MFMA, NMMA - NRD);
+    __builtin_amdgcn_sched_barrier(0);
+    load_frags(1, ca, cb, 3);
+    mma(0);
+#pragma unroll
+    for (int i = 0; i < NRD; ++i) { SGB(SG_MFMA, 1); SGB(SG_DS_RD, 1); }
+    SGB(SG_MFMA, NMMA - NRD);
+    __builtin_amdgcn_sched_barrier(0);
+    // Slice t+1 (issued after the previous barrier) has landed.
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    issue(t + 2, ca, cb);
+    load_frags(0, na, nb_, 0);
+    mma(1);
+#pragma unroll
+    for (int i = 0; i < NRD; ++i) { SGB(SG_MFMA, 1); SGB(SG_DS_RD, 1); SGB(SG_VMEM_RD, 1); }
+    SGB(SG_MFMA, NMMA - NRD);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  if (T > 0) {
+    issue(0, lds_a0, lds_b0);
+    issue(1, lds_a1, lds_b1);
+    static_assert(IA + IB <= 63, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(IA + IB));  // slice 0 landed
+    __syncthreads();
+    load_frags(0, lds_a0, lds_b0, 0);
+    int t = 0;
+    for (; t + 1 < T; t += 2) {
+      slice(t, lds_a0, lds_b0, lds_a1, lds_b1);
+      slice(t + 1, lds_a1, lds_b1, lds_a0, lds_b0);
+    }
+    if (t < T) slice(t, lds_a0, lds_b0, lds_a1, lds_b1);
+    // The copies of slices T and T+1 (out of range: they write zeros) must
+    // land before the epilogue reuses the LDS.
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  }
+  __syncthreads();
+
+  // Epilogue.  acc[nb][mb] register r of lane l holds C[m][n] with
+  // m = wm0 + 32mb + l%32 and n = wn0 + 32nb + 8(r/4) + 4(l/32) + r%4: four
+  // consecutive columns per register group.  Stage the wave's FP16 tile in
+  // LDS array `wave` (row-major, 8-byte slots swizzled by row), then write
+  // it out in 16-byte row chunks, WN/8 lanes per row segment.
+  unsigned char* ep = wave == 0 ? lds_a0 : wave == 1 ? lds_a1 : wave == 2 ? lds_b0 : lds_b1;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        uint2 v;
+        v.x = f16_bits(acc[nb][mb][4 * rq + 0]) | ((unsigned)f16_bits(acc[nb][mb][4 * rq + 1]) << 16);
+        v.y = f16_bits(acc[nb][mb][4 * rq + 2]) | ((unsigned)f16_bits(acc[nb][mb][4 * rq + 3]) << 16);
+        const int row = 32 * mb + l % 32, slot = 8 * nb + 2 * rq + l / 32;
+        *reinterpret_cast<uint2*>(ep + S::epi_byte(row, slot)) = v;
+      }
+  __syncthreads();
+  constexpr int CPR = WN / 8;           // 16-byte chunks per wave-tile row
+  constexpr int RPI = 64 / CPR;         // rows per store instruction
+  unsigned short* __restrict__ C = static_cast<unsigned short*>(p.C);
+  const int rl = l / CPR, c = l % CPR;
+  const int col = n0 + wn0 + 8 * c;
+#pragma unroll
+  for (int pass = 0; pass < WM / RPI; ++pass) {
+    const int row = pass * RPI + rl;
+    const uint2 lo = *reinterpret_cast<const uint2*>(ep + S::epi_byte(row, 2 * c));
+    const uint2 hi = *reinterpret_cast<const uint2*>(ep + S::epi_byte(row, 2 * c + 1));
+    const int grow = m0 + wm0 + row;
+    if (grow < M && col < N) {
+      u32x4 v = {lo.x, lo.y, hi.x, hi.y};
+      *reinterpret_cast<u32x4*>(C + (int64_t)grow * p.ldc + col) = v;
+    }
+  }
+}
+
+template <int BM, int BN, int WM, int WN>
+hipError_t launch(const Params& p, const TileMap& map, bool vec, hipStream_t stream) {
+  using S = Shape<BM, BN, WM, WN>;
+  const int64_t lim = 0x7fffffff;
+  // Every offset (rows past M and K included) must fit the 31-bit range.
+  if (!vec || (int64_t)(p.M + BM) * p.lda * 2 > lim || (int64_t)(BK + 2) * p.ldb * 2 > lim ||
+      ((int64_t)(p.K > 0 ? p.K - 1 : 0) * p.ldb + p.N) * 2 > lim || (int64_t)p.M * p.lda * 2 > lim)
+    return hgemm_launch_shape(BM, BN, WM, WN, p, map, vec, stream);
+  const int64_t a_bytes = p.K > 0 ? ((int64_t)(p.M - 1) * p.lda + p.K) * 2 : 0;
+  const int64_t b_bytes = p.K > 0 ? ((int64_t)(p.K - 1) * p.ldb + p.N) * 2 : 0;
+  const dim3 grid(map.tiles_m * map.tiles_n), block(S::NT);
+  hipLaunchKernelGGL((hgemm_tr_kernel<BM, BN, WM, WN>), grid, block, 0, stream, p, map, a_bytes,
+                     b_bytes);
+  return hipGetLastError();
+}
+
+// Host replay: direct-load placement, fragment reads (including the lane
+// exchange of the transpose read), and epilogue staging, all checked for
+// bounds, for matching the element each lane must see, and for bank
+// conflicts.  Returns 0 when valid.
+template <int BM, int BN, int WM, int WN>
+int layout_check(int banks, int64_t out[2]) {
+  using S = Shape<BM, BN, WM, WN>;
+  int64_t wconf = 0, rconf = 0;
+  // Inverse maps of the two tile layouts: LDS byte -> (row, k) / (k, n).
+  static int a_row_of[S::A_STAGE], a_k_of[S::A_STAGE], b_k_of[S::B_STAGE], b_n_of[S::B_STAGE];
+  for (int i = 0; i < S::A_STAGE; ++i) a_row_of[i] = -1;
+  for (int i = 0; i < S::B_STAGE; ++i) b_k_of[i] = -1;
+  for (int i = 0; i < S::IA; ++i)
+    for (int w = 0; w < S::NW; ++w)
+      for (int l = 0; l < 64; ++l) {
+        const int off = 1024 * (i * S::NW + w) + 16 * l;
+        const int r = S::a_dl_row(i, w, l), q = S::a_dl_q(i, w, l);
+        if (r >= BM || q >= 8 || S::a_byte(r, q) != off) return 1;
+        for (int e = 0; e < 8; ++e) {
+          if (a_row_of[off + 2 * e] != -1) return 2;
+          a_row_of[off + 2 * e] = r;
+          a_k_of[off + 2 * e] = 8 * q + e;
+        }
+      }
+  for (int i = 0; i < S::IB; ++i)
+    for (int w = 0; w < S::NW; ++w)
+      for (int l = 0; l < 64; ++l) {
+        const int off = 1024 * (i * S::NW + w) + 16 * l;
+        const int k = S::b_dl_k(i, w, l), c = S::b_dl_c(i, w, l);
+        if (k >= BK || c >= S::B_CPR || S::b_byte(k, 8 * c) != off) return 3;
+        for (int e = 0; e < 8; ++e) {
+          if (b_k_of[off + 2 * e] != -1) return 4;
+          b_k_of[off + 2 * e] = k;
+          b_n_of[off + 2 * e] = 8 * c + e;
+        }
+      }
+  for (int i = 0; i < S::A_STAGE; i += 2)
+    if (a_row_of[i] < 0) return 5;
+  for (int i = 0; i < S::B_STAGE; i += 2)
+    if (b_k_of[i] < 0) return 6;
+  int addr[64];
+  for (int w = 0; w < S::NW; ++w) {
+    const int wm0 = (w / S::WAVES_N) * WM, wn0 = (w % S::WAVES_N) * WN;
+    for (int j = 0; j < 4; ++j) {
+      for (int mb = 0; mb < S::MB; ++mb) {
+        for (int l = 0; l < 64; ++l) {
+          addr[l] = S::a_frag(wm0, mb, j, l);
+          if (addr[l] < 0 || addr[l] + 16 > S::A_STAGE) return 15;
+          // B_op lane l: A[m = wm0 + 32mb + l%32][k = 16j + 8(l/32) + e].
+          for (int e = 0; e < 8; ++e) {
+            const int b = addr[l] + 2 * e;
+            if (a_row_of[b] != wm0 + 32 * mb + l % 32 || a_k_of[b] != 16 * j + 8 * (l / 32) + e) return 7;
+          }
+          if (addr[l] != S::a_frag(wm0, 0, j, l) + mb * 32 * A_ROW) return 8;
+        }
+        rconf += lds_conflicts(addr, 16, banks);
+      }
+      for (int nb = 0; nb < S::NB; ++nb)
+        for (int j2 = 0; j2 < 2; ++j2) {
+          for (int l = 0; l < 64; ++l) {
+            addr[l] = S::b_frag(wn0, nb, j, j2, l);
+            if (addr[l] != S::b_frag(wn0, nb, 0, 0, l) + 16 * j * S::B_ROW + 4 * j2 * S::B_ROW) return 9;
+          }
+          // Transpose read: output lane j receives element j%4 of the
+          // piece addressed by lane 4t + j/4 of its 16-lane group.
+          for (int l = 0; l < 64; ++l)
+            for (int t = 0; t < 4; ++t) {
+              const int g = l / 16, jj = l % 16;
+              const int src = addr[16 * g + 4 * t + jj / 4] + 2 * (jj % 4);
+              if (src < 0 || src >= S::B_STAGE) return 14;
+              // A_op lane l, element 4*j2 + t: B[k = 16j + 8(l/32) + 4j2 + t][n = wn0 + 32nb + l%32].
+              if (b_k_of[src] != 16 * j + 8 * (l / 32) + 4 * j2 + t || b_n_of[src] != wn0 + 32 * nb + l % 32)
+                return 10;
+            }
+          rconf += lds_conflicts(addr, 8, banks);
+        }
+    }
+  }
+  // Epilogue staging: writes and reads cover the wave's rows exactly once
+  // and agree on the element.
+  static int ep_row[S::EPI_WAVE], ep_col[S::EPI_WAVE];
+  for (int i = 0; i < S::EPI_WAVE; ++i) ep_row[i] = -1;
+  for (int nb = 0; nb < S::NB; ++nb)
+    for (int mb = 0; mb < S::MB; ++mb)
+      for (int rq = 0; rq < 4; ++rq) {
+        for (int l = 0; l < 64; ++l) {
+          const int row = 32 * mb + l % 32, slot = 8 * nb + 2 * rq + l / 32;
+          addr[l] = S::epi_byte(row, slot);
+          if (addr[l] < 0 || addr[l] + 8 > S::EPI_WAVE) return 13;
+          for (int e = 0; e < 4; ++e) {
+            if (ep_row[addr[l] + 2 * e] != -1) return 11;
+            ep_row[addr[l] + 2 * e] = row;
+            ep_col[addr[l] + 2 * e] = 32 * nb + 8 * rq + 4 * (l / 32) + e;
+          }
+        }
+        wconf += lds_conflicts(addr, 8, banks);
+      }
+  constexpr int CPR = WN / 8, RPI = 64 / CPR;
+  for (int pass = 0; pass < WM / RPI; ++pass)
+    for (int half = 0; half < 2; ++half) {
+      for (int l = 0; l < 64; ++l) {
+        const int row = pass * RPI + l / CPR, c = l % CPR;
+        addr[l] = S::epi_byte(row, 2 * c + half);
+        for (int e = 0; e < 4; ++e)
+          if (ep_row[addr[l] + 2 * e] != row || ep_col[addr[l] + 2 * e] != 8 * c + 4 * half + e) return 12;
+      }
+      rconf += lds_conflicts(addr, 8, banks);
+    }
+  out[0] = wconf;
+  out[1] = rconf;
+  return 0;
+}
+
+#define HGEMM_TR_VARIANT(BM, BN, WM, WN)                                                     \
+  Variant {                                                                                  \
+    gemm_config_t{0, GEMM_DTYPE_F16, GEMM_FAMILY_MFMA, BM, BN, BK, WM, WN,                   \
+                  Shape<BM, BN, WM, WN>::NT, 2, Shape<BM, BN, WM, WN>::LDS_BYTES,            \
+                  GEMM_ORDER_XCD, 4, "tr_f16_" #BM "x" #BN "x64_w" #WM "x" #WN},             \
+        &launch<BM, BN, WM, WN>, &layout_check<BM, BN, WM, WN>                               \
+  }
+
+const Variant kVariants[] = {
+    HGEMM_TR_VARIANT(256, 256, 128, 128),
+    HGEMM_TR_VARIANT(256, 128, 128, 64),
+    HGEMM_TR_VARIANT(128, 256, 64, 128),
+    HGEMM_TR_VARIANT(128, 128, 64, 64),
+};
+
+}  // namespace
+
+const Variant* hgemm_tr_variants(int* count) {
+  *count = sizeof(kVariants) / sizeof(kVariants[0]);
+  return kVariants;
+}
+
+}  // namespace gemm

@@ -18,8 +18,8 @@ from tests.gpu_util import check_full, check_rows, exact_equal, log, run
 
 pytestmark = pytest.mark.gpu
 
-F32_CFGS = list(range(7))
-F16_CFGS = list(range(5))
+F32_CFGS = list(range(gemm.gemm_num_configs(gemm.DTYPE_F32)))
+F16_CFGS = list(range(gemm.gemm_num_configs(gemm.DTYPE_F16)))
 
 EDGE_SHAPES = [(1, 1, 1), (2, 3, 5), (31, 33, 17), (64, 64, 64), (127, 129, 65),
                (130, 257, 96), (257, 130, 200), (65, 300, 512)]
