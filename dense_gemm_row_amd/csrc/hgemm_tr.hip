@@ -2,12 +2,12 @@
 // LDS transpose reads: binary16 A and B, FP32 accumulation on
 // v_mfma_f32_32x32x16_f16, one round-to-nearest-even conversion per output.
 //
-// Data path per K slice of 64 (no VGPR staging, no VALU in the main loop):
+// Data path per K slice (no VGPR staging, no VALU in the main loop):
 // * A and B move from global memory straight into LDS with
 //   buffer_load_dwordx4 ... lds: one instruction fills 1 KB of LDS per wave,
 //   lane l writing bytes [16l, 16l+16) of the wave's block, so each lane
 //   fetches the 16-byte global chunk whose (swizzled) LDS position is 16l.
-//   The A tile is row-major (k contiguous, 128-byte rows, chunk XOR
+//   The A tile is row-major (k contiguous, 2*BK-byte rows, chunk XOR
 //   swz_row); the B tile is row-major as in memory (n contiguous, BN*2-byte
 //   rows) with the 16-byte chunk index XORed by 4*(k%4).
 // * The matrix core needs B down columns (8 consecutive k per lane).  The
@@ -28,16 +28,25 @@
 //   columns past N) are range-checked by the hardware and return zeros.  The
 //   last, partial K slice of A is masked per lane.  Fragment addresses are
 //   per-lane constants plus immediate offsets.
-// * Two LDS stages, one barrier per slice; the copy of slice t+2 is issued
-//   right after the barrier that frees its stage, and the last k step's
+// * NS LDS stages (K slices of BK = 32 or 64), one barrier per slice; the
+//   copy of slice t+NS is issued right after the barrier that frees its
+//   stage, so a copy has NS-1 slices of MFMA work to land; the last k step's
 //   MFMAs (registers only) run after the barrier, covering the first
-//   fragment reads of the next stage (the double buffer of "sgemm - beyond
-//   cuBLAS", section 6, with the asynchronous copies that the lqnn.cn SGEMM
-//   article adds in section 3.5).
-// * Epilogue through LDS: each wave stores its FP16 tile row-major into LDS
-//   (rows padded by 8 bytes: conflict-free 8-byte writes), then reads whole
-//   16-byte row chunks back and writes C with 16 lanes per 256-byte row
-//   segment (the coalesced write-back of section 5).
+//   fragment reads of the next stage.  This generalises the double buffer of
+//   "sgemm - beyond cuBLAS" (section 6) with the asynchronous copies that
+//   the lqnn.cn SGEMM article adds in section 3.5.  Each stage is its own
+//   __shared__ array and the loop is unrolled NS times, so every access
+//   names its array statically and the compiler can see that copies into
+//   one stage do not alias reads of another (otherwise it waits for all
+//   copies before every read).
+// * Epilogue through LDS: each wave stores its FP16 tile row-major into its
+//   share of the stage arrays (8-byte slots XOR-swizzled by row:
+//   conflict-free writes), then reads whole 16-byte row chunks back and
+//   writes C with WN/8 lanes per row segment (the coalesced write-back of
+//   section 5).
+#include <type_traits>
+#include <utility>
+
 #include "gemm_internal.h"
 
 namespace gemm {
@@ -51,46 +60,58 @@ typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) f16x8 lds_f16x8;
 
-constexpr int BK = 64;
-constexpr int A_ROW = 128;             // bytes per A tile row (BK halves)
 constexpr unsigned OOB = 0x80000000u;  // offset past every buffer's range
+constexpr int MAX_STAGES = 5;
 
-template <int BM, int BN, int WM, int WN>
+template <int I>
+using IC = std::integral_constant<int, I>;
+
+template <class F, int... I>
+__device__ __forceinline__ void static_for(F&& f, std::integer_sequence<int, I...>) {
+  (f(IC<I>{}), ...);
+}
+
+template <int BM_, int BN_, int WM_, int WN_, int BK_, int NS_>
 struct Shape {
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BK_, NS = NS_;
   static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN, NW = WAVES_M * WAVES_N;
   static constexpr int NT = NW * 64;
-  static constexpr int MB = WM / 32, NB = WN / 32;
-  static constexpr int B_ROW = BN * 2;            // bytes per B tile row
-  static constexpr int B_CPR = B_ROW / 16;        // 16-byte chunks per B row
+  static constexpr int MB = WM / 32, NB = WN / 32, KS = BK / 16;
+  static constexpr int A_ROW = BK * 2, A_CPR = A_ROW / 16;  // bytes / chunks per A row
+  static constexpr int B_ROW = BN * 2, B_CPR = B_ROW / 16;  // bytes / chunks per B row
   static constexpr int A_STAGE = BM * A_ROW, B_STAGE = BK * B_ROW;
-  // LDS: four arrays, A stage 0/1 and B stage 0/1 (separate objects, so
-  // the compiler can tell the copies into one stage from reads of the
-  // other).  In the epilogue wave w stages its FP16 tile in array w.
-  static constexpr int LDS_BYTES = 2 * (A_STAGE + B_STAGE);
-  static constexpr int EPI_ROW = WN * 2;          // bytes per staged FP16 row
-  static constexpr int EPI_SPR = WN / 4;          // 8-byte slots per row
-  static constexpr int EPI_WAVE = WM * EPI_ROW;
-  static constexpr int IA = A_STAGE / 1024 / NW, IB = B_STAGE / 1024 / NW;
-  static_assert(NW == 4 && EPI_WAVE <= A_STAGE && EPI_WAVE <= B_STAGE, "epilogue staging");
+  static constexpr int LDS_BYTES = NS * (A_STAGE + B_STAGE);
+  static constexpr int IA = A_STAGE / 1024 / NW, IB = B_STAGE / 1024 / NW, LPS = IA + IB;
+  // Epilogue: wave w stages its tile in P of the 2*NS stage arrays
+  // (A arrays first), RPA rows per array.
+  static constexpr int EPI_ROW = WN * 2, EPI_SPR = WN / 4;
+  static constexpr int P = (2 * NS) / NW, RPA = WM / P;
+  static constexpr int EPI_CPR = WN / 8, EPI_RPI = 64 / EPI_CPR;  // store pass shape
+  static_assert(BK == 32 || BK == 64, "K slice");
+  static_assert(NS >= 2 && NS <= MAX_STAGES, "stages");
   static_assert(BM % WM == 0 && BN % WN == 0, "wave grid");
   static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile");
   static_assert(A_STAGE % (1024 * NW) == 0 && B_STAGE % (1024 * NW) == 0, "direct-load split");
   static_assert(B_CPR >= 16, "B rows of at least 256 bytes (the k%4 chunk XOR)");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
+  static_assert((NS - 1) * LPS <= 63, "vmcnt field");
+  static_assert(P >= 1 && WM % P == 0 && RPA % 32 == 0 && RPA % EPI_RPI == 0 &&
+                RPA * EPI_ROW <= A_STAGE && RPA * EPI_ROW <= B_STAGE, "epilogue staging");
   // Fragment reads use a per-lane base plus immediate offsets (< 64 KB).
-  static_assert((MB - 1) * 32 * A_ROW < 65536 && 52 * B_ROW < 65536, "immediate offsets");
+  static_assert((MB - 1) * 32 * A_ROW < 65536 && (BK - 12) * B_ROW < 65536, "immediate offsets");
 
-  // B tile: physical chunk of logical chunk c in row k.
-  __host__ __device__ static constexpr int b_phys(int k, int c) { return c ^ (4 * (k % 4)); }
   // Byte offsets within one stage array.
   __host__ __device__ static constexpr int a_byte(int r, int q) { return swz_off(r, q, A_ROW); }
+  __host__ __device__ static constexpr int b_phys(int k, int c) { return c ^ (4 * (k % 4)); }
   __host__ __device__ static constexpr int b_byte(int k, int n) {
     return k * B_ROW + 16 * b_phys(k, n / 8) + 2 * (n % 8);
   }
   // Direct loads: lane l of wave w, instruction i.
-  __host__ __device__ static constexpr int a_dl_row(int i, int w, int l) { return 8 * (i * NW + w) + l / 8; }
+  __host__ __device__ static constexpr int a_dl_row(int i, int w, int l) {
+    return (1024 / A_ROW) * (i * NW + w) + l / A_CPR;
+  }
   __host__ __device__ static constexpr int a_dl_q(int i, int w, int l) {
-    return (l % 8) ^ swz_row(a_dl_row(i, w, l), A_ROW);
+    return (l % A_CPR) ^ swz_row(a_dl_row(i, w, l), A_ROW);
   }
   __host__ __device__ static constexpr int b_dl_k(int i, int w, int l) {
     return (1024 * (i * NW + w) + 16 * l) / B_ROW;
@@ -109,9 +130,9 @@ struct Shape {
     return b_byte(16 * j + 8 * (l / 32) + 4 * j2 + (l % 16) / 4,
                   wn0 + 32 * nb + 16 * ((l / 16) % 2) + 4 * (l % 4));
   }
-  // Epilogue staging: 8-byte slot s (columns 4s..4s+3) of tile row m, XOR
-  // swizzled by the row so that the 32 rows written by one instruction hit
-  // 32 different bank pairs; read back 8 bytes at a time.
+  // Epilogue staging: 8-byte slot s (columns 4s..4s+3) of local row m of an
+  // array, XOR-swizzled by the row so that the 32 rows written by one
+  // instruction hit 32 different bank pairs; read back 8 bytes at a time.
   __host__ __device__ static constexpr int epi_byte(int m, int s) {
     return m * EPI_ROW + 8 * (s ^ (m % EPI_SPR));
   }
@@ -138,7 +159,7 @@ constexpr int SG_MFMA = 0x008, SG_VMEM_RD = 0x020, SG_DS_RD = 0x100;
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
 #define SGB(mask, n) __builtin_amdgcn_sched_group_barrier((mask), (n), 0)
 
-// Issue the LDS-direct copies of K slice s into `stage`.  The buffer
+// Issue the LDS-direct copies of K slice s into one stage.  The buffer
 // descriptors start at the slice (base moved by s*BK along k) and end at the
 // matrix end, so rows past K (and anything past the last element) load as
 // zeros.  A device function rather than a kernel lambda: lambdas of a kernel
@@ -146,13 +167,15 @@ constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
 // host pass drop the kernel's launch stub.
 template <class S>
 __device__ __forceinline__ void issue_slice(const unsigned char* Ab, const unsigned char* Bb,
-                                            int64_t a_bytes, int64_t b_bytes, int s,
+                                            int64_t a_bytes, int64_t b_bytes, int s, bool live,
                                             const unsigned* a_vo, const unsigned* b_vo,
                                             unsigned char* lds_a, unsigned char* lds_b, int wave,
                                             int ldb) {
-  const int64_t ka = 2 * (int64_t)s * BK, kb = (int64_t)s * BK * ldb * 2;
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(Ab + ka, a_bytes - ka);
-  const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bb + kb, b_bytes - kb);
+  // Slices past the last one (issued only to keep the wait counts uniform)
+  // get empty descriptors: they load zeros without touching memory.
+  const int64_t ka = 2 * (int64_t)s * S::BK, kb = (int64_t)s * S::BK * ldb * 2;
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(Ab + ka, live ? a_bytes - ka : 0);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bb + kb, live ? b_bytes - kb : 0);
 #pragma unroll
   for (int i = 0; i < S::IA; ++i) {
     lds_void* dst = (lds_void*)(lds_a + 1024 * (i * S::NW + wave));
@@ -165,16 +188,41 @@ __device__ __forceinline__ void issue_slice(const unsigned char* Ab, const unsig
   }
 }
 
-template <int BM, int BN, int WM, int WN>
-__global__ void __launch_bounds__((Shape<BM, BN, WM, WN>::NT))
+template <class S>
+__global__ void __launch_bounds__(S::NT)
 hgemm_tr_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
-  using S = Shape<BM, BN, WM, WN>;
-  constexpr int NW = S::NW, MB = S::MB, NB = S::NB, IA = S::IA, IB = S::IB;
+  constexpr int NS = S::NS, KS = S::KS, MB = S::MB, NB = S::NB, IA = S::IA, IB = S::IB;
+  constexpr int BM = S::BM, BN = S::BN, WM = S::WM, WN = S::WN, BK = S::BK;
 
-  __shared__ __attribute__((aligned(1024))) unsigned char lds_a0[S::A_STAGE];
-  __shared__ __attribute__((aligned(1024))) unsigned char lds_a1[S::A_STAGE];
-  __shared__ __attribute__((aligned(1024))) unsigned char lds_b0[S::B_STAGE];
-  __shared__ __attribute__((aligned(1024))) unsigned char lds_b1[S::B_STAGE];
+  // Stage arrays: A stages la0..la{NS-1}, B stages lb0..lb{NS-1} (unused
+  // ones are dropped by the compiler).
+  __shared__ __attribute__((aligned(1024))) unsigned char la0[S::A_STAGE], lb0[S::B_STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char la1[S::A_STAGE], lb1[S::B_STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char la2[S::A_STAGE], lb2[S::B_STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char la3[S::A_STAGE], lb3[S::B_STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char la4[S::A_STAGE], lb4[S::B_STAGE];
+  auto A_of = [&](auto I) -> unsigned char* {
+    constexpr int i = decltype(I)::value;
+    if constexpr (i == 0) return la0;
+    else if constexpr (i == 1) return la1;
+    else if constexpr (i == 2) return la2;
+    else if constexpr (i == 3) return la3;
+    else return la4;
+  };
+  auto B_of = [&](auto I) -> unsigned char* {
+    constexpr int i = decltype(I)::value;
+    if constexpr (i == 0) return lb0;
+    else if constexpr (i == 1) return lb1;
+    else if constexpr (i == 2) return lb2;
+    else if constexpr (i == 3) return lb3;
+    else return lb4;
+  };
+  // Array k of the epilogue list [A stages..., B stages...].
+  auto E_of = [&](auto I) -> unsigned char* {
+    constexpr int i = decltype(I)::value;
+    if constexpr (i < NS) return A_of(IC<i>{});
+    else return B_of(IC<(i - NS) % NS>{});
+  };
 
   int tm, tn;
   tile_of_block(blockIdx.x, map, tm, tn);
@@ -207,21 +255,22 @@ hgemm_tr_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
   }
   // Fragment byte offsets: k step j of A and block nb of B; other blocks
   // and k steps are immediate offsets.
-  int a_fb[4], b_fb[NB];
+  int a_fb[KS], b_fb[NB];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) a_fb[j] = S::a_frag(wm0, 0, j, l);
+  for (int j = 0; j < KS; ++j) a_fb[j] = S::a_frag(wm0, 0, j, l);
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) b_fb[nb] = S::b_frag(wn0, nb, 0, 0, l);
 
   auto issue = [&](int s, unsigned char* la, unsigned char* lb) {
-    issue_slice<S>(Ab, Bb, a_bytes, b_bytes, s, s == T - 1 ? a_vo_tail : a_vo, b_vo, la, lb, wave, ldb);
+    issue_slice<S>(Ab, Bb, a_bytes, b_bytes, s, s < T, s == T - 1 ? a_vo_tail : a_vo, b_vo, la, lb,
+                   wave, ldb);
   };
 
   f16x8 fa[2][MB], fb[2][NB];
   auto load_frags = [&](int buf, const unsigned char* la, const unsigned char* lb, int j) {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
-      fa[buf][mb] = *(const lds_f16x8*)(la + a_fb[j] + mb * 32 * A_ROW);
+      fa[buf][mb] = *(const lds_f16x8*)(la + a_fb[j] + mb * 32 * S::A_ROW);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const unsigned char* b = lb + b_fb[nb] + 16 * j * S::B_ROW;
@@ -248,58 +297,54 @@ hgemm_tr_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
 
   constexpr int NMMA = MB * NB;     // MFMAs per k step
   constexpr int NRD = MB + 2 * NB;  // LDS reads per k step
-  // One slice: k steps 0-2 on the current stage with the next step's
-  // fragments in flight; wait for the next stage's copies; barrier; issue
-  // slice t+2 into the freed stage; k step 3 (registers only) under the
-  // first fragment reads of the next stage.  The stage arrays are named
-  // statically (the loop is unrolled by two) so that the copies into one
-  // stage do not make the compiler wait before reads of the other.
-  auto slice = [&](int t, unsigned char* ca, unsigned char* cb, unsigned char* na, unsigned char* nb_) {
-    load_frags(1, ca, cb, 1);
-    mma(0);
+  // Slice t from stage c: k steps 0..KS-2 with the next step's fragments
+  // in flight; wait for slice t+1; barrier; issue slice t+NS into the freed
+  // stage c; last k step (registers only) under the first fragment reads of
+  // stage c+1.
+  auto slice = [&](int t, auto C_) {
+    constexpr int c = decltype(C_)::value, n = (c + 1) % NS;
+    unsigned char* ca = A_of(IC<c>{});
+    unsigned char* cb = B_of(IC<c>{});
 #pragma unroll
-    for (int i = 0; i < NRD; ++i) { SGB(SG_MFMA, 1); SGB(SG_DS_RD, 1); }
-    SGB(SG_MFMA, NMMA - NRD);
-    __builtin_amdgcn_sched_barrier(0);
-    load_frags(0, ca, cb, 2);
-    mma(1);
+    for (int j = 0; j + 1 < KS; ++j) {
+      load_frags((j + 1) & 1, ca, cb, j + 1);
+      mma(j & 1);
 #pragma unroll
-    for (int i = 0; i < NRD; ++i) { SGB(SG_MFMA, 1); SGB(SG_DS_RD, 1); }
-    SGB(SG_MFMA, NMMA - NRD);
-    __builtin_amdgcn_sched_barrier(0);
-    load_frags(1, ca, cb, 3);
-    mma(0);
-#pragma unroll
-    for (int i = 0; i < NRD; ++i) { SGB(SG_MFMA, 1); SGB(SG_DS_RD, 1); }
-    SGB(SG_MFMA, NMMA - NRD);
-    __builtin_amdgcn_sched_barrier(0);
-    // Slice t+1 (issued after the previous barrier) has landed.
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+      for (int i = 0; i < NMMA; ++i) {
+        SGB(SG_MFMA, 1);
+        if (i < NRD) SGB(SG_DS_RD, 1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // Slice t+1 (issued NS-1 barriers ago) has landed; later ones may fly.
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm((NS - 2) * S::LPS));
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
-    issue(t + 2, ca, cb);
-    load_frags(0, na, nb_, 0);
-    mma(1);
+    issue(t + NS, ca, cb);
+    load_frags(0, A_of(IC<n>{}), B_of(IC<n>{}), 0);
+    mma((KS - 1) & 1);
 #pragma unroll
-    for (int i = 0; i < NRD; ++i) { SGB(SG_MFMA, 1); SGB(SG_DS_RD, 1); SGB(SG_VMEM_RD, 1); }
-    SGB(SG_MFMA, NMMA - NRD);
+    for (int i = 0; i < NMMA; ++i) {
+      SGB(SG_MFMA, 1);
+      if (i < NRD) SGB(SG_DS_RD, 1);
+      if (i < S::LPS) SGB(SG_VMEM_RD, 1);
+    }
     __builtin_amdgcn_sched_barrier(0);
   };
+
   if (T > 0) {
-    issue(0, lds_a0, lds_b0);
-    issue(1, lds_a1, lds_b1);
-    static_assert(IA + IB <= 63, "vmcnt field");
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(IA + IB));  // slice 0 landed
+    static_for([&](auto I) { issue(decltype(I)::value, A_of(I), B_of(I)); },
+               std::make_integer_sequence<int, NS>{});
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm((NS - 1) * S::LPS));  // slice 0 landed
     __syncthreads();
-    load_frags(0, lds_a0, lds_b0, 0);
+    load_frags(0, la0, lb0, 0);
     int t = 0;
-    for (; t + 1 < T; t += 2) {
-      slice(t, lds_a0, lds_b0, lds_a1, lds_b1);
-      slice(t + 1, lds_a1, lds_b1, lds_a0, lds_b0);
-    }
-    if (t < T) slice(t, lds_a0, lds_b0, lds_a1, lds_b1);
-    // The copies of slices T and T+1 (out of range: they write zeros) must
-    // land before the epilogue reuses the LDS.
+    for (; t + NS <= T; t += NS)
+      static_for([&](auto I) { slice(t + decltype(I)::value, I); }, std::make_integer_sequence<int, NS>{});
+    static_for([&](auto I) { if (t + decltype(I)::value < T) slice(t + decltype(I)::value, I); },
+               std::make_integer_sequence<int, NS>{});
+    // The copies of the slices past T (out of range: they write zeros)
+    // must land before the epilogue reuses the LDS.
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   }
   __syncthreads();
@@ -307,9 +352,17 @@ hgemm_tr_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
   // Epilogue.  acc[nb][mb] register r of lane l holds C[m][n] with
   // m = wm0 + 32mb + l%32 and n = wn0 + 32nb + 8(r/4) + 4(l/32) + r%4: four
   // consecutive columns per register group.  Stage the wave's FP16 tile in
-  // LDS array `wave` (row-major, 8-byte slots swizzled by row), then write
-  // it out in 16-byte row chunks, WN/8 lanes per row segment.
-  unsigned char* ep = wave == 0 ? lds_a0 : wave == 1 ? lds_a1 : wave == 2 ? lds_b0 : lds_b1;
+  // its P arrays (row-major, 8-byte slots swizzled by row), then write it
+  // out in 16-byte row chunks.
+  unsigned char* ep[S::P];
+  static_for([&](auto I) {
+    constexpr int i = decltype(I)::value;
+    unsigned char* sel = E_of(IC<i>{});
+    static_for([&](auto W) {
+      if (wave == decltype(W)::value) sel = E_of(IC<decltype(W)::value * S::P + i>{});
+    }, std::make_integer_sequence<int, S::NW>{});
+    ep[i] = sel;
+  }, std::make_integer_sequence<int, S::P>{});
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
@@ -320,19 +373,20 @@ hgemm_tr_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
         v.x = f16_bits(acc[nb][mb][4 * rq + 0]) | ((unsigned)f16_bits(acc[nb][mb][4 * rq + 1]) << 16);
         v.y = f16_bits(acc[nb][mb][4 * rq + 2]) | ((unsigned)f16_bits(acc[nb][mb][4 * rq + 3]) << 16);
         const int row = 32 * mb + l % 32, slot = 8 * nb + 2 * rq + l / 32;
-        *reinterpret_cast<uint2*>(ep + S::epi_byte(row, slot)) = v;
+        *reinterpret_cast<uint2*>(ep[row / S::RPA] + S::epi_byte(row % S::RPA, slot)) = v;
       }
   __syncthreads();
-  constexpr int CPR = WN / 8;           // 16-byte chunks per wave-tile row
-  constexpr int RPI = 64 / CPR;         // rows per store instruction
+  constexpr int CPR = S::EPI_CPR, RPI = S::EPI_RPI;
   unsigned short* __restrict__ C = static_cast<unsigned short*>(p.C);
   const int rl = l / CPR, c = l % CPR;
   const int col = n0 + wn0 + 8 * c;
 #pragma unroll
   for (int pass = 0; pass < WM / RPI; ++pass) {
     const int row = pass * RPI + rl;
-    const uint2 lo = *reinterpret_cast<const uint2*>(ep + S::epi_byte(row, 2 * c));
-    const uint2 hi = *reinterpret_cast<const uint2*>(ep + S::epi_byte(row, 2 * c + 1));
+    const unsigned char* e = ep[(pass * RPI) / S::RPA];
+    const int lr = row % S::RPA;
+    const uint2 lo = *reinterpret_cast<const uint2*>(e + S::epi_byte(lr, 2 * c));
+    const uint2 hi = *reinterpret_cast<const uint2*>(e + S::epi_byte(lr, 2 * c + 1));
     const int grow = m0 + wm0 + row;
     if (grow < M && col < N) {
       u32x4 v = {lo.x, lo.y, hi.x, hi.y};
@@ -341,19 +395,17 @@ hgemm_tr_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
   }
 }
 
-template <int BM, int BN, int WM, int WN>
+template <class S>
 hipError_t launch(const Params& p, const TileMap& map, bool vec, hipStream_t stream) {
-  using S = Shape<BM, BN, WM, WN>;
   const int64_t lim = 0x7fffffff;
   // Every offset (rows past M and K included) must fit the 31-bit range.
-  if (!vec || (int64_t)(p.M + BM) * p.lda * 2 > lim || (int64_t)(BK + 2) * p.ldb * 2 > lim ||
+  if (!vec || (int64_t)(p.M + S::BM) * p.lda * 2 > lim || (int64_t)(S::BK + 2) * p.ldb * 2 > lim ||
       ((int64_t)(p.K > 0 ? p.K - 1 : 0) * p.ldb + p.N) * 2 > lim || (int64_t)p.M * p.lda * 2 > lim)
-    return hgemm_launch_shape(BM, BN, WM, WN, p, map, vec, stream);
+    return hgemm_launch_shape(S::BM, S::BN, S::WM, S::WN, p, map, vec, stream);
   const int64_t a_bytes = p.K > 0 ? ((int64_t)(p.M - 1) * p.lda + p.K) * 2 : 0;
   const int64_t b_bytes = p.K > 0 ? ((int64_t)(p.K - 1) * p.ldb + p.N) * 2 : 0;
   const dim3 grid(map.tiles_m * map.tiles_n), block(S::NT);
-  hipLaunchKernelGGL((hgemm_tr_kernel<BM, BN, WM, WN>), grid, block, 0, stream, p, map, a_bytes,
-                     b_bytes);
+  hipLaunchKernelGGL(hgemm_tr_kernel<S>, grid, block, 0, stream, p, map, a_bytes, b_bytes);
   return hipGetLastError();
 }
 
@@ -361,9 +413,9 @@ hipError_t launch(const Params& p, const TileMap& map, bool vec, hipStream_t str
 // exchange of the transpose read), and epilogue staging, all checked for
 // bounds, for matching the element each lane must see, and for bank
 // conflicts.  Returns 0 when valid.
-template <int BM, int BN, int WM, int WN>
+template <class S>
 int layout_check(int banks, int64_t out[2]) {
-  using S = Shape<BM, BN, WM, WN>;
+  constexpr int BM = S::BM, WM = S::WM, WN = S::WN, BK = S::BK;
   int64_t wconf = 0, rconf = 0;
   // Inverse maps of the two tile layouts: LDS byte -> (row, k) / (k, n).
   static int a_row_of[S::A_STAGE], a_k_of[S::A_STAGE], b_k_of[S::B_STAGE], b_n_of[S::B_STAGE];
@@ -374,7 +426,7 @@ int layout_check(int banks, int64_t out[2]) {
       for (int l = 0; l < 64; ++l) {
         const int off = 1024 * (i * S::NW + w) + 16 * l;
         const int r = S::a_dl_row(i, w, l), q = S::a_dl_q(i, w, l);
-        if (r >= BM || q >= 8 || S::a_byte(r, q) != off) return 1;
+        if (r >= BM || q >= S::A_CPR || S::a_byte(r, q) != off) return 1;
         for (int e = 0; e < 8; ++e) {
           if (a_row_of[off + 2 * e] != -1) return 2;
           a_row_of[off + 2 * e] = r;
@@ -400,7 +452,7 @@ int layout_check(int banks, int64_t out[2]) {
   int addr[64];
   for (int w = 0; w < S::NW; ++w) {
     const int wm0 = (w / S::WAVES_N) * WM, wn0 = (w % S::WAVES_N) * WN;
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < S::KS; ++j) {
       for (int mb = 0; mb < S::MB; ++mb) {
         for (int l = 0; l < 64; ++l) {
           addr[l] = S::a_frag(wm0, mb, j, l);
@@ -410,7 +462,7 @@ int layout_check(int banks, int64_t out[2]) {
             const int b = addr[l] + 2 * e;
             if (a_row_of[b] != wm0 + 32 * mb + l % 32 || a_k_of[b] != 16 * j + 8 * (l / 32) + e) return 7;
           }
-          if (addr[l] != S::a_frag(wm0, 0, j, l) + mb * 32 * A_ROW) return 8;
+          if (addr[l] != S::a_frag(wm0, 0, j, l) + mb * 32 * S::A_ROW) return 8;
         }
         rconf += lds_conflicts(addr, 16, banks);
       }
@@ -436,32 +488,37 @@ int layout_check(int banks, int64_t out[2]) {
     }
   }
   // Epilogue staging: writes and reads cover the wave's rows exactly once
-  // and agree on the element.
-  static int ep_row[S::EPI_WAVE], ep_col[S::EPI_WAVE];
-  for (int i = 0; i < S::EPI_WAVE; ++i) ep_row[i] = -1;
+  // per array and agree on the element.
+  constexpr int EW = S::RPA * S::EPI_ROW;
+  static int ep_row[S::P][EW], ep_col[S::P][EW];
+  for (int a = 0; a < S::P; ++a)
+    for (int i = 0; i < EW; ++i) ep_row[a][i] = -1;
   for (int nb = 0; nb < S::NB; ++nb)
     for (int mb = 0; mb < S::MB; ++mb)
       for (int rq = 0; rq < 4; ++rq) {
         for (int l = 0; l < 64; ++l) {
           const int row = 32 * mb + l % 32, slot = 8 * nb + 2 * rq + l / 32;
-          addr[l] = S::epi_byte(row, slot);
-          if (addr[l] < 0 || addr[l] + 8 > S::EPI_WAVE) return 13;
+          const int a = row / S::RPA;
+          addr[l] = S::epi_byte(row % S::RPA, slot);
+          if (a >= S::P || addr[l] < 0 || addr[l] + 8 > EW) return 13;
           for (int e = 0; e < 4; ++e) {
-            if (ep_row[addr[l] + 2 * e] != -1) return 11;
-            ep_row[addr[l] + 2 * e] = row;
-            ep_col[addr[l] + 2 * e] = 32 * nb + 8 * rq + 4 * (l / 32) + e;
+            if (ep_row[a][addr[l] + 2 * e] != -1) return 11;
+            ep_row[a][addr[l] + 2 * e] = row;
+            ep_col[a][addr[l] + 2 * e] = 32 * nb + 8 * rq + 4 * (l / 32) + e;
           }
         }
         wconf += lds_conflicts(addr, 8, banks);
       }
-  constexpr int CPR = WN / 8, RPI = 64 / CPR;
+  constexpr int CPR = S::EPI_CPR, RPI = S::EPI_RPI;
   for (int pass = 0; pass < WM / RPI; ++pass)
     for (int half = 0; half < 2; ++half) {
       for (int l = 0; l < 64; ++l) {
         const int row = pass * RPI + l / CPR, c = l % CPR;
-        addr[l] = S::epi_byte(row, 2 * c + half);
+        const int a = (pass * RPI) / S::RPA;
+        addr[l] = S::epi_byte(row % S::RPA, 2 * c + half);
         for (int e = 0; e < 4; ++e)
-          if (ep_row[addr[l] + 2 * e] != row || ep_col[addr[l] + 2 * e] != 8 * c + 4 * half + e) return 12;
+          if (ep_row[a][addr[l] + 2 * e] != row || ep_col[a][addr[l] + 2 * e] != 8 * c + 4 * half + e)
+            return 12;
       }
       rconf += lds_conflicts(addr, 8, banks);
     }
@@ -470,19 +527,22 @@ int layout_check(int banks, int64_t out[2]) {
   return 0;
 }
 
-#define HGEMM_TR_VARIANT(BM, BN, WM, WN)                                                     \
+#define HGEMM_TR_VARIANT(BM, BN, WM, WN, BK, NS)                                             \
   Variant {                                                                                  \
     gemm_config_t{0, GEMM_DTYPE_F16, GEMM_FAMILY_MFMA, BM, BN, BK, WM, WN,                   \
-                  Shape<BM, BN, WM, WN>::NT, 2, Shape<BM, BN, WM, WN>::LDS_BYTES,            \
-                  GEMM_ORDER_XCD, 4, "tr_f16_" #BM "x" #BN "x64_w" #WM "x" #WN},             \
-        &launch<BM, BN, WM, WN>, &layout_check<BM, BN, WM, WN>                               \
+                  Shape<BM, BN, WM, WN, BK, NS>::NT, NS, Shape<BM, BN, WM, WN, BK, NS>::LDS_BYTES, \
+                  GEMM_ORDER_XCD, 4,                                                         \
+                  "tr_f16_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_s" #NS},                  \
+        &launch<Shape<BM, BN, WM, WN, BK, NS>>, &layout_check<Shape<BM, BN, WM, WN, BK, NS>> \
   }
 
 const Variant kVariants[] = {
-    HGEMM_TR_VARIANT(256, 256, 128, 128),
-    HGEMM_TR_VARIANT(256, 128, 128, 64),
-    HGEMM_TR_VARIANT(128, 256, 64, 128),
-    HGEMM_TR_VARIANT(128, 128, 64, 64),
+    HGEMM_TR_VARIANT(256, 256, 128, 128, 64, 2),
+    HGEMM_TR_VARIANT(256, 256, 128, 128, 32, 4),
+    HGEMM_TR_VARIANT(256, 256, 128, 128, 32, 5),
+    HGEMM_TR_VARIANT(256, 128, 128, 64, 64, 3),
+    HGEMM_TR_VARIANT(128, 256, 64, 128, 64, 3),
+    HGEMM_TR_VARIANT(128, 128, 64, 64, 64, 2),
 };
 
 }  // namespace
