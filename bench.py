@@ -45,31 +45,46 @@ def parse_args():
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
     ap.add_argument("--cpu-threads", type=int, default=16)
     ap.add_argument("--no-check", action="store_true", help="skip the oracle check")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="before the steps, run a plain device copy of this many MiB (read N, "
+                         "write N) three times: the reference kernel that scales HBM counters")
     return ap.parse_args()
 
 
-def source_digest() -> str:
+# Kernel source of each variant family (the traffic figures are tied to it).
+FAMILY_SOURCE = {"mfma_f32": "sgemm_mfma.hip", "simt_f32": "sgemm_simt.hip",
+                 "mfma_f16": "hgemm_mfma.hip", "pipe_f16": "hgemm_pipe.hip",
+                 "tr_f16": "hgemm_tr.hip"}
+
+
+def kernel_digest(variant: str) -> str:
+    """Digest of the sources that define one variant's kernel: its family's
+    file plus the shared index maps and the public header."""
+    family = "_".join(variant.split("_")[:2])
+    files = [os.path.join(ROOT, "dense_gemm_row_amd", "csrc", FAMILY_SOURCE[family]),
+             os.path.join(ROOT, "dense_gemm_row_amd", "csrc", "gemm_internal.h"),
+             os.path.join(ROOT, "include", "gemm.h")]
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "dense_gemm_row_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".h")):
-            with open(os.path.join(csrc, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
+    for path in files:
+        with open(path, "rb") as f:
+            h.update(os.path.basename(path).encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
 
 
-def load_traffic(kernel: str, digest: str):
-    """HBM bytes per launch measured by rocprofv3 counters for this kernel
-    and this exact kernel source, or None."""
+def load_traffic(variant: str, size: int):
+    """HBM bytes per launch that rocprofv3 counters measured for this
+    variant, at this size, from its current source; None when there is no
+    such measurement."""
     path = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
     if not os.path.exists(path):
         return None
+    digest = kernel_digest(variant)
     for line in open(path):
         line = line.strip()
         if not line or line.startswith("#"):
             continue
         kv = dict(tok.split("=", 1) for tok in line.split() if "=" in tok)
-        if kv.get("variant") == kernel and kv.get("source") == digest:
+        if kv.get("variant") == variant and kv.get("source") == digest and kv.get("size") == str(size):
             try:
                 return float(kv["bytes_per_launch"])
             except (KeyError, ValueError):
@@ -133,6 +148,18 @@ def main():
         if st != gemm.GEMM_OK:
             raise gemm.GemmError(st, f"gemm_{k}")
 
+    if args.copy_mib > 0:
+        # Counter calibration: torch.neg over an FP32 buffer is a streaming
+        # copy (each byte read once, written once); a profiler run over this
+        # script sees it next to the GEMM kernels.
+        nel = args.copy_mib * (1 << 20) // 4
+        src = torch.full((nel,), 1.0, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+
     for _ in range(max(args.warmup, 1)):
         for k in kinds:
             launch(k)
@@ -159,45 +186,47 @@ def main():
             print(json.dumps({"error": "parity check failed", "parity": parity}), flush=True)
             sys.exit(1)
 
-    # Timed region: K steps, events around every launch on the launch stream.
-    ev = {k: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)] for k in kinds}
+    # Timed region: K steps.  The launches of one kernel run back to back
+    # (the K SGEMMs, then the K HGEMMs) between events recorded on the launch
+    # stream, so each kernel's average launch duration is its block's time
+    # over K with no event packets between launches.
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(len(kinds) + 1)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
-    for s in range(args.steps):
-        for k in kinds:
-            ev[k][s][0].record(stream)
+    marks[0].record(stream)
+    for i, k in enumerate(kinds):
+        for _ in range(args.steps):
             launch(k)
-            ev[k][s][1].record(stream)
+        marks[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     ms_per_step = wall * 1e3 / args.steps
 
     kernels = {}
-    for k in kinds:
-        times = sorted(e0.elapsed_time(e1) for e0, e1 in ev[k])
-        mean = sum(times) / len(times)
-        med = times[len(times) // 2]
+    for i, k in enumerate(kinds):
+        mean = marks[i].elapsed_time(marks[i + 1]) / args.steps
+        elem = 2 if k == "f16" else 4
         kernels[k] = {
             "variant": cfgs[k].name.decode(), "order": cfgs[k].order, "group_m": cfgs[k].group_m,
-            "ms_mean": round(mean, 5), "ms_median": round(med, 5), "ms_min": round(times[0], 5),
+            "ms_mean": round(mean, 5),
             "tflops": round(flops / (mean * 1e-3) / 1e12, 2),
-            "tflops_median": round(flops / (med * 1e-3) / 1e12, 2),
             "pct_peak": round(100.0 * flops / (mean * 1e-3) / 1e12 / PEAK_TFLOPS[k], 2),
             "peak_tflops": PEAK_TFLOPS[k],
+            "min_bytes_per_launch": 3 * n * n * elem,
         }
 
-    digest = source_digest()
     dom = max(kinds, key=lambda k: kernels[k]["ms_mean"])
 
     def roofline(k):
         kk = kernels[k]
         achieved = flops / (kk["ms_mean"] * 1e-3) / 1e12
-        traffic = load_traffic(kk["variant"], digest)
+        traffic = load_traffic(kk["variant"], n)
         return {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS[k],
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS[k], 4),
-                "traffic": traffic, "kernel": kk["variant"],
-                "algorithmic_flops_per_launch": flops}
+                "traffic": traffic, "traffic_unit": "bytes/launch", "kernel": kk["variant"],
+                "source": kernel_digest(kk["variant"]),
+                "algorithmic_flops_per_launch": flops,
+                "min_bytes_per_launch": kk["min_bytes_per_launch"]}
 
     cpu = None
     if args.cpu_budget > 0:
@@ -246,7 +275,6 @@ def main():
         "roofline_all": {k: roofline(k) for k in kinds},
         "cpu_baseline": cpu,
         "parity": parity,
-        "source_digest": digest,
         "input_gen_s": round(gen_s, 2),
     }
     print(json.dumps(out), flush=True)
