@@ -96,8 +96,8 @@ def main():
     args = parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py runs on one GPU only: this library has no multi-GPU path "
-              "(see DESIGN.md for how the GEMM would shard). Use --gpus 1.", file=sys.stderr)
+        print("bench.py runs on one GPU only: this library has no multi-GPU path (a GEMM "
+              "would shard by rows of A and C, with no exchange). Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

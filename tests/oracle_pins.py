@@ -22,6 +22,7 @@ import numpy as np
 
 import oracle
 from dense_gemm_row_amd import synth
+from tests import golden_data
 
 U64 = 2.0 ** -53  # unit roundoff of binary64
 
@@ -187,8 +188,8 @@ def pin_numpy_matmul(lib):
 
 def pin_f16_decode(lib):
     """Exhaustive binary16 decode against numpy's float16 -> float64, plus
-    closed values: 0x3C00 = 1, 0x7BFF = 65504, 0x0001 = 2**-24,
-    0x0400 = 2**-14, 0x8000 = -0, 0x7C00 = +inf, 0x7E00 = NaN."""
+    the hand-worked patterns of tests/golden/binary16_patterns.txt (zeros,
+    subnormals, the normal range ends, infinities, NaN)."""
     bits = np.arange(65536, dtype=np.uint16)
     mine = _decode(lib, bits)
     ref = bits.view(np.float16).astype(np.float64)
@@ -196,12 +197,14 @@ def pin_f16_decode(lib):
     assert np.array_equal(np.isnan(mine), nan), "NaN patterns"
     assert np.array_equal(mine[~nan], ref[~nan]), "decoded values"
     assert np.array_equal(np.signbit(mine[~nan]), np.signbit(ref[~nan])), "signs"
-    closed = {0x3C00: 1.0, 0x7BFF: 65504.0, 0x0001: 2.0 ** -24, 0x0400: 2.0 ** -14,
-              0x3555: 0.333251953125, 0xC000: -2.0, 0x7C00: float("inf")}
-    for b, v in closed.items():
-        assert lib.oracle_f16_to_f64(b) == v, f"decode 0x{b:04x}"
-    neg0 = lib.oracle_f16_to_f64(0x8000)
-    assert neg0 == 0.0 and np.signbit(neg0), "decode -0"
+    # Patterns worked by hand from the binary16 definition (tests/golden).
+    for bits_s, val_s in golden_data.rows("binary16_patterns.txt"):
+        b, v = int(bits_s, 16), float(val_s)
+        got = lib.oracle_f16_to_f64(b)
+        if np.isnan(v):
+            assert np.isnan(got), f"decode 0x{b:04x}"
+        else:
+            assert got == v and np.signbit(got) == np.signbit(v), f"decode 0x{b:04x}"
 
 
 def _decode(lib, bits):

@@ -14,6 +14,7 @@ import pytest
 
 import oracle
 from dense_gemm_row_amd import gemm, synth
+from tests import golden_data
 from tests.gpu_util import check_full, check_rows, exact_equal, log, run
 
 pytestmark = pytest.mark.gpu
@@ -116,15 +117,20 @@ def test_empty_m_n(kind):
     assert C.shape == (6, 0)
 
 
+def _golden_matrices(name):
+    mats = {}
+    for r in golden_data.rows(name):
+        mats.setdefault(r[0], []).append([int(x, 16) for x in r[2:]])
+    return {k: np.array(v, np.uint16) for k, v in mats.items()}
+
+
 def test_f16_output_rounds_to_nearest_even():
-    # Exact FP32 sums that fall halfway between two FP16 neighbours:
-    #   (1 + 2^-10) * 1.5   = 1.5 + 1.5 ulp : ties-to-even 0x3E02, truncation 0x3E01
-    #   1 + 2^-11           = 1 + 0.5 ulp   : ties-to-even 0x3C00, half-up 0x3C01
-    #   1 + 2^-10 + 2^-11   = 1 + 1.5 ulp   : ties-to-even 0x3C02, truncation 0x3C01
-    h = np.float16
-    A = np.array([[1 + 2 ** -10, 0], [1, 2 ** -11], [1 + 2 ** -10, 2 ** -11]], h)
-    B = np.array([[1.5, 1], [0, 1]], h)
-    expect = np.array([[0x3E02, 0x3C01], [0x3E00, 0x3C00], [0x3E02, 0x3C02]], np.uint16)
+    # Exact FP32 sums that fall halfway between two FP16 neighbours; the
+    # hand-worked expectation is tests/golden/f16_rne_halfway.txt
+    # (ties-to-even differs there from truncation and from half-up).
+    g = _golden_matrices("f16_rne_halfway.txt")
+    A, B, expect = g["A"].view(np.float16), g["B"].view(np.float16), g["C"]
+    assert A.shape == (3, 2) and B.shape == (2, 2) and expect.shape == (3, 2)
     for idx in F16_CFGS:
         log(f"f16 RNE probe cfg={idx}")
         C, _ = run(A, B, _cfg("f16", idx))

@@ -2,14 +2,15 @@
 import numpy as np
 
 from dense_gemm_row_amd import synth
+from tests import golden_data
 
 
 def test_splitmix64_published_sequence():
-    # First outputs of SplitMix64 started from state 0, as printed by the
-    # reference implementation (Vigna's splitmix64.c; Java SplittableRandom
-    # with seed 0 yields the same stream).
-    assert synth.splitmix64(0, 4) == [0xE220A8397B1DCDAF, 0x6E789E6AA1B965F4,
-                                      0x06C45D188009454F, 0xF88BB8A8724C81EC]
+    # First outputs of SplitMix64 started from state 0, as the published
+    # implementations print them (tests/golden/splitmix64_state0.txt).
+    expect = [int(r[0], 16) for r in golden_data.rows("splitmix64_state0.txt")]
+    assert len(expect) == 4
+    assert synth.splitmix64(0, 4) == expect
 
 
 def test_vector_and_scalar_finaliser_agree():
