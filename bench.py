@@ -52,7 +52,7 @@ def parse_args():
 
 
 # Kernel source of each variant family (the traffic figures are tied to it).
-FAMILY_SOURCE = {"mfma_f32": "sgemm_mfma.hip", "simt_f32": "sgemm_simt.hip",
+FAMILY_SOURCE = {"dl_f32": "sgemm_dl.hip", "mfma_f32": "sgemm_mfma.hip", "simt_f32": "sgemm_simt.hip",
                  "mfma_f16": "hgemm_mfma.hip", "pipe_f16": "hgemm_pipe.hip",
                  "tr_f16": "hgemm_tr.hip"}
 

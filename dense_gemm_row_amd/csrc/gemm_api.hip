@@ -61,7 +61,9 @@ struct Table {
   std::vector<Variant> v[2];  // per dtype
   Table() {
     int n = 0;
-    const Variant* p = sgemm_mfma_variants(&n);
+    const Variant* p = sgemm_dl_variants(&n);
+    v[0].insert(v[0].end(), p, p + n);
+    p = sgemm_mfma_variants(&n);
     v[0].insert(v[0].end(), p, p + n);
     p = sgemm_simt_variants(&n);
     v[0].insert(v[0].end(), p, p + n);

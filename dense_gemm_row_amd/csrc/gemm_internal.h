@@ -129,6 +129,7 @@ struct Variant {
 };
 
 // Per-family registration (each kernel file defines its table).
+const Variant* sgemm_dl_variants(int* count);
 const Variant* sgemm_mfma_variants(int* count);
 const Variant* sgemm_simt_variants(int* count);
 const Variant* hgemm_mfma_variants(int* count);
@@ -139,6 +140,10 @@ const Variant* hgemm_tr_variants(int* count);
 // the given workgroup tile (and the given wave tile when it has one); used
 // by the pipelined variants for operands they do not take.
 hipError_t hgemm_launch_shape(int bm, int bn, int wm, int wn, const Params& p, const TileMap& map,
+                              bool vec, hipStream_t stream);
+// The same for FP32: the general SGEMM kernel (sgemm_mfma.hip) with the given
+// workgroup tile, for operands the LDS-direct variants do not take.
+hipError_t sgemm_launch_shape(int bm, int bn, int wm, int wn, const Params& p, const TileMap& map,
                               bool vec, hipStream_t stream);
 
 // Host bank-conflict accounting for one wave-wide LDS access: `addr[64]`

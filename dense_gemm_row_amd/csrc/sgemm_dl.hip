@@ -1,0 +1,448 @@
+// FP32 SGEMM for aligned operands on the gfx950 matrix cores, fed by
+// LDS-direct copies: C = A x B, row-major, FP32 in and out, accumulated by
+// v_mfma_f32_32x32x2_f32.
+//
+// Same arithmetic and register layout as sgemm_mfma.hip (the K permutation
+// inside groups of 8, the column interleave of the B fragment, direct
+// epilogue stores); what changes is how the operands reach LDS and how the
+// loop is scheduled:
+//
+// * A and B go from global memory straight into LDS with
+//   buffer_load_dwordx4 ... lds: one instruction fills 1 KB of LDS per wave,
+//   lane l writing bytes [16l, 16l+16) of the wave's block, so each lane
+//   fetches the 16-byte global chunk whose LDS position is 16l.  The A tile
+//   is row-major (k contiguous, 4*BK-byte rows, chunk XOR swz_row), the B
+//   tile row-major as in memory.  No VGPR staging, no ds_write, no wait for
+//   the copy before a store: the copy of slice t+NS flies while slices
+//   t+1 .. t+NS-1 are computed.
+// * K advances by moving the buffer descriptors' base address and shrinking
+//   their range; loads outside the matrix (rows past M or K, columns past N)
+//   are range-checked by the hardware and return zeros; the last, partial K
+//   slice of A is masked per lane.
+// * Fragments are double-buffered in registers: the LDS reads of k group
+//   g+1 are interleaved with the MFMAs of group g.  One barrier per slice;
+//   the MFMAs of the slice's last group (registers only) run after it,
+//   covering the first fragment reads of the next stage.
+// * NS stages, each its own __shared__ array, the loop unrolled NS times so
+//   that every LDS access names its array statically (the compiler can then
+//   see that a copy into one stage does not alias reads of another).
+//
+// This is the double buffer of "sgemm - beyond cuBLAS" (section 6) with the
+// asynchronous global-to-shared copies of the lqnn.cn SGEMM article
+// (section 3.5), done with gfx950's LDS-direct buffer loads.
+#include <type_traits>
+#include <utility>
+
+#include "gemm_internal.h"
+
+namespace gemm {
+namespace {
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <int NB> struct VecF;
+template <> struct VecF<1> { typedef float T; };
+template <> struct VecF<2> { typedef f32x2 T; };
+template <> struct VecF<4> { typedef f32x4 T; };
+
+constexpr unsigned OOB = 0x80000000u;  // offset past every buffer's range
+constexpr int MAX_STAGES = 4;
+
+template <int I>
+using IC = std::integral_constant<int, I>;
+
+template <class F, int... I>
+__device__ __forceinline__ void static_for(F&& f, std::integer_sequence<int, I...>) {
+  (f(IC<I>{}), ...);
+}
+
+template <int BM_, int BN_, int WM_, int WN_, int BK_, int NS_>
+struct Shape {
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BK_, NS = NS_;
+  static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN, NW = WAVES_M * WAVES_N;
+  static constexpr int NT = NW * 64;
+  static constexpr int MB = WM / 32, NB = WN / 32, KG = BK / 8;  // k groups of 8 per slice
+  static constexpr int A_ROW = BK * 4, A_CPR = A_ROW / 16;       // bytes / chunks per A row
+  static constexpr int B_ROW = BN * 4;                           // bytes per B row
+  static constexpr int A_STAGE = BM * A_ROW, B_STAGE = BK * B_ROW;
+  static constexpr int LDS_BYTES = NS * (A_STAGE + B_STAGE);
+  static constexpr int IA = A_STAGE / 1024 / NW, IB = B_STAGE / 1024 / NW, LPS = IA + IB;
+  static_assert(BK == 16 || BK == 32, "K slice");
+  static_assert(KG % 2 == 0, "fragment double buffer alternates within a slice");
+  static_assert(NS >= 2 && NS <= MAX_STAGES, "stages");
+  static_assert(BM % WM == 0 && BN % WN == 0, "wave grid");
+  static_assert(WM % 32 == 0 && (NB == 1 || NB == 2 || NB == 4), "wave tile");
+  static_assert(A_STAGE % (1024 * NW) == 0 && B_STAGE % (1024 * NW) == 0, "direct-load split");
+  static_assert(B_ROW % 1024 == 0 || 1024 % B_ROW == 0, "B rows tile the 1 KB blocks");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS");
+  static_assert((NS - 1) * LPS <= 63, "vmcnt field");
+  static_assert((MB - 1) * 32 * A_ROW < 65536 && BK * B_ROW < 65536, "immediate offsets");
+
+  // Byte offsets within one stage array.
+  __host__ __device__ static constexpr int a_byte(int r, int q) { return swz_off(r, q, A_ROW); }
+  __host__ __device__ static constexpr int b_byte(int k, int n) { return k * B_ROW + 4 * n; }
+  // Direct loads: lane l of wave w, instruction i.
+  __host__ __device__ static constexpr int a_dl_row(int i, int w, int l) {
+    return (1024 / A_ROW) * (i * NW + w) + l / A_CPR;
+  }
+  __host__ __device__ static constexpr int a_dl_q(int i, int w, int l) {
+    return (l % A_CPR) ^ swz_row(a_dl_row(i, w, l), A_ROW);
+  }
+  __host__ __device__ static constexpr int b_dl_k(int i, int w, int l) {
+    return (1024 * (i * NW + w) + 16 * l) / B_ROW;
+  }
+  __host__ __device__ static constexpr int b_dl_c(int i, int w, int l) {
+    return (1024 * (i * NW + w) + 16 * l) % B_ROW / 16;
+  }
+  // Fragment reads for k group g of a slice.  Within the group, MFMA step s
+  // (0..3) takes physical k = 8g + 4h + s in lane half h = l/32.
+  //  A: lane reads row wm0 + 32mb + l%32, chunk 2g + h (k = 8g + 4h .. +3).
+  __host__ __device__ static constexpr int a_frag(int wm0, int mb, int g, int l) {
+    return a_byte(wm0 + 32 * mb + l % 32, 2 * g + l / 32);
+  }
+  //  B: lane reads row 8g + 4h + s, the NB columns wn0 + NB*(l%32) + nb.
+  __host__ __device__ static constexpr int b_frag(int wn0, int g, int s, int l) {
+    return b_byte(8 * g + 4 * (l / 32) + s, wn0 + NB * (l % 32));
+  }
+};
+
+__device__ inline f32x16 mfma(float a, float b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const unsigned char* base, int64_t bytes) {
+  // Raw buffer (stride 0); num_records in bytes; loads past it return 0.
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(base), 0,
+                                           (int)(bytes > 0 ? bytes : 0), 0x00020000);
+}
+
+constexpr int SG_MFMA = 0x008, SG_VMEM_RD = 0x020, SG_DS_RD = 0x100;
+
+// s_waitcnt immediate: vmcnt(n) (6 bits, split 4 + 2) with expcnt and
+// lgkmcnt left at their maximum (no wait).
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
+#define SGB(mask, n) __builtin_amdgcn_sched_group_barrier((mask), (n), 0)
+
+// Issue the LDS-direct copies of K slice s into one stage.  A device
+// function, not a kernel lambda: lambdas of a kernel are also compiled for
+// the host, and a descriptor value there makes the host pass drop the
+// kernel's launch stub.  Slices past the last one (issued only to keep the
+// wait counts uniform) get empty descriptors and touch no memory.
+template <class S>
+__device__ __forceinline__ void issue_slice(const unsigned char* Ab, const unsigned char* Bb,
+                                            int64_t a_bytes, int64_t b_bytes, int s, bool live,
+                                            const unsigned* a_vo, const unsigned* b_vo,
+                                            unsigned char* lds_a, unsigned char* lds_b, int wave,
+                                            int ldb) {
+  const int64_t ka = 4 * (int64_t)s * S::BK, kb = (int64_t)s * S::BK * ldb * 4;
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(Ab + ka, live ? a_bytes - ka : 0);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bb + kb, live ? b_bytes - kb : 0);
+#pragma unroll
+  for (int i = 0; i < S::IA; ++i) {
+    lds_void* dst = (lds_void*)(lds_a + 1024 * (i * S::NW + wave));
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, dst, 16, a_vo[i], 0, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < S::IB; ++i) {
+    lds_void* dst = (lds_void*)(lds_b + 1024 * (i * S::NW + wave));
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, dst, 16, b_vo[i], 0, 0, 0);
+  }
+}
+
+template <class S>
+__global__ void __launch_bounds__(S::NT)
+sgemm_dl_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
+  constexpr int NS = S::NS, KG = S::KG, MB = S::MB, NB = S::NB, IA = S::IA, IB = S::IB;
+  constexpr int BM = S::BM, BN = S::BN, WM = S::WM, WN = S::WN, BK = S::BK;
+  typedef typename VecF<NB>::T vecNB;
+  typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+  typedef __attribute__((address_space(3))) vecNB lds_vecNB;
+
+  // Stage arrays (unused ones are dropped by the compiler).
+  __shared__ __attribute__((aligned(1024))) unsigned char la0[S::A_STAGE], lb0[S::B_STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char la1[S::A_STAGE], lb1[S::B_STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char la2[S::A_STAGE], lb2[S::B_STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char la3[S::A_STAGE], lb3[S::B_STAGE];
+  auto A_of = [&](auto I) -> unsigned char* {
+    constexpr int i = decltype(I)::value;
+    if constexpr (i == 0) return la0;
+    else if constexpr (i == 1) return la1;
+    else if constexpr (i == 2) return la2;
+    else return la3;
+  };
+  auto B_of = [&](auto I) -> unsigned char* {
+    constexpr int i = decltype(I)::value;
+    if constexpr (i == 0) return lb0;
+    else if constexpr (i == 1) return lb1;
+    else if constexpr (i == 2) return lb2;
+    else return lb3;
+  };
+
+  int tm, tn;
+  tile_of_block(blockIdx.x, map, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int M = p.M, N = p.N, K = p.K;
+  const int lda = (int)p.lda, ldb = (int)p.ldb;
+  const unsigned char* Ab = static_cast<const unsigned char*>(p.A);
+  const unsigned char* Bb = static_cast<const unsigned char*>(p.B);
+
+  const int tid = threadIdx.x;
+  const int l = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm0 = (wave / S::WAVES_N) * WM, wn0 = (wave % S::WAVES_N) * WN;
+  const int T = (K + BK - 1) / BK;
+
+  // Direct-load offsets (relative to the slice's descriptor base).
+  unsigned a_vo[IA], a_vo_tail[IA], b_vo[IB];
+#pragma unroll
+  for (int i = 0; i < IA; ++i) {
+    const int r = S::a_dl_row(i, wave, l), q = S::a_dl_q(i, wave, l);
+    const bool ok = (m0 + r) < M;
+    a_vo[i] = ok ? 4u * ((unsigned)(m0 + r) * (unsigned)lda + 4u * q) : OOB;
+    a_vo_tail[i] = ((T - 1) * BK + 4 * q < K) ? a_vo[i] : OOB;
+  }
+#pragma unroll
+  for (int i = 0; i < IB; ++i) {
+    const int k = S::b_dl_k(i, wave, l), c = S::b_dl_c(i, wave, l);
+    const bool ok = (n0 + 4 * c) < N;
+    b_vo[i] = ok ? 4u * ((unsigned)k * (unsigned)ldb + (unsigned)(n0 + 4 * c)) : OOB;
+  }
+  // Fragment byte offsets: group g of A (other row blocks are immediate
+  // offsets), and group 0 step 0 of B (other steps and groups likewise).
+  int a_fb[KG];
+#pragma unroll
+  for (int g = 0; g < KG; ++g) a_fb[g] = S::a_frag(wm0, 0, g, l);
+  const int b_fb = S::b_frag(wn0, 0, 0, l);
+
+  auto issue = [&](int s, unsigned char* la, unsigned char* lb) __attribute__((always_inline)) {
+    issue_slice<S>(Ab, Bb, a_bytes, b_bytes, s, s < T, s == T - 1 ? a_vo_tail : a_vo, b_vo, la, lb,
+                   wave, ldb);
+  };
+
+  f32x4 fa[2][MB];
+  vecNB fb[2][4];
+  auto load_frags = [&](int buf, const unsigned char* la, const unsigned char* lb, int g)
+      __attribute__((always_inline)) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+      fa[buf][mb] = *(const lds_f32x4*)(la + a_fb[g] + mb * 32 * S::A_ROW);
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      fb[buf][s] = *(const lds_vecNB*)(lb + b_fb + (8 * g + s) * S::B_ROW);
+  };
+
+  f32x16 acc[MB][NB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[mb][nb][r] = 0.f;
+  auto mma = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          float bv;
+          if constexpr (NB == 1) bv = fb[buf][s]; else bv = fb[buf][s][nb];
+          acc[mb][nb] = mfma(fa[buf][mb][s], bv, acc[mb][nb]);
+        }
+  };
+
+  constexpr int NMMA = 4 * MB * NB;  // MFMAs per k group
+  constexpr int NRD = MB + 4;        // LDS reads per k group
+  // (The lambdas are forced inline: a slice of the larger tiles is several
+  // hundred MFMAs, past the inliner's budget, and an out-of-line call would
+  // move the accumulators to scratch memory.)
+  // Slice t from stage c: groups 0..KG-2 with the next group's fragments
+  // in flight; wait for slice t+1; barrier; issue slice t+NS into stage c;
+  // last group's MFMAs under the first fragment reads of stage c+1.
+  auto slice = [&](int t, auto C_) __attribute__((always_inline)) {
+    constexpr int c = decltype(C_)::value, n = (c + 1) % NS;
+    unsigned char* ca = A_of(IC<c>{});
+    unsigned char* cb = B_of(IC<c>{});
+#pragma unroll
+    for (int g = 0; g + 1 < KG; ++g) {
+      load_frags((g + 1) & 1, ca, cb, g + 1);
+      mma(g & 1);
+#pragma unroll
+      for (int i = 0; i < NMMA; ++i) {
+        SGB(SG_MFMA, 1);
+        if (i < NRD) SGB(SG_DS_RD, 1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm((NS - 2) * S::LPS));
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    issue(t + NS, ca, cb);
+    load_frags(0, A_of(IC<n>{}), B_of(IC<n>{}), 0);
+    mma((KG - 1) & 1);
+#pragma unroll
+    for (int i = 0; i < NMMA; ++i) {
+      SGB(SG_MFMA, 1);
+      if (i < NRD) SGB(SG_DS_RD, 1);
+      if (i < S::LPS) SGB(SG_VMEM_RD, 1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  if (T > 0) {
+    static_for([&](auto I) { issue(decltype(I)::value, A_of(I), B_of(I)); },
+               std::make_integer_sequence<int, NS>{});
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm((NS - 1) * S::LPS));  // slice 0 landed
+    __syncthreads();
+    load_frags(0, la0, lb0, 0);
+    int t = 0;
+    for (; t + NS <= T; t += NS)
+      static_for([&](auto I) { slice(t + decltype(I)::value, I); }, std::make_integer_sequence<int, NS>{});
+    static_for([&](auto I) { if (t + decltype(I)::value < T) slice(t + decltype(I)::value, I); },
+               std::make_integer_sequence<int, NS>{});
+    // The copies issued past the last slice still write LDS: they must land
+    // before the workgroup ends and its LDS is handed to another.
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  }
+
+  // Epilogue: acc[mb][nb] register r of lane l holds C[m][n] with
+  // m = wm0 + 32mb + 8(r/4) + 4(l/32) + r%4 and n = wn0 + NB*(l%32) + nb:
+  // the lane's NB columns of a row are adjacent (one 4*NB-byte store; 32
+  // lanes cover 128*NB contiguous bytes of the row).
+  float* __restrict__ C = static_cast<float*>(p.C);
+  const int col = n0 + wn0 + NB * (l % 32);
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = m0 + wm0 + 32 * mb + 8 * (r / 4) + 4 * (l / 32) + (r % 4);
+      if (row < M && col < N) {
+        vecNB v;
+        if constexpr (NB == 1) {
+          v = acc[mb][0][r];
+        } else {
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) v[nb] = acc[mb][nb][r];
+        }
+        *reinterpret_cast<vecNB*>(C + (int64_t)row * p.ldc + col) = v;
+      }
+    }
+}
+
+template <class S>
+hipError_t launch(const Params& p, const TileMap& map, bool vec, hipStream_t stream) {
+  const int64_t lim = 0x7fffffff;
+  // Every offset (rows past M and K included) must fit the 31-bit range.
+  if (!vec || (int64_t)(p.M + S::BM) * p.lda * 4 > lim || (int64_t)(S::BK + 2) * p.ldb * 4 > lim ||
+      ((int64_t)(p.K > 0 ? p.K - 1 : 0) * p.ldb + p.N) * 4 > lim)
+    return sgemm_launch_shape(S::BM, S::BN, S::WM, S::WN, p, map, vec, stream);
+  const int64_t a_bytes = p.K > 0 ? ((int64_t)(p.M - 1) * p.lda + p.K) * 4 : 0;
+  const int64_t b_bytes = p.K > 0 ? ((int64_t)(p.K - 1) * p.ldb + p.N) * 4 : 0;
+  const dim3 grid(map.tiles_m * map.tiles_n), block(S::NT);
+  hipLaunchKernelGGL(sgemm_dl_kernel<S>, grid, block, 0, stream, p, map, a_bytes, b_bytes);
+  return hipGetLastError();
+}
+
+// Host replay: direct-load placement and fragment reads (bounds, the element
+// each lane must see in each MFMA step, bank conflicts).  Returns 0 when
+// valid.
+template <class S>
+int layout_check(int banks, int64_t out[2]) {
+  constexpr int BM = S::BM, BK = S::BK, NB = S::NB;
+  int64_t rconf = 0;
+  static int a_row_of[S::A_STAGE], a_k_of[S::A_STAGE], b_k_of[S::B_STAGE], b_n_of[S::B_STAGE];
+  for (int i = 0; i < S::A_STAGE; ++i) a_row_of[i] = -1;
+  for (int i = 0; i < S::B_STAGE; ++i) b_k_of[i] = -1;
+  for (int i = 0; i < S::IA; ++i)
+    for (int w = 0; w < S::NW; ++w)
+      for (int l = 0; l < 64; ++l) {
+        const int off = 1024 * (i * S::NW + w) + 16 * l;
+        const int r = S::a_dl_row(i, w, l), q = S::a_dl_q(i, w, l);
+        if (r >= BM || q >= S::A_CPR || S::a_byte(r, q) != off) return 1;
+        for (int e = 0; e < 4; ++e) {
+          if (a_row_of[off + 4 * e] != -1) return 2;
+          a_row_of[off + 4 * e] = r;
+          a_k_of[off + 4 * e] = 4 * q + e;
+        }
+      }
+  for (int i = 0; i < S::IB; ++i)
+    for (int w = 0; w < S::NW; ++w)
+      for (int l = 0; l < 64; ++l) {
+        const int off = 1024 * (i * S::NW + w) + 16 * l;
+        const int k = S::b_dl_k(i, w, l), c = S::b_dl_c(i, w, l);
+        if (k >= BK || S::b_byte(k, 4 * c) != off) return 3;
+        for (int e = 0; e < 4; ++e) {
+          if (b_k_of[off + 4 * e] != -1) return 4;
+          b_k_of[off + 4 * e] = k;
+          b_n_of[off + 4 * e] = 4 * c + e;
+        }
+      }
+  for (int i = 0; i < S::A_STAGE; i += 4)
+    if (a_row_of[i] < 0) return 5;
+  for (int i = 0; i < S::B_STAGE; i += 4)
+    if (b_k_of[i] < 0) return 6;
+  int addr[64];
+  for (int w = 0; w < S::NW; ++w) {
+    const int wm0 = (w / S::WAVES_N) * S::WM, wn0 = (w % S::WAVES_N) * S::WN;
+    for (int g = 0; g < S::KG; ++g) {
+      for (int mb = 0; mb < S::MB; ++mb) {
+        for (int l = 0; l < 64; ++l) {
+          addr[l] = S::a_frag(wm0, mb, g, l);
+          if (addr[l] < 0 || addr[l] + 16 > S::A_STAGE) return 7;
+          if (addr[l] != S::a_frag(wm0, 0, g, l) + mb * 32 * S::A_ROW) return 8;
+          // Step s: A[m = wm0 + 32mb + l%32][k = 8g + 4(l/32) + s].
+          for (int s = 0; s < 4; ++s) {
+            const int b = addr[l] + 4 * s;
+            if (a_row_of[b] != wm0 + 32 * mb + l % 32 || a_k_of[b] != 8 * g + 4 * (l / 32) + s) return 9;
+          }
+        }
+        rconf += lds_conflicts(addr, 16, banks);
+      }
+      for (int s = 0; s < 4; ++s) {
+        for (int l = 0; l < 64; ++l) {
+          addr[l] = S::b_frag(wn0, g, s, l);
+          if (addr[l] < 0 || addr[l] + 4 * NB > S::B_STAGE) return 10;
+          if (addr[l] != S::b_frag(wn0, 0, 0, l) + (8 * g + s) * S::B_ROW) return 11;
+          // Block nb, step s: B[k = 8g + 4(l/32) + s][n = wn0 + NB*(l%32) + nb].
+          for (int nb = 0; nb < NB; ++nb) {
+            const int b = addr[l] + 4 * nb;
+            if (b_k_of[b] != 8 * g + 4 * (l / 32) + s || b_n_of[b] != wn0 + NB * (l % 32) + nb) return 12;
+          }
+        }
+        rconf += lds_conflicts(addr, 4 * NB, banks);
+      }
+    }
+  }
+  out[0] = 0;  // no LDS writes by the waves (copies are LDS-direct)
+  out[1] = rconf;
+  return 0;
+}
+
+#define SGEMM_DL_VARIANT(BM, BN, WM, WN, BK, NS, GM)                                         \
+  Variant {                                                                                  \
+    gemm_config_t{0, GEMM_DTYPE_F32, GEMM_FAMILY_MFMA, BM, BN, BK, WM, WN,                   \
+                  Shape<BM, BN, WM, WN, BK, NS>::NT, NS, Shape<BM, BN, WM, WN, BK, NS>::LDS_BYTES, \
+                  GEMM_ORDER_XCD, GM,                                                        \
+                  "dl_f32_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_s" #NS},                  \
+        &launch<Shape<BM, BN, WM, WN, BK, NS>>, &layout_check<Shape<BM, BN, WM, WN, BK, NS>> \
+  }
+
+const Variant kVariants[] = {
+    SGEMM_DL_VARIANT(256, 256, 128, 128, 32, 2, 4),
+    SGEMM_DL_VARIANT(256, 256, 128, 128, 16, 4, 4),
+    SGEMM_DL_VARIANT(256, 128, 128, 64, 32, 3, 8),
+    SGEMM_DL_VARIANT(128, 256, 64, 128, 32, 3, 8),
+    SGEMM_DL_VARIANT(128, 128, 64, 64, 32, 3, 8),
+};
+
+}  // namespace
+
+const Variant* sgemm_dl_variants(int* count) {
+  *count = sizeof(kVariants) / sizeof(kVariants[0]);
+  return kVariants;
+}
+
+}  // namespace gemm

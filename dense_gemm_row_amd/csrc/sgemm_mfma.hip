@@ -329,12 +329,24 @@ const Variant kVariants[] = {
     SGEMM_MFMA_VARIANT(128, 128, 32, 64, 64),
     SGEMM_MFMA_VARIANT(128, 128, 16, 64, 64),
     SGEMM_MFMA_VARIANT(256, 128, 32, 128, 64),
+    SGEMM_MFMA_VARIANT(256, 256, 32, 128, 128),
     SGEMM_MFMA_VARIANT(128, 256, 32, 64, 128),
     SGEMM_MFMA_VARIANT(64, 64, 32, 32, 32),
     SGEMM_MFMA_VARIANT(128, 64, 32, 64, 32),
 };
 
 }  // namespace
+
+hipError_t sgemm_launch_shape(int bm, int bn, int wm, int wn, const Params& p, const TileMap& map,
+                              bool vec, hipStream_t stream) {
+  // The tile map depends on the workgroup tile only: any wave split of the
+  // same bm x bn tile computes the same tiles.  Prefer the same wave tile.
+  const Variant* pick = nullptr;
+  for (const Variant& v : kVariants)
+    if (v.desc.bm == bm && v.desc.bn == bn && (!pick || (v.desc.wm == wm && v.desc.wn == wn)))
+      pick = &v;
+  return pick ? pick->launch(p, map, vec, stream) : hipErrorInvalidValue;
+}
 
 const Variant* sgemm_mfma_variants(int* count) {
   *count = sizeof(kVariants) / sizeof(kVariants[0]);

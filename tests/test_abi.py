@@ -179,11 +179,13 @@ def test_tuning_table(tmp_path):
         gemm.gemm_select_config(gemm.DTYPE_F32, 333, 444, 555).id != cfg.id
 
 
-def test_every_pipelined_variant_has_a_general_fallback():
-    """Unaligned operands of a pipelined FP16 variant run the general kernel
-    with the same workgroup tile (same tile map), which must exist."""
-    cfgs = gemm.configs(gemm.DTYPE_F16)
+@pytest.mark.parametrize("dt", [gemm.DTYPE_F32, gemm.DTYPE_F16])
+def test_every_pipelined_variant_has_a_general_fallback(dt):
+    """Unaligned operands of an LDS-direct or pipelined variant run the
+    general kernel with the same workgroup tile (same tile map), which must
+    exist."""
+    cfgs = gemm.configs(dt)
     general = {(c.bm, c.bn) for c in cfgs if c.name.decode().startswith("mfma_")}
     for c in cfgs:
-        if c.name.decode().startswith("pipe_"):
+        if c.name.decode().startswith(("pipe_", "tr_", "dl_")):
             assert (c.bm, c.bn) in general, c.name
