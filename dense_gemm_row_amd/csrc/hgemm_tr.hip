@@ -29,10 +29,15 @@
 //   last, partial K slice of A is masked per lane.  Fragment addresses are
 //   per-lane constants plus immediate offsets.
 // * NS LDS stages (K slices of BK = 32 or 64), one barrier per slice; the
-//   copy of slice t+NS is issued right after the barrier that frees its
-//   stage, so a copy has NS-1 slices of MFMA work to land; the last k step's
-//   MFMAs (registers only) run after the barrier, covering the first
-//   fragment reads of the next stage.  This generalises the double buffer of
+//   last k step's MFMAs (registers only) run after the barrier, covering
+//   the first fragment reads of the next stage.  With two stages the copy
+//   of slice t+2 is issued in one burst right after the barrier that frees
+//   its stage.  With three or more, the copies of slice t+NS-1 are spread
+//   evenly over all k steps of slice t (a few per k step between MFMAs):
+//   a wave that issues an LDS-direct copy can stall at issue when the
+//   vector memory path is busy, and a burst of copies stalls the MFMA
+//   stream behind it.  The barrier itself carries no memory fence (see
+//   loop_barrier), so copies of later slices stay in flight across it.  This generalises the double buffer of
 //   "sgemm - beyond cuBLAS" (section 6) with the asynchronous copies that
 //   the lqnn.cn SGEMM article adds in section 3.5.  Each stage is its own
 //   __shared__ array and the loop is unrolled NS times, so every access
@@ -77,11 +82,17 @@ struct Shape {
   static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN, NW = WAVES_M * WAVES_N;
   static constexpr int NT = NW * 64;
   static constexpr int MB = WM / 32, NB = WN / 32, KS = BK / 16;
+  static constexpr int NMMA_ = MB * NB;  // MFMAs per k step
   static constexpr int A_ROW = BK * 2, A_CPR = A_ROW / 16;  // bytes / chunks per A row
   static constexpr int B_ROW = BN * 2, B_CPR = B_ROW / 16;  // bytes / chunks per B row
   static constexpr int A_STAGE = BM * A_ROW, B_STAGE = BK * B_ROW;
   static constexpr int LDS_BYTES = NS * (A_STAGE + B_STAGE);
   static constexpr int IA = A_STAGE / 1024 / NW, IB = B_STAGE / 1024 / NW, LPS = IA + IB;
+  // With three or more stages a slice's copies are spread over the k steps
+  // of the slice before (PP per step); with two they go out in one burst
+  // after the barrier that frees their stage.
+  static constexpr bool SPREAD = NS >= 3;
+  static constexpr int PP = LPS / KS;
   // Epilogue: wave w stages its tile in P of the 2*NS stage arrays
   // (A arrays first), RPA rows per array.
   static constexpr int EPI_ROW = WN * 2, EPI_SPR = WN / 4;
@@ -95,6 +106,11 @@ struct Shape {
   static_assert(B_CPR >= 16, "B rows of at least 256 bytes (the k%4 chunk XOR)");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
   static_assert((NS - 1) * LPS <= 63, "vmcnt field");
+  static_assert(!SPREAD || (LPS % KS == 0 && PP <= NMMA_), "copies split evenly over k steps");
+  // Spread: MFMA slot i of a k step carries a copy when i*PP/NMMA steps up.
+  __host__ __device__ static constexpr bool copy_slot(int i) {
+    return (i + 1) * PP / NMMA_ > i * PP / NMMA_;
+  }
   static_assert(P >= 1 && WM % P == 0 && RPA % 32 == 0 && RPA % EPI_RPI == 0 &&
                 RPA * EPI_ROW <= A_STAGE && RPA * EPI_ROW <= B_STAGE, "epilogue staging");
   // Fragment reads use a per-lane base plus immediate offsets (< 64 KB).
@@ -157,6 +173,24 @@ constexpr int SG_MFMA = 0x008, SG_VMEM_RD = 0x020, SG_DS_RD = 0x100;
 // s_waitcnt immediate: vmcnt(n) (6 bits, split 4 + 2) with expcnt and
 // lgkmcnt left at their maximum (no wait).
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
+// The same with lgkmcnt(0): this wave's LDS reads have returned.
+constexpr int waitcnt_vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0070; }
+
+// Workgroup barrier for the K loop, after this wave's fragment reads have
+// returned and all but its N most recent copies have landed.  No memory
+// fence: the loop's only LDS traffic is the fragment reads and the
+// LDS-direct copies, both covered by the explicit wait, while the release
+// fence of __syncthreads() would also wait for every copy still in flight
+// (vmcnt(0)) and collapse the stage pipeline to one slice.
+// (The empty asm statements keep the compiler from moving memory accesses
+// across the barrier, which the fence would otherwise have prevented.)
+template <int N>
+__device__ __forceinline__ void loop_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(N));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 #define SGB(mask, n) __builtin_amdgcn_sched_group_barrier((mask), (n), 0)
 
 // Issue the LDS-direct copies of K slice s into one stage.  The buffer
@@ -165,7 +199,7 @@ constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
 // zeros.  A device function rather than a kernel lambda: lambdas of a kernel
 // are also compiled for the host, and a descriptor value there makes the
 // host pass drop the kernel's launch stub.
-template <class S>
+template <class S, int Q0 = 0, int Q1 = S::LPS>
 __device__ __forceinline__ void issue_slice(const unsigned char* Ab, const unsigned char* Bb,
                                             int64_t a_bytes, int64_t b_bytes, int s, bool live,
                                             const unsigned* a_vo, const unsigned* b_vo,
@@ -176,15 +210,16 @@ __device__ __forceinline__ void issue_slice(const unsigned char* Ab, const unsig
   const int64_t ka = 2 * (int64_t)s * S::BK, kb = (int64_t)s * S::BK * ldb * 2;
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(Ab + ka, live ? a_bytes - ka : 0);
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bb + kb, live ? b_bytes - kb : 0);
+  // Copy instructions Q0 .. Q1-1 of the slice: A's IA blocks, then B's IB.
 #pragma unroll
-  for (int i = 0; i < S::IA; ++i) {
-    lds_void* dst = (lds_void*)(lds_a + 1024 * (i * S::NW + wave));
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, dst, 16, a_vo[i], 0, 0, 0);
-  }
-#pragma unroll
-  for (int i = 0; i < S::IB; ++i) {
-    lds_void* dst = (lds_void*)(lds_b + 1024 * (i * S::NW + wave));
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, dst, 16, b_vo[i], 0, 0, 0);
+  for (int q = Q0; q < Q1; ++q) {
+    if (q < S::IA) {
+      lds_void* dst = (lds_void*)(lds_a + 1024 * (q * S::NW + wave));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, dst, 16, a_vo[q], 0, 0, 0);
+    } else {
+      lds_void* dst = (lds_void*)(lds_b + 1024 * ((q - S::IA) * S::NW + wave));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, dst, 16, b_vo[q - S::IA], 0, 0, 0);
+    }
   }
 }
 
@@ -261,13 +296,20 @@ hgemm_tr_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) b_fb[nb] = S::b_frag(wn0, nb, 0, 0, l);
 
-  auto issue = [&](int s, unsigned char* la, unsigned char* lb) {
+  auto issue = [&](int s, unsigned char* la, unsigned char* lb) __attribute__((always_inline)) {
     issue_slice<S>(Ab, Bb, a_bytes, b_bytes, s, s < T, s == T - 1 ? a_vo_tail : a_vo, b_vo, la, lb,
                    wave, ldb);
   };
+  // Part j (of KS) of slice s's copies.
+  auto issue_part = [&](int s, auto J, unsigned char* la, unsigned char* lb) __attribute__((always_inline)) {
+    constexpr int j = decltype(J)::value;
+    issue_slice<S, j * S::PP, (j + 1) * S::PP>(Ab, Bb, a_bytes, b_bytes, s, s < T,
+                                               s == T - 1 ? a_vo_tail : a_vo, b_vo, la, lb, wave, ldb);
+  };
 
   f16x8 fa[2][MB], fb[2][NB];
-  auto load_frags = [&](int buf, const unsigned char* la, const unsigned char* lb, int j) {
+  auto load_frags = [&](int buf, const unsigned char* la, const unsigned char* lb, int j)
+      __attribute__((always_inline)) {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
       fa[buf][mb] = *(const lds_f16x8*)(la + a_fb[j] + mb * 32 * S::A_ROW);
@@ -288,55 +330,76 @@ hgemm_tr_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[nb][mb][r] = 0.f;
-  auto mma = [&](int buf) {
+  auto mma = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) acc[nb][mb] = mfma(fb[buf][nb], fa[buf][mb], acc[nb][mb]);
   };
 
+  // (The lambdas are forced inline: an out-of-line call would move the
+  // accumulators to scratch memory.)
   constexpr int NMMA = MB * NB;     // MFMAs per k step
   constexpr int NRD = MB + 2 * NB;  // LDS reads per k step
   // Slice t from stage c: k steps 0..KS-2 with the next step's fragments
   // in flight; wait for slice t+1; barrier; issue slice t+NS into the freed
   // stage c; last k step (registers only) under the first fragment reads of
   // stage c+1.
-  auto slice = [&](int t, auto C_) {
-    constexpr int c = decltype(C_)::value, n = (c + 1) % NS;
+  auto slice = [&](int t, auto C_) __attribute__((always_inline)) {
+    constexpr int c = decltype(C_)::value, n = (c + 1) % NS, f = (c + NS - 1) % NS;
     unsigned char* ca = A_of(IC<c>{});
     unsigned char* cb = B_of(IC<c>{});
-#pragma unroll
-    for (int j = 0; j + 1 < KS; ++j) {
+    static_for([&](auto J) __attribute__((always_inline)) {
+      constexpr int j = decltype(J)::value;
       load_frags((j + 1) & 1, ca, cb, j + 1);
+      // Spread: parts 1..KS-1 of slice t+NS-1 into stage f (free since the
+      // last barrier), the PP copies evenly among the k step's MFMAs.
+      if constexpr (S::SPREAD) issue_part(t + NS - 1, IC<j + 1>{}, A_of(IC<f>{}), B_of(IC<f>{}));
       mma(j & 1);
 #pragma unroll
       for (int i = 0; i < NMMA; ++i) {
         SGB(SG_MFMA, 1);
         if (i < NRD) SGB(SG_DS_RD, 1);
+        if constexpr (S::SPREAD)
+          if (S::copy_slot(i)) SGB(SG_VMEM_RD, 1);
       }
       __builtin_amdgcn_sched_barrier(0);
-    }
-    // Slice t+1 (issued NS-1 barriers ago) has landed; later ones may fly.
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm((NS - 2) * S::LPS));
-    __syncthreads();
+    }, std::make_integer_sequence<int, KS - 1>{});
+    // Slice t+1 has landed; the copies of the later slices may still fly.
+    loop_barrier<(NS - 2) * S::LPS>();
     __builtin_amdgcn_sched_barrier(0);
-    issue(t + NS, ca, cb);
+    // Stage c is free now: slice t+NS goes there (burst: all of it; spread:
+    // part 0, the rest during the next slice's k steps).
+    if constexpr (S::SPREAD) issue_part(t + NS, IC<0>{}, ca, cb);
+    else issue(t + NS, ca, cb);
     load_frags(0, A_of(IC<n>{}), B_of(IC<n>{}), 0);
     mma((KS - 1) & 1);
 #pragma unroll
     for (int i = 0; i < NMMA; ++i) {
       SGB(SG_MFMA, 1);
       if (i < NRD) SGB(SG_DS_RD, 1);
-      if (i < S::LPS) SGB(SG_VMEM_RD, 1);
+      if constexpr (S::SPREAD) {
+        if (S::copy_slot(i)) SGB(SG_VMEM_RD, 1);
+      } else {
+        if (i < S::LPS) SGB(SG_VMEM_RD, 1);
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
   };
 
   if (T > 0) {
-    static_for([&](auto I) { issue(decltype(I)::value, A_of(I), B_of(I)); },
-               std::make_integer_sequence<int, NS>{});
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm((NS - 1) * S::LPS));  // slice 0 landed
-    __syncthreads();
+    if constexpr (S::SPREAD) {
+      // Slices 0..NS-2 whole, part 0 of slice NS-1 (the first slice's k
+      // steps issue the rest); then wait for slice 0.
+      static_for([&](auto I) { issue(decltype(I)::value, A_of(I), B_of(I)); },
+                 std::make_integer_sequence<int, NS - 1>{});
+      issue_part(NS - 1, IC<0>{}, A_of(IC<NS - 1>{}), B_of(IC<NS - 1>{}));
+      loop_barrier<(NS - 2) * S::LPS + S::PP>();  // slice 0 landed
+    } else {
+      static_for([&](auto I) { issue(decltype(I)::value, A_of(I), B_of(I)); },
+                 std::make_integer_sequence<int, NS>{});
+      loop_barrier<(NS - 1) * S::LPS>();  // slice 0 landed
+    }
     load_frags(0, la0, lb0, 0);
     int t = 0;
     for (; t + NS <= T; t += NS)

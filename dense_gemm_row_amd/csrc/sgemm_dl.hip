@@ -124,6 +124,24 @@ constexpr int SG_MFMA = 0x008, SG_VMEM_RD = 0x020, SG_DS_RD = 0x100;
 // s_waitcnt immediate: vmcnt(n) (6 bits, split 4 + 2) with expcnt and
 // lgkmcnt left at their maximum (no wait).
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
+// The same with lgkmcnt(0): this wave's LDS reads have returned.
+constexpr int waitcnt_vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0070; }
+
+// Workgroup barrier for the K loop, after this wave's fragment reads have
+// returned and all but its N most recent copies have landed.  No memory
+// fence: the loop's only LDS traffic is the fragment reads and the
+// LDS-direct copies, both covered by the explicit wait, while the release
+// fence of __syncthreads() would also wait for every copy still in flight
+// (vmcnt(0)) and collapse the stage pipeline to one slice.
+// (The empty asm statements keep the compiler from moving memory accesses
+// across the barrier, which the fence would otherwise have prevented.)
+template <int N>
+__device__ __forceinline__ void loop_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(N));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 #define SGB(mask, n) __builtin_amdgcn_sched_group_barrier((mask), (n), 0)
 
 // Issue the LDS-direct copies of K slice s into one stage.  A device
@@ -277,8 +295,7 @@ sgemm_dl_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm((NS - 2) * S::LPS));
-    __syncthreads();
+    loop_barrier<(NS - 2) * S::LPS>();
     __builtin_amdgcn_sched_barrier(0);
     issue(t + NS, ca, cb);
     load_frags(0, A_of(IC<n>{}), B_of(IC<n>{}), 0);
@@ -295,8 +312,7 @@ sgemm_dl_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
   if (T > 0) {
     static_for([&](auto I) { issue(decltype(I)::value, A_of(I), B_of(I)); },
                std::make_integer_sequence<int, NS>{});
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm((NS - 1) * S::LPS));  // slice 0 landed
-    __syncthreads();
+    loop_barrier<(NS - 1) * S::LPS>();  // slice 0 landed
     load_frags(0, la0, lb0, 0);
     int t = 0;
     for (; t + NS <= T; t += NS)
