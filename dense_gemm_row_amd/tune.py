@@ -1,0 +1,163 @@
+"""Tile and launch tuner for libgemm on the current GPU.
+
+For every requested (dtype, M, N, K) it times each matrix-core variant of
+that dtype under each candidate tile order, on device-resident random
+operands, and keeps the fastest.  It writes the winners as a tuning table,
+the text format that ``gemm_load_tuning`` reads (lines
+``dtype M N K name order group_m``), and prints one JSON report line per
+shape: the winner, the runner-up, and the shape heuristic's own choice,
+each with its mean launch time and TFLOP/s.
+
+    python -m dense_gemm_row_amd.tune --shapes 4096x4096x4096 1024x1024x8192 \\
+        --dtypes f32 f16 --out tuning.txt
+
+Timing: a few untimed launches, then ``--reps`` launches back to back
+between two HIP events on the launch stream (mean per launch).  Every
+candidate passes through the C-ABI with its configuration forced
+(``gemm_f32_ex`` / ``gemm_f16_ex``); a candidate the library rejects is
+skipped.  Library-wide tuning state is left cleared at exit.
+
+(The per-shape table and the search over tiles, waves and orders are the
+autotuning step that the GB300 GEMM article describes for vendor libraries,
+section 5.1, and the tile-size choice the lqnn.cn SGEMM article discusses in
+its closing section, here measured instead of hand-picked.)
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import sys
+
+ORDERS = {"row": 0, "grouped": 1, "xcd": 2}
+
+
+def parse_shape(s: str) -> tuple[int, int, int]:
+    parts = s.lower().split("x")
+    if len(parts) != 3:
+        raise argparse.ArgumentTypeError(f"shape {s!r}: expected MxNxK")
+    M, N, K = (int(p) for p in parts)
+    if min(M, N, K) < 1:
+        raise argparse.ArgumentTypeError(f"shape {s!r}: sizes must be positive")
+    return M, N, K
+
+
+def parse_order(s: str) -> tuple[int, int]:
+    name, _, gm = s.partition(":")
+    if name not in ORDERS:
+        raise argparse.ArgumentTypeError(f"order {s!r}: one of {sorted(ORDERS)}[:group_m]")
+    return ORDERS[name], int(gm) if gm else 1
+
+
+def candidates(gemm, dtype: int, orders: list[tuple[int, int]]):
+    """Every matrix-core variant of `dtype` under every order."""
+    for cfg in gemm.configs(dtype):
+        if cfg.family != gemm.FAMILY_MFMA:
+            continue
+        for order, gm in orders:
+            c = gemm.gemm_get_config(dtype, cfg.id)
+            c.order, c.group_m = order, gm
+            yield c
+
+
+def time_config(gemm, torch, fn, args, cfg, stream, warmup: int, reps: int) -> float | None:
+    """Mean milliseconds per launch, or None if the library rejects it."""
+    for _ in range(warmup):
+        if fn(*args, stream.cuda_stream, cfg) != gemm.GEMM_OK:
+            return None
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        fn(*args, stream.cuda_stream, cfg)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def tune_shape(gemm, torch, kind: str, M: int, N: int, K: int, orders, warmup: int,
+               reps: int) -> dict:
+    dtype = gemm.DTYPE_F32 if kind == "f32" else gemm.DTYPE_F16
+    tdt = torch.float32 if kind == "f32" else torch.float16
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(M * 1000003 + N * 1009 + K)
+    a = (torch.rand((M, K), device=dev, generator=gen) * 2 - 1).to(tdt)
+    b = (torch.rand((K, N), device=dev, generator=gen) * 2 - 1).to(tdt)
+    c = torch.empty((M, N), device=dev, dtype=tdt)
+    fn = gemm.gemm_f32_ex if kind == "f32" else gemm.gemm_f16_ex
+    args = (M, N, K, a.data_ptr(), K, b.data_ptr(), N, c.data_ptr(), N)
+    stream = torch.cuda.current_stream(dev)
+    flops = 2.0 * M * N * K
+    reps_here = max(3, min(reps, int(reps * 4096.0 ** 3 / (M * N * K) + 0.5)))
+
+    results = []
+    for cfg in candidates(gemm, dtype, orders):
+        ms = time_config(gemm, torch, fn, args, cfg, stream, warmup, reps_here)
+        if ms is not None:
+            results.append((ms, cfg.name.decode(), cfg.order, cfg.group_m))
+    results.sort()
+    gemm.gemm_load_tuning(None)
+    h = gemm.gemm_select_config(dtype, M, N, K)
+    h_ms = time_config(gemm, torch, fn, args, h, stream, warmup, reps_here)
+
+    def entry(ms, name, order, gm):
+        return {"variant": name, "order": order, "group_m": gm, "ms": round(ms, 5),
+                "tflops": round(flops / (ms * 1e-3) / 1e12, 2)}
+
+    rep = {"dtype": kind, "M": M, "N": N, "K": K, "candidates": len(results),
+           "all": [[name, order, gm, round(flops / (ms * 1e-3) / 1e12, 1)]
+                   for ms, name, order, gm in results],
+           "best": entry(*results[0]) if results else None,
+           "second": entry(*results[1]) if len(results) > 1 else None,
+           "heuristic": entry(h_ms, h.name.decode(), h.order, h.group_m) if h_ms else None}
+    del a, b, c
+    return rep
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--shapes", nargs="+", type=parse_shape, required=True, help="MxNxK ...")
+    ap.add_argument("--dtypes", nargs="+", choices=["f32", "f16"], default=["f32", "f16"])
+    ap.add_argument("--orders", nargs="+", type=parse_order,
+                    default=[parse_order("xcd:4"), parse_order("xcd:8"), parse_order("grouped:8")],
+                    help="tile orders to try: row | grouped:G | xcd:G")
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--reps", type=int, default=20, help="timed launches at 4096^3 (scaled by size)")
+    ap.add_argument("--out", default=None, help="write the tuning table here")
+    args = ap.parse_args(argv)
+
+    import torch
+
+    from dense_gemm_row_amd import gemm
+
+    if not torch.cuda.is_available():
+        print("tune needs a GPU", file=sys.stderr)
+        return 1
+    gemm.lib()
+    torch.cuda.set_device(0)
+    lines = ["# libgemm tuning table: dtype M N K variant order group_m",
+             f"# written by dense_gemm_row_amd.tune on {torch.cuda.get_device_name(0)}"]
+    for kind in args.dtypes:
+        for M, N, K in args.shapes:
+            rep = tune_shape(gemm, torch, kind, M, N, K, args.orders, args.warmup, args.reps)
+            print(json.dumps(rep), flush=True)
+            b = rep["best"]
+            if b:
+                lines.append(f"# {b['ms']} ms, {b['tflops']} TFLOP/s (heuristic "
+                             f"{rep['heuristic']['variant'] if rep['heuristic'] else '-'}: "
+                             f"{rep['heuristic']['tflops'] if rep['heuristic'] else '-'} TFLOP/s)")
+                lines.append(f"{kind} {M} {N} {K} {b['variant']} {b['order']} {b['group_m']}")
+    gemm.gemm_load_tuning(None)
+    if args.out:
+        with open(args.out, "w") as f:
+            f.write("\n".join(lines) + "\n")
+        st = gemm.gemm_load_tuning(args.out)  # the table must load back
+        gemm.gemm_load_tuning(None)
+        if st != gemm.GEMM_OK:
+            print(f"written table does not load: {gemm.gemm_last_error()}", file=sys.stderr)
+            return 1
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
