@@ -86,7 +86,7 @@ const Table& table() {
 struct TuneEntry {
   int dtype;
   int64_t M, N, K;
-  int id, order, group_m;
+  int id, order, group_m, splits;
 };
 std::vector<TuneEntry> g_tuning;
 std::mutex g_tuning_mu;
@@ -100,47 +100,87 @@ int find_by_name(int dtype, const char* name) {
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Heuristic: among the MFMA variants, prefer the largest tile area that
-// still gives at least one workgroup per CU (256 CUs); otherwise the one
-// with the most workgroups.  Ties go to the earlier table entry.
-gemm_config_t heuristic(int dtype, int64_t M, int64_t N, int64_t K) {
-  (void)K;
-  const auto& v = table().v[dtype];
-  const int64_t kCUs = 256;
-  int best = -1;
-  int64_t best_area = -1, best_tiles = -1;
-  for (size_t i = 0; i < v.size(); ++i) {
-    const gemm_config_t& d = v[i].desc;
-    if (d.family != GEMM_FAMILY_MFMA) continue;
-    const int64_t tiles = cdiv(M, d.bm) * cdiv(N, d.bn);
-    const int64_t area = (int64_t)d.bm * d.bn;
-    if (tiles >= kCUs) {
-      if (best_tiles < kCUs || area > best_area) {
-        best = (int)i;
-        best_area = area;
-        best_tiles = tiles;
-      }
-    } else if (best_tiles < kCUs && (tiles > best_tiles || (tiles == best_tiles && area > best_area))) {
-      best = (int)i;
-      best_area = area;
-      best_tiles = tiles;
-    }
-  }
-  return v[best < 0 ? 0 : best].desc;
+// Split-K chunking: Kc = roundup(ceil(K / splits), 64) (a whole number of
+// K slices for every variant, 16-byte aligned chunk bases), S = ceil(K / Kc).
+constexpr int64_t kChunkAlign = 64;
+void split_shape(int64_t K, int64_t splits, int64_t& S, int64_t& Kc) {
+  if (splits < 1) splits = 1;
+  Kc = cdiv(cdiv(K, splits), kChunkAlign) * kChunkAlign;
+  if (Kc < 1) Kc = kChunkAlign;
+  S = K > 0 ? cdiv(K, Kc) : 1;
 }
 
-gemm_config_t select(int dtype, int64_t M, int64_t N, int64_t K) {
+// Shape heuristic: a cost model over the matrix-core variants (a tuning
+// table entry overrides it for its exact shape).  Times in seconds:
+//   GEMM:   rounds * 2*bm*bn*Kc / (eff * R / w),  rounds = ceil(WGs / slots),
+//           w = workgroups per CU (as LDS allows, at most 2; 1 when there
+//           are no more workgroups than CUs), slots = 256 w,
+//           R = per-CU rate of the best tile with the GPU full (measured
+//           on MI355X at 4096^3), eff = the variant's relative whole-GPU
+//           rate when full;
+//   split:  + (2*S*M*N*4 + M*N*es) bytes / 4 TB/s + a launch, for the
+//           partials written, read back and the result written.
+// Ties go to the earlier table entry.
+struct Choice {
+  int id = -1;
+  int64_t splits = 1;
+  double t = 1e30;
+};
+
+double gemm_seconds(int dtype, const Variant& v, int64_t M, int64_t N, int64_t Kc, int64_t S) {
+  const gemm_config_t& d = v.desc;
+  const double rate = dtype == GEMM_DTYPE_F32 ? 0.59e12 : 4.7e12;
+  int64_t per_cu = (160 * 1024) / (d.lds_bytes > 0 ? d.lds_bytes : 1);
+  per_cu = per_cu < 1 ? 1 : per_cu > 2 ? 2 : per_cu;
+  const int64_t wgs = cdiv(M, d.bm) * cdiv(N, d.bn) * S;
+  const int64_t rounds = cdiv(wgs, 256 * per_cu);
+  const double eff = v.eff > 0.f ? v.eff : 0.1;
+  // A CU running w workgroups at once gives each 1/w of its rate; with
+  // fewer workgroups than CUs each runs alone.
+  const int64_t w = wgs <= 256 ? 1 : per_cu;
+  return (double)rounds * 2.0 * d.bm * d.bn * (double)(Kc > 0 ? Kc : 1) * w / (eff * rate);
+}
+
+Choice heuristic(int dtype, int64_t M, int64_t N, int64_t K, bool allow_split) {
+  const auto& v = table().v[dtype];
+  const double es = dtype == GEMM_DTYPE_F32 ? 4.0 : 2.0;
+  Choice best;
+  for (size_t i = 0; i < v.size(); ++i) {
+    if (v[i].desc.family != GEMM_FAMILY_MFMA) continue;
+    const double t1 = gemm_seconds(dtype, v[i], M, N, K, 1);
+    if (t1 < best.t) best = Choice{(int)i, 1, t1};
+    if (!allow_split || !v[i].launch_partial || M == 0 || N == 0) continue;
+    for (int64_t want = 2; want <= 32; ++want) {
+      int64_t S, Kc;
+      split_shape(K, want, S, Kc);
+      if (S != want) continue;
+      if (Kc < 256) break;
+      const double t = gemm_seconds(dtype, v[i], M, N, Kc, S) +
+                       (2.0 * S * M * N * 4.0 + M * N * es) / 4.0e12 + 4e-6;
+      if (t < best.t) best = Choice{(int)i, S, t};
+    }
+  }
+  if (best.id < 0) best.id = 0;
+  return best;
+}
+
+// Plain calls (split = false) never split; split-K calls may.
+gemm_config_t select(int dtype, int64_t M, int64_t N, int64_t K, bool split = false) {
   {
     std::lock_guard<std::mutex> lk(g_tuning_mu);
     for (const auto& e : g_tuning)
-      if (e.dtype == dtype && e.M == M && e.N == N && e.K == K) {
+      if (e.dtype == dtype && e.M == M && e.N == N && e.K == K && (split || e.splits <= 1)) {
         gemm_config_t d = table().v[dtype][e.id].desc;
         d.order = e.order;
         d.group_m = e.group_m;
+        d.splits = split ? e.splits : 1;
         return d;
       }
   }
-  return heuristic(dtype, M, N, K);
+  const Choice c = heuristic(dtype, M, N, K, split);
+  gemm_config_t d = table().v[dtype][c.id].desc;
+  d.splits = (int32_t)c.splits;
+  return d;
 }
 
 TileMap make_map(const gemm_config_t& c, int64_t M, int64_t N) {
@@ -186,29 +226,56 @@ gemm_status_t validate(int dtype, int64_t M, int64_t N, int64_t K, const void* A
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-gemm_status_t run(int dtype, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
-                  const void* B, int64_t ldb, void* C, int64_t ldc, void* stream,
-                  const gemm_config_t* forced) {
-  g_err[0] = 0;
-  gemm_status_t st = validate(dtype, M, N, K, A, lda, B, ldb, C, ldc);
-  if (st != GEMM_OK) return st;
-  gemm_config_t cfg;
+// Resolves the configuration of a call: the forced one (checked), or the
+// selection for the shape.
+gemm_status_t resolve(int dtype, int64_t M, int64_t N, int64_t K, const gemm_config_t* forced,
+                      bool split, gemm_config_t& cfg) {
   const auto& v = table().v[dtype];
-  if (forced) {
-    if (forced->id < 0 || forced->id >= (int32_t)v.size())
-      return fail(GEMM_ERR_UNSUPPORTED, "config id %d not in the %s table", forced->id,
-                  dtype == GEMM_DTYPE_F32 ? "f32" : "f16");
-    if (forced->order < GEMM_ORDER_ROW || forced->order > GEMM_ORDER_XCD || forced->group_m < 1)
-      return fail(GEMM_ERR_UNSUPPORTED, "bad tile order %d / group_m %d", forced->order,
-                  forced->group_m);
-    cfg = v[forced->id].desc;
-    cfg.order = forced->order;
-    cfg.group_m = forced->group_m;
-  } else {
-    cfg = select(dtype, M, N, K);
+  if (!forced) {
+    cfg = select(dtype, M, N, K, split);
+    return GEMM_OK;
   }
-  if (M == 0 || N == 0) return GEMM_OK;
+  if (forced->id < 0 || forced->id >= (int32_t)v.size())
+    return fail(GEMM_ERR_UNSUPPORTED, "config id %d not in the %s table", forced->id,
+                dtype == GEMM_DTYPE_F32 ? "f32" : "f16");
+  if (forced->order < GEMM_ORDER_ROW || forced->order > GEMM_ORDER_XCD || forced->group_m < 1)
+    return fail(GEMM_ERR_UNSUPPORTED, "bad tile order %d / group_m %d", forced->order,
+                forced->group_m);
+  if (split && forced->splits < 0) return fail(GEMM_ERR_UNSUPPORTED, "negative splits");
+  cfg = v[forced->id].desc;
+  cfg.order = forced->order;
+  cfg.group_m = forced->group_m;
+  cfg.splits = split ? forced->splits : 1;
+  if (split && cfg.splits == 0) {
+    // The model's best split count for this variant.
+    double best = 1e30;
+    cfg.splits = 1;
+    for (int64_t want = 1; want <= 32; ++want) {
+      int64_t S, Kc;
+      split_shape(K, want, S, Kc);
+      if (S != want) continue;
+      if (want > 1 && (Kc < 256 || !v[forced->id].launch_partial)) break;
+      const double es = dtype == GEMM_DTYPE_F32 ? 4.0 : 2.0;
+      const double t = gemm_seconds(dtype, v[forced->id], M, N, Kc, S) +
+                       (S > 1 ? (2.0 * S * M * N * 4.0 + M * N * es) / 4.0e12 + 4e-6 : 0.0);
+      if (t < best) {
+        best = t;
+        cfg.splits = (int32_t)S;
+      }
+    }
+  }
+  return GEMM_OK;
+}
 
+bool vector_path(int dtype, const void* A, int64_t lda, const void* B, int64_t ldb, const void* C,
+                 int64_t ldc, int64_t K, int64_t N) {
+  const int w = dtype == GEMM_DTYPE_F32 ? 4 : 8;  // elements per 16 bytes
+  return aligned16(A) && aligned16(B) && aligned16(C) && lda % w == 0 && ldb % w == 0 &&
+         ldc % w == 0 && K % w == 0 && N % w == 0;
+}
+
+Params make_params(const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc,
+                   int64_t M, int64_t N, int64_t K) {
   Params p;
   p.A = A;
   p.B = B;
@@ -219,11 +286,71 @@ gemm_status_t run(int dtype, int64_t M, int64_t N, int64_t K, const void* A, int
   p.M = (int)M;
   p.N = (int)N;
   p.K = (int)K;
-  const int w = dtype == GEMM_DTYPE_F32 ? 4 : 8;  // elements per 16 bytes
-  const bool vec = aligned16(A) && aligned16(B) && aligned16(C) && lda % w == 0 &&
-                   ldb % w == 0 && ldc % w == 0 && K % w == 0 && N % w == 0;
+  return p;
+}
+
+gemm_status_t launch_plain(int dtype, const gemm_config_t& cfg, int64_t M, int64_t N, int64_t K,
+                           const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
+                           int64_t ldc, void* stream) {
+  const Params p = make_params(A, lda, B, ldb, C, ldc, M, N, K);
+  const bool vec = vector_path(dtype, A, lda, B, ldb, C, ldc, K, N);
   const TileMap map = make_map(cfg, M, N);
-  const hipError_t e = v[cfg.id].launch(p, map, vec, static_cast<hipStream_t>(stream));
+  const hipError_t e = table().v[dtype][cfg.id].launch(p, map, vec, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(GEMM_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+  return GEMM_OK;
+}
+
+gemm_status_t run(int dtype, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                  const void* B, int64_t ldb, void* C, int64_t ldc, void* stream,
+                  const gemm_config_t* forced) {
+  g_err[0] = 0;
+  gemm_status_t st = validate(dtype, M, N, K, A, lda, B, ldb, C, ldc);
+  if (st != GEMM_OK) return st;
+  gemm_config_t cfg;
+  st = resolve(dtype, M, N, K, forced, false, cfg);
+  if (st != GEMM_OK) return st;
+  if (M == 0 || N == 0) return GEMM_OK;
+  return launch_plain(dtype, cfg, M, N, K, A, lda, B, ldb, C, ldc, stream);
+}
+
+gemm_status_t run_splitk(int dtype, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                         const void* B, int64_t ldb, void* C, int64_t ldc, void* ws,
+                         int64_t ws_bytes, void* stream, const gemm_config_t* forced) {
+  g_err[0] = 0;
+  gemm_status_t st = validate(dtype, M, N, K, A, lda, B, ldb, C, ldc);
+  if (st != GEMM_OK) return st;
+  if (ws_bytes < 0) return fail(GEMM_ERR_INVALID_ARG, "negative workspace size");
+  gemm_config_t cfg;
+  st = resolve(dtype, M, N, K, forced, true, cfg);
+  if (st != GEMM_OK) return st;
+  if (M == 0 || N == 0) return GEMM_OK;
+  int64_t S, Kc;
+  split_shape(K, cfg.splits, S, Kc);
+  const Variant& var = table().v[dtype][cfg.id];
+  const bool vec = vector_path(dtype, A, lda, B, ldb, C, ldc, K, N);
+  if (S <= 1 || K == 0 || !vec || !var.launch_partial)
+    return launch_plain(dtype, cfg, M, N, K, A, lda, B, ldb, C, ldc, stream);
+  const int64_t need = S * M * N * 4;
+  if (!ws) return fail(GEMM_ERR_INVALID_ARG, "workspace is NULL (%lld bytes needed)", (long long)need);
+  if (ws_bytes < need)
+    return fail(GEMM_ERR_INVALID_ARG, "workspace of %lld bytes, %lld needed", (long long)ws_bytes,
+                (long long)need);
+  if (!aligned16(ws)) return fail(GEMM_ERR_INVALID_ARG, "workspace not 16-byte aligned");
+  const size_t es = dtype == GEMM_DTYPE_F32 ? 4 : 2;
+  if (overlap(ws, (size_t)need, A, span_bytes(M, K, lda, es)) ||
+      overlap(ws, (size_t)need, B, span_bytes(K, N, ldb, es)) ||
+      overlap(ws, (size_t)need, C, span_bytes(M, N, ldc, es)))
+    return fail(GEMM_ERR_ALIAS, "workspace overlaps A, B or C");
+  Params p = make_params(A, lda, B, ldb, ws, N, M, N, K);
+  p.splits = (int)S;
+  p.kc = (int)Kc;
+  p.c_stride = M * N;
+  const TileMap map = make_map(cfg, M, N);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  hipError_t e = var.launch_partial(p, map, vec, hs);
+  if (e == hipErrorNotSupported)  // offsets beyond the fast kernel's range
+    return launch_plain(dtype, cfg, M, N, K, A, lda, B, ldb, C, ldc, stream);
+  if (e == hipSuccess) e = splitk_reduce(dtype, static_cast<const float*>(ws), (int)S, (int)M, (int)N, C, ldc, hs);
   if (e != hipSuccess) return fail(GEMM_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
   return GEMM_OK;
 }
@@ -258,6 +385,38 @@ gemm_status_t gemm_f16_ex(int64_t M, int64_t N, int64_t K, const gemm_f16_t* A, 
                           void* stream, const gemm_config_t* cfg) {
   if (!cfg) return fail(GEMM_ERR_INVALID_ARG, "cfg is NULL");
   return run(GEMM_DTYPE_F16, M, N, K, A, lda, B, ldb, C, ldc, stream, cfg);
+}
+
+gemm_status_t gemm_f32_splitk(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
+                              const float* B, int64_t ldb, float* C, int64_t ldc, void* workspace,
+                              int64_t workspace_bytes, void* stream, const gemm_config_t* cfg) {
+  return run_splitk(GEMM_DTYPE_F32, M, N, K, A, lda, B, ldb, C, ldc, workspace, workspace_bytes,
+                    stream, cfg);
+}
+
+gemm_status_t gemm_f16_splitk(int64_t M, int64_t N, int64_t K, const gemm_f16_t* A, int64_t lda,
+                              const gemm_f16_t* B, int64_t ldb, gemm_f16_t* C, int64_t ldc,
+                              void* workspace, int64_t workspace_bytes, void* stream,
+                              const gemm_config_t* cfg) {
+  return run_splitk(GEMM_DTYPE_F16, M, N, K, A, lda, B, ldb, C, ldc, workspace, workspace_bytes,
+                    stream, cfg);
+}
+
+int64_t gemm_splitk_workspace_bytes(int32_t dtype, int64_t M, int64_t N, int64_t K, int32_t splits) {
+  if ((dtype != GEMM_DTYPE_F32 && dtype != GEMM_DTYPE_F16) || M < 0 || N < 0 || K < 0) return -1;
+  if (splits <= 0) splits = select(dtype, M, N, K, true).splits;
+  int64_t S, Kc;
+  split_shape(K, splits, S, Kc);
+  return (S > 1 && M > 0 && N > 0) ? S * M * N * 4 : 0;
+}
+
+gemm_status_t gemm_select_splitk_config(int32_t dtype, int64_t M, int64_t N, int64_t K,
+                                        gemm_config_t* out) {
+  if (dtype != GEMM_DTYPE_F32 && dtype != GEMM_DTYPE_F16)
+    return fail(GEMM_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  if (!out || M < 0 || N < 0 || K < 0) return fail(GEMM_ERR_INVALID_ARG, "bad arguments");
+  *out = select(dtype, M, N, K, true);
+  return GEMM_OK;
 }
 
 int32_t gemm_num_configs(int32_t dtype) {
@@ -321,18 +480,20 @@ gemm_status_t gemm_load_tuning(const char* path) {
       if (line[0] == '#' || line[0] == '\n') continue;
       char dt[16], name[64];
       long long M, N, K;
-      int order, gm;
-      if (sscanf(line, "%15s %lld %lld %lld %63s %d %d", dt, &M, &N, &K, name, &order, &gm) != 7) {
+      int order, gm, splits = 1;
+      const int got = sscanf(line, "%15s %lld %lld %lld %63s %d %d %d", dt, &M, &N, &K, name, &order,
+                             &gm, &splits);
+      if (got != 7 && got != 8) {
         fclose(f);
-        return fail(GEMM_ERR_INVALID_ARG, "%s:%d: expected 'dtype M N K name order group_m'", path, lineno);
+        return fail(GEMM_ERR_INVALID_ARG, "%s:%d: expected 'dtype M N K name order group_m [splits]'", path, lineno);
       }
       const int dtype = strcmp(dt, "f32") == 0 ? 0 : strcmp(dt, "f16") == 0 ? 1 : -1;
       const int id = dtype < 0 ? -1 : find_by_name(dtype, name);
-      if (id < 0 || order < GEMM_ORDER_ROW || order > GEMM_ORDER_XCD || gm < 1) {
+      if (id < 0 || order < GEMM_ORDER_ROW || order > GEMM_ORDER_XCD || gm < 1 || splits < 1) {
         fclose(f);
         return fail(GEMM_ERR_INVALID_ARG, "%s:%d: unknown dtype/variant or bad order", path, lineno);
       }
-      entries.push_back(TuneEntry{dtype, M, N, K, id, order, gm});
+      entries.push_back(TuneEntry{dtype, M, N, K, id, order, gm, splits});
     }
     fclose(f);
   }

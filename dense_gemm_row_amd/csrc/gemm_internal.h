@@ -22,6 +22,11 @@ struct Params {
   void* C;
   int64_t lda, ldb, ldc;
   int M, N, K;
+  // Split-K (kernels with a partial form only): workgroup row blockIdx.y =
+  // s < splits computes K range [s*kc, min(K, (s+1)*kc)) into the FP32
+  // partial C + s*c_stride.  splits = 1: the whole K into C.
+  int splits = 1, kc = 0;
+  int64_t c_stride = 0;
 };
 
 // Workgroup -> output tile order.  See gemm_order_t in gemm.h.
@@ -126,6 +131,13 @@ struct Variant {
   gemm_config_t desc;  // id / order / group_m are defaults, filled at init
   LaunchFn launch;
   LayoutFn layout_check;
+  // Launch of the split-K partial products (FP32 output into the
+  // workspace, grid rows = p.splits), or nullptr when the kernel has none.
+  LaunchFn launch_partial;
+  // Throughput of one workgroup of this variant relative to the best tile
+  // of its dtype, both with the GPU full (measured at 4096^3 on MI355X);
+  // the shape heuristic's cost model divides tile work by it.
+  float eff;
 };
 
 // Per-family registration (each kernel file defines its table).
@@ -145,6 +157,12 @@ hipError_t hgemm_launch_shape(int bm, int bn, int wm, int wn, const Params& p, c
 // workgroup tile, for operands the LDS-direct variants do not take.
 hipError_t sgemm_launch_shape(int bm, int bn, int wm, int wn, const Params& p, const TileMap& map,
                               bool vec, hipStream_t stream);
+
+// Split-K reduction: C[i][j] = sum over s < S (in order) of
+// W[s*M*N + i*N + j], written as FP32 (dtype F32) or FP16 rounded to nearest
+// even (dtype F16).  Enqueued on `stream`.
+hipError_t splitk_reduce(int dtype, const float* W, int S, int M, int N, void* C, int64_t ldc,
+                         hipStream_t stream);
 
 // Host bank-conflict accounting for one wave-wide LDS access: `addr[64]`
 // byte addresses of `width` bytes each.  Returns the extra passes over the

@@ -343,20 +343,20 @@ int layout_check(int banks, int64_t out[2]) {
   return 0;
 }
 
-#define HGEMM_MFMA_VARIANT(BM, BN, WM, WN)                                                   \
+#define HGEMM_MFMA_VARIANT(BM, BN, WM, WN, EFF)                                                 \
   Variant {                                                                                  \
     gemm_config_t{0, GEMM_DTYPE_F16, GEMM_FAMILY_MFMA, BM, BN, BK, WM, WN,                   \
                   Shape<BM, BN, WM, WN>::NT, 2, Shape<BM, BN, WM, WN>::LDS_BYTES,            \
-                  GEMM_ORDER_XCD, 4, "mfma_f16_" #BM "x" #BN "x64_w" #WM "x" #WN},           \
-        &launch<BM, BN, WM, WN>, &layout_check<BM, BN, WM, WN>                               \
+                  GEMM_ORDER_XCD, 4, 1, "mfma_f16_" #BM "x" #BN "x64_w" #WM "x" #WN},           \
+        &launch<BM, BN, WM, WN>, &layout_check<BM, BN, WM, WN>, nullptr, EFF                 \
   }
 
 const Variant kVariants[] = {
-    HGEMM_MFMA_VARIANT(256, 256, 128, 128),
-    HGEMM_MFMA_VARIANT(256, 128, 128, 64),
-    HGEMM_MFMA_VARIANT(128, 256, 64, 128),
-    HGEMM_MFMA_VARIANT(128, 128, 64, 64),
-    HGEMM_MFMA_VARIANT(64, 64, 32, 32),
+    HGEMM_MFMA_VARIANT(256, 256, 128, 128, 0.80f),
+    HGEMM_MFMA_VARIANT(256, 128, 128, 64, 0.72f),
+    HGEMM_MFMA_VARIANT(128, 256, 64, 128, 0.72f),
+    HGEMM_MFMA_VARIANT(128, 128, 64, 64, 0.60f),
+    HGEMM_MFMA_VARIANT(64, 64, 32, 32, 0.20f),
 };
 
 }  // namespace

@@ -58,6 +58,7 @@ namespace gemm {
 namespace {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -262,10 +263,16 @@ hgemm_tr_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
   int tm, tn;
   tile_of_block(blockIdx.x, map, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
-  const int M = p.M, N = p.N, K = p.K;
   const int lda = (int)p.lda, ldb = (int)p.ldb;
-  const unsigned char* Ab = static_cast<const unsigned char*>(p.A);
-  const unsigned char* Bb = static_cast<const unsigned char*>(p.B);
+  // Split-K: workgroup row sk takes K chunk [sk*kc, min(K, (sk+1)*kc)); the
+  // operand bases and buffer ranges move to the chunk, C to its partial.
+  const int sk = blockIdx.y;
+  const int kc = p.splits > 1 ? p.kc : p.K;
+  const int M = p.M, N = p.N, K = min(kc, p.K - sk * kc);
+  const unsigned char* Ab = static_cast<const unsigned char*>(p.A) + 2 * (int64_t)sk * kc;
+  const unsigned char* Bb = static_cast<const unsigned char*>(p.B) + 2 * (int64_t)sk * kc * ldb;
+  a_bytes -= 2 * (int64_t)sk * kc;
+  b_bytes -= 2 * (int64_t)sk * kc * ldb;
 
   const int tid = threadIdx.x;
   const int l = tid & 63;
@@ -410,6 +417,28 @@ hgemm_tr_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
     // must land before the epilogue reuses the LDS.
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   }
+  if (p.splits > 1) {
+    // Split-K partial: FP32 C (the workspace) written straight from the
+    // accumulators, no FP16 rounding, no LDS round trip.
+    // acc[nb][mb] register 4rq+e of lane l is C[m][n], m = wm0 + 32mb +
+    // l%32, n = wn0 + 32nb + 8rq + 4(l/32) + e: one 16-byte store each.
+    float* __restrict__ Cf = static_cast<float*>(p.C) + sk * p.c_stride;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          const int row = m0 + wm0 + 32 * mb + l % 32;
+          const int col = n0 + wn0 + 32 * nb + 8 * rq + 4 * (l / 32);
+          if (row < M && col < N) {
+            f32x4 v = {acc[nb][mb][4 * rq], acc[nb][mb][4 * rq + 1], acc[nb][mb][4 * rq + 2],
+                       acc[nb][mb][4 * rq + 3]};
+            *reinterpret_cast<f32x4*>(Cf + (int64_t)row * p.ldc + col) = v;
+          }
+        }
+    return;
+  }
   __syncthreads();
 
   // Epilogue.  acc[nb][mb] register r of lane l holds C[m][n] with
@@ -458,16 +487,20 @@ hgemm_tr_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
   }
 }
 
+// With p.splits > 1 this is the split-K partial launch (FP32 partials).
 template <class S>
 hipError_t launch(const Params& p, const TileMap& map, bool vec, hipStream_t stream) {
   const int64_t lim = 0x7fffffff;
   // Every offset (rows past M and K included) must fit the 31-bit range.
   if (!vec || (int64_t)(p.M + S::BM) * p.lda * 2 > lim || (int64_t)(S::BK + 2) * p.ldb * 2 > lim ||
-      ((int64_t)(p.K > 0 ? p.K - 1 : 0) * p.ldb + p.N) * 2 > lim || (int64_t)p.M * p.lda * 2 > lim)
+      ((int64_t)(p.K > 0 ? p.K - 1 : 0) * p.ldb + p.N) * 2 > lim || (int64_t)p.M * p.lda * 2 > lim) {
+    // The general kernel has no split-K form: the caller runs unsplit.
+    if (p.splits > 1) return hipErrorNotSupported;
     return hgemm_launch_shape(S::BM, S::BN, S::WM, S::WN, p, map, vec, stream);
+  }
   const int64_t a_bytes = p.K > 0 ? ((int64_t)(p.M - 1) * p.lda + p.K) * 2 : 0;
   const int64_t b_bytes = p.K > 0 ? ((int64_t)(p.K - 1) * p.ldb + p.N) * 2 : 0;
-  const dim3 grid(map.tiles_m * map.tiles_n), block(S::NT);
+  const dim3 grid(map.tiles_m * map.tiles_n, p.splits), block(S::NT);
   hipLaunchKernelGGL(hgemm_tr_kernel<S>, grid, block, 0, stream, p, map, a_bytes, b_bytes);
   return hipGetLastError();
 }
@@ -590,22 +623,23 @@ int layout_check(int banks, int64_t out[2]) {
   return 0;
 }
 
-#define HGEMM_TR_VARIANT(BM, BN, WM, WN, BK, NS)                                             \
+#define HGEMM_TR_VARIANT(BM, BN, WM, WN, BK, NS, EFF)                                             \
   Variant {                                                                                  \
     gemm_config_t{0, GEMM_DTYPE_F16, GEMM_FAMILY_MFMA, BM, BN, BK, WM, WN,                   \
                   Shape<BM, BN, WM, WN, BK, NS>::NT, NS, Shape<BM, BN, WM, WN, BK, NS>::LDS_BYTES, \
-                  GEMM_ORDER_XCD, 4,                                                         \
+                  GEMM_ORDER_XCD, 4, 1,                                                      \
                   "tr_f16_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_s" #NS},                  \
-        &launch<Shape<BM, BN, WM, WN, BK, NS>>, &layout_check<Shape<BM, BN, WM, WN, BK, NS>> \
+        &launch<Shape<BM, BN, WM, WN, BK, NS>>, &layout_check<Shape<BM, BN, WM, WN, BK, NS>>, \
+        &launch<Shape<BM, BN, WM, WN, BK, NS>>, EFF                                         \
   }
 
 const Variant kVariants[] = {
-    HGEMM_TR_VARIANT(256, 256, 128, 128, 64, 2),
-    HGEMM_TR_VARIANT(256, 256, 128, 128, 32, 4),
-    HGEMM_TR_VARIANT(256, 256, 128, 128, 32, 5),
-    HGEMM_TR_VARIANT(256, 128, 128, 64, 64, 3),
-    HGEMM_TR_VARIANT(128, 256, 64, 128, 64, 3),
-    HGEMM_TR_VARIANT(128, 128, 64, 64, 64, 2),
+    HGEMM_TR_VARIANT(256, 256, 128, 128, 64, 2, 1.00f),
+    HGEMM_TR_VARIANT(256, 256, 128, 128, 32, 4, 0.99f),
+    HGEMM_TR_VARIANT(256, 256, 128, 128, 32, 5, 0.99f),
+    HGEMM_TR_VARIANT(256, 128, 128, 64, 64, 3, 0.90f),
+    HGEMM_TR_VARIANT(128, 256, 64, 128, 64, 3, 0.89f),
+    HGEMM_TR_VARIANT(128, 128, 64, 64, 64, 2, 0.71f),
 };
 
 }  // namespace

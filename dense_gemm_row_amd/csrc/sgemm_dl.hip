@@ -202,10 +202,16 @@ sgemm_dl_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
   int tm, tn;
   tile_of_block(blockIdx.x, map, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
-  const int M = p.M, N = p.N, K = p.K;
   const int lda = (int)p.lda, ldb = (int)p.ldb;
-  const unsigned char* Ab = static_cast<const unsigned char*>(p.A);
-  const unsigned char* Bb = static_cast<const unsigned char*>(p.B);
+  // Split-K: workgroup row sk takes K chunk [sk*kc, min(K, (sk+1)*kc)); the
+  // operand bases and buffer ranges move to the chunk, C to its partial.
+  const int sk = blockIdx.y;
+  const int kc = p.splits > 1 ? p.kc : p.K;
+  const int M = p.M, N = p.N, K = min(kc, p.K - sk * kc);
+  const unsigned char* Ab = static_cast<const unsigned char*>(p.A) + 4 * (int64_t)sk * kc;
+  const unsigned char* Bb = static_cast<const unsigned char*>(p.B) + 4 * (int64_t)sk * kc * ldb;
+  a_bytes -= 4 * (int64_t)sk * kc;
+  b_bytes -= 4 * (int64_t)sk * kc * ldb;
 
   const int tid = threadIdx.x;
   const int l = tid & 63;
@@ -328,7 +334,7 @@ sgemm_dl_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
   // m = wm0 + 32mb + 8(r/4) + 4(l/32) + r%4 and n = wn0 + NB*(l%32) + nb:
   // the lane's NB columns of a row are adjacent (one 4*NB-byte store; 32
   // lanes cover 128*NB contiguous bytes of the row).
-  float* __restrict__ C = static_cast<float*>(p.C);
+  float* __restrict__ C = static_cast<float*>(p.C) + sk * p.c_stride;
   const int col = n0 + wn0 + NB * (l % 32);
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
@@ -353,11 +359,14 @@ hipError_t launch(const Params& p, const TileMap& map, bool vec, hipStream_t str
   const int64_t lim = 0x7fffffff;
   // Every offset (rows past M and K included) must fit the 31-bit range.
   if (!vec || (int64_t)(p.M + S::BM) * p.lda * 4 > lim || (int64_t)(S::BK + 2) * p.ldb * 4 > lim ||
-      ((int64_t)(p.K > 0 ? p.K - 1 : 0) * p.ldb + p.N) * 4 > lim)
+      ((int64_t)(p.K > 0 ? p.K - 1 : 0) * p.ldb + p.N) * 4 > lim) {
+    // The general kernel has no split-K form: the caller runs unsplit.
+    if (p.splits > 1) return hipErrorNotSupported;
     return sgemm_launch_shape(S::BM, S::BN, S::WM, S::WN, p, map, vec, stream);
+  }
   const int64_t a_bytes = p.K > 0 ? ((int64_t)(p.M - 1) * p.lda + p.K) * 4 : 0;
   const int64_t b_bytes = p.K > 0 ? ((int64_t)(p.K - 1) * p.ldb + p.N) * 4 : 0;
-  const dim3 grid(map.tiles_m * map.tiles_n), block(S::NT);
+  const dim3 grid(map.tiles_m * map.tiles_n, p.splits), block(S::NT);
   hipLaunchKernelGGL(sgemm_dl_kernel<S>, grid, block, 0, stream, p, map, a_bytes, b_bytes);
   return hipGetLastError();
 }
@@ -437,21 +446,22 @@ int layout_check(int banks, int64_t out[2]) {
   return 0;
 }
 
-#define SGEMM_DL_VARIANT(BM, BN, WM, WN, BK, NS, GM)                                         \
+#define SGEMM_DL_VARIANT(BM, BN, WM, WN, BK, NS, GM, EFF)                                         \
   Variant {                                                                                  \
     gemm_config_t{0, GEMM_DTYPE_F32, GEMM_FAMILY_MFMA, BM, BN, BK, WM, WN,                   \
                   Shape<BM, BN, WM, WN, BK, NS>::NT, NS, Shape<BM, BN, WM, WN, BK, NS>::LDS_BYTES, \
-                  GEMM_ORDER_XCD, GM,                                                        \
+                  GEMM_ORDER_XCD, GM, 1,                                                     \
                   "dl_f32_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_s" #NS},                  \
-        &launch<Shape<BM, BN, WM, WN, BK, NS>>, &layout_check<Shape<BM, BN, WM, WN, BK, NS>> \
+        &launch<Shape<BM, BN, WM, WN, BK, NS>>, &layout_check<Shape<BM, BN, WM, WN, BK, NS>>, \
+        &launch<Shape<BM, BN, WM, WN, BK, NS>>, EFF                                         \
   }
 
 const Variant kVariants[] = {
-    SGEMM_DL_VARIANT(256, 256, 128, 128, 32, 2, 4),
-    SGEMM_DL_VARIANT(256, 256, 128, 128, 16, 4, 4),
-    SGEMM_DL_VARIANT(256, 128, 128, 64, 32, 3, 8),
-    SGEMM_DL_VARIANT(128, 256, 64, 128, 32, 3, 8),
-    SGEMM_DL_VARIANT(128, 128, 64, 64, 32, 3, 8),
+    SGEMM_DL_VARIANT(256, 256, 128, 128, 32, 2, 4, 1.00f),
+    SGEMM_DL_VARIANT(256, 256, 128, 128, 16, 4, 4, 0.99f),
+    SGEMM_DL_VARIANT(256, 128, 128, 64, 32, 3, 8, 0.97f),
+    SGEMM_DL_VARIANT(128, 256, 64, 128, 32, 3, 8, 0.97f),
+    SGEMM_DL_VARIANT(128, 128, 64, 64, 32, 3, 8, 0.95f),
 };
 
 }  // namespace

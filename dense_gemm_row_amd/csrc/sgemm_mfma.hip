@@ -317,22 +317,22 @@ int layout_check(int banks, int64_t out[2]) {
   return 0;
 }
 
-#define SGEMM_MFMA_VARIANT(BM, BN, BK, WM, WN)                                               \
+#define SGEMM_MFMA_VARIANT(BM, BN, BK, WM, WN, EFF)                                               \
   Variant {                                                                                  \
     gemm_config_t{0, GEMM_DTYPE_F32, GEMM_FAMILY_MFMA, BM, BN, BK, WM, WN,                   \
                   Shape<BM, BN, BK, WM, WN>::NT, 2, Shape<BM, BN, BK, WM, WN>::LDS_BYTES,    \
-                  GEMM_ORDER_XCD, 8, "mfma_f32_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN},      \
-        &launch<BM, BN, BK, WM, WN>, &layout_check<BM, BN, BK, WM, WN>                       \
+                  GEMM_ORDER_XCD, 8, 1, "mfma_f32_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN},      \
+        &launch<BM, BN, BK, WM, WN>, &layout_check<BM, BN, BK, WM, WN>, nullptr, EFF         \
   }
 
 const Variant kVariants[] = {
-    SGEMM_MFMA_VARIANT(128, 128, 32, 64, 64),
-    SGEMM_MFMA_VARIANT(128, 128, 16, 64, 64),
-    SGEMM_MFMA_VARIANT(256, 128, 32, 128, 64),
-    SGEMM_MFMA_VARIANT(256, 256, 32, 128, 128),
-    SGEMM_MFMA_VARIANT(128, 256, 32, 64, 128),
-    SGEMM_MFMA_VARIANT(64, 64, 32, 32, 32),
-    SGEMM_MFMA_VARIANT(128, 64, 32, 64, 32),
+    SGEMM_MFMA_VARIANT(128, 128, 32, 64, 64, 0.75f),
+    SGEMM_MFMA_VARIANT(128, 128, 16, 64, 64, 0.72f),
+    SGEMM_MFMA_VARIANT(256, 128, 32, 128, 64, 0.80f),
+    SGEMM_MFMA_VARIANT(256, 256, 32, 128, 128, 0.83f),
+    SGEMM_MFMA_VARIANT(128, 256, 32, 64, 128, 0.80f),
+    SGEMM_MFMA_VARIANT(64, 64, 32, 32, 32, 0.55f),
+    SGEMM_MFMA_VARIANT(128, 64, 32, 64, 32, 0.65f),
 };
 
 }  // namespace

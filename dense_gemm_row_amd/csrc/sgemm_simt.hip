@@ -214,8 +214,8 @@ int layout_check(int banks, int64_t out[2]) {
 
 const Variant kVariants[] = {
     Variant{gemm_config_t{0, GEMM_DTYPE_F32, GEMM_FAMILY_SIMT, BM, BN, BK, 8, 8, NT, 2, LDS_BYTES,
-                          GEMM_ORDER_XCD, 8, "simt_f32_128x128x16_t8x8"},
-            &launch, &layout_check},
+                          GEMM_ORDER_XCD, 8, 1, "simt_f32_128x128x16_t8x8"},
+            &launch, &layout_check, nullptr, 0.32f},
 };
 
 }  // namespace

@@ -6,8 +6,9 @@ if the library is missing, loading raises.
 
 ``matmul`` is a convenience for torch tensors on the GPU: it reads shapes,
 strides, data pointers and the current stream and calls ``gemm_f32`` /
-``gemm_f16`` (or the ``_ex`` forms).  Torch provides memory and streams
-only.
+``gemm_f16`` (or the ``_ex`` forms), or the split-K forms when the library
+says that splitting pays for the shape (then torch allocates the
+workspace).  Torch provides memory and streams only.
 """
 from __future__ import annotations
 
@@ -32,8 +33,9 @@ ORDER_ROW = 0
 ORDER_GROUPED = 1
 ORDER_XCD = 2
 
-EXPORTS = ["gemm_f32", "gemm_f16", "gemm_f32_ex", "gemm_f16_ex", "gemm_num_configs",
-           "gemm_get_config", "gemm_select_config", "gemm_tile_of_block",
+EXPORTS = ["gemm_f32", "gemm_f16", "gemm_f32_ex", "gemm_f16_ex", "gemm_f32_splitk",
+           "gemm_f16_splitk", "gemm_splitk_workspace_bytes", "gemm_select_splitk_config",
+           "gemm_num_configs", "gemm_get_config", "gemm_select_config", "gemm_tile_of_block",
            "gemm_layout_check", "gemm_load_tuning", "gemm_status_string",
            "gemm_last_error", "gemm_version"]
 
@@ -44,7 +46,7 @@ class GemmConfig(ctypes.Structure):
                 ("wm", ctypes.c_int32), ("wn", ctypes.c_int32), ("threads", ctypes.c_int32),
                 ("stages", ctypes.c_int32), ("lds_bytes", ctypes.c_int32),
                 ("order", ctypes.c_int32), ("group_m", ctypes.c_int32),
-                ("name", ctypes.c_char * 48)]
+                ("splits", ctypes.c_int32), ("name", ctypes.c_char * 48)]
 
     def as_dict(self) -> dict:
         d = {f: getattr(self, f) for f, _ in self._fields_}
@@ -77,6 +79,13 @@ def _declare(lib):
     for name in ("gemm_f32_ex", "gemm_f16_ex"):
         getattr(lib, name).argtypes = gemm_args + [cfgp]
         getattr(lib, name).restype = ctypes.c_int
+    for name in ("gemm_f32_splitk", "gemm_f16_splitk"):
+        getattr(lib, name).argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, p, i64, p, cfgp]
+        getattr(lib, name).restype = ctypes.c_int
+    lib.gemm_splitk_workspace_bytes.argtypes = [i32, i64, i64, i64, i32]
+    lib.gemm_splitk_workspace_bytes.restype = i64
+    lib.gemm_select_splitk_config.argtypes = [i32, i64, i64, i64, cfgp]
+    lib.gemm_select_splitk_config.restype = ctypes.c_int
     lib.gemm_num_configs.argtypes = [i32]
     lib.gemm_num_configs.restype = i32
     lib.gemm_get_config.argtypes = [i32, i32, cfgp]
@@ -131,6 +140,30 @@ def gemm_f32_ex(M, N, K, A, lda, B, ldb, C, ldc, stream, cfg: GemmConfig) -> int
 def gemm_f16_ex(M, N, K, A, lda, B, ldb, C, ldc, stream, cfg: GemmConfig) -> int:
     return lib().gemm_f16_ex(M, N, K, A, lda, B, ldb, C, ldc, stream,
                              ctypes.byref(cfg) if cfg is not None else None)
+
+
+def gemm_f32_splitk(M, N, K, A, lda, B, ldb, C, ldc, workspace, workspace_bytes, stream=None,
+                    cfg: GemmConfig | None = None) -> int:
+    return lib().gemm_f32_splitk(M, N, K, A, lda, B, ldb, C, ldc, workspace, workspace_bytes, stream,
+                                 ctypes.byref(cfg) if cfg is not None else None)
+
+
+def gemm_f16_splitk(M, N, K, A, lda, B, ldb, C, ldc, workspace, workspace_bytes, stream=None,
+                    cfg: GemmConfig | None = None) -> int:
+    return lib().gemm_f16_splitk(M, N, K, A, lda, B, ldb, C, ldc, workspace, workspace_bytes, stream,
+                                 ctypes.byref(cfg) if cfg is not None else None)
+
+
+def gemm_splitk_workspace_bytes(dtype: int, M: int, N: int, K: int, splits: int = 0) -> int:
+    return lib().gemm_splitk_workspace_bytes(dtype, M, N, K, splits)
+
+
+def gemm_select_splitk_config(dtype: int, M: int, N: int, K: int) -> GemmConfig:
+    out = GemmConfig()
+    st = lib().gemm_select_splitk_config(dtype, M, N, K, ctypes.byref(out))
+    if st != GEMM_OK:
+        raise GemmError(st, "gemm_select_splitk_config")
+    return out
 
 
 def gemm_num_configs(dtype: int) -> int:
@@ -212,10 +245,15 @@ def _ld(t) -> int:
     return max(int(t.stride(0)), 1) if t.shape[0] > 1 else max(int(t.shape[1]), 1)
 
 
-def matmul(a, b, out=None, config: GemmConfig | None = None, stream=None):
+def matmul(a, b, out=None, config: GemmConfig | None = None, stream=None, split_k: bool = True):
     """C = a @ b on the GPU through libgemm.  a: M x K, b: K x N, both
     float32 or both float16, row-major (any row stride).  Returns ``out``
-    (allocated when None).  Raises GemmError on a non-OK status."""
+    (allocated when None).  Raises GemmError on a non-OK status.
+
+    With ``config`` None and ``split_k`` True, shapes for which the library
+    chooses split-K (too few output tiles for the GPU) run the split-K form
+    with a workspace allocated here; a ``config`` with ``splits`` > 1 forces
+    that split."""
     import torch
     if a.dtype != b.dtype or a.dtype not in (torch.float32, torch.float16):
         raise TypeError("a and b must both be float32 or both float16")
@@ -232,6 +270,18 @@ def matmul(a, b, out=None, config: GemmConfig | None = None, stream=None):
     if stream is None:
         stream = torch.cuda.current_stream(a.device).cuda_stream
     args = (M, N, K, a.data_ptr(), _ld(a), b.data_ptr(), _ld(b), out.data_ptr(), _ld(out), stream)
+    dtype = DTYPE_F32 if a.dtype == torch.float32 else DTYPE_F16
+    split_cfg = config
+    if split_cfg is None and split_k and M > 0 and N > 0:
+        split_cfg = gemm_select_splitk_config(dtype, M, N, K)
+    if split_cfg is not None and split_cfg.splits > 1:
+        nbytes = gemm_splitk_workspace_bytes(dtype, M, N, K, split_cfg.splits)
+        ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=a.device)
+        fn = gemm_f32_splitk if dtype == DTYPE_F32 else gemm_f16_splitk
+        st = fn(*args[:9], ws.data_ptr(), ws.numel(), stream, split_cfg)
+        if st != GEMM_OK:
+            raise GemmError(st, fn.__name__)
+        return out
     if a.dtype == torch.float32:
         st = gemm_f32(*args) if config is None else gemm_f32_ex(*args, config)
     else:

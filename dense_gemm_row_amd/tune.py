@@ -2,7 +2,9 @@
 
 For every requested (dtype, M, N, K) it times each matrix-core variant of
 that dtype under each candidate tile order, on device-resident random
-operands, and keeps the fastest.  It writes the winners as a tuning table,
+operands, and keeps the fastest; with ``--splits`` it also times the
+split-K form at those split counts for variants whose output tiles leave
+CUs idle.  It writes the winners as a tuning table,
 the text format that ``gemm_load_tuning`` reads (lines
 ``dtype M N K name order group_m``), and prints one JSON report line per
 shape: the winner, the runner-up, and the shape heuristic's own choice,
@@ -59,23 +61,28 @@ def candidates(gemm, dtype: int, orders: list[tuple[int, int]]):
             yield c
 
 
-def time_config(gemm, torch, fn, args, cfg, stream, warmup: int, reps: int) -> float | None:
-    """Mean milliseconds per launch, or None if the library rejects it."""
+def time_config(gemm, torch, fn, args, cfg, stream, warmup: int, reps: int, ws=None) -> float | None:
+    """Mean milliseconds per call, or None if the library rejects it.  With
+    `ws` (a device buffer) the call is the split-K form."""
+    extra = () if ws is None else (ws.data_ptr(), ws.numel())
+
+    def call():
+        return fn(*args, *extra, stream.cuda_stream, cfg)
     for _ in range(warmup):
-        if fn(*args, stream.cuda_stream, cfg) != gemm.GEMM_OK:
+        if call() != gemm.GEMM_OK:
             return None
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for _ in range(reps):
-        fn(*args, stream.cuda_stream, cfg)
+        call()
     e1.record(stream)
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / reps
 
 
 def tune_shape(gemm, torch, kind: str, M: int, N: int, K: int, orders, warmup: int,
-               reps: int) -> dict:
+               reps: int, splits=(1,)) -> dict:
     dtype = gemm.DTYPE_F32 if kind == "f32" else gemm.DTYPE_F16
     tdt = torch.float32 if kind == "f32" else torch.float16
     dev = torch.device("cuda:0")
@@ -90,27 +97,46 @@ def tune_shape(gemm, torch, kind: str, M: int, N: int, K: int, orders, warmup: i
     flops = 2.0 * M * N * K
     reps_here = max(3, min(reps, int(reps * 4096.0 ** 3 / (M * N * K) + 0.5)))
 
+    # Split-K candidates (gemm_*_splitk with cfg.splits) only where the
+    # unsplit tiles leave CUs idle; one workspace serves them all.
+    fn_split = gemm.gemm_f32_splitk if kind == "f32" else gemm.gemm_f16_splitk
+    max_ws = max([gemm.gemm_splitk_workspace_bytes(dtype, M, N, K, s) for s in splits] + [16])
+    ws = torch.empty(max_ws, dtype=torch.uint8, device=dev) if max(splits) > 1 else None
+
     results = []
     for cfg in candidates(gemm, dtype, orders):
-        ms = time_config(gemm, torch, fn, args, cfg, stream, warmup, reps_here)
-        if ms is not None:
-            results.append((ms, cfg.name.decode(), cfg.order, cfg.group_m))
+        tiles = -(-M // cfg.bm) * -(-N // cfg.bn)
+        for sp in splits:
+            if sp == 1:
+                ms = time_config(gemm, torch, fn, args, cfg, stream, warmup, reps_here)
+            elif tiles < 256 and gemm.gemm_splitk_workspace_bytes(dtype, M, N, K, sp) > 0:
+                cfg.splits = sp
+                ms = time_config(gemm, torch, fn_split, args, cfg, stream, warmup, reps_here, ws)
+            else:
+                continue
+            if ms is not None:
+                results.append((ms, cfg.name.decode(), cfg.order, cfg.group_m, sp))
     results.sort()
     gemm.gemm_load_tuning(None)
     h = gemm.gemm_select_config(dtype, M, N, K)
     h_ms = time_config(gemm, torch, fn, args, h, stream, warmup, reps_here)
+    hs = gemm.gemm_select_splitk_config(dtype, M, N, K)
+    hs_ms = time_config(gemm, torch, fn_split, args, hs, stream, warmup, reps_here, ws) \
+        if ws is not None and hs.splits > 1 else None
 
-    def entry(ms, name, order, gm):
-        return {"variant": name, "order": order, "group_m": gm, "ms": round(ms, 5),
+    def entry(ms, name, order, gm, sp=1):
+        return {"variant": name, "order": order, "group_m": gm, "splits": sp, "ms": round(ms, 5),
                 "tflops": round(flops / (ms * 1e-3) / 1e12, 2)}
 
     rep = {"dtype": kind, "M": M, "N": N, "K": K, "candidates": len(results),
-           "all": [[name, order, gm, round(flops / (ms * 1e-3) / 1e12, 1)]
-                   for ms, name, order, gm in results],
+           "all": [[name, order, gm, sp, round(flops / (ms * 1e-3) / 1e12, 1)]
+                   for ms, name, order, gm, sp in results],
            "best": entry(*results[0]) if results else None,
            "second": entry(*results[1]) if len(results) > 1 else None,
-           "heuristic": entry(h_ms, h.name.decode(), h.order, h.group_m) if h_ms else None}
-    del a, b, c
+           "heuristic": entry(h_ms, h.name.decode(), h.order, h.group_m) if h_ms else None,
+           "heuristic_splitk": entry(hs_ms, hs.name.decode(), hs.order, hs.group_m, hs.splits)
+           if hs_ms else None}
+    del a, b, c, ws
     return rep
 
 
@@ -121,6 +147,8 @@ def main(argv=None) -> int:
     ap.add_argument("--orders", nargs="+", type=parse_order,
                     default=[parse_order("xcd:4"), parse_order("xcd:8"), parse_order("grouped:8")],
                     help="tile orders to try: row | grouped:G | xcd:G")
+    ap.add_argument("--splits", nargs="+", type=int, default=[1],
+                    help="split-K counts to try where the output tiles leave CUs idle")
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--reps", type=int, default=20, help="timed launches at 4096^3 (scaled by size)")
     ap.add_argument("--out", default=None, help="write the tuning table here")
@@ -139,14 +167,15 @@ def main(argv=None) -> int:
              f"# written by dense_gemm_row_amd.tune on {torch.cuda.get_device_name(0)}"]
     for kind in args.dtypes:
         for M, N, K in args.shapes:
-            rep = tune_shape(gemm, torch, kind, M, N, K, args.orders, args.warmup, args.reps)
+            rep = tune_shape(gemm, torch, kind, M, N, K, args.orders, args.warmup, args.reps,
+                             tuple(sorted(set([1] + args.splits))))
             print(json.dumps(rep), flush=True)
             b = rep["best"]
             if b:
                 lines.append(f"# {b['ms']} ms, {b['tflops']} TFLOP/s (heuristic "
                              f"{rep['heuristic']['variant'] if rep['heuristic'] else '-'}: "
                              f"{rep['heuristic']['tflops'] if rep['heuristic'] else '-'} TFLOP/s)")
-                lines.append(f"{kind} {M} {N} {K} {b['variant']} {b['order']} {b['group_m']}")
+                lines.append(f"{kind} {M} {N} {K} {b['variant']} {b['order']} {b['group_m']} {b['splits']}")
     gemm.gemm_load_tuning(None)
     if args.out:
         with open(args.out, "w") as f:

@@ -97,6 +97,8 @@ typedef struct gemm_config {
     int32_t lds_bytes;  /* LDS per workgroup                                 */
     int32_t order;      /* gemm_order_t                                      */
     int32_t group_m;    /* band height in tile rows for GROUPED/XCD orders   */
+    int32_t splits;     /* K chunks for gemm_*_splitk (1 = no split); the
+                           plain and _ex entry points ignore it             */
     char name[48];      /* e.g. "mfma_f32_128x128x32_w64x64"                 */
 } gemm_config_t;
 
@@ -131,14 +133,65 @@ gemm_status_t gemm_f16_ex(int64_t M, int64_t N, int64_t K,
                           gemm_f16_t *C, int64_t ldc, void *stream,
                           const gemm_config_t *cfg);
 
+/*
+ * Split-K GEMM: the same results contract as gemm_f32 / gemm_f16, for shapes
+ * with too few output tiles to fill the GPU (e.g. M = N = 1024, K = 8192).
+ * The K range is cut into S chunks of Kc = roundup(ceil(K / splits), 64)
+ * (S = ceil(K / Kc) <= splits); one launch computes every chunk's FP32
+ * partial product into `workspace` (S x M x N floats, row-major), and a
+ * second launch sums the S partials of each element in chunk order and
+ * writes C (FP32, or FP16 rounded to nearest even once, after the sum).
+ * The order of the sum is fixed, so results are bit-reproducible for a
+ * given configuration.  Splitting the K sum of the pages' C = A x B
+ * changes only the order of its additions ("nxbn.cn GB300 GEMM",
+ * section 6.2, on split-K and summation order).
+ *
+ * cfg      NULL: variant and split count from gemm_select_config.  Else
+ *          cfg->id / order / group_m pick the variant for the partial
+ *          products and cfg->splits the requested S (0 = choose).
+ * workspace  Caller-owned device memory of at least
+ *          gemm_splitk_workspace_bytes(dtype, M, N, K, splits) bytes,
+ *          16-byte aligned, not overlapping A, B or C (-> ALIAS).  Too small
+ *          or NULL (when a split happens) -> INVALID_ARG.  The library does
+ *          not allocate.  Its contents on return are unspecified.
+ * Falls back to the unsplit path (no workspace use) when S comes out as 1,
+ * when the operands do not take the vector path (alignment as above), or
+ * when the chosen variant has no split-K form.  Concurrent calls must not
+ * share a workspace.
+ */
+gemm_status_t gemm_f32_splitk(int64_t M, int64_t N, int64_t K,
+                              const float *A, int64_t lda,
+                              const float *B, int64_t ldb,
+                              float *C, int64_t ldc,
+                              void *workspace, int64_t workspace_bytes,
+                              void *stream, const gemm_config_t *cfg);
+gemm_status_t gemm_f16_splitk(int64_t M, int64_t N, int64_t K,
+                              const gemm_f16_t *A, int64_t lda,
+                              const gemm_f16_t *B, int64_t ldb,
+                              gemm_f16_t *C, int64_t ldc,
+                              void *workspace, int64_t workspace_bytes,
+                              void *stream, const gemm_config_t *cfg);
+
+/* Workspace bytes a split-K call with `splits` requested chunks needs
+ * (0 when it would not split; splits <= 0 means the library's choice for
+ * the shape).  Negative sizes give -1. */
+int64_t gemm_splitk_workspace_bytes(int32_t dtype, int64_t M, int64_t N, int64_t K,
+                                    int32_t splits);
+
 /* Variant table: count per dtype, and the description of variant idx. */
 int32_t gemm_num_configs(int32_t dtype);
 gemm_status_t gemm_get_config(int32_t dtype, int32_t idx, gemm_config_t *out);
 
 /* The configuration gemm_f32 / gemm_f16 would use for this shape (host
- * only; no GPU work). */
+ * only; no GPU work; splits = 1). */
 gemm_status_t gemm_select_config(int32_t dtype, int64_t M, int64_t N, int64_t K,
                                  gemm_config_t *out);
+
+/* The configuration gemm_f32_splitk / gemm_f16_splitk would use with
+ * cfg = NULL: variant, tile order and split count (1 when splitting does not
+ * pay for this shape).  Host only. */
+gemm_status_t gemm_select_splitk_config(int32_t dtype, int64_t M, int64_t N, int64_t K,
+                                        gemm_config_t *out);
 
 /* Workgroup-to-tile map of a configuration (host only): the tile
  * (tile_m, tile_n) that workgroup `block` computes for an M x N output.
@@ -154,10 +207,10 @@ gemm_status_t gemm_tile_of_block(const gemm_config_t *cfg, int64_t M, int64_t N,
 gemm_status_t gemm_layout_check(int32_t dtype, int32_t idx, int32_t banks,
                                 int64_t out[2]);
 
-/* Tuning table: a text file of lines "dtype M N K name order group_m"
- * (dtype f32|f16).  Exact-shape matches override the heuristic.  Loading
- * replaces the previous table; NULL clears it.  Not safe to call
- * concurrently with GEMM calls. */
+/* Tuning table: a text file of lines "dtype M N K name order group_m
+ * [splits]" (dtype f32|f16; splits defaults to 1).  Exact-shape matches
+ * override the heuristic.  Loading replaces the previous table; NULL clears
+ * it.  Not safe to call concurrently with GEMM calls. */
 gemm_status_t gemm_load_tuning(const char *path);
 
 const char *gemm_status_string(gemm_status_t status);

@@ -73,27 +73,51 @@ class DevMatrix:
         return bool(ok)
 
 
+WS_GUARD = 256  # canary floats on each side of a split-K workspace
+
+
 def run(A: np.ndarray, B: np.ndarray, cfg=None, pad=(0, 0, 0), offset=(0, 0, 0),
-        repeat: int = 1):
-    """Compute A @ B through libgemm.  Returns (C as numpy, C DevMatrix)."""
+        repeat: int = 1, split=None):
+    """Compute A @ B through libgemm.  Returns (C as numpy, C DevMatrix).
+
+    split: None for the plain entry points; "auto" for gemm_*_splitk with
+    cfg = NULL; or a GemmConfig (its `splits` set) for a forced split-K
+    call.  The workspace is sized by gemm_splitk_workspace_bytes and has
+    canary guards that must survive the call."""
     kind = "f32" if A.dtype == np.float32 else "f16"
+    dtype = gemm.DTYPE_F32 if kind == "f32" else gemm.DTYPE_F16
     M, K = A.shape
     N = B.shape[1]
     dA = DevMatrix(A, M, K, kind, pad=pad[0], offset=offset[0])
     dB = DevMatrix(B, K, N, kind, pad=pad[1], offset=offset[1])
     dC = DevMatrix(None, M, N, kind, pad=pad[2], offset=offset[2])
     stream = torch.cuda.current_stream().cuda_stream
+    ws = None
+    if split is not None:
+        scfg = None if split == "auto" else split
+        nbytes = gemm.gemm_splitk_workspace_bytes(dtype, M, N, K, 0 if scfg is None else scfg.splits)
+        nfl = (max(nbytes, 0) + 3) // 4
+        host = np.full(2 * WS_GUARD + nfl, CANARY_F32, dtype=np.uint32)
+        ws = torch.from_numpy(host.view(np.int32)).to("cuda")
     for _ in range(repeat):
-        args = (M, N, K, dA.ptr, dA.ld, dB.ptr, dB.ld, dC.ptr, dC.ld, stream)
-        if kind == "f32":
-            st = gemm.gemm_f32(*args) if cfg is None else gemm.gemm_f32_ex(*args, cfg)
+        args = (M, N, K, dA.ptr, dA.ld, dB.ptr, dB.ld, dC.ptr, dC.ld)
+        if split is not None:
+            fn = gemm.gemm_f32_splitk if kind == "f32" else gemm.gemm_f16_splitk
+            st = fn(*args, ws.data_ptr() + 4 * WS_GUARD, 4 * (ws.numel() - 2 * WS_GUARD), stream,
+                    None if split == "auto" else split)
+        elif kind == "f32":
+            st = gemm.gemm_f32(*args, stream) if cfg is None else gemm.gemm_f32_ex(*args, stream, cfg)
         else:
-            st = gemm.gemm_f16(*args) if cfg is None else gemm.gemm_f16_ex(*args, cfg)
+            st = gemm.gemm_f16(*args, stream) if cfg is None else gemm.gemm_f16_ex(*args, stream, cfg)
         if st != gemm.GEMM_OK:
             raise gemm.GemmError(st, "gemm call")
     torch.cuda.synchronize()
     flat = dC.fetch()
     assert dC.untouched_outside(flat), "kernel wrote outside C[0:M, 0:N]"
+    if ws is not None:
+        w = ws.cpu().numpy().view(np.uint32)
+        assert np.all(w[:WS_GUARD] == CANARY_F32) and np.all(w[len(w) - WS_GUARD:] == CANARY_F32), \
+            "split-K wrote outside its workspace"
     return dC.matrix(flat), dC
 
 

@@ -189,3 +189,61 @@ def test_every_pipelined_variant_has_a_general_fallback(dt):
     for c in cfgs:
         if c.name.decode().startswith(("pipe_", "tr_", "dl_")):
             assert (c.bm, c.bn) in general, c.name
+
+
+def test_splitk_workspace_and_selection():
+    f32, f16 = gemm.DTYPE_F32, gemm.DTYPE_F16
+    assert gemm.gemm_splitk_workspace_bytes(f32, 1024, 1024, 8192, 4) == 4 * 1024 * 1024 * 4
+    # Kc = roundup(ceil(1000 / 3), 64) = 384 -> 3 chunks.
+    assert gemm.gemm_splitk_workspace_bytes(f16, 10, 20, 1000, 3) == 3 * 10 * 20 * 4
+    assert gemm.gemm_splitk_workspace_bytes(f32, 10, 20, 1000, 64) == 16 * 10 * 20 * 4
+    assert gemm.gemm_splitk_workspace_bytes(f32, 10, 20, 64, 4) == 0      # one chunk
+    assert gemm.gemm_splitk_workspace_bytes(f32, 10, 20, 1000, 1) == 0
+    assert gemm.gemm_splitk_workspace_bytes(f32, -1, 20, 1000, 2) == -1
+    assert gemm.gemm_splitk_workspace_bytes(7, 1, 1, 1, 2) == -1
+    for dt in (f32, f16):
+        assert gemm.gemm_select_splitk_config(dt, 1024, 1024, 8192).splits > 1
+        assert gemm.gemm_select_splitk_config(dt, 4096, 4096, 4096).splits == 1
+        assert gemm.gemm_select_config(dt, 1024, 1024, 8192).splits == 1
+        auto = gemm.gemm_splitk_workspace_bytes(dt, 1024, 1024, 8192, 0)
+        assert auto == gemm.gemm_select_splitk_config(dt, 1024, 1024, 8192).splits * 1024 * 1024 * 4
+
+
+@pytest.mark.parametrize("fn", [gemm.gemm_f32_splitk, gemm.gemm_f16_splitk])
+def test_splitk_argument_validation(fn):
+    # A shape that splits (aligned fake pointers): workspace problems are
+    # caught on the host before any launch.
+    M, N, K = 1024, 1024, 8192
+    cfg = gemm.gemm_select_splitk_config(gemm.DTYPE_F32 if fn is gemm.gemm_f32_splitk else gemm.DTYPE_F16,
+                                         M, N, K)
+    A, B, C = 0x100000000, 0x200000000, 0x300000000
+    W = 0x400000000
+    need = gemm.gemm_splitk_workspace_bytes(cfg.dtype, M, N, K, cfg.splits)
+    base = (M, N, K, A, K, B, N, C, N)
+    assert fn(*base, 0, need, None, cfg) == gemm.GEMM_ERR_INVALID_ARG          # NULL
+    assert fn(*base, W, need - 4, None, cfg) == gemm.GEMM_ERR_INVALID_ARG      # too small
+    assert fn(*base, W + 4, need, None, cfg) == gemm.GEMM_ERR_INVALID_ARG      # misaligned
+    assert fn(*base, W, -1, None, cfg) == gemm.GEMM_ERR_INVALID_ARG            # negative size
+    assert fn(*base, C + 64, need, None, cfg) == gemm.GEMM_ERR_ALIAS           # overlaps C
+    assert fn(*base, A, need, None, cfg) == gemm.GEMM_ERR_ALIAS                # overlaps A
+    bad = gemm.gemm_get_config(cfg.dtype, cfg.id)
+    bad.splits = -2
+    assert fn(*base, W, need, None, bad) == gemm.GEMM_ERR_UNSUPPORTED
+    # Ordinary argument errors come first, as for the plain calls.
+    assert fn(-1, N, K, A, K, B, N, C, N, W, need, None, cfg) == gemm.GEMM_ERR_INVALID_ARG
+
+
+def test_tuning_table_splits_column(tmp_path):
+    cfg = gemm.config_by_name(gemm.DTYPE_F16, "tr_f16_256x128x64_w128x64_s3")
+    path = tmp_path / "t.txt"
+    path.write_text(f"f16 1024 1024 8192 {cfg.name.decode()} 2 4 8\n")
+    assert gemm.gemm_load_tuning(str(path)) == gemm.GEMM_OK
+    try:
+        s = gemm.gemm_select_splitk_config(gemm.DTYPE_F16, 1024, 1024, 8192)
+        assert s.id == cfg.id and s.splits == 8 and s.group_m == 4
+        # Plain calls never split; a split entry does not bind them.
+        assert gemm.gemm_select_config(gemm.DTYPE_F16, 1024, 1024, 8192).splits == 1
+    finally:
+        gemm.gemm_load_tuning(None)
+    path.write_text(f"f16 1 2 3 {cfg.name.decode()} 2 4 0\n")
+    assert gemm.gemm_load_tuning(str(path)) == gemm.GEMM_ERR_INVALID_ARG

@@ -202,3 +202,85 @@ def test_random_sampled_full_size(kind, shape):
                        oracle.SGEMM_TOL if kind == "f32" else oracle.HGEMM_TOL)
     log(f"  entries: max_rel={rep['max_rel']:.3e}")
     assert rep["ok"], rep
+
+
+# --------------------------------------------------------------------------
+# Split-K (gemm_*_splitk): partial products into a guarded workspace, then
+# the fixed-order reduction.
+# --------------------------------------------------------------------------
+def _split_cfgs(kind):
+    """Every variant with a split-K form (the LDS-direct families)."""
+    pre = "dl_" if kind == "f32" else "tr_"
+    dt = gemm.DTYPE_F32 if kind == "f32" else gemm.DTYPE_F16
+    return [c for c in gemm.configs(dt) if c.name.decode().startswith(pre)]
+
+
+SPLIT_SHAPES = [(200, 136, 1000), (64, 64, 512), (130, 257, 4096), (1, 8, 200)]
+
+
+@pytest.mark.parametrize("kind", ["f32", "f16"])
+@pytest.mark.parametrize("shape", SPLIT_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_splitk_exact_small_int(kind, shape):
+    """Exact inputs: every split count gives the oracle's bits (K chunks of
+    a multiple of 64 with a ragged last chunk, and counts the shape clamps)."""
+    M, N, K = shape
+    A, B = _ints(M, N, K, kind, seed=11)
+    for cfg in _split_cfgs(kind):
+        for splits in (2, 3, 7, 64):
+            cfg.splits = splits
+            log(f"{kind} split-K exact cfg={cfg.name.decode()} splits={splits} shape={shape}")
+            C, _ = run(A, B, split=cfg)
+            assert exact_equal(A, B, C), (cfg.name, splits)
+
+
+@pytest.mark.parametrize("kind", ["f32", "f16"])
+def test_splitk_random_and_deterministic(kind):
+    M, N, K = 300, 520, 3000
+    A, B = synth.workload(M, N, K, kind, seed=5)
+    for cfg in _split_cfgs(kind):
+        cfg.splits = 4
+        log(f"{kind} split-K random cfg={cfg.name.decode()} {M}x{N}x{K}")
+        C1, _ = run(A, B, split=cfg)
+        rep = check_full(A, B, C1)
+        log(f"  max_rel={rep['max_rel']:.3e}")
+        assert rep["ok"], rep
+        C2, _ = run(A, B, split=cfg, repeat=2)
+        assert np.array_equal(C1.view(np.uint8), C2.view(np.uint8))
+
+
+@pytest.mark.parametrize("kind", ["f32", "f16"])
+def test_splitk_unaligned_falls_back(kind):
+    """Padded (unaligned) leading dimensions take the unsplit general path."""
+    A, B = _ints(70, 90, 700, kind, seed=3)
+    cfg = _split_cfgs(kind)[0]
+    cfg.splits = 4
+    log(f"{kind} split-K unaligned fallback")
+    C, _ = run(A, B, split=cfg, pad=(3, 5, 7))
+    assert exact_equal(A, B, C)
+
+
+@pytest.mark.parametrize("kind", ["f32", "f16"])
+def test_splitk_full_size_auto(kind):
+    """The shape split-K exists for, with the library's own choice."""
+    M, N, K = 1024, 1024, 8192
+    sel = gemm.gemm_select_splitk_config(gemm.DTYPE_F32 if kind == "f32" else gemm.DTYPE_F16, M, N, K)
+    assert sel.splits > 1
+    A, B = synth.workload(M, N, K, kind)
+    log(f"{kind} split-K auto {M}x{N}x{K}: {sel.name.decode()} splits={sel.splits}")
+    C, _ = run(A, B, split="auto")
+    rng = np.random.default_rng(2)
+    rows = sorted(set([0, M - 1] + rng.integers(0, M, 24).tolist()))
+    rep = check_rows(A, B, C, rows)
+    log(f"  rows: max_rel={rep['max_rel']:.3e}")
+    assert rep["ok"], rep
+
+
+def test_matmul_uses_split_k():
+    import torch
+    A, B = synth.workload(1024, 1024, 8192, "f16", seed=9)
+    log("matmul f16 1024x1024x8192 (split-K)")
+    c = gemm.matmul(torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda())
+    torch.cuda.synchronize()
+    C = c.cpu().numpy()
+    rep = check_rows(A, B, C, [0, 511, 1023])
+    assert rep["ok"], rep
