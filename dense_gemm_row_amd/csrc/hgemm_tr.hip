@@ -77,9 +77,11 @@ __device__ __forceinline__ void static_for(F&& f, std::integer_sequence<int, I..
   (f(IC<I>{}), ...);
 }
 
-template <int BM_, int BN_, int WM_, int WN_, int BK_, int NS_>
+// PARTIAL_: the split-K form, whose epilogue writes FP32 partials.
+template <int BM_, int BN_, int WM_, int WN_, int BK_, int NS_, bool PARTIAL_ = false>
 struct Shape {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BK_, NS = NS_;
+  static constexpr bool PARTIAL = PARTIAL_;
   static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN, NW = WAVES_M * WAVES_N;
   static constexpr int NT = NW * 64;
   static constexpr int MB = WM / 32, NB = WN / 32, KS = BK / 16;
@@ -417,7 +419,7 @@ hgemm_tr_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
     // must land before the epilogue reuses the LDS.
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   }
-  if (p.splits > 1) {
+  if constexpr (S::PARTIAL) {
     // Split-K partial: FP32 C (the workspace) written straight from the
     // accumulators, no FP16 rounding, no LDS round trip.
     // acc[nb][mb] register 4rq+e of lane l is C[m][n], m = wm0 + 32mb +
@@ -487,7 +489,7 @@ hgemm_tr_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
   }
 }
 
-// With p.splits > 1 this is the split-K partial launch (FP32 partials).
+// With S::PARTIAL this is the split-K partial launch (FP32 partials).
 template <class S>
 hipError_t launch(const Params& p, const TileMap& map, bool vec, hipStream_t stream) {
   const int64_t lim = 0x7fffffff;
@@ -630,7 +632,7 @@ int layout_check(int banks, int64_t out[2]) {
                   GEMM_ORDER_XCD, 4, 1,                                                      \
                   "tr_f16_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_s" #NS},                  \
         &launch<Shape<BM, BN, WM, WN, BK, NS>>, &layout_check<Shape<BM, BN, WM, WN, BK, NS>>, \
-        &launch<Shape<BM, BN, WM, WN, BK, NS>>, EFF                                         \
+        &launch<Shape<BM, BN, WM, WN, BK, NS, true>>, EFF                                   \
   }
 
 const Variant kVariants[] = {
