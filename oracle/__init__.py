@@ -65,6 +65,11 @@ def _declare(lib):
         fn = getattr(lib, name)
         fn.argtypes = [i64, p, i64, p, i64, p, p, i64, p, p]
         fn.restype = ctypes.c_int
+    for name in ("oracle_epilogue_rows_f32", "oracle_epilogue_rows_f16"):
+        fn = getattr(lib, name)
+        fn.argtypes = [i64, i64, ctypes.c_double, ctypes.c_double, p, i64, p, ctypes.c_int, p,
+                       p, i64, p, i64]
+        fn.restype = ctypes.c_int
     for name in ("oracle_check_f32", "oracle_check_f16"):
         fn = getattr(lib, name)
         fn.argtypes = [i64, i64, p, i64, p, i64, p, i64, ctypes.c_double, p, p]
@@ -161,6 +166,45 @@ def gemm_rows(A: np.ndarray, B: np.ndarray, rows=None, threads: int | None = Non
             int(threads or default_threads()))
     if rc != 0:
         raise RuntimeError(f"oracle_gemm_rows failed with code {rc}")
+    return C, D
+
+
+ACT_NONE, ACT_RELU = 0, 1
+
+
+def gemm_rows_epi(A: np.ndarray, B: np.ndarray, C0, alpha: float, beta: float, bias=None,
+                  act: int = ACT_NONE, rows=None, threads: int | None = None, lib=None):
+    """C_ref and D of the fused-epilogue product
+    act(alpha * (A @ B) + beta * C0 + bias[j]) for the rows ``rows`` (all
+    when None).  C0 (M x N, the type of A) is read only when beta != 0; bias
+    is None or N float32 values; act is ACT_NONE or ACT_RELU."""
+    lib = lib or load()
+    C, D = gemm_rows(A, B, rows=rows, threads=threads, lib=lib)
+    kind = _kind(A)
+    M, N = A.shape[0], B.shape[1]
+    dt = np.float32 if kind == "f32" else np.uint16
+    c0_ptr, ldc0, keep = None, max(N, 1), []
+    if beta != 0.0:
+        C0m = _bits16(C0) if kind == "f16" else C0
+        C0m, ldc0 = _as_matrix(C0m, dt)
+        if C0m.shape != (M, N):
+            raise ValueError("C0 must be M x N")
+        keep.append(C0m)
+        c0_ptr = _ptr(C0m)
+    b_ptr = None
+    if bias is not None:
+        bias = np.ascontiguousarray(np.asarray(bias, dtype=np.float32))
+        if bias.shape != (N,):
+            raise ValueError("bias must hold N values")
+        b_ptr = _ptr(bias)
+    rows_arr = None if rows is None else np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    rp = None if rows_arr is None else _ptr(rows_arr)
+    if C.size:
+        fn = lib.oracle_epilogue_rows_f32 if kind == "f32" else lib.oracle_epilogue_rows_f16
+        rc = fn(C.shape[0], N, float(alpha), float(beta), c0_ptr, ldc0, b_ptr, int(act), rp,
+                _ptr(C), N, _ptr(D), N)
+        if rc != 0:
+            raise RuntimeError(f"oracle_epilogue_rows failed with code {rc}")
     return C, D
 
 

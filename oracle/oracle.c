@@ -200,6 +200,67 @@ int oracle_gemm_rows_f16(int64_t nrows, int64_t N, int64_t K,
 }
 
 /*
+ * Fused epilogue, applied to rows of C_ref and D produced by
+ * oracle_gemm_rows_* (in place):
+ *   C[t][j] <- act(alpha * C[t][j] + beta * C0[i][j] + bias[j])
+ *   D[t][j] <- |alpha| * D[t][j] + |beta * C0[i][j]| + |bias[j]|
+ * with i = rows[t] (t when rows is NULL).  D stays a bound on the rounding
+ * error scale: the activation (act 1: max(x, 0)) is 1-Lipschitz.
+ * Sources: the alpha and beta parameters of the tiled kernel in the lqnn.cn
+ * SGEMM article (section 3.3), read with their usual BLAS meaning, since the
+ * page leaves beta unapplied; bias and activation fused into the GEMM's
+ * epilogue as the GB300 GEMM article proposes (section 7.1).
+ * beta == 0: C0 is not read (it may be NULL or hold NaN).  bias == NULL: no
+ * bias term.  Returns 0, or -1 on bad arguments.
+ */
+static int run_epilogue(int dtype, int64_t nrows, int64_t N, double alpha, double beta,
+                        const void *C0, int64_t ldc0, const float *bias, int act,
+                        const int64_t *rows, double *C, int64_t ldr, double *D, int64_t ldd)
+{
+    if (nrows < 0 || N < 0 || ldr < N || ldd < N || (act != 0 && act != 1))
+        return -1;
+    if (beta != 0.0 && (!C0 || ldc0 < N))
+        return -1;
+    for (int64_t t = 0; t < nrows; ++t) {
+        const int64_t i = rows ? rows[t] : t;
+        for (int64_t j = 0; j < N; ++j) {
+            double v = alpha * C[t * ldr + j];
+            double d = fabs(alpha) * D[t * ldd + j];
+            if (beta != 0.0) {
+                const double c0 = beta * load_elem(C0, dtype, i * ldc0 + j);
+                v += c0;
+                d += fabs(c0);
+            }
+            if (bias) {
+                v += (double)bias[j];
+                d += fabs((double)bias[j]);
+            }
+            if (act == 1 && v < 0.0)
+                v = 0.0;
+            C[t * ldr + j] = v;
+            D[t * ldd + j] = d;
+        }
+    }
+    return 0;
+}
+
+int oracle_epilogue_rows_f32(int64_t nrows, int64_t N, double alpha, double beta,
+                             const float *C0, int64_t ldc0, const float *bias, int act,
+                             const int64_t *rows, double *C, int64_t ldr, double *D, int64_t ldd)
+{
+    return run_epilogue(ORACLE_F32, nrows, N, alpha, beta, C0, ldc0, bias, act, rows, C, ldr,
+                        D, ldd);
+}
+
+int oracle_epilogue_rows_f16(int64_t nrows, int64_t N, double alpha, double beta,
+                             const uint16_t *C0, int64_t ldc0, const float *bias, int act,
+                             const int64_t *rows, double *C, int64_t ldr, double *D, int64_t ldd)
+{
+    return run_epilogue(ORACLE_F16, nrows, N, alpha, beta, C0, ldc0, bias, act, rows, C, ldr,
+                        D, ldd);
+}
+
+/*
  * Single entries C_ref[ii[t]][jj[t]] and D[ii[t]][jj[t]], each one a plain
  * dot product over k ascending (the same order as the row routine).
  */

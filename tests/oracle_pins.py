@@ -240,9 +240,74 @@ def pin_error_metric(lib):
     assert rep["max_rel"] == 0.25, "f16 decoded before comparing"
 
 
+# --------------------------------------------------------------------------
+# Fused epilogue: act(alpha * (A @ B) + beta * C0 + bias[j]) and its error
+# scale |alpha| D + |beta C0| + |bias|.
+# --------------------------------------------------------------------------
+def pin_epilogue_closed_form(lib):
+    """All-ones A, B give A @ B = K exactly, so the epilogue's value is a
+    closed form: alpha K + beta C0[i][j] + bias[j] (then max(., 0) for
+    relu).  Non-square shapes and a row subset catch a bias indexed by row
+    or a C0 indexed by the output slot instead of the row."""
+    for dt in _dtypes():
+        M, N, K = 5, 7, 6
+        A, B = np.ones((M, K), dtype=dt), np.ones((K, N), dtype=dt)
+        C0 = synth.small_int(31, 2, M, N, -3, 3, dtype=dt)
+        bias = (np.arange(N) - 3).astype(np.float32)
+        rows = [4, 1]
+        c0 = C0.astype(np.float64)[rows]
+        for alpha, beta, act in ((2.0, -1.5, 0), (-1.0, 0.5, 1), (0.5, 0.0, 0)):
+            C, D = oracle.gemm_rows_epi(A, B, C0, alpha, beta, bias, act, rows=rows, lib=lib)
+            v = alpha * K + beta * c0 + bias[None, :].astype(np.float64)
+            if act == 1:
+                v = np.maximum(v, 0.0)
+            d = abs(alpha) * K + np.abs(beta * c0) + np.abs(bias[None, :].astype(np.float64))
+            assert np.array_equal(C, v), f"epilogue value alpha={alpha} beta={beta} act={act}"
+            assert np.array_equal(D, d), f"epilogue scale alpha={alpha} beta={beta}"
+
+
+def pin_epilogue_reduces_to_plain(lib):
+    """alpha = 1, beta = 0, no bias, no activation is the plain product
+    (C0 full of NaN must not leak in: beta = 0 means C is not read)."""
+    for dt in _dtypes():
+        A, B = _rand(dt, 41, 0, 9, 13), _rand(dt, 41, 1, 13, 6)
+        C0 = np.full((9, 6), np.nan, dtype=dt)
+        C, D = oracle.gemm_rows_epi(A, B, C0, 1.0, 0.0, None, 0, lib=lib)
+        Cp, Dp = oracle.gemm_rows(A, B, lib=lib)
+        assert np.array_equal(C, Cp) and np.array_equal(D, Dp), "plain special case"
+        C, _ = oracle.gemm_rows_epi(A, B, C0, 2.0, 0.0, np.ones(6, np.float32), 0, lib=lib)
+        assert np.all(np.isfinite(C)), "beta = 0 read C0"
+
+
+def pin_epilogue_bruteforce(lib, trials: int = 30):
+    """Tiny random cases against exact rational arithmetic of the epilogue
+    formula (value within one double rounding per operation of the exact
+    one, relative to the scale)."""
+    rng = random.Random(7)
+    for t in range(trials):
+        for dt in _dtypes():
+            M, N, K = rng.randint(1, 4), rng.randint(1, 4), rng.randint(1, 5)
+            A, B = _rand(dt, 100 + t, 0, M, K), _rand(dt, 100 + t, 1, K, N)
+            C0 = _rand(dt, 100 + t, 2, M, N)
+            bias = _rand(np.float32, 100 + t, 3, 1, N).ravel()
+            alpha, beta = rng.choice([1.0, -0.75, 3.0]), rng.choice([0.0, 0.5, -2.0])
+            act = rng.choice([0, 1])
+            C, D = oracle.gemm_rows_epi(A, B, C0, alpha, beta, bias, act, lib=lib)
+            for i in range(M):
+                for j in range(N):
+                    s = sum(_exact_fraction(A[i, k]) * _exact_fraction(B[k, j]) for k in range(K))
+                    v = Fraction(alpha) * s + Fraction(beta) * _exact_fraction(C0[i, j]) + \
+                        _exact_fraction(bias[j])
+                    if act == 1 and v < 0:
+                        v = Fraction(0)
+                    assert abs(Fraction(C[i, j]) - v) <= Fraction(8 * (K + 3)) * \
+                        Fraction(U64) * Fraction(D[i, j]), "epilogue brute force"
+
+
 PINS = [pin_identity, pin_permutation, pin_all_ones, pin_rank1, pin_k0_k1,
         pin_bruteforce_fractions, pin_numpy_matmul, pin_f16_decode,
-        pin_error_metric]
+        pin_error_metric, pin_epilogue_closed_form, pin_epilogue_reduces_to_plain,
+        pin_epilogue_bruteforce]
 
 
 def run_all(lib) -> list[str]:

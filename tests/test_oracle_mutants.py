@@ -44,6 +44,13 @@ MUTANTS = {
     "metric_zero_den_hidden": ("r = (diff == 0.0) ? 0.0 : INFINITY;", "r = 0.0;"),
     "metric_nan_ignored": ("++n_nonfinite;\n                r = INFINITY;",
                            "r = 0.0;"),
+    "epi_drop_beta": ("                v += c0;\n", "\n"),
+    "epi_bias_by_row": ("v += (double)bias[j];", "v += (double)bias[i % N];"),
+    "epi_c0_by_slot": ("load_elem(C0, dtype, i * ldc0 + j)", "load_elem(C0, dtype, t * ldc0 + j)"),
+    "epi_relu_wrong_way": ("if (act == 1 && v < 0.0)", "if (act == 1 && v > 0.0)"),
+    "epi_scale_no_alpha": ("double d = fabs(alpha) * D[t * ldd + j];", "double d = D[t * ldd + j];"),
+    "epi_reads_c0_when_beta_zero": ("if (beta != 0.0) {\n                const double c0",
+                                    "if (1) {\n                const double c0"),
 }
 
 
