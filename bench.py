@@ -45,6 +45,9 @@ def parse_args():
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
     ap.add_argument("--cpu-threads", type=int, default=16)
     ap.add_argument("--no-check", action="store_true", help="skip the oracle check")
+    ap.add_argument("--epilogue", action="store_true",
+                    help="time the fused-epilogue entry points instead: C = relu(A x B + C + bias) "
+                         "(alpha 1, beta 1: the old C is read)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="before the steps, run a plain device copy of this many MiB (read N, "
                          "write N) three times: the reference kernel that scales HBM counters")
@@ -141,10 +144,24 @@ def main():
     stream = torch.cuda.current_stream(dev)
     sptr = stream.cuda_stream
 
+    # Fused-epilogue mode: bias = uniform[-1, 1) (stream 3), C starts as the
+    # RNE of uniform[-1, 1) (stream 2) and is read back by every launch.
+    epi, bias_dev, C0 = None, None, {}
+    if args.epilogue:
+        bias_host = synth.uniform_f32(0, 3, 1, n).ravel()
+        bias_dev = torch.from_numpy(bias_host).to(dev)
+        epi = gemm.GemmEpilogue(1.0, 1.0, bias_dev.data_ptr(), gemm.ACT_RELU)
+        for k in kinds:
+            C0[k] = synth.uniform_f32(0, 2, n, n).astype(np.float32 if k == "f32" else np.float16)
+
     def launch(k):
         a, b, c = devbuf[k]
-        fn = gemm.gemm_f32_ex if k == "f32" else gemm.gemm_f16_ex
-        st = fn(n, n, n, a.data_ptr(), n, b.data_ptr(), n, c.data_ptr(), n, sptr, cfgs[k])
+        if epi is not None:
+            fn = gemm.gemm_f32_epi if k == "f32" else gemm.gemm_f16_epi
+            st = fn(n, n, n, a.data_ptr(), n, b.data_ptr(), n, c.data_ptr(), n, sptr, cfgs[k], epi)
+        else:
+            fn = gemm.gemm_f32_ex if k == "f32" else gemm.gemm_f16_ex
+            st = fn(n, n, n, a.data_ptr(), n, b.data_ptr(), n, c.data_ptr(), n, sptr, cfgs[k])
         if st != gemm.GEMM_OK:
             raise gemm.GemmError(st, f"gemm_{k}")
 
@@ -160,9 +177,16 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    for _ in range(max(args.warmup, 1)):
+    if epi is not None:
+        # One launch from the known C0 for the parity check; the warmup
+        # follows it (the epilogue reads C, so later launches change it).
         for k in kinds:
+            devbuf[k][2].copy_(torch.from_numpy(C0[k]).to(dev))
             launch(k)
+    else:
+        for _ in range(max(args.warmup, 1)):
+            for k in kinds:
+                launch(k)
     torch.cuda.synchronize()
 
     parity = {}
@@ -173,6 +197,14 @@ def main():
             A, B = host[k]
             C = devbuf[k][2].cpu().numpy()
             rows = sorted(set([0, n - 1] + rng.integers(0, n, 6).tolist()))
+            if epi is not None:
+                ref, den = oracle.gemm_rows_epi(A, B, C0[k], 1.0, 1.0, bias_host, oracle.ACT_RELU,
+                                                rows=rows, threads=min(args.cpu_threads, 16))
+                rep = oracle.check(np.ascontiguousarray(C[rows]), ref, den,
+                                   oracle.SGEMM_TOL if k == "f32" else oracle.HGEMM_TOL)
+                parity[k] = {"rows": len(rows), "entries": 0, "tol": rep["tol"],
+                             "max_rel": rep["max_rel"], "ok": rep["ok"]}
+                continue
             ref, den = oracle.gemm_rows(A, B, rows=rows, threads=min(args.cpu_threads, 16))
             tol = oracle.SGEMM_TOL if k == "f32" else oracle.HGEMM_TOL
             rep = oracle.check(np.ascontiguousarray(C[rows]), ref, den, tol)
@@ -185,6 +217,11 @@ def main():
         if not all(p["ok"] for p in parity.values()):
             print(json.dumps({"error": "parity check failed", "parity": parity}), flush=True)
             sys.exit(1)
+    if epi is not None:
+        for _ in range(max(args.warmup, 1)):
+            for k in kinds:
+                launch(k)
+        torch.cuda.synchronize()
 
     # Timed region: K steps.  The launches of one kernel run back to back
     # (the K SGEMMs, then the K HGEMMs) between events recorded on the launch
@@ -220,7 +257,8 @@ def main():
     def roofline(k):
         kk = kernels[k]
         achieved = flops / (kk["ms_mean"] * 1e-3) / 1e12
-        traffic = load_traffic(kk["variant"], n)
+        # The counters were taken on the plain kernels.
+        traffic = None if epi is not None else load_traffic(kk["variant"], n)
         return {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS[k],
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS[k], 4),
                 "traffic": traffic, "traffic_unit": "bytes/launch", "kernel": kk["variant"],
@@ -267,7 +305,8 @@ def main():
         "vs_baseline": None,
         "dtype": "+".join(kinds),
         "data": "synthetic",
-        "config": {"workload": f"sgemm+hgemm {n}x{n}x{n} row-major, uniform[-1,1) seed 0",
+        "config": {"workload": f"sgemm+hgemm {n}x{n}x{n} row-major, uniform[-1,1) seed 0"
+                               + (", fused epilogue relu(AB + C + bias)" if epi is not None else ""),
                    "M": n, "N": n, "K": n, "step": " then ".join(
                        "SGEMM fp32" if k == "f32" else "HGEMM fp16-in fp32-acc fp16-out" for k in kinds)},
         "kernels": kernels,

@@ -141,12 +141,13 @@ double gemm_seconds(int dtype, const Variant& v, int64_t M, int64_t N, int64_t K
   return (double)rounds * 2.0 * d.bm * d.bn * (double)(Kc > 0 ? Kc : 1) * w / (eff * rate);
 }
 
-Choice heuristic(int dtype, int64_t M, int64_t N, int64_t K, bool allow_split) {
+Choice heuristic(int dtype, int64_t M, int64_t N, int64_t K, bool allow_split, bool need_epi = false) {
   const auto& v = table().v[dtype];
   const double es = dtype == GEMM_DTYPE_F32 ? 4.0 : 2.0;
   Choice best;
   for (size_t i = 0; i < v.size(); ++i) {
     if (v[i].desc.family != GEMM_FAMILY_MFMA) continue;
+    if (need_epi && !v[i].launch_epi) continue;
     const double t1 = gemm_seconds(dtype, v[i], M, N, K, 1);
     if (t1 < best.t) best = Choice{(int)i, 1, t1};
     if (!allow_split || !v[i].launch_partial || M == 0 || N == 0) continue;
@@ -165,11 +166,13 @@ Choice heuristic(int dtype, int64_t M, int64_t N, int64_t K, bool allow_split) {
 }
 
 // Plain calls (split = false) never split; split-K calls may.
-gemm_config_t select(int dtype, int64_t M, int64_t N, int64_t K, bool split = false) {
+gemm_config_t select(int dtype, int64_t M, int64_t N, int64_t K, bool split = false,
+                     bool need_epi = false) {
   {
     std::lock_guard<std::mutex> lk(g_tuning_mu);
     for (const auto& e : g_tuning)
-      if (e.dtype == dtype && e.M == M && e.N == N && e.K == K && (split || e.splits <= 1)) {
+      if (e.dtype == dtype && e.M == M && e.N == N && e.K == K && (split || e.splits <= 1) &&
+          (!need_epi || table().v[dtype][e.id].launch_epi)) {
         gemm_config_t d = table().v[dtype][e.id].desc;
         d.order = e.order;
         d.group_m = e.group_m;
@@ -177,7 +180,7 @@ gemm_config_t select(int dtype, int64_t M, int64_t N, int64_t K, bool split = fa
         return d;
       }
   }
-  const Choice c = heuristic(dtype, M, N, K, split);
+  const Choice c = heuristic(dtype, M, N, K, split, need_epi);
   gemm_config_t d = table().v[dtype][c.id].desc;
   d.splits = (int32_t)c.splits;
   return d;
@@ -229,10 +232,10 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 // Resolves the configuration of a call: the forced one (checked), or the
 // selection for the shape.
 gemm_status_t resolve(int dtype, int64_t M, int64_t N, int64_t K, const gemm_config_t* forced,
-                      bool split, gemm_config_t& cfg) {
+                      bool split, gemm_config_t& cfg, bool need_epi = false) {
   const auto& v = table().v[dtype];
   if (!forced) {
-    cfg = select(dtype, M, N, K, split);
+    cfg = select(dtype, M, N, K, split, need_epi);
     return GEMM_OK;
   }
   if (forced->id < 0 || forced->id >= (int32_t)v.size())
@@ -242,6 +245,8 @@ gemm_status_t resolve(int dtype, int64_t M, int64_t N, int64_t K, const gemm_con
     return fail(GEMM_ERR_UNSUPPORTED, "bad tile order %d / group_m %d", forced->order,
                 forced->group_m);
   if (split && forced->splits < 0) return fail(GEMM_ERR_UNSUPPORTED, "negative splits");
+  if (need_epi && !v[forced->id].launch_epi)
+    return fail(GEMM_ERR_UNSUPPORTED, "variant %s has no fused-epilogue form", v[forced->id].desc.name);
   cfg = v[forced->id].desc;
   cfg.order = forced->order;
   cfg.group_m = forced->group_m;
@@ -311,6 +316,38 @@ gemm_status_t run(int dtype, int64_t M, int64_t N, int64_t K, const void* A, int
   if (st != GEMM_OK) return st;
   if (M == 0 || N == 0) return GEMM_OK;
   return launch_plain(dtype, cfg, M, N, K, A, lda, B, ldb, C, ldc, stream);
+}
+
+gemm_status_t run_epi(int dtype, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                      const void* B, int64_t ldb, void* C, int64_t ldc, void* stream,
+                      const gemm_config_t* forced, const gemm_epilogue_t* epi) {
+  g_err[0] = 0;
+  gemm_status_t st = validate(dtype, M, N, K, A, lda, B, ldb, C, ldc);
+  if (st != GEMM_OK) return st;
+  if (!epi) return fail(GEMM_ERR_INVALID_ARG, "epi is NULL");
+  if (epi->act != GEMM_ACT_NONE && epi->act != GEMM_ACT_RELU)
+    return fail(GEMM_ERR_INVALID_ARG, "unknown activation %d", epi->act);
+  const size_t es = dtype == GEMM_DTYPE_F32 ? 4 : 2;
+  if (epi->bias && overlap(epi->bias, (size_t)N * 4, C, span_bytes(M, N, ldc, es)))
+    return fail(GEMM_ERR_ALIAS, "bias overlaps C");
+  gemm_config_t cfg;
+  st = resolve(dtype, M, N, K, forced, false, cfg, true);
+  if (st != GEMM_OK) return st;
+  if (M == 0 || N == 0) return GEMM_OK;
+  Params p = make_params(A, lda, B, ldb, C, ldc, M, N, K);
+  p.epi.on = true;
+  p.epi.alpha = epi->alpha;
+  p.epi.beta = epi->beta;
+  p.epi.bias = epi->bias;
+  p.epi.act = epi->act;
+  // The vector forms read the bias four floats at a time.
+  const bool vec = vector_path(dtype, A, lda, B, ldb, C, ldc, K, N) &&
+                   (!epi->bias || aligned16(epi->bias));
+  const TileMap map = make_map(cfg, M, N);
+  const hipError_t e =
+      table().v[dtype][cfg.id].launch_epi(p, map, vec, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(GEMM_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+  return GEMM_OK;
 }
 
 gemm_status_t run_splitk(int dtype, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
@@ -385,6 +422,18 @@ gemm_status_t gemm_f16_ex(int64_t M, int64_t N, int64_t K, const gemm_f16_t* A, 
                           void* stream, const gemm_config_t* cfg) {
   if (!cfg) return fail(GEMM_ERR_INVALID_ARG, "cfg is NULL");
   return run(GEMM_DTYPE_F16, M, N, K, A, lda, B, ldb, C, ldc, stream, cfg);
+}
+
+gemm_status_t gemm_f32_epi(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
+                           const float* B, int64_t ldb, float* C, int64_t ldc, void* stream,
+                           const gemm_config_t* cfg, const gemm_epilogue_t* epi) {
+  return run_epi(GEMM_DTYPE_F32, M, N, K, A, lda, B, ldb, C, ldc, stream, cfg, epi);
+}
+
+gemm_status_t gemm_f16_epi(int64_t M, int64_t N, int64_t K, const gemm_f16_t* A, int64_t lda,
+                           const gemm_f16_t* B, int64_t ldb, gemm_f16_t* C, int64_t ldc,
+                           void* stream, const gemm_config_t* cfg, const gemm_epilogue_t* epi) {
+  return run_epi(GEMM_DTYPE_F16, M, N, K, A, lda, B, ldb, C, ldc, stream, cfg, epi);
 }
 
 gemm_status_t gemm_f32_splitk(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,

@@ -16,6 +16,26 @@ namespace gemm {
 // ---------------------------------------------------------------------------
 // Kernel arguments.
 // ---------------------------------------------------------------------------
+// Fused epilogue of gemm_*_epi (on = false: plain C = A x B).
+struct Epi {
+  bool on = false;
+  float alpha = 1.f, beta = 0.f;
+  const float* bias = nullptr;
+  int act = GEMM_ACT_NONE;
+};
+
+// One output of the fused epilogue: alpha*acc (+ beta*c_old when beta != 0)
+// (+ bias when there is one), then the activation; FP32 throughout.  The
+// caller reads c_old and bias only when they take part (C must not be read
+// when beta == 0).
+__device__ __forceinline__ float epi_value(const Epi& e, float acc, float c_old, float bias) {
+  float v = e.alpha * acc;
+  if (e.beta != 0.f) v = __builtin_fmaf(e.beta, c_old, v);
+  if (e.bias) v += bias;
+  if (e.act == GEMM_ACT_RELU) v = v < 0.f ? 0.f : v;
+  return v;
+}
+
 struct Params {
   const void* A;
   const void* B;
@@ -27,6 +47,7 @@ struct Params {
   // partial C + s*c_stride.  splits = 1: the whole K into C.
   int splits = 1, kc = 0;
   int64_t c_stride = 0;
+  Epi epi;
 };
 
 // Workgroup -> output tile order.  See gemm_order_t in gemm.h.
@@ -138,6 +159,9 @@ struct Variant {
   // of its dtype, both with the GPU full (measured at 4096^3 on MI355X);
   // the shape heuristic's cost model divides tile work by it.
   float eff;
+  // Launch with the fused epilogue (p.epi.on), or nullptr when the kernel
+  // has no such form.
+  LaunchFn launch_epi;
 };
 
 // Per-family registration (each kernel file defines its table).

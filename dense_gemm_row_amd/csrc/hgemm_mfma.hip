@@ -81,7 +81,7 @@ __device__ inline unsigned short f16_bits(float x) {
   return __builtin_bit_cast(unsigned short, static_cast<_Float16>(x));
 }
 
-template <int BM, int BN, int WM, int WN, bool VEC>
+template <int BM, int BN, int WM, int WN, bool VEC, bool EPI>
 __global__ void __launch_bounds__((Shape<BM, BN, WM, WN>::NT))
 hgemm_mfma_kernel(Params p, TileMap map) {
   using S = Shape<BM, BN, WM, WN>;
@@ -231,7 +231,19 @@ hgemm_mfma_kernel(Params p, TileMap map) {
   }
 
   // Epilogue: FP32 -> FP16 (RNE), NB adjacent columns per lane and row.
+  // EPI: the fused epilogue (alpha, beta with the old FP16 C, bias,
+  // activation) in FP32 before the one rounding.
   const int col = n0 + wn0 + NB * lrow;
+  auto out = [&](int mb, int nb, int r, const unsigned short* dst) -> unsigned short {
+    if constexpr (!EPI) {
+      return f16_bits(acc[mb][nb][r]);
+    } else {
+      const float c_old =
+          p.epi.beta != 0.f ? (float)__builtin_bit_cast(_Float16, dst[nb]) : 0.f;
+      const float bias = p.epi.bias ? p.epi.bias[col + nb] : 0.f;
+      return f16_bits(epi_value(p.epi, acc[mb][nb][r], c_old, bias));
+    }
+  };
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
@@ -243,20 +255,19 @@ hgemm_mfma_kernel(Params p, TileMap map) {
         if (col < N) {
           if constexpr (NB == 4) {
             uint2 v;
-            v.x = f16_bits(acc[mb][0][r]) | ((unsigned)f16_bits(acc[mb][1][r]) << 16);
-            v.y = f16_bits(acc[mb][2][r]) | ((unsigned)f16_bits(acc[mb][3][r]) << 16);
+            v.x = out(mb, 0, r, dst) | ((unsigned)out(mb, 1, r, dst) << 16);
+            v.y = out(mb, 2, r, dst) | ((unsigned)out(mb, 3, r, dst) << 16);
             *reinterpret_cast<uint2*>(dst) = v;
           } else if constexpr (NB == 2) {
-            *reinterpret_cast<unsigned*>(dst) =
-                f16_bits(acc[mb][0][r]) | ((unsigned)f16_bits(acc[mb][1][r]) << 16);
+            *reinterpret_cast<unsigned*>(dst) = out(mb, 0, r, dst) | ((unsigned)out(mb, 1, r, dst) << 16);
           } else {
-            *dst = f16_bits(acc[mb][0][r]);
+            *dst = out(mb, 0, r, dst);
           }
         }
       } else {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
-          if (col + nb < N) dst[nb] = f16_bits(acc[mb][nb][r]);
+          if (col + nb < N) dst[nb] = out(mb, nb, r, dst);
       }
     }
   }
@@ -266,10 +277,17 @@ template <int BM, int BN, int WM, int WN>
 hipError_t launch(const Params& p, const TileMap& map, bool vec, hipStream_t stream) {
   using S = Shape<BM, BN, WM, WN>;
   const dim3 grid(map.tiles_m * map.tiles_n), block(S::NT);
-  if (vec)
-    hipLaunchKernelGGL((hgemm_mfma_kernel<BM, BN, WM, WN, true>), grid, block, 0, stream, p, map);
-  else
-    hipLaunchKernelGGL((hgemm_mfma_kernel<BM, BN, WM, WN, false>), grid, block, 0, stream, p, map);
+  if (p.epi.on) {
+    if (vec)
+      hipLaunchKernelGGL((hgemm_mfma_kernel<BM, BN, WM, WN, true, true>), grid, block, 0, stream, p, map);
+    else
+      hipLaunchKernelGGL((hgemm_mfma_kernel<BM, BN, WM, WN, false, true>), grid, block, 0, stream, p, map);
+  } else {
+    if (vec)
+      hipLaunchKernelGGL((hgemm_mfma_kernel<BM, BN, WM, WN, true, false>), grid, block, 0, stream, p, map);
+    else
+      hipLaunchKernelGGL((hgemm_mfma_kernel<BM, BN, WM, WN, false, false>), grid, block, 0, stream, p, map);
+  }
   return hipGetLastError();
 }
 
@@ -348,7 +366,8 @@ int layout_check(int banks, int64_t out[2]) {
     gemm_config_t{0, GEMM_DTYPE_F16, GEMM_FAMILY_MFMA, BM, BN, BK, WM, WN,                   \
                   Shape<BM, BN, WM, WN>::NT, 2, Shape<BM, BN, WM, WN>::LDS_BYTES,            \
                   GEMM_ORDER_XCD, 4, 1, "mfma_f16_" #BM "x" #BN "x64_w" #WM "x" #WN},           \
-        &launch<BM, BN, WM, WN>, &layout_check<BM, BN, WM, WN>, nullptr, EFF                 \
+        &launch<BM, BN, WM, WN>, &layout_check<BM, BN, WM, WN>, nullptr, EFF,                \
+        &launch<BM, BN, WM, WN>                                                              \
   }
 
 const Variant kVariants[] = {

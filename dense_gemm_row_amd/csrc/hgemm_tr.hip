@@ -77,11 +77,13 @@ __device__ __forceinline__ void static_for(F&& f, std::integer_sequence<int, I..
   (f(IC<I>{}), ...);
 }
 
-// PARTIAL_: the split-K form, whose epilogue writes FP32 partials.
-template <int BM_, int BN_, int WM_, int WN_, int BK_, int NS_, bool PARTIAL_ = false>
+// MODE_: 0 the plain kernel; 1 the split-K form, whose epilogue writes FP32
+// partials; 2 the form with the fused epilogue (alpha, beta, bias,
+// activation).
+template <int BM_, int BN_, int WM_, int WN_, int BK_, int NS_, int MODE_ = 0>
 struct Shape {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BK_, NS = NS_;
-  static constexpr bool PARTIAL = PARTIAL_;
+  static constexpr bool PARTIAL = MODE_ == 1, EPI = MODE_ == 2;
   static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN, NW = WAVES_M * WAVES_N;
   static constexpr int NT = NW * 64;
   static constexpr int MB = WM / 32, NB = WN / 32, KS = BK / 16;
@@ -441,6 +443,36 @@ hgemm_tr_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
         }
     return;
   }
+  if constexpr (S::EPI) {
+    // Fused epilogue straight from the accumulators (same element map as
+    // the partial form): alpha, beta with the old FP16 C (read only when
+    // beta != 0), bias, activation, in FP32; one rounding to FP16; one
+    // 8-byte store of four adjacent outputs.
+    typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+    unsigned short* __restrict__ Ch = static_cast<unsigned short*>(p.C);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          const int row = m0 + wm0 + 32 * mb + l % 32;
+          const int col = n0 + wn0 + 32 * nb + 8 * rq + 4 * (l / 32);
+          if (row < M && col < N) {
+            unsigned short* dst = Ch + (int64_t)row * p.ldc + col;
+            f16x4 c_old = {};
+            f32x4 bias = {};
+            if (p.epi.beta != 0.f) c_old = *reinterpret_cast<const f16x4*>(dst);
+            if (p.epi.bias) bias = *reinterpret_cast<const f32x4*>(p.epi.bias + col);
+            f16x4 h;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              h[e] = (_Float16)epi_value(p.epi, acc[nb][mb][4 * rq + e], (float)c_old[e], bias[e]);
+            *reinterpret_cast<f16x4*>(dst) = h;
+          }
+        }
+    return;
+  }
   __syncthreads();
 
   // Epilogue.  acc[nb][mb] register r of lane l holds C[m][n] with
@@ -632,7 +664,8 @@ int layout_check(int banks, int64_t out[2]) {
                   GEMM_ORDER_XCD, 4, 1,                                                      \
                   "tr_f16_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_s" #NS},                  \
         &launch<Shape<BM, BN, WM, WN, BK, NS>>, &layout_check<Shape<BM, BN, WM, WN, BK, NS>>, \
-        &launch<Shape<BM, BN, WM, WN, BK, NS, true>>, EFF                                   \
+        &launch<Shape<BM, BN, WM, WN, BK, NS, 1>>, EFF,                                     \
+        &launch<Shape<BM, BN, WM, WN, BK, NS, 2>>                                           \
   }
 
 const Variant kVariants[] = {

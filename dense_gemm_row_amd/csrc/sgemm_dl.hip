@@ -59,9 +59,11 @@ __device__ __forceinline__ void static_for(F&& f, std::integer_sequence<int, I..
   (f(IC<I>{}), ...);
 }
 
-template <int BM_, int BN_, int WM_, int WN_, int BK_, int NS_>
+// EPI_: the form with the fused epilogue (alpha, beta, bias, activation).
+template <int BM_, int BN_, int WM_, int WN_, int BK_, int NS_, bool EPI_ = false>
 struct Shape {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BK_, NS = NS_;
+  static constexpr bool EPI = EPI_;
   static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN, NW = WAVES_M * WAVES_N;
   static constexpr int NT = NW * 64;
   static constexpr int MB = WM / 32, NB = WN / 32, KG = BK / 8;  // k groups of 8 per slice
@@ -343,13 +345,27 @@ sgemm_dl_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
       const int row = m0 + wm0 + 32 * mb + 8 * (r / 4) + 4 * (l / 32) + (r % 4);
       if (row < M && col < N) {
         vecNB v;
+        float* dst = C + (int64_t)row * p.ldc + col;
         if constexpr (NB == 1) {
           v = acc[mb][0][r];
         } else {
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb) v[nb] = acc[mb][nb][r];
         }
-        *reinterpret_cast<vecNB*>(C + (int64_t)row * p.ldc + col) = v;
+        if constexpr (S::EPI) {
+          // Fused epilogue on the FP32 accumulators (the old C is read only
+          // when beta != 0).
+          vecNB c_old = {}, bias = {};
+          if (p.epi.beta != 0.f) c_old = *reinterpret_cast<const vecNB*>(dst);
+          if (p.epi.bias) bias = *reinterpret_cast<const vecNB*>(p.epi.bias + col);
+          if constexpr (NB == 1) {
+            v = epi_value(p.epi, v, c_old, bias);
+          } else {
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) v[nb] = epi_value(p.epi, v[nb], c_old[nb], bias[nb]);
+          }
+        }
+        *reinterpret_cast<vecNB*>(dst) = v;
       }
     }
 }
@@ -453,7 +469,8 @@ int layout_check(int banks, int64_t out[2]) {
                   GEMM_ORDER_XCD, GM, 1,                                                     \
                   "dl_f32_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_s" #NS},                  \
         &launch<Shape<BM, BN, WM, WN, BK, NS>>, &layout_check<Shape<BM, BN, WM, WN, BK, NS>>, \
-        &launch<Shape<BM, BN, WM, WN, BK, NS>>, EFF                                         \
+        &launch<Shape<BM, BN, WM, WN, BK, NS>>, EFF,                                        \
+        &launch<Shape<BM, BN, WM, WN, BK, NS, true>>                                        \
   }
 
 const Variant kVariants[] = {

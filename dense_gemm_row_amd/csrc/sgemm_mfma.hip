@@ -83,7 +83,7 @@ __device__ inline f32x16 mfma(float a, float b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
 
-template <int BM, int BN, int BK, int WM, int WN, bool VEC>
+template <int BM, int BN, int BK, int WM, int WN, bool VEC, bool EPI>
 __global__ void __launch_bounds__((Shape<BM, BN, BK, WM, WN>::NT))
 sgemm_mfma_kernel(Params p, TileMap map) {
   using S = Shape<BM, BN, BK, WM, WN>;
@@ -215,8 +215,19 @@ sgemm_mfma_kernel(Params p, TileMap map) {
     }
   }
 
-  // Epilogue: lane owns NB adjacent columns of each of its rows.
+  // Epilogue: lane owns NB adjacent columns of each of its rows.  EPI:
+  // the fused epilogue (alpha, beta with the old C, bias, activation) on
+  // the FP32 accumulators before the store.
   const int col = n0 + wn0 + NB * lrow;
+  auto out = [&](int mb, int nb, int r, const float* dst) -> float {
+    if constexpr (!EPI) {
+      return acc[mb][nb][r];
+    } else {
+      const float c_old = p.epi.beta != 0.f ? dst[nb] : 0.f;
+      const float bias = p.epi.bias ? p.epi.bias[col + nb] : 0.f;
+      return epi_value(p.epi, acc[mb][nb][r], c_old, bias);
+    }
+  };
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
@@ -228,17 +239,17 @@ sgemm_mfma_kernel(Params p, TileMap map) {
         if (col < N) {
           vecNB v;
           if constexpr (NB == 1) {
-            v = acc[mb][0][r];
+            v = out(mb, 0, r, dst);
           } else {
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) v[nb] = acc[mb][nb][r];
+            for (int nb = 0; nb < NB; ++nb) v[nb] = out(mb, nb, r, dst);
           }
           *reinterpret_cast<vecNB*>(dst) = v;
         }
       } else {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
-          if (col + nb < N) dst[nb] = acc[mb][nb][r];
+          if (col + nb < N) dst[nb] = out(mb, nb, r, dst);
       }
     }
   }
@@ -248,10 +259,17 @@ template <int BM, int BN, int BK, int WM, int WN>
 hipError_t launch(const Params& p, const TileMap& map, bool vec, hipStream_t stream) {
   using S = Shape<BM, BN, BK, WM, WN>;
   const dim3 grid(map.tiles_m * map.tiles_n), block(S::NT);
-  if (vec)
-    hipLaunchKernelGGL((sgemm_mfma_kernel<BM, BN, BK, WM, WN, true>), grid, block, 0, stream, p, map);
-  else
-    hipLaunchKernelGGL((sgemm_mfma_kernel<BM, BN, BK, WM, WN, false>), grid, block, 0, stream, p, map);
+  if (p.epi.on) {
+    if (vec)
+      hipLaunchKernelGGL((sgemm_mfma_kernel<BM, BN, BK, WM, WN, true, true>), grid, block, 0, stream, p, map);
+    else
+      hipLaunchKernelGGL((sgemm_mfma_kernel<BM, BN, BK, WM, WN, false, true>), grid, block, 0, stream, p, map);
+  } else {
+    if (vec)
+      hipLaunchKernelGGL((sgemm_mfma_kernel<BM, BN, BK, WM, WN, true, false>), grid, block, 0, stream, p, map);
+    else
+      hipLaunchKernelGGL((sgemm_mfma_kernel<BM, BN, BK, WM, WN, false, false>), grid, block, 0, stream, p, map);
+  }
   return hipGetLastError();
 }
 
@@ -322,7 +340,8 @@ int layout_check(int banks, int64_t out[2]) {
     gemm_config_t{0, GEMM_DTYPE_F32, GEMM_FAMILY_MFMA, BM, BN, BK, WM, WN,                   \
                   Shape<BM, BN, BK, WM, WN>::NT, 2, Shape<BM, BN, BK, WM, WN>::LDS_BYTES,    \
                   GEMM_ORDER_XCD, 8, 1, "mfma_f32_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN},      \
-        &launch<BM, BN, BK, WM, WN>, &layout_check<BM, BN, BK, WM, WN>, nullptr, EFF         \
+        &launch<BM, BN, BK, WM, WN>, &layout_check<BM, BN, BK, WM, WN>, nullptr, EFF,        \
+        &launch<BM, BN, BK, WM, WN>                                                          \
   }
 
 const Variant kVariants[] = {

@@ -33,7 +33,11 @@ ORDER_ROW = 0
 ORDER_GROUPED = 1
 ORDER_XCD = 2
 
-EXPORTS = ["gemm_f32", "gemm_f16", "gemm_f32_ex", "gemm_f16_ex", "gemm_f32_splitk",
+ACT_NONE = 0
+ACT_RELU = 1
+
+EXPORTS = ["gemm_f32", "gemm_f16", "gemm_f32_ex", "gemm_f16_ex", "gemm_f32_epi", "gemm_f16_epi",
+           "gemm_f32_splitk",
            "gemm_f16_splitk", "gemm_splitk_workspace_bytes", "gemm_select_splitk_config",
            "gemm_num_configs", "gemm_get_config", "gemm_select_config", "gemm_tile_of_block",
            "gemm_layout_check", "gemm_load_tuning", "gemm_status_string",
@@ -57,6 +61,12 @@ class GemmConfig(ctypes.Structure):
         return f"GemmConfig({self.as_dict()})"
 
 
+class GemmEpilogue(ctypes.Structure):
+    """gemm_epilogue_t: C = act(alpha * (A x B) + beta * C + bias[j])."""
+    _fields_ = [("alpha", ctypes.c_float), ("beta", ctypes.c_float), ("bias", ctypes.c_void_p),
+                ("act", ctypes.c_int32)]
+
+
 class GemmError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
@@ -78,6 +88,9 @@ def _declare(lib):
         getattr(lib, name).restype = ctypes.c_int
     for name in ("gemm_f32_ex", "gemm_f16_ex"):
         getattr(lib, name).argtypes = gemm_args + [cfgp]
+        getattr(lib, name).restype = ctypes.c_int
+    for name in ("gemm_f32_epi", "gemm_f16_epi"):
+        getattr(lib, name).argtypes = gemm_args + [cfgp, ctypes.POINTER(GemmEpilogue)]
         getattr(lib, name).restype = ctypes.c_int
     for name in ("gemm_f32_splitk", "gemm_f16_splitk"):
         getattr(lib, name).argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, p, i64, p, cfgp]
@@ -140,6 +153,20 @@ def gemm_f32_ex(M, N, K, A, lda, B, ldb, C, ldc, stream, cfg: GemmConfig) -> int
 def gemm_f16_ex(M, N, K, A, lda, B, ldb, C, ldc, stream, cfg: GemmConfig) -> int:
     return lib().gemm_f16_ex(M, N, K, A, lda, B, ldb, C, ldc, stream,
                              ctypes.byref(cfg) if cfg is not None else None)
+
+
+def gemm_f32_epi(M, N, K, A, lda, B, ldb, C, ldc, stream, cfg: GemmConfig | None,
+                 epi: GemmEpilogue | None) -> int:
+    return lib().gemm_f32_epi(M, N, K, A, lda, B, ldb, C, ldc, stream,
+                              ctypes.byref(cfg) if cfg is not None else None,
+                              ctypes.byref(epi) if epi is not None else None)
+
+
+def gemm_f16_epi(M, N, K, A, lda, B, ldb, C, ldc, stream, cfg: GemmConfig | None,
+                 epi: GemmEpilogue | None) -> int:
+    return lib().gemm_f16_epi(M, N, K, A, lda, B, ldb, C, ldc, stream,
+                              ctypes.byref(cfg) if cfg is not None else None,
+                              ctypes.byref(epi) if epi is not None else None)
 
 
 def gemm_f32_splitk(M, N, K, A, lda, B, ldb, C, ldc, workspace, workspace_bytes, stream=None,
@@ -245,7 +272,8 @@ def _ld(t) -> int:
     return max(int(t.stride(0)), 1) if t.shape[0] > 1 else max(int(t.shape[1]), 1)
 
 
-def matmul(a, b, out=None, config: GemmConfig | None = None, stream=None, split_k: bool = True):
+def matmul(a, b, out=None, config: GemmConfig | None = None, stream=None, split_k: bool = True,
+           alpha: float = 1.0, beta: float = 0.0, bias=None, act: int = ACT_NONE):
     """C = a @ b on the GPU through libgemm.  a: M x K, b: K x N, both
     float32 or both float16, row-major (any row stride).  Returns ``out``
     (allocated when None).  Raises GemmError on a non-OK status.
@@ -253,7 +281,11 @@ def matmul(a, b, out=None, config: GemmConfig | None = None, stream=None, split_
     With ``config`` None and ``split_k`` True, shapes for which the library
     chooses split-K (too few output tiles for the GPU) run the split-K form
     with a workspace allocated here; a ``config`` with ``splits`` > 1 forces
-    that split."""
+    that split.
+
+    alpha, beta, bias (a float32 GPU tensor of N values) and act select the
+    fused epilogue out = act(alpha * (a @ b) + beta * out + bias) (through
+    gemm_*_epi; ``out`` must then be given when beta != 0)."""
     import torch
     if a.dtype != b.dtype or a.dtype not in (torch.float32, torch.float16):
         raise TypeError("a and b must both be float32 or both float16")
@@ -271,6 +303,17 @@ def matmul(a, b, out=None, config: GemmConfig | None = None, stream=None, split_
         stream = torch.cuda.current_stream(a.device).cuda_stream
     args = (M, N, K, a.data_ptr(), _ld(a), b.data_ptr(), _ld(b), out.data_ptr(), _ld(out), stream)
     dtype = DTYPE_F32 if a.dtype == torch.float32 else DTYPE_F16
+    if alpha != 1.0 or beta != 0.0 or bias is not None or act != ACT_NONE:
+        if bias is not None and (bias.dtype != torch.float32 or bias.numel() != N or not bias.is_cuda
+                                 or not bias.is_contiguous()):
+            raise ValueError("bias must be a contiguous float32 GPU tensor of N values")
+        epi = GemmEpilogue(float(alpha), float(beta), bias.data_ptr() if bias is not None else None,
+                           int(act))
+        fn = gemm_f32_epi if dtype == DTYPE_F32 else gemm_f16_epi
+        st = fn(*args, config, epi)
+        if st != GEMM_OK:
+            raise GemmError(st, fn.__name__)
+        return out
     split_cfg = config
     if split_cfg is None and split_k and M > 0 and N > 0:
         split_cfg = gemm_select_splitk_config(dtype, M, N, K)

@@ -178,6 +178,49 @@ gemm_status_t gemm_f16_splitk(int64_t M, int64_t N, int64_t K,
 int64_t gemm_splitk_workspace_bytes(int32_t dtype, int64_t M, int64_t N, int64_t K,
                                     int32_t splits);
 
+/* Activation applied by the fused epilogue. */
+typedef enum gemm_act {
+    GEMM_ACT_NONE = 0,
+    GEMM_ACT_RELU = 1 /* max(x, 0) */
+} gemm_act_t;
+
+/*
+ * Fused epilogue: C = act(alpha * (A x B) + beta * C + bias[j]).
+ * alpha and beta are the scaling parameters of the tiled SGEMM kernel in
+ * the lqnn.cn SGEMM article (section 3.3; the page leaves beta unapplied,
+ * here it has its BLAS meaning); bias and activation are the post-GEMM
+ * operations that the GB300 GEMM article (section 7.1) fuses into the
+ * epilogue instead of a second pass over C.
+ */
+typedef struct gemm_epilogue {
+    float alpha;       /* scales the product A x B                            */
+    float beta;        /* scales the old C; 0: C is not read (may hold NaN)   */
+    const float *bias; /* NULL, or N device floats added per column j         */
+    int32_t act;       /* gemm_act_t                                          */
+} gemm_epilogue_t;
+
+/*
+ * GEMM with the fused epilogue, computed in FP32 from the FP32 accumulator
+ * (and, for FP16, from the binary16 old C) and rounded once to the output
+ * type.  Same layout, stream, alignment and error conventions as gemm_f32 /
+ * gemm_f16, plus:
+ *   epi NULL or epi->act unknown                       -> INVALID_ARG
+ *   bias overlapping C                                 -> ALIAS
+ *   forced variant without a fused-epilogue form       -> UNSUPPORTED
+ * cfg NULL: the same selection as gemm_f32 / gemm_f16 (among the variants
+ * with a fused-epilogue form).  K == 0 gives C = act(beta * C + bias).
+ */
+gemm_status_t gemm_f32_epi(int64_t M, int64_t N, int64_t K,
+                           const float *A, int64_t lda,
+                           const float *B, int64_t ldb,
+                           float *C, int64_t ldc, void *stream,
+                           const gemm_config_t *cfg, const gemm_epilogue_t *epi);
+gemm_status_t gemm_f16_epi(int64_t M, int64_t N, int64_t K,
+                           const gemm_f16_t *A, int64_t lda,
+                           const gemm_f16_t *B, int64_t ldb,
+                           gemm_f16_t *C, int64_t ldc, void *stream,
+                           const gemm_config_t *cfg, const gemm_epilogue_t *epi);
+
 /* Variant table: count per dtype, and the description of variant idx. */
 int32_t gemm_num_configs(int32_t dtype);
 gemm_status_t gemm_get_config(int32_t dtype, int32_t idx, gemm_config_t *out);

@@ -77,20 +77,35 @@ WS_GUARD = 256  # canary floats on each side of a split-K workspace
 
 
 def run(A: np.ndarray, B: np.ndarray, cfg=None, pad=(0, 0, 0), offset=(0, 0, 0),
-        repeat: int = 1, split=None):
+        repeat: int = 1, split=None, epi=None):
     """Compute A @ B through libgemm.  Returns (C as numpy, C DevMatrix).
 
     split: None for the plain entry points; "auto" for gemm_*_splitk with
     cfg = NULL; or a GemmConfig (its `splits` set) for a forced split-K
     call.  The workspace is sized by gemm_splitk_workspace_bytes and has
-    canary guards that must survive the call."""
+    canary guards that must survive the call.
+
+    epi: None, or a dict with alpha, beta, C0 (initial C, or None: C keeps
+    its NaN canaries), bias (float32 array of N, or None), act and
+    bias_offset (floats to misalign the bias by): gemm_*_epi with `cfg`
+    (None: the library's choice)."""
     kind = "f32" if A.dtype == np.float32 else "f16"
     dtype = gemm.DTYPE_F32 if kind == "f32" else gemm.DTYPE_F16
     M, K = A.shape
     N = B.shape[1]
     dA = DevMatrix(A, M, K, kind, pad=pad[0], offset=offset[0])
     dB = DevMatrix(B, K, N, kind, pad=pad[1], offset=offset[1])
-    dC = DevMatrix(None, M, N, kind, pad=pad[2], offset=offset[2])
+    dC = DevMatrix(None if epi is None else epi.get("C0"), M, N, kind, pad=pad[2], offset=offset[2])
+    bias_dev, epi_s = None, None
+    if epi is not None:
+        bias = epi.get("bias")
+        boff = epi.get("bias_offset", 0)
+        if bias is not None:
+            host = np.concatenate([np.zeros(boff, np.float32), np.asarray(bias, np.float32)])
+            bias_dev = torch.from_numpy(host).to("cuda")
+        epi_s = gemm.GemmEpilogue(float(epi.get("alpha", 1.0)), float(epi.get("beta", 0.0)),
+                                  bias_dev.data_ptr() + 4 * boff if bias_dev is not None else None,
+                                  int(epi.get("act", 0)))
     stream = torch.cuda.current_stream().cuda_stream
     ws = None
     if split is not None:
@@ -101,7 +116,10 @@ def run(A: np.ndarray, B: np.ndarray, cfg=None, pad=(0, 0, 0), offset=(0, 0, 0),
         ws = torch.from_numpy(host.view(np.int32)).to("cuda")
     for _ in range(repeat):
         args = (M, N, K, dA.ptr, dA.ld, dB.ptr, dB.ld, dC.ptr, dC.ld)
-        if split is not None:
+        if epi is not None:
+            fn = gemm.gemm_f32_epi if kind == "f32" else gemm.gemm_f16_epi
+            st = fn(*args, stream, cfg, epi_s)
+        elif split is not None:
             fn = gemm.gemm_f32_splitk if kind == "f32" else gemm.gemm_f16_splitk
             st = fn(*args, ws.data_ptr() + 4 * WS_GUARD, 4 * (ws.numel() - 2 * WS_GUARD), stream,
                     None if split == "auto" else split)

@@ -247,3 +247,21 @@ def test_tuning_table_splits_column(tmp_path):
         gemm.gemm_load_tuning(None)
     path.write_text(f"f16 1 2 3 {cfg.name.decode()} 2 4 0\n")
     assert gemm.gemm_load_tuning(str(path)) == gemm.GEMM_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("fn", [gemm.gemm_f32_epi, gemm.gemm_f16_epi])
+def test_epilogue_argument_validation(fn):
+    dt = gemm.DTYPE_F32 if fn is gemm.gemm_f32_epi else gemm.DTYPE_F16
+    es = 4 if dt == gemm.DTYPE_F32 else 2
+    base = (64, 64, 64, PA, 64, PB, 64, PC, 64, None)
+    ok = gemm.GemmEpilogue(1.0, 0.0, None, gemm.ACT_NONE)
+    assert fn(*base, None, None) == gemm.GEMM_ERR_INVALID_ARG                     # epi NULL
+    assert fn(*base, None, gemm.GemmEpilogue(1.0, 0.0, None, 7)) == gemm.GEMM_ERR_INVALID_ARG
+    assert fn(*base, None, gemm.GemmEpilogue(1.0, 0.0, PC + 64 * es, 0)) == gemm.GEMM_ERR_ALIAS
+    assert fn(-1, 64, 64, PA, 64, PB, 64, PC, 64, None, None, ok) == gemm.GEMM_ERR_INVALID_ARG
+    # Variants without a fused-epilogue form are refused when forced.
+    for c in gemm.configs(dt):
+        name = c.name.decode()
+        if name.startswith(("pipe_", "simt_")):
+            assert fn(*base, c, ok) == gemm.GEMM_ERR_UNSUPPORTED, name
+    assert fn(0, 64, 64, PA, 64, PB, 64, 0, 64, None, None, ok) == gemm.GEMM_OK   # M == 0

@@ -284,3 +284,92 @@ def test_matmul_uses_split_k():
     C = c.cpu().numpy()
     rep = check_rows(A, B, C, [0, 511, 1023])
     assert rep["ok"], rep
+
+
+# --------------------------------------------------------------------------
+# Fused epilogue (gemm_*_epi): act(alpha * AB + beta * C + bias).
+# --------------------------------------------------------------------------
+def _epi_cfgs(kind):
+    dt = gemm.DTYPE_F32 if kind == "f32" else gemm.DTYPE_F16
+    return [c for c in gemm.configs(dt) if c.name.decode().startswith(("dl_", "tr_", "mfma_"))]
+
+
+EPI_CASES = [dict(alpha=2.0, beta=-1.0, act=0), dict(alpha=-1.0, beta=0.5, act=1),
+             dict(alpha=1.0, beta=0.0, act=1)]
+EPI_SHAPES = [(1, 8, 8), (31, 40, 17), (130, 264, 96), (257, 136, 64)]
+
+
+def _epi_ref(A, B, C0, e, bias):
+    return oracle.gemm_rows_epi(A, B, C0, e["alpha"], e["beta"], bias, e["act"])
+
+
+@pytest.mark.parametrize("kind", ["f32", "f16"])
+@pytest.mark.parametrize("shape", EPI_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_epilogue_exact_small_int(kind, shape):
+    """Small integers, alpha, beta in {2, -1, 0.5, 0}, integer bias: every
+    value is exact in FP32 and FP16, so each variant with a fused-epilogue
+    form must match the oracle bit for bit (beta = 0 with C holding NaN
+    canaries checks that C is not read)."""
+    M, N, K = shape
+    dt = np.float32 if kind == "f32" else np.float16
+    A, B = _ints(M, N, K, kind, seed=13)
+    C0 = synth.small_int(13, 2, M, N, -3, 3, dtype=dt)
+    bias = synth.small_int(13, 3, 1, N, -3, 3).ravel()
+    for cfg in _epi_cfgs(kind):
+        for e in EPI_CASES:
+            log(f"{kind} epilogue exact cfg={cfg.name.decode()} {e} shape={shape}")
+            c0 = C0 if e["beta"] != 0.0 else None
+            C, _ = run(A, B, cfg, epi=dict(e, C0=c0, bias=bias))
+            ref, _ = _epi_ref(A, B, C0, e, bias)
+            assert np.array_equal(C.astype(np.float64), ref), (cfg.name, e)
+
+
+@pytest.mark.parametrize("kind", ["f32", "f16"])
+def test_epilogue_random_and_paths(kind):
+    """Random operands, random bias, alpha/beta not powers of two: within the
+    tolerance on the epilogue's error scale, for the library's choice, the
+    unaligned path (padded leading dimensions) and a misaligned bias."""
+    M, N, K = 300, 520, 700
+    A, B = synth.workload(M, N, K, kind, seed=21)
+    dt = np.float32 if kind == "f32" else np.float16
+    C0 = synth.uniform_f32(21, 2, M, N).astype(dt)
+    bias = synth.uniform_f32(21, 3, 1, N).ravel()
+    e = dict(alpha=0.7, beta=-0.3, act=1)
+    ref, den = _epi_ref(A, B, C0, e, bias)
+    tol = oracle.SGEMM_TOL if kind == "f32" else oracle.HGEMM_TOL
+    for name, kw in (("auto", {}), ("padded", dict(pad=(3, 5, 7))), ("bias+1", {"boff": 1})):
+        log(f"{kind} epilogue random {name}")
+        epi = dict(e, C0=C0, bias=bias, bias_offset=kw.pop("boff", 0))
+        C, _ = run(A, B, None, epi=epi, **kw)
+        rep = oracle.check(C, ref, den, tol)
+        log(f"  max_rel={rep['max_rel']:.3e}")
+        assert rep["ok"], (name, rep)
+
+
+@pytest.mark.parametrize("kind", ["f32", "f16"])
+def test_epilogue_k_zero(kind):
+    """K = 0: C = act(beta * C + bias)."""
+    dt = np.float32 if kind == "f32" else np.float16
+    A, B = np.zeros((40, 0), dt), np.zeros((0, 24), dt)
+    C0 = synth.small_int(3, 2, 40, 24, -3, 3, dtype=dt)
+    bias = synth.small_int(3, 3, 1, 24, -3, 3).ravel()
+    e = dict(alpha=3.0, beta=2.0, act=1)
+    log(f"{kind} epilogue K=0")
+    C, _ = run(A, B, None, epi=dict(e, C0=C0, bias=bias))
+    expect = np.maximum(2.0 * C0.astype(np.float64) + bias[None, :], 0.0)
+    assert np.array_equal(C.astype(np.float64), expect)
+
+
+def test_matmul_fused_epilogue():
+    import torch
+    A, B = synth.workload(256, 512, 384, "f16", seed=17)
+    C0 = synth.uniform_f32(17, 2, 256, 512).astype(np.float16)
+    bias = synth.uniform_f32(17, 3, 1, 512).ravel()
+    out = torch.from_numpy(C0.copy()).cuda()
+    log("matmul f16 fused epilogue")
+    gemm.matmul(torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda(), out=out, alpha=1.5,
+                beta=0.25, bias=torch.from_numpy(bias).cuda(), act=gemm.ACT_RELU)
+    torch.cuda.synchronize()
+    ref, den = oracle.gemm_rows_epi(A, B, C0, 1.5, 0.25, bias, 1)
+    rep = oracle.check(out.cpu().numpy(), ref, den, oracle.HGEMM_TOL)
+    assert rep["ok"], rep
