@@ -157,6 +157,15 @@ struct Shape {
   __host__ __device__ static constexpr int epi_byte(int m, int s) {
     return m * EPI_ROW + 8 * (s ^ (m % EPI_SPR));
   }
+  // Fused-epilogue staging (FP32, two passes of WM/2 rows in the same
+  // region): R32 rows per array, 16-byte chunk q of local row m at chunk
+  // position q ^ (m % CPR32); RPI32 rows per read instruction.
+  static constexpr int CPR32 = WN / 4, ROW32 = WN * 4, R32 = RPA / 2, RPI32 = 64 / CPR32;
+  static_assert(MB % 2 == 0 && CPR32 >= 16 && R32 % RPI32 == 0 && R32 % 32 == 0 &&
+                R32 * ROW32 == RPA * EPI_ROW, "fused-epilogue staging");
+  __host__ __device__ static constexpr int epi32_byte(int m, int q) {
+    return m * ROW32 + 16 * (q ^ (m % CPR32));
+  }
 };
 
 __device__ inline f32x16 mfma(f16x8 a, f16x8 b, f32x16 c) {
@@ -443,36 +452,6 @@ hgemm_tr_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
         }
     return;
   }
-  if constexpr (S::EPI) {
-    // Fused epilogue straight from the accumulators (same element map as
-    // the partial form): alpha, beta with the old FP16 C (read only when
-    // beta != 0), bias, activation, in FP32; one rounding to FP16; one
-    // 8-byte store of four adjacent outputs.
-    typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
-    unsigned short* __restrict__ Ch = static_cast<unsigned short*>(p.C);
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int rq = 0; rq < 4; ++rq) {
-          const int row = m0 + wm0 + 32 * mb + l % 32;
-          const int col = n0 + wn0 + 32 * nb + 8 * rq + 4 * (l / 32);
-          if (row < M && col < N) {
-            unsigned short* dst = Ch + (int64_t)row * p.ldc + col;
-            f16x4 c_old = {};
-            f32x4 bias = {};
-            if (p.epi.beta != 0.f) c_old = *reinterpret_cast<const f16x4*>(dst);
-            if (p.epi.bias) bias = *reinterpret_cast<const f32x4*>(p.epi.bias + col);
-            f16x4 h;
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              h[e] = (_Float16)epi_value(p.epi, acc[nb][mb][4 * rq + e], (float)c_old[e], bias[e]);
-            *reinterpret_cast<f16x4*>(dst) = h;
-          }
-        }
-    return;
-  }
   __syncthreads();
 
   // Epilogue.  acc[nb][mb] register r of lane l holds C[m][n] with
@@ -489,6 +468,76 @@ hgemm_tr_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
     }, std::make_integer_sequence<int, S::NW>{});
     ep[i] = sel;
   }, std::make_integer_sequence<int, S::P>{});
+  if constexpr (S::EPI) {
+    // Fused epilogue: the FP32 accumulators go through the same LDS region
+    // in two passes of WM/2 rows (FP32 takes twice the FP16 bytes), 16-byte
+    // chunks XOR-swizzled by row (conflict-free writes and reads); each
+    // lane then reads four adjacent FP32 values of one row, applies alpha,
+    // beta with the old FP16 C (read only when beta != 0), bias and the
+    // activation, rounds once and stores 8 bytes: 32 lanes per 256-byte row
+    // segment, coalesced like the plain epilogue.
+    typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+    typedef int v2i __attribute__((ext_vector_type(2)));
+    const __amdgpu_buffer_rsrc_t rc =
+        make_rsrc(static_cast<const unsigned char*>(p.C), ((int64_t)(M - 1) * p.ldc + N) * 2);
+    constexpr int R32 = S::R32, CPR32 = S::CPR32, RPI32 = S::RPI32;
+    const int q = l % CPR32, col = n0 + wn0 + 4 * q;  // this lane's four columns
+    f32x4 bias = {};
+    if (p.epi.bias && col < N) bias = *reinterpret_cast<const f32x4*>(p.epi.bias + col);
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int mbl = 0; mbl < MB / 2; ++mbl)
+#pragma unroll
+          for (int rq = 0; rq < 4; ++rq) {
+            const int mb = pass * (MB / 2) + mbl;
+            const int m = 32 * mbl + l % 32, q = 8 * nb + 2 * rq + l / 32;
+            f32x4 v = {acc[nb][mb][4 * rq], acc[nb][mb][4 * rq + 1], acc[nb][mb][4 * rq + 2],
+                       acc[nb][mb][4 * rq + 3]};
+            *reinterpret_cast<f32x4*>(ep[m / R32] + S::epi32_byte(m % R32, q)) = v;
+          }
+      // Old-C loads batched (eight rows, then one wait), bias loaded once,
+      // and no branches: the old C is read and the result written through
+      // a buffer descriptor over C, out-of-range elements getting an offset
+      // past its range (loads return 0, stores are dropped).  Per-element
+      // branches would split the code into blocks across which the
+      // compiler waits for every memory operation, stores included.
+      constexpr int ITS = (WM / 2) / RPI32, BATCH = 8;
+      static_assert(ITS % BATCH == 0, "epilogue batches");
+#pragma unroll
+      for (int b0 = 0; b0 < ITS; b0 += BATCH) {
+        unsigned off[BATCH];
+        v2i c_old[BATCH];
+        f32x4 v[BATCH];
+#pragma unroll
+        for (int i = 0; i < BATCH; ++i) {
+          const int row = m0 + wm0 + pass * (WM / 2) + (b0 + i) * RPI32 + l / CPR32;
+          off[i] = (row < M) & (col < N) ? 2u * ((unsigned)row * (unsigned)p.ldc + (unsigned)col) : OOB;
+          c_old[i] = v2i{0, 0};
+        }
+        if (p.epi.beta != 0.f) {
+#pragma unroll
+          for (int i = 0; i < BATCH; ++i) c_old[i] = __builtin_amdgcn_raw_buffer_load_b64(rc, off[i], 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < BATCH; ++i) {
+          const int r = (b0 + i) * RPI32 + l / CPR32;
+          v[i] = *reinterpret_cast<const f32x4*>(ep[((b0 + i) * RPI32) / R32] + S::epi32_byte(r % R32, q));
+        }
+#pragma unroll
+        for (int i = 0; i < BATCH; ++i) {
+          const f16x4 c = __builtin_bit_cast(f16x4, c_old[i]);
+          f16x4 h;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) h[e] = (_Float16)epi_value(p.epi, v[i][e], (float)c[e], bias[e]);
+          __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2i, h), rc, off[i], 0, 0);
+        }
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
@@ -527,7 +576,8 @@ hipError_t launch(const Params& p, const TileMap& map, bool vec, hipStream_t str
   const int64_t lim = 0x7fffffff;
   // Every offset (rows past M and K included) must fit the 31-bit range.
   if (!vec || (int64_t)(p.M + S::BM) * p.lda * 2 > lim || (int64_t)(S::BK + 2) * p.ldb * 2 > lim ||
-      ((int64_t)(p.K > 0 ? p.K - 1 : 0) * p.ldb + p.N) * 2 > lim || (int64_t)p.M * p.lda * 2 > lim) {
+      ((int64_t)(p.K > 0 ? p.K - 1 : 0) * p.ldb + p.N) * 2 > lim || (int64_t)p.M * p.lda * 2 > lim ||
+      (S::EPI && (int64_t)p.M * p.ldc * 2 > lim)) {
     // The general kernel has no split-K form: the caller runs unsplit.
     if (p.splits > 1) return hipErrorNotSupported;
     return hgemm_launch_shape(S::BM, S::BN, S::WM, S::WN, p, map, vec, stream);
@@ -652,6 +702,41 @@ int layout_check(int banks, int64_t out[2]) {
       }
       rconf += lds_conflicts(addr, 8, banks);
     }
+  // Fused-epilogue staging (one pass; both passes use the same map): FP32
+  // writes cover the wave's region once, reads return the element written.
+  {
+    constexpr int R32 = S::R32, CPR32 = S::CPR32, RPI32 = S::RPI32, E32 = R32 * S::ROW32;
+    static int e_row[S::P][E32 / 4], e_col[S::P][E32 / 4];
+    for (int a = 0; a < S::P; ++a)
+      for (int i = 0; i < E32 / 4; ++i) e_row[a][i] = -1;
+    for (int nb = 0; nb < S::NB; ++nb)
+      for (int mbl = 0; mbl < S::MB / 2; ++mbl)
+        for (int rq = 0; rq < 4; ++rq) {
+          for (int l = 0; l < 64; ++l) {
+            const int m = 32 * mbl + l % 32, q = 8 * nb + 2 * rq + l / 32;
+            const int a = m / R32;
+            addr[l] = S::epi32_byte(m % R32, q);
+            if (a >= S::P || addr[l] < 0 || addr[l] + 16 > E32) return 16;
+            for (int e = 0; e < 4; ++e) {
+              if (e_row[a][addr[l] / 4 + e] != -1) return 17;
+              e_row[a][addr[l] / 4 + e] = m;
+              e_col[a][addr[l] / 4 + e] = 32 * nb + 8 * rq + 4 * (l / 32) + e;
+            }
+          }
+          wconf += lds_conflicts(addr, 16, banks);
+        }
+    for (int it = 0; it < (WM / 2) / RPI32; ++it) {
+      for (int l = 0; l < 64; ++l) {
+        const int r = it * RPI32 + l / CPR32, q = l % CPR32;
+        const int a = (it * RPI32) / R32;
+        if (r / R32 != a) return 18;
+        addr[l] = S::epi32_byte(r % R32, q);
+        for (int e = 0; e < 4; ++e)
+          if (e_row[a][addr[l] / 4 + e] != r || e_col[a][addr[l] / 4 + e] != 4 * q + e) return 19;
+      }
+      rconf += lds_conflicts(addr, 16, banks);
+    }
+  }
   out[0] = wconf;
   out[1] = rconf;
   return 0;

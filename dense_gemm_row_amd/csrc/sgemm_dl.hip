@@ -338,36 +338,79 @@ sgemm_dl_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
   // lanes cover 128*NB contiguous bytes of the row).
   float* __restrict__ C = static_cast<float*>(p.C) + sk * p.c_stride;
   const int col = n0 + wn0 + NB * (l % 32);
+  auto row_of = [&](int mb, int r) { return m0 + wm0 + 32 * mb + 8 * (r / 4) + 4 * (l / 32) + (r % 4); };
+  auto acc_vec = [&](int mb, int r) {
+    vecNB v;
+    if constexpr (NB == 1) {
+      v = acc[mb][0][r];
+    } else {
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
+      for (int nb = 0; nb < NB; ++nb) v[nb] = acc[mb][nb][r];
+    }
+    return v;
+  };
+  if constexpr (!S::EPI) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = m0 + wm0 + 32 * mb + 8 * (r / 4) + 4 * (l / 32) + (r % 4);
-      if (row < M && col < N) {
-        vecNB v;
-        float* dst = C + (int64_t)row * p.ldc + col;
-        if constexpr (NB == 1) {
-          v = acc[mb][0][r];
-        } else {
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-          for (int nb = 0; nb < NB; ++nb) v[nb] = acc[mb][nb][r];
+      for (int r = 0; r < 16; ++r) {
+        const int row = row_of(mb, r);
+        if (row < M && col < N) *reinterpret_cast<vecNB*>(C + (int64_t)row * p.ldc + col) = acc_vec(mb, r);
+      }
+  } else {
+    // Fused epilogue on the FP32 accumulators.  The bias of the lane's
+    // columns is loaded once; the old C (read only when beta != 0) is
+    // loaded BATCH rows at a time ahead of their stores; the old C and the
+    // result go through a buffer descriptor over C, out-of-range elements
+    // getting an offset past its range (loads return 0, stores are
+    // dropped), so there are no per-element branches, across which the
+    // compiler would wait for every memory operation, stores included.
+    typedef int vi4 __attribute__((ext_vector_type(4)));
+    typedef int vi2 __attribute__((ext_vector_type(2)));
+    const __amdgpu_buffer_rsrc_t rc =
+        make_rsrc(reinterpret_cast<const unsigned char*>(C), ((int64_t)(M - 1) * p.ldc + N) * 4);
+    auto load = [&](unsigned off) -> vecNB {
+      if constexpr (NB == 4) return __builtin_bit_cast(vecNB, __builtin_amdgcn_raw_buffer_load_b128(rc, off, 0, 0));
+      else if constexpr (NB == 2) return __builtin_bit_cast(vecNB, __builtin_amdgcn_raw_buffer_load_b64(rc, off, 0, 0));
+      else return __builtin_bit_cast(vecNB, __builtin_amdgcn_raw_buffer_load_b32(rc, off, 0, 0));
+    };
+    auto store = [&](vecNB v, unsigned off) {
+      if constexpr (NB == 4) __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(vi4, v), rc, off, 0, 0);
+      else if constexpr (NB == 2) __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(vi2, v), rc, off, 0, 0);
+      else __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, v), rc, off, 0, 0);
+    };
+    vecNB bias = {};
+    if (p.epi.bias && col < N) bias = *reinterpret_cast<const vecNB*>(p.epi.bias + col);
+    constexpr int BATCH = NB == 4 ? 4 : 8;  // registers: BATCH * NB floats in flight
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int r0 = 0; r0 < 16; r0 += BATCH) {
+        unsigned off[BATCH];
+        vecNB c_old[BATCH];
+#pragma unroll
+        for (int i = 0; i < BATCH; ++i) {
+          const int row = row_of(mb, r0 + i);
+          off[i] = (row < M) & (col < N) ? 4u * ((unsigned)row * (unsigned)p.ldc + (unsigned)col) : OOB;
+          c_old[i] = vecNB{};
         }
-        if constexpr (S::EPI) {
-          // Fused epilogue on the FP32 accumulators (the old C is read only
-          // when beta != 0).
-          vecNB c_old = {}, bias = {};
-          if (p.epi.beta != 0.f) c_old = *reinterpret_cast<const vecNB*>(dst);
-          if (p.epi.bias) bias = *reinterpret_cast<const vecNB*>(p.epi.bias + col);
+        if (p.epi.beta != 0.f) {
+#pragma unroll
+          for (int i = 0; i < BATCH; ++i) c_old[i] = load(off[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < BATCH; ++i) {
+          vecNB v = acc_vec(mb, r0 + i);
           if constexpr (NB == 1) {
-            v = epi_value(p.epi, v, c_old, bias);
+            v = epi_value(p.epi, v, c_old[i], bias);
           } else {
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) v[nb] = epi_value(p.epi, v[nb], c_old[nb], bias[nb]);
+            for (int nb = 0; nb < NB; ++nb) v[nb] = epi_value(p.epi, v[nb], c_old[i][nb], bias[nb]);
           }
+          store(v, off[i]);
         }
-        *reinterpret_cast<vecNB*>(dst) = v;
       }
-    }
+  }
 }
 
 template <class S>
@@ -375,7 +418,8 @@ hipError_t launch(const Params& p, const TileMap& map, bool vec, hipStream_t str
   const int64_t lim = 0x7fffffff;
   // Every offset (rows past M and K included) must fit the 31-bit range.
   if (!vec || (int64_t)(p.M + S::BM) * p.lda * 4 > lim || (int64_t)(S::BK + 2) * p.ldb * 4 > lim ||
-      ((int64_t)(p.K > 0 ? p.K - 1 : 0) * p.ldb + p.N) * 4 > lim) {
+      ((int64_t)(p.K > 0 ? p.K - 1 : 0) * p.ldb + p.N) * 4 > lim ||
+      (S::EPI && (int64_t)p.M * p.ldc * 4 > lim)) {
     // The general kernel has no split-K form: the caller runs unsplit.
     if (p.splits > 1) return hipErrorNotSupported;
     return sgemm_launch_shape(S::BM, S::BN, S::WM, S::WN, p, map, vec, stream);
