@@ -65,6 +65,10 @@ def _declare(lib):
         fn = getattr(lib, name)
         fn.argtypes = [i64, p, i64, p, i64, p, p, i64, p, p]
         fn.restype = ctypes.c_int
+    for name in ("oracle_gemm_rows_bt_f32", "oracle_gemm_rows_bt_f16"):
+        fn = getattr(lib, name)
+        fn.argtypes = [i64, i64, i64, p, i64, p, i64, p, p, i64, p, i64]
+        fn.restype = ctypes.c_int
     for name in ("oracle_epilogue_rows_f32", "oracle_epilogue_rows_f16"):
         fn = getattr(lib, name)
         fn.argtypes = [i64, i64, ctypes.c_double, ctypes.c_double, p, i64, p, ctypes.c_int, p,
@@ -166,6 +170,42 @@ def gemm_rows(A: np.ndarray, B: np.ndarray, rows=None, threads: int | None = Non
             int(threads or default_threads()))
     if rc != 0:
         raise RuntimeError(f"oracle_gemm_rows failed with code {rc}")
+    return C, D
+
+
+def gemm_rows_bt(A: np.ndarray, Bt: np.ndarray, rows=None, lib=None):
+    """C_ref and D (float64) for C = A @ Bt.T, B given transposed: Bt is
+    N x K.  Single-threaded (test sizes only)."""
+    lib = lib or load()
+    kind = _kind(A)
+    if _kind(Bt) != kind:
+        raise TypeError("A and Bt must have the same element type")
+    dt = np.float32 if kind == "f32" else np.uint16
+    if kind == "f16":
+        A, Bt = _bits16(A), _bits16(Bt)
+    A, lda = _as_matrix(A, dt)
+    Bt, ldbt = _as_matrix(Bt, dt)
+    M, K = A.shape
+    N, K2 = Bt.shape
+    if K2 != K:
+        raise ValueError(f"inner dimensions differ: {K} vs {K2}")
+    if rows is None:
+        nrows, rows_arr, rp = M, None, None
+    else:
+        rows_arr = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        if rows_arr.size and (rows_arr.min() < 0 or rows_arr.max() >= M):
+            raise IndexError("row index out of range")
+        nrows, rp = rows_arr.size, _ptr(rows_arr)
+    C = np.zeros((nrows, N), dtype=np.float64)
+    D = np.zeros((nrows, N), dtype=np.float64)
+    if nrows == 0 or N == 0:
+        return C, D
+    fn = lib.oracle_gemm_rows_bt_f32 if kind == "f32" else lib.oracle_gemm_rows_bt_f16
+    a_ptr = _ptr(A) if A.size else _ptr(np.zeros(1, dt))
+    b_ptr = _ptr(Bt) if Bt.size else _ptr(np.zeros(1, dt))
+    rc = fn(nrows, N, K, a_ptr, lda, b_ptr, ldbt, rp, _ptr(C), N, _ptr(D), N)
+    if rc != 0:
+        raise RuntimeError(f"oracle_gemm_rows_bt failed with code {rc}")
     return C, D
 
 

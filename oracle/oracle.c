@@ -200,6 +200,70 @@ int oracle_gemm_rows_f16(int64_t nrows, int64_t N, int64_t K,
 }
 
 /*
+ * Rows of C_ref and D for B given transposed: Bt is the N x K row-major
+ * matrix with Bt[j][k] = B[k][j] (B column-major, the layout of the
+ * baseline kernel in the lqnn.cn SGEMM article, section 3.1), so
+ *   C_ref[i][j] = sum_k A[i][k] * Bt[j][k],  D[i][j] = sum_k |A[i][k]| |Bt[j][k]|
+ * with the same i-k-j order (k ascending) as oracle_gemm_rows_*.
+ */
+static void *rows_worker_bt(void *arg)
+{
+    const rows_job *jb = (const rows_job *)arg;
+    for (int64_t t = jb->r_begin; t < jb->r_end; ++t) {
+        const int64_t i = jb->rows ? jb->rows[t] : t;
+        double *acc = jb->C + t * jb->ldr;
+        double *den = jb->D + t * jb->ldd;
+        for (int64_t j = 0; j < jb->N; ++j) {
+            acc[j] = 0.0;
+            den[j] = 0.0;
+        }
+        for (int64_t k = 0; k < jb->K; ++k) {
+            const double a = load_elem(jb->A, jb->dtype, i * jb->lda + k);
+            for (int64_t j = 0; j < jb->N; ++j) {
+                const double bt = load_elem(jb->B, jb->dtype, j * jb->ldb + k);
+                acc[j] += a * bt;
+                den[j] += fabs(a) * fabs(bt);
+            }
+        }
+    }
+    return NULL;
+}
+
+static int run_rows_bt(int dtype, int64_t nrows, int64_t N, int64_t K, const void *A, int64_t lda,
+                       const void *Bt, int64_t ldbt, const int64_t *rows, double *C, int64_t ldr,
+                       double *D, int64_t ldd)
+{
+    if (nrows < 0 || N < 0 || K < 0 || ldr < N || ldd < N)
+        return -1;
+    rows_job jb;
+    jb.dtype = dtype;
+    jb.N = N; jb.K = K;
+    jb.A = A; jb.lda = lda;
+    jb.B = Bt; jb.ldb = ldbt;
+    jb.rows = rows;
+    jb.r_begin = 0;
+    jb.r_end = nrows;
+    jb.C = C; jb.ldr = ldr;
+    jb.D = D; jb.ldd = ldd;
+    rows_worker_bt(&jb);
+    return 0;
+}
+
+int oracle_gemm_rows_bt_f32(int64_t nrows, int64_t N, int64_t K, const float *A, int64_t lda,
+                            const float *Bt, int64_t ldbt, const int64_t *rows, double *C,
+                            int64_t ldr, double *D, int64_t ldd)
+{
+    return run_rows_bt(ORACLE_F32, nrows, N, K, A, lda, Bt, ldbt, rows, C, ldr, D, ldd);
+}
+
+int oracle_gemm_rows_bt_f16(int64_t nrows, int64_t N, int64_t K, const uint16_t *A, int64_t lda,
+                            const uint16_t *Bt, int64_t ldbt, const int64_t *rows, double *C,
+                            int64_t ldr, double *D, int64_t ldd)
+{
+    return run_rows_bt(ORACLE_F16, nrows, N, K, A, lda, Bt, ldbt, rows, C, ldr, D, ldd);
+}
+
+/*
  * Fused epilogue, applied to rows of C_ref and D produced by
  * oracle_gemm_rows_* (in place):
  *   C[t][j] <- act(alpha * C[t][j] + beta * C0[i][j] + bias[j])

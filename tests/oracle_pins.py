@@ -304,10 +304,57 @@ def pin_epilogue_bruteforce(lib, trials: int = 30):
                         Fraction(U64) * Fraction(D[i, j]), "epilogue brute force"
 
 
+# --------------------------------------------------------------------------
+# B given transposed (column-major B): C = A @ Bt^T.
+# --------------------------------------------------------------------------
+def pin_bt_identity_permutation(lib):
+    """Bt = I gives C = A; Bt = P (a permutation) gives C = A P^T, i.e.
+    column j of C is column p[j] of A; both exact."""
+    for dt in _dtypes():
+        A = _rand(dt, 51, 0, 7, 9)
+        C, _ = oracle.gemm_rows_bt(A, np.eye(9, dtype=dt), lib=lib)
+        assert np.array_equal(C, A.astype(np.float64)), "Bt = I"
+        perm = synth.permutation(51, 2, 9)
+        P = np.zeros((9, 9), dtype=dt)
+        P[np.arange(9), perm] = 1
+        C, _ = oracle.gemm_rows_bt(A, P, lib=lib)
+        assert np.array_equal(C, A.astype(np.float64)[:, perm]), "Bt = P"
+
+
+def pin_bt_matches_plain_transpose(lib):
+    """The transposed-B product of Bt equals the plain product of the
+    materialised transpose B = Bt^T bit for bit (same k order), also with
+    padded leading dimensions and a row subset."""
+    for dt in _dtypes():
+        A, Bt = _rand(dt, 52, 0, 11, 37), _rand(dt, 52, 1, 13, 37)
+        C, D = oracle.gemm_rows_bt(A, _padded(Bt, 3), rows=[10, 0, 4], lib=lib)
+        Cp, Dp = oracle.gemm_rows(A, np.ascontiguousarray(Bt.T), rows=[10, 0, 4], lib=lib)
+        assert np.array_equal(C, Cp) and np.array_equal(D, Dp), "Bt vs plain transpose"
+
+
+def pin_bt_rank1(lib):
+    """A with only column c nonzero and Bt with only column c nonzero:
+    C = u v^T exactly; a different column in Bt gives 0."""
+    for dt in _dtypes():
+        M, N, K = 5, 6, 8
+        u = synth.small_int(53, 0, M, 1, -3, 3).ravel()
+        v = synth.small_int(53, 1, N, 1, -3, 3).ravel()
+        A, Bt = np.zeros((M, K), dtype=dt), np.zeros((N, K), dtype=dt)
+        A[:, 2] = u
+        Bt[:, 2] = v
+        C, _ = oracle.gemm_rows_bt(A, Bt, lib=lib)
+        assert np.array_equal(C, np.outer(u, v)), "rank-1 Bt"
+        Bt2 = np.zeros((N, K), dtype=dt)
+        Bt2[:, 3] = v
+        C2, _ = oracle.gemm_rows_bt(A, Bt2, lib=lib)
+        assert not np.any(C2), "mismatched k"
+
+
 PINS = [pin_identity, pin_permutation, pin_all_ones, pin_rank1, pin_k0_k1,
         pin_bruteforce_fractions, pin_numpy_matmul, pin_f16_decode,
         pin_error_metric, pin_epilogue_closed_form, pin_epilogue_reduces_to_plain,
-        pin_epilogue_bruteforce]
+        pin_epilogue_bruteforce, pin_bt_identity_permutation, pin_bt_matches_plain_transpose,
+        pin_bt_rank1]
 
 
 def run_all(lib) -> list[str]:

@@ -44,6 +44,12 @@ MUTANTS = {
     "metric_zero_den_hidden": ("r = (diff == 0.0) ? 0.0 : INFINITY;", "r = 0.0;"),
     "metric_nan_ignored": ("++n_nonfinite;\n                r = INFINITY;",
                            "r = 0.0;"),
+    "bt_index_swapped": ("const double bt = load_elem(jb->B, jb->dtype, j * jb->ldb + k);",
+                         "const double bt = load_elem(jb->B, jb->dtype, k * jb->ldb + j);"),
+    "bt_ignores_ld": ("const double bt = load_elem(jb->B, jb->dtype, j * jb->ldb + k);",
+                      "const double bt = load_elem(jb->B, jb->dtype, j * jb->K + k);"),
+    "bt_drops_last_k": ("        for (int64_t k = 0; k < jb->K; ++k) {\n            const double a = load_elem(jb->A, jb->dtype, i * jb->lda + k);\n            for (int64_t j = 0; j < jb->N; ++j) {\n                const double bt",
+                        "        for (int64_t k = 0; k + 1 < jb->K; ++k) {\n            const double a = load_elem(jb->A, jb->dtype, i * jb->lda + k);\n            for (int64_t j = 0; j < jb->N; ++j) {\n                const double bt"),
     "epi_drop_beta": ("                v += c0;\n", "\n"),
     "epi_bias_by_row": ("v += (double)bias[j];", "v += (double)bias[i % N];"),
     "epi_c0_by_slot": ("load_elem(C0, dtype, i * ldc0 + j)", "load_elem(C0, dtype, t * ldc0 + j)"),
