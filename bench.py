@@ -48,6 +48,9 @@ def parse_args():
     ap.add_argument("--epilogue", action="store_true",
                     help="time the fused-epilogue entry points instead: C = relu(A x B + C + bias) "
                          "(alpha 1, beta 1: the old C is read)")
+    ap.add_argument("--bt", action="store_true",
+                    help="time the transposed-B entry points instead: B held as its N x K "
+                         "transpose (column-major B)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="before the steps, run a plain device copy of this many MiB (read N, "
                          "write N) three times: the reference kernel that scales HBM counters")
@@ -127,8 +130,13 @@ def main():
     gen_s = time.time() - t0
     tdt = {"f32": torch.float32, "f16": torch.float16}
     devbuf = {}
+    if args.bt and args.epilogue:
+        print("--bt and --epilogue are separate modes", file=sys.stderr)
+        sys.exit(2)
     for k in kinds:
         A, B = host[k]
+        if args.bt:
+            B = np.ascontiguousarray(B.T)
         devbuf[k] = (torch.from_numpy(A).to(dev), torch.from_numpy(B).to(dev),
                      torch.empty((n, n), dtype=tdt[k], device=dev))
     cfgs = {}
@@ -159,6 +167,9 @@ def main():
         if epi is not None:
             fn = gemm.gemm_f32_epi if k == "f32" else gemm.gemm_f16_epi
             st = fn(n, n, n, a.data_ptr(), n, b.data_ptr(), n, c.data_ptr(), n, sptr, cfgs[k], epi)
+        elif args.bt:
+            fn = gemm.gemm_f32_bt if k == "f32" else gemm.gemm_f16_bt
+            st = fn(n, n, n, a.data_ptr(), n, b.data_ptr(), n, c.data_ptr(), n, sptr, cfgs[k])
         else:
             fn = gemm.gemm_f32_ex if k == "f32" else gemm.gemm_f16_ex
             st = fn(n, n, n, a.data_ptr(), n, b.data_ptr(), n, c.data_ptr(), n, sptr, cfgs[k])
@@ -203,6 +214,13 @@ def main():
                 rep = oracle.check(np.ascontiguousarray(C[rows]), ref, den,
                                    oracle.SGEMM_TOL if k == "f32" else oracle.HGEMM_TOL)
                 parity[k] = {"rows": len(rows), "entries": 0, "tol": rep["tol"],
+                             "max_rel": rep["max_rel"], "ok": rep["ok"]}
+                continue
+            tol = oracle.SGEMM_TOL if k == "f32" else oracle.HGEMM_TOL
+            if args.bt:
+                ref, den = oracle.gemm_rows_bt(A, np.ascontiguousarray(B.T), rows=rows)
+                rep = oracle.check(np.ascontiguousarray(C[rows]), ref, den, tol)
+                parity[k] = {"rows": len(rows), "entries": 0, "tol": tol,
                              "max_rel": rep["max_rel"], "ok": rep["ok"]}
                 continue
             ref, den = oracle.gemm_rows(A, B, rows=rows, threads=min(args.cpu_threads, 16))
@@ -258,7 +276,7 @@ def main():
         kk = kernels[k]
         achieved = flops / (kk["ms_mean"] * 1e-3) / 1e12
         # The counters were taken on the plain kernels.
-        traffic = None if epi is not None else load_traffic(kk["variant"], n)
+        traffic = None if epi is not None or args.bt else load_traffic(kk["variant"], n)
         return {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS[k],
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS[k], 4),
                 "traffic": traffic, "traffic_unit": "bytes/launch", "kernel": kk["variant"],
@@ -306,7 +324,8 @@ def main():
         "dtype": "+".join(kinds),
         "data": "synthetic",
         "config": {"workload": f"sgemm+hgemm {n}x{n}x{n} row-major, uniform[-1,1) seed 0"
-                               + (", fused epilogue relu(AB + C + bias)" if epi is not None else ""),
+                               + (", fused epilogue relu(AB + C + bias)" if epi is not None else "")
+                               + (", B given transposed (N x K)" if args.bt else ""),
                    "M": n, "N": n, "K": n, "step": " then ".join(
                        "SGEMM fp32" if k == "f32" else "HGEMM fp16-in fp32-acc fp16-out" for k in kinds)},
         "kernels": kernels,

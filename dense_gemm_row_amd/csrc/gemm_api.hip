@@ -141,13 +141,15 @@ double gemm_seconds(int dtype, const Variant& v, int64_t M, int64_t N, int64_t K
   return (double)rounds * 2.0 * d.bm * d.bn * (double)(Kc > 0 ? Kc : 1) * w / (eff * rate);
 }
 
-Choice heuristic(int dtype, int64_t M, int64_t N, int64_t K, bool allow_split, bool need_epi = false) {
+Choice heuristic(int dtype, int64_t M, int64_t N, int64_t K, bool allow_split, bool need_epi = false,
+                 bool need_bt = false) {
   const auto& v = table().v[dtype];
   const double es = dtype == GEMM_DTYPE_F32 ? 4.0 : 2.0;
   Choice best;
   for (size_t i = 0; i < v.size(); ++i) {
     if (v[i].desc.family != GEMM_FAMILY_MFMA) continue;
     if (need_epi && !v[i].launch_epi) continue;
+    if (need_bt && !v[i].launch_bt) continue;
     const double t1 = gemm_seconds(dtype, v[i], M, N, K, 1);
     if (t1 < best.t) best = Choice{(int)i, 1, t1};
     if (!allow_split || !v[i].launch_partial || M == 0 || N == 0) continue;
@@ -167,12 +169,12 @@ Choice heuristic(int dtype, int64_t M, int64_t N, int64_t K, bool allow_split, b
 
 // Plain calls (split = false) never split; split-K calls may.
 gemm_config_t select(int dtype, int64_t M, int64_t N, int64_t K, bool split = false,
-                     bool need_epi = false) {
+                     bool need_epi = false, bool need_bt = false) {
   {
     std::lock_guard<std::mutex> lk(g_tuning_mu);
     for (const auto& e : g_tuning)
       if (e.dtype == dtype && e.M == M && e.N == N && e.K == K && (split || e.splits <= 1) &&
-          (!need_epi || table().v[dtype][e.id].launch_epi)) {
+          (!need_epi || table().v[dtype][e.id].launch_epi) && !need_bt) {
         gemm_config_t d = table().v[dtype][e.id].desc;
         d.order = e.order;
         d.group_m = e.group_m;
@@ -180,7 +182,7 @@ gemm_config_t select(int dtype, int64_t M, int64_t N, int64_t K, bool split = fa
         return d;
       }
   }
-  const Choice c = heuristic(dtype, M, N, K, split, need_epi);
+  const Choice c = heuristic(dtype, M, N, K, split, need_epi, need_bt);
   gemm_config_t d = table().v[dtype][c.id].desc;
   d.splits = (int32_t)c.splits;
   return d;
@@ -207,13 +209,15 @@ size_t span_bytes(int64_t rows, int64_t cols, int64_t ld, size_t es) {
   return ((size_t)(rows - 1) * (size_t)ld + (size_t)cols) * es;
 }
 
+// bt: B is given transposed (Bt, N x K row-major, leading dimension ldb).
 gemm_status_t validate(int dtype, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
-                       const void* B, int64_t ldb, const void* C, int64_t ldc) {
+                       const void* B, int64_t ldb, const void* C, int64_t ldc, bool bt = false) {
   if (M < 0 || N < 0 || K < 0) return fail(GEMM_ERR_INVALID_ARG, "negative dimension");
   const int64_t lim = 0x7fffffff;
   if (M > lim || N > lim || K > lim) return fail(GEMM_ERR_INVALID_ARG, "dimension above 2^31-1");
   if (lda < (K > 1 ? K : 1)) return fail(GEMM_ERR_INVALID_ARG, "lda < max(1, K)");
-  if (ldb < (N > 1 ? N : 1)) return fail(GEMM_ERR_INVALID_ARG, "ldb < max(1, N)");
+  if (!bt && ldb < (N > 1 ? N : 1)) return fail(GEMM_ERR_INVALID_ARG, "ldb < max(1, N)");
+  if (bt && ldb < (K > 1 ? K : 1)) return fail(GEMM_ERR_INVALID_ARG, "ldbt < max(1, K)");
   if (ldc < (N > 1 ? N : 1)) return fail(GEMM_ERR_INVALID_ARG, "ldc < max(1, N)");
   if (M > 0 && K > 0 && !A) return fail(GEMM_ERR_INVALID_ARG, "A is NULL");
   if (K > 0 && N > 0 && !B) return fail(GEMM_ERR_INVALID_ARG, "B is NULL");
@@ -222,7 +226,8 @@ gemm_status_t validate(int dtype, int64_t M, int64_t N, int64_t K, const void* A
   if (cdiv(M, 64) * cdiv(N, 64) > tiles_lim) return fail(GEMM_ERR_INVALID_ARG, "output too large");
   const size_t es = dtype == GEMM_DTYPE_F32 ? 4 : 2;
   const size_t cb = span_bytes(M, N, ldc, es);
-  if (overlap(C, cb, A, span_bytes(M, K, lda, es)) || overlap(C, cb, B, span_bytes(K, N, ldb, es)))
+  if (overlap(C, cb, A, span_bytes(M, K, lda, es)) ||
+      overlap(C, cb, B, bt ? span_bytes(N, K, ldb, es) : span_bytes(K, N, ldb, es)))
     return fail(GEMM_ERR_ALIAS, "C overlaps A or B");
   return GEMM_OK;
 }
@@ -232,10 +237,10 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 // Resolves the configuration of a call: the forced one (checked), or the
 // selection for the shape.
 gemm_status_t resolve(int dtype, int64_t M, int64_t N, int64_t K, const gemm_config_t* forced,
-                      bool split, gemm_config_t& cfg, bool need_epi = false) {
+                      bool split, gemm_config_t& cfg, bool need_epi = false, bool need_bt = false) {
   const auto& v = table().v[dtype];
   if (!forced) {
-    cfg = select(dtype, M, N, K, split, need_epi);
+    cfg = select(dtype, M, N, K, split, need_epi, need_bt);
     return GEMM_OK;
   }
   if (forced->id < 0 || forced->id >= (int32_t)v.size())
@@ -247,6 +252,8 @@ gemm_status_t resolve(int dtype, int64_t M, int64_t N, int64_t K, const gemm_con
   if (split && forced->splits < 0) return fail(GEMM_ERR_UNSUPPORTED, "negative splits");
   if (need_epi && !v[forced->id].launch_epi)
     return fail(GEMM_ERR_UNSUPPORTED, "variant %s has no fused-epilogue form", v[forced->id].desc.name);
+  if (need_bt && !v[forced->id].launch_bt)
+    return fail(GEMM_ERR_UNSUPPORTED, "variant %s has no transposed-B form", v[forced->id].desc.name);
   cfg = v[forced->id].desc;
   cfg.order = forced->order;
   cfg.group_m = forced->group_m;
@@ -316,6 +323,26 @@ gemm_status_t run(int dtype, int64_t M, int64_t N, int64_t K, const void* A, int
   if (st != GEMM_OK) return st;
   if (M == 0 || N == 0) return GEMM_OK;
   return launch_plain(dtype, cfg, M, N, K, A, lda, B, ldb, C, ldc, stream);
+}
+
+gemm_status_t run_bt(int dtype, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                     const void* Bt, int64_t ldbt, void* C, int64_t ldc, void* stream,
+                     const gemm_config_t* forced) {
+  g_err[0] = 0;
+  gemm_status_t st = validate(dtype, M, N, K, A, lda, Bt, ldbt, C, ldc, true);
+  if (st != GEMM_OK) return st;
+  gemm_config_t cfg;
+  st = resolve(dtype, M, N, K, forced, false, cfg, false, true);
+  if (st != GEMM_OK) return st;
+  if (M == 0 || N == 0) return GEMM_OK;
+  Params p = make_params(A, lda, Bt, ldbt, C, ldc, M, N, K);
+  p.bt = true;
+  const bool vec = vector_path(dtype, A, lda, Bt, ldbt, C, ldc, K, N);
+  const TileMap map = make_map(cfg, M, N);
+  const hipError_t e =
+      table().v[dtype][cfg.id].launch_bt(p, map, vec, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(GEMM_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+  return GEMM_OK;
 }
 
 gemm_status_t run_epi(int dtype, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
@@ -422,6 +449,18 @@ gemm_status_t gemm_f16_ex(int64_t M, int64_t N, int64_t K, const gemm_f16_t* A, 
                           void* stream, const gemm_config_t* cfg) {
   if (!cfg) return fail(GEMM_ERR_INVALID_ARG, "cfg is NULL");
   return run(GEMM_DTYPE_F16, M, N, K, A, lda, B, ldb, C, ldc, stream, cfg);
+}
+
+gemm_status_t gemm_f32_bt(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
+                          const float* Bt, int64_t ldbt, float* C, int64_t ldc, void* stream,
+                          const gemm_config_t* cfg) {
+  return run_bt(GEMM_DTYPE_F32, M, N, K, A, lda, Bt, ldbt, C, ldc, stream, cfg);
+}
+
+gemm_status_t gemm_f16_bt(int64_t M, int64_t N, int64_t K, const gemm_f16_t* A, int64_t lda,
+                          const gemm_f16_t* Bt, int64_t ldbt, gemm_f16_t* C, int64_t ldc,
+                          void* stream, const gemm_config_t* cfg) {
+  return run_bt(GEMM_DTYPE_F16, M, N, K, A, lda, Bt, ldbt, C, ldc, stream, cfg);
 }
 
 gemm_status_t gemm_f32_epi(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,

@@ -48,6 +48,10 @@ struct Params {
   int splits = 1, kc = 0;
   int64_t c_stride = 0;
   Epi epi;
+  // B given transposed: B points at Bt (N x K row-major, leading dimension
+  // ldb), i.e. column-major B.  Kernels without such a form ignore it and
+  // must not be launched with it.
+  bool bt = false;
 };
 
 // Workgroup -> output tile order.  See gemm_order_t in gemm.h.
@@ -162,6 +166,9 @@ struct Variant {
   // Launch with the fused epilogue (p.epi.on), or nullptr when the kernel
   // has no such form.
   LaunchFn launch_epi;
+  // Launch with B given transposed (p.bt), or nullptr when the kernel has
+  // no such form.
+  LaunchFn launch_bt;
 };
 
 // Per-family registration (each kernel file defines its table).

@@ -51,12 +51,13 @@ struct Shape {
   static constexpr int B_BLOCKS = (BK / 8) * (BN / 8); // 8x8 blocks
   static constexpr int CA = A_CHUNKS / NT;
   static constexpr int CB = (B_BLOCKS + NT - 1) / NT;
+  static constexpr int CBT = BN * (BK / 8) / NT;  // B given transposed: Bt chunks per thread
   static constexpr int A_STAGE = BM * ROW_BYTES, B_STAGE = BN * ROW_BYTES;  // bytes
   static constexpr int STAGE = A_STAGE + B_STAGE;
   static constexpr int LDS_BYTES = 2 * STAGE;
   static_assert(BM % WM == 0 && BN % WN == 0, "wave grid");
   static_assert(WM % 32 == 0 && (NB == 1 || NB == 2 || NB == 4), "wave tile");
-  static_assert(A_CHUNKS % NT == 0, "A staging split");
+  static_assert(A_CHUNKS % NT == 0 && (BN * (BK / 8)) % NT == 0, "A / Bt staging split");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 
   // A chunk q (8 halves) of tile row r.
@@ -81,7 +82,10 @@ __device__ inline unsigned short f16_bits(float x) {
   return __builtin_bit_cast(unsigned short, static_cast<_Float16>(x));
 }
 
-template <int BM, int BN, int WM, int WN, bool VEC, bool EPI>
+// BT: B given transposed (p.bt: Bt, N x K row-major).  Its rows are already
+// k-contiguous per output column, so they are staged like A's chunks into
+// the transposed B tile (no register transpose).
+template <int BM, int BN, int WM, int WN, bool VEC, bool EPI, bool BT>
 __global__ void __launch_bounds__((Shape<BM, BN, WM, WN>::NT))
 hgemm_mfma_kernel(Params p, TileMap map) {
   using S = Shape<BM, BN, WM, WN>;
@@ -131,8 +135,23 @@ hgemm_mfma_kernel(Params p, TileMap map) {
     b_src[i] = B + (int64_t)(8 * r) * p.ldb + (b_col[i] < N ? b_col[i] : 0);
   }
 
+  // BT staging: Bt chunk (tile column n, k chunk q) per slot.
+  const unsigned short* bt_src[S::CBT];
+  bool bt_ok[S::CBT];
+  int bt_k[S::CBT], bt_dst[S::CBT];
+#pragma unroll
+  for (int i = 0; i < S::CBT; ++i) {
+    const int id = tid + i * NT;
+    const int n = id / (BK / 8), q = id % (BK / 8);
+    bt_ok[i] = (n0 + n) < N;
+    bt_src[i] = B + (int64_t)(bt_ok[i] ? n0 + n : 0) * p.ldb + 8 * q;
+    bt_k[i] = 8 * q;
+    bt_dst[i] = S::b_chunk(n, q);
+  }
+
   u32x4 ra[CA];
   u32x4 rb[CB][8];
+  u32x4 rbt[S::CBT];
 
   auto load_slice = [&](int k0) {
 #pragma unroll
@@ -149,6 +168,24 @@ hgemm_mfma_kernel(Params p, TileMap map) {
 #pragma unroll
         for (int d = 0; d < 4; ++d) ra[i][d] = e[2 * d] | ((unsigned)e[2 * d + 1] << 16);
       }
+    }
+    if constexpr (BT) {
+#pragma unroll
+      for (int i = 0; i < S::CBT; ++i) {
+        const int kg = k0 + bt_k[i];
+        if (VEC) {
+          u32x4 v = {0u, 0u, 0u, 0u};
+          if (bt_ok[i] && kg < K) v = *reinterpret_cast<const u32x4*>(bt_src[i] + k0);
+          rbt[i] = v;
+        } else {
+          unsigned short e[8];
+#pragma unroll
+          for (int t = 0; t < 8; ++t) e[t] = (bt_ok[i] && kg + t < K) ? bt_src[i][k0 + t] : 0;
+#pragma unroll
+          for (int d = 0; d < 4; ++d) rbt[i][d] = e[2 * d] | ((unsigned)e[2 * d + 1] << 16);
+        }
+      }
+      return;
     }
 #pragma unroll
     for (int i = 0; i < CB; ++i) {
@@ -175,6 +212,11 @@ hgemm_mfma_kernel(Params p, TileMap map) {
     unsigned char* base = smem + stage * S::STAGE;
 #pragma unroll
     for (int i = 0; i < CA; ++i) *reinterpret_cast<u32x4*>(base + a_dst[i]) = ra[i];
+    if constexpr (BT) {
+#pragma unroll
+      for (int i = 0; i < S::CBT; ++i) *reinterpret_cast<u32x4*>(base + bt_dst[i]) = rbt[i];
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < CB; ++i) {
       if (!b_on[i]) continue;
@@ -277,16 +319,22 @@ template <int BM, int BN, int WM, int WN>
 hipError_t launch(const Params& p, const TileMap& map, bool vec, hipStream_t stream) {
   using S = Shape<BM, BN, WM, WN>;
   const dim3 grid(map.tiles_m * map.tiles_n), block(S::NT);
-  if (p.epi.on) {
+  if (p.bt) {  // transposed B (the fused epilogue is not combined with it)
+    if (p.epi.on) return hipErrorNotSupported;
     if (vec)
-      hipLaunchKernelGGL((hgemm_mfma_kernel<BM, BN, WM, WN, true, true>), grid, block, 0, stream, p, map);
+      hipLaunchKernelGGL((hgemm_mfma_kernel<BM, BN, WM, WN, true, false, true>), grid, block, 0, stream, p, map);
     else
-      hipLaunchKernelGGL((hgemm_mfma_kernel<BM, BN, WM, WN, false, true>), grid, block, 0, stream, p, map);
+      hipLaunchKernelGGL((hgemm_mfma_kernel<BM, BN, WM, WN, false, false, true>), grid, block, 0, stream, p, map);
+  } else if (p.epi.on) {
+    if (vec)
+      hipLaunchKernelGGL((hgemm_mfma_kernel<BM, BN, WM, WN, true, true, false>), grid, block, 0, stream, p, map);
+    else
+      hipLaunchKernelGGL((hgemm_mfma_kernel<BM, BN, WM, WN, false, true, false>), grid, block, 0, stream, p, map);
   } else {
     if (vec)
-      hipLaunchKernelGGL((hgemm_mfma_kernel<BM, BN, WM, WN, true, false>), grid, block, 0, stream, p, map);
+      hipLaunchKernelGGL((hgemm_mfma_kernel<BM, BN, WM, WN, true, false, false>), grid, block, 0, stream, p, map);
     else
-      hipLaunchKernelGGL((hgemm_mfma_kernel<BM, BN, WM, WN, false, false>), grid, block, 0, stream, p, map);
+      hipLaunchKernelGGL((hgemm_mfma_kernel<BM, BN, WM, WN, false, false, false>), grid, block, 0, stream, p, map);
   }
   return hipGetLastError();
 }
@@ -367,7 +415,7 @@ int layout_check(int banks, int64_t out[2]) {
                   Shape<BM, BN, WM, WN>::NT, 2, Shape<BM, BN, WM, WN>::LDS_BYTES,            \
                   GEMM_ORDER_XCD, 4, 1, "mfma_f16_" #BM "x" #BN "x64_w" #WM "x" #WN},           \
         &launch<BM, BN, WM, WN>, &layout_check<BM, BN, WM, WN>, nullptr, EFF,                \
-        &launch<BM, BN, WM, WN>                                                              \
+        &launch<BM, BN, WM, WN>, &launch<BM, BN, WM, WN>                                     \
   }
 
 const Variant kVariants[] = {

@@ -79,18 +79,21 @@ __device__ __forceinline__ void static_for(F&& f, std::integer_sequence<int, I..
 
 // MODE_: 0 the plain kernel; 1 the split-K form, whose epilogue writes FP32
 // partials; 2 the form with the fused epilogue (alpha, beta, bias,
-// activation).
-template <int BM_, int BN_, int WM_, int WN_, int BK_, int NS_, int MODE_ = 0>
+// activation).  BT_: B is given transposed (Bt, N x K row-major, i.e.
+// column-major B); its tile is then staged and read exactly like A's (one
+// LDS row per output column, k contiguous), with no transpose read.
+template <int BM_, int BN_, int WM_, int WN_, int BK_, int NS_, int MODE_ = 0, bool BT_ = false>
 struct Shape {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BK_, NS = NS_;
-  static constexpr bool PARTIAL = MODE_ == 1, EPI = MODE_ == 2;
+  static constexpr bool PARTIAL = MODE_ == 1, EPI = MODE_ == 2, BT = BT_;
   static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN, NW = WAVES_M * WAVES_N;
   static constexpr int NT = NW * 64;
   static constexpr int MB = WM / 32, NB = WN / 32, KS = BK / 16;
   static constexpr int NMMA_ = MB * NB;  // MFMAs per k step
   static constexpr int A_ROW = BK * 2, A_CPR = A_ROW / 16;  // bytes / chunks per A row
-  static constexpr int B_ROW = BN * 2, B_CPR = B_ROW / 16;  // bytes / chunks per B row
-  static constexpr int A_STAGE = BM * A_ROW, B_STAGE = BK * B_ROW;
+  // B rows: BK rows of BN columns, or (BT) BN rows of BK k values.
+  static constexpr int B_ROW = BT ? BK * 2 : BN * 2, B_CPR = B_ROW / 16;  // bytes / chunks
+  static constexpr int A_STAGE = BM * A_ROW, B_STAGE = BT ? BN * B_ROW : BK * B_ROW;
   static constexpr int LDS_BYTES = NS * (A_STAGE + B_STAGE);
   static constexpr int IA = A_STAGE / 1024 / NW, IB = B_STAGE / 1024 / NW, LPS = IA + IB;
   // With three or more stages a slice's copies are spread over the k steps
@@ -108,7 +111,7 @@ struct Shape {
   static_assert(BM % WM == 0 && BN % WN == 0, "wave grid");
   static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile");
   static_assert(A_STAGE % (1024 * NW) == 0 && B_STAGE % (1024 * NW) == 0, "direct-load split");
-  static_assert(B_CPR >= 16, "B rows of at least 256 bytes (the k%4 chunk XOR)");
+  static_assert(BT || B_CPR >= 16, "B rows of at least 256 bytes (the k%4 chunk XOR)");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
   static_assert((NS - 1) * LPS <= 63, "vmcnt field");
   static_assert(!SPREAD || (LPS % KS == 0 && PP <= NMMA_), "copies split evenly over k steps");
@@ -119,7 +122,8 @@ struct Shape {
   static_assert(P >= 1 && WM % P == 0 && RPA % 32 == 0 && RPA % EPI_RPI == 0 &&
                 RPA * EPI_ROW <= A_STAGE && RPA * EPI_ROW <= B_STAGE, "epilogue staging");
   // Fragment reads use a per-lane base plus immediate offsets (< 64 KB).
-  static_assert((MB - 1) * 32 * A_ROW < 65536 && (BK - 12) * B_ROW < 65536, "immediate offsets");
+  static_assert((MB - 1) * 32 * A_ROW < 65536 && (BK - 12) * B_ROW < 65536 &&
+                (NB - 1) * 32 * B_ROW < 65536, "immediate offsets");
 
   // Byte offsets within one stage array.
   __host__ __device__ static constexpr int a_byte(int r, int q) { return swz_off(r, q, A_ROW); }
@@ -150,6 +154,13 @@ struct Shape {
   __host__ __device__ static constexpr int b_frag(int wn0, int nb, int j, int j2, int l) {
     return b_byte(16 * j + 8 * (l / 32) + 4 * j2 + (l % 16) / 4,
                   wn0 + 32 * nb + 16 * ((l / 16) % 2) + 4 * (l % 4));
+  }
+  // BT: B tile row n (one output column), 16-byte k chunk q, placed and read
+  // with A's maps (B_ROW == A_ROW): lane reads column wn0 + 32nb + l%32,
+  // chunk 2j + l/32 of k step j (the MFMA A operand of C^T directly).
+  __host__ __device__ static constexpr int bt_byte(int n, int q) { return swz_off(n, q, B_ROW); }
+  __host__ __device__ static constexpr int bt_frag(int wn0, int nb, int j, int l) {
+    return bt_byte(wn0 + 32 * nb + l % 32, 2 * j + l / 32);
   }
   // Epilogue staging: 8-byte slot s (columns 4s..4s+3) of local row m of an
   // array, XOR-swizzled by the row so that the 32 rows written by one
@@ -216,12 +227,13 @@ __device__ __forceinline__ void loop_barrier() {
 template <class S, int Q0 = 0, int Q1 = S::LPS>
 __device__ __forceinline__ void issue_slice(const unsigned char* Ab, const unsigned char* Bb,
                                             int64_t a_bytes, int64_t b_bytes, int s, bool live,
-                                            const unsigned* a_vo, const unsigned* b_vo,
+                                            const unsigned* a_vo, const unsigned* b_vo,  // this slice's
                                             unsigned char* lds_a, unsigned char* lds_b, int wave,
                                             int ldb) {
   // Slices past the last one (issued only to keep the wait counts uniform)
   // get empty descriptors: they load zeros without touching memory.
-  const int64_t ka = 2 * (int64_t)s * S::BK, kb = (int64_t)s * S::BK * ldb * 2;
+  const int64_t ka = 2 * (int64_t)s * S::BK;
+  const int64_t kb = S::BT ? ka : (int64_t)s * S::BK * ldb * 2;
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(Ab + ka, live ? a_bytes - ka : 0);
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bb + kb, live ? b_bytes - kb : 0);
   // Copy instructions Q0 .. Q1-1 of the slice: A's IA blocks, then B's IB.
@@ -283,9 +295,10 @@ hgemm_tr_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
   const int kc = p.splits > 1 ? p.kc : p.K;
   const int M = p.M, N = p.N, K = min(kc, p.K - sk * kc);
   const unsigned char* Ab = static_cast<const unsigned char*>(p.A) + 2 * (int64_t)sk * kc;
-  const unsigned char* Bb = static_cast<const unsigned char*>(p.B) + 2 * (int64_t)sk * kc * ldb;
+  const int64_t bshift = S::BT ? 2 * (int64_t)sk * kc : 2 * (int64_t)sk * kc * ldb;
+  const unsigned char* Bb = static_cast<const unsigned char*>(p.B) + bshift;
   a_bytes -= 2 * (int64_t)sk * kc;
-  b_bytes -= 2 * (int64_t)sk * kc * ldb;
+  b_bytes -= bshift;
 
   const int tid = threadIdx.x;
   const int l = tid & 63;
@@ -294,7 +307,7 @@ hgemm_tr_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
   const int T = (K + BK - 1) / BK;
 
   // Direct-load offsets (relative to the slice's descriptor base).
-  unsigned a_vo[IA], a_vo_tail[IA], b_vo[IB];
+  unsigned a_vo[IA], a_vo_tail[IA], b_vo[IB], b_vo_tail[IB];
 #pragma unroll
   for (int i = 0; i < IA; ++i) {
     const int r = S::a_dl_row(i, wave, l), q = S::a_dl_q(i, wave, l);
@@ -304,27 +317,42 @@ hgemm_tr_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
   }
 #pragma unroll
   for (int i = 0; i < IB; ++i) {
-    const int k = S::b_dl_k(i, wave, l), c = S::b_dl_c(i, wave, l);
-    const bool ok = (n0 + 8 * c) < N;
-    b_vo[i] = ok ? 2u * ((unsigned)k * (unsigned)ldb + (unsigned)(n0 + 8 * c)) : OOB;
+    if constexpr (S::BT) {
+      // Bt row n0 + r (output column), k chunk q: A's placement.
+      const int r = S::a_dl_row(i, wave, l), q = S::a_dl_q(i, wave, l);
+      const bool ok = (n0 + r) < N;
+      b_vo[i] = ok ? 2u * ((unsigned)(n0 + r) * (unsigned)ldb + 8u * q) : OOB;
+      b_vo_tail[i] = ((T - 1) * BK + 8 * q < K) ? b_vo[i] : OOB;
+    } else {
+      const int k = S::b_dl_k(i, wave, l), c = S::b_dl_c(i, wave, l);
+      const bool ok = (n0 + 8 * c) < N;
+      b_vo[i] = ok ? 2u * ((unsigned)k * (unsigned)ldb + (unsigned)(n0 + 8 * c)) : OOB;
+      b_vo_tail[i] = b_vo[i];  // rows past K are past the buffer's range
+    }
   }
   // Fragment byte offsets: k step j of A and block nb of B; other blocks
   // and k steps are immediate offsets.
-  int a_fb[KS], b_fb[NB];
+  int a_fb[KS], b_fb[S::BT ? KS : NB];
 #pragma unroll
   for (int j = 0; j < KS; ++j) a_fb[j] = S::a_frag(wm0, 0, j, l);
+  if constexpr (S::BT) {
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) b_fb[nb] = S::b_frag(wn0, nb, 0, 0, l);
+    for (int j = 0; j < KS; ++j) b_fb[j] = S::bt_frag(wn0, 0, j, l);
+  } else {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) b_fb[nb] = S::b_frag(wn0, nb, 0, 0, l);
+  }
 
   auto issue = [&](int s, unsigned char* la, unsigned char* lb) __attribute__((always_inline)) {
-    issue_slice<S>(Ab, Bb, a_bytes, b_bytes, s, s < T, s == T - 1 ? a_vo_tail : a_vo, b_vo, la, lb,
-                   wave, ldb);
+    issue_slice<S>(Ab, Bb, a_bytes, b_bytes, s, s < T, s == T - 1 ? a_vo_tail : a_vo,
+                   s == T - 1 ? b_vo_tail : b_vo, la, lb, wave, ldb);
   };
   // Part j (of KS) of slice s's copies.
   auto issue_part = [&](int s, auto J, unsigned char* la, unsigned char* lb) __attribute__((always_inline)) {
     constexpr int j = decltype(J)::value;
     issue_slice<S, j * S::PP, (j + 1) * S::PP>(Ab, Bb, a_bytes, b_bytes, s, s < T,
-                                               s == T - 1 ? a_vo_tail : a_vo, b_vo, la, lb, wave, ldb);
+                                               s == T - 1 ? a_vo_tail : a_vo,
+                                               s == T - 1 ? b_vo_tail : b_vo, la, lb, wave, ldb);
   };
 
   f16x8 fa[2][MB], fb[2][NB];
@@ -333,12 +361,18 @@ hgemm_tr_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
       fa[buf][mb] = *(const lds_f16x8*)(la + a_fb[j] + mb * 32 * S::A_ROW);
+    if constexpr (S::BT) {
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const unsigned char* b = lb + b_fb[nb] + 16 * j * S::B_ROW;
-      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)b);
-      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(b + 4 * S::B_ROW));
-      fb[buf][nb] = __builtin_bit_cast(f16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      for (int nb = 0; nb < NB; ++nb)
+        fb[buf][nb] = *(const lds_f16x8*)(lb + b_fb[j] + nb * 32 * S::B_ROW);
+    } else {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const unsigned char* b = lb + b_fb[nb] + 16 * j * S::B_ROW;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)b);
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(b + 4 * S::B_ROW));
+        fb[buf][nb] = __builtin_bit_cast(f16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
     }
   };
 
@@ -360,7 +394,7 @@ hgemm_tr_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
   // (The lambdas are forced inline: an out-of-line call would move the
   // accumulators to scratch memory.)
   constexpr int NMMA = MB * NB;     // MFMAs per k step
-  constexpr int NRD = MB + 2 * NB;  // LDS reads per k step
+  constexpr int NRD = MB + (S::BT ? 1 : 2) * NB;  // LDS reads per k step
   // Slice t from stage c: k steps 0..KS-2 with the next step's fragments
   // in flight; wait for slice t+1; barrier; issue slice t+NS into the freed
   // stage c; last k step (registers only) under the first fragment reads of
@@ -574,25 +608,73 @@ hgemm_tr_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
 template <class S>
 hipError_t launch(const Params& p, const TileMap& map, bool vec, hipStream_t stream) {
   const int64_t lim = 0x7fffffff;
-  // Every offset (rows past M and K included) must fit the 31-bit range.
-  if (!vec || (int64_t)(p.M + S::BM) * p.lda * 2 > lim || (int64_t)(S::BK + 2) * p.ldb * 2 > lim ||
-      ((int64_t)(p.K > 0 ? p.K - 1 : 0) * p.ldb + p.N) * 2 > lim || (int64_t)p.M * p.lda * 2 > lim ||
+  // Every offset (rows past M, N and K included) must fit the 31-bit range.
+  const bool b_far = S::BT ? (int64_t)(p.N + S::BN) * p.ldb * 2 > lim
+                           : (int64_t)(S::BK + 2) * p.ldb * 2 > lim ||
+                                 ((int64_t)(p.K > 0 ? p.K - 1 : 0) * p.ldb + p.N) * 2 > lim;
+  if (!vec || (int64_t)(p.M + S::BM) * p.lda * 2 > lim || b_far || (int64_t)p.M * p.lda * 2 > lim ||
       (S::EPI && (int64_t)p.M * p.ldc * 2 > lim)) {
     // The general kernel has no split-K form: the caller runs unsplit.
     if (p.splits > 1) return hipErrorNotSupported;
     return hgemm_launch_shape(S::BM, S::BN, S::WM, S::WN, p, map, vec, stream);
   }
   const int64_t a_bytes = p.K > 0 ? ((int64_t)(p.M - 1) * p.lda + p.K) * 2 : 0;
-  const int64_t b_bytes = p.K > 0 ? ((int64_t)(p.K - 1) * p.ldb + p.N) * 2 : 0;
+  const int64_t b_bytes = p.K <= 0 ? 0
+                          : S::BT ? ((int64_t)(p.N - 1) * p.ldb + p.K) * 2
+                                  : ((int64_t)(p.K - 1) * p.ldb + p.N) * 2;
   const dim3 grid(map.tiles_m * map.tiles_n, p.splits), block(S::NT);
   hipLaunchKernelGGL(hgemm_tr_kernel<S>, grid, block, 0, stream, p, map, a_bytes, b_bytes);
   return hipGetLastError();
 }
 
+// Host replay of the transposed-B form's B side: direct-load placement of
+// Bt rows (A's maps) and the fragment reads, checked for coverage, bounds,
+// the element each lane must see and bank conflicts (added to *rconf).
+// Returns 0 when valid, else a code from 20.
+template <class S>
+int layout_check_bt(int banks, int64_t* rconf) {
+  static_assert(S::BT, "transposed-B shape");
+  static int n_of[S::B_STAGE], k_of[S::B_STAGE];
+  for (int i = 0; i < S::B_STAGE; ++i) n_of[i] = -1;
+  for (int i = 0; i < S::IB; ++i)
+    for (int w = 0; w < S::NW; ++w)
+      for (int l = 0; l < 64; ++l) {
+        const int off = 1024 * (i * S::NW + w) + 16 * l;
+        const int r = S::a_dl_row(i, w, l), q = S::a_dl_q(i, w, l);
+        if (r >= S::BN || q >= S::B_CPR || S::bt_byte(r, q) != off) return 20;
+        for (int e = 0; e < 8; ++e) {
+          if (n_of[off + 2 * e] != -1) return 21;
+          n_of[off + 2 * e] = r;
+          k_of[off + 2 * e] = 8 * q + e;
+        }
+      }
+  for (int i = 0; i < S::B_STAGE; i += 2)
+    if (n_of[i] < 0) return 22;
+  int addr[64];
+  for (int w = 0; w < S::NW; ++w) {
+    const int wn0 = (w % S::WAVES_N) * S::WN;
+    for (int j = 0; j < S::KS; ++j)
+      for (int nb = 0; nb < S::NB; ++nb) {
+        for (int l = 0; l < 64; ++l) {
+          addr[l] = S::bt_frag(wn0, nb, j, l);
+          if (addr[l] < 0 || addr[l] + 16 > S::B_STAGE) return 23;
+          if (addr[l] != S::bt_frag(wn0, 0, j, l) + nb * 32 * S::B_ROW) return 24;
+          // A_op lane l, element e: B[k = 16j + 8(l/32) + e][n = wn0 + 32nb + l%32].
+          for (int e = 0; e < 8; ++e)
+            if (n_of[addr[l] + 2 * e] != wn0 + 32 * nb + l % 32 ||
+                k_of[addr[l] + 2 * e] != 16 * j + 8 * (l / 32) + e)
+              return 25;
+        }
+        *rconf += lds_conflicts(addr, 16, banks);
+      }
+  }
+  return 0;
+}
+
 // Host replay: direct-load placement, fragment reads (including the lane
 // exchange of the transpose read), and epilogue staging, all checked for
 // bounds, for matching the element each lane must see, and for bank
-// conflicts.  Returns 0 when valid.
+// conflicts; then the transposed-B form's B side.  Returns 0 when valid.
 template <class S>
 int layout_check(int banks, int64_t out[2]) {
   constexpr int BM = S::BM, WM = S::WM, WN = S::WN, BK = S::BK;
@@ -737,6 +819,8 @@ int layout_check(int banks, int64_t out[2]) {
       rconf += lds_conflicts(addr, 16, banks);
     }
   }
+  const int rc = layout_check_bt<Shape<S::BM, S::BN, S::WM, S::WN, S::BK, S::NS, 0, true>>(banks, &rconf);
+  if (rc != 0) return rc;
   out[0] = wconf;
   out[1] = rconf;
   return 0;
@@ -750,7 +834,8 @@ int layout_check(int banks, int64_t out[2]) {
                   "tr_f16_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_s" #NS},                  \
         &launch<Shape<BM, BN, WM, WN, BK, NS>>, &layout_check<Shape<BM, BN, WM, WN, BK, NS>>, \
         &launch<Shape<BM, BN, WM, WN, BK, NS, 1>>, EFF,                                     \
-        &launch<Shape<BM, BN, WM, WN, BK, NS, 2>>                                           \
+        &launch<Shape<BM, BN, WM, WN, BK, NS, 2>>,                                          \
+        &launch<Shape<BM, BN, WM, WN, BK, NS, 0, true>>                                     \
   }
 
 const Variant kVariants[] = {

@@ -60,16 +60,21 @@ __device__ __forceinline__ void static_for(F&& f, std::integer_sequence<int, I..
 }
 
 // EPI_: the form with the fused epilogue (alpha, beta, bias, activation).
-template <int BM_, int BN_, int WM_, int WN_, int BK_, int NS_, bool EPI_ = false>
+// BT_: B given transposed (Bt, N x K row-major, i.e. column-major B): its
+// tile is staged like A's, one LDS row per output column with k contiguous,
+// the columns of each wave block de-interleaved (LDS row wn0 + 32nb + j
+// holds column wn0 + NB*j + nb) so that a lane's 16-byte read gives four k
+// steps of its column and 16 lanes read 16 consecutive rows.
+template <int BM_, int BN_, int WM_, int WN_, int BK_, int NS_, bool EPI_ = false, bool BT_ = false>
 struct Shape {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BK_, NS = NS_;
-  static constexpr bool EPI = EPI_;
+  static constexpr bool EPI = EPI_, BT = BT_;
   static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN, NW = WAVES_M * WAVES_N;
   static constexpr int NT = NW * 64;
   static constexpr int MB = WM / 32, NB = WN / 32, KG = BK / 8;  // k groups of 8 per slice
   static constexpr int A_ROW = BK * 4, A_CPR = A_ROW / 16;       // bytes / chunks per A row
-  static constexpr int B_ROW = BN * 4;                           // bytes per B row
-  static constexpr int A_STAGE = BM * A_ROW, B_STAGE = BK * B_ROW;
+  static constexpr int B_ROW = BT ? BK * 4 : BN * 4;             // bytes per B row
+  static constexpr int A_STAGE = BM * A_ROW, B_STAGE = BT ? BN * B_ROW : BK * B_ROW;
   static constexpr int LDS_BYTES = NS * (A_STAGE + B_STAGE);
   static constexpr int IA = A_STAGE / 1024 / NW, IB = B_STAGE / 1024 / NW, LPS = IA + IB;
   static_assert(BK == 16 || BK == 32, "K slice");
@@ -79,6 +84,7 @@ struct Shape {
   static_assert(WM % 32 == 0 && (NB == 1 || NB == 2 || NB == 4), "wave tile");
   static_assert(A_STAGE % (1024 * NW) == 0 && B_STAGE % (1024 * NW) == 0, "direct-load split");
   static_assert(B_ROW % 1024 == 0 || 1024 % B_ROW == 0, "B rows tile the 1 KB blocks");
+  static_assert(!BT || (NB - 1) * 32 * B_ROW < 65536, "immediate offsets (BT)");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
   static_assert((NS - 1) * LPS <= 63, "vmcnt field");
   static_assert((MB - 1) * 32 * A_ROW < 65536 && BK * B_ROW < 65536, "immediate offsets");
@@ -108,6 +114,16 @@ struct Shape {
   //  B: lane reads row 8g + 4h + s, the NB columns wn0 + NB*(l%32) + nb.
   __host__ __device__ static constexpr int b_frag(int wn0, int g, int s, int l) {
     return b_byte(8 * g + 4 * (l / 32) + s, wn0 + NB * (l % 32));
+  }
+  // BT: tile column held by LDS row R, the LDS placement of (row R, k
+  // chunk q), and the fragment read of block nb in k group g: LDS row
+  // wn0 + 32nb + l%32 (column wn0 + NB*(l%32) + nb), chunk 2g + l/32.
+  __host__ __device__ static constexpr int bt_col(int R) {
+    return (R / WN) * WN + NB * (R % 32) + (R % WN) / 32;
+  }
+  __host__ __device__ static constexpr int bt_byte(int R, int q) { return swz_off(R, q, B_ROW); }
+  __host__ __device__ static constexpr int bt_frag(int wn0, int nb, int g, int l) {
+    return bt_byte(wn0 + 32 * nb + l % 32, 2 * g + l / 32);
   }
 };
 
@@ -157,7 +173,8 @@ __device__ __forceinline__ void issue_slice(const unsigned char* Ab, const unsig
                                             const unsigned* a_vo, const unsigned* b_vo,
                                             unsigned char* lds_a, unsigned char* lds_b, int wave,
                                             int ldb) {
-  const int64_t ka = 4 * (int64_t)s * S::BK, kb = (int64_t)s * S::BK * ldb * 4;
+  const int64_t ka = 4 * (int64_t)s * S::BK;
+  const int64_t kb = S::BT ? ka : (int64_t)s * S::BK * ldb * 4;
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(Ab + ka, live ? a_bytes - ka : 0);
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bb + kb, live ? b_bytes - kb : 0);
 #pragma unroll
@@ -211,9 +228,10 @@ sgemm_dl_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
   const int kc = p.splits > 1 ? p.kc : p.K;
   const int M = p.M, N = p.N, K = min(kc, p.K - sk * kc);
   const unsigned char* Ab = static_cast<const unsigned char*>(p.A) + 4 * (int64_t)sk * kc;
-  const unsigned char* Bb = static_cast<const unsigned char*>(p.B) + 4 * (int64_t)sk * kc * ldb;
+  const int64_t bshift = S::BT ? 4 * (int64_t)sk * kc : 4 * (int64_t)sk * kc * ldb;
+  const unsigned char* Bb = static_cast<const unsigned char*>(p.B) + bshift;
   a_bytes -= 4 * (int64_t)sk * kc;
-  b_bytes -= 4 * (int64_t)sk * kc * ldb;
+  b_bytes -= bshift;
 
   const int tid = threadIdx.x;
   const int l = tid & 63;
@@ -222,7 +240,7 @@ sgemm_dl_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
   const int T = (K + BK - 1) / BK;
 
   // Direct-load offsets (relative to the slice's descriptor base).
-  unsigned a_vo[IA], a_vo_tail[IA], b_vo[IB];
+  unsigned a_vo[IA], a_vo_tail[IA], b_vo[IB], b_vo_tail[IB];
 #pragma unroll
   for (int i = 0; i < IA; ++i) {
     const int r = S::a_dl_row(i, wave, l), q = S::a_dl_q(i, wave, l);
@@ -232,20 +250,32 @@ sgemm_dl_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
   }
 #pragma unroll
   for (int i = 0; i < IB; ++i) {
-    const int k = S::b_dl_k(i, wave, l), c = S::b_dl_c(i, wave, l);
-    const bool ok = (n0 + 4 * c) < N;
-    b_vo[i] = ok ? 4u * ((unsigned)k * (unsigned)ldb + (unsigned)(n0 + 4 * c)) : OOB;
+    if constexpr (S::BT) {
+      // LDS row R holds Bt row n0 + bt_col(R); k chunk q as for A.
+      const int R = S::a_dl_row(i, wave, l), q = S::a_dl_q(i, wave, l);
+      const int n = n0 + S::bt_col(R);
+      b_vo[i] = n < N ? 4u * ((unsigned)n * (unsigned)ldb + 4u * q) : OOB;
+      b_vo_tail[i] = ((T - 1) * BK + 4 * q < K) ? b_vo[i] : OOB;
+    } else {
+      const int k = S::b_dl_k(i, wave, l), c = S::b_dl_c(i, wave, l);
+      const bool ok = (n0 + 4 * c) < N;
+      b_vo[i] = ok ? 4u * ((unsigned)k * (unsigned)ldb + (unsigned)(n0 + 4 * c)) : OOB;
+      b_vo_tail[i] = b_vo[i];  // rows past K are past the buffer's range
+    }
   }
   // Fragment byte offsets: group g of A (other row blocks are immediate
   // offsets), and group 0 step 0 of B (other steps and groups likewise).
   int a_fb[KG];
 #pragma unroll
   for (int g = 0; g < KG; ++g) a_fb[g] = S::a_frag(wm0, 0, g, l);
-  const int b_fb = S::b_frag(wn0, 0, 0, l);
+  const int b_fb = S::BT ? 0 : S::b_frag(wn0, 0, 0, l);
+  int bt_fb[KG];
+#pragma unroll
+  for (int g = 0; g < KG; ++g) bt_fb[g] = S::BT ? S::bt_frag(wn0, 0, g, l) : 0;
 
   auto issue = [&](int s, unsigned char* la, unsigned char* lb) __attribute__((always_inline)) {
-    issue_slice<S>(Ab, Bb, a_bytes, b_bytes, s, s < T, s == T - 1 ? a_vo_tail : a_vo, b_vo, la, lb,
-                   wave, ldb);
+    issue_slice<S>(Ab, Bb, a_bytes, b_bytes, s, s < T, s == T - 1 ? a_vo_tail : a_vo,
+                   s == T - 1 ? b_vo_tail : b_vo, la, lb, wave, ldb);
   };
 
   f32x4 fa[2][MB];
@@ -255,9 +285,22 @@ sgemm_dl_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
       fa[buf][mb] = *(const lds_f32x4*)(la + a_fb[g] + mb * 32 * S::A_ROW);
+    if constexpr (S::BT) {
+      // One 16-byte read per block nb: its column's values for steps 0..3.
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
-      fb[buf][s] = *(const lds_vecNB*)(lb + b_fb + (8 * g + s) * S::B_ROW);
+      for (int nb = 0; nb < NB; ++nb) {
+        const f32x4 t = *(const lds_f32x4*)(lb + bt_fb[g] + nb * 32 * S::B_ROW);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          if constexpr (NB == 1) fb[buf][s] = t[s];
+          else fb[buf][s][nb] = t[s];
+        }
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        fb[buf][s] = *(const lds_vecNB*)(lb + b_fb + (8 * g + s) * S::B_ROW);
+    }
   };
 
   f32x16 acc[MB][NB];
@@ -281,7 +324,7 @@ sgemm_dl_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
   };
 
   constexpr int NMMA = 4 * MB * NB;  // MFMAs per k group
-  constexpr int NRD = MB + 4;        // LDS reads per k group
+  constexpr int NRD = MB + (S::BT ? NB : 4);  // LDS reads per k group
   // (The lambdas are forced inline: a slice of the larger tiles is several
   // hundred MFMAs, past the inliner's budget, and an out-of-line call would
   // move the accumulators to scratch memory.)
@@ -418,17 +461,64 @@ hipError_t launch(const Params& p, const TileMap& map, bool vec, hipStream_t str
   const int64_t lim = 0x7fffffff;
   // Every offset (rows past M and K included) must fit the 31-bit range.
   if (!vec || (int64_t)(p.M + S::BM) * p.lda * 4 > lim || (int64_t)(S::BK + 2) * p.ldb * 4 > lim ||
-      ((int64_t)(p.K > 0 ? p.K - 1 : 0) * p.ldb + p.N) * 4 > lim ||
+      (S::BT ? (int64_t)(p.N + S::BN) * p.ldb * 4 > lim
+             : ((int64_t)(p.K > 0 ? p.K - 1 : 0) * p.ldb + p.N) * 4 > lim) ||
       (S::EPI && (int64_t)p.M * p.ldc * 4 > lim)) {
     // The general kernel has no split-K form: the caller runs unsplit.
     if (p.splits > 1) return hipErrorNotSupported;
     return sgemm_launch_shape(S::BM, S::BN, S::WM, S::WN, p, map, vec, stream);
   }
   const int64_t a_bytes = p.K > 0 ? ((int64_t)(p.M - 1) * p.lda + p.K) * 4 : 0;
-  const int64_t b_bytes = p.K > 0 ? ((int64_t)(p.K - 1) * p.ldb + p.N) * 4 : 0;
+  const int64_t b_bytes = p.K <= 0 ? 0
+                          : S::BT ? ((int64_t)(p.N - 1) * p.ldb + p.K) * 4
+                                  : ((int64_t)(p.K - 1) * p.ldb + p.N) * 4;
   const dim3 grid(map.tiles_m * map.tiles_n, p.splits), block(S::NT);
   hipLaunchKernelGGL(sgemm_dl_kernel<S>, grid, block, 0, stream, p, map, a_bytes, b_bytes);
   return hipGetLastError();
+}
+
+// Host replay of the transposed-B form's B side: Bt rows placed by the
+// direct loads (each LDS byte once, row R holding column bt_col(R)), and the
+// fragment reads giving each lane the element its MFMA step needs; bank
+// conflicts are added to *rconf.  Returns 0 when valid, else a code from 20.
+template <class S>
+int layout_check_bt(int banks, int64_t* rconf) {
+  static_assert(S::BT, "transposed-B shape");
+  static int n_of[S::B_STAGE], k_of[S::B_STAGE];
+  for (int i = 0; i < S::B_STAGE; ++i) n_of[i] = -1;
+  for (int i = 0; i < S::IB; ++i)
+    for (int w = 0; w < S::NW; ++w)
+      for (int l = 0; l < 64; ++l) {
+        const int off = 1024 * (i * S::NW + w) + 16 * l;
+        const int R = S::a_dl_row(i, w, l), q = S::a_dl_q(i, w, l);
+        if (R >= S::BN || q >= S::BK / 4 || S::bt_byte(R, q) != off) return 20;
+        for (int e = 0; e < 4; ++e) {
+          if (n_of[off + 4 * e] != -1) return 21;
+          n_of[off + 4 * e] = S::bt_col(R);
+          k_of[off + 4 * e] = 4 * q + e;
+        }
+      }
+  for (int i = 0; i < S::B_STAGE; i += 4)
+    if (n_of[i] < 0) return 22;
+  int addr[64];
+  for (int w = 0; w < S::NW; ++w) {
+    const int wn0 = (w % S::WAVES_N) * S::WN;
+    for (int g = 0; g < S::KG; ++g)
+      for (int nb = 0; nb < S::NB; ++nb) {
+        for (int l = 0; l < 64; ++l) {
+          addr[l] = S::bt_frag(wn0, nb, g, l);
+          if (addr[l] < 0 || addr[l] + 16 > S::B_STAGE) return 23;
+          if (addr[l] != S::bt_frag(wn0, 0, g, l) + nb * 32 * S::B_ROW) return 24;
+          // Step s: B[k = 8g + 4(l/32) + s][n = wn0 + NB*(l%32) + nb].
+          for (int st = 0; st < 4; ++st)
+            if (n_of[addr[l] + 4 * st] != wn0 + S::NB * (l % 32) + nb ||
+                k_of[addr[l] + 4 * st] != 8 * g + 4 * (l / 32) + st)
+              return 25;
+        }
+        *rconf += lds_conflicts(addr, 16, banks);
+      }
+  }
+  return 0;
 }
 
 // Host replay: direct-load placement and fragment reads (bounds, the element
@@ -501,6 +591,8 @@ int layout_check(int banks, int64_t out[2]) {
       }
     }
   }
+  const int rc = layout_check_bt<Shape<S::BM, S::BN, S::WM, S::WN, S::BK, S::NS, false, true>>(banks, &rconf);
+  if (rc != 0) return rc;
   out[0] = 0;  // no LDS writes by the waves (copies are LDS-direct)
   out[1] = rconf;
   return 0;
@@ -514,7 +606,8 @@ int layout_check(int banks, int64_t out[2]) {
                   "dl_f32_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_s" #NS},                  \
         &launch<Shape<BM, BN, WM, WN, BK, NS>>, &layout_check<Shape<BM, BN, WM, WN, BK, NS>>, \
         &launch<Shape<BM, BN, WM, WN, BK, NS>>, EFF,                                        \
-        &launch<Shape<BM, BN, WM, WN, BK, NS, true>>                                        \
+        &launch<Shape<BM, BN, WM, WN, BK, NS, true>>,                                       \
+        &launch<Shape<BM, BN, WM, WN, BK, NS, false, true>>                                 \
   }
 
 const Variant kVariants[] = {

@@ -83,7 +83,11 @@ __device__ inline f32x16 mfma(float a, float b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
 
-template <int BM, int BN, int BK, int WM, int WN, bool VEC, bool EPI>
+// BT: B given transposed (p.bt: Bt, N x K row-major).  A thread loads four
+// consecutive k of one column (one 16-byte load in VEC form) and stores them
+// down that column of the row-major B tile; consecutive lanes take
+// consecutive columns, so each 4-byte store of a wave covers 64 banks.
+template <int BM, int BN, int BK, int WM, int WN, bool VEC, bool EPI, bool BT>
 __global__ void __launch_bounds__((Shape<BM, BN, BK, WM, WN>::NT))
 sgemm_mfma_kernel(Params p, TileMap map) {
   using S = Shape<BM, BN, BK, WM, WN>;
@@ -130,6 +134,20 @@ sgemm_mfma_kernel(Params p, TileMap map) {
     b_dst[i] = S::b_chunk(k, nq);
   }
 
+  // BT staging: (column n, k chunk q) per slot.
+  const float* bt_src[CB];
+  bool bt_ok[CB];
+  int bt_k[CB], bt_dst[CB];
+#pragma unroll
+  for (int i = 0; i < CB; ++i) {
+    const int id = tid + i * NT;
+    const int n = id % BN, q = id / BN;
+    bt_ok[i] = (n0 + n) < N;
+    bt_src[i] = B + (int64_t)(bt_ok[i] ? n0 + n : 0) * p.ldb + 4 * q;
+    bt_k[i] = 4 * q;
+    bt_dst[i] = (4 * q) * BN + n;
+  }
+
   f32x4 ra[CA], rb[CB];
 
   auto load_slice = [&](int k0) {
@@ -145,6 +163,21 @@ sgemm_mfma_kernel(Params p, TileMap map) {
         for (int e = 0; e < 4; ++e)
           ra[i][e] = (a_row_ok[i] && kg + e < K) ? a_src[i][k0 + e] : 0.f;
       }
+    }
+    if constexpr (BT) {
+#pragma unroll
+      for (int i = 0; i < CB; ++i) {
+        const int kg = k0 + bt_k[i];
+        if (VEC) {
+          f32x4 v = {0.f, 0.f, 0.f, 0.f};
+          if (bt_ok[i] && kg < K) v = *reinterpret_cast<const f32x4*>(bt_src[i] + k0);
+          rb[i] = v;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) rb[i][e] = (bt_ok[i] && kg + e < K) ? bt_src[i][k0 + e] : 0.f;
+        }
+      }
+      return;
     }
 #pragma unroll
     for (int i = 0; i < CB; ++i) {
@@ -167,6 +200,13 @@ sgemm_mfma_kernel(Params p, TileMap map) {
     float* Bs = As + S::A_STAGE;
 #pragma unroll
     for (int i = 0; i < CA; ++i) *reinterpret_cast<f32x4*>(As + a_dst[i]) = ra[i];
+    if constexpr (BT) {
+#pragma unroll
+      for (int i = 0; i < CB; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Bs[bt_dst[i] + e * BN] = rb[i][e];
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < CB; ++i) *reinterpret_cast<f32x4*>(Bs + b_dst[i]) = rb[i];
   };
@@ -259,17 +299,20 @@ template <int BM, int BN, int BK, int WM, int WN>
 hipError_t launch(const Params& p, const TileMap& map, bool vec, hipStream_t stream) {
   using S = Shape<BM, BN, BK, WM, WN>;
   const dim3 grid(map.tiles_m * map.tiles_n), block(S::NT);
-  if (p.epi.on) {
-    if (vec)
-      hipLaunchKernelGGL((sgemm_mfma_kernel<BM, BN, BK, WM, WN, true, true>), grid, block, 0, stream, p, map);
-    else
-      hipLaunchKernelGGL((sgemm_mfma_kernel<BM, BN, BK, WM, WN, false, true>), grid, block, 0, stream, p, map);
+#define SGEMM_MFMA_LAUNCH(V, E, T) \
+  hipLaunchKernelGGL((sgemm_mfma_kernel<BM, BN, BK, WM, WN, V, E, T>), grid, block, 0, stream, p, map)
+  if (p.bt) {  // transposed B (the fused epilogue is not combined with it)
+    if (p.epi.on) return hipErrorNotSupported;
+    if (vec) SGEMM_MFMA_LAUNCH(true, false, true);
+    else SGEMM_MFMA_LAUNCH(false, false, true);
+  } else if (p.epi.on) {
+    if (vec) SGEMM_MFMA_LAUNCH(true, true, false);
+    else SGEMM_MFMA_LAUNCH(false, true, false);
   } else {
-    if (vec)
-      hipLaunchKernelGGL((sgemm_mfma_kernel<BM, BN, BK, WM, WN, true, false>), grid, block, 0, stream, p, map);
-    else
-      hipLaunchKernelGGL((sgemm_mfma_kernel<BM, BN, BK, WM, WN, false, false>), grid, block, 0, stream, p, map);
+    if (vec) SGEMM_MFMA_LAUNCH(true, false, false);
+    else SGEMM_MFMA_LAUNCH(false, false, false);
   }
+#undef SGEMM_MFMA_LAUNCH
   return hipGetLastError();
 }
 
@@ -341,7 +384,7 @@ int layout_check(int banks, int64_t out[2]) {
                   Shape<BM, BN, BK, WM, WN>::NT, 2, Shape<BM, BN, BK, WM, WN>::LDS_BYTES,    \
                   GEMM_ORDER_XCD, 8, 1, "mfma_f32_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN},      \
         &launch<BM, BN, BK, WM, WN>, &layout_check<BM, BN, BK, WM, WN>, nullptr, EFF,        \
-        &launch<BM, BN, BK, WM, WN>                                                          \
+        &launch<BM, BN, BK, WM, WN>, &launch<BM, BN, BK, WM, WN>                             \
   }
 
 const Variant kVariants[] = {

@@ -36,7 +36,8 @@ ORDER_XCD = 2
 ACT_NONE = 0
 ACT_RELU = 1
 
-EXPORTS = ["gemm_f32", "gemm_f16", "gemm_f32_ex", "gemm_f16_ex", "gemm_f32_epi", "gemm_f16_epi",
+EXPORTS = ["gemm_f32", "gemm_f16", "gemm_f32_ex", "gemm_f16_ex", "gemm_f32_bt", "gemm_f16_bt",
+           "gemm_f32_epi", "gemm_f16_epi",
            "gemm_f32_splitk",
            "gemm_f16_splitk", "gemm_splitk_workspace_bytes", "gemm_select_splitk_config",
            "gemm_num_configs", "gemm_get_config", "gemm_select_config", "gemm_tile_of_block",
@@ -87,6 +88,9 @@ def _declare(lib):
         getattr(lib, name).argtypes = gemm_args
         getattr(lib, name).restype = ctypes.c_int
     for name in ("gemm_f32_ex", "gemm_f16_ex"):
+        getattr(lib, name).argtypes = gemm_args + [cfgp]
+        getattr(lib, name).restype = ctypes.c_int
+    for name in ("gemm_f32_bt", "gemm_f16_bt"):
         getattr(lib, name).argtypes = gemm_args + [cfgp]
         getattr(lib, name).restype = ctypes.c_int
     for name in ("gemm_f32_epi", "gemm_f16_epi"):
@@ -152,6 +156,16 @@ def gemm_f32_ex(M, N, K, A, lda, B, ldb, C, ldc, stream, cfg: GemmConfig) -> int
 
 def gemm_f16_ex(M, N, K, A, lda, B, ldb, C, ldc, stream, cfg: GemmConfig) -> int:
     return lib().gemm_f16_ex(M, N, K, A, lda, B, ldb, C, ldc, stream,
+                             ctypes.byref(cfg) if cfg is not None else None)
+
+
+def gemm_f32_bt(M, N, K, A, lda, Bt, ldbt, C, ldc, stream=None, cfg: GemmConfig | None = None) -> int:
+    return lib().gemm_f32_bt(M, N, K, A, lda, Bt, ldbt, C, ldc, stream,
+                             ctypes.byref(cfg) if cfg is not None else None)
+
+
+def gemm_f16_bt(M, N, K, A, lda, Bt, ldbt, C, ldc, stream=None, cfg: GemmConfig | None = None) -> int:
+    return lib().gemm_f16_bt(M, N, K, A, lda, Bt, ldbt, C, ldc, stream,
                              ctypes.byref(cfg) if cfg is not None else None)
 
 
@@ -273,7 +287,8 @@ def _ld(t) -> int:
 
 
 def matmul(a, b, out=None, config: GemmConfig | None = None, stream=None, split_k: bool = True,
-           alpha: float = 1.0, beta: float = 0.0, bias=None, act: int = ACT_NONE):
+           alpha: float = 1.0, beta: float = 0.0, bias=None, act: int = ACT_NONE,
+           b_transposed: bool = False):
     """C = a @ b on the GPU through libgemm.  a: M x K, b: K x N, both
     float32 or both float16, row-major (any row stride).  Returns ``out``
     (allocated when None).  Raises GemmError on a non-OK status.
@@ -282,6 +297,9 @@ def matmul(a, b, out=None, config: GemmConfig | None = None, stream=None, split_
     chooses split-K (too few output tiles for the GPU) run the split-K form
     with a workspace allocated here; a ``config`` with ``splits`` > 1 forces
     that split.
+
+    b_transposed: ``b`` holds B^T (N x K, row-major) and the product is
+    a @ b.T (gemm_*_bt; not combined with split-K or the fused epilogue).
 
     alpha, beta, bias (a float32 GPU tensor of N values) and act select the
     fused epilogue out = act(alpha * (a @ b) + beta * out + bias) (through
@@ -292,7 +310,7 @@ def matmul(a, b, out=None, config: GemmConfig | None = None, stream=None, split_
     if not (a.is_cuda and b.is_cuda):
         raise ValueError("a and b must be GPU tensors")
     M, K = a.shape
-    K2, N = b.shape
+    N, K2 = b.shape if b_transposed else (b.shape[1], b.shape[0])
     if K2 != K:
         raise ValueError(f"inner dimensions differ: {K} vs {K2}")
     if out is None:
@@ -303,6 +321,14 @@ def matmul(a, b, out=None, config: GemmConfig | None = None, stream=None, split_
         stream = torch.cuda.current_stream(a.device).cuda_stream
     args = (M, N, K, a.data_ptr(), _ld(a), b.data_ptr(), _ld(b), out.data_ptr(), _ld(out), stream)
     dtype = DTYPE_F32 if a.dtype == torch.float32 else DTYPE_F16
+    if b_transposed:
+        if alpha != 1.0 or beta != 0.0 or bias is not None or act != ACT_NONE:
+            raise ValueError("b_transposed does not take the fused epilogue")
+        fn = gemm_f32_bt if dtype == DTYPE_F32 else gemm_f16_bt
+        st = fn(*args[:9], stream, config)
+        if st != GEMM_OK:
+            raise GemmError(st, fn.__name__)
+        return out
     if alpha != 1.0 or beta != 0.0 or bias is not None or act != ACT_NONE:
         if bias is not None and (bias.dtype != torch.float32 or bias.numel() != N or not bias.is_cuda
                                  or not bias.is_contiguous()):

@@ -178,6 +178,28 @@ gemm_status_t gemm_f16_splitk(int64_t M, int64_t N, int64_t K,
 int64_t gemm_splitk_workspace_bytes(int32_t dtype, int64_t M, int64_t N, int64_t K,
                                     int32_t splits);
 
+/*
+ * GEMM with B given transposed: C = A x B where B is passed as Bt, the
+ * N x K row-major matrix with Bt[j*ldbt + k] = B[k][j] (column-major B, the
+ * layout of the baseline kernel in the lqnn.cn SGEMM article, section 3.1;
+ * the page transposes it before its GEMM, here the matrix cores read its
+ * k-contiguous columns directly).  Same conventions as gemm_f32 / gemm_f16
+ * with ldbt >= max(1, K) in place of ldb >= max(1, N); the vector path needs
+ * ldbt a multiple of 4 (FP32) or 8 (FP16).  cfg NULL: the selection for the
+ * shape among the variants with a transposed-B form; a forced variant
+ * without one -> UNSUPPORTED.
+ */
+gemm_status_t gemm_f32_bt(int64_t M, int64_t N, int64_t K,
+                          const float *A, int64_t lda,
+                          const float *Bt, int64_t ldbt,
+                          float *C, int64_t ldc, void *stream,
+                          const gemm_config_t *cfg);
+gemm_status_t gemm_f16_bt(int64_t M, int64_t N, int64_t K,
+                          const gemm_f16_t *A, int64_t lda,
+                          const gemm_f16_t *Bt, int64_t ldbt,
+                          gemm_f16_t *C, int64_t ldc, void *stream,
+                          const gemm_config_t *cfg);
+
 /* Activation applied by the fused epilogue. */
 typedef enum gemm_act {
     GEMM_ACT_NONE = 0,

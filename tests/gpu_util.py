@@ -77,7 +77,7 @@ WS_GUARD = 256  # canary floats on each side of a split-K workspace
 
 
 def run(A: np.ndarray, B: np.ndarray, cfg=None, pad=(0, 0, 0), offset=(0, 0, 0),
-        repeat: int = 1, split=None, epi=None):
+        repeat: int = 1, split=None, epi=None, bt: bool = False):
     """Compute A @ B through libgemm.  Returns (C as numpy, C DevMatrix).
 
     split: None for the plain entry points; "auto" for gemm_*_splitk with
@@ -88,13 +88,16 @@ def run(A: np.ndarray, B: np.ndarray, cfg=None, pad=(0, 0, 0), offset=(0, 0, 0),
     epi: None, or a dict with alpha, beta, C0 (initial C, or None: C keeps
     its NaN canaries), bias (float32 array of N, or None), act and
     bias_offset (floats to misalign the bias by): gemm_*_epi with `cfg`
-    (None: the library's choice)."""
+    (None: the library's choice).
+
+    bt: B is given transposed (the argument is Bt, N x K) and the call is
+    gemm_*_bt; A @ Bt.T is computed."""
     kind = "f32" if A.dtype == np.float32 else "f16"
     dtype = gemm.DTYPE_F32 if kind == "f32" else gemm.DTYPE_F16
     M, K = A.shape
-    N = B.shape[1]
+    N = B.shape[0] if bt else B.shape[1]
     dA = DevMatrix(A, M, K, kind, pad=pad[0], offset=offset[0])
-    dB = DevMatrix(B, K, N, kind, pad=pad[1], offset=offset[1])
+    dB = DevMatrix(B, *((N, K) if bt else (K, N)), kind, pad=pad[1], offset=offset[1])
     dC = DevMatrix(None if epi is None else epi.get("C0"), M, N, kind, pad=pad[2], offset=offset[2])
     bias_dev, epi_s = None, None
     if epi is not None:
@@ -116,7 +119,10 @@ def run(A: np.ndarray, B: np.ndarray, cfg=None, pad=(0, 0, 0), offset=(0, 0, 0),
         ws = torch.from_numpy(host.view(np.int32)).to("cuda")
     for _ in range(repeat):
         args = (M, N, K, dA.ptr, dA.ld, dB.ptr, dB.ld, dC.ptr, dC.ld)
-        if epi is not None:
+        if bt:
+            fn = gemm.gemm_f32_bt if kind == "f32" else gemm.gemm_f16_bt
+            st = fn(*args, stream, cfg)
+        elif epi is not None:
             fn = gemm.gemm_f32_epi if kind == "f32" else gemm.gemm_f16_epi
             st = fn(*args, stream, cfg, epi_s)
         elif split is not None:

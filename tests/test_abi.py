@@ -265,3 +265,22 @@ def test_epilogue_argument_validation(fn):
         if name.startswith(("pipe_", "simt_")):
             assert fn(*base, c, ok) == gemm.GEMM_ERR_UNSUPPORTED, name
     assert fn(0, 64, 64, PA, 64, PB, 64, 0, 64, None, None, ok) == gemm.GEMM_OK   # M == 0
+
+
+@pytest.mark.parametrize("fn", [gemm.gemm_f32_bt, gemm.gemm_f16_bt])
+def test_bt_argument_validation(fn):
+    """Transposed-B entry points: ldbt is checked against K (not N), the
+    alias check covers the N x K span of Bt, and forced variants without a
+    transposed-B form are refused; all before any launch."""
+    dt = gemm.DTYPE_F32 if fn is gemm.gemm_f32_bt else gemm.DTYPE_F16
+    es = 4 if dt == gemm.DTYPE_F32 else 2
+    # M=64, N=32, K=128: ldbt must be >= 128 even though N = 32.
+    assert fn(64, 32, 128, PA, 128, PB, 64, PC, 32) == gemm.GEMM_ERR_INVALID_ARG
+    assert fn(64, 32, 128, PA, 128, PB, 127, PC, 32) == gemm.GEMM_ERR_INVALID_ARG
+    # C starting inside the last row of Bt (N-1 rows of 128 plus 128) aliases.
+    assert fn(64, 32, 128, PA, 128, PB, 128, PB + (31 * 128 + 100) * es, 32) == gemm.GEMM_ERR_ALIAS
+    for c in gemm.configs(dt):
+        name = c.name.decode()
+        if name.startswith(("pipe_", "simt_")):
+            assert fn(64, 32, 128, PA, 128, PB, 128, PC, 32, None, c) == gemm.GEMM_ERR_UNSUPPORTED, name
+    assert fn(0, 32, 128, PA, 128, PB, 128, 0, 32) == gemm.GEMM_OK  # M == 0

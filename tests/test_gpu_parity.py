@@ -373,3 +373,80 @@ def test_matmul_fused_epilogue():
     ref, den = oracle.gemm_rows_epi(A, B, C0, 1.5, 0.25, bias, 1)
     rep = oracle.check(out.cpu().numpy(), ref, den, oracle.HGEMM_TOL)
     assert rep["ok"], rep
+
+
+# --- B given transposed (gemm_*_bt: Bt is N x K row-major) -----------------
+
+def _bt_cfgs(kind):
+    dt = gemm.DTYPE_F32 if kind == "f32" else gemm.DTYPE_F16
+    return [c for c in gemm.configs(dt) if c.name.decode().startswith(("dl_", "tr_", "mfma_"))]
+
+
+BT_SHAPES = [(1, 1, 1), (2, 3, 5), (31, 33, 17), (127, 129, 65), (130, 257, 96),
+             (257, 130, 200), (65, 300, 512)]
+
+
+@pytest.mark.parametrize("kind", ["f32", "f16"])
+@pytest.mark.parametrize("shape", BT_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_bt_exact_small_int(kind, shape):
+    """Small integers: every variant with a transposed-B form matches the
+    oracle's A @ Bt^T bit for bit, plain and with padded leading dimensions
+    (NaN canaries in the padding, so a read past K or N would show)."""
+    M, N, K = shape
+    dt = np.float32 if kind == "f32" else np.float16
+    A = synth.small_int(29, 0, M, K, dtype=dt)
+    Bt = synth.small_int(29, 1, N, K, dtype=dt)
+    ref, _ = oracle.gemm_rows_bt(A, Bt)
+    for cfg in _bt_cfgs(kind):
+        for pad in ((0, 0, 0), (3, 5, 1)):
+            log(f"{kind} bt exact cfg={cfg.name.decode()} shape={shape} pad={pad}")
+            C, _ = run(A, Bt, cfg, pad=pad, bt=True)
+            assert np.array_equal(C.astype(np.float64), ref), (cfg.name, pad)
+
+
+@pytest.mark.parametrize("kind", ["f32", "f16"])
+def test_bt_random_and_paths(kind):
+    """Random operands: the library's choice, padded leading dimensions and
+    a misaligned Bt (the general kernel's scalar path), within tolerance,
+    and equal to the plain entry point on the materialised B."""
+    M, N, K = 300, 520, 700
+    A, B = synth.workload(M, N, K, kind, seed=31)
+    Bt = np.ascontiguousarray(B.T)
+    ref, den = oracle.gemm_rows_bt(A, Bt)
+    tol = oracle.SGEMM_TOL if kind == "f32" else oracle.HGEMM_TOL
+    for name, kw in (("auto", {}), ("padded", dict(pad=(3, 5, 7))), ("bt+1", dict(offset=(0, 1, 0)))):
+        log(f"{kind} bt random {name}")
+        C, _ = run(A, Bt, None, bt=True, **kw)
+        rep = oracle.check(C, ref, den, tol)
+        log(f"  max_rel={rep['max_rel']:.3e}")
+        assert rep["ok"], (name, rep)
+
+
+@pytest.mark.parametrize("kind", ["f32", "f16"])
+def test_bt_full_size_sampled(kind):
+    """4096^3 with B given transposed, through the library's choice: sampled
+    rows against the oracle."""
+    M = N = K = 4096
+    A, B = synth.workload(M, N, K, kind, seed=5)
+    Bt = np.ascontiguousarray(B.T)
+    del B
+    log(f"{kind} bt 4096^3")
+    C, _ = run(A, Bt, None, bt=True)
+    rows = np.array([0, 1, 255, 256, 2047, 4000, 4095])
+    ref, den = oracle.gemm_rows_bt(A, Bt, rows=rows)
+    rep = oracle.check(np.ascontiguousarray(C[rows]), ref, den,
+                       oracle.SGEMM_TOL if kind == "f32" else oracle.HGEMM_TOL)
+    log(f"  max_rel={rep['max_rel']:.3e}")
+    assert rep["ok"], rep
+
+
+def test_matmul_b_transposed():
+    import torch
+    A, B = synth.workload(200, 264, 136, "f32", seed=37)
+    bt = torch.from_numpy(np.ascontiguousarray(B.T)).cuda()
+    log("matmul f32 b_transposed")
+    out = gemm.matmul(torch.from_numpy(A).cuda(), bt, b_transposed=True)
+    torch.cuda.synchronize()
+    ref, den = oracle.gemm_rows_bt(A, np.ascontiguousarray(B.T))
+    rep = oracle.check(out.cpu().numpy(), ref, den, oracle.SGEMM_TOL)
+    assert rep["ok"], rep
