@@ -18,7 +18,9 @@ increment 0x9E3779B97F4A7C15).
   be regenerated on its own.
 * ``uniform[-1, 1)``: ``(u_t >> 40) * 2**-23 - 1``, a 24-bit grid value that
   is exact in FP32.  FP16 inputs are the round-to-nearest-even FP16 value of
-  that FP32 number (numpy's ``astype(np.float16)``).
+  that FP32 number (numpy's ``astype(np.float16)``); BF16 inputs are the
+  round-to-nearest-even bfloat16 value of it (:func:`to_bf16`), held as
+  uint16 bit patterns under the marker dtype :data:`BF16`.
 
 Streams: A uses stream 0 and B stream 1.  The workloads draw i.i.d.
 uniform[-1, 1) entries from seed 0, the synthetic square and rectangular
@@ -35,6 +37,10 @@ _C2 = 0x94D049BB133111EB
 
 STREAM_A = 0
 STREAM_B = 1
+
+# bfloat16 bit patterns: a one-field structured dtype over uint16 (numpy has
+# no bfloat16); ``x.view(np.uint16)`` gives the bits.
+BF16 = np.dtype([("bf16", "<u2")])
 
 
 def mix64_int(z: int) -> int:
@@ -102,12 +108,39 @@ def uniform_f16(seed: int, stream: int, rows: int, cols: int) -> np.ndarray:
     return uniform_f32(seed, stream, rows, cols).astype(np.float16)
 
 
+def to_bf16(x) -> np.ndarray:
+    """float32 values to bfloat16 bit patterns (dtype BF16), rounding to
+    nearest with ties to even on the 16 dropped bits; NaN stays a quiet NaN
+    with its sign."""
+    bits = np.array(x, dtype=np.float32, order="C").view(np.uint32)
+    lsb = (bits >> np.uint32(16)) & np.uint32(1)
+    with np.errstate(over="ignore"):
+        rounded = (bits + np.uint32(0x7FFF) + lsb) >> np.uint32(16)
+    nan = (bits & np.uint32(0x7FFFFFFF)) > np.uint32(0x7F800000)
+    out = np.where(nan, (bits >> np.uint32(16)) | np.uint32(0x40), rounded)
+    return out.astype(np.uint16).view(BF16)
+
+
+def bf16_to_f32(b) -> np.ndarray:
+    """bfloat16 bit patterns (BF16 or uint16) to float32: the pattern is the
+    upper half of the binary32 encoding, so this is exact."""
+    bits = np.array(np.asarray(b).view(np.uint16), order="C").astype(np.uint32)
+    return (bits << np.uint32(16)).view(np.float32)
+
+
+def uniform_bf16(seed: int, stream: int, rows: int, cols: int) -> np.ndarray:
+    """The FP32 matrix of :func:`uniform_f32` rounded to bfloat16 (RNE)."""
+    return to_bf16(uniform_f32(seed, stream, rows, cols))
+
+
 def small_int(seed: int, stream: int, rows: int, cols: int, lo: int = -2,
               hi: int = 2, dtype=np.float32) -> np.ndarray:
     """Integers in [lo, hi] (as ``dtype``): with |a|, |b| <= 2 and K <= 512
     every partial sum of a GEMM is an integer below 2**11, exact in FP32 and
     FP16, so the product has one correct answer."""
     n = rows * cols
+    if dtype == BF16:
+        return to_bf16(small_int(seed, stream, rows, cols, lo, hi, np.float32))
     if n == 0:
         return np.zeros((rows, cols), dtype=dtype)
     u = stream_u64(seed, stream, n) >> np.uint64(32)
@@ -130,4 +163,6 @@ def workload(M: int, N: int, K: int, dtype: str, seed: int = 0):
         return (uniform_f32(seed, STREAM_A, M, K), uniform_f32(seed, STREAM_B, K, N))
     if dtype == "f16":
         return (uniform_f16(seed, STREAM_A, M, K), uniform_f16(seed, STREAM_B, K, N))
+    if dtype == "bf16":
+        return (uniform_bf16(seed, STREAM_A, M, K), uniform_bf16(seed, STREAM_B, K, N))
     raise ValueError(f"unknown dtype {dtype!r}")

@@ -16,6 +16,11 @@ marshals numpy arrays:
 * :func:`gemm_entries` -- the same quantities for single (i, j) pairs.
 * :func:`check` -- ``max_ij |C_gpu - C_ref| / D`` plus counts.
 * :func:`f16_to_f64` -- exact IEEE binary16 decoding.
+* :func:`bf16_to_f64` -- exact bfloat16 decoding.
+
+Element types: float32, float16 (or uint16 binary16 bit patterns), and
+bfloat16 as uint16 bit patterns viewed with the marker dtype :data:`BF16`
+(numpy has no bfloat16 type).
 
 Parity status: pinned (see the oracle tests in ``tests/``).
 """
@@ -40,6 +45,15 @@ _lib = None
 
 SGEMM_TOL = 1e-5
 HGEMM_TOL = 2e-3
+# BF16 output: unit roundoff 2**-8 (RNE to 8 significant bits), plus at most
+# K * 2**-24 for FP32 accumulation of exact products at K <= 8192.
+BF16_TOL = 5e-3
+
+# bfloat16 bit patterns: a one-field structured dtype over uint16, so that a
+# BF16 matrix cannot be mistaken for binary16 or plain integers.
+BF16 = np.dtype([("bf16", "<u2")])
+
+TOL = {"f32": SGEMM_TOL, "f16": HGEMM_TOL, "bf16": BF16_TOL}
 
 
 def build(src: str = _SRC, out: str = _LIB, extra_flags=()) -> str:
@@ -57,24 +71,29 @@ def _declare(lib):
     lib.oracle_f16_to_f64.restype = ctypes.c_double
     lib.oracle_f16_array_to_f64.argtypes = [p, p, i64]
     lib.oracle_f16_array_to_f64.restype = None
-    for name in ("oracle_gemm_rows_f32", "oracle_gemm_rows_f16"):
+    lib.oracle_bf16_to_f64.argtypes = [ctypes.c_uint16]
+    lib.oracle_bf16_to_f64.restype = ctypes.c_double
+    lib.oracle_bf16_array_to_f64.argtypes = [p, p, i64]
+    lib.oracle_bf16_array_to_f64.restype = None
+    for name in ("oracle_gemm_rows_f32", "oracle_gemm_rows_f16", "oracle_gemm_rows_bf16"):
         fn = getattr(lib, name)
         fn.argtypes = [i64, i64, i64, p, i64, p, i64, p, p, i64, p, i64, ctypes.c_int]
         fn.restype = ctypes.c_int
-    for name in ("oracle_gemm_entries_f32", "oracle_gemm_entries_f16"):
+    for name in ("oracle_gemm_entries_f32", "oracle_gemm_entries_f16", "oracle_gemm_entries_bf16"):
         fn = getattr(lib, name)
         fn.argtypes = [i64, p, i64, p, i64, p, p, i64, p, p]
         fn.restype = ctypes.c_int
-    for name in ("oracle_gemm_rows_bt_f32", "oracle_gemm_rows_bt_f16"):
+    for name in ("oracle_gemm_rows_bt_f32", "oracle_gemm_rows_bt_f16", "oracle_gemm_rows_bt_bf16"):
         fn = getattr(lib, name)
         fn.argtypes = [i64, i64, i64, p, i64, p, i64, p, p, i64, p, i64]
         fn.restype = ctypes.c_int
-    for name in ("oracle_epilogue_rows_f32", "oracle_epilogue_rows_f16"):
+    for name in ("oracle_epilogue_rows_f32", "oracle_epilogue_rows_f16",
+                 "oracle_epilogue_rows_bf16"):
         fn = getattr(lib, name)
         fn.argtypes = [i64, i64, ctypes.c_double, ctypes.c_double, p, i64, p, ctypes.c_int, p,
                        p, i64, p, i64]
         fn.restype = ctypes.c_int
-    for name in ("oracle_check_f32", "oracle_check_f16"):
+    for name in ("oracle_check_f32", "oracle_check_f16", "oracle_check_bf16"):
         fn = getattr(lib, name)
         fn.argtypes = [i64, i64, p, i64, p, i64, p, i64, ctypes.c_double, p, p]
         fn.restype = None
@@ -126,25 +145,33 @@ def _kind(a: np.ndarray) -> str:
         return "f32"
     if a.dtype == np.float16 or a.dtype == np.uint16:
         return "f16"
+    if a.dtype == BF16:
+        return "bf16"
     raise TypeError(f"unsupported dtype {a.dtype}")
 
 
 def _bits16(a: np.ndarray) -> np.ndarray:
-    return a.view(np.uint16) if a.dtype == np.float16 else a
+    return a.view(np.uint16) if a.dtype in (np.float16, BF16) else a
+
+
+def _raw(a: np.ndarray, kind: str) -> tuple[np.ndarray, type]:
+    """The array as the C routines take it (float32, or uint16 bits)."""
+    if kind == "f32":
+        return a, np.float32
+    return _bits16(a), np.uint16
 
 
 def gemm_rows(A: np.ndarray, B: np.ndarray, rows=None, threads: int | None = None,
               lib=None):
     """C_ref and D (both float64) for the rows ``rows`` of C (all rows when
     None).  A is M x K, B is K x N; float32, or float16 (or uint16 binary16
-    bit patterns)."""
+    bit patterns), or bfloat16 (:data:`BF16`)."""
     lib = lib or load()
     kind = _kind(A)
     if _kind(B) != kind:
         raise TypeError("A and B must have the same element type")
-    dt = np.float32 if kind == "f32" else np.uint16
-    if kind == "f16":
-        A, B = _bits16(A), _bits16(B)
+    A, dt = _raw(A, kind)
+    B, _ = _raw(B, kind)
     A, lda = _as_matrix(A, dt)
     B, ldb = _as_matrix(B, dt)
     M, K = A.shape
@@ -162,7 +189,7 @@ def gemm_rows(A: np.ndarray, B: np.ndarray, rows=None, threads: int | None = Non
     D = np.zeros((nrows, N), dtype=np.float64)
     if nrows == 0 or N == 0:
         return C, D
-    fn = lib.oracle_gemm_rows_f32 if kind == "f32" else lib.oracle_gemm_rows_f16
+    fn = getattr(lib, f"oracle_gemm_rows_{kind}")
     # A dummy one-element buffer stands in for A or B when K == 0.
     a_ptr = _ptr(A) if A.size else _ptr(np.zeros(1, dt))
     b_ptr = _ptr(B) if B.size else _ptr(np.zeros(1, dt))
@@ -180,9 +207,8 @@ def gemm_rows_bt(A: np.ndarray, Bt: np.ndarray, rows=None, lib=None):
     kind = _kind(A)
     if _kind(Bt) != kind:
         raise TypeError("A and Bt must have the same element type")
-    dt = np.float32 if kind == "f32" else np.uint16
-    if kind == "f16":
-        A, Bt = _bits16(A), _bits16(Bt)
+    A, dt = _raw(A, kind)
+    Bt, _ = _raw(Bt, kind)
     A, lda = _as_matrix(A, dt)
     Bt, ldbt = _as_matrix(Bt, dt)
     M, K = A.shape
@@ -200,7 +226,7 @@ def gemm_rows_bt(A: np.ndarray, Bt: np.ndarray, rows=None, lib=None):
     D = np.zeros((nrows, N), dtype=np.float64)
     if nrows == 0 or N == 0:
         return C, D
-    fn = lib.oracle_gemm_rows_bt_f32 if kind == "f32" else lib.oracle_gemm_rows_bt_f16
+    fn = getattr(lib, f"oracle_gemm_rows_bt_{kind}")
     a_ptr = _ptr(A) if A.size else _ptr(np.zeros(1, dt))
     b_ptr = _ptr(Bt) if Bt.size else _ptr(np.zeros(1, dt))
     rc = fn(nrows, N, K, a_ptr, lda, b_ptr, ldbt, rp, _ptr(C), N, _ptr(D), N)
@@ -222,10 +248,11 @@ def gemm_rows_epi(A: np.ndarray, B: np.ndarray, C0, alpha: float, beta: float, b
     C, D = gemm_rows(A, B, rows=rows, threads=threads, lib=lib)
     kind = _kind(A)
     M, N = A.shape[0], B.shape[1]
-    dt = np.float32 if kind == "f32" else np.uint16
     c0_ptr, ldc0, keep = None, max(N, 1), []
     if beta != 0.0:
-        C0m = _bits16(C0) if kind == "f16" else C0
+        if _kind(C0) != kind:
+            raise TypeError("C0 must have the element type of A")
+        C0m, dt = _raw(C0, kind)
         C0m, ldc0 = _as_matrix(C0m, dt)
         if C0m.shape != (M, N):
             raise ValueError("C0 must be M x N")
@@ -240,7 +267,7 @@ def gemm_rows_epi(A: np.ndarray, B: np.ndarray, C0, alpha: float, beta: float, b
     rows_arr = None if rows is None else np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
     rp = None if rows_arr is None else _ptr(rows_arr)
     if C.size:
-        fn = lib.oracle_epilogue_rows_f32 if kind == "f32" else lib.oracle_epilogue_rows_f16
+        fn = getattr(lib, f"oracle_epilogue_rows_{kind}")
         rc = fn(C.shape[0], N, float(alpha), float(beta), c0_ptr, ldc0, b_ptr, int(act), rp,
                 _ptr(C), N, _ptr(D), N)
         if rc != 0:
@@ -252,9 +279,10 @@ def gemm_entries(A: np.ndarray, B: np.ndarray, ii, jj, lib=None):
     """C_ref[ii[t], jj[t]] and D[ii[t], jj[t]] as float64 vectors."""
     lib = lib or load()
     kind = _kind(A)
-    dt = np.float32 if kind == "f32" else np.uint16
-    if kind == "f16":
-        A, B = _bits16(A), _bits16(B)
+    if _kind(B) != kind:
+        raise TypeError("A and B must have the same element type")
+    A, dt = _raw(A, kind)
+    B, _ = _raw(B, kind)
     A, lda = _as_matrix(A, dt)
     B, ldb = _as_matrix(B, dt)
     M, K = A.shape
@@ -269,7 +297,7 @@ def gemm_entries(A: np.ndarray, B: np.ndarray, ii, jj, lib=None):
     d = np.zeros(ii.size, dtype=np.float64)
     if ii.size == 0:
         return c, d
-    fn = lib.oracle_gemm_entries_f32 if kind == "f32" else lib.oracle_gemm_entries_f16
+    fn = getattr(lib, f"oracle_gemm_entries_{kind}")
     a_ptr = _ptr(A) if A.size else _ptr(np.zeros(1, dt))
     b_ptr = _ptr(B) if B.size else _ptr(np.zeros(1, dt))
     rc = fn(K, a_ptr, lda, b_ptr, ldb, _ptr(ii), _ptr(jj), ii.size, _ptr(c), _ptr(d))
@@ -281,12 +309,11 @@ def gemm_entries(A: np.ndarray, B: np.ndarray, ii, jj, lib=None):
 def check(C_gpu: np.ndarray, C_ref: np.ndarray, D: np.ndarray, tol: float,
           lib=None) -> dict:
     """Element-wise error ratio |C_gpu - C_ref| / D, maximised.  C_gpu is
-    float32 or float16 / uint16 bit patterns (judged after FP16 rounding)."""
+    float32, float16 / uint16 bit patterns or :data:`BF16` (a 16-bit result
+    is judged after its own output rounding)."""
     lib = lib or load()
     kind = _kind(C_gpu)
-    dt = np.float32 if kind == "f32" else np.uint16
-    if kind == "f16":
-        C_gpu = _bits16(C_gpu)
+    C_gpu, dt = _raw(C_gpu, kind)
     C_gpu, ldc = _as_matrix(C_gpu, dt)
     R, ldr = _as_matrix(np.asarray(C_ref, dtype=np.float64), np.float64)
     Dm, ldd = _as_matrix(np.asarray(D, dtype=np.float64), np.float64)
@@ -296,7 +323,7 @@ def check(C_gpu: np.ndarray, C_ref: np.ndarray, D: np.ndarray, tol: float,
     out = np.zeros(4, dtype=np.float64)
     cnt = np.zeros(2, dtype=np.int64)
     if M and N:
-        fn = lib.oracle_check_f32 if kind == "f32" else lib.oracle_check_f16
+        fn = getattr(lib, f"oracle_check_{kind}")
         fn(M, N, _ptr(C_gpu), ldc, _ptr(R), ldr, _ptr(Dm), ldd, float(tol),
            _ptr(out), _ptr(cnt))
     return {"max_rel": float(out[0]), "max_abs": float(out[1]),
@@ -312,4 +339,14 @@ def f16_to_f64(bits) -> np.ndarray:
     out = np.empty(b.shape, dtype=np.float64)
     if b.size:
         lib.oracle_f16_array_to_f64(_ptr(b), _ptr(out), b.size)
+    return out
+
+
+def bf16_to_f64(bits) -> np.ndarray:
+    """Exact decode of bfloat16 bit patterns (:data:`BF16` or uint16 array)."""
+    lib = load()
+    b = np.ascontiguousarray(_bits16(np.asarray(bits)).astype(np.uint16, copy=False))
+    out = np.empty(b.shape, dtype=np.float64)
+    if b.size:
+        lib.oracle_bf16_array_to_f64(_ptr(b), _ptr(out), b.size)
     return out

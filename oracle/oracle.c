@@ -28,7 +28,11 @@
  *
  * FP16 inputs arrive as IEEE binary16 bit patterns and are decoded by this
  * file's own bit-level decoder (exact, including subnormals, signed zeros,
- * infinities and NaN).
+ * infinities and NaN).  BF16 inputs (bfloat16: the upper 16 bits of a
+ * binary32, the 16-bit type the GB300 GEMM article lists beside FP16 in
+ * sections 1.1 and 5.1) arrive as bit patterns too and have a decoder of
+ * their own; a BF16 x BF16 product carries at most 16 significant bits, so
+ * it is exact in double as well.
  *
  * Parity status: pinned.  The pins (identity, permutation, all-ones closed
  * form C_ij = K, rank-1 outer products, K = 0 and K = 1, brute force against
@@ -74,15 +78,45 @@ void oracle_f16_array_to_f64(const uint16_t *src, double *dst, int64_t n)
 }
 
 /* ---------------------------------------------------------------------- */
+/* bfloat16 -> binary64, exact.                                            */
+/* Layout: 1 sign bit, 8 exponent bits (bias 127), 7 fraction bits.        */
+/* ---------------------------------------------------------------------- */
+double oracle_bf16_to_f64(uint16_t h)
+{
+    const int sign = (h >> 15) & 1;
+    const int expo = (h >> 7) & 0xff;
+    const int frac = h & 0x7f;
+    double mag;
+    if (expo == 0) {
+        /* zero or subnormal: frac * 2^(1 - 127 - 7) */
+        mag = ldexp((double)frac, -133);
+    } else if (expo == 0xff) {
+        mag = frac ? NAN : INFINITY;
+    } else {
+        /* normal: (128 + frac) * 2^(expo - 127 - 7) */
+        mag = ldexp((double)(0x80 | frac), expo - 134);
+    }
+    return sign ? -mag : mag;
+}
+
+void oracle_bf16_array_to_f64(const uint16_t *src, double *dst, int64_t n)
+{
+    for (int64_t t = 0; t < n; ++t)
+        dst[t] = oracle_bf16_to_f64(src[t]);
+}
+
+/* ---------------------------------------------------------------------- */
 /* Input access: element (i, k) of a row-major matrix with leading         */
 /* dimension ld lives at base[i * ld + k].                                  */
 /* ---------------------------------------------------------------------- */
-enum { ORACLE_F32 = 0, ORACLE_F16 = 1 };
+enum { ORACLE_F32 = 0, ORACLE_F16 = 1, ORACLE_BF16 = 2 };
 
 static double load_elem(const void *base, int dtype, int64_t idx)
 {
     if (dtype == ORACLE_F32)
         return (double)((const float *)base)[idx];
+    if (dtype == ORACLE_BF16)
+        return oracle_bf16_to_f64(((const uint16_t *)base)[idx]);
     return oracle_f16_to_f64(((const uint16_t *)base)[idx]);
 }
 
@@ -199,6 +233,15 @@ int oracle_gemm_rows_f16(int64_t nrows, int64_t N, int64_t K,
                     nthreads);
 }
 
+int oracle_gemm_rows_bf16(int64_t nrows, int64_t N, int64_t K,
+                          const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb,
+                          const int64_t *rows, double *C, int64_t ldr,
+                          double *D, int64_t ldd, int nthreads)
+{
+    return run_rows(ORACLE_BF16, nrows, N, K, A, lda, B, ldb, rows, C, ldr, D, ldd,
+                    nthreads);
+}
+
 /*
  * Rows of C_ref and D for B given transposed: Bt is the N x K row-major
  * matrix with Bt[j][k] = B[k][j] (B column-major, the layout of the
@@ -263,6 +306,13 @@ int oracle_gemm_rows_bt_f16(int64_t nrows, int64_t N, int64_t K, const uint16_t 
     return run_rows_bt(ORACLE_F16, nrows, N, K, A, lda, Bt, ldbt, rows, C, ldr, D, ldd);
 }
 
+int oracle_gemm_rows_bt_bf16(int64_t nrows, int64_t N, int64_t K, const uint16_t *A,
+                             int64_t lda, const uint16_t *Bt, int64_t ldbt, const int64_t *rows,
+                             double *C, int64_t ldr, double *D, int64_t ldd)
+{
+    return run_rows_bt(ORACLE_BF16, nrows, N, K, A, lda, Bt, ldbt, rows, C, ldr, D, ldd);
+}
+
 /*
  * Fused epilogue, applied to rows of C_ref and D produced by
  * oracle_gemm_rows_* (in place):
@@ -324,6 +374,14 @@ int oracle_epilogue_rows_f16(int64_t nrows, int64_t N, double alpha, double beta
                         D, ldd);
 }
 
+int oracle_epilogue_rows_bf16(int64_t nrows, int64_t N, double alpha, double beta,
+                              const uint16_t *C0, int64_t ldc0, const float *bias, int act,
+                              const int64_t *rows, double *C, int64_t ldr, double *D, int64_t ldd)
+{
+    return run_epilogue(ORACLE_BF16, nrows, N, alpha, beta, C0, ldc0, bias, act, rows, C, ldr,
+                        D, ldd);
+}
+
 /*
  * Single entries C_ref[ii[t]][jj[t]] and D[ii[t]][jj[t]], each one a plain
  * dot product over k ascending (the same order as the row routine).
@@ -362,13 +420,20 @@ int oracle_gemm_entries_f16(int64_t K, const uint16_t *A, int64_t lda,
     return run_entries(ORACLE_F16, K, A, lda, B, ldb, ii, jj, n, c, d);
 }
 
+int oracle_gemm_entries_bf16(int64_t K, const uint16_t *A, int64_t lda,
+                             const uint16_t *B, int64_t ldb, const int64_t *ii,
+                             const int64_t *jj, int64_t n, double *c, double *d)
+{
+    return run_entries(ORACLE_BF16, K, A, lda, B, ldb, ii, jj, n, c, d);
+}
+
 /* ---------------------------------------------------------------------- */
 /* Error metric.                                                           */
 /*   r_ij = |C_gpu[i][j] - C_ref[i][j]| / D[i][j]                           */
 /*   r_ij = 0 when numerator and D are both 0; +inf when only D is 0.      */
 /*   e = max r_ij.  A NaN or Inf in C_gpu is counted as non-finite.         */
-/* C_gpu is widened exactly (FP32) or decoded exactly (FP16 bit patterns),  */
-/* i.e. the FP16 result is judged after its own output rounding.           */
+/* C_gpu is widened exactly (FP32) or decoded exactly (FP16 or BF16 bit     */
+/* patterns), i.e. a 16-bit result is judged after its own output rounding.*/
 /* out[0] = e, out[1] = max |C_gpu - C_ref|, out[2] = i of e, out[3] = j.   */
 /* cnt[0] = #(r_ij > tol), cnt[1] = #non-finite C_gpu entries.              */
 /* ---------------------------------------------------------------------- */
@@ -427,4 +492,11 @@ void oracle_check_f16(int64_t M, int64_t N, const uint16_t *C, int64_t ldc,
                       double tol, double *out, int64_t *cnt)
 {
     check_common(ORACLE_F16, M, N, C, ldc, R, ldr, D, ldd, tol, out, cnt);
+}
+
+void oracle_check_bf16(int64_t M, int64_t N, const uint16_t *C, int64_t ldc,
+                       const double *R, int64_t ldr, const double *D, int64_t ldd,
+                       double tol, double *out, int64_t *cnt)
+{
+    check_common(ORACLE_BF16, M, N, C, ldc, R, ldr, D, ldd, tol, out, cnt);
 }

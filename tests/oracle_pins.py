@@ -11,7 +11,10 @@ blocking", quant67.com, introduction; "hgemm_naive_kernel explained",
 yuyanqi.com, section 1.1).  The pages print no worked matrices, so the pins
 are closed forms (identity, permutation, all-ones C_ij = K, rank-1 outer
 products, K = 0, K = 1), brute force against exact rational arithmetic, a
-float64 library matmul, and the exhaustive binary16 table.
+float64 library matmul, and the exhaustive binary16 and bfloat16 tables.
+Every structural pin runs for FP32, FP16 and BF16 inputs (BF16 as bit
+patterns under the marker dtype; values are built and widened here through
+the binary32 definition of bfloat16, independently of the oracle's decoder).
 """
 from __future__ import annotations
 
@@ -27,22 +30,42 @@ from tests import golden_data
 U64 = 2.0 ** -53  # unit roundoff of binary64
 
 
+BF16 = synth.BF16
+
+
+def _make(x, dt) -> np.ndarray:
+    """Values (exactly representable in dt) as an array of element type dt."""
+    x = np.asarray(x, dtype=np.float64)
+    if dt == BF16:
+        return synth.to_bf16(x.astype(np.float32))
+    return x.astype(dt)
+
+
+def _wide(x: np.ndarray) -> np.ndarray:
+    """The exact values of x as float64."""
+    if x.dtype == BF16:
+        return synth.bf16_to_f32(x).astype(np.float64)
+    return x.astype(np.float64)
+
+
 def _padded(x: np.ndarray, pad: int) -> np.ndarray:
     """A row-major view of ``x`` whose leading dimension is cols + pad; the
     pad columns hold NaN so that reading them poisons the result."""
     rows, cols = x.shape
-    big = np.full((rows, cols + pad), np.nan, dtype=x.dtype)
+    big = _make(np.full((rows, cols + pad), np.nan), x.dtype)
     big[:, :cols] = x
     return big[:, :cols]
 
 
 def _dtypes():
-    return (np.float32, np.float16)
+    return (np.float32, np.float16, BF16)
 
 
 def _rand(dtype, seed, stream, r, c):
     if dtype == np.float32:
         return synth.uniform_f32(seed, stream, r, c)
+    if dtype == BF16:
+        return synth.uniform_bf16(seed, stream, r, c)
     return synth.uniform_f16(seed, stream, r, c)
 
 
@@ -51,15 +74,15 @@ def pin_identity(lib):
     for dt in _dtypes():
         for (M, N, K) in [(5, 7, 5), (1, 9, 1), (12, 3, 12)]:
             B = _rand(dt, 11, 1, K, N)
-            A = np.eye(M, K, dtype=dt)
+            A = _make(np.eye(M, K), dt)
             C, D = oracle.gemm_rows(_padded(A, 3), _padded(B, 5), lib=lib)
-            assert np.array_equal(C, B.astype(np.float64)), "A=I must give C=B"
-            assert np.array_equal(D, np.abs(B.astype(np.float64))), "A=I: D=|B|"
+            assert np.array_equal(C, _wide(B)), "A=I must give C=B"
+            assert np.array_equal(D, np.abs(_wide(B))), "A=I: D=|B|"
         for (M, N, K) in [(7, 5, 5), (9, 1, 1), (3, 12, 12)]:
             A = _rand(dt, 12, 0, M, K)
-            B = np.eye(K, N, dtype=dt)
+            B = _make(np.eye(K, N), dt)
             C, D = oracle.gemm_rows(_padded(A, 2), _padded(B, 4), lib=lib)
-            assert np.array_equal(C, A.astype(np.float64)), "B=I must give C=A"
+            assert np.array_equal(C, _wide(A)), "B=I must give C=A"
 
 
 def pin_permutation(lib):
@@ -68,19 +91,21 @@ def pin_permutation(lib):
     for dt in _dtypes():
         K, N = 9, 6
         p = synth.permutation(3, 2, K)
-        A = np.zeros((K, K), dtype=dt)
+        A = np.zeros((K, K))
         A[np.arange(K), p] = 1
+        A = _make(A, dt)
         B = _rand(dt, 13, 1, K, N)
         C, _ = oracle.gemm_rows(_padded(A, 1), _padded(B, 3), lib=lib)
-        assert np.array_equal(C, B[p].astype(np.float64)), "C = P B"
+        assert np.array_equal(C, _wide(B)[p]), "C = P B"
         M, K = 4, 7
         q = synth.permutation(4, 2, K)
-        Bq = np.zeros((K, K), dtype=dt)
+        Bq = np.zeros((K, K))
         Bq[np.arange(K), q] = 1
+        Bq = _make(Bq, dt)
         A2 = _rand(dt, 14, 0, M, K)
         C2, _ = oracle.gemm_rows(A2, Bq, lib=lib)
         expect = np.zeros((M, K))
-        expect[:, q] = A2.astype(np.float64)
+        expect[:, q] = _wide(A2)
         assert np.array_equal(C2, expect), "C = A Q"
 
 
@@ -88,8 +113,8 @@ def pin_all_ones(lib):
     """All-ones A and B: C_ij = K and D_ij = K exactly."""
     for dt in _dtypes():
         for (M, N, K) in [(1, 1, 1), (2, 3, 5), (7, 1, 9), (33, 17, 64), (3, 4, 1000)]:
-            A = np.ones((M, K), dtype=dt)
-            B = np.ones((K, N), dtype=dt)
+            A = _make(np.ones((M, K)), dt)
+            B = _make(np.ones((K, N)), dt)
             C, D = oracle.gemm_rows(_padded(A, 1), B, lib=lib)
             assert np.all(C == K) and np.all(D == K), f"all-ones must give K={K}"
             c, d = oracle.gemm_entries(A, B, [M - 1, 0], [0, N - 1], lib=lib)
@@ -104,16 +129,17 @@ def pin_rank1(lib):
         u = synth.small_int(5, 0, M, 1, -3, 3).ravel()
         v = synth.small_int(5, 1, 1, N, -3, 3).ravel()
         for c in (0, 3, K - 1):
-            A = np.zeros((M, K), dtype=dt)
-            B = np.zeros((K, N), dtype=dt)
+            A = np.zeros((M, K))
+            B = np.zeros((K, N))
             A[:, c] = u
             B[c, :] = v
+            A, B = _make(A, dt), _make(B, dt)
             C, D = oracle.gemm_rows(A, _padded(B, 2), lib=lib)
             assert np.array_equal(C, np.outer(u, v)), "rank-1: C = u v^T"
             assert np.array_equal(D, np.abs(np.outer(u, v))), "rank-1: D"
-            B2 = np.zeros((K, N), dtype=dt)
+            B2 = np.zeros((K, N))
             B2[(c + 1) % K, :] = v
-            C2, _ = oracle.gemm_rows(A, B2, lib=lib)
+            C2, _ = oracle.gemm_rows(A, _make(B2, dt), lib=lib)
             assert not np.any(C2), "mismatched k must give C = 0"
 
 
@@ -121,14 +147,14 @@ def pin_k0_k1(lib):
     """K = 0 is the empty sum (C = 0, D = 0); K = 1 gives C_ij = a_i b_j,
     exact in double."""
     for dt in _dtypes():
-        A = np.zeros((4, 0), dtype=dt)
-        B = np.zeros((0, 3), dtype=dt)
+        A = _make(np.zeros((4, 0)), dt)
+        B = _make(np.zeros((0, 3)), dt)
         C, D = oracle.gemm_rows(A, B, lib=lib)
         assert C.shape == (4, 3) and not np.any(C) and not np.any(D), "K=0"
         A = _rand(dt, 21, 0, 5, 1)
         B = _rand(dt, 21, 1, 1, 7)
         C, _ = oracle.gemm_rows(A, B, lib=lib)
-        expect = np.outer(A.astype(np.float64).ravel(), B.astype(np.float64).ravel())
+        expect = np.outer(_wide(A).ravel(), _wide(B).ravel())
         assert np.array_equal(C, expect), "K=1: C = a b^T"
 
 
@@ -143,19 +169,20 @@ def pin_bruteforce_fractions(lib, trials: int = 60):
     exact sum of |a||b|."""
     rng = random.Random(1234)
     for trial in range(trials):
-        dt = np.float32 if trial % 2 == 0 else np.float16
+        dt = _dtypes()[trial % 3]
         M, N, K = rng.randint(1, 6), rng.randint(1, 6), rng.randint(1, 6)
         A = _rand(dt, 100 + trial, 0, M, K)
         B = _rand(dt, 100 + trial, 1, K, N)
-        A = A * dt(2.0 ** rng.randint(-6, 6))  # vary magnitudes
+        A = _make(_wide(A) * 2.0 ** rng.randint(-6, 6), dt)  # vary magnitudes
         C, D = oracle.gemm_rows(_padded(A, rng.randint(0, 3)),
                                 _padded(B, rng.randint(0, 3)), lib=lib)
         ce, de = oracle.gemm_entries(A, B, [M - 1], [N - 1], lib=lib)
+        Aw, Bw = _wide(A), _wide(B)
         for i in range(M):
             for j in range(N):
-                exact = sum(_exact_fraction(A[i, k]) * _exact_fraction(B[k, j])
+                exact = sum(_exact_fraction(Aw[i, k]) * _exact_fraction(Bw[k, j])
                             for k in range(K))
-                den = sum(abs(_exact_fraction(A[i, k]) * _exact_fraction(B[k, j]))
+                den = sum(abs(_exact_fraction(Aw[i, k]) * _exact_fraction(Bw[k, j]))
                           for k in range(K))
                 bound = Fraction(K) * Fraction(U64) * den
                 assert abs(Fraction(C[i, j]) - exact) <= bound, (
@@ -171,7 +198,7 @@ def pin_numpy_matmul(lib):
     for dt in _dtypes():
         A = _rand(dt, 0, 0, 256, 256)
         B = _rand(dt, 0, 1, 256, 256)
-        A64, B64 = A.astype(np.float64), B.astype(np.float64)
+        A64, B64 = _wide(A), _wide(B)
         C, D = oracle.gemm_rows(A, B, threads=4, lib=lib)
         ref = A64 @ B64
         den = np.abs(A64) @ np.abs(B64)
@@ -207,6 +234,28 @@ def pin_f16_decode(lib):
             assert got == v and np.signbit(got) == np.signbit(v), f"decode 0x{b:04x}"
 
 
+def pin_bf16_decode(lib):
+    """Exhaustive bfloat16 decode against the binary32 reading of the same
+    16 bits followed by 16 zero bits (bfloat16 is the upper half of a
+    binary32), plus the hand-worked patterns of
+    tests/golden/bfloat16_patterns.txt."""
+    bits = np.arange(65536, dtype=np.uint16)
+    out = np.empty(bits.shape, dtype=np.float64)
+    lib.oracle_bf16_array_to_f64(bits.ctypes.data, out.ctypes.data, bits.size)
+    ref = (bits.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(out), nan), "bf16 NaN patterns"
+    assert np.array_equal(out[~nan], ref[~nan]), "bf16 decoded values"
+    assert np.array_equal(np.signbit(out[~nan]), np.signbit(ref[~nan])), "bf16 signs"
+    for bits_s, val_s in golden_data.rows("bfloat16_patterns.txt"):
+        b, v = int(bits_s, 16), float.fromhex(val_s) if "p" in val_s else float(val_s)
+        got = lib.oracle_bf16_to_f64(b)
+        if np.isnan(v):
+            assert np.isnan(got), f"bf16 decode 0x{b:04x}"
+        else:
+            assert got == v and np.signbit(got) == np.signbit(v), f"bf16 decode 0x{b:04x}"
+
+
 def _decode(lib, bits):
     out = np.empty(bits.shape, dtype=np.float64)
     lib.oracle_f16_array_to_f64(bits.ctypes.data, out.ctypes.data, bits.size)
@@ -238,6 +287,9 @@ def pin_error_metric(lib):
     H[0, 0] = np.float16(1.5)
     rep = oracle.check(H, R, D, 0.3, lib=lib)
     assert rep["max_rel"] == 0.25, "f16 decoded before comparing"
+    Hb = _make(np.array([[1.5, 2.0, 0.0], [4.0, -1.0, 0.0]]), BF16)
+    rep = oracle.check(Hb, R, D, 0.3, lib=lib)
+    assert rep["max_rel"] == 0.25 and rep["worst"] == (0, 0), "bf16 decoded before comparing"
 
 
 # --------------------------------------------------------------------------
@@ -251,11 +303,11 @@ def pin_epilogue_closed_form(lib):
     or a C0 indexed by the output slot instead of the row."""
     for dt in _dtypes():
         M, N, K = 5, 7, 6
-        A, B = np.ones((M, K), dtype=dt), np.ones((K, N), dtype=dt)
+        A, B = _make(np.ones((M, K)), dt), _make(np.ones((K, N)), dt)
         C0 = synth.small_int(31, 2, M, N, -3, 3, dtype=dt)
         bias = (np.arange(N) - 3).astype(np.float32)
         rows = [4, 1]
-        c0 = C0.astype(np.float64)[rows]
+        c0 = _wide(C0)[rows]
         for alpha, beta, act in ((2.0, -1.5, 0), (-1.0, 0.5, 1), (0.5, 0.0, 0)):
             C, D = oracle.gemm_rows_epi(A, B, C0, alpha, beta, bias, act, rows=rows, lib=lib)
             v = alpha * K + beta * c0 + bias[None, :].astype(np.float64)
@@ -271,7 +323,7 @@ def pin_epilogue_reduces_to_plain(lib):
     (C0 full of NaN must not leak in: beta = 0 means C is not read)."""
     for dt in _dtypes():
         A, B = _rand(dt, 41, 0, 9, 13), _rand(dt, 41, 1, 13, 6)
-        C0 = np.full((9, 6), np.nan, dtype=dt)
+        C0 = _make(np.full((9, 6), np.nan), dt)
         C, D = oracle.gemm_rows_epi(A, B, C0, 1.0, 0.0, None, 0, lib=lib)
         Cp, Dp = oracle.gemm_rows(A, B, lib=lib)
         assert np.array_equal(C, Cp) and np.array_equal(D, Dp), "plain special case"
@@ -293,10 +345,11 @@ def pin_epilogue_bruteforce(lib, trials: int = 30):
             alpha, beta = rng.choice([1.0, -0.75, 3.0]), rng.choice([0.0, 0.5, -2.0])
             act = rng.choice([0, 1])
             C, D = oracle.gemm_rows_epi(A, B, C0, alpha, beta, bias, act, lib=lib)
+            Aw, Bw, C0w = _wide(A), _wide(B), _wide(C0)
             for i in range(M):
                 for j in range(N):
-                    s = sum(_exact_fraction(A[i, k]) * _exact_fraction(B[k, j]) for k in range(K))
-                    v = Fraction(alpha) * s + Fraction(beta) * _exact_fraction(C0[i, j]) + \
+                    s = sum(_exact_fraction(Aw[i, k]) * _exact_fraction(Bw[k, j]) for k in range(K))
+                    v = Fraction(alpha) * s + Fraction(beta) * _exact_fraction(C0w[i, j]) + \
                         _exact_fraction(bias[j])
                     if act == 1 and v < 0:
                         v = Fraction(0)
@@ -312,13 +365,13 @@ def pin_bt_identity_permutation(lib):
     column j of C is column p[j] of A; both exact."""
     for dt in _dtypes():
         A = _rand(dt, 51, 0, 7, 9)
-        C, _ = oracle.gemm_rows_bt(A, np.eye(9, dtype=dt), lib=lib)
-        assert np.array_equal(C, A.astype(np.float64)), "Bt = I"
+        C, _ = oracle.gemm_rows_bt(A, _make(np.eye(9), dt), lib=lib)
+        assert np.array_equal(C, _wide(A)), "Bt = I"
         perm = synth.permutation(51, 2, 9)
-        P = np.zeros((9, 9), dtype=dt)
+        P = np.zeros((9, 9))
         P[np.arange(9), perm] = 1
-        C, _ = oracle.gemm_rows_bt(A, P, lib=lib)
-        assert np.array_equal(C, A.astype(np.float64)[:, perm]), "Bt = P"
+        C, _ = oracle.gemm_rows_bt(A, _make(P, dt), lib=lib)
+        assert np.array_equal(C, _wide(A)[:, perm]), "Bt = P"
 
 
 def pin_bt_matches_plain_transpose(lib):
@@ -339,19 +392,20 @@ def pin_bt_rank1(lib):
         M, N, K = 5, 6, 8
         u = synth.small_int(53, 0, M, 1, -3, 3).ravel()
         v = synth.small_int(53, 1, N, 1, -3, 3).ravel()
-        A, Bt = np.zeros((M, K), dtype=dt), np.zeros((N, K), dtype=dt)
+        A, Bt = np.zeros((M, K)), np.zeros((N, K))
         A[:, 2] = u
         Bt[:, 2] = v
-        C, _ = oracle.gemm_rows_bt(A, Bt, lib=lib)
+        A = _make(A, dt)
+        C, _ = oracle.gemm_rows_bt(A, _make(Bt, dt), lib=lib)
         assert np.array_equal(C, np.outer(u, v)), "rank-1 Bt"
-        Bt2 = np.zeros((N, K), dtype=dt)
+        Bt2 = np.zeros((N, K))
         Bt2[:, 3] = v
-        C2, _ = oracle.gemm_rows_bt(A, Bt2, lib=lib)
+        C2, _ = oracle.gemm_rows_bt(A, _make(Bt2, dt), lib=lib)
         assert not np.any(C2), "mismatched k"
 
 
 PINS = [pin_identity, pin_permutation, pin_all_ones, pin_rank1, pin_k0_k1,
-        pin_bruteforce_fractions, pin_numpy_matmul, pin_f16_decode,
+        pin_bruteforce_fractions, pin_numpy_matmul, pin_f16_decode, pin_bf16_decode,
         pin_error_metric, pin_epilogue_closed_form, pin_epilogue_reduces_to_plain,
         pin_epilogue_bruteforce, pin_bt_identity_permutation, pin_bt_matches_plain_transpose,
         pin_bt_rank1]

@@ -30,3 +30,34 @@ def test_bad_arguments(lib):
         oracle.gemm_rows(A, B, rows=[2])
     with pytest.raises(TypeError):
         oracle.gemm_rows(A, B.astype(np.float16))
+
+
+@pytest.mark.parametrize("name,kind", [("f16_rne_halfway.txt", "f16"), ("bf16_rne_halfway.txt", "bf16")])
+def test_rounding_probe_fixtures(lib, name, kind):
+    """The hand-worked output-rounding fixtures: the oracle's exact sums of
+    their A and B are the ties the headers describe, and the stored C
+    patterns are the ties-to-even roundings of those sums (numpy's float16
+    conversion, torch's bfloat16 conversion: library routines)."""
+    import numpy as np
+    import torch
+
+    from dense_gemm_row_amd import synth
+    from tests import golden_data
+    g = {}
+    for r in golden_data.rows(name):
+        g.setdefault(r[0], []).append([int(x, 16) for x in r[2:]])
+    bits = {k: np.array(v, dtype=np.uint16) for k, v in g.items()}
+    view = np.float16 if kind == "f16" else synth.BF16
+    C, _ = oracle.gemm_rows(bits["A"].view(view), bits["B"].view(view), lib=lib)
+    c32 = C.astype(np.float32)
+    assert np.array_equal(c32.astype(np.float64), C), "the sums are exact in FP32"
+    if kind == "f16":
+        rne = c32.astype(np.float16).view(np.uint16)
+        ulp = 2.0 ** -10
+    else:
+        rne = torch.from_numpy(c32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        ulp = 2.0 ** -7
+    assert np.array_equal(rne, bits["C"])
+    # Four of the six sums sit exactly halfway between neighbours on [1, 2).
+    frac = (C - 1.0) / ulp
+    assert np.sum(frac - np.floor(frac) == 0.5) == 4

@@ -38,6 +38,15 @@ MUTANTS = {
     "f16_subnormal": ("mag = ldexp((double)frac, -24);",
                       "mag = ldexp((double)frac, -25);"),
     "f16_sign": ("return sign ? -mag : mag;", "return mag;"),
+    "bf16_bias": ("mag = ldexp((double)(0x80 | frac), expo - 134);",
+                  "mag = ldexp((double)(0x80 | frac), expo - 133);"),
+    "bf16_no_hidden_bit": ("mag = ldexp((double)(0x80 | frac), expo - 134);",
+                           "mag = ldexp((double)frac, expo - 134);"),
+    "bf16_subnormal": ("mag = ldexp((double)frac, -133);", "mag = ldexp((double)frac, -126);"),
+    "bf16_fraction_width": ("const int expo = (h >> 7) & 0xff;\n    const int frac = h & 0x7f;",
+                            "const int expo = (h >> 8) & 0x7f;\n    const int frac = h & 0xff;"),
+    "bf16_decoded_as_f16": ("    if (dtype == ORACLE_BF16)\n        return oracle_bf16_to_f64",
+                            "    if (0)\n        return oracle_bf16_to_f64"),
     "entries_drop_k": ("for (int64_t k = 0; k < K; ++k) {",
                        "for (int64_t k = 0; k + 1 < K; ++k) {"),
     "metric_absolute": ("r = diff / den;", "r = diff;"),

@@ -60,3 +60,30 @@ def test_small_int_range():
 def test_permutation_valid():
     p = synth.permutation(0, 2, 1000)
     assert np.array_equal(np.sort(p), np.arange(1000))
+
+
+def test_to_bf16_rounds_to_nearest_even():
+    """RNE onto bfloat16 against torch's float32 -> bfloat16 conversion (a
+    library routine) on every float32 pattern class the inputs can reach
+    plus the tie cases worked by hand: 1 + 2**-8 is half an ulp above 1
+    (ties to the even 1.0, 0x3F80), 1 + 3 * 2**-8 is half an ulp above
+    1 + 2**-7 (ties to the even 1 + 2**-6, 0x3F82)."""
+    import torch
+    x = np.concatenate([synth.uniform_f32(3, 0, 200, 200).ravel(),
+                        np.array([1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, -(1 + 2.0 ** -8), 0.0, -0.0,
+                                  3.0e38, 1e-40, 2.0 ** -133, 65504.0], dtype=np.float32)])
+    mine = synth.to_bf16(x).view(np.uint16)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(mine, ref)
+    assert int(synth.to_bf16(np.float32(1 + 2.0 ** -8)).view(np.uint16)) == 0x3F80
+    assert int(synth.to_bf16(np.float32(1 + 3 * 2.0 ** -8)).view(np.uint16)) == 0x3F82
+    assert np.array_equal(synth.bf16_to_f32(synth.to_bf16(np.float32(1.5))), np.float32(1.5))
+
+
+def test_bf16_workload_is_rounded_f32():
+    A, B = synth.workload(7, 5, 9, "bf16", seed=2)
+    assert A.dtype == synth.BF16 and A.shape == (7, 9) and B.shape == (9, 5)
+    a32 = synth.uniform_f32(2, 0, 7, 9)
+    assert np.all(np.abs(synth.bf16_to_f32(A) - a32) <= np.abs(a32) * 2.0 ** -8 + 1e-38)
+    ints = synth.small_int(4, 1, 6, 6, dtype=synth.BF16)
+    assert np.array_equal(synth.bf16_to_f32(ints), synth.small_int(4, 1, 6, 6))
