@@ -26,7 +26,10 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_TFLOPS = {"f32": 157.3, "f16": 2516.6}  # MI355X dense matrix peaks
+PEAK_TFLOPS = {"f32": 157.3, "f16": 2516.6, "bf16": 2516.6}  # MI355X dense matrix peaks
+WORKLOAD_NAME = {("f32", "f16"): "sgemm+hgemm"}
+STEP_NAME = {"f32": "SGEMM fp32", "f16": "HGEMM fp16-in fp32-acc fp16-out",
+             "bf16": "BF16 GEMM bf16-in fp32-acc bf16-out"}
 HBM_PEAK_GBS = 8000.0
 
 
@@ -36,9 +39,11 @@ def parse_args():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--size", type=int, default=4096, help="M = N = K")
-    ap.add_argument("--dtypes", default="f32,f16", help="kernels in one step")
+    ap.add_argument("--dtypes", default="f32,f16",
+                    help="kernels in one step (f32, f16, bf16; the headline step is f32,f16)")
     ap.add_argument("--f32-config", default=None, help="force an FP32 variant by name")
     ap.add_argument("--f16-config", default=None, help="force an FP16 variant by name")
+    ap.add_argument("--bf16-config", default=None, help="force a BF16 variant by name")
     ap.add_argument("--order", type=int, default=None, help="force the tile order")
     ap.add_argument("--group-m", type=int, default=None, help="force the band height")
     ap.add_argument("--cpu-budget", type=float, default=20.0,
@@ -60,7 +65,7 @@ def parse_args():
 # Kernel source of each variant family (the traffic figures are tied to it).
 FAMILY_SOURCE = {"dl_f32": "sgemm_dl.hip", "mfma_f32": "sgemm_mfma.hip", "simt_f32": "sgemm_simt.hip",
                  "mfma_f16": "hgemm_mfma.hip", "pipe_f16": "hgemm_pipe.hip",
-                 "tr_f16": "hgemm_tr.hip"}
+                 "tr_f16": "hgemm_tr.hip", "mfma_bf16": "hgemm_mfma.hip", "tr_bf16": "hgemm_tr.hip"}
 
 
 def kernel_digest(variant: str) -> str:
@@ -119,16 +124,32 @@ def main():
     torch.cuda.set_device(dev)
     n = args.size
     kinds = [k for k in args.dtypes.split(",") if k]
+    if not kinds or any(k not in PEAK_TFLOPS for k in kinds):
+        print(f"--dtypes: a comma list of {sorted(PEAK_TFLOPS)}", file=sys.stderr)
+        sys.exit(2)
     flops = 2.0 * n * n * n
 
     # Inputs: i.i.d. uniform[-1, 1) from seed 0 (A stream 0, B stream 1); the
-    # FP16 operands are the RNE roundings of the FP32 ones.
+    # FP16 and BF16 operands are the RNE roundings of the FP32 ones.
     t0 = time.time()
     A32 = synth.uniform_f32(0, synth.STREAM_A, n, n)
     B32 = synth.uniform_f32(0, synth.STREAM_B, n, n)
     host = {"f32": (A32, B32), "f16": (A32.astype(np.float16), B32.astype(np.float16))}
+    if "bf16" in kinds:
+        host["bf16"] = (synth.to_bf16(A32), synth.to_bf16(B32))
     gen_s = time.time() - t0
-    tdt = {"f32": torch.float32, "f16": torch.float16}
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+    dcode = {"f32": gemm.DTYPE_F32, "f16": gemm.DTYPE_F16, "bf16": gemm.DTYPE_BF16}
+
+    def to_dev(x):  # BF16 travels as its bit patterns
+        if x.dtype == synth.BF16:
+            return torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(x).to(dev)
+
+    def from_dev(t):
+        if t.dtype == torch.bfloat16:
+            return t.view(torch.int16).cpu().numpy().view(np.uint16).view(synth.BF16)
+        return t.cpu().numpy()
     devbuf = {}
     if args.bt and args.epilogue:
         print("--bt and --epilogue are separate modes", file=sys.stderr)
@@ -137,12 +158,12 @@ def main():
         A, B = host[k]
         if args.bt:
             B = np.ascontiguousarray(B.T)
-        devbuf[k] = (torch.from_numpy(A).to(dev), torch.from_numpy(B).to(dev),
+        devbuf[k] = (to_dev(A), to_dev(B),
                      torch.empty((n, n), dtype=tdt[k], device=dev))
     cfgs = {}
     for k in kinds:
-        dt = gemm.DTYPE_F32 if k == "f32" else gemm.DTYPE_F16
-        name = args.f32_config if k == "f32" else args.f16_config
+        dt = dcode[k]
+        name = {"f32": args.f32_config, "f16": args.f16_config, "bf16": args.bf16_config}[k]
         c = gemm.config_by_name(dt, name) if name else gemm.gemm_select_config(dt, n, n, n)
         if args.order is not None:
             c.order = args.order
@@ -160,19 +181,18 @@ def main():
         bias_dev = torch.from_numpy(bias_host).to(dev)
         epi = gemm.GemmEpilogue(1.0, 1.0, bias_dev.data_ptr(), gemm.ACT_RELU)
         for k in kinds:
-            C0[k] = synth.uniform_f32(0, 2, n, n).astype(np.float32 if k == "f32" else np.float16)
+            c0 = synth.uniform_f32(0, 2, n, n)
+            C0[k] = c0 if k == "f32" else c0.astype(np.float16) if k == "f16" else synth.to_bf16(c0)
 
     def launch(k):
         a, b, c = devbuf[k]
+        args3 = (n, n, n, a.data_ptr(), n, b.data_ptr(), n, c.data_ptr(), n, sptr, cfgs[k])
         if epi is not None:
-            fn = gemm.gemm_f32_epi if k == "f32" else gemm.gemm_f16_epi
-            st = fn(n, n, n, a.data_ptr(), n, b.data_ptr(), n, c.data_ptr(), n, sptr, cfgs[k], epi)
+            st = gemm.entry(dcode[k], "_epi")(*args3, epi)
         elif args.bt:
-            fn = gemm.gemm_f32_bt if k == "f32" else gemm.gemm_f16_bt
-            st = fn(n, n, n, a.data_ptr(), n, b.data_ptr(), n, c.data_ptr(), n, sptr, cfgs[k])
+            st = gemm.entry(dcode[k], "_bt")(*args3)
         else:
-            fn = gemm.gemm_f32_ex if k == "f32" else gemm.gemm_f16_ex
-            st = fn(n, n, n, a.data_ptr(), n, b.data_ptr(), n, c.data_ptr(), n, sptr, cfgs[k])
+            st = gemm.entry(dcode[k], "_ex")(*args3)
         if st != gemm.GEMM_OK:
             raise gemm.GemmError(st, f"gemm_{k}")
 
@@ -192,7 +212,7 @@ def main():
         # One launch from the known C0 for the parity check; the warmup
         # follows it (the epilogue reads C, so later launches change it).
         for k in kinds:
-            devbuf[k][2].copy_(torch.from_numpy(C0[k]).to(dev))
+            devbuf[k][2].copy_(to_dev(C0[k]))
             launch(k)
     else:
         for _ in range(max(args.warmup, 1)):
@@ -206,17 +226,16 @@ def main():
         rng = np.random.default_rng(1)
         for k in kinds:
             A, B = host[k]
-            C = devbuf[k][2].cpu().numpy()
+            C = from_dev(devbuf[k][2])
             rows = sorted(set([0, n - 1] + rng.integers(0, n, 6).tolist()))
             if epi is not None:
                 ref, den = oracle.gemm_rows_epi(A, B, C0[k], 1.0, 1.0, bias_host, oracle.ACT_RELU,
                                                 rows=rows, threads=min(args.cpu_threads, 16))
-                rep = oracle.check(np.ascontiguousarray(C[rows]), ref, den,
-                                   oracle.SGEMM_TOL if k == "f32" else oracle.HGEMM_TOL)
+                rep = oracle.check(np.ascontiguousarray(C[rows]), ref, den, oracle.TOL[k])
                 parity[k] = {"rows": len(rows), "entries": 0, "tol": rep["tol"],
                              "max_rel": rep["max_rel"], "ok": rep["ok"]}
                 continue
-            tol = oracle.SGEMM_TOL if k == "f32" else oracle.HGEMM_TOL
+            tol = oracle.TOL[k]
             if args.bt:
                 ref, den = oracle.gemm_rows_bt(A, np.ascontiguousarray(B.T), rows=rows)
                 rep = oracle.check(np.ascontiguousarray(C[rows]), ref, den, tol)
@@ -224,7 +243,6 @@ def main():
                              "max_rel": rep["max_rel"], "ok": rep["ok"]}
                 continue
             ref, den = oracle.gemm_rows(A, B, rows=rows, threads=min(args.cpu_threads, 16))
-            tol = oracle.SGEMM_TOL if k == "f32" else oracle.HGEMM_TOL
             rep = oracle.check(np.ascontiguousarray(C[rows]), ref, den, tol)
             ii, jj = rng.integers(0, n, 512), rng.integers(0, n, 512)
             ce, de = oracle.gemm_entries(A, B, ii, jj)
@@ -260,7 +278,7 @@ def main():
     kernels = {}
     for i, k in enumerate(kinds):
         mean = marks[i].elapsed_time(marks[i + 1]) / args.steps
-        elem = 2 if k == "f16" else 4
+        elem = 4 if k == "f32" else 2
         kernels[k] = {
             "variant": cfgs[k].name.decode(), "order": cfgs[k].order, "group_m": cfgs[k].group_m,
             "ms_mean": round(mean, 5),
@@ -303,7 +321,7 @@ def main():
             dt = time.perf_counter() - t1
             spent += dt
             done_flops += 2.0 * rows * n * n
-            parts.append(f"{rows} rows of the {n}^3 {'SGEMM' if k == 'f32' else 'HGEMM'}")
+            parts.append(f"{rows} rows of the {n}^3 {STEP_NAME[k].split(' ')[0]} {k}")
         cpu = {"value": round(done_flops / spent / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
                "kind": "oracle", "seconds": round(spent, 2),
                "sample": " + ".join(parts) + " (FP64 i-k-j oracle, all columns of each row)"}
@@ -323,11 +341,11 @@ def main():
         "vs_baseline": None,
         "dtype": "+".join(kinds),
         "data": "synthetic",
-        "config": {"workload": f"sgemm+hgemm {n}x{n}x{n} row-major, uniform[-1,1) seed 0"
+        "config": {"workload": f"{WORKLOAD_NAME.get(tuple(kinds), '+'.join(kinds) + ' gemm')} "
+                               f"{n}x{n}x{n} row-major, uniform[-1,1) seed 0"
                                + (", fused epilogue relu(AB + C + bias)" if epi is not None else "")
                                + (", B given transposed (N x K)" if args.bt else ""),
-                   "M": n, "N": n, "K": n, "step": " then ".join(
-                       "SGEMM fp32" if k == "f32" else "HGEMM fp16-in fp32-acc fp16-out" for k in kinds)},
+                   "M": n, "N": n, "K": n, "step": " then ".join(STEP_NAME[k] for k in kinds)},
         "kernels": kernels,
         "roofline": roofline(dom),
         "roofline_all": {k: roofline(k) for k in kinds},

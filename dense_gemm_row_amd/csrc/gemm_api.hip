@@ -57,8 +57,16 @@ gemm_status_t fail(gemm_status_t st, const char* fmt, ...) {
   return st;
 }
 
+constexpr int kDtypes = 3;  // F32, F16, BF16
+
+bool valid_dtype(int d) { return d == GEMM_DTYPE_F32 || d == GEMM_DTYPE_F16 || d == GEMM_DTYPE_BF16; }
+
+const char* dtype_name(int d) {
+  return d == GEMM_DTYPE_F32 ? "f32" : d == GEMM_DTYPE_F16 ? "f16" : "bf16";
+}
+
 struct Table {
-  std::vector<Variant> v[2];  // per dtype
+  std::vector<Variant> v[kDtypes];  // per dtype
   Table() {
     int n = 0;
     const Variant* p = sgemm_dl_variants(&n);
@@ -73,7 +81,11 @@ struct Table {
     v[1].insert(v[1].end(), p, p + n);
     p = hgemm_mfma_variants(&n);
     v[1].insert(v[1].end(), p, p + n);
-    for (int d = 0; d < 2; ++d)
+    p = hgemm_tr_variants(&n, true);
+    v[2].insert(v[2].end(), p, p + n);
+    p = hgemm_mfma_variants(&n, true);
+    v[2].insert(v[2].end(), p, p + n);
+    for (int d = 0; d < kDtypes; ++d)
       for (size_t i = 0; i < v[d].size(); ++i) v[d][i].desc.id = (int32_t)i;
   }
 };
@@ -245,7 +257,7 @@ gemm_status_t resolve(int dtype, int64_t M, int64_t N, int64_t K, const gemm_con
   }
   if (forced->id < 0 || forced->id >= (int32_t)v.size())
     return fail(GEMM_ERR_UNSUPPORTED, "config id %d not in the %s table", forced->id,
-                dtype == GEMM_DTYPE_F32 ? "f32" : "f16");
+                dtype_name(dtype));
   if (forced->order < GEMM_ORDER_ROW || forced->order > GEMM_ORDER_XCD || forced->group_m < 1)
     return fail(GEMM_ERR_UNSUPPORTED, "bad tile order %d / group_m %d", forced->order,
                 forced->group_m);
@@ -286,9 +298,10 @@ bool vector_path(int dtype, const void* A, int64_t lda, const void* B, int64_t l
          ldc % w == 0 && K % w == 0 && N % w == 0;
 }
 
-Params make_params(const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc,
-                   int64_t M, int64_t N, int64_t K) {
+Params make_params(int dtype, const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
+                   int64_t ldc, int64_t M, int64_t N, int64_t K) {
   Params p;
+  p.bf16 = dtype == GEMM_DTYPE_BF16;
   p.A = A;
   p.B = B;
   p.C = C;
@@ -304,7 +317,7 @@ Params make_params(const void* A, int64_t lda, const void* B, int64_t ldb, void*
 gemm_status_t launch_plain(int dtype, const gemm_config_t& cfg, int64_t M, int64_t N, int64_t K,
                            const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
                            int64_t ldc, void* stream) {
-  const Params p = make_params(A, lda, B, ldb, C, ldc, M, N, K);
+  const Params p = make_params(dtype, A, lda, B, ldb, C, ldc, M, N, K);
   const bool vec = vector_path(dtype, A, lda, B, ldb, C, ldc, K, N);
   const TileMap map = make_map(cfg, M, N);
   const hipError_t e = table().v[dtype][cfg.id].launch(p, map, vec, static_cast<hipStream_t>(stream));
@@ -335,7 +348,7 @@ gemm_status_t run_bt(int dtype, int64_t M, int64_t N, int64_t K, const void* A, 
   st = resolve(dtype, M, N, K, forced, false, cfg, false, true);
   if (st != GEMM_OK) return st;
   if (M == 0 || N == 0) return GEMM_OK;
-  Params p = make_params(A, lda, Bt, ldbt, C, ldc, M, N, K);
+  Params p = make_params(dtype, A, lda, Bt, ldbt, C, ldc, M, N, K);
   p.bt = true;
   const bool vec = vector_path(dtype, A, lda, Bt, ldbt, C, ldc, K, N);
   const TileMap map = make_map(cfg, M, N);
@@ -361,7 +374,7 @@ gemm_status_t run_epi(int dtype, int64_t M, int64_t N, int64_t K, const void* A,
   st = resolve(dtype, M, N, K, forced, false, cfg, true);
   if (st != GEMM_OK) return st;
   if (M == 0 || N == 0) return GEMM_OK;
-  Params p = make_params(A, lda, B, ldb, C, ldc, M, N, K);
+  Params p = make_params(dtype, A, lda, B, ldb, C, ldc, M, N, K);
   p.epi.on = true;
   p.epi.alpha = epi->alpha;
   p.epi.beta = epi->beta;
@@ -405,7 +418,7 @@ gemm_status_t run_splitk(int dtype, int64_t M, int64_t N, int64_t K, const void*
       overlap(ws, (size_t)need, B, span_bytes(K, N, ldb, es)) ||
       overlap(ws, (size_t)need, C, span_bytes(M, N, ldc, es)))
     return fail(GEMM_ERR_ALIAS, "workspace overlaps A, B or C");
-  Params p = make_params(A, lda, B, ldb, ws, N, M, N, K);
+  Params p = make_params(dtype, A, lda, B, ldb, ws, N, M, N, K);
   p.splits = (int)S;
   p.kc = (int)Kc;
   p.c_stride = M * N;
@@ -437,6 +450,12 @@ gemm_status_t gemm_f16(int64_t M, int64_t N, int64_t K, const gemm_f16_t* A, int
   return run(GEMM_DTYPE_F16, M, N, K, A, lda, B, ldb, C, ldc, stream, nullptr);
 }
 
+gemm_status_t gemm_bf16(int64_t M, int64_t N, int64_t K, const gemm_bf16_t* A, int64_t lda,
+                        const gemm_bf16_t* B, int64_t ldb, gemm_bf16_t* C, int64_t ldc,
+                        void* stream) {
+  return run(GEMM_DTYPE_BF16, M, N, K, A, lda, B, ldb, C, ldc, stream, nullptr);
+}
+
 gemm_status_t gemm_f32_ex(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
                           const float* B, int64_t ldb, float* C, int64_t ldc, void* stream,
                           const gemm_config_t* cfg) {
@@ -451,6 +470,13 @@ gemm_status_t gemm_f16_ex(int64_t M, int64_t N, int64_t K, const gemm_f16_t* A, 
   return run(GEMM_DTYPE_F16, M, N, K, A, lda, B, ldb, C, ldc, stream, cfg);
 }
 
+gemm_status_t gemm_bf16_ex(int64_t M, int64_t N, int64_t K, const gemm_bf16_t* A, int64_t lda,
+                           const gemm_bf16_t* B, int64_t ldb, gemm_bf16_t* C, int64_t ldc,
+                           void* stream, const gemm_config_t* cfg) {
+  if (!cfg) return fail(GEMM_ERR_INVALID_ARG, "cfg is NULL");
+  return run(GEMM_DTYPE_BF16, M, N, K, A, lda, B, ldb, C, ldc, stream, cfg);
+}
+
 gemm_status_t gemm_f32_bt(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
                           const float* Bt, int64_t ldbt, float* C, int64_t ldc, void* stream,
                           const gemm_config_t* cfg) {
@@ -463,6 +489,12 @@ gemm_status_t gemm_f16_bt(int64_t M, int64_t N, int64_t K, const gemm_f16_t* A, 
   return run_bt(GEMM_DTYPE_F16, M, N, K, A, lda, Bt, ldbt, C, ldc, stream, cfg);
 }
 
+gemm_status_t gemm_bf16_bt(int64_t M, int64_t N, int64_t K, const gemm_bf16_t* A, int64_t lda,
+                           const gemm_bf16_t* Bt, int64_t ldbt, gemm_bf16_t* C, int64_t ldc,
+                           void* stream, const gemm_config_t* cfg) {
+  return run_bt(GEMM_DTYPE_BF16, M, N, K, A, lda, Bt, ldbt, C, ldc, stream, cfg);
+}
+
 gemm_status_t gemm_f32_epi(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
                            const float* B, int64_t ldb, float* C, int64_t ldc, void* stream,
                            const gemm_config_t* cfg, const gemm_epilogue_t* epi) {
@@ -473,6 +505,12 @@ gemm_status_t gemm_f16_epi(int64_t M, int64_t N, int64_t K, const gemm_f16_t* A,
                            const gemm_f16_t* B, int64_t ldb, gemm_f16_t* C, int64_t ldc,
                            void* stream, const gemm_config_t* cfg, const gemm_epilogue_t* epi) {
   return run_epi(GEMM_DTYPE_F16, M, N, K, A, lda, B, ldb, C, ldc, stream, cfg, epi);
+}
+
+gemm_status_t gemm_bf16_epi(int64_t M, int64_t N, int64_t K, const gemm_bf16_t* A, int64_t lda,
+                            const gemm_bf16_t* B, int64_t ldb, gemm_bf16_t* C, int64_t ldc,
+                            void* stream, const gemm_config_t* cfg, const gemm_epilogue_t* epi) {
+  return run_epi(GEMM_DTYPE_BF16, M, N, K, A, lda, B, ldb, C, ldc, stream, cfg, epi);
 }
 
 gemm_status_t gemm_f32_splitk(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
@@ -490,8 +528,16 @@ gemm_status_t gemm_f16_splitk(int64_t M, int64_t N, int64_t K, const gemm_f16_t*
                     stream, cfg);
 }
 
+gemm_status_t gemm_bf16_splitk(int64_t M, int64_t N, int64_t K, const gemm_bf16_t* A,
+                               int64_t lda, const gemm_bf16_t* B, int64_t ldb, gemm_bf16_t* C,
+                               int64_t ldc, void* workspace, int64_t workspace_bytes, void* stream,
+                               const gemm_config_t* cfg) {
+  return run_splitk(GEMM_DTYPE_BF16, M, N, K, A, lda, B, ldb, C, ldc, workspace, workspace_bytes,
+                    stream, cfg);
+}
+
 int64_t gemm_splitk_workspace_bytes(int32_t dtype, int64_t M, int64_t N, int64_t K, int32_t splits) {
-  if ((dtype != GEMM_DTYPE_F32 && dtype != GEMM_DTYPE_F16) || M < 0 || N < 0 || K < 0) return -1;
+  if (!valid_dtype(dtype) || M < 0 || N < 0 || K < 0) return -1;
   if (splits <= 0) splits = select(dtype, M, N, K, true).splits;
   int64_t S, Kc;
   split_shape(K, splits, S, Kc);
@@ -500,7 +546,7 @@ int64_t gemm_splitk_workspace_bytes(int32_t dtype, int64_t M, int64_t N, int64_t
 
 gemm_status_t gemm_select_splitk_config(int32_t dtype, int64_t M, int64_t N, int64_t K,
                                         gemm_config_t* out) {
-  if (dtype != GEMM_DTYPE_F32 && dtype != GEMM_DTYPE_F16)
+  if (!valid_dtype(dtype))
     return fail(GEMM_ERR_INVALID_ARG, "unknown dtype %d", dtype);
   if (!out || M < 0 || N < 0 || K < 0) return fail(GEMM_ERR_INVALID_ARG, "bad arguments");
   *out = select(dtype, M, N, K, true);
@@ -508,12 +554,12 @@ gemm_status_t gemm_select_splitk_config(int32_t dtype, int64_t M, int64_t N, int
 }
 
 int32_t gemm_num_configs(int32_t dtype) {
-  if (dtype != GEMM_DTYPE_F32 && dtype != GEMM_DTYPE_F16) return 0;
+  if (!valid_dtype(dtype)) return 0;
   return (int32_t)table().v[dtype].size();
 }
 
 gemm_status_t gemm_get_config(int32_t dtype, int32_t idx, gemm_config_t* out) {
-  if (dtype != GEMM_DTYPE_F32 && dtype != GEMM_DTYPE_F16)
+  if (!valid_dtype(dtype))
     return fail(GEMM_ERR_INVALID_ARG, "unknown dtype %d", dtype);
   if (!out) return fail(GEMM_ERR_INVALID_ARG, "out is NULL");
   const auto& v = table().v[dtype];
@@ -524,7 +570,7 @@ gemm_status_t gemm_get_config(int32_t dtype, int32_t idx, gemm_config_t* out) {
 
 gemm_status_t gemm_select_config(int32_t dtype, int64_t M, int64_t N, int64_t K,
                                  gemm_config_t* out) {
-  if (dtype != GEMM_DTYPE_F32 && dtype != GEMM_DTYPE_F16)
+  if (!valid_dtype(dtype))
     return fail(GEMM_ERR_INVALID_ARG, "unknown dtype %d", dtype);
   if (!out || M < 0 || N < 0 || K < 0) return fail(GEMM_ERR_INVALID_ARG, "bad arguments");
   *out = select(dtype, M, N, K);
@@ -546,7 +592,7 @@ gemm_status_t gemm_tile_of_block(const gemm_config_t* cfg, int64_t M, int64_t N,
 }
 
 gemm_status_t gemm_layout_check(int32_t dtype, int32_t idx, int32_t banks, int64_t out[2]) {
-  if (dtype != GEMM_DTYPE_F32 && dtype != GEMM_DTYPE_F16)
+  if (!valid_dtype(dtype))
     return fail(GEMM_ERR_INVALID_ARG, "unknown dtype %d", dtype);
   const auto& v = table().v[dtype];
   if (idx < 0 || idx >= (int32_t)v.size() || !out || banks <= 0 || banks > 64 || (banks & (banks - 1)))
@@ -575,7 +621,9 @@ gemm_status_t gemm_load_tuning(const char* path) {
         fclose(f);
         return fail(GEMM_ERR_INVALID_ARG, "%s:%d: expected 'dtype M N K name order group_m [splits]'", path, lineno);
       }
-      const int dtype = strcmp(dt, "f32") == 0 ? 0 : strcmp(dt, "f16") == 0 ? 1 : -1;
+      int dtype = -1;
+      for (int d = 0; d < kDtypes; ++d)
+        if (strcmp(dt, dtype_name(d)) == 0) dtype = d;
       const int id = dtype < 0 ? -1 : find_by_name(dtype, name);
       if (id < 0 || order < GEMM_ORDER_ROW || order > GEMM_ORDER_XCD || gm < 1 || splits < 1) {
         fclose(f);

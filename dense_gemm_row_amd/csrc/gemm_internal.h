@@ -9,6 +9,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "gemm.h"
 
 namespace gemm {
@@ -52,7 +54,45 @@ struct Params {
   // ldb), i.e. column-major B.  Kernels without such a form ignore it and
   // must not be launched with it.
   bool bt = false;
+  // 16-bit kernels: A, B and C (and the old C read by the fused epilogue)
+  // hold bfloat16 instead of binary16.  The general FP16 kernel reads it at
+  // launch; the LDS-direct kernels have it in their template instead.
+  bool bf16 = false;
 };
+
+// ---------------------------------------------------------------------------
+// The two 16-bit element types of the half-precision kernels: binary16
+// (_Float16) and bfloat16 (__bf16, the upper half of a binary32).  Both
+// enter the matrix cores as 8-element operands of v_mfma_f32_32x32x16_*
+// (FP32 accumulation) and leave through one round-to-nearest-even
+// conversion per output.  Operands travel as _Float16 vectors either way
+// (the bits are what matter) and are reinterpreted for the bf16 form.
+// ---------------------------------------------------------------------------
+template <bool BF>
+using half_t = std::conditional_t<BF, __bf16, _Float16>;
+typedef _Float16 h16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 b16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+template <bool BF>
+__device__ __forceinline__ f32x16_t mfma16(h16x8_t a, h16x8_t b, f32x16_t c) {
+  if constexpr (BF)
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(b16x8_t, a),
+                                                    __builtin_bit_cast(b16x8_t, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+// float -> 16-bit pattern, rounded to nearest even (v_cvt_f16_f32 or
+// v_cvt_pk_bf16_f32), and the exact widening back.
+template <bool BF>
+__device__ __forceinline__ unsigned short round16(float x) {
+  return __builtin_bit_cast(unsigned short, static_cast<half_t<BF>>(x));
+}
+template <bool BF>
+__device__ __forceinline__ float widen16(unsigned short h) {
+  return static_cast<float>(__builtin_bit_cast(half_t<BF>, h));
+}
 
 // Workgroup -> output tile order.  See gemm_order_t in gemm.h.
 struct TileMap {
@@ -175,13 +215,16 @@ struct Variant {
 const Variant* sgemm_dl_variants(int* count);
 const Variant* sgemm_mfma_variants(int* count);
 const Variant* sgemm_simt_variants(int* count);
-const Variant* hgemm_mfma_variants(int* count);
+// The 16-bit families register a binary16 table and, where they have a
+// bfloat16 form, a bfloat16 one (bf16 = true; count 0 when there is none).
+const Variant* hgemm_mfma_variants(int* count, bool bf16 = false);
 const Variant* hgemm_pipe_variants(int* count);
-const Variant* hgemm_tr_variants(int* count);
+const Variant* hgemm_tr_variants(int* count, bool bf16 = false);
 
-// Launch the general FP16 kernel (any alignment, 64-bit addressing) with
-// the given workgroup tile (and the given wave tile when it has one); used
-// by the pipelined variants for operands they do not take.
+// Launch the general 16-bit kernel (any alignment, 64-bit addressing; FP16
+// or, with p.bf16, BF16) with the given workgroup tile (and the given wave
+// tile when it has one); used by the pipelined variants for operands they
+// do not take.
 hipError_t hgemm_launch_shape(int bm, int bn, int wm, int wn, const Params& p, const TileMap& map,
                               bool vec, hipStream_t stream);
 // The same for FP32: the general SGEMM kernel (sgemm_mfma.hip) with the given
@@ -190,8 +233,8 @@ hipError_t sgemm_launch_shape(int bm, int bn, int wm, int wn, const Params& p, c
                               bool vec, hipStream_t stream);
 
 // Split-K reduction: C[i][j] = sum over s < S (in order) of
-// W[s*M*N + i*N + j], written as FP32 (dtype F32) or FP16 rounded to nearest
-// even (dtype F16).  Enqueued on `stream`.
+// W[s*M*N + i*N + j], written as FP32 (dtype F32), or as FP16 (dtype F16)
+// or BF16 (dtype BF16) rounded to nearest even.  Enqueued on `stream`.
 hipError_t splitk_reduce(int dtype, const float* W, int S, int M, int N, void* C, int64_t ldc,
                          hipStream_t stream);
 

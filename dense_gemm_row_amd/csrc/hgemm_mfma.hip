@@ -73,19 +73,12 @@ struct Shape {
   }
 };
 
-__device__ inline f32x16 mfma(f16x8 a, f16x8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
-}
-
-__device__ inline unsigned short f16_bits(float x) {
-  // v_cvt_f16_f32: round to nearest even (checked on the device).
-  return __builtin_bit_cast(unsigned short, static_cast<_Float16>(x));
-}
-
 // BT: B given transposed (p.bt: Bt, N x K row-major).  Its rows are already
 // k-contiguous per output column, so they are staged like A's chunks into
-// the transposed B tile (no register transpose).
-template <int BM, int BN, int WM, int WN, bool VEC, bool EPI, bool BT>
+// the transposed B tile (no register transpose).  BF: the elements are
+// bfloat16 (v_mfma_f32_32x32x16_bf16 and bfloat16 conversions; the staging
+// moves 16-bit patterns either way).
+template <int BM, int BN, int WM, int WN, bool VEC, bool EPI, bool BT, bool BF>
 __global__ void __launch_bounds__((Shape<BM, BN, WM, WN>::NT))
 hgemm_mfma_kernel(Params p, TileMap map) {
   using S = Shape<BM, BN, WM, WN>;
@@ -265,25 +258,24 @@ hgemm_mfma_kernel(Params p, TileMap map) {
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-          for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = mfma(a[mb], b[nb], acc[mb][nb]);
+          for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = mfma16<BF>(a[mb], b[nb], acc[mb][nb]);
       }
       if (t + 1 < T) store_slice(cur ^ 1);
       __syncthreads();
     }
   }
 
-  // Epilogue: FP32 -> FP16 (RNE), NB adjacent columns per lane and row.
-  // EPI: the fused epilogue (alpha, beta with the old FP16 C, bias,
+  // Epilogue: FP32 -> FP16 or BF16 (RNE), NB adjacent columns per lane and
+  // row.  EPI: the fused epilogue (alpha, beta with the old 16-bit C, bias,
   // activation) in FP32 before the one rounding.
   const int col = n0 + wn0 + NB * lrow;
   auto out = [&](int mb, int nb, int r, const unsigned short* dst) -> unsigned short {
     if constexpr (!EPI) {
-      return f16_bits(acc[mb][nb][r]);
+      return round16<BF>(acc[mb][nb][r]);
     } else {
-      const float c_old =
-          p.epi.beta != 0.f ? (float)__builtin_bit_cast(_Float16, dst[nb]) : 0.f;
+      const float c_old = p.epi.beta != 0.f ? widen16<BF>(dst[nb]) : 0.f;
       const float bias = p.epi.bias ? p.epi.bias[col + nb] : 0.f;
-      return f16_bits(epi_value(p.epi, acc[mb][nb][r], c_old, bias));
+      return round16<BF>(epi_value(p.epi, acc[mb][nb][r], c_old, bias));
     }
   };
 #pragma unroll
@@ -315,28 +307,35 @@ hgemm_mfma_kernel(Params p, TileMap map) {
   }
 }
 
-template <int BM, int BN, int WM, int WN>
-hipError_t launch(const Params& p, const TileMap& map, bool vec, hipStream_t stream) {
+template <int BM, int BN, int WM, int WN, bool BF>
+hipError_t launch_typed(const Params& p, const TileMap& map, bool vec, hipStream_t stream) {
   using S = Shape<BM, BN, WM, WN>;
   const dim3 grid(map.tiles_m * map.tiles_n), block(S::NT);
   if (p.bt) {  // transposed B (the fused epilogue is not combined with it)
     if (p.epi.on) return hipErrorNotSupported;
     if (vec)
-      hipLaunchKernelGGL((hgemm_mfma_kernel<BM, BN, WM, WN, true, false, true>), grid, block, 0, stream, p, map);
+      hipLaunchKernelGGL((hgemm_mfma_kernel<BM, BN, WM, WN, true, false, true, BF>), grid, block, 0, stream, p, map);
     else
-      hipLaunchKernelGGL((hgemm_mfma_kernel<BM, BN, WM, WN, false, false, true>), grid, block, 0, stream, p, map);
+      hipLaunchKernelGGL((hgemm_mfma_kernel<BM, BN, WM, WN, false, false, true, BF>), grid, block, 0, stream, p, map);
   } else if (p.epi.on) {
     if (vec)
-      hipLaunchKernelGGL((hgemm_mfma_kernel<BM, BN, WM, WN, true, true, false>), grid, block, 0, stream, p, map);
+      hipLaunchKernelGGL((hgemm_mfma_kernel<BM, BN, WM, WN, true, true, false, BF>), grid, block, 0, stream, p, map);
     else
-      hipLaunchKernelGGL((hgemm_mfma_kernel<BM, BN, WM, WN, false, true, false>), grid, block, 0, stream, p, map);
+      hipLaunchKernelGGL((hgemm_mfma_kernel<BM, BN, WM, WN, false, true, false, BF>), grid, block, 0, stream, p, map);
   } else {
     if (vec)
-      hipLaunchKernelGGL((hgemm_mfma_kernel<BM, BN, WM, WN, true, false, false>), grid, block, 0, stream, p, map);
+      hipLaunchKernelGGL((hgemm_mfma_kernel<BM, BN, WM, WN, true, false, false, BF>), grid, block, 0, stream, p, map);
     else
-      hipLaunchKernelGGL((hgemm_mfma_kernel<BM, BN, WM, WN, false, false, false>), grid, block, 0, stream, p, map);
+      hipLaunchKernelGGL((hgemm_mfma_kernel<BM, BN, WM, WN, false, false, false, BF>), grid, block, 0, stream, p, map);
   }
   return hipGetLastError();
+}
+
+// One launch function for both element types: p.bf16 picks the instance.
+template <int BM, int BN, int WM, int WN>
+hipError_t launch(const Params& p, const TileMap& map, bool vec, hipStream_t stream) {
+  return p.bf16 ? launch_typed<BM, BN, WM, WN, true>(p, map, vec, stream)
+                : launch_typed<BM, BN, WM, WN, false>(p, map, vec, stream);
 }
 
 // Host replay of one K slice's LDS accesses (see the FP32 kernel).
@@ -409,22 +408,24 @@ int layout_check(int banks, int64_t out[2]) {
   return 0;
 }
 
-#define HGEMM_MFMA_VARIANT(BM, BN, WM, WN, EFF)                                                 \
+#define HGEMM_MFMA_VARIANT(DT, TAG, BM, BN, WM, WN, EFF)                                        \
   Variant {                                                                                  \
-    gemm_config_t{0, GEMM_DTYPE_F16, GEMM_FAMILY_MFMA, BM, BN, BK, WM, WN,                   \
+    gemm_config_t{0, DT, GEMM_FAMILY_MFMA, BM, BN, BK, WM, WN,                               \
                   Shape<BM, BN, WM, WN>::NT, 2, Shape<BM, BN, WM, WN>::LDS_BYTES,            \
-                  GEMM_ORDER_XCD, 4, 1, "mfma_f16_" #BM "x" #BN "x64_w" #WM "x" #WN},           \
+                  GEMM_ORDER_XCD, 4, 1, "mfma_" TAG "_" #BM "x" #BN "x64_w" #WM "x" #WN},     \
         &launch<BM, BN, WM, WN>, &layout_check<BM, BN, WM, WN>, nullptr, EFF,                \
         &launch<BM, BN, WM, WN>, &launch<BM, BN, WM, WN>                                     \
   }
 
-const Variant kVariants[] = {
-    HGEMM_MFMA_VARIANT(256, 256, 128, 128, 0.80f),
-    HGEMM_MFMA_VARIANT(256, 128, 128, 64, 0.72f),
-    HGEMM_MFMA_VARIANT(128, 256, 64, 128, 0.72f),
-    HGEMM_MFMA_VARIANT(128, 128, 64, 64, 0.60f),
-    HGEMM_MFMA_VARIANT(64, 64, 32, 32, 0.20f),
-};
+#define HGEMM_MFMA_TABLE(DT, TAG)                                \
+  {HGEMM_MFMA_VARIANT(DT, TAG, 256, 256, 128, 128, 0.80f),       \
+   HGEMM_MFMA_VARIANT(DT, TAG, 256, 128, 128, 64, 0.72f),        \
+   HGEMM_MFMA_VARIANT(DT, TAG, 128, 256, 64, 128, 0.72f),        \
+   HGEMM_MFMA_VARIANT(DT, TAG, 128, 128, 64, 64, 0.60f),         \
+   HGEMM_MFMA_VARIANT(DT, TAG, 64, 64, 32, 32, 0.20f)}
+
+const Variant kVariants[] = HGEMM_MFMA_TABLE(GEMM_DTYPE_F16, "f16");
+const Variant kVariantsBf[] = HGEMM_MFMA_TABLE(GEMM_DTYPE_BF16, "bf16");
 
 }  // namespace
 
@@ -432,6 +433,7 @@ hipError_t hgemm_launch_shape(int bm, int bn, int wm, int wn, const Params& p, c
                               bool vec, hipStream_t stream) {
   // The tile map depends on the workgroup tile only: any wave split of the
   // same bm x bn tile computes the same tiles.  Prefer the same wave tile.
+  // (The launch reads p.bf16, so the binary16 table serves both types.)
   const Variant* pick = nullptr;
   for (const Variant& v : kVariants)
     if (v.desc.bm == bm && v.desc.bn == bn && (!pick || (v.desc.wm == wm && v.desc.wn == wn)))
@@ -439,9 +441,10 @@ hipError_t hgemm_launch_shape(int bm, int bn, int wm, int wn, const Params& p, c
   return pick ? pick->launch(p, map, vec, stream) : hipErrorInvalidValue;
 }
 
-const Variant* hgemm_mfma_variants(int* count) {
-  *count = sizeof(kVariants) / sizeof(kVariants[0]);
-  return kVariants;
+const Variant* hgemm_mfma_variants(int* count, bool bf16) {
+  *count = bf16 ? sizeof(kVariantsBf) / sizeof(kVariantsBf[0])
+                : sizeof(kVariants) / sizeof(kVariants[0]);
+  return bf16 ? kVariantsBf : kVariants;
 }
 
 }  // namespace gemm

@@ -1,6 +1,9 @@
 // FP16 HGEMM for aligned operands, built around gfx950's LDS-direct loads and
 // LDS transpose reads: binary16 A and B, FP32 accumulation on
 // v_mfma_f32_32x32x16_f16, one round-to-nearest-even conversion per output.
+// The same kernel, with v_mfma_f32_32x32x16_bf16 and bfloat16 conversions,
+// is the BF16 GEMM (Shape's BF_): the data path moves 16-bit patterns and
+// never looks inside them.
 //
 // Data path per K slice (no VGPR staging, no VALU in the main loop):
 // * A and B move from global memory straight into LDS with
@@ -81,11 +84,13 @@ __device__ __forceinline__ void static_for(F&& f, std::integer_sequence<int, I..
 // partials; 2 the form with the fused epilogue (alpha, beta, bias,
 // activation).  BT_: B is given transposed (Bt, N x K row-major, i.e.
 // column-major B); its tile is then staged and read exactly like A's (one
-// LDS row per output column, k contiguous), with no transpose read.
-template <int BM_, int BN_, int WM_, int WN_, int BK_, int NS_, int MODE_ = 0, bool BT_ = false>
+// LDS row per output column, k contiguous), with no transpose read.  BF_:
+// the elements are bfloat16.
+template <int BM_, int BN_, int WM_, int WN_, int BK_, int NS_, int MODE_ = 0, bool BT_ = false,
+          bool BF_ = false>
 struct Shape {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BK_, NS = NS_;
-  static constexpr bool PARTIAL = MODE_ == 1, EPI = MODE_ == 2, BT = BT_;
+  static constexpr bool PARTIAL = MODE_ == 1, EPI = MODE_ == 2, BT = BT_, BF = BF_;
   static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN, NW = WAVES_M * WAVES_N;
   static constexpr int NT = NW * 64;
   static constexpr int MB = WM / 32, NB = WN / 32, KS = BK / 16;
@@ -178,14 +183,6 @@ struct Shape {
     return m * ROW32 + 16 * (q ^ (m % CPR32));
   }
 };
-
-__device__ inline f32x16 mfma(f16x8 a, f16x8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
-}
-
-__device__ inline unsigned short f16_bits(float x) {
-  return __builtin_bit_cast(unsigned short, static_cast<_Float16>(x));
-}
 
 __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const unsigned char* base, int64_t bytes) {
   // Raw buffer (stride 0); num_records in bytes; loads past it return 0.
@@ -388,7 +385,7 @@ hgemm_tr_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) acc[nb][mb] = mfma(fb[buf][nb], fa[buf][mb], acc[nb][mb]);
+      for (int mb = 0; mb < MB; ++mb) acc[nb][mb] = mfma16<S::BF>(fb[buf][nb], fa[buf][mb], acc[nb][mb]);
   };
 
   // (The lambdas are forced inline: an out-of-line call would move the
@@ -510,7 +507,8 @@ hgemm_tr_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
     // beta with the old FP16 C (read only when beta != 0), bias and the
     // activation, rounds once and stores 8 bytes: 32 lanes per 256-byte row
     // segment, coalesced like the plain epilogue.
-    typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+    typedef half_t<S::BF> H;
+    typedef H h16x4 __attribute__((ext_vector_type(4)));
     typedef int v2i __attribute__((ext_vector_type(2)));
     const __amdgpu_buffer_rsrc_t rc =
         make_rsrc(static_cast<const unsigned char*>(p.C), ((int64_t)(M - 1) * p.ldc + N) * 2);
@@ -562,10 +560,10 @@ hgemm_tr_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
         }
 #pragma unroll
         for (int i = 0; i < BATCH; ++i) {
-          const f16x4 c = __builtin_bit_cast(f16x4, c_old[i]);
-          f16x4 h;
+          const h16x4 c = __builtin_bit_cast(h16x4, c_old[i]);
+          h16x4 h;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) h[e] = (_Float16)epi_value(p.epi, v[i][e], (float)c[e], bias[e]);
+          for (int e = 0; e < 4; ++e) h[e] = (H)epi_value(p.epi, v[i][e], (float)c[e], bias[e]);
           __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2i, h), rc, off[i], 0, 0);
         }
       }
@@ -579,8 +577,10 @@ hgemm_tr_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
 #pragma unroll
       for (int rq = 0; rq < 4; ++rq) {
         uint2 v;
-        v.x = f16_bits(acc[nb][mb][4 * rq + 0]) | ((unsigned)f16_bits(acc[nb][mb][4 * rq + 1]) << 16);
-        v.y = f16_bits(acc[nb][mb][4 * rq + 2]) | ((unsigned)f16_bits(acc[nb][mb][4 * rq + 3]) << 16);
+        v.x = round16<S::BF>(acc[nb][mb][4 * rq + 0]) |
+              ((unsigned)round16<S::BF>(acc[nb][mb][4 * rq + 1]) << 16);
+        v.y = round16<S::BF>(acc[nb][mb][4 * rq + 2]) |
+              ((unsigned)round16<S::BF>(acc[nb][mb][4 * rq + 3]) << 16);
         const int row = 32 * mb + l % 32, slot = 8 * nb + 2 * rq + l / 32;
         *reinterpret_cast<uint2*>(ep[row / S::RPA] + S::epi_byte(row % S::RPA, slot)) = v;
       }
@@ -826,32 +826,38 @@ int layout_check(int banks, int64_t out[2]) {
   return 0;
 }
 
-#define HGEMM_TR_VARIANT(BM, BN, WM, WN, BK, NS, EFF)                                             \
+#define HGEMM_TR_VARIANT(BF, DT, TAG, BM, BN, WM, WN, BK, NS, EFF)                               \
   Variant {                                                                                  \
-    gemm_config_t{0, GEMM_DTYPE_F16, GEMM_FAMILY_MFMA, BM, BN, BK, WM, WN,                   \
+    gemm_config_t{0, DT, GEMM_FAMILY_MFMA, BM, BN, BK, WM, WN,                               \
                   Shape<BM, BN, WM, WN, BK, NS>::NT, NS, Shape<BM, BN, WM, WN, BK, NS>::LDS_BYTES, \
                   GEMM_ORDER_XCD, 4, 1,                                                      \
-                  "tr_f16_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_s" #NS},                  \
-        &launch<Shape<BM, BN, WM, WN, BK, NS>>, &layout_check<Shape<BM, BN, WM, WN, BK, NS>>, \
-        &launch<Shape<BM, BN, WM, WN, BK, NS, 1>>, EFF,                                     \
-        &launch<Shape<BM, BN, WM, WN, BK, NS, 2>>,                                          \
-        &launch<Shape<BM, BN, WM, WN, BK, NS, 0, true>>                                     \
+                  "tr_" TAG "_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_s" #NS},              \
+        &launch<Shape<BM, BN, WM, WN, BK, NS, 0, false, BF>>,                                \
+        &layout_check<Shape<BM, BN, WM, WN, BK, NS>>,                                        \
+        &launch<Shape<BM, BN, WM, WN, BK, NS, 1, false, BF>>, EFF,                           \
+        &launch<Shape<BM, BN, WM, WN, BK, NS, 2, false, BF>>,                                \
+        &launch<Shape<BM, BN, WM, WN, BK, NS, 0, true, BF>>                                  \
   }
 
-const Variant kVariants[] = {
-    HGEMM_TR_VARIANT(256, 256, 128, 128, 64, 2, 1.00f),
-    HGEMM_TR_VARIANT(256, 256, 128, 128, 32, 4, 0.99f),
-    HGEMM_TR_VARIANT(256, 256, 128, 128, 32, 5, 0.99f),
-    HGEMM_TR_VARIANT(256, 128, 128, 64, 64, 3, 0.90f),
-    HGEMM_TR_VARIANT(128, 256, 64, 128, 64, 3, 0.89f),
-    HGEMM_TR_VARIANT(128, 128, 64, 64, 64, 2, 0.71f),
-};
+// The LDS layouts and the data path do not depend on the element type, so
+// both tables share the layout checks and the measured tile efficiencies.
+#define HGEMM_TR_TABLE(BF, DT, TAG)                                   \
+  {HGEMM_TR_VARIANT(BF, DT, TAG, 256, 256, 128, 128, 64, 2, 1.00f), \
+   HGEMM_TR_VARIANT(BF, DT, TAG, 256, 256, 128, 128, 32, 4, 0.99f), \
+   HGEMM_TR_VARIANT(BF, DT, TAG, 256, 256, 128, 128, 32, 5, 0.99f), \
+   HGEMM_TR_VARIANT(BF, DT, TAG, 256, 128, 128, 64, 64, 3, 0.90f),  \
+   HGEMM_TR_VARIANT(BF, DT, TAG, 128, 256, 64, 128, 64, 3, 0.89f),  \
+   HGEMM_TR_VARIANT(BF, DT, TAG, 128, 128, 64, 64, 64, 2, 0.71f)}
+
+const Variant kVariants[] = HGEMM_TR_TABLE(false, GEMM_DTYPE_F16, "f16");
+const Variant kVariantsBf[] = HGEMM_TR_TABLE(true, GEMM_DTYPE_BF16, "bf16");
 
 }  // namespace
 
-const Variant* hgemm_tr_variants(int* count) {
-  *count = sizeof(kVariants) / sizeof(kVariants[0]);
-  return kVariants;
+const Variant* hgemm_tr_variants(int* count, bool bf16) {
+  *count = bf16 ? sizeof(kVariantsBf) / sizeof(kVariantsBf[0])
+                : sizeof(kVariants) / sizeof(kVariants[0]);
+  return bf16 ? kVariantsBf : kVariants;
 }
 
 }  // namespace gemm

@@ -1,6 +1,6 @@
 // Split-K reduction: C[i][j] = sum_{s=0}^{S-1} W[s][i][j], summed in chunk
 // order s = 0, 1, ..., S-1 in FP32 (so the result is the same on every run),
-// then written as FP32, or as FP16 with one round-to-nearest-even.
+// then written as FP32, or as FP16 or BF16 with one round-to-nearest-even.
 //
 // W holds the S partial products of a split-K GEMM, each an M x N FP32
 // matrix with leading dimension N, planes M*N floats apart.  The kernel is
@@ -18,7 +18,10 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 
-template <bool F16OUT>
+// Output element: FP32, FP16 or BF16.
+enum Out { kF32 = 0, kF16 = 1, kBF16 = 2 };
+
+template <int OUT>
 __global__ void __launch_bounds__(kThreads)
 splitk_reduce_vec(const float* __restrict__ W, int S, int M, int N, void* C, int64_t ldc) {
   const int64_t groups = (int64_t)N / 4;
@@ -29,16 +32,17 @@ splitk_reduce_vec(const float* __restrict__ W, int S, int M, int N, void* C, int
   const float* w = W + row * N + 4 * c4;
   f32x4 acc = *reinterpret_cast<const f32x4*>(w);
   for (int s = 1; s < S; ++s) acc += *reinterpret_cast<const f32x4*>(w + s * plane);
-  if constexpr (F16OUT) {
-    typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
-    f16x4 h = {(_Float16)acc[0], (_Float16)acc[1], (_Float16)acc[2], (_Float16)acc[3]};
-    *reinterpret_cast<f16x4*>(static_cast<_Float16*>(C) + row * ldc + 4 * c4) = h;
+  if constexpr (OUT != kF32) {
+    typedef half_t<OUT == kBF16> H;
+    typedef H h16x4 __attribute__((ext_vector_type(4)));
+    h16x4 h = {(H)acc[0], (H)acc[1], (H)acc[2], (H)acc[3]};
+    *reinterpret_cast<h16x4*>(static_cast<H*>(C) + row * ldc + 4 * c4) = h;
   } else {
     *reinterpret_cast<f32x4*>(static_cast<float*>(C) + row * ldc + 4 * c4) = acc;
   }
 }
 
-template <bool F16OUT>
+template <int OUT>
 __global__ void __launch_bounds__(kThreads)
 splitk_reduce_scalar(const float* __restrict__ W, int S, int M, int N, void* C, int64_t ldc) {
   const int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x;
@@ -47,8 +51,8 @@ splitk_reduce_scalar(const float* __restrict__ W, int S, int M, int N, void* C, 
   const int64_t plane = (int64_t)M * N;
   float acc = W[e];
   for (int s = 1; s < S; ++s) acc += W[e + s * plane];
-  if constexpr (F16OUT)
-    static_cast<_Float16*>(C)[row * ldc + col] = (_Float16)acc;
+  if constexpr (OUT != kF32)
+    static_cast<unsigned short*>(C)[row * ldc + col] = round16<OUT == kBF16>(acc);
   else
     static_cast<float*>(C)[row * ldc + col] = acc;
 }
@@ -58,22 +62,26 @@ splitk_reduce_scalar(const float* __restrict__ W, int S, int M, int N, void* C, 
 hipError_t splitk_reduce(int dtype, const float* W, int S, int M, int N, void* C, int64_t ldc,
                          hipStream_t stream) {
   if (M <= 0 || N <= 0) return hipSuccess;
-  const bool f16 = dtype == GEMM_DTYPE_F16;
-  const uintptr_t align = f16 ? 8 : 16;  // bytes of one 4-element store
+  const bool f16 = dtype != GEMM_DTYPE_F32;  // a 16-bit output
+  const uintptr_t align = f16 ? 8 : 16;    // bytes of one 4-element store
   const bool vec = N % 4 == 0 && ldc % 4 == 0 && ((uintptr_t)C % align) == 0 &&
                    ((uintptr_t)W % 16) == 0;
   const int64_t work = vec ? (int64_t)M * (N / 4) : (int64_t)M * N;
   const dim3 grid((unsigned)((work + kThreads - 1) / kThreads)), block(kThreads);
   if (vec) {
-    if (f16)
-      hipLaunchKernelGGL(splitk_reduce_vec<true>, grid, block, 0, stream, W, S, M, N, C, ldc);
+    if (dtype == GEMM_DTYPE_BF16)
+      hipLaunchKernelGGL(splitk_reduce_vec<kBF16>, grid, block, 0, stream, W, S, M, N, C, ldc);
+    else if (f16)
+      hipLaunchKernelGGL(splitk_reduce_vec<kF16>, grid, block, 0, stream, W, S, M, N, C, ldc);
     else
-      hipLaunchKernelGGL(splitk_reduce_vec<false>, grid, block, 0, stream, W, S, M, N, C, ldc);
+      hipLaunchKernelGGL(splitk_reduce_vec<kF32>, grid, block, 0, stream, W, S, M, N, C, ldc);
   } else {
-    if (f16)
-      hipLaunchKernelGGL(splitk_reduce_scalar<true>, grid, block, 0, stream, W, S, M, N, C, ldc);
+    if (dtype == GEMM_DTYPE_BF16)
+      hipLaunchKernelGGL(splitk_reduce_scalar<kBF16>, grid, block, 0, stream, W, S, M, N, C, ldc);
+    else if (f16)
+      hipLaunchKernelGGL(splitk_reduce_scalar<kF16>, grid, block, 0, stream, W, S, M, N, C, ldc);
     else
-      hipLaunchKernelGGL(splitk_reduce_scalar<false>, grid, block, 0, stream, W, S, M, N, C, ldc);
+      hipLaunchKernelGGL(splitk_reduce_scalar<kF32>, grid, block, 0, stream, W, S, M, N, C, ldc);
   }
   return hipGetLastError();
 }

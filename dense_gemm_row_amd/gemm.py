@@ -6,7 +6,7 @@ if the library is missing, loading raises.
 
 ``matmul`` is a convenience for torch tensors on the GPU: it reads shapes,
 strides, data pointers and the current stream and calls ``gemm_f32`` /
-``gemm_f16`` (or the ``_ex`` forms), or the split-K forms when the library
+``gemm_f16`` / ``gemm_bf16`` (or the ``_ex`` forms), or the split-K forms when the library
 says that splitting pays for the shape (then torch allocates the
 workspace).  Torch provides memory and streams only.
 """
@@ -27,6 +27,7 @@ GEMM_ERR_ALIAS = -4
 
 DTYPE_F32 = 0
 DTYPE_F16 = 1
+DTYPE_BF16 = 2
 FAMILY_MFMA = 0
 FAMILY_SIMT = 1
 ORDER_ROW = 0
@@ -36,10 +37,11 @@ ORDER_XCD = 2
 ACT_NONE = 0
 ACT_RELU = 1
 
-EXPORTS = ["gemm_f32", "gemm_f16", "gemm_f32_ex", "gemm_f16_ex", "gemm_f32_bt", "gemm_f16_bt",
-           "gemm_f32_epi", "gemm_f16_epi",
-           "gemm_f32_splitk",
-           "gemm_f16_splitk", "gemm_splitk_workspace_bytes", "gemm_select_splitk_config",
+EXPORTS = ["gemm_f32", "gemm_f16", "gemm_bf16", "gemm_f32_ex", "gemm_f16_ex", "gemm_bf16_ex",
+           "gemm_f32_bt", "gemm_f16_bt", "gemm_bf16_bt",
+           "gemm_f32_epi", "gemm_f16_epi", "gemm_bf16_epi",
+           "gemm_f32_splitk", "gemm_f16_splitk", "gemm_bf16_splitk",
+           "gemm_splitk_workspace_bytes", "gemm_select_splitk_config",
            "gemm_num_configs", "gemm_get_config", "gemm_select_config", "gemm_tile_of_block",
            "gemm_layout_check", "gemm_load_tuning", "gemm_status_string",
            "gemm_last_error", "gemm_version"]
@@ -84,19 +86,17 @@ def _declare(lib):
     i64, i32, p = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
     cfgp = ctypes.POINTER(GemmConfig)
     gemm_args = [i64, i64, i64, p, i64, p, i64, p, i64, p]
-    for name in ("gemm_f32", "gemm_f16"):
-        getattr(lib, name).argtypes = gemm_args
-        getattr(lib, name).restype = ctypes.c_int
-    for name in ("gemm_f32_ex", "gemm_f16_ex"):
+    types = ("f32", "f16", "bf16")
+    for t in types:
+        getattr(lib, f"gemm_{t}").argtypes = gemm_args
+        getattr(lib, f"gemm_{t}").restype = ctypes.c_int
+    for name in [f"gemm_{t}_ex" for t in types] + [f"gemm_{t}_bt" for t in types]:
         getattr(lib, name).argtypes = gemm_args + [cfgp]
         getattr(lib, name).restype = ctypes.c_int
-    for name in ("gemm_f32_bt", "gemm_f16_bt"):
-        getattr(lib, name).argtypes = gemm_args + [cfgp]
-        getattr(lib, name).restype = ctypes.c_int
-    for name in ("gemm_f32_epi", "gemm_f16_epi"):
+    for name in (f"gemm_{t}_epi" for t in types):
         getattr(lib, name).argtypes = gemm_args + [cfgp, ctypes.POINTER(GemmEpilogue)]
         getattr(lib, name).restype = ctypes.c_int
-    for name in ("gemm_f32_splitk", "gemm_f16_splitk"):
+    for name in (f"gemm_{t}_splitk" for t in types):
         getattr(lib, name).argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, p, i64, p, cfgp]
         getattr(lib, name).restype = ctypes.c_int
     lib.gemm_splitk_workspace_bytes.argtypes = [i32, i64, i64, i64, i32]
@@ -149,6 +149,10 @@ def gemm_f16(M, N, K, A, lda, B, ldb, C, ldc, stream=None) -> int:
     return lib().gemm_f16(M, N, K, A, lda, B, ldb, C, ldc, stream)
 
 
+def gemm_bf16(M, N, K, A, lda, B, ldb, C, ldc, stream=None) -> int:
+    return lib().gemm_bf16(M, N, K, A, lda, B, ldb, C, ldc, stream)
+
+
 def gemm_f32_ex(M, N, K, A, lda, B, ldb, C, ldc, stream, cfg: GemmConfig) -> int:
     return lib().gemm_f32_ex(M, N, K, A, lda, B, ldb, C, ldc, stream,
                              ctypes.byref(cfg) if cfg is not None else None)
@@ -159,6 +163,11 @@ def gemm_f16_ex(M, N, K, A, lda, B, ldb, C, ldc, stream, cfg: GemmConfig) -> int
                              ctypes.byref(cfg) if cfg is not None else None)
 
 
+def gemm_bf16_ex(M, N, K, A, lda, B, ldb, C, ldc, stream, cfg: GemmConfig) -> int:
+    return lib().gemm_bf16_ex(M, N, K, A, lda, B, ldb, C, ldc, stream,
+                              ctypes.byref(cfg) if cfg is not None else None)
+
+
 def gemm_f32_bt(M, N, K, A, lda, Bt, ldbt, C, ldc, stream=None, cfg: GemmConfig | None = None) -> int:
     return lib().gemm_f32_bt(M, N, K, A, lda, Bt, ldbt, C, ldc, stream,
                              ctypes.byref(cfg) if cfg is not None else None)
@@ -167,6 +176,11 @@ def gemm_f32_bt(M, N, K, A, lda, Bt, ldbt, C, ldc, stream=None, cfg: GemmConfig 
 def gemm_f16_bt(M, N, K, A, lda, Bt, ldbt, C, ldc, stream=None, cfg: GemmConfig | None = None) -> int:
     return lib().gemm_f16_bt(M, N, K, A, lda, Bt, ldbt, C, ldc, stream,
                              ctypes.byref(cfg) if cfg is not None else None)
+
+
+def gemm_bf16_bt(M, N, K, A, lda, Bt, ldbt, C, ldc, stream=None, cfg: GemmConfig | None = None) -> int:
+    return lib().gemm_bf16_bt(M, N, K, A, lda, Bt, ldbt, C, ldc, stream,
+                              ctypes.byref(cfg) if cfg is not None else None)
 
 
 def gemm_f32_epi(M, N, K, A, lda, B, ldb, C, ldc, stream, cfg: GemmConfig | None,
@@ -183,6 +197,13 @@ def gemm_f16_epi(M, N, K, A, lda, B, ldb, C, ldc, stream, cfg: GemmConfig | None
                               ctypes.byref(epi) if epi is not None else None)
 
 
+def gemm_bf16_epi(M, N, K, A, lda, B, ldb, C, ldc, stream, cfg: GemmConfig | None,
+                  epi: GemmEpilogue | None) -> int:
+    return lib().gemm_bf16_epi(M, N, K, A, lda, B, ldb, C, ldc, stream,
+                               ctypes.byref(cfg) if cfg is not None else None,
+                               ctypes.byref(epi) if epi is not None else None)
+
+
 def gemm_f32_splitk(M, N, K, A, lda, B, ldb, C, ldc, workspace, workspace_bytes, stream=None,
                     cfg: GemmConfig | None = None) -> int:
     return lib().gemm_f32_splitk(M, N, K, A, lda, B, ldb, C, ldc, workspace, workspace_bytes, stream,
@@ -193,6 +214,20 @@ def gemm_f16_splitk(M, N, K, A, lda, B, ldb, C, ldc, workspace, workspace_bytes,
                     cfg: GemmConfig | None = None) -> int:
     return lib().gemm_f16_splitk(M, N, K, A, lda, B, ldb, C, ldc, workspace, workspace_bytes, stream,
                                  ctypes.byref(cfg) if cfg is not None else None)
+
+
+def gemm_bf16_splitk(M, N, K, A, lda, B, ldb, C, ldc, workspace, workspace_bytes, stream=None,
+                     cfg: GemmConfig | None = None) -> int:
+    return lib().gemm_bf16_splitk(M, N, K, A, lda, B, ldb, C, ldc, workspace, workspace_bytes,
+                                  stream, ctypes.byref(cfg) if cfg is not None else None)
+
+
+# Entry points per dtype code, for callers that dispatch on it.
+def entry(dtype: int, form: str = ""):
+    """The binding of gemm_<type><form> (form "", "_ex", "_bt", "_epi",
+    "_splitk") for dtype DTYPE_F32 / DTYPE_F16 / DTYPE_BF16."""
+    name = {DTYPE_F32: "f32", DTYPE_F16: "f16", DTYPE_BF16: "bf16"}[dtype]
+    return globals()[f"gemm_{name}{form}"]
 
 
 def gemm_splitk_workspace_bytes(dtype: int, M: int, N: int, K: int, splits: int = 0) -> int:
@@ -289,9 +324,9 @@ def _ld(t) -> int:
 def matmul(a, b, out=None, config: GemmConfig | None = None, stream=None, split_k: bool = True,
            alpha: float = 1.0, beta: float = 0.0, bias=None, act: int = ACT_NONE,
            b_transposed: bool = False):
-    """C = a @ b on the GPU through libgemm.  a: M x K, b: K x N, both
-    float32 or both float16, row-major (any row stride).  Returns ``out``
-    (allocated when None).  Raises GemmError on a non-OK status.
+    """C = a @ b on the GPU through libgemm.  a: M x K, b: K x N, of one
+    type (float32, float16 or bfloat16), row-major (any row stride).
+    Returns ``out`` (allocated when None).  Raises GemmError on a non-OK status.
 
     With ``config`` None and ``split_k`` True, shapes for which the library
     chooses split-K (too few output tiles for the GPU) run the split-K form
@@ -305,8 +340,9 @@ def matmul(a, b, out=None, config: GemmConfig | None = None, stream=None, split_
     fused epilogue out = act(alpha * (a @ b) + beta * out + bias) (through
     gemm_*_epi; ``out`` must then be given when beta != 0)."""
     import torch
-    if a.dtype != b.dtype or a.dtype not in (torch.float32, torch.float16):
-        raise TypeError("a and b must both be float32 or both float16")
+    dtypes = {torch.float32: DTYPE_F32, torch.float16: DTYPE_F16, torch.bfloat16: DTYPE_BF16}
+    if a.dtype != b.dtype or a.dtype not in dtypes:
+        raise TypeError("a and b must both be float32, float16 or bfloat16")
     if not (a.is_cuda and b.is_cuda):
         raise ValueError("a and b must be GPU tensors")
     M, K = a.shape
@@ -320,11 +356,11 @@ def matmul(a, b, out=None, config: GemmConfig | None = None, stream=None, split_
     if stream is None:
         stream = torch.cuda.current_stream(a.device).cuda_stream
     args = (M, N, K, a.data_ptr(), _ld(a), b.data_ptr(), _ld(b), out.data_ptr(), _ld(out), stream)
-    dtype = DTYPE_F32 if a.dtype == torch.float32 else DTYPE_F16
+    dtype = dtypes[a.dtype]
     if b_transposed:
         if alpha != 1.0 or beta != 0.0 or bias is not None or act != ACT_NONE:
             raise ValueError("b_transposed does not take the fused epilogue")
-        fn = gemm_f32_bt if dtype == DTYPE_F32 else gemm_f16_bt
+        fn = entry(dtype, "_bt")
         st = fn(*args[:9], stream, config)
         if st != GEMM_OK:
             raise GemmError(st, fn.__name__)
@@ -335,7 +371,7 @@ def matmul(a, b, out=None, config: GemmConfig | None = None, stream=None, split_
             raise ValueError("bias must be a contiguous float32 GPU tensor of N values")
         epi = GemmEpilogue(float(alpha), float(beta), bias.data_ptr() if bias is not None else None,
                            int(act))
-        fn = gemm_f32_epi if dtype == DTYPE_F32 else gemm_f16_epi
+        fn = entry(dtype, "_epi")
         st = fn(*args, config, epi)
         if st != GEMM_OK:
             raise GemmError(st, fn.__name__)
@@ -346,15 +382,13 @@ def matmul(a, b, out=None, config: GemmConfig | None = None, stream=None, split_
     if split_cfg is not None and split_cfg.splits > 1:
         nbytes = gemm_splitk_workspace_bytes(dtype, M, N, K, split_cfg.splits)
         ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=a.device)
-        fn = gemm_f32_splitk if dtype == DTYPE_F32 else gemm_f16_splitk
+        fn = entry(dtype, "_splitk")
         st = fn(*args[:9], ws.data_ptr(), ws.numel(), stream, split_cfg)
         if st != GEMM_OK:
             raise GemmError(st, fn.__name__)
         return out
-    if a.dtype == torch.float32:
-        st = gemm_f32(*args) if config is None else gemm_f32_ex(*args, config)
-    else:
-        st = gemm_f16(*args) if config is None else gemm_f16_ex(*args, config)
+    fn = entry(dtype) if config is None else entry(dtype, "_ex")
+    st = fn(*args) if config is None else fn(*args, config)
     if st != GEMM_OK:
-        raise GemmError(st, "gemm_f32" if a.dtype == torch.float32 else "gemm_f16")
+        raise GemmError(st, fn.__name__)
     return out

@@ -31,7 +31,9 @@
  *            of the K-sum is the kernel's (results agree with the exact sum
  *            within |C - C_exact| <= 1e-5 * sum_k |A_ik||B_kj| for the
  *            supported sizes).  FP16: FP16 inputs, FP32 accumulation, one
- *            round-to-nearest-even conversion to FP16 per output.
+ *            round-to-nearest-even conversion to FP16 per output.  BF16:
+ *            the same with bfloat16 inputs and output (8 significant bits:
+ *            |C - C_exact| <= 5e-3 * sum_k |A_ik||B_kj|).
  * Errors     No exception or abort crosses this interface.  Argument errors
  *            are detected on the host before any GPU work is enqueued:
  *              M, N or K < 0                              -> INVALID_ARG
@@ -62,13 +64,19 @@ typedef enum gemm_status {
 
 /* IEEE 754 binary16 bit pattern. */
 typedef uint16_t gemm_f16_t;
+/* bfloat16 bit pattern: the upper 16 bits of an IEEE 754 binary32. */
+typedef uint16_t gemm_bf16_t;
 
-typedef enum gemm_dtype { GEMM_DTYPE_F32 = 0, GEMM_DTYPE_F16 = 1 } gemm_dtype_t;
+typedef enum gemm_dtype {
+    GEMM_DTYPE_F32 = 0,
+    GEMM_DTYPE_F16 = 1,
+    GEMM_DTYPE_BF16 = 2
+} gemm_dtype_t;
 
 /* Kernel families. */
 typedef enum gemm_family {
     GEMM_FAMILY_MFMA = 0, /* matrix-core kernels (v_mfma_f32_32x32x2_f32,
-                             v_mfma_f32_32x32x16_f16)                     */
+                             v_mfma_f32_32x32x16_f16 / _bf16)             */
     GEMM_FAMILY_SIMT = 1  /* vector-FMA kernel, kept as an ablation (FP32) */
 } gemm_family_t;
 
@@ -120,8 +128,22 @@ gemm_status_t gemm_f16(int64_t M, int64_t N, int64_t K,
                        const gemm_f16_t *B, int64_t ldb,
                        gemm_f16_t *C, int64_t ldc, void *stream);
 
-/* As gemm_f32 / gemm_f16 with a forced variant and tile order (tests,
- * tuner, ablation).  cfg->id must name a variant of the matching dtype. */
+/*
+ * BF16 GEMM, C = A x B: bfloat16 inputs, FP32 accumulation, bfloat16 output
+ * rounded to nearest even.  BF16 is the 16-bit type the GB300 GEMM article
+ * lists beside FP16 for the matrix units (sections 1.1 and 5.1); it keeps
+ * FP32's exponent range with 8 significant bits.  Same kernels as FP16 with
+ * the bf16 matrix instruction; every gemm_f16_* entry point has a gemm_bf16_*
+ * counterpart with the same contract.
+ */
+gemm_status_t gemm_bf16(int64_t M, int64_t N, int64_t K,
+                        const gemm_bf16_t *A, int64_t lda,
+                        const gemm_bf16_t *B, int64_t ldb,
+                        gemm_bf16_t *C, int64_t ldc, void *stream);
+
+/* As gemm_f32 / gemm_f16 / gemm_bf16 with a forced variant and tile order
+ * (tests, tuner, ablation).  cfg->id must name a variant of the matching
+ * dtype. */
 gemm_status_t gemm_f32_ex(int64_t M, int64_t N, int64_t K,
                           const float *A, int64_t lda,
                           const float *B, int64_t ldb,
@@ -132,6 +154,11 @@ gemm_status_t gemm_f16_ex(int64_t M, int64_t N, int64_t K,
                           const gemm_f16_t *B, int64_t ldb,
                           gemm_f16_t *C, int64_t ldc, void *stream,
                           const gemm_config_t *cfg);
+gemm_status_t gemm_bf16_ex(int64_t M, int64_t N, int64_t K,
+                           const gemm_bf16_t *A, int64_t lda,
+                           const gemm_bf16_t *B, int64_t ldb,
+                           gemm_bf16_t *C, int64_t ldc, void *stream,
+                           const gemm_config_t *cfg);
 
 /*
  * Split-K GEMM: the same results contract as gemm_f32 / gemm_f16, for shapes
@@ -140,7 +167,8 @@ gemm_status_t gemm_f16_ex(int64_t M, int64_t N, int64_t K,
  * (S = ceil(K / Kc) <= splits); one launch computes every chunk's FP32
  * partial product into `workspace` (S x M x N floats, row-major), and a
  * second launch sums the S partials of each element in chunk order and
- * writes C (FP32, or FP16 rounded to nearest even once, after the sum).
+ * writes C (FP32, or FP16 / BF16 rounded to nearest even once, after the
+ * sum).
  * The order of the sum is fixed, so results are bit-reproducible for a
  * given configuration.  Splitting the K sum of the pages' C = A x B
  * changes only the order of its additions ("nxbn.cn GB300 GEMM",
@@ -171,6 +199,12 @@ gemm_status_t gemm_f16_splitk(int64_t M, int64_t N, int64_t K,
                               gemm_f16_t *C, int64_t ldc,
                               void *workspace, int64_t workspace_bytes,
                               void *stream, const gemm_config_t *cfg);
+gemm_status_t gemm_bf16_splitk(int64_t M, int64_t N, int64_t K,
+                               const gemm_bf16_t *A, int64_t lda,
+                               const gemm_bf16_t *B, int64_t ldb,
+                               gemm_bf16_t *C, int64_t ldc,
+                               void *workspace, int64_t workspace_bytes,
+                               void *stream, const gemm_config_t *cfg);
 
 /* Workspace bytes a split-K call with `splits` requested chunks needs
  * (0 when it would not split; splits <= 0 means the library's choice for
@@ -199,6 +233,11 @@ gemm_status_t gemm_f16_bt(int64_t M, int64_t N, int64_t K,
                           const gemm_f16_t *Bt, int64_t ldbt,
                           gemm_f16_t *C, int64_t ldc, void *stream,
                           const gemm_config_t *cfg);
+gemm_status_t gemm_bf16_bt(int64_t M, int64_t N, int64_t K,
+                           const gemm_bf16_t *A, int64_t lda,
+                           const gemm_bf16_t *Bt, int64_t ldbt,
+                           gemm_bf16_t *C, int64_t ldc, void *stream,
+                           const gemm_config_t *cfg);
 
 /* Activation applied by the fused epilogue. */
 typedef enum gemm_act {
@@ -223,7 +262,7 @@ typedef struct gemm_epilogue {
 
 /*
  * GEMM with the fused epilogue, computed in FP32 from the FP32 accumulator
- * (and, for FP16, from the binary16 old C) and rounded once to the output
+ * (and, for FP16 / BF16, from the 16-bit old C) and rounded once to the output
  * type.  Same layout, stream, alignment and error conventions as gemm_f32 /
  * gemm_f16, plus:
  *   epi NULL or epi->act unknown                       -> INVALID_ARG
@@ -242,6 +281,11 @@ gemm_status_t gemm_f16_epi(int64_t M, int64_t N, int64_t K,
                            const gemm_f16_t *B, int64_t ldb,
                            gemm_f16_t *C, int64_t ldc, void *stream,
                            const gemm_config_t *cfg, const gemm_epilogue_t *epi);
+gemm_status_t gemm_bf16_epi(int64_t M, int64_t N, int64_t K,
+                            const gemm_bf16_t *A, int64_t lda,
+                            const gemm_bf16_t *B, int64_t ldb,
+                            gemm_bf16_t *C, int64_t ldc, void *stream,
+                            const gemm_config_t *cfg, const gemm_epilogue_t *epi);
 
 /* Variant table: count per dtype, and the description of variant idx. */
 int32_t gemm_num_configs(int32_t dtype);
@@ -273,7 +317,7 @@ gemm_status_t gemm_layout_check(int32_t dtype, int32_t idx, int32_t banks,
                                 int64_t out[2]);
 
 /* Tuning table: a text file of lines "dtype M N K name order group_m
- * [splits]" (dtype f32|f16; splits defaults to 1).  Exact-shape matches
+ * [splits]" (dtype f32|f16|bf16; splits defaults to 1).  Exact-shape matches
  * override the heuristic.  Loading replaces the previous table; NULL clears
  * it.  Not safe to call concurrently with GEMM calls. */
 gemm_status_t gemm_load_tuning(const char *path);

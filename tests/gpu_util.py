@@ -14,10 +14,31 @@ import numpy as np
 import torch
 
 import oracle
-from dense_gemm_row_amd import gemm
+from dense_gemm_row_amd import gemm, synth
 
 CANARY_F32 = np.uint32(0x7FC0DEAD)  # a quiet NaN payload nobody computes
 CANARY_F16 = np.uint16(0x7E5A)
+CANARY_BF16 = np.uint16(0x7FDA)
+CANARY = {"f32": CANARY_F32, "f16": CANARY_F16, "bf16": CANARY_BF16}
+DTYPE = {"f32": gemm.DTYPE_F32, "f16": gemm.DTYPE_F16, "bf16": gemm.DTYPE_BF16}
+VIEW = {"f32": np.float32, "f16": np.float16, "bf16": synth.BF16}
+
+
+def kind_of(a: np.ndarray) -> str:
+    if a.dtype == np.float32:
+        return "f32"
+    if a.dtype == np.float16:
+        return "f16"
+    if a.dtype == synth.BF16:
+        return "bf16"
+    raise TypeError(f"unsupported dtype {a.dtype}")
+
+
+def wide(x: np.ndarray) -> np.ndarray:
+    """Exact float64 values of an FP32 / FP16 / BF16 array."""
+    if x.dtype == synth.BF16:
+        return synth.bf16_to_f32(x).astype(np.float64)
+    return x.astype(np.float64)
 
 
 def log(msg: str) -> None:
@@ -36,7 +57,7 @@ class DevMatrix:
         self.guard = guard + offset
         self.bits = np.uint32 if kind == "f32" else np.uint16
         self.es = 4 if kind == "f32" else 2
-        canary = CANARY_F32 if kind == "f32" else CANARY_F16
+        canary = CANARY[kind]
         n = self.guard + rows * self.ld + guard
         flat = np.full(n, canary, dtype=self.bits)
         if host is not None and rows and cols:
@@ -57,15 +78,15 @@ class DevMatrix:
     def matrix(self, flat: np.ndarray | None = None) -> np.ndarray:
         flat = self.fetch() if flat is None else flat
         if self.rows == 0:
-            return np.zeros((0, self.cols), dtype=np.float32 if self.kind == "f32" else np.float16)
+            return np.zeros((0, self.cols), dtype=self.bits).view(VIEW[self.kind])
         view = flat[self.guard:self.guard + self.rows * self.ld].reshape(self.rows, self.ld)
         out = np.ascontiguousarray(view[:, :self.cols])
-        return out.view(np.float32 if self.kind == "f32" else np.float16)
+        return out.view(VIEW[self.kind])
 
     def untouched_outside(self, flat: np.ndarray | None = None) -> bool:
         """Canaries intact before, after and in the row padding."""
         flat = self.fetch() if flat is None else flat
-        canary = CANARY_F32 if self.kind == "f32" else CANARY_F16
+        canary = CANARY[self.kind]
         body = flat[self.guard:self.guard + self.rows * self.ld]
         ok = np.all(flat[:self.guard] == canary) and np.all(flat[self.guard + self.rows * self.ld:] == canary)
         if self.rows and self.ld > self.cols:
@@ -92,8 +113,8 @@ def run(A: np.ndarray, B: np.ndarray, cfg=None, pad=(0, 0, 0), offset=(0, 0, 0),
 
     bt: B is given transposed (the argument is Bt, N x K) and the call is
     gemm_*_bt; A @ Bt.T is computed."""
-    kind = "f32" if A.dtype == np.float32 else "f16"
-    dtype = gemm.DTYPE_F32 if kind == "f32" else gemm.DTYPE_F16
+    kind = kind_of(A)
+    dtype = DTYPE[kind]
     M, K = A.shape
     N = B.shape[0] if bt else B.shape[1]
     dA = DevMatrix(A, M, K, kind, pad=pad[0], offset=offset[0])
@@ -120,19 +141,17 @@ def run(A: np.ndarray, B: np.ndarray, cfg=None, pad=(0, 0, 0), offset=(0, 0, 0),
     for _ in range(repeat):
         args = (M, N, K, dA.ptr, dA.ld, dB.ptr, dB.ld, dC.ptr, dC.ld)
         if bt:
-            fn = gemm.gemm_f32_bt if kind == "f32" else gemm.gemm_f16_bt
-            st = fn(*args, stream, cfg)
+            st = gemm.entry(dtype, "_bt")(*args, stream, cfg)
         elif epi is not None:
-            fn = gemm.gemm_f32_epi if kind == "f32" else gemm.gemm_f16_epi
-            st = fn(*args, stream, cfg, epi_s)
+            st = gemm.entry(dtype, "_epi")(*args, stream, cfg, epi_s)
         elif split is not None:
-            fn = gemm.gemm_f32_splitk if kind == "f32" else gemm.gemm_f16_splitk
-            st = fn(*args, ws.data_ptr() + 4 * WS_GUARD, 4 * (ws.numel() - 2 * WS_GUARD), stream,
-                    None if split == "auto" else split)
-        elif kind == "f32":
-            st = gemm.gemm_f32(*args, stream) if cfg is None else gemm.gemm_f32_ex(*args, stream, cfg)
+            st = gemm.entry(dtype, "_splitk")(*args, ws.data_ptr() + 4 * WS_GUARD,
+                                              4 * (ws.numel() - 2 * WS_GUARD), stream,
+                                              None if split == "auto" else split)
+        elif cfg is None:
+            st = gemm.entry(dtype)(*args, stream)
         else:
-            st = gemm.gemm_f16(*args, stream) if cfg is None else gemm.gemm_f16_ex(*args, stream, cfg)
+            st = gemm.entry(dtype, "_ex")(*args, stream, cfg)
         if st != gemm.GEMM_OK:
             raise gemm.GemmError(st, "gemm call")
     torch.cuda.synchronize()
@@ -146,24 +165,38 @@ def run(A: np.ndarray, B: np.ndarray, cfg=None, pad=(0, 0, 0), offset=(0, 0, 0),
 
 
 def tol_for(kind: str) -> float:
-    return oracle.SGEMM_TOL if kind == "f32" else oracle.HGEMM_TOL
+    return oracle.TOL[kind]
 
 
 def check_full(A, B, C, tol=None) -> dict:
-    kind = "f32" if A.dtype == np.float32 else "f16"
     ref, den = oracle.gemm_rows(A, B)
-    return oracle.check(C, ref, den, tol_for(kind) if tol is None else tol)
+    return oracle.check(C, ref, den, tol_for(kind_of(A)) if tol is None else tol)
 
 
 def check_rows(A, B, C, rows, tol=None) -> dict:
-    kind = "f32" if A.dtype == np.float32 else "f16"
     ref, den = oracle.gemm_rows(A, B, rows=rows)
-    return oracle.check(np.ascontiguousarray(C[rows]), ref, den, tol_for(kind) if tol is None else tol)
+    return oracle.check(np.ascontiguousarray(C[rows]), ref, den,
+                        tol_for(kind_of(A)) if tol is None else tol)
+
+
+def rounded(ref: np.ndarray, kind: str) -> np.ndarray:
+    """The one correct output for exact inputs: the oracle's exact result
+    (which must be an FP32 value, e.g. an integer below 2**24) rounded once
+    to the output type, to nearest with ties to even (numpy's float16 and
+    torch's bfloat16 conversions), as float64."""
+    ref32 = ref.astype(np.float32)
+    assert np.array_equal(ref32.astype(np.float64), ref), "exact results must be FP32 values"
+    if kind == "f32":
+        return ref
+    if kind == "f16":
+        return ref32.astype(np.float16).astype(np.float64)
+    import torch
+    return torch.from_numpy(ref32).to(torch.bfloat16).to(torch.float64).numpy()
 
 
 def exact_equal(A, B, C) -> bool:
-    """Bit-exact agreement with the oracle (for inputs whose product is
-    exactly representable): compare the decoded output to C_ref."""
+    """Agreement with the oracle for inputs whose products and sums are
+    exact in FP32: the decoded output equals the exact C_ref rounded once
+    to the output type (C_ref itself whenever it is representable)."""
     ref, _ = oracle.gemm_rows(A, B)
-    got = C.astype(np.float64)
-    return bool(np.array_equal(got, ref))
+    return bool(np.array_equal(wide(C), rounded(ref, kind_of(A))))

@@ -17,6 +17,12 @@ HEADER = os.path.join(ROOT, "include", "gemm.h")
 PA, PB, PC = 0x10000000, 0x20000000, 0x30000000
 
 
+def _dtype_of(fn):
+    """The dtype code of a binding gemm_<type>[_form]."""
+    t = fn.__name__.split("_")[1]
+    return {"f32": gemm.DTYPE_F32, "f16": gemm.DTYPE_F16, "bf16": gemm.DTYPE_BF16}[t]
+
+
 def header_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
@@ -39,7 +45,7 @@ def test_version_and_status_strings():
         assert gemm.gemm_status_string(st) == s
 
 
-@pytest.mark.parametrize("fn", [gemm.gemm_f32, gemm.gemm_f16])
+@pytest.mark.parametrize("fn", [gemm.gemm_f32, gemm.gemm_f16, gemm.gemm_bf16])
 def test_argument_validation(fn):
     bad = [
         ((-1, 4, 4, PA, 4, PB, 4, PC, 4), gemm.GEMM_ERR_INVALID_ARG),
@@ -60,7 +66,7 @@ def test_argument_validation(fn):
         assert gemm.gemm_last_error() != ""
 
 
-@pytest.mark.parametrize("fn", [gemm.gemm_f32, gemm.gemm_f16])
+@pytest.mark.parametrize("fn", [gemm.gemm_f32, gemm.gemm_f16, gemm.gemm_bf16])
 def test_degenerate_sizes_are_noops(fn):
     # M == 0 or N == 0: nothing to do, OK, no launch (NULL C allowed).
     assert fn(0, 4, 4, PA, 4, PB, 4, 0, 4, None) == gemm.GEMM_OK
@@ -84,7 +90,7 @@ def test_forced_config_validation():
 
 
 def test_config_table_consistent():
-    for dt in (gemm.DTYPE_F32, gemm.DTYPE_F16):
+    for dt in (gemm.DTYPE_F32, gemm.DTYPE_F16, gemm.DTYPE_BF16):
         cfgs = gemm.configs(dt)
         assert cfgs
         names = [c.name.decode() for c in cfgs]
@@ -101,7 +107,7 @@ SHAPES = [(1, 1), (33, 17), (128, 128), (300, 520), (4096, 4096), (4000, 4000),
           (8192, 8192), (1024, 1024), (4096, 11008), (2048, 640)]
 
 
-@pytest.mark.parametrize("dt", [gemm.DTYPE_F32, gemm.DTYPE_F16])
+@pytest.mark.parametrize("dt", [gemm.DTYPE_F32, gemm.DTYPE_F16, gemm.DTYPE_BF16])
 @pytest.mark.parametrize("order", [gemm.ORDER_ROW, gemm.ORDER_GROUPED, gemm.ORDER_XCD])
 def test_tile_map_is_a_bijection(dt, order):
     for cfg in gemm.configs(dt):
@@ -131,7 +137,7 @@ def test_xcd_order_gives_each_xcd_a_compact_region():
         assert len(rows) == 4 and len(cols) == 8, (x, rows, cols)
 
 
-@pytest.mark.parametrize("dt", [gemm.DTYPE_F32, gemm.DTYPE_F16])
+@pytest.mark.parametrize("dt", [gemm.DTYPE_F32, gemm.DTYPE_F16, gemm.DTYPE_BF16])
 def test_lds_layouts(dt):
     """Every variant's LDS staging writes cover each stage exactly once, all
     fragment reads stay in bounds and read what the staging wrote for the
@@ -156,7 +162,7 @@ def test_heuristic_selection():
     assert c.family == gemm.FAMILY_MFMA and c.bm * c.bn == 256 * 256
     small = gemm.gemm_select_config(gemm.DTYPE_F32, 256, 256, 256)
     assert small.bm * small.bn <= 64 * 64 * 4
-    for dt in (gemm.DTYPE_F32, gemm.DTYPE_F16):
+    for dt in (gemm.DTYPE_F32, gemm.DTYPE_F16, gemm.DTYPE_BF16):
         for M, N, K in [(1, 1, 1), (4096, 11008, 4096), (1024, 1024, 8192)]:
             assert gemm.gemm_select_config(dt, M, N, K).family == gemm.FAMILY_MFMA
 
@@ -179,7 +185,7 @@ def test_tuning_table(tmp_path):
         gemm.gemm_select_config(gemm.DTYPE_F32, 333, 444, 555).id != cfg.id
 
 
-@pytest.mark.parametrize("dt", [gemm.DTYPE_F32, gemm.DTYPE_F16])
+@pytest.mark.parametrize("dt", [gemm.DTYPE_F32, gemm.DTYPE_F16, gemm.DTYPE_BF16])
 def test_every_pipelined_variant_has_a_general_fallback(dt):
     """Unaligned operands of an LDS-direct or pipelined variant run the
     general kernel with the same workgroup tile (same tile map), which must
@@ -209,12 +215,12 @@ def test_splitk_workspace_and_selection():
         assert auto == gemm.gemm_select_splitk_config(dt, 1024, 1024, 8192).splits * 1024 * 1024 * 4
 
 
-@pytest.mark.parametrize("fn", [gemm.gemm_f32_splitk, gemm.gemm_f16_splitk])
+@pytest.mark.parametrize("fn", [gemm.gemm_f32_splitk, gemm.gemm_f16_splitk, gemm.gemm_bf16_splitk])
 def test_splitk_argument_validation(fn):
     # A shape that splits (aligned fake pointers): workspace problems are
     # caught on the host before any launch.
     M, N, K = 1024, 1024, 8192
-    cfg = gemm.gemm_select_splitk_config(gemm.DTYPE_F32 if fn is gemm.gemm_f32_splitk else gemm.DTYPE_F16,
+    cfg = gemm.gemm_select_splitk_config(_dtype_of(fn),
                                          M, N, K)
     A, B, C = 0x100000000, 0x200000000, 0x300000000
     W = 0x400000000
@@ -249,9 +255,9 @@ def test_tuning_table_splits_column(tmp_path):
     assert gemm.gemm_load_tuning(str(path)) == gemm.GEMM_ERR_INVALID_ARG
 
 
-@pytest.mark.parametrize("fn", [gemm.gemm_f32_epi, gemm.gemm_f16_epi])
+@pytest.mark.parametrize("fn", [gemm.gemm_f32_epi, gemm.gemm_f16_epi, gemm.gemm_bf16_epi])
 def test_epilogue_argument_validation(fn):
-    dt = gemm.DTYPE_F32 if fn is gemm.gemm_f32_epi else gemm.DTYPE_F16
+    dt = _dtype_of(fn)
     es = 4 if dt == gemm.DTYPE_F32 else 2
     base = (64, 64, 64, PA, 64, PB, 64, PC, 64, None)
     ok = gemm.GemmEpilogue(1.0, 0.0, None, gemm.ACT_NONE)
@@ -267,12 +273,12 @@ def test_epilogue_argument_validation(fn):
     assert fn(0, 64, 64, PA, 64, PB, 64, 0, 64, None, None, ok) == gemm.GEMM_OK   # M == 0
 
 
-@pytest.mark.parametrize("fn", [gemm.gemm_f32_bt, gemm.gemm_f16_bt])
+@pytest.mark.parametrize("fn", [gemm.gemm_f32_bt, gemm.gemm_f16_bt, gemm.gemm_bf16_bt])
 def test_bt_argument_validation(fn):
     """Transposed-B entry points: ldbt is checked against K (not N), the
     alias check covers the N x K span of Bt, and forced variants without a
     transposed-B form are refused; all before any launch."""
-    dt = gemm.DTYPE_F32 if fn is gemm.gemm_f32_bt else gemm.DTYPE_F16
+    dt = _dtype_of(fn)
     es = 4 if dt == gemm.DTYPE_F32 else 2
     # M=64, N=32, K=128: ldbt must be >= 128 even though N = 32.
     assert fn(64, 32, 128, PA, 128, PB, 64, PC, 32) == gemm.GEMM_ERR_INVALID_ARG
@@ -284,3 +290,24 @@ def test_bt_argument_validation(fn):
         if name.startswith(("pipe_", "simt_")):
             assert fn(64, 32, 128, PA, 128, PB, 128, PC, 32, None, c) == gemm.GEMM_ERR_UNSUPPORTED, name
     assert fn(0, 32, 128, PA, 128, PB, 128, 0, 32) == gemm.GEMM_OK  # M == 0
+
+
+def test_bf16_tables_mirror_f16():
+    """The BF16 table is the FP16 kernels with the bf16 matrix instruction:
+    the same tiles and forms, one for one, under bf16 names; a BF16 config
+    is refused by the FP16 entry points' id check only when out of range,
+    and the selection picks a matrix-core variant."""
+    f16 = [c for c in gemm.configs(gemm.DTYPE_F16) if not c.name.decode().startswith("pipe_")]
+    bf16 = gemm.configs(gemm.DTYPE_BF16)
+    assert [c.name.decode().replace("_f16_", "_bf16_") for c in f16] == [c.name.decode() for c in bf16]
+    for a, b in zip(f16, bf16):
+        assert (a.bm, a.bn, a.bk, a.wm, a.wn, a.stages, a.lds_bytes) == \
+            (b.bm, b.bn, b.bk, b.wm, b.wn, b.stages, b.lds_bytes)
+        assert b.dtype == gemm.DTYPE_BF16
+    c = gemm.gemm_select_config(gemm.DTYPE_BF16, 4096, 4096, 4096)
+    assert c.name.decode().startswith("tr_bf16_") and c.bm * c.bn == 256 * 256
+    s = gemm.gemm_select_splitk_config(gemm.DTYPE_BF16, 1024, 1024, 8192)
+    assert s.splits > 1
+    assert gemm.gemm_num_configs(3) == 0
+    with pytest.raises(gemm.GemmError):
+        gemm.gemm_get_config(3, 0)
