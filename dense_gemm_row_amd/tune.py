@@ -83,15 +83,15 @@ def time_config(gemm, torch, fn, args, cfg, stream, warmup: int, reps: int, ws=N
 
 def tune_shape(gemm, torch, kind: str, M: int, N: int, K: int, orders, warmup: int,
                reps: int, splits=(1,)) -> dict:
-    dtype = gemm.DTYPE_F32 if kind == "f32" else gemm.DTYPE_F16
-    tdt = torch.float32 if kind == "f32" else torch.float16
+    dtype = {"f32": gemm.DTYPE_F32, "f16": gemm.DTYPE_F16, "bf16": gemm.DTYPE_BF16}[kind]
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[kind]
     dev = torch.device("cuda:0")
     gen = torch.Generator(device=dev)
     gen.manual_seed(M * 1000003 + N * 1009 + K)
     a = (torch.rand((M, K), device=dev, generator=gen) * 2 - 1).to(tdt)
     b = (torch.rand((K, N), device=dev, generator=gen) * 2 - 1).to(tdt)
     c = torch.empty((M, N), device=dev, dtype=tdt)
-    fn = gemm.gemm_f32_ex if kind == "f32" else gemm.gemm_f16_ex
+    fn = gemm.entry(dtype, "_ex")
     args = (M, N, K, a.data_ptr(), K, b.data_ptr(), N, c.data_ptr(), N)
     stream = torch.cuda.current_stream(dev)
     flops = 2.0 * M * N * K
@@ -99,7 +99,7 @@ def tune_shape(gemm, torch, kind: str, M: int, N: int, K: int, orders, warmup: i
 
     # Split-K candidates (gemm_*_splitk with cfg.splits) only where the
     # unsplit tiles leave CUs idle; one workspace serves them all.
-    fn_split = gemm.gemm_f32_splitk if kind == "f32" else gemm.gemm_f16_splitk
+    fn_split = gemm.entry(dtype, "_splitk")
     max_ws = max([gemm.gemm_splitk_workspace_bytes(dtype, M, N, K, s) for s in splits] + [16])
     ws = torch.empty(max_ws, dtype=torch.uint8, device=dev) if max(splits) > 1 else None
 
@@ -143,7 +143,7 @@ def tune_shape(gemm, torch, kind: str, M: int, N: int, K: int, orders, warmup: i
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--shapes", nargs="+", type=parse_shape, required=True, help="MxNxK ...")
-    ap.add_argument("--dtypes", nargs="+", choices=["f32", "f16"], default=["f32", "f16"])
+    ap.add_argument("--dtypes", nargs="+", choices=["f32", "f16", "bf16"], default=["f32", "f16"])
     ap.add_argument("--orders", nargs="+", type=parse_order,
                     default=[parse_order("xcd:4"), parse_order("xcd:8"), parse_order("grouped:8")],
                     help="tile orders to try: row | grouped:G | xcd:G")
