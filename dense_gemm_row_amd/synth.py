@@ -20,7 +20,9 @@ increment 0x9E3779B97F4A7C15).
   is exact in FP32.  FP16 inputs are the round-to-nearest-even FP16 value of
   that FP32 number (numpy's ``astype(np.float16)``); BF16 inputs are the
   round-to-nearest-even bfloat16 value of it (:func:`to_bf16`), held as
-  uint16 bit patterns under the marker dtype :data:`BF16`.
+  uint16 bit patterns under the marker dtype :data:`BF16`; FP8 inputs are
+  the round-to-nearest-even OCP E4M3 value (:func:`to_e4m3`), bytes under
+  :data:`F8`.
 
 Streams: A uses stream 0 and B stream 1.  The workloads draw i.i.d.
 uniform[-1, 1) entries from seed 0, the synthetic square and rectangular
@@ -41,6 +43,19 @@ STREAM_B = 1
 # bfloat16 bit patterns: a one-field structured dtype over uint16 (numpy has
 # no bfloat16); ``x.view(np.uint16)`` gives the bits.
 BF16 = np.dtype([("bf16", "<u2")])
+# FP8 E4M3 (OCP) byte patterns: 1 sign, 4 exponent (bias 7), 3 fraction
+# bits, no infinities, 0x7F / 0xFF NaN, largest finite 448.
+F8 = np.dtype([("e4m3", "u1")])
+
+
+def _e4m3_table() -> np.ndarray:
+    """float64 value of each non-negative code 0x00..0x7E (increasing)."""
+    codes = np.arange(0x7F)
+    e, f = codes >> 3, codes & 7
+    return np.where(e == 0, f * 2.0 ** -9, (8 + f) * 2.0 ** (e.astype(np.float64) - 10))
+
+
+_E4M3 = _e4m3_table()
 
 
 def mix64_int(z: int) -> int:
@@ -128,6 +143,35 @@ def bf16_to_f32(b) -> np.ndarray:
     return (bits << np.uint32(16)).view(np.float32)
 
 
+def to_e4m3(x) -> np.ndarray:
+    """float32 values to FP8 E4M3 byte patterns (dtype F8), rounding to
+    nearest with ties to even; magnitudes past 464 (halfway above 448) and
+    NaN become NaN (0x7F with the sign)."""
+    v = np.array(x, dtype=np.float64, order="C")
+    mag = np.abs(v)
+    hi = np.clip(np.searchsorted(_E4M3, mag, side="left"), 0, len(_E4M3) - 1)
+    lo = np.maximum(hi - 1, 0)
+    d_lo, d_hi = mag - _E4M3[lo], _E4M3[hi] - mag
+    # nearest; on a tie the even code (its lowest fraction bit is 0)
+    pick = np.where((d_lo < d_hi) | ((d_lo == d_hi) & (lo % 2 == 0)), lo, hi)
+    pick = np.where(mag <= _E4M3[0], 0, pick)
+    code = np.where(np.isnan(mag) | (mag > 464.0), 0x7F, pick).astype(np.uint8)
+    code = code | (np.signbit(v).astype(np.uint8) << np.uint8(7))
+    return code.view(F8)
+
+
+def e4m3_to_f32(b) -> np.ndarray:
+    """FP8 E4M3 byte patterns (F8 or uint8) to float32 (exact)."""
+    codes = np.array(np.asarray(b).view(np.uint8), order="C")
+    mag = np.where((codes & 0x7F) == 0x7F, np.nan, _E4M3[np.minimum(codes & 0x7F, 0x7E)])
+    return np.where(codes & 0x80, -mag, mag).astype(np.float32)
+
+
+def uniform_f8(seed: int, stream: int, rows: int, cols: int) -> np.ndarray:
+    """The FP32 matrix of :func:`uniform_f32` rounded to FP8 E4M3 (RNE)."""
+    return to_e4m3(uniform_f32(seed, stream, rows, cols))
+
+
 def uniform_bf16(seed: int, stream: int, rows: int, cols: int) -> np.ndarray:
     """The FP32 matrix of :func:`uniform_f32` rounded to bfloat16 (RNE)."""
     return to_bf16(uniform_f32(seed, stream, rows, cols))
@@ -141,6 +185,8 @@ def small_int(seed: int, stream: int, rows: int, cols: int, lo: int = -2,
     n = rows * cols
     if dtype == BF16:
         return to_bf16(small_int(seed, stream, rows, cols, lo, hi, np.float32))
+    if dtype == F8:
+        return to_e4m3(small_int(seed, stream, rows, cols, lo, hi, np.float32))
     if n == 0:
         return np.zeros((rows, cols), dtype=dtype)
     u = stream_u64(seed, stream, n) >> np.uint64(32)
@@ -165,4 +211,6 @@ def workload(M: int, N: int, K: int, dtype: str, seed: int = 0):
         return (uniform_f16(seed, STREAM_A, M, K), uniform_f16(seed, STREAM_B, K, N))
     if dtype == "bf16":
         return (uniform_bf16(seed, STREAM_A, M, K), uniform_bf16(seed, STREAM_B, K, N))
+    if dtype == "f8":
+        return (uniform_f8(seed, STREAM_A, M, K), uniform_f8(seed, STREAM_B, K, N))
     raise ValueError(f"unknown dtype {dtype!r}")

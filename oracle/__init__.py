@@ -17,10 +17,12 @@ marshals numpy arrays:
 * :func:`check` -- ``max_ij |C_gpu - C_ref| / D`` plus counts.
 * :func:`f16_to_f64` -- exact IEEE binary16 decoding.
 * :func:`bf16_to_f64` -- exact bfloat16 decoding.
+* :func:`e4m3_to_f64` -- exact FP8 E4M3 decoding.
 
-Element types: float32, float16 (or uint16 binary16 bit patterns), and
+Element types: float32, float16 (or uint16 binary16 bit patterns),
 bfloat16 as uint16 bit patterns viewed with the marker dtype :data:`BF16`
-(numpy has no bfloat16 type).
+(numpy has no bfloat16 type), and FP8 E4M3 as bytes under :data:`F8`.
+An FP8 product's C (and the old C of its fused epilogue) is bfloat16.
 
 Parity status: pinned (see the oracle tests in ``tests/``).
 """
@@ -48,12 +50,17 @@ HGEMM_TOL = 2e-3
 # BF16 output: unit roundoff 2**-8 (RNE to 8 significant bits), plus at most
 # K * 2**-24 for FP32 accumulation of exact products at K <= 8192.
 BF16_TOL = 5e-3
+# FP8 E4M3 inputs, FP32 accumulation, BF16 output: products are exact in
+# FP32 (4 x 4 significant bits), so the bound is BF16's.
+F8_TOL = 5e-3
 
 # bfloat16 bit patterns: a one-field structured dtype over uint16, so that a
 # BF16 matrix cannot be mistaken for binary16 or plain integers.
 BF16 = np.dtype([("bf16", "<u2")])
+# FP8 E4M3 (OCP) byte patterns, the same way.
+F8 = np.dtype([("e4m3", "u1")])
 
-TOL = {"f32": SGEMM_TOL, "f16": HGEMM_TOL, "bf16": BF16_TOL}
+TOL = {"f32": SGEMM_TOL, "f16": HGEMM_TOL, "bf16": BF16_TOL, "f8": F8_TOL}
 
 
 def build(src: str = _SRC, out: str = _LIB, extra_flags=()) -> str:
@@ -75,15 +82,22 @@ def _declare(lib):
     lib.oracle_bf16_to_f64.restype = ctypes.c_double
     lib.oracle_bf16_array_to_f64.argtypes = [p, p, i64]
     lib.oracle_bf16_array_to_f64.restype = None
-    for name in ("oracle_gemm_rows_f32", "oracle_gemm_rows_f16", "oracle_gemm_rows_bf16"):
+    lib.oracle_e4m3_to_f64.argtypes = [ctypes.c_uint8]
+    lib.oracle_e4m3_to_f64.restype = ctypes.c_double
+    lib.oracle_e4m3_array_to_f64.argtypes = [p, p, i64]
+    lib.oracle_e4m3_array_to_f64.restype = None
+    for name in ("oracle_gemm_rows_f32", "oracle_gemm_rows_f16", "oracle_gemm_rows_bf16",
+                 "oracle_gemm_rows_f8"):
         fn = getattr(lib, name)
         fn.argtypes = [i64, i64, i64, p, i64, p, i64, p, p, i64, p, i64, ctypes.c_int]
         fn.restype = ctypes.c_int
-    for name in ("oracle_gemm_entries_f32", "oracle_gemm_entries_f16", "oracle_gemm_entries_bf16"):
+    for name in ("oracle_gemm_entries_f32", "oracle_gemm_entries_f16", "oracle_gemm_entries_bf16",
+                 "oracle_gemm_entries_f8"):
         fn = getattr(lib, name)
         fn.argtypes = [i64, p, i64, p, i64, p, p, i64, p, p]
         fn.restype = ctypes.c_int
-    for name in ("oracle_gemm_rows_bt_f32", "oracle_gemm_rows_bt_f16", "oracle_gemm_rows_bt_bf16"):
+    for name in ("oracle_gemm_rows_bt_f32", "oracle_gemm_rows_bt_f16", "oracle_gemm_rows_bt_bf16",
+                 "oracle_gemm_rows_bt_f8"):
         fn = getattr(lib, name)
         fn.argtypes = [i64, i64, i64, p, i64, p, i64, p, p, i64, p, i64]
         fn.restype = ctypes.c_int
@@ -147,6 +161,8 @@ def _kind(a: np.ndarray) -> str:
         return "f16"
     if a.dtype == BF16:
         return "bf16"
+    if a.dtype == F8:
+        return "f8"
     raise TypeError(f"unsupported dtype {a.dtype}")
 
 
@@ -155,10 +171,17 @@ def _bits16(a: np.ndarray) -> np.ndarray:
 
 
 def _raw(a: np.ndarray, kind: str) -> tuple[np.ndarray, type]:
-    """The array as the C routines take it (float32, or uint16 bits)."""
+    """The array as the C routines take it (float32, uint16 or uint8 bits)."""
     if kind == "f32":
         return a, np.float32
+    if kind == "f8":
+        return a.view(np.uint8), np.uint8
     return _bits16(a), np.uint16
+
+
+def out_kind(kind: str) -> str:
+    """The element type of C for inputs of `kind` (FP8 products are BF16)."""
+    return "bf16" if kind == "f8" else kind
 
 
 def gemm_rows(A: np.ndarray, B: np.ndarray, rows=None, threads: int | None = None,
@@ -242,17 +265,19 @@ def gemm_rows_epi(A: np.ndarray, B: np.ndarray, C0, alpha: float, beta: float, b
                   act: int = ACT_NONE, rows=None, threads: int | None = None, lib=None):
     """C_ref and D of the fused-epilogue product
     act(alpha * (A @ B) + beta * C0 + bias[j]) for the rows ``rows`` (all
-    when None).  C0 (M x N, the type of A) is read only when beta != 0; bias
-    is None or N float32 values; act is ACT_NONE or ACT_RELU."""
+    when None).  C0 (M x N, the type of C) is read only when beta != 0; bias
+    is None or N float32 values; act is ACT_NONE or ACT_RELU.  For FP8
+    inputs C0 is BF16, the type of their C."""
     lib = lib or load()
     C, D = gemm_rows(A, B, rows=rows, threads=threads, lib=lib)
     kind = _kind(A)
     M, N = A.shape[0], B.shape[1]
     c0_ptr, ldc0, keep = None, max(N, 1), []
+    ok = out_kind(kind)
     if beta != 0.0:
-        if _kind(C0) != kind:
-            raise TypeError("C0 must have the element type of A")
-        C0m, dt = _raw(C0, kind)
+        if _kind(C0) != ok:
+            raise TypeError("C0 must have the element type of C")
+        C0m, dt = _raw(C0, ok)
         C0m, ldc0 = _as_matrix(C0m, dt)
         if C0m.shape != (M, N):
             raise ValueError("C0 must be M x N")
@@ -267,7 +292,7 @@ def gemm_rows_epi(A: np.ndarray, B: np.ndarray, C0, alpha: float, beta: float, b
     rows_arr = None if rows is None else np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
     rp = None if rows_arr is None else _ptr(rows_arr)
     if C.size:
-        fn = getattr(lib, f"oracle_epilogue_rows_{kind}")
+        fn = getattr(lib, f"oracle_epilogue_rows_{ok}")
         rc = fn(C.shape[0], N, float(alpha), float(beta), c0_ptr, ldc0, b_ptr, int(act), rp,
                 _ptr(C), N, _ptr(D), N)
         if rc != 0:
@@ -349,4 +374,15 @@ def bf16_to_f64(bits) -> np.ndarray:
     out = np.empty(b.shape, dtype=np.float64)
     if b.size:
         lib.oracle_bf16_array_to_f64(_ptr(b), _ptr(out), b.size)
+    return out
+
+
+def e4m3_to_f64(bits) -> np.ndarray:
+    """Exact decode of FP8 E4M3 byte patterns (:data:`F8` or uint8 array)."""
+    lib = load()
+    b = np.asarray(bits)
+    b = np.ascontiguousarray(b.view(np.uint8) if b.dtype == F8 else b.astype(np.uint8, copy=False))
+    out = np.empty(b.shape, dtype=np.float64)
+    if b.size:
+        lib.oracle_e4m3_array_to_f64(_ptr(b), _ptr(out), b.size)
     return out

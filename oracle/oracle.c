@@ -32,7 +32,9 @@
  * binary32, the 16-bit type the GB300 GEMM article lists beside FP16 in
  * sections 1.1 and 5.1) arrive as bit patterns too and have a decoder of
  * their own; a BF16 x BF16 product carries at most 16 significant bits, so
- * it is exact in double as well.
+ * it is exact in double as well.  FP8 inputs (OCP E4M3: the 8-bit type the
+ * GB300 GEMM article puts a tier above FP16 in section 1.1) arrive as byte
+ * patterns with a decoder of their own (4 significant bits, products exact).
  *
  * Parity status: pinned.  The pins (identity, permutation, all-ones closed
  * form C_ij = K, rank-1 outer products, K = 0 and K = 1, brute force against
@@ -106,15 +108,44 @@ void oracle_bf16_array_to_f64(const uint16_t *src, double *dst, int64_t n)
 }
 
 /* ---------------------------------------------------------------------- */
+/* FP8 E4M3 (OCP) -> binary64, exact.                                      */
+/* Layout: 1 sign bit, 4 exponent bits (bias 7), 3 fraction bits; no       */
+/* infinities: exponent 15 with fraction 7 is NaN, the rest are finite     */
+/* (largest 448); exponent 0 holds zeros and subnormals (fraction * 2^-9). */
+/* ---------------------------------------------------------------------- */
+double oracle_e4m3_to_f64(uint8_t b)
+{
+    const int sign = (b >> 7) & 1;
+    const int expo = (b >> 3) & 0xf;
+    const int frac = b & 0x7;
+    double mag;
+    if (expo == 0xf && frac == 0x7)
+        mag = NAN;
+    else if (expo == 0)
+        mag = ldexp((double)frac, -9);
+    else
+        mag = ldexp((double)(0x8 | frac), expo - 10);
+    return sign ? -mag : mag;
+}
+
+void oracle_e4m3_array_to_f64(const uint8_t *src, double *dst, int64_t n)
+{
+    for (int64_t t = 0; t < n; ++t)
+        dst[t] = oracle_e4m3_to_f64(src[t]);
+}
+
+/* ---------------------------------------------------------------------- */
 /* Input access: element (i, k) of a row-major matrix with leading         */
 /* dimension ld lives at base[i * ld + k].                                  */
 /* ---------------------------------------------------------------------- */
-enum { ORACLE_F32 = 0, ORACLE_F16 = 1, ORACLE_BF16 = 2 };
+enum { ORACLE_F32 = 0, ORACLE_F16 = 1, ORACLE_BF16 = 2, ORACLE_E4M3 = 3 };
 
 static double load_elem(const void *base, int dtype, int64_t idx)
 {
     if (dtype == ORACLE_F32)
         return (double)((const float *)base)[idx];
+    if (dtype == ORACLE_E4M3)
+        return oracle_e4m3_to_f64(((const uint8_t *)base)[idx]);
     if (dtype == ORACLE_BF16)
         return oracle_bf16_to_f64(((const uint16_t *)base)[idx]);
     return oracle_f16_to_f64(((const uint16_t *)base)[idx]);
@@ -242,6 +273,15 @@ int oracle_gemm_rows_bf16(int64_t nrows, int64_t N, int64_t K,
                     nthreads);
 }
 
+int oracle_gemm_rows_f8(int64_t nrows, int64_t N, int64_t K,
+                        const uint8_t *A, int64_t lda, const uint8_t *B, int64_t ldb,
+                        const int64_t *rows, double *C, int64_t ldr,
+                        double *D, int64_t ldd, int nthreads)
+{
+    return run_rows(ORACLE_E4M3, nrows, N, K, A, lda, B, ldb, rows, C, ldr, D, ldd,
+                    nthreads);
+}
+
 /*
  * Rows of C_ref and D for B given transposed: Bt is the N x K row-major
  * matrix with Bt[j][k] = B[k][j] (B column-major, the layout of the
@@ -311,6 +351,13 @@ int oracle_gemm_rows_bt_bf16(int64_t nrows, int64_t N, int64_t K, const uint16_t
                              double *C, int64_t ldr, double *D, int64_t ldd)
 {
     return run_rows_bt(ORACLE_BF16, nrows, N, K, A, lda, Bt, ldbt, rows, C, ldr, D, ldd);
+}
+
+int oracle_gemm_rows_bt_f8(int64_t nrows, int64_t N, int64_t K, const uint8_t *A,
+                           int64_t lda, const uint8_t *Bt, int64_t ldbt, const int64_t *rows,
+                           double *C, int64_t ldr, double *D, int64_t ldd)
+{
+    return run_rows_bt(ORACLE_E4M3, nrows, N, K, A, lda, Bt, ldbt, rows, C, ldr, D, ldd);
 }
 
 /*
@@ -425,6 +472,13 @@ int oracle_gemm_entries_bf16(int64_t K, const uint16_t *A, int64_t lda,
                              const int64_t *jj, int64_t n, double *c, double *d)
 {
     return run_entries(ORACLE_BF16, K, A, lda, B, ldb, ii, jj, n, c, d);
+}
+
+int oracle_gemm_entries_f8(int64_t K, const uint8_t *A, int64_t lda,
+                           const uint8_t *B, int64_t ldb, const int64_t *ii,
+                           const int64_t *jj, int64_t n, double *c, double *d)
+{
+    return run_entries(ORACLE_E4M3, K, A, lda, B, ldb, ii, jj, n, c, d);
 }
 
 /* ---------------------------------------------------------------------- */

@@ -12,9 +12,11 @@ yuyanqi.com, section 1.1).  The pages print no worked matrices, so the pins
 are closed forms (identity, permutation, all-ones C_ij = K, rank-1 outer
 products, K = 0, K = 1), brute force against exact rational arithmetic, a
 float64 library matmul, and the exhaustive binary16 and bfloat16 tables.
-Every structural pin runs for FP32, FP16 and BF16 inputs (BF16 as bit
-patterns under the marker dtype; values are built and widened here through
-the binary32 definition of bfloat16, independently of the oracle's decoder).
+Every structural pin runs for FP32, FP16, BF16 and FP8 E4M3 inputs (BF16
+and FP8 as bit patterns under marker dtypes; values are built and widened
+here through the seeded-input module's conversions, which are checked
+against torch's, independently of the oracle's decoders).  An FP8
+product's C, and the old C of its epilogue, is BF16.
 """
 from __future__ import annotations
 
@@ -31,6 +33,12 @@ U64 = 2.0 ** -53  # unit roundoff of binary64
 
 
 BF16 = synth.BF16
+F8 = synth.F8
+
+
+def _out(dt):
+    """Element type of C for inputs of type dt."""
+    return BF16 if dt == F8 else dt
 
 
 def _make(x, dt) -> np.ndarray:
@@ -38,6 +46,8 @@ def _make(x, dt) -> np.ndarray:
     x = np.asarray(x, dtype=np.float64)
     if dt == BF16:
         return synth.to_bf16(x.astype(np.float32))
+    if dt == F8:
+        return synth.to_e4m3(x.astype(np.float32))
     return x.astype(dt)
 
 
@@ -45,6 +55,8 @@ def _wide(x: np.ndarray) -> np.ndarray:
     """The exact values of x as float64."""
     if x.dtype == BF16:
         return synth.bf16_to_f32(x).astype(np.float64)
+    if x.dtype == F8:
+        return synth.e4m3_to_f32(x).astype(np.float64)
     return x.astype(np.float64)
 
 
@@ -58,7 +70,7 @@ def _padded(x: np.ndarray, pad: int) -> np.ndarray:
 
 
 def _dtypes():
-    return (np.float32, np.float16, BF16)
+    return (np.float32, np.float16, BF16, F8)
 
 
 def _rand(dtype, seed, stream, r, c):
@@ -66,6 +78,8 @@ def _rand(dtype, seed, stream, r, c):
         return synth.uniform_f32(seed, stream, r, c)
     if dtype == BF16:
         return synth.uniform_bf16(seed, stream, r, c)
+    if dtype == F8:
+        return synth.uniform_f8(seed, stream, r, c)
     return synth.uniform_f16(seed, stream, r, c)
 
 
@@ -169,7 +183,7 @@ def pin_bruteforce_fractions(lib, trials: int = 60):
     exact sum of |a||b|."""
     rng = random.Random(1234)
     for trial in range(trials):
-        dt = _dtypes()[trial % 3]
+        dt = _dtypes()[trial % len(_dtypes())]
         M, N, K = rng.randint(1, 6), rng.randint(1, 6), rng.randint(1, 6)
         A = _rand(dt, 100 + trial, 0, M, K)
         B = _rand(dt, 100 + trial, 1, K, N)
@@ -256,6 +270,28 @@ def pin_bf16_decode(lib):
             assert got == v and np.signbit(got) == np.signbit(v), f"bf16 decode 0x{b:04x}"
 
 
+def pin_e4m3_decode(lib):
+    """Exhaustive FP8 E4M3 decode against torch's float8_e4m3fn (a library
+    routine) widened to float64, plus the hand-worked patterns of
+    tests/golden/float8_e4m3_patterns.txt."""
+    import torch
+    bits = np.arange(256, dtype=np.uint8)
+    out = np.empty(bits.shape, dtype=np.float64)
+    lib.oracle_e4m3_array_to_f64(bits.ctypes.data, out.ctypes.data, bits.size)
+    ref = torch.from_numpy(bits).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(out), nan), "e4m3 NaN patterns"
+    assert np.array_equal(out[~nan], ref[~nan]), "e4m3 decoded values"
+    assert np.array_equal(np.signbit(out[~nan]), np.signbit(ref[~nan])), "e4m3 signs"
+    for bits_s, val_s in golden_data.rows("float8_e4m3_patterns.txt"):
+        b, v = int(bits_s, 16), float.fromhex(val_s) if "p" in val_s else float(val_s)
+        got = lib.oracle_e4m3_to_f64(b)
+        if np.isnan(v):
+            assert np.isnan(got), f"e4m3 decode 0x{b:02x}"
+        else:
+            assert got == v and np.signbit(got) == np.signbit(v), f"e4m3 decode 0x{b:02x}"
+
+
 def _decode(lib, bits):
     out = np.empty(bits.shape, dtype=np.float64)
     lib.oracle_f16_array_to_f64(bits.ctypes.data, out.ctypes.data, bits.size)
@@ -304,7 +340,7 @@ def pin_epilogue_closed_form(lib):
     for dt in _dtypes():
         M, N, K = 5, 7, 6
         A, B = _make(np.ones((M, K)), dt), _make(np.ones((K, N)), dt)
-        C0 = synth.small_int(31, 2, M, N, -3, 3, dtype=dt)
+        C0 = synth.small_int(31, 2, M, N, -3, 3, dtype=_out(dt))
         bias = (np.arange(N) - 3).astype(np.float32)
         rows = [4, 1]
         c0 = _wide(C0)[rows]
@@ -323,7 +359,7 @@ def pin_epilogue_reduces_to_plain(lib):
     (C0 full of NaN must not leak in: beta = 0 means C is not read)."""
     for dt in _dtypes():
         A, B = _rand(dt, 41, 0, 9, 13), _rand(dt, 41, 1, 13, 6)
-        C0 = _make(np.full((9, 6), np.nan), dt)
+        C0 = _make(np.full((9, 6), np.nan), _out(dt))
         C, D = oracle.gemm_rows_epi(A, B, C0, 1.0, 0.0, None, 0, lib=lib)
         Cp, Dp = oracle.gemm_rows(A, B, lib=lib)
         assert np.array_equal(C, Cp) and np.array_equal(D, Dp), "plain special case"
@@ -340,7 +376,7 @@ def pin_epilogue_bruteforce(lib, trials: int = 30):
         for dt in _dtypes():
             M, N, K = rng.randint(1, 4), rng.randint(1, 4), rng.randint(1, 5)
             A, B = _rand(dt, 100 + t, 0, M, K), _rand(dt, 100 + t, 1, K, N)
-            C0 = _rand(dt, 100 + t, 2, M, N)
+            C0 = _rand(_out(dt), 100 + t, 2, M, N)
             bias = _rand(np.float32, 100 + t, 3, 1, N).ravel()
             alpha, beta = rng.choice([1.0, -0.75, 3.0]), rng.choice([0.0, 0.5, -2.0])
             act = rng.choice([0, 1])
@@ -406,6 +442,7 @@ def pin_bt_rank1(lib):
 
 PINS = [pin_identity, pin_permutation, pin_all_ones, pin_rank1, pin_k0_k1,
         pin_bruteforce_fractions, pin_numpy_matmul, pin_f16_decode, pin_bf16_decode,
+        pin_e4m3_decode,
         pin_error_metric, pin_epilogue_closed_form, pin_epilogue_reduces_to_plain,
         pin_epilogue_bruteforce, pin_bt_identity_permutation, pin_bt_matches_plain_transpose,
         pin_bt_rank1]

@@ -47,6 +47,14 @@ MUTANTS = {
                             "const int expo = (h >> 8) & 0x7f;\n    const int frac = h & 0xff;"),
     "bf16_decoded_as_f16": ("    if (dtype == ORACLE_BF16)\n        return oracle_bf16_to_f64",
                             "    if (0)\n        return oracle_bf16_to_f64"),
+    "e4m3_bias": ("mag = ldexp((double)(0x8 | frac), expo - 10);",
+                  "mag = ldexp((double)(0x8 | frac), expo - 11);"),
+    "e4m3_no_hidden_bit": ("mag = ldexp((double)(0x8 | frac), expo - 10);",
+                           "mag = ldexp((double)frac, expo - 10);"),
+    "e4m3_subnormal": ("mag = ldexp((double)frac, -9);", "mag = ldexp((double)frac, -10);"),
+    "e4m3_all_top_exponent_nan": ("if (expo == 0xf && frac == 0x7)", "if (expo == 0xf)"),
+    "e4m3_decoded_as_f16": ("    if (dtype == ORACLE_E4M3)\n        return oracle_e4m3_to_f64",
+                            "    if (0)\n        return oracle_e4m3_to_f64"),
     "entries_drop_k": ("for (int64_t k = 0; k < K; ++k) {",
                        "for (int64_t k = 0; k + 1 < K; ++k) {"),
     "metric_absolute": ("r = diff / den;", "r = diff;"),

@@ -87,3 +87,24 @@ def test_bf16_workload_is_rounded_f32():
     assert np.all(np.abs(synth.bf16_to_f32(A) - a32) <= np.abs(a32) * 2.0 ** -8 + 1e-38)
     ints = synth.small_int(4, 1, 6, 6, dtype=synth.BF16)
     assert np.array_equal(synth.bf16_to_f32(ints), synth.small_int(4, 1, 6, 6))
+
+
+def test_to_e4m3_matches_torch():
+    """RNE onto FP8 E4M3 against torch's float32 -> float8_e4m3fn (a
+    library routine): the workload's values, ties (1 + 2**-4 is half an ulp
+    above 1 -> 1.0; 1 + 3 * 2**-4 ties to 1.25), subnormals, the top of the
+    range (448; past 464 is NaN) and signed zeros; and the decode back."""
+    import torch
+    x = np.concatenate([synth.uniform_f32(5, 0, 200, 200).ravel(),
+                        np.array([1 + 2.0 ** -4, 1 + 3 * 2.0 ** -4, -1.5, 448.0, 463.0, 464.0, 465.0,
+                                  2.0 ** -9, 3 * 2.0 ** -10, 2.0 ** -11, 0.0, -0.0], np.float32)])
+    mine = synth.to_e4m3(x).view(np.uint8)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(mine, ref)
+    back = synth.e4m3_to_f32(mine)
+    tref = torch.from_numpy(ref).view(torch.float8_e4m3fn).float().numpy()
+    assert np.array_equal(np.isnan(back), np.isnan(tref))
+    ok = ~np.isnan(tref)
+    assert np.array_equal(back[ok], tref[ok])
+    ints = synth.small_int(4, 1, 6, 6, dtype=synth.F8)
+    assert np.array_equal(synth.e4m3_to_f32(ints), synth.small_int(4, 1, 6, 6))
