@@ -26,10 +26,10 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_TFLOPS = {"f32": 157.3, "f16": 2516.6, "bf16": 2516.6}  # MI355X dense matrix peaks
+PEAK_TFLOPS = {"f32": 157.3, "f16": 2516.6, "bf16": 2516.6, "f8": 5033.2}  # MI355X dense matrix peaks
 WORKLOAD_NAME = {("f32", "f16"): "sgemm+hgemm"}
 STEP_NAME = {"f32": "SGEMM fp32", "f16": "HGEMM fp16-in fp32-acc fp16-out",
-             "bf16": "BF16 GEMM bf16-in fp32-acc bf16-out"}
+             "bf16": "BF16 GEMM bf16-in fp32-acc bf16-out", "f8": "FP8 GEMM e4m3-in fp32-acc bf16-out"}
 HBM_PEAK_GBS = 8000.0
 
 
@@ -40,10 +40,11 @@ def parse_args():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--size", type=int, default=4096, help="M = N = K")
     ap.add_argument("--dtypes", default="f32,f16",
-                    help="kernels in one step (f32, f16, bf16; the headline step is f32,f16)")
+                    help="kernels in one step (f32, f16, bf16, f8; the headline step is f32,f16)")
     ap.add_argument("--f32-config", default=None, help="force an FP32 variant by name")
     ap.add_argument("--f16-config", default=None, help="force an FP16 variant by name")
     ap.add_argument("--bf16-config", default=None, help="force a BF16 variant by name")
+    ap.add_argument("--f8-config", default=None, help="force an FP8 variant by name")
     ap.add_argument("--order", type=int, default=None, help="force the tile order")
     ap.add_argument("--group-m", type=int, default=None, help="force the band height")
     ap.add_argument("--cpu-budget", type=float, default=20.0,
@@ -65,7 +66,8 @@ def parse_args():
 # Kernel source of each variant family (the traffic figures are tied to it).
 FAMILY_SOURCE = {"dl_f32": "sgemm_dl.hip", "mfma_f32": "sgemm_mfma.hip", "simt_f32": "sgemm_simt.hip",
                  "mfma_f16": "hgemm_mfma.hip", "pipe_f16": "hgemm_pipe.hip",
-                 "tr_f16": "hgemm_tr.hip", "mfma_bf16": "hgemm_mfma.hip", "tr_bf16": "hgemm_tr.hip"}
+                 "tr_f16": "hgemm_tr.hip", "mfma_bf16": "hgemm_mfma.hip", "tr_bf16": "hgemm_tr.hip",
+                 "tr_f8": "hgemm_tr.hip"}
 
 
 def kernel_digest(variant: str) -> str:
@@ -137,13 +139,18 @@ def main():
     host = {"f32": (A32, B32), "f16": (A32.astype(np.float16), B32.astype(np.float16))}
     if "bf16" in kinds:
         host["bf16"] = (synth.to_bf16(A32), synth.to_bf16(B32))
+    if "f8" in kinds:
+        host["f8"] = (synth.to_e4m3(A32), synth.to_e4m3(B32))
     gen_s = time.time() - t0
-    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
-    dcode = {"f32": gemm.DTYPE_F32, "f16": gemm.DTYPE_F16, "bf16": gemm.DTYPE_BF16}
+    # Type of C (FP8 products are BF16).
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16, "f8": torch.bfloat16}
+    dcode = {"f32": gemm.DTYPE_F32, "f16": gemm.DTYPE_F16, "bf16": gemm.DTYPE_BF16, "f8": gemm.DTYPE_F8}
 
-    def to_dev(x):  # BF16 travels as its bit patterns
+    def to_dev(x):  # BF16 and FP8 travel as their bit patterns
         if x.dtype == synth.BF16:
             return torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+        if x.dtype == synth.F8:
+            return torch.from_numpy(x.view(np.uint8)).to(dev).view(torch.float8_e4m3fn)
         return torch.from_numpy(x).to(dev)
 
     def from_dev(t):
@@ -163,7 +170,8 @@ def main():
     cfgs = {}
     for k in kinds:
         dt = dcode[k]
-        name = {"f32": args.f32_config, "f16": args.f16_config, "bf16": args.bf16_config}[k]
+        name = {"f32": args.f32_config, "f16": args.f16_config, "bf16": args.bf16_config,
+                "f8": args.f8_config}[k]
         c = gemm.config_by_name(dt, name) if name else gemm.gemm_select_config(dt, n, n, n)
         if args.order is not None:
             c.order = args.order
@@ -279,13 +287,14 @@ def main():
     for i, k in enumerate(kinds):
         mean = marks[i].elapsed_time(marks[i + 1]) / args.steps
         elem = 4 if k == "f32" else 2
+        in_elem = 1 if k == "f8" else elem
         kernels[k] = {
             "variant": cfgs[k].name.decode(), "order": cfgs[k].order, "group_m": cfgs[k].group_m,
             "ms_mean": round(mean, 5),
             "tflops": round(flops / (mean * 1e-3) / 1e12, 2),
             "pct_peak": round(100.0 * flops / (mean * 1e-3) / 1e12 / PEAK_TFLOPS[k], 2),
             "peak_tflops": PEAK_TFLOPS[k],
-            "min_bytes_per_launch": 3 * n * n * elem,
+            "min_bytes_per_launch": n * n * (2 * in_elem + elem),
         }
 
     dom = max(kinds, key=lambda k: kernels[k]["ms_mean"])

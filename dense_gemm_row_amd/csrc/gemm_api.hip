@@ -57,13 +57,19 @@ gemm_status_t fail(gemm_status_t st, const char* fmt, ...) {
   return st;
 }
 
-constexpr int kDtypes = 3;  // F32, F16, BF16
+constexpr int kDtypes = 4;  // F32, F16, BF16, F8 (E4M3 in, BF16 out)
 
-bool valid_dtype(int d) { return d == GEMM_DTYPE_F32 || d == GEMM_DTYPE_F16 || d == GEMM_DTYPE_BF16; }
+bool valid_dtype(int d) { return d >= GEMM_DTYPE_F32 && d <= GEMM_DTYPE_F8; }
 
 const char* dtype_name(int d) {
-  return d == GEMM_DTYPE_F32 ? "f32" : d == GEMM_DTYPE_F16 ? "f16" : "bf16";
+  return d == GEMM_DTYPE_F32 ? "f32" : d == GEMM_DTYPE_F16 ? "f16" : d == GEMM_DTYPE_BF16 ? "bf16" : "f8";
 }
+
+// Bytes of one A / B element and of one C element.
+size_t in_bytes(int d) { return d == GEMM_DTYPE_F32 ? 4 : d == GEMM_DTYPE_F8 ? 1 : 2; }
+size_t out_bytes(int d) { return d == GEMM_DTYPE_F32 ? 4 : 2; }
+// The type of C (the split-K reduction writes it).
+int out_dtype(int d) { return d == GEMM_DTYPE_F8 ? GEMM_DTYPE_BF16 : d; }
 
 struct Table {
   std::vector<Variant> v[kDtypes];  // per dtype
@@ -81,10 +87,12 @@ struct Table {
     v[1].insert(v[1].end(), p, p + n);
     p = hgemm_mfma_variants(&n);
     v[1].insert(v[1].end(), p, p + n);
-    p = hgemm_tr_variants(&n, true);
+    p = hgemm_tr_variants(&n, 1);
     v[2].insert(v[2].end(), p, p + n);
     p = hgemm_mfma_variants(&n, true);
     v[2].insert(v[2].end(), p, p + n);
+    p = hgemm_tr_variants(&n, 2);
+    v[3].insert(v[3].end(), p, p + n);
     for (int d = 0; d < kDtypes; ++d)
       for (size_t i = 0; i < v[d].size(); ++i) v[d][i].desc.id = (int32_t)i;
   }
@@ -141,7 +149,7 @@ struct Choice {
 
 double gemm_seconds(int dtype, const Variant& v, int64_t M, int64_t N, int64_t Kc, int64_t S) {
   const gemm_config_t& d = v.desc;
-  const double rate = dtype == GEMM_DTYPE_F32 ? 0.59e12 : 4.7e12;
+  const double rate = dtype == GEMM_DTYPE_F32 ? 0.59e12 : dtype == GEMM_DTYPE_F8 ? 9.4e12 : 4.7e12;
   int64_t per_cu = (160 * 1024) / (d.lds_bytes > 0 ? d.lds_bytes : 1);
   per_cu = per_cu < 1 ? 1 : per_cu > 2 ? 2 : per_cu;
   const int64_t wgs = cdiv(M, d.bm) * cdiv(N, d.bn) * S;
@@ -156,7 +164,7 @@ double gemm_seconds(int dtype, const Variant& v, int64_t M, int64_t N, int64_t K
 Choice heuristic(int dtype, int64_t M, int64_t N, int64_t K, bool allow_split, bool need_epi = false,
                  bool need_bt = false) {
   const auto& v = table().v[dtype];
-  const double es = dtype == GEMM_DTYPE_F32 ? 4.0 : 2.0;
+  const double es = (double)out_bytes(dtype);
   Choice best;
   for (size_t i = 0; i < v.size(); ++i) {
     if (v[i].desc.family != GEMM_FAMILY_MFMA) continue;
@@ -236,8 +244,8 @@ gemm_status_t validate(int dtype, int64_t M, int64_t N, int64_t K, const void* A
   if (M > 0 && N > 0 && !C) return fail(GEMM_ERR_INVALID_ARG, "C is NULL");
   const int64_t tiles_lim = 0x7fffffff;
   if (cdiv(M, 64) * cdiv(N, 64) > tiles_lim) return fail(GEMM_ERR_INVALID_ARG, "output too large");
-  const size_t es = dtype == GEMM_DTYPE_F32 ? 4 : 2;
-  const size_t cb = span_bytes(M, N, ldc, es);
+  const size_t es = in_bytes(dtype);
+  const size_t cb = span_bytes(M, N, ldc, out_bytes(dtype));
   if (overlap(C, cb, A, span_bytes(M, K, lda, es)) ||
       overlap(C, cb, B, bt ? span_bytes(N, K, ldb, es) : span_bytes(K, N, ldb, es)))
     return fail(GEMM_ERR_ALIAS, "C overlaps A or B");
@@ -279,7 +287,7 @@ gemm_status_t resolve(int dtype, int64_t M, int64_t N, int64_t K, const gemm_con
       split_shape(K, want, S, Kc);
       if (S != want) continue;
       if (want > 1 && (Kc < 256 || !v[forced->id].launch_partial)) break;
-      const double es = dtype == GEMM_DTYPE_F32 ? 4.0 : 2.0;
+      const double es = (double)out_bytes(dtype);
       const double t = gemm_seconds(dtype, v[forced->id], M, N, Kc, S) +
                        (S > 1 ? (2.0 * S * M * N * 4.0 + M * N * es) / 4.0e12 + 4e-6 : 0.0);
       if (t < best) {
@@ -293,9 +301,18 @@ gemm_status_t resolve(int dtype, int64_t M, int64_t N, int64_t K, const gemm_con
 
 bool vector_path(int dtype, const void* A, int64_t lda, const void* B, int64_t ldb, const void* C,
                  int64_t ldc, int64_t K, int64_t N) {
-  const int w = dtype == GEMM_DTYPE_F32 ? 4 : 8;  // elements per 16 bytes
+  const int64_t w = 16 / (int64_t)in_bytes(dtype), wc = 16 / (int64_t)out_bytes(dtype);  // per 16 bytes
+  // FP8 with K = 0 reads neither A nor B (C = 0): only C's layout matters.
+  if (dtype == GEMM_DTYPE_F8 && K == 0) return aligned16(C) && ldc % wc == 0 && N % wc == 0;
   return aligned16(A) && aligned16(B) && aligned16(C) && lda % w == 0 && ldb % w == 0 &&
-         ldc % w == 0 && K % w == 0 && N % w == 0;
+         ldc % wc == 0 && K % w == 0 && N % w == 0;
+}
+
+// FP8 runs on the LDS-direct kernels only (no general kernel).
+gemm_status_t f8_unsupported() {
+  return fail(GEMM_ERR_UNSUPPORTED,
+              "FP8 operands need 16-byte aligned A, B, C, K, N, lda and ldb multiples of 16, "
+              "ldc a multiple of 8, and byte offsets below 2^31");
 }
 
 Params make_params(int dtype, const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
@@ -319,8 +336,10 @@ gemm_status_t launch_plain(int dtype, const gemm_config_t& cfg, int64_t M, int64
                            int64_t ldc, void* stream) {
   const Params p = make_params(dtype, A, lda, B, ldb, C, ldc, M, N, K);
   const bool vec = vector_path(dtype, A, lda, B, ldb, C, ldc, K, N);
+  if (dtype == GEMM_DTYPE_F8 && !vec) return f8_unsupported();
   const TileMap map = make_map(cfg, M, N);
   const hipError_t e = table().v[dtype][cfg.id].launch(p, map, vec, static_cast<hipStream_t>(stream));
+  if (e == hipErrorNotSupported && dtype == GEMM_DTYPE_F8) return f8_unsupported();
   if (e != hipSuccess) return fail(GEMM_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
   return GEMM_OK;
 }
@@ -351,9 +370,11 @@ gemm_status_t run_bt(int dtype, int64_t M, int64_t N, int64_t K, const void* A, 
   Params p = make_params(dtype, A, lda, Bt, ldbt, C, ldc, M, N, K);
   p.bt = true;
   const bool vec = vector_path(dtype, A, lda, Bt, ldbt, C, ldc, K, N);
+  if (dtype == GEMM_DTYPE_F8 && !vec) return f8_unsupported();
   const TileMap map = make_map(cfg, M, N);
   const hipError_t e =
       table().v[dtype][cfg.id].launch_bt(p, map, vec, static_cast<hipStream_t>(stream));
+  if (e == hipErrorNotSupported && dtype == GEMM_DTYPE_F8) return f8_unsupported();
   if (e != hipSuccess) return fail(GEMM_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
   return GEMM_OK;
 }
@@ -367,8 +388,7 @@ gemm_status_t run_epi(int dtype, int64_t M, int64_t N, int64_t K, const void* A,
   if (!epi) return fail(GEMM_ERR_INVALID_ARG, "epi is NULL");
   if (epi->act != GEMM_ACT_NONE && epi->act != GEMM_ACT_RELU)
     return fail(GEMM_ERR_INVALID_ARG, "unknown activation %d", epi->act);
-  const size_t es = dtype == GEMM_DTYPE_F32 ? 4 : 2;
-  if (epi->bias && overlap(epi->bias, (size_t)N * 4, C, span_bytes(M, N, ldc, es)))
+  if (epi->bias && overlap(epi->bias, (size_t)N * 4, C, span_bytes(M, N, ldc, out_bytes(dtype))))
     return fail(GEMM_ERR_ALIAS, "bias overlaps C");
   gemm_config_t cfg;
   st = resolve(dtype, M, N, K, forced, false, cfg, true);
@@ -383,9 +403,11 @@ gemm_status_t run_epi(int dtype, int64_t M, int64_t N, int64_t K, const void* A,
   // The vector forms read the bias four floats at a time.
   const bool vec = vector_path(dtype, A, lda, B, ldb, C, ldc, K, N) &&
                    (!epi->bias || aligned16(epi->bias));
+  if (dtype == GEMM_DTYPE_F8 && !vec) return f8_unsupported();
   const TileMap map = make_map(cfg, M, N);
   const hipError_t e =
       table().v[dtype][cfg.id].launch_epi(p, map, vec, static_cast<hipStream_t>(stream));
+  if (e == hipErrorNotSupported && dtype == GEMM_DTYPE_F8) return f8_unsupported();
   if (e != hipSuccess) return fail(GEMM_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
   return GEMM_OK;
 }
@@ -413,10 +435,10 @@ gemm_status_t run_splitk(int dtype, int64_t M, int64_t N, int64_t K, const void*
     return fail(GEMM_ERR_INVALID_ARG, "workspace of %lld bytes, %lld needed", (long long)ws_bytes,
                 (long long)need);
   if (!aligned16(ws)) return fail(GEMM_ERR_INVALID_ARG, "workspace not 16-byte aligned");
-  const size_t es = dtype == GEMM_DTYPE_F32 ? 4 : 2;
+  const size_t es = in_bytes(dtype);
   if (overlap(ws, (size_t)need, A, span_bytes(M, K, lda, es)) ||
       overlap(ws, (size_t)need, B, span_bytes(K, N, ldb, es)) ||
-      overlap(ws, (size_t)need, C, span_bytes(M, N, ldc, es)))
+      overlap(ws, (size_t)need, C, span_bytes(M, N, ldc, out_bytes(dtype))))
     return fail(GEMM_ERR_ALIAS, "workspace overlaps A, B or C");
   Params p = make_params(dtype, A, lda, B, ldb, ws, N, M, N, K);
   p.splits = (int)S;
@@ -427,7 +449,8 @@ gemm_status_t run_splitk(int dtype, int64_t M, int64_t N, int64_t K, const void*
   hipError_t e = var.launch_partial(p, map, vec, hs);
   if (e == hipErrorNotSupported)  // offsets beyond the fast kernel's range
     return launch_plain(dtype, cfg, M, N, K, A, lda, B, ldb, C, ldc, stream);
-  if (e == hipSuccess) e = splitk_reduce(dtype, static_cast<const float*>(ws), (int)S, (int)M, (int)N, C, ldc, hs);
+  if (e == hipSuccess)
+    e = splitk_reduce(out_dtype(dtype), static_cast<const float*>(ws), (int)S, (int)M, (int)N, C, ldc, hs);
   if (e != hipSuccess) return fail(GEMM_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
   return GEMM_OK;
 }
@@ -533,6 +556,38 @@ gemm_status_t gemm_bf16_splitk(int64_t M, int64_t N, int64_t K, const gemm_bf16_
                                int64_t ldc, void* workspace, int64_t workspace_bytes, void* stream,
                                const gemm_config_t* cfg) {
   return run_splitk(GEMM_DTYPE_BF16, M, N, K, A, lda, B, ldb, C, ldc, workspace, workspace_bytes,
+                    stream, cfg);
+}
+
+gemm_status_t gemm_f8(int64_t M, int64_t N, int64_t K, const gemm_f8_t* A, int64_t lda,
+                      const gemm_f8_t* B, int64_t ldb, gemm_bf16_t* C, int64_t ldc, void* stream) {
+  return run(GEMM_DTYPE_F8, M, N, K, A, lda, B, ldb, C, ldc, stream, nullptr);
+}
+
+gemm_status_t gemm_f8_ex(int64_t M, int64_t N, int64_t K, const gemm_f8_t* A, int64_t lda,
+                         const gemm_f8_t* B, int64_t ldb, gemm_bf16_t* C, int64_t ldc, void* stream,
+                         const gemm_config_t* cfg) {
+  if (!cfg) return fail(GEMM_ERR_INVALID_ARG, "cfg is NULL");
+  return run(GEMM_DTYPE_F8, M, N, K, A, lda, B, ldb, C, ldc, stream, cfg);
+}
+
+gemm_status_t gemm_f8_bt(int64_t M, int64_t N, int64_t K, const gemm_f8_t* A, int64_t lda,
+                         const gemm_f8_t* Bt, int64_t ldbt, gemm_bf16_t* C, int64_t ldc,
+                         void* stream, const gemm_config_t* cfg) {
+  return run_bt(GEMM_DTYPE_F8, M, N, K, A, lda, Bt, ldbt, C, ldc, stream, cfg);
+}
+
+gemm_status_t gemm_f8_epi(int64_t M, int64_t N, int64_t K, const gemm_f8_t* A, int64_t lda,
+                          const gemm_f8_t* B, int64_t ldb, gemm_bf16_t* C, int64_t ldc,
+                          void* stream, const gemm_config_t* cfg, const gemm_epilogue_t* epi) {
+  return run_epi(GEMM_DTYPE_F8, M, N, K, A, lda, B, ldb, C, ldc, stream, cfg, epi);
+}
+
+gemm_status_t gemm_f8_splitk(int64_t M, int64_t N, int64_t K, const gemm_f8_t* A, int64_t lda,
+                             const gemm_f8_t* B, int64_t ldb, gemm_bf16_t* C, int64_t ldc,
+                             void* workspace, int64_t workspace_bytes, void* stream,
+                             const gemm_config_t* cfg) {
+  return run_splitk(GEMM_DTYPE_F8, M, N, K, A, lda, B, ldb, C, ldc, workspace, workspace_bytes,
                     stream, cfg);
 }
 

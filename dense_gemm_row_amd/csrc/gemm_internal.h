@@ -56,7 +56,7 @@ struct Params {
   bool bt = false;
   // 16-bit kernels: A, B and C (and the old C read by the fused epilogue)
   // hold bfloat16 instead of binary16.  The general FP16 kernel reads it at
-  // launch; the LDS-direct kernels have it in their template instead.
+  // launch; the LDS-direct kernels have it (and FP8) in their template.
   bool bf16 = false;
 };
 
@@ -81,6 +81,16 @@ __device__ __forceinline__ f32x16_t mfma16(h16x8_t a, h16x8_t b, f32x16_t c) {
                                                     __builtin_bit_cast(b16x8_t, b), c, 0, 0, 0);
   else
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+// FP8 E4M3 (OCP) operands, 32 per lane (k 64 per instruction):
+// v_mfma_f32_32x32x64_f8f6f4 with both format fields 0 (E4M3) and no block
+// scales (the scaled builtin with zero scale operands selects the unscaled
+// instruction; checked on the device: scale 0 and 127 both give x1).
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ f32x16_t mfma_e4m3(i32x8_t a, i32x8_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
 // float -> 16-bit pattern, rounded to nearest even (v_cvt_f16_f32 or
@@ -216,10 +226,11 @@ const Variant* sgemm_dl_variants(int* count);
 const Variant* sgemm_mfma_variants(int* count);
 const Variant* sgemm_simt_variants(int* count);
 // The 16-bit families register a binary16 table and, where they have a
-// bfloat16 form, a bfloat16 one (bf16 = true; count 0 when there is none).
+// bfloat16 form, a bfloat16 one (bf16 = true); the LDS-direct family also
+// an FP8 E4M3 one (ty: 0 FP16, 1 BF16, 2 FP8 with BF16 output).
 const Variant* hgemm_mfma_variants(int* count, bool bf16 = false);
 const Variant* hgemm_pipe_variants(int* count);
-const Variant* hgemm_tr_variants(int* count, bool bf16 = false);
+const Variant* hgemm_tr_variants(int* count, int ty = 0);
 
 // Launch the general 16-bit kernel (any alignment, 64-bit addressing; FP16
 // or, with p.bf16, BF16) with the given workgroup tile (and the given wave

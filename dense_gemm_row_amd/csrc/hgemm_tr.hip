@@ -2,8 +2,14 @@
 // LDS transpose reads: binary16 A and B, FP32 accumulation on
 // v_mfma_f32_32x32x16_f16, one round-to-nearest-even conversion per output.
 // The same kernel, with v_mfma_f32_32x32x16_bf16 and bfloat16 conversions,
-// is the BF16 GEMM (Shape's BF_): the data path moves 16-bit patterns and
-// never looks inside them.
+// is the BF16 GEMM, and with 8-bit elements, v_mfma_f32_32x32x64_f8f6f4
+// (k 64 per MFMA) and bfloat16 output it is the FP8 E4M3 GEMM (Shape's
+// TY_): the data path moves bit patterns and never looks inside them.  For
+// FP8, a lane's operand is 32 bytes (two 16-byte A chunks; four
+// ds_read_b64_tr_b8 reads of B, the byte form of the transpose read below:
+// output lane j of a 16-lane group gets byte j%8 of the 8-byte pieces of
+// lanes j/8 + 2t, t = 0..7, measured on the device), and B's 16-byte chunk
+// index is XORed by 2*(k%8) instead of 4*(k%4).
 //
 // Data path per K slice (no VGPR staging, no VALU in the main loop):
 // * A and B move from global memory straight into LDS with
@@ -65,7 +71,11 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) f16x8 lds_f16x8;
 
@@ -84,20 +94,29 @@ __device__ __forceinline__ void static_for(F&& f, std::integer_sequence<int, I..
 // partials; 2 the form with the fused epilogue (alpha, beta, bias,
 // activation).  BT_: B is given transposed (Bt, N x K row-major, i.e.
 // column-major B); its tile is then staged and read exactly like A's (one
-// LDS row per output column, k contiguous), with no transpose read.  BF_:
-// the elements are bfloat16.
+// LDS row per output column, k contiguous), with no transpose read.  TY_:
+// the element types, 0 binary16 in and out, 1 bfloat16 in and out, 2 FP8
+// E4M3 in and bfloat16 out.
 template <int BM_, int BN_, int WM_, int WN_, int BK_, int NS_, int MODE_ = 0, bool BT_ = false,
-          bool BF_ = false>
+          int TY_ = 0>
 struct Shape {
-  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BK_, NS = NS_;
-  static constexpr bool PARTIAL = MODE_ == 1, EPI = MODE_ == 2, BT = BT_, BF = BF_;
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BK_, NS = NS_, TY = TY_;
+  static constexpr bool PARTIAL = MODE_ == 1, EPI = MODE_ == 2, BT = BT_;
+  static constexpr bool BF = TY != 0;   // C (and the epilogue's old C) is bfloat16
+  static constexpr bool F8 = TY == 2;   // A and B are FP8 E4M3
+  static constexpr int ES = F8 ? 1 : 2;    // input element bytes
+  static constexpr int CE = 16 / ES;       // input elements per 16-byte chunk
+  static constexpr int KW = F8 ? 64 : 16;  // k per MFMA
+  static constexpr int FR = F8 ? 2 : 1;    // 16-byte chunks per lane in an A / Bt operand
+  static constexpr int TRN = F8 ? 4 : 2;   // transpose reads per B operand
+  static constexpr int RR = F8 ? 8 : 4;    // k rows (elements per lane) of one transpose read
   static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN, NW = WAVES_M * WAVES_N;
   static constexpr int NT = NW * 64;
-  static constexpr int MB = WM / 32, NB = WN / 32, KS = BK / 16;
+  static constexpr int MB = WM / 32, NB = WN / 32, KS = BK / KW;
   static constexpr int NMMA_ = MB * NB;  // MFMAs per k step
-  static constexpr int A_ROW = BK * 2, A_CPR = A_ROW / 16;  // bytes / chunks per A row
+  static constexpr int A_ROW = BK * ES, A_CPR = A_ROW / 16;  // bytes / chunks per A row
   // B rows: BK rows of BN columns, or (BT) BN rows of BK k values.
-  static constexpr int B_ROW = BT ? BK * 2 : BN * 2, B_CPR = B_ROW / 16;  // bytes / chunks
+  static constexpr int B_ROW = BT ? BK * ES : BN * ES, B_CPR = B_ROW / 16;  // bytes / chunks
   static constexpr int A_STAGE = BM * A_ROW, B_STAGE = BT ? BN * B_ROW : BK * B_ROW;
   static constexpr int LDS_BYTES = NS * (A_STAGE + B_STAGE);
   static constexpr int IA = A_STAGE / 1024 / NW, IB = B_STAGE / 1024 / NW, LPS = IA + IB;
@@ -111,7 +130,10 @@ struct Shape {
   static constexpr int EPI_ROW = WN * 2, EPI_SPR = WN / 4;
   static constexpr int P = (2 * NS) / NW, RPA = WM / P;
   static constexpr int EPI_CPR = WN / 8, EPI_RPI = 64 / EPI_CPR;  // store pass shape
-  static_assert(BK == 32 || BK == 64, "K slice");
+  static_assert(F8 ? BK == 128 : (BK == 32 || BK == 64), "K slice");
+  // Fragments alternate between two register sets by k step, and slice t+1's
+  // first step reuses set 0: an even number of k steps per slice.
+  static_assert(KS % 2 == 0, "k steps per slice");
   static_assert(NS >= 2 && NS <= MAX_STAGES, "stages");
   static_assert(BM % WM == 0 && BN % WN == 0, "wave grid");
   static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile");
@@ -127,14 +149,17 @@ struct Shape {
   static_assert(P >= 1 && WM % P == 0 && RPA % 32 == 0 && RPA % EPI_RPI == 0 &&
                 RPA * EPI_ROW <= A_STAGE && RPA * EPI_ROW <= B_STAGE, "epilogue staging");
   // Fragment reads use a per-lane base plus immediate offsets (< 64 KB).
-  static_assert((MB - 1) * 32 * A_ROW < 65536 && (BK - 12) * B_ROW < 65536 &&
+  static_assert((MB - 1) * 32 * A_ROW < 65536 && (BK - KW + RR * (TRN - 1)) * B_ROW < 65536 &&
                 (NB - 1) * 32 * B_ROW < 65536, "immediate offsets");
 
   // Byte offsets within one stage array.
   __host__ __device__ static constexpr int a_byte(int r, int q) { return swz_off(r, q, A_ROW); }
-  __host__ __device__ static constexpr int b_phys(int k, int c) { return c ^ (4 * (k % 4)); }
+  // B chunk XOR: the rows one transpose read touches (4 for 16-bit, 8 for
+  // 8-bit) land on distinct 16-byte (32-byte) bank slots.
+  __host__ __device__ static constexpr int b_swz(int k) { return F8 ? 2 * (k % 8) : 4 * (k % 4); }
+  __host__ __device__ static constexpr int b_phys(int k, int c) { return c ^ b_swz(k); }
   __host__ __device__ static constexpr int b_byte(int k, int n) {
-    return k * B_ROW + 16 * b_phys(k, n / 8) + 2 * (n % 8);
+    return k * B_ROW + 16 * b_phys(k, n / CE) + ES * (n % CE);
   }
   // Direct loads: lane l of wave w, instruction i.
   __host__ __device__ static constexpr int a_dl_row(int i, int w, int l) {
@@ -147,25 +172,30 @@ struct Shape {
     return (1024 * (i * NW + w) + 16 * l) / B_ROW;
   }
   __host__ __device__ static constexpr int b_dl_c(int i, int w, int l) {
-    return ((1024 * (i * NW + w) + 16 * l) % B_ROW / 16) ^ (4 * (b_dl_k(i, w, l) % 4));
+    return ((1024 * (i * NW + w) + 16 * l) % B_ROW / 16) ^ b_swz(b_dl_k(i, w, l));
   }
-  // Fragment reads for k step j of a slice.
-  //  B_op (A values): lane reads row wm0 + 32mb + l%32, chunk 2j + l/32.
-  __host__ __device__ static constexpr int a_frag(int wm0, int mb, int j, int l) {
-    return a_byte(wm0 + 32 * mb + l % 32, 2 * j + l / 32);
+  // Fragment reads for k step j of a slice.  Lane l's operand holds k
+  // KW*j + (KW/2)*(l/32) + 0 .. KW/2-1 (any k order common to both operands
+  // gives the same product; this one keeps each lane's k run contiguous).
+  //  B_op (A values): lane reads row wm0 + 32mb + l%32, chunks
+  //  FR*(2j + l/32) + part.
+  __host__ __device__ static constexpr int a_frag(int wm0, int mb, int j, int l, int part = 0) {
+    return a_byte(wm0 + 32 * mb + l % 32, FR * (2 * j + l / 32) + part);
   }
-  //  A_op (B values, transpose read j2 of 2): lane 4t+q of 16-lane group g
-  //  points at row 16j + 8h + 4j2 + t, columns wn0 + 32nb + 16(g%2) + 4q.
-  __host__ __device__ static constexpr int b_frag(int wn0, int nb, int j, int j2, int l) {
-    return b_byte(16 * j + 8 * (l / 32) + 4 * j2 + (l % 16) / 4,
-                  wn0 + 32 * nb + 16 * ((l / 16) % 2) + 4 * (l % 4));
+  //  A_op (B values, transpose read jr of TRN): lane LPR*t + q of 16-lane
+  //  group g (LPR = 16/RR lanes per row) points at row KW*j + (KW/2)h +
+  //  RR*jr + t, columns wn0 + 32nb + 16(g%2) + (8/ES)q.
+  __host__ __device__ static constexpr int b_frag(int wn0, int nb, int j, int jr, int l) {
+    return b_byte(KW * j + (KW / 2) * (l / 32) + RR * jr + (l % 16) / (16 / RR),
+                  wn0 + 32 * nb + 16 * ((l / 16) % 2) + (8 / ES) * (l % (16 / RR)));
   }
   // BT: B tile row n (one output column), 16-byte k chunk q, placed and read
   // with A's maps (B_ROW == A_ROW): lane reads column wn0 + 32nb + l%32,
-  // chunk 2j + l/32 of k step j (the MFMA A operand of C^T directly).
+  // chunks FR*(2j + l/32) + part of k step j (the MFMA A operand of C^T
+  // directly).
   __host__ __device__ static constexpr int bt_byte(int n, int q) { return swz_off(n, q, B_ROW); }
-  __host__ __device__ static constexpr int bt_frag(int wn0, int nb, int j, int l) {
-    return bt_byte(wn0 + 32 * nb + l % 32, 2 * j + l / 32);
+  __host__ __device__ static constexpr int bt_frag(int wn0, int nb, int j, int l, int part = 0) {
+    return bt_byte(wn0 + 32 * nb + l % 32, FR * (2 * j + l / 32) + part);
   }
   // Epilogue staging: 8-byte slot s (columns 4s..4s+3) of local row m of an
   // array, XOR-swizzled by the row so that the 32 rows written by one
@@ -229,8 +259,8 @@ __device__ __forceinline__ void issue_slice(const unsigned char* Ab, const unsig
                                             int ldb) {
   // Slices past the last one (issued only to keep the wait counts uniform)
   // get empty descriptors: they load zeros without touching memory.
-  const int64_t ka = 2 * (int64_t)s * S::BK;
-  const int64_t kb = S::BT ? ka : (int64_t)s * S::BK * ldb * 2;
+  const int64_t ka = S::ES * (int64_t)s * S::BK;
+  const int64_t kb = S::BT ? ka : (int64_t)s * S::BK * ldb * S::ES;
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(Ab + ka, live ? a_bytes - ka : 0);
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bb + kb, live ? b_bytes - kb : 0);
   // Copy instructions Q0 .. Q1-1 of the slice: A's IA blocks, then B's IB.
@@ -291,10 +321,10 @@ hgemm_tr_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
   const int sk = blockIdx.y;
   const int kc = p.splits > 1 ? p.kc : p.K;
   const int M = p.M, N = p.N, K = min(kc, p.K - sk * kc);
-  const unsigned char* Ab = static_cast<const unsigned char*>(p.A) + 2 * (int64_t)sk * kc;
-  const int64_t bshift = S::BT ? 2 * (int64_t)sk * kc : 2 * (int64_t)sk * kc * ldb;
+  const unsigned char* Ab = static_cast<const unsigned char*>(p.A) + S::ES * (int64_t)sk * kc;
+  const int64_t bshift = S::BT ? S::ES * (int64_t)sk * kc : S::ES * (int64_t)sk * kc * ldb;
   const unsigned char* Bb = static_cast<const unsigned char*>(p.B) + bshift;
-  a_bytes -= 2 * (int64_t)sk * kc;
+  a_bytes -= S::ES * (int64_t)sk * kc;
   b_bytes -= bshift;
 
   const int tid = threadIdx.x;
@@ -309,8 +339,8 @@ hgemm_tr_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
   for (int i = 0; i < IA; ++i) {
     const int r = S::a_dl_row(i, wave, l), q = S::a_dl_q(i, wave, l);
     const bool ok = (m0 + r) < M;
-    a_vo[i] = ok ? 2u * ((unsigned)(m0 + r) * (unsigned)lda + 8u * q) : OOB;
-    a_vo_tail[i] = ((T - 1) * BK + 8 * q < K) ? a_vo[i] : OOB;
+    a_vo[i] = ok ? (unsigned)S::ES * ((unsigned)(m0 + r) * (unsigned)lda + (unsigned)S::CE * q) : OOB;
+    a_vo_tail[i] = ((T - 1) * BK + S::CE * q < K) ? a_vo[i] : OOB;
   }
 #pragma unroll
   for (int i = 0; i < IB; ++i) {
@@ -318,23 +348,28 @@ hgemm_tr_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
       // Bt row n0 + r (output column), k chunk q: A's placement.
       const int r = S::a_dl_row(i, wave, l), q = S::a_dl_q(i, wave, l);
       const bool ok = (n0 + r) < N;
-      b_vo[i] = ok ? 2u * ((unsigned)(n0 + r) * (unsigned)ldb + 8u * q) : OOB;
-      b_vo_tail[i] = ((T - 1) * BK + 8 * q < K) ? b_vo[i] : OOB;
+      b_vo[i] = ok ? (unsigned)S::ES * ((unsigned)(n0 + r) * (unsigned)ldb + (unsigned)S::CE * q) : OOB;
+      b_vo_tail[i] = ((T - 1) * BK + S::CE * q < K) ? b_vo[i] : OOB;
     } else {
       const int k = S::b_dl_k(i, wave, l), c = S::b_dl_c(i, wave, l);
-      const bool ok = (n0 + 8 * c) < N;
-      b_vo[i] = ok ? 2u * ((unsigned)k * (unsigned)ldb + (unsigned)(n0 + 8 * c)) : OOB;
+      const bool ok = (n0 + S::CE * c) < N;
+      b_vo[i] = ok ? (unsigned)S::ES * ((unsigned)k * (unsigned)ldb + (unsigned)(n0 + S::CE * c)) : OOB;
       b_vo_tail[i] = b_vo[i];  // rows past K are past the buffer's range
     }
   }
   // Fragment byte offsets: k step j of A and block nb of B; other blocks
   // and k steps are immediate offsets.
-  int a_fb[KS], b_fb[S::BT ? KS : NB];
+  constexpr int FR = S::FR;
+  int a_fb[KS * FR], b_fb[S::BT ? KS * FR : NB];
 #pragma unroll
-  for (int j = 0; j < KS; ++j) a_fb[j] = S::a_frag(wm0, 0, j, l);
+  for (int j = 0; j < KS; ++j)
+#pragma unroll
+    for (int q = 0; q < FR; ++q) a_fb[j * FR + q] = S::a_frag(wm0, 0, j, l, q);
   if constexpr (S::BT) {
 #pragma unroll
-    for (int j = 0; j < KS; ++j) b_fb[j] = S::bt_frag(wn0, 0, j, l);
+    for (int j = 0; j < KS; ++j)
+#pragma unroll
+      for (int q = 0; q < FR; ++q) b_fb[j * FR + q] = S::bt_frag(wn0, 0, j, l, q);
   } else {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) b_fb[nb] = S::b_frag(wn0, nb, 0, 0, l);
@@ -352,9 +387,38 @@ hgemm_tr_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
                                                s == T - 1 ? b_vo_tail : b_vo, la, lb, wave, ldb);
   };
 
-  f16x8 fa[2][MB], fb[2][NB];
+  // An operand: 8 16-bit or 32 8-bit values per lane.
+  typedef std::conditional_t<S::F8, i32x8_t, f16x8> Frag;
+  Frag fa[2][MB], fb[2][NB];
+  // Two 16-byte chunks of one lane's FP8 operand (positions differ by the
+  // row's XOR).
+  auto two_chunks = [](const unsigned char* p0, const unsigned char* p1) __attribute__((always_inline)) {
+    const u32x4 x0 = *(const lds_u32x4*)p0, x1 = *(const lds_u32x4*)p1;
+    return __builtin_bit_cast(i32x8_t, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
   auto load_frags = [&](int buf, const unsigned char* la, const unsigned char* lb, int j)
       __attribute__((always_inline)) {
+    if constexpr (S::F8) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+        fa[buf][mb] = two_chunks(la + a_fb[2 * j] + mb * 32 * S::A_ROW, la + a_fb[2 * j + 1] + mb * 32 * S::A_ROW);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        if constexpr (S::BT) {
+          fb[buf][nb] = two_chunks(lb + b_fb[2 * j] + nb * 32 * S::B_ROW, lb + b_fb[2 * j + 1] + nb * 32 * S::B_ROW);
+        } else {
+          const unsigned char* b = lb + b_fb[nb] + S::KW * j * S::B_ROW;
+          const i32x2 r0 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)b);
+          const i32x2 r1 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(b + 8 * S::B_ROW));
+          const i32x2 r2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(b + 16 * S::B_ROW));
+          const i32x2 r3 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(b + 24 * S::B_ROW));
+          const i32x4 lo = __builtin_shufflevector(r0, r1, 0, 1, 2, 3);
+          const i32x4 hi = __builtin_shufflevector(r2, r3, 0, 1, 2, 3);
+          fb[buf][nb] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+      }
+      return;
+    } else {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
       fa[buf][mb] = *(const lds_f16x8*)(la + a_fb[j] + mb * 32 * S::A_ROW);
@@ -371,6 +435,7 @@ hgemm_tr_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
         fb[buf][nb] = __builtin_bit_cast(f16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       }
     }
+    }
   };
 
   // acc[nb][mb]: block of C^T (rows n, columns m).
@@ -385,13 +450,18 @@ hgemm_tr_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) acc[nb][mb] = mfma16<S::BF>(fb[buf][nb], fa[buf][mb], acc[nb][mb]);
+      for (int mb = 0; mb < MB; ++mb) {
+        if constexpr (S::F8)
+          acc[nb][mb] = mfma_e4m3(fb[buf][nb], fa[buf][mb], acc[nb][mb]);
+        else
+          acc[nb][mb] = mfma16<S::BF>(fb[buf][nb], fa[buf][mb], acc[nb][mb]);
+      }
   };
 
   // (The lambdas are forced inline: an out-of-line call would move the
   // accumulators to scratch memory.)
   constexpr int NMMA = MB * NB;     // MFMAs per k step
-  constexpr int NRD = MB + (S::BT ? 1 : 2) * NB;  // LDS reads per k step
+  constexpr int NRD = MB * FR + (S::BT ? FR : S::TRN) * NB;  // LDS reads per k step
   // Slice t from stage c: k steps 0..KS-2 with the next step's fragments
   // in flight; wait for slice t+1; barrier; issue slice t+NS into the freed
   // stage c; last k step (registers only) under the first fragment reads of
@@ -609,19 +679,21 @@ template <class S>
 hipError_t launch(const Params& p, const TileMap& map, bool vec, hipStream_t stream) {
   const int64_t lim = 0x7fffffff;
   // Every offset (rows past M, N and K included) must fit the 31-bit range.
-  const bool b_far = S::BT ? (int64_t)(p.N + S::BN) * p.ldb * 2 > lim
-                           : (int64_t)(S::BK + 2) * p.ldb * 2 > lim ||
-                                 ((int64_t)(p.K > 0 ? p.K - 1 : 0) * p.ldb + p.N) * 2 > lim;
-  if (!vec || (int64_t)(p.M + S::BM) * p.lda * 2 > lim || b_far || (int64_t)p.M * p.lda * 2 > lim ||
+  constexpr int ES = S::ES;
+  const bool b_far = S::BT ? (int64_t)(p.N + S::BN) * p.ldb * ES > lim
+                           : (int64_t)(S::BK + 2) * p.ldb * ES > lim ||
+                                 ((int64_t)(p.K > 0 ? p.K - 1 : 0) * p.ldb + p.N) * ES > lim;
+  if (!vec || (int64_t)(p.M + S::BM) * p.lda * ES > lim || b_far || (int64_t)p.M * p.lda * ES > lim ||
       (S::EPI && (int64_t)p.M * p.ldc * 2 > lim)) {
-    // The general kernel has no split-K form: the caller runs unsplit.
-    if (p.splits > 1) return hipErrorNotSupported;
+    // The general kernel has no split-K form (the caller runs unsplit) and
+    // no FP8 form (the caller reports the operands unsupported).
+    if (p.splits > 1 || S::F8) return hipErrorNotSupported;
     return hgemm_launch_shape(S::BM, S::BN, S::WM, S::WN, p, map, vec, stream);
   }
-  const int64_t a_bytes = p.K > 0 ? ((int64_t)(p.M - 1) * p.lda + p.K) * 2 : 0;
+  const int64_t a_bytes = p.K > 0 ? ((int64_t)(p.M - 1) * p.lda + p.K) * ES : 0;
   const int64_t b_bytes = p.K <= 0 ? 0
-                          : S::BT ? ((int64_t)(p.N - 1) * p.ldb + p.K) * 2
-                                  : ((int64_t)(p.K - 1) * p.ldb + p.N) * 2;
+                          : S::BT ? ((int64_t)(p.N - 1) * p.ldb + p.K) * ES
+                                  : ((int64_t)(p.K - 1) * p.ldb + p.N) * ES;
   const dim3 grid(map.tiles_m * map.tiles_n, p.splits), block(S::NT);
   hipLaunchKernelGGL(hgemm_tr_kernel<S>, grid, block, 0, stream, p, map, a_bytes, b_bytes);
   return hipGetLastError();
@@ -642,31 +714,33 @@ int layout_check_bt(int banks, int64_t* rconf) {
         const int off = 1024 * (i * S::NW + w) + 16 * l;
         const int r = S::a_dl_row(i, w, l), q = S::a_dl_q(i, w, l);
         if (r >= S::BN || q >= S::B_CPR || S::bt_byte(r, q) != off) return 20;
-        for (int e = 0; e < 8; ++e) {
-          if (n_of[off + 2 * e] != -1) return 21;
-          n_of[off + 2 * e] = r;
-          k_of[off + 2 * e] = 8 * q + e;
+        for (int e = 0; e < S::CE; ++e) {
+          if (n_of[off + S::ES * e] != -1) return 21;
+          n_of[off + S::ES * e] = r;
+          k_of[off + S::ES * e] = S::CE * q + e;
         }
       }
-  for (int i = 0; i < S::B_STAGE; i += 2)
+  for (int i = 0; i < S::B_STAGE; i += S::ES)
     if (n_of[i] < 0) return 22;
   int addr[64];
   for (int w = 0; w < S::NW; ++w) {
     const int wn0 = (w % S::WAVES_N) * S::WN;
     for (int j = 0; j < S::KS; ++j)
-      for (int nb = 0; nb < S::NB; ++nb) {
-        for (int l = 0; l < 64; ++l) {
-          addr[l] = S::bt_frag(wn0, nb, j, l);
-          if (addr[l] < 0 || addr[l] + 16 > S::B_STAGE) return 23;
-          if (addr[l] != S::bt_frag(wn0, 0, j, l) + nb * 32 * S::B_ROW) return 24;
-          // A_op lane l, element e: B[k = 16j + 8(l/32) + e][n = wn0 + 32nb + l%32].
-          for (int e = 0; e < 8; ++e)
-            if (n_of[addr[l] + 2 * e] != wn0 + 32 * nb + l % 32 ||
-                k_of[addr[l] + 2 * e] != 16 * j + 8 * (l / 32) + e)
-              return 25;
+      for (int nb = 0; nb < S::NB; ++nb)
+        for (int part = 0; part < S::FR; ++part) {
+          for (int l = 0; l < 64; ++l) {
+            addr[l] = S::bt_frag(wn0, nb, j, l, part);
+            if (addr[l] < 0 || addr[l] + 16 > S::B_STAGE) return 23;
+            if (addr[l] != S::bt_frag(wn0, 0, j, l, part) + nb * 32 * S::B_ROW) return 24;
+            // A_op lane l, element e of this chunk:
+            // B[k = KW j + (KW/2)(l/32) + CE part + e][n = wn0 + 32nb + l%32].
+            for (int e = 0; e < S::CE; ++e)
+              if (n_of[addr[l] + S::ES * e] != wn0 + 32 * nb + l % 32 ||
+                  k_of[addr[l] + S::ES * e] != S::KW * j + (S::KW / 2) * (l / 32) + S::CE * part + e)
+                return 25;
+          }
+          *rconf += lds_conflicts(addr, 16, banks);
         }
-        *rconf += lds_conflicts(addr, 16, banks);
-      }
   }
   return 0;
 }
@@ -689,10 +763,10 @@ int layout_check(int banks, int64_t out[2]) {
         const int off = 1024 * (i * S::NW + w) + 16 * l;
         const int r = S::a_dl_row(i, w, l), q = S::a_dl_q(i, w, l);
         if (r >= BM || q >= S::A_CPR || S::a_byte(r, q) != off) return 1;
-        for (int e = 0; e < 8; ++e) {
-          if (a_row_of[off + 2 * e] != -1) return 2;
-          a_row_of[off + 2 * e] = r;
-          a_k_of[off + 2 * e] = 8 * q + e;
+        for (int e = 0; e < S::CE; ++e) {
+          if (a_row_of[off + S::ES * e] != -1) return 2;
+          a_row_of[off + S::ES * e] = r;
+          a_k_of[off + S::ES * e] = S::CE * q + e;
         }
       }
   for (int i = 0; i < S::IB; ++i)
@@ -700,49 +774,57 @@ int layout_check(int banks, int64_t out[2]) {
       for (int l = 0; l < 64; ++l) {
         const int off = 1024 * (i * S::NW + w) + 16 * l;
         const int k = S::b_dl_k(i, w, l), c = S::b_dl_c(i, w, l);
-        if (k >= BK || c >= S::B_CPR || S::b_byte(k, 8 * c) != off) return 3;
-        for (int e = 0; e < 8; ++e) {
-          if (b_k_of[off + 2 * e] != -1) return 4;
-          b_k_of[off + 2 * e] = k;
-          b_n_of[off + 2 * e] = 8 * c + e;
+        if (k >= BK || c >= S::B_CPR || S::b_byte(k, S::CE * c) != off) return 3;
+        for (int e = 0; e < S::CE; ++e) {
+          if (b_k_of[off + S::ES * e] != -1) return 4;
+          b_k_of[off + S::ES * e] = k;
+          b_n_of[off + S::ES * e] = S::CE * c + e;
         }
       }
-  for (int i = 0; i < S::A_STAGE; i += 2)
+  for (int i = 0; i < S::A_STAGE; i += S::ES)
     if (a_row_of[i] < 0) return 5;
-  for (int i = 0; i < S::B_STAGE; i += 2)
+  for (int i = 0; i < S::B_STAGE; i += S::ES)
     if (b_k_of[i] < 0) return 6;
   int addr[64];
   for (int w = 0; w < S::NW; ++w) {
     const int wm0 = (w / S::WAVES_N) * WM, wn0 = (w % S::WAVES_N) * WN;
     for (int j = 0; j < S::KS; ++j) {
-      for (int mb = 0; mb < S::MB; ++mb) {
-        for (int l = 0; l < 64; ++l) {
-          addr[l] = S::a_frag(wm0, mb, j, l);
-          if (addr[l] < 0 || addr[l] + 16 > S::A_STAGE) return 15;
-          // B_op lane l: A[m = wm0 + 32mb + l%32][k = 16j + 8(l/32) + e].
-          for (int e = 0; e < 8; ++e) {
-            const int b = addr[l] + 2 * e;
-            if (a_row_of[b] != wm0 + 32 * mb + l % 32 || a_k_of[b] != 16 * j + 8 * (l / 32) + e) return 7;
-          }
-          if (addr[l] != S::a_frag(wm0, 0, j, l) + mb * 32 * S::A_ROW) return 8;
-        }
-        rconf += lds_conflicts(addr, 16, banks);
-      }
-      for (int nb = 0; nb < S::NB; ++nb)
-        for (int j2 = 0; j2 < 2; ++j2) {
+      for (int mb = 0; mb < S::MB; ++mb)
+        for (int part = 0; part < S::FR; ++part) {
           for (int l = 0; l < 64; ++l) {
-            addr[l] = S::b_frag(wn0, nb, j, j2, l);
-            if (addr[l] != S::b_frag(wn0, nb, 0, 0, l) + 16 * j * S::B_ROW + 4 * j2 * S::B_ROW) return 9;
+            addr[l] = S::a_frag(wm0, mb, j, l, part);
+            if (addr[l] < 0 || addr[l] + 16 > S::A_STAGE) return 15;
+            // B_op lane l, element e of this chunk:
+            // A[m = wm0 + 32mb + l%32][k = KW j + (KW/2)(l/32) + CE part + e].
+            for (int e = 0; e < S::CE; ++e) {
+              const int b = addr[l] + S::ES * e;
+              if (a_row_of[b] != wm0 + 32 * mb + l % 32 ||
+                  a_k_of[b] != S::KW * j + (S::KW / 2) * (l / 32) + S::CE * part + e)
+                return 7;
+            }
+            if (addr[l] != S::a_frag(wm0, 0, j, l, part) + mb * 32 * S::A_ROW) return 8;
           }
-          // Transpose read: output lane j receives element j%4 of the
-          // piece addressed by lane 4t + j/4 of its 16-lane group.
+          rconf += lds_conflicts(addr, 16, banks);
+        }
+      for (int nb = 0; nb < S::NB; ++nb)
+        for (int jr = 0; jr < S::TRN; ++jr) {
+          for (int l = 0; l < 64; ++l) {
+            addr[l] = S::b_frag(wn0, nb, j, jr, l);
+            if (addr[l] != S::b_frag(wn0, nb, 0, 0, l) + (S::KW * j + S::RR * jr) * S::B_ROW) return 9;
+          }
+          // Transpose read of RR elements per lane: output lane jj of a
+          // 16-lane group receives element jj%RR of the piece addressed by
+          // lane LPR*t + jj/RR of the group (LPR = 16/RR lanes per row).
+          constexpr int LPR = 16 / S::RR;
           for (int l = 0; l < 64; ++l)
-            for (int t = 0; t < 4; ++t) {
+            for (int t = 0; t < S::RR; ++t) {
               const int g = l / 16, jj = l % 16;
-              const int src = addr[16 * g + 4 * t + jj / 4] + 2 * (jj % 4);
+              const int src = addr[16 * g + LPR * t + jj / S::RR] + S::ES * (jj % S::RR);
               if (src < 0 || src >= S::B_STAGE) return 14;
-              // A_op lane l, element 4*j2 + t: B[k = 16j + 8(l/32) + 4j2 + t][n = wn0 + 32nb + l%32].
-              if (b_k_of[src] != 16 * j + 8 * (l / 32) + 4 * j2 + t || b_n_of[src] != wn0 + 32 * nb + l % 32)
+              // A_op lane l, element RR*jr + t:
+              // B[k = KW j + (KW/2)(l/32) + RR jr + t][n = wn0 + 32nb + l%32].
+              if (b_k_of[src] != S::KW * j + (S::KW / 2) * (l / 32) + S::RR * jr + t ||
+                  b_n_of[src] != wn0 + 32 * nb + l % 32)
                 return 10;
             }
           rconf += lds_conflicts(addr, 8, banks);
@@ -819,45 +901,54 @@ int layout_check(int banks, int64_t out[2]) {
       rconf += lds_conflicts(addr, 16, banks);
     }
   }
-  const int rc = layout_check_bt<Shape<S::BM, S::BN, S::WM, S::WN, S::BK, S::NS, 0, true>>(banks, &rconf);
+  const int rc = layout_check_bt<Shape<S::BM, S::BN, S::WM, S::WN, S::BK, S::NS, 0, true, S::TY>>(banks, &rconf);
   if (rc != 0) return rc;
   out[0] = wconf;
   out[1] = rconf;
   return 0;
 }
 
-#define HGEMM_TR_VARIANT(BF, DT, TAG, BM, BN, WM, WN, BK, NS, EFF)                               \
+#define HGEMM_TR_VARIANT(TY, DT, TAG, BM, BN, WM, WN, BK, NS, EFF)                               \
   Variant {                                                                                  \
     gemm_config_t{0, DT, GEMM_FAMILY_MFMA, BM, BN, BK, WM, WN,                               \
-                  Shape<BM, BN, WM, WN, BK, NS>::NT, NS, Shape<BM, BN, WM, WN, BK, NS>::LDS_BYTES, \
+                  Shape<BM, BN, WM, WN, BK, NS, 0, false, TY>::NT, NS,                       \
+                  Shape<BM, BN, WM, WN, BK, NS, 0, false, TY>::LDS_BYTES,                    \
                   GEMM_ORDER_XCD, 4, 1,                                                      \
                   "tr_" TAG "_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_s" #NS},              \
-        &launch<Shape<BM, BN, WM, WN, BK, NS, 0, false, BF>>,                                \
-        &layout_check<Shape<BM, BN, WM, WN, BK, NS>>,                                        \
-        &launch<Shape<BM, BN, WM, WN, BK, NS, 1, false, BF>>, EFF,                           \
-        &launch<Shape<BM, BN, WM, WN, BK, NS, 2, false, BF>>,                                \
-        &launch<Shape<BM, BN, WM, WN, BK, NS, 0, true, BF>>                                  \
+        &launch<Shape<BM, BN, WM, WN, BK, NS, 0, false, TY>>,                                \
+        &layout_check<Shape<BM, BN, WM, WN, BK, NS, 0, false, TY>>,                          \
+        &launch<Shape<BM, BN, WM, WN, BK, NS, 1, false, TY>>, EFF,                           \
+        &launch<Shape<BM, BN, WM, WN, BK, NS, 2, false, TY>>,                                \
+        &launch<Shape<BM, BN, WM, WN, BK, NS, 0, true, TY>>                                  \
   }
 
-// The LDS layouts and the data path do not depend on the element type, so
-// both tables share the layout checks and the measured tile efficiencies.
-#define HGEMM_TR_TABLE(BF, DT, TAG)                                   \
-  {HGEMM_TR_VARIANT(BF, DT, TAG, 256, 256, 128, 128, 64, 2, 1.00f), \
-   HGEMM_TR_VARIANT(BF, DT, TAG, 256, 256, 128, 128, 32, 4, 0.99f), \
-   HGEMM_TR_VARIANT(BF, DT, TAG, 256, 256, 128, 128, 32, 5, 0.99f), \
-   HGEMM_TR_VARIANT(BF, DT, TAG, 256, 128, 128, 64, 64, 3, 0.90f),  \
-   HGEMM_TR_VARIANT(BF, DT, TAG, 128, 256, 64, 128, 64, 3, 0.89f),  \
-   HGEMM_TR_VARIANT(BF, DT, TAG, 128, 128, 64, 64, 64, 2, 0.71f)}
+// The 16-bit LDS layouts and data path do not depend on the element type,
+// so FP16 and BF16 share the tiles and the measured tile efficiencies.  FP8
+// moves 128 k per slice in the same bytes; its B rows must span 256 bytes
+// (the 2*(k%8) chunk XOR), so its tiles are 256 columns wide.
+#define HGEMM_TR_TABLE(TY, DT, TAG)                                   \
+  {HGEMM_TR_VARIANT(TY, DT, TAG, 256, 256, 128, 128, 64, 2, 1.00f), \
+   HGEMM_TR_VARIANT(TY, DT, TAG, 256, 256, 128, 128, 32, 4, 0.99f), \
+   HGEMM_TR_VARIANT(TY, DT, TAG, 256, 256, 128, 128, 32, 5, 0.99f), \
+   HGEMM_TR_VARIANT(TY, DT, TAG, 256, 128, 128, 64, 64, 3, 0.90f),  \
+   HGEMM_TR_VARIANT(TY, DT, TAG, 128, 256, 64, 128, 64, 3, 0.89f),  \
+   HGEMM_TR_VARIANT(TY, DT, TAG, 128, 128, 64, 64, 64, 2, 0.71f)}
 
-const Variant kVariants[] = HGEMM_TR_TABLE(false, GEMM_DTYPE_F16, "f16");
-const Variant kVariantsBf[] = HGEMM_TR_TABLE(true, GEMM_DTYPE_BF16, "bf16");
+const Variant kVariants[] = HGEMM_TR_TABLE(0, GEMM_DTYPE_F16, "f16");
+const Variant kVariantsBf[] = HGEMM_TR_TABLE(1, GEMM_DTYPE_BF16, "bf16");
+const Variant kVariantsF8[] = {
+    HGEMM_TR_VARIANT(2, GEMM_DTYPE_F8, "f8", 256, 256, 128, 128, 128, 2, 1.00f),
+    HGEMM_TR_VARIANT(2, GEMM_DTYPE_F8, "f8", 128, 256, 64, 128, 128, 3, 0.89f),
+};
 
 }  // namespace
 
-const Variant* hgemm_tr_variants(int* count, bool bf16) {
-  *count = bf16 ? sizeof(kVariantsBf) / sizeof(kVariantsBf[0])
-                : sizeof(kVariants) / sizeof(kVariants[0]);
-  return bf16 ? kVariantsBf : kVariants;
+const Variant* hgemm_tr_variants(int* count, int ty) {
+  const Variant* v = ty == 2 ? kVariantsF8 : ty == 1 ? kVariantsBf : kVariants;
+  *count = ty == 2 ? sizeof(kVariantsF8) / sizeof(kVariantsF8[0])
+                   : ty == 1 ? sizeof(kVariantsBf) / sizeof(kVariantsBf[0])
+                             : sizeof(kVariants) / sizeof(kVariants[0]);
+  return v;
 }
 
 }  // namespace gemm

@@ -28,6 +28,7 @@ GEMM_ERR_ALIAS = -4
 DTYPE_F32 = 0
 DTYPE_F16 = 1
 DTYPE_BF16 = 2
+DTYPE_F8 = 3  # FP8 E4M3 A and B, bfloat16 C
 FAMILY_MFMA = 0
 FAMILY_SIMT = 1
 ORDER_ROW = 0
@@ -37,10 +38,8 @@ ORDER_XCD = 2
 ACT_NONE = 0
 ACT_RELU = 1
 
-EXPORTS = ["gemm_f32", "gemm_f16", "gemm_bf16", "gemm_f32_ex", "gemm_f16_ex", "gemm_bf16_ex",
-           "gemm_f32_bt", "gemm_f16_bt", "gemm_bf16_bt",
-           "gemm_f32_epi", "gemm_f16_epi", "gemm_bf16_epi",
-           "gemm_f32_splitk", "gemm_f16_splitk", "gemm_bf16_splitk",
+TYPES = ("f32", "f16", "bf16", "f8")
+EXPORTS = [f"gemm_{t}{form}" for form in ("", "_ex", "_bt", "_epi", "_splitk") for t in TYPES] + [
            "gemm_splitk_workspace_bytes", "gemm_select_splitk_config",
            "gemm_num_configs", "gemm_get_config", "gemm_select_config", "gemm_tile_of_block",
            "gemm_layout_check", "gemm_load_tuning", "gemm_status_string",
@@ -86,7 +85,7 @@ def _declare(lib):
     i64, i32, p = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
     cfgp = ctypes.POINTER(GemmConfig)
     gemm_args = [i64, i64, i64, p, i64, p, i64, p, i64, p]
-    types = ("f32", "f16", "bf16")
+    types = TYPES
     for t in types:
         getattr(lib, f"gemm_{t}").argtypes = gemm_args
         getattr(lib, f"gemm_{t}").restype = ctypes.c_int
@@ -153,6 +152,10 @@ def gemm_bf16(M, N, K, A, lda, B, ldb, C, ldc, stream=None) -> int:
     return lib().gemm_bf16(M, N, K, A, lda, B, ldb, C, ldc, stream)
 
 
+def gemm_f8(M, N, K, A, lda, B, ldb, C, ldc, stream=None) -> int:
+    return lib().gemm_f8(M, N, K, A, lda, B, ldb, C, ldc, stream)
+
+
 def gemm_f32_ex(M, N, K, A, lda, B, ldb, C, ldc, stream, cfg: GemmConfig) -> int:
     return lib().gemm_f32_ex(M, N, K, A, lda, B, ldb, C, ldc, stream,
                              ctypes.byref(cfg) if cfg is not None else None)
@@ -168,6 +171,11 @@ def gemm_bf16_ex(M, N, K, A, lda, B, ldb, C, ldc, stream, cfg: GemmConfig) -> in
                               ctypes.byref(cfg) if cfg is not None else None)
 
 
+def gemm_f8_ex(M, N, K, A, lda, B, ldb, C, ldc, stream, cfg: GemmConfig) -> int:
+    return lib().gemm_f8_ex(M, N, K, A, lda, B, ldb, C, ldc, stream,
+                            ctypes.byref(cfg) if cfg is not None else None)
+
+
 def gemm_f32_bt(M, N, K, A, lda, Bt, ldbt, C, ldc, stream=None, cfg: GemmConfig | None = None) -> int:
     return lib().gemm_f32_bt(M, N, K, A, lda, Bt, ldbt, C, ldc, stream,
                              ctypes.byref(cfg) if cfg is not None else None)
@@ -181,6 +189,11 @@ def gemm_f16_bt(M, N, K, A, lda, Bt, ldbt, C, ldc, stream=None, cfg: GemmConfig 
 def gemm_bf16_bt(M, N, K, A, lda, Bt, ldbt, C, ldc, stream=None, cfg: GemmConfig | None = None) -> int:
     return lib().gemm_bf16_bt(M, N, K, A, lda, Bt, ldbt, C, ldc, stream,
                               ctypes.byref(cfg) if cfg is not None else None)
+
+
+def gemm_f8_bt(M, N, K, A, lda, Bt, ldbt, C, ldc, stream=None, cfg: GemmConfig | None = None) -> int:
+    return lib().gemm_f8_bt(M, N, K, A, lda, Bt, ldbt, C, ldc, stream,
+                            ctypes.byref(cfg) if cfg is not None else None)
 
 
 def gemm_f32_epi(M, N, K, A, lda, B, ldb, C, ldc, stream, cfg: GemmConfig | None,
@@ -204,6 +217,13 @@ def gemm_bf16_epi(M, N, K, A, lda, B, ldb, C, ldc, stream, cfg: GemmConfig | Non
                                ctypes.byref(epi) if epi is not None else None)
 
 
+def gemm_f8_epi(M, N, K, A, lda, B, ldb, C, ldc, stream, cfg: GemmConfig | None,
+                epi: GemmEpilogue | None) -> int:
+    return lib().gemm_f8_epi(M, N, K, A, lda, B, ldb, C, ldc, stream,
+                             ctypes.byref(cfg) if cfg is not None else None,
+                             ctypes.byref(epi) if epi is not None else None)
+
+
 def gemm_f32_splitk(M, N, K, A, lda, B, ldb, C, ldc, workspace, workspace_bytes, stream=None,
                     cfg: GemmConfig | None = None) -> int:
     return lib().gemm_f32_splitk(M, N, K, A, lda, B, ldb, C, ldc, workspace, workspace_bytes, stream,
@@ -222,11 +242,17 @@ def gemm_bf16_splitk(M, N, K, A, lda, B, ldb, C, ldc, workspace, workspace_bytes
                                   stream, ctypes.byref(cfg) if cfg is not None else None)
 
 
+def gemm_f8_splitk(M, N, K, A, lda, B, ldb, C, ldc, workspace, workspace_bytes, stream=None,
+                   cfg: GemmConfig | None = None) -> int:
+    return lib().gemm_f8_splitk(M, N, K, A, lda, B, ldb, C, ldc, workspace, workspace_bytes,
+                                stream, ctypes.byref(cfg) if cfg is not None else None)
+
+
 # Entry points per dtype code, for callers that dispatch on it.
 def entry(dtype: int, form: str = ""):
     """The binding of gemm_<type><form> (form "", "_ex", "_bt", "_epi",
-    "_splitk") for dtype DTYPE_F32 / DTYPE_F16 / DTYPE_BF16."""
-    name = {DTYPE_F32: "f32", DTYPE_F16: "f16", DTYPE_BF16: "bf16"}[dtype]
+    "_splitk") for dtype DTYPE_F32 / DTYPE_F16 / DTYPE_BF16 / DTYPE_F8."""
+    name = {DTYPE_F32: "f32", DTYPE_F16: "f16", DTYPE_BF16: "bf16", DTYPE_F8: "f8"}[dtype]
     return globals()[f"gemm_{name}{form}"]
 
 
@@ -325,8 +351,9 @@ def matmul(a, b, out=None, config: GemmConfig | None = None, stream=None, split_
            alpha: float = 1.0, beta: float = 0.0, bias=None, act: int = ACT_NONE,
            b_transposed: bool = False):
     """C = a @ b on the GPU through libgemm.  a: M x K, b: K x N, of one
-    type (float32, float16 or bfloat16), row-major (any row stride).
-    Returns ``out`` (allocated when None).  Raises GemmError on a non-OK status.
+    type (float32, float16, bfloat16, or float8_e4m3fn with a bfloat16
+    result), row-major (any row stride).  Returns ``out`` (allocated when
+    None).  Raises GemmError on a non-OK status.
 
     With ``config`` None and ``split_k`` True, shapes for which the library
     chooses split-K (too few output tiles for the GPU) run the split-K form
@@ -340,9 +367,11 @@ def matmul(a, b, out=None, config: GemmConfig | None = None, stream=None, split_
     fused epilogue out = act(alpha * (a @ b) + beta * out + bias) (through
     gemm_*_epi; ``out`` must then be given when beta != 0)."""
     import torch
-    dtypes = {torch.float32: DTYPE_F32, torch.float16: DTYPE_F16, torch.bfloat16: DTYPE_BF16}
+    dtypes = {torch.float32: DTYPE_F32, torch.float16: DTYPE_F16, torch.bfloat16: DTYPE_BF16,
+              torch.float8_e4m3fn: DTYPE_F8}
     if a.dtype != b.dtype or a.dtype not in dtypes:
-        raise TypeError("a and b must both be float32, float16 or bfloat16")
+        raise TypeError("a and b must both be float32, float16, bfloat16 or float8_e4m3fn")
+    c_dtype = torch.bfloat16 if a.dtype == torch.float8_e4m3fn else a.dtype
     if not (a.is_cuda and b.is_cuda):
         raise ValueError("a and b must be GPU tensors")
     M, K = a.shape
@@ -350,8 +379,8 @@ def matmul(a, b, out=None, config: GemmConfig | None = None, stream=None, split_
     if K2 != K:
         raise ValueError(f"inner dimensions differ: {K} vs {K2}")
     if out is None:
-        out = torch.empty((M, N), dtype=a.dtype, device=a.device)
-    if out.shape != (M, N) or out.dtype != a.dtype:
+        out = torch.empty((M, N), dtype=c_dtype, device=a.device)
+    if out.shape != (M, N) or out.dtype != c_dtype:
         raise ValueError("out has the wrong shape or dtype")
     if stream is None:
         stream = torch.cuda.current_stream(a.device).cuda_stream

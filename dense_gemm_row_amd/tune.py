@@ -83,14 +83,17 @@ def time_config(gemm, torch, fn, args, cfg, stream, warmup: int, reps: int, ws=N
 
 def tune_shape(gemm, torch, kind: str, M: int, N: int, K: int, orders, warmup: int,
                reps: int, splits=(1,)) -> dict:
-    dtype = {"f32": gemm.DTYPE_F32, "f16": gemm.DTYPE_F16, "bf16": gemm.DTYPE_BF16}[kind]
-    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[kind]
+    dtype = {"f32": gemm.DTYPE_F32, "f16": gemm.DTYPE_F16, "bf16": gemm.DTYPE_BF16,
+             "f8": gemm.DTYPE_F8}[kind]
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16,
+           "f8": torch.float8_e4m3fn}[kind]
+    cdt = torch.bfloat16 if kind == "f8" else tdt  # FP8 products are BF16
     dev = torch.device("cuda:0")
     gen = torch.Generator(device=dev)
     gen.manual_seed(M * 1000003 + N * 1009 + K)
     a = (torch.rand((M, K), device=dev, generator=gen) * 2 - 1).to(tdt)
     b = (torch.rand((K, N), device=dev, generator=gen) * 2 - 1).to(tdt)
-    c = torch.empty((M, N), device=dev, dtype=tdt)
+    c = torch.empty((M, N), device=dev, dtype=cdt)
     fn = gemm.entry(dtype, "_ex")
     args = (M, N, K, a.data_ptr(), K, b.data_ptr(), N, c.data_ptr(), N)
     stream = torch.cuda.current_stream(dev)
@@ -143,7 +146,7 @@ def tune_shape(gemm, torch, kind: str, M: int, N: int, K: int, orders, warmup: i
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--shapes", nargs="+", type=parse_shape, required=True, help="MxNxK ...")
-    ap.add_argument("--dtypes", nargs="+", choices=["f32", "f16", "bf16"], default=["f32", "f16"])
+    ap.add_argument("--dtypes", nargs="+", choices=["f32", "f16", "bf16", "f8"], default=["f32", "f16"])
     ap.add_argument("--orders", nargs="+", type=parse_order,
                     default=[parse_order("xcd:4"), parse_order("xcd:8"), parse_order("grouped:8")],
                     help="tile orders to try: row | grouped:G | xcd:G")

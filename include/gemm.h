@@ -66,17 +66,22 @@ typedef enum gemm_status {
 typedef uint16_t gemm_f16_t;
 /* bfloat16 bit pattern: the upper 16 bits of an IEEE 754 binary32. */
 typedef uint16_t gemm_bf16_t;
+/* FP8 E4M3 byte (OCP 8-bit floating point: 1 sign, 4 exponent bits with
+ * bias 7, 3 fraction bits, no infinities, largest finite 448). */
+typedef uint8_t gemm_f8_t;
 
 typedef enum gemm_dtype {
     GEMM_DTYPE_F32 = 0,
     GEMM_DTYPE_F16 = 1,
-    GEMM_DTYPE_BF16 = 2
+    GEMM_DTYPE_BF16 = 2,
+    GEMM_DTYPE_F8 = 3 /* E4M3 A and B, bfloat16 C */
 } gemm_dtype_t;
 
 /* Kernel families. */
 typedef enum gemm_family {
     GEMM_FAMILY_MFMA = 0, /* matrix-core kernels (v_mfma_f32_32x32x2_f32,
-                             v_mfma_f32_32x32x16_f16 / _bf16)             */
+                             v_mfma_f32_32x32x16_f16 / _bf16,
+                             v_mfma_f32_32x32x64_f8f6f4)                  */
     GEMM_FAMILY_SIMT = 1  /* vector-FMA kernel, kept as an ablation (FP32) */
 } gemm_family_t;
 
@@ -141,7 +146,24 @@ gemm_status_t gemm_bf16(int64_t M, int64_t N, int64_t K,
                         const gemm_bf16_t *B, int64_t ldb,
                         gemm_bf16_t *C, int64_t ldc, void *stream);
 
-/* As gemm_f32 / gemm_f16 / gemm_bf16 with a forced variant and tile order
+/*
+ * FP8 GEMM, C = A x B: FP8 E4M3 inputs, FP32 accumulation, bfloat16 output
+ * rounded to nearest even (E4M3 products reach 448^2 * K, past FP16's
+ * range; bfloat16 keeps FP32's).  FP8 is the tier above FP16 that the
+ * GB300 GEMM article names for the matrix units (section 1.1).  Inputs are
+ * taken as they are (no scale factors; the fused-epilogue form's alpha
+ * applies a per-tensor scale).  Only the vector layout is supported: A, B,
+ * C 16-byte aligned, K, N, lda, ldb multiples of 16, ldc a multiple of 8
+ * (else UNSUPPORTED, before any launch).  Every gemm_f16_* entry point has a
+ * gemm_f8_* counterpart with gemm_f8_t A and B and gemm_bf16_t C;
+ * gemm_splitk_workspace_bytes takes GEMM_DTYPE_F8.
+ */
+gemm_status_t gemm_f8(int64_t M, int64_t N, int64_t K,
+                      const gemm_f8_t *A, int64_t lda,
+                      const gemm_f8_t *B, int64_t ldb,
+                      gemm_bf16_t *C, int64_t ldc, void *stream);
+
+/* As gemm_f32 / gemm_f16 / gemm_bf16 / gemm_f8 with a forced variant and tile order
  * (tests, tuner, ablation).  cfg->id must name a variant of the matching
  * dtype. */
 gemm_status_t gemm_f32_ex(int64_t M, int64_t N, int64_t K,
@@ -159,6 +181,11 @@ gemm_status_t gemm_bf16_ex(int64_t M, int64_t N, int64_t K,
                            const gemm_bf16_t *B, int64_t ldb,
                            gemm_bf16_t *C, int64_t ldc, void *stream,
                            const gemm_config_t *cfg);
+gemm_status_t gemm_f8_ex(int64_t M, int64_t N, int64_t K,
+                         const gemm_f8_t *A, int64_t lda,
+                         const gemm_f8_t *B, int64_t ldb,
+                         gemm_bf16_t *C, int64_t ldc, void *stream,
+                         const gemm_config_t *cfg);
 
 /*
  * Split-K GEMM: the same results contract as gemm_f32 / gemm_f16, for shapes
@@ -205,6 +232,12 @@ gemm_status_t gemm_bf16_splitk(int64_t M, int64_t N, int64_t K,
                                gemm_bf16_t *C, int64_t ldc,
                                void *workspace, int64_t workspace_bytes,
                                void *stream, const gemm_config_t *cfg);
+gemm_status_t gemm_f8_splitk(int64_t M, int64_t N, int64_t K,
+                             const gemm_f8_t *A, int64_t lda,
+                             const gemm_f8_t *B, int64_t ldb,
+                             gemm_bf16_t *C, int64_t ldc,
+                             void *workspace, int64_t workspace_bytes,
+                             void *stream, const gemm_config_t *cfg);
 
 /* Workspace bytes a split-K call with `splits` requested chunks needs
  * (0 when it would not split; splits <= 0 means the library's choice for
@@ -238,6 +271,11 @@ gemm_status_t gemm_bf16_bt(int64_t M, int64_t N, int64_t K,
                            const gemm_bf16_t *Bt, int64_t ldbt,
                            gemm_bf16_t *C, int64_t ldc, void *stream,
                            const gemm_config_t *cfg);
+gemm_status_t gemm_f8_bt(int64_t M, int64_t N, int64_t K,
+                         const gemm_f8_t *A, int64_t lda,
+                         const gemm_f8_t *Bt, int64_t ldbt,
+                         gemm_bf16_t *C, int64_t ldc, void *stream,
+                         const gemm_config_t *cfg);
 
 /* Activation applied by the fused epilogue. */
 typedef enum gemm_act {
@@ -286,6 +324,11 @@ gemm_status_t gemm_bf16_epi(int64_t M, int64_t N, int64_t K,
                             const gemm_bf16_t *B, int64_t ldb,
                             gemm_bf16_t *C, int64_t ldc, void *stream,
                             const gemm_config_t *cfg, const gemm_epilogue_t *epi);
+gemm_status_t gemm_f8_epi(int64_t M, int64_t N, int64_t K,
+                          const gemm_f8_t *A, int64_t lda,
+                          const gemm_f8_t *B, int64_t ldb,
+                          gemm_bf16_t *C, int64_t ldc, void *stream,
+                          const gemm_config_t *cfg, const gemm_epilogue_t *epi);
 
 /* Variant table: count per dtype, and the description of variant idx. */
 int32_t gemm_num_configs(int32_t dtype);
@@ -317,7 +360,7 @@ gemm_status_t gemm_layout_check(int32_t dtype, int32_t idx, int32_t banks,
                                 int64_t out[2]);
 
 /* Tuning table: a text file of lines "dtype M N K name order group_m
- * [splits]" (dtype f32|f16|bf16; splits defaults to 1).  Exact-shape matches
+ * [splits]" (dtype f32|f16|bf16|f8; splits defaults to 1).  Exact-shape matches
  * override the heuristic.  Loading replaces the previous table; NULL clears
  * it.  Not safe to call concurrently with GEMM calls. */
 gemm_status_t gemm_load_tuning(const char *path);

@@ -19,9 +19,12 @@ from dense_gemm_row_amd import gemm, synth
 CANARY_F32 = np.uint32(0x7FC0DEAD)  # a quiet NaN payload nobody computes
 CANARY_F16 = np.uint16(0x7E5A)
 CANARY_BF16 = np.uint16(0x7FDA)
-CANARY = {"f32": CANARY_F32, "f16": CANARY_F16, "bf16": CANARY_BF16}
-DTYPE = {"f32": gemm.DTYPE_F32, "f16": gemm.DTYPE_F16, "bf16": gemm.DTYPE_BF16}
-VIEW = {"f32": np.float32, "f16": np.float16, "bf16": synth.BF16}
+CANARY_F8 = np.uint8(0x7F)  # the E4M3 NaN
+CANARY = {"f32": CANARY_F32, "f16": CANARY_F16, "bf16": CANARY_BF16, "f8": CANARY_F8}
+DTYPE = {"f32": gemm.DTYPE_F32, "f16": gemm.DTYPE_F16, "bf16": gemm.DTYPE_BF16, "f8": gemm.DTYPE_F8}
+VIEW = {"f32": np.float32, "f16": np.float16, "bf16": synth.BF16, "f8": synth.F8}
+BITS = {"f32": np.uint32, "f16": np.uint16, "bf16": np.uint16, "f8": np.uint8}
+TORCH_BITS = {"f32": np.int32, "f16": np.int16, "bf16": np.int16, "f8": np.int8}
 
 
 def kind_of(a: np.ndarray) -> str:
@@ -31,6 +34,8 @@ def kind_of(a: np.ndarray) -> str:
         return "f16"
     if a.dtype == synth.BF16:
         return "bf16"
+    if a.dtype == synth.F8:
+        return "f8"
     raise TypeError(f"unsupported dtype {a.dtype}")
 
 
@@ -38,6 +43,8 @@ def wide(x: np.ndarray) -> np.ndarray:
     """Exact float64 values of an FP32 / FP16 / BF16 array."""
     if x.dtype == synth.BF16:
         return synth.bf16_to_f32(x).astype(np.float64)
+    if x.dtype == synth.F8:
+        return synth.e4m3_to_f32(x).astype(np.float64)
     return x.astype(np.float64)
 
 
@@ -55,18 +62,16 @@ class DevMatrix:
         self.rows, self.cols, self.kind = rows, cols, kind
         self.ld = max(cols + pad, 1)
         self.guard = guard + offset
-        self.bits = np.uint32 if kind == "f32" else np.uint16
-        self.es = 4 if kind == "f32" else 2
+        self.bits = BITS[kind]
+        self.es = np.dtype(self.bits).itemsize
         canary = CANARY[kind]
         n = self.guard + rows * self.ld + guard
         flat = np.full(n, canary, dtype=self.bits)
         if host is not None and rows and cols:
             view = flat[self.guard:self.guard + rows * self.ld].reshape(rows, self.ld)
             view[:, :cols] = host.view(self.bits)
-        tdt = torch.int32 if kind == "f32" else torch.int16
         self.flat_host = flat
-        self.dev = torch.from_numpy(flat.view(np.int32 if kind == "f32" else np.int16)).to("cuda")
-        assert self.dev.dtype == tdt
+        self.dev = torch.from_numpy(flat.view(TORCH_BITS[kind])).to("cuda")
 
     @property
     def ptr(self) -> int:
@@ -114,12 +119,13 @@ def run(A: np.ndarray, B: np.ndarray, cfg=None, pad=(0, 0, 0), offset=(0, 0, 0),
     bt: B is given transposed (the argument is Bt, N x K) and the call is
     gemm_*_bt; A @ Bt.T is computed."""
     kind = kind_of(A)
+    ckind = oracle.out_kind(kind)  # FP8 products are BF16
     dtype = DTYPE[kind]
     M, K = A.shape
     N = B.shape[0] if bt else B.shape[1]
     dA = DevMatrix(A, M, K, kind, pad=pad[0], offset=offset[0])
     dB = DevMatrix(B, *((N, K) if bt else (K, N)), kind, pad=pad[1], offset=offset[1])
-    dC = DevMatrix(None if epi is None else epi.get("C0"), M, N, kind, pad=pad[2], offset=offset[2])
+    dC = DevMatrix(None if epi is None else epi.get("C0"), M, N, ckind, pad=pad[2], offset=offset[2])
     bias_dev, epi_s = None, None
     if epi is not None:
         bias = epi.get("bias")
@@ -188,6 +194,8 @@ def rounded(ref: np.ndarray, kind: str) -> np.ndarray:
     assert np.array_equal(ref32.astype(np.float64), ref), "exact results must be FP32 values"
     if kind == "f32":
         return ref
+    if kind == "f8":
+        kind = "bf16"
     if kind == "f16":
         return ref32.astype(np.float16).astype(np.float64)
     import torch

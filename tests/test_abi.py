@@ -20,7 +20,7 @@ PA, PB, PC = 0x10000000, 0x20000000, 0x30000000
 def _dtype_of(fn):
     """The dtype code of a binding gemm_<type>[_form]."""
     t = fn.__name__.split("_")[1]
-    return {"f32": gemm.DTYPE_F32, "f16": gemm.DTYPE_F16, "bf16": gemm.DTYPE_BF16}[t]
+    return {"f32": gemm.DTYPE_F32, "f16": gemm.DTYPE_F16, "bf16": gemm.DTYPE_BF16, "f8": gemm.DTYPE_F8}[t]
 
 
 def header_functions():
@@ -308,6 +308,35 @@ def test_bf16_tables_mirror_f16():
     assert c.name.decode().startswith("tr_bf16_") and c.bm * c.bn == 256 * 256
     s = gemm.gemm_select_splitk_config(gemm.DTYPE_BF16, 1024, 1024, 8192)
     assert s.splits > 1
-    assert gemm.gemm_num_configs(3) == 0
+    assert gemm.gemm_num_configs(4) == 0
     with pytest.raises(gemm.GemmError):
-        gemm.gemm_get_config(3, 0)
+        gemm.gemm_get_config(4, 0)
+
+
+def test_f8_table_and_validation():
+    """FP8 (E4M3 in, BF16 out): LDS-direct variants only, layouts valid and
+    conflict-free; operands off the vector layout are refused (UNSUPPORTED)
+    before any launch; sizes are checked with 1-byte A/B and 2-byte C."""
+    cfgs = gemm.configs(gemm.DTYPE_F8)
+    assert cfgs and all(c.name.decode().startswith("tr_f8_") and c.bk == 128 for c in cfgs)
+    for c in cfgs:
+        assert gemm.gemm_layout_check(gemm.DTYPE_F8, c.id, 64) == (0, 0), c.name
+    sel = gemm.gemm_select_config(gemm.DTYPE_F8, 4096, 4096, 4096)
+    assert sel.bm * sel.bn == 256 * 256
+    assert gemm.gemm_select_splitk_config(gemm.DTYPE_F8, 1024, 1024, 8192).splits > 1
+    f = gemm.gemm_f8
+    U = gemm.GEMM_ERR_UNSUPPORTED
+    assert f(64, 64, 64, PA + 8, 64, PB, 64, PC, 64) == U        # A not 16-byte aligned
+    assert f(64, 64, 72, PA, 72, PB, 64, PC, 64) == U            # K not a multiple of 16
+    assert f(64, 72, 64, PA, 64, PB, 72, PC, 72) == U            # N not a multiple of 16
+    assert f(64, 64, 64, PA, 64, PB, 64, PC, 68) == U            # ldc not a multiple of 8
+    assert "FP8" in gemm.gemm_last_error()
+    assert gemm.gemm_f8_bt(64, 64, 64, PA, 64, PB, 72, PC, 64) == U
+    assert gemm.gemm_f8_splitk(64, 64, 4096, PA, 4096, PB, 64 + 8, PC, 64, PC + (1 << 20), 1 << 24) == U
+    ok = gemm.GemmEpilogue(1.0, 0.0, None, gemm.ACT_NONE)
+    assert gemm.gemm_f8_epi(64, 64, 64, PA, 64, PB, 64, PC + 2, 64, None, None, ok) == U
+    # C is 2 bytes per element, A and B 1: C just past A's 64 x 64 bytes is fine,
+    # C overlapping B's last row is not.
+    assert f(0, 64, 64, PA, 64, PB, 64, PA + 64 * 64, 64) == gemm.GEMM_OK
+    assert f(64, 64, 64, PA, 64, PB, 64, PB + 63 * 64, 64) == gemm.GEMM_ERR_ALIAS
+    assert gemm.gemm_splitk_workspace_bytes(gemm.DTYPE_F8, 10, 20, 1000, 3) == 3 * 10 * 20 * 4

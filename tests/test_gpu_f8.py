@@ -1,0 +1,293 @@
+"""GPU parity of the FP8 GEMM (gemm_f8*, through the C-ABI) against the CPU
+oracle: FP8 E4M3 inputs, FP32 accumulation, bfloat16 output.
+
+* Exact inputs (small integers, identity, permutation, the rounding probe):
+  E4M3 products are exact in FP32, so the one correct output is the
+  oracle's exact result rounded once to bfloat16 (ties to even); every FP8
+  variant must produce it on edge shapes (M ragged; N and K multiples of 16,
+  the vector layout FP8 requires), padded leading dimensions, every tile
+  order and every form (plain, split-K, fused epilogue, transposed B).
+* Random uniform[-1, 1) inputs rounded to E4M3: max_ij |C - C_ref| /
+  sum_k |A_ik||B_kj| <= 5e-3 (bfloat16's unit roundoff plus the FP32
+  accumulation bound), judged after the output rounding.
+* Operands off the vector layout are refused with GEMM_ERR_UNSUPPORTED.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from dense_gemm_row_amd import gemm, synth
+from tests import golden_data
+from tests.gpu_util import check_full, check_rows, exact_equal, log, rounded, run, wide
+
+pytestmark = pytest.mark.gpu
+
+F8 = synth.F8
+DT = gemm.DTYPE_F8
+CFGS = list(range(gemm.gemm_num_configs(DT)))
+TOL = oracle.F8_TOL
+
+EDGE_SHAPES = [(1, 16, 16), (2, 16, 32), (31, 48, 16), (64, 64, 128), (127, 144, 80),
+               (130, 272, 96), (257, 128, 208), (65, 304, 512)]
+
+
+def _ints(M, N, K, seed=7):
+    return synth.small_int(seed, 0, M, K, dtype=F8), synth.small_int(seed, 1, K, N, dtype=F8)
+
+
+def _cfg(idx, order=None, group_m=None):
+    c = gemm.gemm_get_config(DT, idx)
+    if order is not None:
+        c.order = order
+    if group_m is not None:
+        c.group_m = group_m
+    return c
+
+
+def _bits(x):
+    return x.view(np.uint16)
+
+
+def test_f8_table():
+    assert len(CFGS) >= 2
+    assert all(gemm.gemm_get_config(DT, i).dtype == DT for i in CFGS)
+
+
+@pytest.mark.parametrize("idx", CFGS)
+@pytest.mark.parametrize("shape", EDGE_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_f8_exact_small_int(idx, shape):
+    M, N, K = shape
+    A, B = _ints(M, N, K)
+    cfg = _cfg(idx)
+    log(f"f8 exact cfg={cfg.name.decode()} shape={shape}")
+    C, _ = run(A, B, cfg)
+    assert exact_equal(A, B, C)
+
+
+@pytest.mark.parametrize("order", [gemm.ORDER_ROW, gemm.ORDER_GROUPED, gemm.ORDER_XCD])
+def test_f8_tile_orders_exact(order):
+    M, N, K = 300, 528, 144
+    A, B = _ints(M, N, K, seed=11)
+    for idx in CFGS:
+        cfg = _cfg(idx, order=order, group_m=3)
+        log(f"f8 order={order} cfg={cfg.name.decode()}")
+        C, _ = run(A, B, cfg)
+        assert exact_equal(A, B, C), cfg.name
+
+
+@pytest.mark.parametrize("pad", [(16, 32, 8), (48, 16, 24)])
+def test_f8_padded_leading_dimensions(pad):
+    M, N, K = 129, 208, 272
+    A, B = _ints(M, N, K, seed=3)
+    for idx in CFGS:
+        cfg = _cfg(idx)
+        log(f"f8 pad={pad} cfg={cfg.name.decode()}")
+        C, _ = run(A, B, cfg, pad=pad)
+        assert exact_equal(A, B, C), cfg.name
+
+
+@pytest.mark.parametrize("pad,offset", [((1, 0, 0), (0, 0, 0)), ((0, 0, 0), (1, 0, 0)),
+                                        ((0, 0, 0), (0, 0, 1))])
+def test_f8_off_vector_layout_is_refused(pad, offset):
+    """lda not a multiple of 16, A or C misaligned: UNSUPPORTED, and C
+    untouched (run's canary check)."""
+    A, B = _ints(64, 64, 64, seed=5)
+    log(f"f8 unsupported pad={pad} offset={offset}")
+    with pytest.raises(gemm.GemmError) as e:
+        run(A, B, None, pad=pad, offset=offset)
+    assert e.value.status == gemm.GEMM_ERR_UNSUPPORTED
+
+
+def test_f8_output_rounds_to_nearest_even():
+    # Exact FP32 sums of E4M3 products halfway between two bfloat16
+    # neighbours (tests/golden/f8_bf16_rne_halfway.txt), zero-padded to
+    # K = N = 16 for the vector layout.
+    mats = {}
+    for r in golden_data.rows("f8_bf16_rne_halfway.txt"):
+        mats.setdefault(r[0], []).append([int(x, 16) for x in r[2:]])
+    A = np.zeros((3, 16), np.uint8)
+    B = np.zeros((16, 16), np.uint8)
+    A[:, :3] = np.array(mats["A"], np.uint8)
+    B[:3, :2] = np.array(mats["B"], np.uint8)
+    expect = np.array(mats["C"], np.uint16)
+    for idx in CFGS:
+        log(f"f8 RNE probe cfg={idx}")
+        C, _ = run(A.view(F8), B.view(F8), _cfg(idx))
+        assert np.array_equal(_bits(C)[:, :2], expect), _bits(C)[:, :2]
+        assert not np.any(_bits(C)[:, 2:])
+
+
+def test_f8_k_zero_and_empty():
+    log("f8 K=0, M=0")
+    C, _ = run(synth.to_e4m3(np.zeros((70, 0), np.float32)), synth.to_e4m3(np.zeros((0, 96), np.float32)))
+    assert C.shape == (70, 96) and np.all(_bits(C) == 0)
+    C, _ = run(synth.to_e4m3(np.zeros((0, 16), np.float32)), synth.to_e4m3(np.ones((16, 32), np.float32)))
+    assert C.shape == (0, 32)
+
+
+def test_f8_identity_and_permutation_4096():
+    n = 4096
+    B = synth.uniform_f8(5, 1, n, n)
+    eye = synth.to_e4m3(np.eye(n, dtype=np.float32))
+    log("f8 identity 4096")
+    C, _ = run(eye, B)
+    assert np.array_equal(wide(C), wide(B))  # every E4M3 value is a BF16 value
+    p = synth.permutation(9, 2, n)
+    P = np.zeros((n, n), np.float32)
+    P[np.arange(n), p] = 1
+    log("f8 permutation 4096")
+    C, _ = run(synth.to_e4m3(P), B)
+    assert np.array_equal(wide(C), wide(B)[p])
+
+
+def test_f8_deterministic():
+    A, B = synth.workload(1024, 1024, 1024, "f8", seed=4)
+    log("f8 determinism")
+    C1, _ = run(A, B)
+    C2, _ = run(A, B, repeat=3)
+    assert np.array_equal(_bits(C1), _bits(C2))
+
+
+@pytest.mark.parametrize("n", [256, 2048])
+def test_f8_random_full_check(n):
+    A, B = synth.workload(n, n, n, "f8")
+    for idx in CFGS if n == 256 else [None]:
+        cfg = None if idx is None else _cfg(idx)
+        log(f"f8 random {n}^3 cfg={'auto' if cfg is None else cfg.name.decode()}")
+        C, _ = run(A, B, cfg)
+        rep = check_full(A, B, C)
+        log(f"  max_rel={rep['max_rel']:.3e} max_abs={rep['max_abs']:.3e}")
+        assert rep["ok"], rep
+
+
+SWEEP = [(4096, 4096, 4096), (8192, 8192, 1024), (4096, 11008, 4096), (4000, 4000, 4000)]
+
+
+@pytest.mark.parametrize("shape", SWEEP, ids=lambda s: "x".join(map(str, s)))
+def test_f8_random_sampled_full_size(shape):
+    M, N, K = shape
+    A, B = synth.workload(M, N, K, "f8")
+    log(f"f8 random {shape} (auto config)")
+    C, _ = run(A, B)
+    rng = np.random.default_rng(0)
+    rows = sorted(set([0, M - 1, M // 2] + rng.integers(0, M, 24).tolist()))
+    rep = check_rows(A, B, C, rows)
+    log(f"  rows: max_rel={rep['max_rel']:.3e}")
+    assert rep["ok"], rep
+    ii, jj = rng.integers(0, M, 1000), rng.integers(0, N, 1000)
+    ii[:2], jj[:2] = [M - 1, 0], [N - 1, N - 1]
+    ref, den = oracle.gemm_entries(A, B, ii, jj)
+    rep = oracle.check(C[ii, jj].reshape(1, -1), ref.reshape(1, -1), den.reshape(1, -1), TOL)
+    log(f"  entries: max_rel={rep['max_rel']:.3e}")
+    assert rep["ok"], rep
+
+
+# --- split-K -------------------------------------------------------------------
+@pytest.mark.parametrize("shape", [(200, 144, 1024), (130, 256, 4096), (1, 16, 256)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_f8_splitk_exact_small_int(shape):
+    M, N, K = shape
+    A, B = _ints(M, N, K, seed=11)
+    for cfg in gemm.configs(DT):
+        for splits in (2, 3, 7):
+            cfg.splits = splits
+            log(f"f8 split-K exact cfg={cfg.name.decode()} splits={splits} shape={shape}")
+            C, _ = run(A, B, split=cfg)
+            assert exact_equal(A, B, C), (cfg.name, splits)
+
+
+def test_f8_splitk_auto_full_size():
+    M, N, K = 1024, 1024, 8192
+    sel = gemm.gemm_select_splitk_config(DT, M, N, K)
+    assert sel.splits > 1
+    A, B = synth.workload(M, N, K, "f8")
+    log(f"f8 split-K auto {M}x{N}x{K}: {sel.name.decode()} splits={sel.splits}")
+    C1, _ = run(A, B, split="auto")
+    rep = check_rows(A, B, C1, [0, 1, 511, 1000, 1023])
+    log(f"  rows: max_rel={rep['max_rel']:.3e}")
+    assert rep["ok"], rep
+    C2, _ = run(A, B, split="auto", repeat=2)
+    assert np.array_equal(_bits(C1), _bits(C2))
+
+
+# --- fused epilogue (old C and result in bfloat16) --------------------------------
+def _epi_ref(A, B, C0, e, bias):
+    return oracle.gemm_rows_epi(A, B, C0, e["alpha"], e["beta"], bias, e["act"])
+
+
+@pytest.mark.parametrize("shape", [(1, 16, 16), (31, 48, 32), (130, 272, 96), (257, 144, 64)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_f8_epilogue_exact_small_int(shape):
+    M, N, K = shape
+    A, B = _ints(M, N, K, seed=13)
+    C0 = synth.small_int(13, 2, M, N, -3, 3, dtype=synth.BF16)
+    bias = synth.small_int(13, 3, 1, N, -3, 3).ravel()
+    cases = [dict(alpha=2.0, beta=-1.0, act=0), dict(alpha=-1.0, beta=0.5, act=1),
+             dict(alpha=1.0, beta=0.0, act=1)]
+    for cfg in gemm.configs(DT):
+        for e in cases:
+            log(f"f8 epilogue exact cfg={cfg.name.decode()} {e} shape={shape}")
+            C, _ = run(A, B, cfg, epi=dict(e, C0=C0 if e["beta"] != 0.0 else None, bias=bias))
+            ref, _ = _epi_ref(A, B, C0, e, bias)
+            assert np.array_equal(wide(C), rounded(ref, "bf16")), (cfg.name, e)
+
+
+def test_f8_epilogue_random_scale():
+    """alpha as a per-tensor dequantisation scale, beta with the old C, bias
+    and ReLU, within tolerance on the epilogue's error scale."""
+    M, N, K = 300, 528, 704
+    A, B = synth.workload(M, N, K, "f8", seed=21)
+    C0 = synth.uniform_bf16(21, 2, M, N)
+    bias = synth.uniform_f32(21, 3, 1, N).ravel()
+    e = dict(alpha=0.0625, beta=-0.3, act=1)
+    ref, den = _epi_ref(A, B, C0, e, bias)
+    for name, kw in (("auto", {}), ("padded", dict(pad=(16, 32, 8)))):
+        log(f"f8 epilogue random {name}")
+        C, _ = run(A, B, None, epi=dict(e, C0=C0, bias=bias), **kw)
+        rep = oracle.check(C, ref, den, TOL)
+        log(f"  max_rel={rep['max_rel']:.3e}")
+        assert rep["ok"], (name, rep)
+
+
+# --- B given transposed ---------------------------------------------------------
+@pytest.mark.parametrize("shape", [(2, 16, 16), (127, 144, 80), (257, 128, 208), (65, 304, 512)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_f8_bt_exact_small_int(shape):
+    M, N, K = shape
+    A = synth.small_int(29, 0, M, K, dtype=F8)
+    Bt = synth.small_int(29, 1, N, K, dtype=F8)
+    ref, _ = oracle.gemm_rows_bt(A, Bt)
+    for cfg in gemm.configs(DT):
+        for pad in ((0, 0, 0), (16, 32, 8)):
+            log(f"f8 bt exact cfg={cfg.name.decode()} shape={shape} pad={pad}")
+            C, _ = run(A, Bt, cfg, pad=pad, bt=True)
+            assert np.array_equal(wide(C), rounded(ref, "bf16")), (cfg.name, pad)
+
+
+def test_f8_bt_full_size_sampled():
+    n = 4096
+    A, B = synth.workload(n, n, n, "f8", seed=5)
+    Bt = np.ascontiguousarray(B.T)
+    del B
+    log("f8 bt 4096^3")
+    C, _ = run(A, Bt, None, bt=True)
+    rows = np.array([0, 1, 255, 256, 2047, 4095])
+    ref, den = oracle.gemm_rows_bt(A, Bt, rows=rows)
+    rep = oracle.check(np.ascontiguousarray(C[rows]), ref, den, TOL)
+    log(f"  max_rel={rep['max_rel']:.3e}")
+    assert rep["ok"], rep
+
+
+def test_f8_matmul_torch():
+    import torch
+    A, B = synth.workload(200, 272, 144, "f8", seed=37)
+    ta = torch.from_numpy(A.view(np.uint8)).cuda().view(torch.float8_e4m3fn)
+    tb = torch.from_numpy(B.view(np.uint8)).cuda().view(torch.float8_e4m3fn)
+    log("matmul f8")
+    out = gemm.matmul(ta, tb)
+    torch.cuda.synchronize()
+    assert out.dtype == torch.bfloat16
+    C = out.view(torch.int16).cpu().numpy().view(np.uint16).view(synth.BF16)
+    ref, den = oracle.gemm_rows(A, B)
+    rep = oracle.check(C, ref, den, TOL)
+    assert rep["ok"], rep

@@ -32,7 +32,8 @@ def test_bad_arguments(lib):
         oracle.gemm_rows(A, B.astype(np.float16))
 
 
-@pytest.mark.parametrize("name,kind", [("f16_rne_halfway.txt", "f16"), ("bf16_rne_halfway.txt", "bf16")])
+@pytest.mark.parametrize("name,kind", [("f16_rne_halfway.txt", "f16"), ("bf16_rne_halfway.txt", "bf16"),
+                                       ("f8_bf16_rne_halfway.txt", "f8")])
 def test_rounding_probe_fixtures(lib, name, kind):
     """The hand-worked output-rounding fixtures: the oracle's exact sums of
     their A and B are the ties the headers describe, and the stored C
@@ -46,8 +47,9 @@ def test_rounding_probe_fixtures(lib, name, kind):
     g = {}
     for r in golden_data.rows(name):
         g.setdefault(r[0], []).append([int(x, 16) for x in r[2:]])
-    bits = {k: np.array(v, dtype=np.uint16) for k, v in g.items()}
-    view = np.float16 if kind == "f16" else synth.BF16
+    ins = np.uint8 if kind == "f8" else np.uint16
+    bits = {k: np.array(v, dtype=ins if k in "AB" else np.uint16) for k, v in g.items()}
+    view = {"f16": np.float16, "bf16": synth.BF16, "f8": synth.F8}[kind]
     C, _ = oracle.gemm_rows(bits["A"].view(view), bits["B"].view(view), lib=lib)
     c32 = C.astype(np.float32)
     assert np.array_equal(c32.astype(np.float64), C), "the sums are exact in FP32"
@@ -58,6 +60,7 @@ def test_rounding_probe_fixtures(lib, name, kind):
         rne = torch.from_numpy(c32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
         ulp = 2.0 ** -7
     assert np.array_equal(rne, bits["C"])
-    # Four of the six sums sit exactly halfway between neighbours on [1, 2).
+    # Four (FP8 probe: three) of the six sums sit exactly halfway between
+    # neighbours on [1, 2).
     frac = (C - 1.0) / ulp
-    assert np.sum(frac - np.floor(frac) == 0.5) == 4
+    assert np.sum(frac - np.floor(frac) == 0.5) == (3 if kind == "f8" else 4)
