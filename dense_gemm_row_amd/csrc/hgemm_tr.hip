@@ -130,10 +130,12 @@ struct Shape {
   static constexpr int EPI_ROW = WN * 2, EPI_SPR = WN / 4;
   static constexpr int P = (2 * NS) / NW, RPA = WM / P;
   static constexpr int EPI_CPR = WN / 8, EPI_RPI = 64 / EPI_CPR;  // store pass shape
-  static_assert(F8 ? BK == 128 : (BK == 32 || BK == 64), "K slice");
-  // Fragments alternate between two register sets by k step, and slice t+1's
-  // first step reuses set 0: an even number of k steps per slice.
-  static_assert(KS % 2 == 0, "k steps per slice");
+  static_assert(F8 ? (BK == 64 || BK == 128) : (BK == 32 || BK == 64), "K slice");
+  // Fragments alternate between two register sets by global k step
+  // (slice * KS + step); the slice loop is unrolled NS times, so the set of
+  // each step is static when NS * KS is even.
+  static_assert((NS * KS) % 2 == 0, "k steps per unrolled slice group");
+  __host__ __device__ static constexpr int frag_set(int stage, int j) { return (stage * KS + j) & 1; }
   static_assert(NS >= 2 && NS <= MAX_STAGES, "stages");
   static_assert(BM % WM == 0 && BN % WN == 0, "wave grid");
   static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile");
@@ -472,11 +474,11 @@ hgemm_tr_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
     unsigned char* cb = B_of(IC<c>{});
     static_for([&](auto J) __attribute__((always_inline)) {
       constexpr int j = decltype(J)::value;
-      load_frags((j + 1) & 1, ca, cb, j + 1);
+      load_frags(S::frag_set(c, j + 1), ca, cb, j + 1);
       // Spread: parts 1..KS-1 of slice t+NS-1 into stage f (free since the
       // last barrier), the PP copies evenly among the k step's MFMAs.
       if constexpr (S::SPREAD) issue_part(t + NS - 1, IC<j + 1>{}, A_of(IC<f>{}), B_of(IC<f>{}));
-      mma(j & 1);
+      mma(S::frag_set(c, j));
 #pragma unroll
       for (int i = 0; i < NMMA; ++i) {
         SGB(SG_MFMA, 1);
@@ -493,8 +495,8 @@ hgemm_tr_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
     // part 0, the rest during the next slice's k steps).
     if constexpr (S::SPREAD) issue_part(t + NS, IC<0>{}, ca, cb);
     else issue(t + NS, ca, cb);
-    load_frags(0, A_of(IC<n>{}), B_of(IC<n>{}), 0);
-    mma((KS - 1) & 1);
+    load_frags(S::frag_set(c + 1, 0), A_of(IC<n>{}), B_of(IC<n>{}), 0);
+    mma(S::frag_set(c, KS - 1));
 #pragma unroll
     for (int i = 0; i < NMMA; ++i) {
       SGB(SG_MFMA, 1);
@@ -938,6 +940,7 @@ const Variant kVariants[] = HGEMM_TR_TABLE(0, GEMM_DTYPE_F16, "f16");
 const Variant kVariantsBf[] = HGEMM_TR_TABLE(1, GEMM_DTYPE_BF16, "bf16");
 const Variant kVariantsF8[] = {
     HGEMM_TR_VARIANT(2, GEMM_DTYPE_F8, "f8", 256, 256, 128, 128, 128, 2, 1.00f),
+    HGEMM_TR_VARIANT(2, GEMM_DTYPE_F8, "f8", 256, 256, 128, 128, 64, 4, 0.85f),
     HGEMM_TR_VARIANT(2, GEMM_DTYPE_F8, "f8", 128, 256, 64, 128, 128, 3, 0.89f),
 };
 
