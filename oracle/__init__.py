@@ -18,6 +18,9 @@ marshals numpy arrays:
 * :func:`f16_to_f64` -- exact IEEE binary16 decoding.
 * :func:`bf16_to_f64` -- exact bfloat16 decoding.
 * :func:`e4m3_to_f64` -- exact FP8 E4M3 decoding.
+* :func:`quantize_i8` and :func:`q8_allowed` -- INT8 quantisation of epilogue
+  values (ties to even, saturating) and the codes a result within a given
+  error of the exact value may take.
 
 Element types: float32, float16 (or uint16 binary16 bit patterns),
 bfloat16 as uint16 bit patterns viewed with the marker dtype :data:`BF16`
@@ -82,6 +85,10 @@ def _declare(lib):
     lib.oracle_bf16_to_f64.restype = ctypes.c_double
     lib.oracle_bf16_array_to_f64.argtypes = [p, p, i64]
     lib.oracle_bf16_array_to_f64.restype = None
+    lib.oracle_quantize_i8.argtypes = [ctypes.c_double]
+    lib.oracle_quantize_i8.restype = ctypes.c_int
+    lib.oracle_quantize_i8_array.argtypes = [p, p, i64]
+    lib.oracle_quantize_i8_array.restype = None
     lib.oracle_e4m3_to_f64.argtypes = [ctypes.c_uint8]
     lib.oracle_e4m3_to_f64.restype = ctypes.c_double
     lib.oracle_e4m3_array_to_f64.argtypes = [p, p, i64]
@@ -386,3 +393,24 @@ def e4m3_to_f64(bits) -> np.ndarray:
     if b.size:
         lib.oracle_e4m3_array_to_f64(_ptr(b), _ptr(out), b.size)
     return out
+
+
+def quantize_i8(v) -> np.ndarray:
+    """INT8 codes of float64 values: nearest integer, ties to even,
+    saturated to [-128, 127] (oracle_quantize_i8)."""
+    lib = load()
+    v = np.ascontiguousarray(np.asarray(v, dtype=np.float64))
+    q = np.empty(v.shape, dtype=np.int8)
+    if v.size:
+        lib.oracle_quantize_i8_array(_ptr(v), _ptr(q), v.size)
+    return q
+
+
+def q8_allowed(v: np.ndarray, err: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """(lo, hi) int8 bounds of the codes that a computed value within
+    `err` of the exact epilogue value `v` may quantise to: quantisation is
+    monotone, so they are the codes of v - err and v + err.  A result is
+    valid when lo <= q <= hi (one code except near a rounding boundary)."""
+    v = np.asarray(v, dtype=np.float64)
+    err = np.asarray(err, dtype=np.float64)
+    return quantize_i8(v - err), quantize_i8(v + err)

@@ -430,6 +430,40 @@ int oracle_epilogue_rows_bf16(int64_t nrows, int64_t N, double alpha, double bet
 }
 
 /*
+ * INT8 quantisation of an epilogue value v (the output of the fused
+ * epilogue, whose alpha carries the quantisation scale): round to the
+ * nearest integer with ties to even, then saturate to [-128, 127].  The
+ * GB300 GEMM article (section 7.1) fuses this FP32-to-INT8 conversion with
+ * its scaling into the GEMM's epilogue.  The rounding is IEEE
+ * roundTiesToEven applied to an integer result; NaN maps to 0.
+ */
+int oracle_quantize_i8(double v)
+{
+    if (v != v)
+        return 0;
+    if (v >= 127.0)
+        return 127;
+    if (v <= -128.0)
+        return -128;
+    const double f = floor(v);
+    const double frac = v - f;
+    double r;
+    if (frac > 0.5)
+        r = f + 1.0;
+    else if (frac < 0.5)
+        r = f;
+    else
+        r = (fmod(f, 2.0) == 0.0) ? f : f + 1.0; /* tie: the even neighbour */
+    return (int)r;
+}
+
+void oracle_quantize_i8_array(const double *v, int8_t *q, int64_t n)
+{
+    for (int64_t t = 0; t < n; ++t)
+        q[t] = (int8_t)oracle_quantize_i8(v[t]);
+}
+
+/*
  * Single entries C_ref[ii[t]][jj[t]] and D[ii[t]][jj[t]], each one a plain
  * dot product over k ascending (the same order as the row routine).
  */

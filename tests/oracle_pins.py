@@ -440,12 +440,40 @@ def pin_bt_rank1(lib):
         assert not np.any(C2), "mismatched k"
 
 
+# --------------------------------------------------------------------------
+# INT8 quantisation of epilogue values: ties to even, saturating.
+# --------------------------------------------------------------------------
+def pin_quantize_i8(lib):
+    """Closed forms: integers map to themselves; x.5 goes to the even
+    neighbour in both signs (IEEE roundTiesToEven); other fractions to the
+    nearest; values past the range saturate to 127 / -128; and brute force
+    against exact rational rounding on a grid of quarters and near-ties."""
+    cases = {0.0: 0, -0.0: 0, 1.0: 1, -7.0: -7, 0.5: 0, 1.5: 2, 2.5: 2, -0.5: 0, -1.5: -2,
+             -2.5: -2, 126.5: 126, 127.5: 127, -127.5: -128, -128.5: -128, 0.49999: 0,
+             0.50001: 1, -0.50001: -1, 300.0: 127, -300.0: -128, 127.0: 127, -128.0: -128,
+             1e30: 127, -1e30: -128}
+    for v, want in cases.items():
+        got = lib.oracle_quantize_i8(v)
+        assert got == want, f"quantize({v}) = {got}, want {want}"
+    grid = np.arange(-600, 601) / 4.0  # quarters: many ties, both signs, saturation
+    grid = np.concatenate([grid, grid + 2.0 ** -20, grid - 2.0 ** -20])
+    q = np.empty(grid.shape, dtype=np.int8)
+    lib.oracle_quantize_i8_array(grid.ctypes.data, q.ctypes.data, grid.size)
+    for v, got in zip(grid.tolist(), q.tolist()):
+        x = Fraction(v)
+        f = x.numerator // x.denominator
+        frac = x - f
+        r = f + 1 if frac > Fraction(1, 2) else f if frac < Fraction(1, 2) else (f if f % 2 == 0 else f + 1)
+        r = max(-128, min(127, r))
+        assert got == r, f"quantize({v}) = {got}, want {r}"
+
+
 PINS = [pin_identity, pin_permutation, pin_all_ones, pin_rank1, pin_k0_k1,
         pin_bruteforce_fractions, pin_numpy_matmul, pin_f16_decode, pin_bf16_decode,
         pin_e4m3_decode,
         pin_error_metric, pin_epilogue_closed_form, pin_epilogue_reduces_to_plain,
         pin_epilogue_bruteforce, pin_bt_identity_permutation, pin_bt_matches_plain_transpose,
-        pin_bt_rank1]
+        pin_bt_rank1, pin_quantize_i8]
 
 
 def run_all(lib) -> list[str]:

@@ -55,6 +55,10 @@ MUTANTS = {
     "e4m3_all_top_exponent_nan": ("if (expo == 0xf && frac == 0x7)", "if (expo == 0xf)"),
     "e4m3_decoded_as_f16": ("    if (dtype == ORACLE_E4M3)\n        return oracle_e4m3_to_f64",
                             "    if (0)\n        return oracle_e4m3_to_f64"),
+    "q8_ties_up": ("r = (fmod(f, 2.0) == 0.0) ? f : f + 1.0;", "r = f + 1.0;"),
+    "q8_truncate": ("    else if (frac < 0.5)\n        r = f;", "    else if (frac < 0.999)\n        r = f;"),
+    "q8_no_low_saturation": ("    if (v <= -128.0)\n        return -128;", "    if (v <= -129.0)\n        return -129;"),
+    "q8_high_saturation_off_by_one": ("    if (v >= 127.0)\n        return 127;", "    if (v >= 127.0)\n        return 126;"),
     "entries_drop_k": ("for (int64_t k = 0; k < K; ++k) {",
                        "for (int64_t k = 0; k + 1 < K; ++k) {"),
     "metric_absolute": ("r = diff / den;", "r = diff;"),
