@@ -162,7 +162,7 @@ double gemm_seconds(int dtype, const Variant& v, int64_t M, int64_t N, int64_t K
 }
 
 Choice heuristic(int dtype, int64_t M, int64_t N, int64_t K, bool allow_split, bool need_epi = false,
-                 bool need_bt = false) {
+                 bool need_bt = false, bool need_q8 = false) {
   const auto& v = table().v[dtype];
   const double es = (double)out_bytes(dtype);
   Choice best;
@@ -170,6 +170,7 @@ Choice heuristic(int dtype, int64_t M, int64_t N, int64_t K, bool allow_split, b
     if (v[i].desc.family != GEMM_FAMILY_MFMA) continue;
     if (need_epi && !v[i].launch_epi) continue;
     if (need_bt && !v[i].launch_bt) continue;
+    if (need_q8 && !v[i].launch_q8) continue;
     const double t1 = gemm_seconds(dtype, v[i], M, N, K, 1);
     if (t1 < best.t) best = Choice{(int)i, 1, t1};
     if (!allow_split || !v[i].launch_partial || M == 0 || N == 0) continue;
@@ -189,12 +190,12 @@ Choice heuristic(int dtype, int64_t M, int64_t N, int64_t K, bool allow_split, b
 
 // Plain calls (split = false) never split; split-K calls may.
 gemm_config_t select(int dtype, int64_t M, int64_t N, int64_t K, bool split = false,
-                     bool need_epi = false, bool need_bt = false) {
+                     bool need_epi = false, bool need_bt = false, bool need_q8 = false) {
   {
     std::lock_guard<std::mutex> lk(g_tuning_mu);
     for (const auto& e : g_tuning)
       if (e.dtype == dtype && e.M == M && e.N == N && e.K == K && (split || e.splits <= 1) &&
-          (!need_epi || table().v[dtype][e.id].launch_epi) && !need_bt) {
+          (!need_epi || table().v[dtype][e.id].launch_epi) && !need_bt && !need_q8) {
         gemm_config_t d = table().v[dtype][e.id].desc;
         d.order = e.order;
         d.group_m = e.group_m;
@@ -202,7 +203,7 @@ gemm_config_t select(int dtype, int64_t M, int64_t N, int64_t K, bool split = fa
         return d;
       }
   }
-  const Choice c = heuristic(dtype, M, N, K, split, need_epi, need_bt);
+  const Choice c = heuristic(dtype, M, N, K, split, need_epi, need_bt, need_q8);
   gemm_config_t d = table().v[dtype][c.id].desc;
   d.splits = (int32_t)c.splits;
   return d;
@@ -230,8 +231,10 @@ size_t span_bytes(int64_t rows, int64_t cols, int64_t ld, size_t es) {
 }
 
 // bt: B is given transposed (Bt, N x K row-major, leading dimension ldb).
+// c_es: bytes of one C element when not the dtype's (INT8 codes: 1).
 gemm_status_t validate(int dtype, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
-                       const void* B, int64_t ldb, const void* C, int64_t ldc, bool bt = false) {
+                       const void* B, int64_t ldb, const void* C, int64_t ldc, bool bt = false,
+                       size_t c_es = 0) {
   if (M < 0 || N < 0 || K < 0) return fail(GEMM_ERR_INVALID_ARG, "negative dimension");
   const int64_t lim = 0x7fffffff;
   if (M > lim || N > lim || K > lim) return fail(GEMM_ERR_INVALID_ARG, "dimension above 2^31-1");
@@ -245,7 +248,7 @@ gemm_status_t validate(int dtype, int64_t M, int64_t N, int64_t K, const void* A
   const int64_t tiles_lim = 0x7fffffff;
   if (cdiv(M, 64) * cdiv(N, 64) > tiles_lim) return fail(GEMM_ERR_INVALID_ARG, "output too large");
   const size_t es = in_bytes(dtype);
-  const size_t cb = span_bytes(M, N, ldc, out_bytes(dtype));
+  const size_t cb = span_bytes(M, N, ldc, c_es ? c_es : out_bytes(dtype));
   if (overlap(C, cb, A, span_bytes(M, K, lda, es)) ||
       overlap(C, cb, B, bt ? span_bytes(N, K, ldb, es) : span_bytes(K, N, ldb, es)))
     return fail(GEMM_ERR_ALIAS, "C overlaps A or B");
@@ -257,10 +260,11 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 // Resolves the configuration of a call: the forced one (checked), or the
 // selection for the shape.
 gemm_status_t resolve(int dtype, int64_t M, int64_t N, int64_t K, const gemm_config_t* forced,
-                      bool split, gemm_config_t& cfg, bool need_epi = false, bool need_bt = false) {
+                      bool split, gemm_config_t& cfg, bool need_epi = false, bool need_bt = false,
+                      bool need_q8 = false) {
   const auto& v = table().v[dtype];
   if (!forced) {
-    cfg = select(dtype, M, N, K, split, need_epi, need_bt);
+    cfg = select(dtype, M, N, K, split, need_epi, need_bt, need_q8);
     return GEMM_OK;
   }
   if (forced->id < 0 || forced->id >= (int32_t)v.size())
@@ -274,6 +278,8 @@ gemm_status_t resolve(int dtype, int64_t M, int64_t N, int64_t K, const gemm_con
     return fail(GEMM_ERR_UNSUPPORTED, "variant %s has no fused-epilogue form", v[forced->id].desc.name);
   if (need_bt && !v[forced->id].launch_bt)
     return fail(GEMM_ERR_UNSUPPORTED, "variant %s has no transposed-B form", v[forced->id].desc.name);
+  if (need_q8 && !v[forced->id].launch_q8)
+    return fail(GEMM_ERR_UNSUPPORTED, "variant %s has no INT8-epilogue form", v[forced->id].desc.name);
   cfg = v[forced->id].desc;
   cfg.order = forced->order;
   cfg.group_m = forced->group_m;
@@ -300,8 +306,9 @@ gemm_status_t resolve(int dtype, int64_t M, int64_t N, int64_t K, const gemm_con
 }
 
 bool vector_path(int dtype, const void* A, int64_t lda, const void* B, int64_t ldb, const void* C,
-                 int64_t ldc, int64_t K, int64_t N) {
-  const int64_t w = 16 / (int64_t)in_bytes(dtype), wc = 16 / (int64_t)out_bytes(dtype);  // per 16 bytes
+                 int64_t ldc, int64_t K, int64_t N, size_t c_es = 0) {
+  const int64_t w = 16 / (int64_t)in_bytes(dtype);  // elements per 16 bytes
+  const int64_t wc = 16 / (int64_t)(c_es ? c_es : out_bytes(dtype));
   // FP8 with K = 0 reads neither A nor B (C = 0): only C's layout matters.
   if (dtype == GEMM_DTYPE_F8 && K == 0) return aligned16(C) && ldc % wc == 0 && N % wc == 0;
   return aligned16(A) && aligned16(B) && aligned16(C) && lda % w == 0 && ldb % w == 0 &&
@@ -408,6 +415,45 @@ gemm_status_t run_epi(int dtype, int64_t M, int64_t N, int64_t K, const void* A,
   const hipError_t e =
       table().v[dtype][cfg.id].launch_epi(p, map, vec, static_cast<hipStream_t>(stream));
   if (e == hipErrorNotSupported && dtype == GEMM_DTYPE_F8) return f8_unsupported();
+  if (e != hipSuccess) return fail(GEMM_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+  return GEMM_OK;
+}
+
+// INT8-quantising epilogue: Q = sat8(rne(act(alpha * A x B + bias))).
+gemm_status_t run_q8(int dtype, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                     const void* B, int64_t ldb, int8_t* Q, int64_t ldq, void* stream,
+                     const gemm_config_t* forced, const gemm_epilogue_t* epi) {
+  g_err[0] = 0;
+  gemm_status_t st = validate(dtype, M, N, K, A, lda, B, ldb, Q, ldq, false, 1);
+  if (st != GEMM_OK) return st;
+  if (!epi) return fail(GEMM_ERR_INVALID_ARG, "epi is NULL");
+  if (epi->act != GEMM_ACT_NONE && epi->act != GEMM_ACT_RELU)
+    return fail(GEMM_ERR_INVALID_ARG, "unknown activation %d", epi->act);
+  if (epi->beta != 0.f)
+    return fail(GEMM_ERR_INVALID_ARG, "the INT8 epilogue has no beta term (epi->beta must be 0)");
+  if (epi->bias && overlap(epi->bias, (size_t)N * 4, Q, span_bytes(M, N, ldq, 1)))
+    return fail(GEMM_ERR_ALIAS, "bias overlaps Q");
+  gemm_config_t cfg;
+  st = resolve(dtype, M, N, K, forced, false, cfg, false, false, true);
+  if (st != GEMM_OK) return st;
+  if (M == 0 || N == 0) return GEMM_OK;
+  Params p = make_params(dtype, A, lda, B, ldb, Q, ldq, M, N, K);
+  p.epi.on = true;
+  p.epi.alpha = epi->alpha;
+  p.epi.beta = 0.f;
+  p.epi.bias = epi->bias;
+  p.epi.act = epi->act;
+  const bool vec = vector_path(dtype, A, lda, B, ldb, Q, ldq, K, N, 1) &&
+                   (!epi->bias || aligned16(epi->bias));
+  auto unsupported = [] {
+    return fail(GEMM_ERR_UNSUPPORTED,
+                "the INT8 epilogue needs 16-byte aligned operands, Q and bias, K and N multiples "
+                "of 16 bytes of A and B elements, ldq a multiple of 16, and byte offsets below 2^31");
+  };
+  if (!vec) return unsupported();
+  const TileMap map = make_map(cfg, M, N);
+  const hipError_t e = table().v[dtype][cfg.id].launch_q8(p, map, vec, static_cast<hipStream_t>(stream));
+  if (e == hipErrorNotSupported) return unsupported();
   if (e != hipSuccess) return fail(GEMM_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
   return GEMM_OK;
 }
@@ -589,6 +635,30 @@ gemm_status_t gemm_f8_splitk(int64_t M, int64_t N, int64_t K, const gemm_f8_t* A
                              const gemm_config_t* cfg) {
   return run_splitk(GEMM_DTYPE_F8, M, N, K, A, lda, B, ldb, C, ldc, workspace, workspace_bytes,
                     stream, cfg);
+}
+
+gemm_status_t gemm_f32_epi_q8(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
+                              const float* B, int64_t ldb, int8_t* Q, int64_t ldq, void* stream,
+                              const gemm_config_t* cfg, const gemm_epilogue_t* epi) {
+  return run_q8(GEMM_DTYPE_F32, M, N, K, A, lda, B, ldb, Q, ldq, stream, cfg, epi);
+}
+
+gemm_status_t gemm_f16_epi_q8(int64_t M, int64_t N, int64_t K, const gemm_f16_t* A, int64_t lda,
+                              const gemm_f16_t* B, int64_t ldb, int8_t* Q, int64_t ldq,
+                              void* stream, const gemm_config_t* cfg, const gemm_epilogue_t* epi) {
+  return run_q8(GEMM_DTYPE_F16, M, N, K, A, lda, B, ldb, Q, ldq, stream, cfg, epi);
+}
+
+gemm_status_t gemm_bf16_epi_q8(int64_t M, int64_t N, int64_t K, const gemm_bf16_t* A, int64_t lda,
+                               const gemm_bf16_t* B, int64_t ldb, int8_t* Q, int64_t ldq,
+                               void* stream, const gemm_config_t* cfg, const gemm_epilogue_t* epi) {
+  return run_q8(GEMM_DTYPE_BF16, M, N, K, A, lda, B, ldb, Q, ldq, stream, cfg, epi);
+}
+
+gemm_status_t gemm_f8_epi_q8(int64_t M, int64_t N, int64_t K, const gemm_f8_t* A, int64_t lda,
+                             const gemm_f8_t* B, int64_t ldb, int8_t* Q, int64_t ldq, void* stream,
+                             const gemm_config_t* cfg, const gemm_epilogue_t* epi) {
+  return run_q8(GEMM_DTYPE_F8, M, N, K, A, lda, B, ldb, Q, ldq, stream, cfg, epi);
 }
 
 int64_t gemm_splitk_workspace_bytes(int32_t dtype, int64_t M, int64_t N, int64_t K, int32_t splits) {

@@ -26,6 +26,19 @@ struct Epi {
   int act = GEMM_ACT_NONE;
 };
 
+// INT8 code of a fused-epilogue value (the quantising epilogue: alpha
+// carries the scale): round to nearest with ties to even (v_rndne_f32) after
+// saturating to [-128, 127]; NaN gives 0.
+__device__ __forceinline__ int quantize_i8(float v) {
+  v = v == v ? v : 0.f;
+  return (int)__builtin_rintf(__builtin_fminf(__builtin_fmaxf(v, -128.f), 127.f));
+}
+
+// Four INT8 codes packed little-endian into one 32-bit word.
+__device__ __forceinline__ int pack_i8x4(int a, int b, int c, int d) {
+  return (a & 0xff) | ((b & 0xff) << 8) | ((c & 0xff) << 16) | (d << 24);
+}
+
 // One output of the fused epilogue: alpha*acc (+ beta*c_old when beta != 0)
 // (+ bias when there is one), then the activation; FP32 throughout.  The
 // caller reads c_old and bias only when they take part (C must not be read
@@ -219,6 +232,9 @@ struct Variant {
   // Launch with B given transposed (p.bt), or nullptr when the kernel has
   // no such form.
   LaunchFn launch_bt;
+  // Launch of the INT8-quantising fused epilogue (C holds int8 codes,
+  // p.epi.beta == 0), or nullptr when the kernel has no such form.
+  LaunchFn launch_q8;
 };
 
 // Per-family registration (each kernel file defines its table).

@@ -92,7 +92,7 @@ __device__ __forceinline__ void static_for(F&& f, std::integer_sequence<int, I..
 
 // MODE_: 0 the plain kernel; 1 the split-K form, whose epilogue writes FP32
 // partials; 2 the form with the fused epilogue (alpha, beta, bias,
-// activation).  BT_: B is given transposed (Bt, N x K row-major, i.e.
+// activation); 3 the fused epilogue writing INT8 codes (C is int8, beta 0).  BT_: B is given transposed (Bt, N x K row-major, i.e.
 // column-major B); its tile is then staged and read exactly like A's (one
 // LDS row per output column, k contiguous), with no transpose read.  TY_:
 // the element types, 0 binary16 in and out, 1 bfloat16 in and out, 2 FP8
@@ -101,7 +101,7 @@ template <int BM_, int BN_, int WM_, int WN_, int BK_, int NS_, int MODE_ = 0, b
           int TY_ = 0>
 struct Shape {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BK_, NS = NS_, TY = TY_;
-  static constexpr bool PARTIAL = MODE_ == 1, EPI = MODE_ == 2, BT = BT_;
+  static constexpr bool PARTIAL = MODE_ == 1, EPI = MODE_ == 2 || MODE_ == 3, Q8 = MODE_ == 3, BT = BT_;
   static constexpr bool BF = TY != 0;   // C (and the epilogue's old C) is bfloat16
   static constexpr bool F8 = TY == 2;   // A and B are FP8 E4M3
   static constexpr int ES = F8 ? 1 : 2;    // input element bytes
@@ -582,8 +582,10 @@ hgemm_tr_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
     typedef half_t<S::BF> H;
     typedef H h16x4 __attribute__((ext_vector_type(4)));
     typedef int v2i __attribute__((ext_vector_type(2)));
+    // C's element: 2 bytes (FP16 / BF16), or 1 (INT8 codes).
+    constexpr unsigned CB = S::Q8 ? 1u : 2u;
     const __amdgpu_buffer_rsrc_t rc =
-        make_rsrc(static_cast<const unsigned char*>(p.C), ((int64_t)(M - 1) * p.ldc + N) * 2);
+        make_rsrc(static_cast<const unsigned char*>(p.C), ((int64_t)(M - 1) * p.ldc + N) * CB);
     constexpr int R32 = S::R32, CPR32 = S::CPR32, RPI32 = S::RPI32;
     const int q = l % CPR32, col = n0 + wn0 + 4 * q;  // this lane's four columns
     f32x4 bias = {};
@@ -618,10 +620,10 @@ hgemm_tr_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
 #pragma unroll
         for (int i = 0; i < BATCH; ++i) {
           const int row = m0 + wm0 + pass * (WM / 2) + (b0 + i) * RPI32 + l / CPR32;
-          off[i] = (row < M) & (col < N) ? 2u * ((unsigned)row * (unsigned)p.ldc + (unsigned)col) : OOB;
+          off[i] = (row < M) & (col < N) ? CB * ((unsigned)row * (unsigned)p.ldc + (unsigned)col) : OOB;
           c_old[i] = v2i{0, 0};
         }
-        if (p.epi.beta != 0.f) {
+        if (!S::Q8 && p.epi.beta != 0.f) {
 #pragma unroll
           for (int i = 0; i < BATCH; ++i) c_old[i] = __builtin_amdgcn_raw_buffer_load_b64(rc, off[i], 0, 0);
         }
@@ -632,11 +634,19 @@ hgemm_tr_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
         }
 #pragma unroll
         for (int i = 0; i < BATCH; ++i) {
-          const h16x4 c = __builtin_bit_cast(h16x4, c_old[i]);
-          h16x4 h;
+          if constexpr (S::Q8) {
+            const int w = pack_i8x4(quantize_i8(epi_value(p.epi, v[i][0], 0.f, bias[0])),
+                                    quantize_i8(epi_value(p.epi, v[i][1], 0.f, bias[1])),
+                                    quantize_i8(epi_value(p.epi, v[i][2], 0.f, bias[2])),
+                                    quantize_i8(epi_value(p.epi, v[i][3], 0.f, bias[3])));
+            __builtin_amdgcn_raw_buffer_store_b32(w, rc, off[i], 0, 0);
+          } else {
+            const h16x4 c = __builtin_bit_cast(h16x4, c_old[i]);
+            h16x4 h;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) h[e] = (H)epi_value(p.epi, v[i][e], (float)c[e], bias[e]);
-          __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2i, h), rc, off[i], 0, 0);
+            for (int e = 0; e < 4; ++e) h[e] = (H)epi_value(p.epi, v[i][e], (float)c[e], bias[e]);
+            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2i, h), rc, off[i], 0, 0);
+          }
         }
       }
     }
@@ -688,8 +698,9 @@ hipError_t launch(const Params& p, const TileMap& map, bool vec, hipStream_t str
   if (!vec || (int64_t)(p.M + S::BM) * p.lda * ES > lim || b_far || (int64_t)p.M * p.lda * ES > lim ||
       (S::EPI && (int64_t)p.M * p.ldc * 2 > lim)) {
     // The general kernel has no split-K form (the caller runs unsplit) and
-    // no FP8 form (the caller reports the operands unsupported).
-    if (p.splits > 1 || S::F8) return hipErrorNotSupported;
+    // no FP8 or INT8-output form (the caller reports the operands
+    // unsupported).
+    if (p.splits > 1 || S::F8 || S::Q8) return hipErrorNotSupported;
     return hgemm_launch_shape(S::BM, S::BN, S::WM, S::WN, p, map, vec, stream);
   }
   const int64_t a_bytes = p.K > 0 ? ((int64_t)(p.M - 1) * p.lda + p.K) * ES : 0;
@@ -921,7 +932,8 @@ int layout_check(int banks, int64_t out[2]) {
         &layout_check<Shape<BM, BN, WM, WN, BK, NS, 0, false, TY>>,                          \
         &launch<Shape<BM, BN, WM, WN, BK, NS, 1, false, TY>>, EFF,                           \
         &launch<Shape<BM, BN, WM, WN, BK, NS, 2, false, TY>>,                                \
-        &launch<Shape<BM, BN, WM, WN, BK, NS, 0, true, TY>>                                  \
+        &launch<Shape<BM, BN, WM, WN, BK, NS, 0, true, TY>>,                                 \
+        &launch<Shape<BM, BN, WM, WN, BK, NS, 3, false, TY>>                                 \
   }
 
 // The 16-bit LDS layouts and data path do not depend on the element type,

@@ -65,10 +65,12 @@ __device__ __forceinline__ void static_for(F&& f, std::integer_sequence<int, I..
 // the columns of each wave block de-interleaved (LDS row wn0 + 32nb + j
 // holds column wn0 + NB*j + nb) so that a lane's 16-byte read gives four k
 // steps of its column and 16 lanes read 16 consecutive rows.
-template <int BM_, int BN_, int WM_, int WN_, int BK_, int NS_, bool EPI_ = false, bool BT_ = false>
+// Q8_: the fused epilogue writes INT8 codes (C is int8, beta is 0).
+template <int BM_, int BN_, int WM_, int WN_, int BK_, int NS_, bool EPI_ = false, bool BT_ = false,
+          bool Q8_ = false>
 struct Shape {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BK_, NS = NS_;
-  static constexpr bool EPI = EPI_, BT = BT_;
+  static constexpr bool EPI = EPI_ || Q8_, BT = BT_, Q8 = Q8_;
   static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN, NW = WAVES_M * WAVES_N;
   static constexpr int NT = NW * 64;
   static constexpr int MB = WM / 32, NB = WN / 32, KG = BK / 8;  // k groups of 8 per slice
@@ -400,6 +402,35 @@ sgemm_dl_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
         const int row = row_of(mb, r);
         if (row < M && col < N) *reinterpret_cast<vecNB*>(C + (int64_t)row * p.ldc + col) = acc_vec(mb, r);
       }
+  } else if constexpr (S::Q8) {
+    // INT8-quantising epilogue: the lane's NB adjacent columns of a row
+    // become NB bytes, stored branch-free through a byte-addressed buffer
+    // descriptor over C (out-of-range elements: an offset past its range).
+    const __amdgpu_buffer_rsrc_t rq =
+        make_rsrc(reinterpret_cast<const unsigned char*>(p.C), (int64_t)(M - 1) * p.ldc + N);
+    vecNB bias = {};
+    if (p.epi.bias && col < N) bias = *reinterpret_cast<const vecNB*>(p.epi.bias + col);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = row_of(mb, r);
+        const unsigned off = (row < M) & (col < N) ? (unsigned)row * (unsigned)p.ldc + (unsigned)col : OOB;
+        const vecNB v = acc_vec(mb, r);
+        if constexpr (NB == 4) {
+          const int w = pack_i8x4(quantize_i8(epi_value(p.epi, v[0], 0.f, bias[0])),
+                                  quantize_i8(epi_value(p.epi, v[1], 0.f, bias[1])),
+                                  quantize_i8(epi_value(p.epi, v[2], 0.f, bias[2])),
+                                  quantize_i8(epi_value(p.epi, v[3], 0.f, bias[3])));
+          __builtin_amdgcn_raw_buffer_store_b32(w, rq, off, 0, 0);
+        } else if constexpr (NB == 2) {
+          const int w = (quantize_i8(epi_value(p.epi, v[0], 0.f, bias[0])) & 0xff) |
+                        (quantize_i8(epi_value(p.epi, v[1], 0.f, bias[1])) << 8);
+          __builtin_amdgcn_raw_buffer_store_b16((short)w, rq, off, 0, 0);
+        } else {
+          __builtin_amdgcn_raw_buffer_store_b8((char)quantize_i8(epi_value(p.epi, v, 0.f, bias)), rq, off, 0, 0);
+        }
+      }
   } else {
     // Fused epilogue on the FP32 accumulators.  The bias of the lane's
     // columns is loaded once; the old C (read only when beta != 0) is
@@ -464,8 +495,9 @@ hipError_t launch(const Params& p, const TileMap& map, bool vec, hipStream_t str
       (S::BT ? (int64_t)(p.N + S::BN) * p.ldb * 4 > lim
              : ((int64_t)(p.K > 0 ? p.K - 1 : 0) * p.ldb + p.N) * 4 > lim) ||
       (S::EPI && (int64_t)p.M * p.ldc * 4 > lim)) {
-    // The general kernel has no split-K form: the caller runs unsplit.
-    if (p.splits > 1) return hipErrorNotSupported;
+    // The general kernel has no split-K form (the caller runs unsplit) and
+    // no INT8 form (the caller reports the operands unsupported).
+    if (p.splits > 1 || S::Q8) return hipErrorNotSupported;
     return sgemm_launch_shape(S::BM, S::BN, S::WM, S::WN, p, map, vec, stream);
   }
   const int64_t a_bytes = p.K > 0 ? ((int64_t)(p.M - 1) * p.lda + p.K) * 4 : 0;
@@ -607,7 +639,8 @@ int layout_check(int banks, int64_t out[2]) {
         &launch<Shape<BM, BN, WM, WN, BK, NS>>, &layout_check<Shape<BM, BN, WM, WN, BK, NS>>, \
         &launch<Shape<BM, BN, WM, WN, BK, NS>>, EFF,                                        \
         &launch<Shape<BM, BN, WM, WN, BK, NS, true>>,                                       \
-        &launch<Shape<BM, BN, WM, WN, BK, NS, false, true>>                                 \
+        &launch<Shape<BM, BN, WM, WN, BK, NS, false, true>>,                                \
+        &launch<Shape<BM, BN, WM, WN, BK, NS, false, false, true>>                          \
   }
 
 const Variant kVariants[] = {

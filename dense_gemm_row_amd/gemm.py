@@ -39,7 +39,8 @@ ACT_NONE = 0
 ACT_RELU = 1
 
 TYPES = ("f32", "f16", "bf16", "f8")
-EXPORTS = [f"gemm_{t}{form}" for form in ("", "_ex", "_bt", "_epi", "_splitk") for t in TYPES] + [
+EXPORTS = [f"gemm_{t}{form}" for form in ("", "_ex", "_bt", "_epi", "_epi_q8", "_splitk")
+           for t in TYPES] + [
            "gemm_splitk_workspace_bytes", "gemm_select_splitk_config",
            "gemm_num_configs", "gemm_get_config", "gemm_select_config", "gemm_tile_of_block",
            "gemm_layout_check", "gemm_load_tuning", "gemm_status_string",
@@ -92,7 +93,7 @@ def _declare(lib):
     for name in [f"gemm_{t}_ex" for t in types] + [f"gemm_{t}_bt" for t in types]:
         getattr(lib, name).argtypes = gemm_args + [cfgp]
         getattr(lib, name).restype = ctypes.c_int
-    for name in (f"gemm_{t}_epi" for t in types):
+    for name in [f"gemm_{t}_epi" for t in types] + [f"gemm_{t}_epi_q8" for t in types]:
         getattr(lib, name).argtypes = gemm_args + [cfgp, ctypes.POINTER(GemmEpilogue)]
         getattr(lib, name).restype = ctypes.c_int
     for name in (f"gemm_{t}_splitk" for t in types):
@@ -248,10 +249,27 @@ def gemm_f8_splitk(M, N, K, A, lda, B, ldb, C, ldc, workspace, workspace_bytes, 
                                 stream, ctypes.byref(cfg) if cfg is not None else None)
 
 
+def _q8(name):
+    def fn(M, N, K, A, lda, B, ldb, Q, ldq, stream, cfg: GemmConfig | None,
+           epi: GemmEpilogue | None) -> int:
+        return getattr(lib(), name)(M, N, K, A, lda, B, ldb, Q, ldq, stream,
+                                    ctypes.byref(cfg) if cfg is not None else None,
+                                    ctypes.byref(epi) if epi is not None else None)
+    fn.__name__ = name
+    return fn
+
+
+# The INT8-quantising epilogue: Q = sat8(rne(act(alpha * A x B + bias))).
+gemm_f32_epi_q8 = _q8("gemm_f32_epi_q8")
+gemm_f16_epi_q8 = _q8("gemm_f16_epi_q8")
+gemm_bf16_epi_q8 = _q8("gemm_bf16_epi_q8")
+gemm_f8_epi_q8 = _q8("gemm_f8_epi_q8")
+
+
 # Entry points per dtype code, for callers that dispatch on it.
 def entry(dtype: int, form: str = ""):
     """The binding of gemm_<type><form> (form "", "_ex", "_bt", "_epi",
-    "_splitk") for dtype DTYPE_F32 / DTYPE_F16 / DTYPE_BF16 / DTYPE_F8."""
+    "_epi_q8", "_splitk") for dtype DTYPE_F32 / DTYPE_F16 / DTYPE_BF16 / DTYPE_F8."""
     name = {DTYPE_F32: "f32", DTYPE_F16: "f16", DTYPE_BF16: "bf16", DTYPE_F8: "f8"}[dtype]
     return globals()[f"gemm_{name}{form}"]
 

@@ -330,6 +330,45 @@ gemm_status_t gemm_f8_epi(int64_t M, int64_t N, int64_t K,
                           gemm_bf16_t *C, int64_t ldc, void *stream,
                           const gemm_config_t *cfg, const gemm_epilogue_t *epi);
 
+/*
+ * GEMM with the INT8-quantising epilogue: the fused epilogue's value,
+ * computed in FP32 from the accumulator, is rounded to the nearest integer
+ * (ties to even) and saturated to [-128, 127]:
+ *     Q[i][j] = sat8(rne(act(alpha * (A x B)[i][j] + bias[j])))
+ * so the FP32 result becomes INT8 with its scaling inside the GEMM instead
+ * of a separate quantisation pass over C (the epilogue fusion of the GB300
+ * GEMM article, section 7.1).  alpha is the per-tensor quantisation scale
+ * (1 / step); epi->beta must be 0 (an INT8 old C has no meaning here:
+ * INVALID_ARG otherwise).  Q is M x N int8, row-major, leading dimension ldq
+ * (>= max(1, N)); its columns [N, ldq) are never written; it must not
+ * overlap A, B or the bias (-> ALIAS).  A NaN value gives 0.
+ * Supported on the vector layout only: A, B, Q and bias 16-byte aligned, K,
+ * N, lda, ldb multiples of 16 bytes' worth of A/B elements, ldq a multiple
+ * of 16 (else UNSUPPORTED before any launch).  cfg NULL: the selection
+ * among the variants with an INT8 form; a forced variant without one ->
+ * UNSUPPORTED.
+ */
+gemm_status_t gemm_f32_epi_q8(int64_t M, int64_t N, int64_t K,
+                              const float *A, int64_t lda,
+                              const float *B, int64_t ldb,
+                              int8_t *Q, int64_t ldq, void *stream,
+                              const gemm_config_t *cfg, const gemm_epilogue_t *epi);
+gemm_status_t gemm_f16_epi_q8(int64_t M, int64_t N, int64_t K,
+                              const gemm_f16_t *A, int64_t lda,
+                              const gemm_f16_t *B, int64_t ldb,
+                              int8_t *Q, int64_t ldq, void *stream,
+                              const gemm_config_t *cfg, const gemm_epilogue_t *epi);
+gemm_status_t gemm_bf16_epi_q8(int64_t M, int64_t N, int64_t K,
+                               const gemm_bf16_t *A, int64_t lda,
+                               const gemm_bf16_t *B, int64_t ldb,
+                               int8_t *Q, int64_t ldq, void *stream,
+                               const gemm_config_t *cfg, const gemm_epilogue_t *epi);
+gemm_status_t gemm_f8_epi_q8(int64_t M, int64_t N, int64_t K,
+                             const gemm_f8_t *A, int64_t lda,
+                             const gemm_f8_t *B, int64_t ldb,
+                             int8_t *Q, int64_t ldq, void *stream,
+                             const gemm_config_t *cfg, const gemm_epilogue_t *epi);
+
 /* Variant table: count per dtype, and the description of variant idx. */
 int32_t gemm_num_configs(int32_t dtype);
 gemm_status_t gemm_get_config(int32_t dtype, int32_t idx, gemm_config_t *out);

@@ -20,11 +20,12 @@ CANARY_F32 = np.uint32(0x7FC0DEAD)  # a quiet NaN payload nobody computes
 CANARY_F16 = np.uint16(0x7E5A)
 CANARY_BF16 = np.uint16(0x7FDA)
 CANARY_F8 = np.uint8(0x7F)  # the E4M3 NaN
-CANARY = {"f32": CANARY_F32, "f16": CANARY_F16, "bf16": CANARY_BF16, "f8": CANARY_F8}
+CANARY_I8 = np.uint8(0x5A)  # INT8 outputs: any byte is a code, so this marks only the padding
+CANARY = {"f32": CANARY_F32, "f16": CANARY_F16, "bf16": CANARY_BF16, "f8": CANARY_F8, "i8": CANARY_I8}
 DTYPE = {"f32": gemm.DTYPE_F32, "f16": gemm.DTYPE_F16, "bf16": gemm.DTYPE_BF16, "f8": gemm.DTYPE_F8}
-VIEW = {"f32": np.float32, "f16": np.float16, "bf16": synth.BF16, "f8": synth.F8}
-BITS = {"f32": np.uint32, "f16": np.uint16, "bf16": np.uint16, "f8": np.uint8}
-TORCH_BITS = {"f32": np.int32, "f16": np.int16, "bf16": np.int16, "f8": np.int8}
+VIEW = {"f32": np.float32, "f16": np.float16, "bf16": synth.BF16, "f8": synth.F8, "i8": np.int8}
+BITS = {"f32": np.uint32, "f16": np.uint16, "bf16": np.uint16, "f8": np.uint8, "i8": np.uint8}
+TORCH_BITS = {"f32": np.int32, "f16": np.int16, "bf16": np.int16, "f8": np.int8, "i8": np.int8}
 
 
 def kind_of(a: np.ndarray) -> str:
@@ -168,6 +169,31 @@ def run(A: np.ndarray, B: np.ndarray, cfg=None, pad=(0, 0, 0), offset=(0, 0, 0),
         assert np.all(w[:WS_GUARD] == CANARY_F32) and np.all(w[len(w) - WS_GUARD:] == CANARY_F32), \
             "split-K wrote outside its workspace"
     return dC.matrix(flat), dC
+
+
+def run_q8(A: np.ndarray, B: np.ndarray, cfg, epi: dict, pad=(0, 0, 0), offset=(0, 0, 0)):
+    """The INT8-quantising epilogue (gemm_*_epi_q8) through libgemm: returns
+    Q (int8 numpy) after checking that nothing outside Q[0:M, 0:N] changed.
+    epi: alpha, bias (float32 array of N, or None), act."""
+    kind = kind_of(A)
+    M, K = A.shape
+    N = B.shape[1]
+    dA = DevMatrix(A, M, K, kind, pad=pad[0], offset=offset[0])
+    dB = DevMatrix(B, K, N, kind, pad=pad[1], offset=offset[1])
+    dQ = DevMatrix(None, M, N, "i8", pad=pad[2], offset=offset[2])
+    bias = epi.get("bias")
+    bias_dev = torch.from_numpy(np.asarray(bias, np.float32)).to("cuda") if bias is not None else None
+    e = gemm.GemmEpilogue(float(epi.get("alpha", 1.0)), 0.0,
+                          bias_dev.data_ptr() if bias_dev is not None else None, int(epi.get("act", 0)))
+    stream = torch.cuda.current_stream().cuda_stream
+    st = gemm.entry(DTYPE[kind], "_epi_q8")(M, N, K, dA.ptr, dA.ld, dB.ptr, dB.ld, dQ.ptr, dQ.ld,
+                                             stream, cfg, e)
+    if st != gemm.GEMM_OK:
+        raise gemm.GemmError(st, "gemm_epi_q8")
+    torch.cuda.synchronize()
+    flat = dQ.fetch()
+    assert dQ.untouched_outside(flat), "kernel wrote outside Q[0:M, 0:N]"
+    return dQ.matrix(flat)
 
 
 def tol_for(kind: str) -> float:

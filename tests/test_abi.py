@@ -340,3 +340,25 @@ def test_f8_table_and_validation():
     assert f(0, 64, 64, PA, 64, PB, 64, PA + 64 * 64, 64) == gemm.GEMM_OK
     assert f(64, 64, 64, PA, 64, PB, 64, PB + 63 * 64, 64) == gemm.GEMM_ERR_ALIAS
     assert gemm.gemm_splitk_workspace_bytes(gemm.DTYPE_F8, 10, 20, 1000, 3) == 3 * 10 * 20 * 4
+
+
+@pytest.mark.parametrize("fn", [gemm.gemm_f32_epi_q8, gemm.gemm_f16_epi_q8, gemm.gemm_bf16_epi_q8,
+                                gemm.gemm_f8_epi_q8])
+def test_q8_argument_validation(fn):
+    """The INT8 epilogue: beta must be 0, the activation known, the bias not
+    overlapping Q (1-byte elements), variants without an INT8 form refused
+    when forced, and operands off the vector layout refused, all before
+    any launch."""
+    dt = _dtype_of(fn)
+    base = (64, 64, 64, PA, 64, PB, 64, PC, 64, None)
+    ok = gemm.GemmEpilogue(1.0, 0.0, None, gemm.ACT_NONE)
+    assert fn(*base, None, None) == gemm.GEMM_ERR_INVALID_ARG
+    assert fn(*base, None, gemm.GemmEpilogue(1.0, 0.5, None, 0)) == gemm.GEMM_ERR_INVALID_ARG
+    assert "beta" in gemm.gemm_last_error()
+    assert fn(*base, None, gemm.GemmEpilogue(1.0, 0.0, None, 9)) == gemm.GEMM_ERR_INVALID_ARG
+    assert fn(*base, None, gemm.GemmEpilogue(1.0, 0.0, PC + 63 * 64 + 60, 0)) == gemm.GEMM_ERR_ALIAS
+    for c in gemm.configs(dt):
+        if not c.name.decode().startswith(("dl_", "tr_")):
+            assert fn(*base[:-1], None, c, ok) == gemm.GEMM_ERR_UNSUPPORTED, c.name
+    assert fn(64, 64, 64, PA, 64, PB, 64, PC, 72, None, None, ok) == gemm.GEMM_ERR_UNSUPPORTED  # ldq % 16
+    assert fn(0, 64, 64, PA, 64, PB, 64, 0, 64, None, None, ok) == gemm.GEMM_OK
