@@ -450,3 +450,43 @@ def test_matmul_b_transposed():
     ref, den = oracle.gemm_rows_bt(A, np.ascontiguousarray(B.T))
     rep = oracle.check(out.cpu().numpy(), ref, den, oracle.SGEMM_TOL)
     assert rep["ok"], rep
+
+
+# --- very large leading dimensions (byte offsets past 2^31) -----------------------
+@pytest.mark.parametrize("kind", ["f32", "f16", "bf16", "f8"])
+def test_offsets_past_31_bits(kind):
+    """A with a row stride that puts its last rows more than 2^31 bytes from
+    its base: the LDS-direct kernels' 32-bit buffer offsets cannot reach
+    them, so FP32/FP16/BF16 take the general kernels (64-bit addressing)
+    with the same results, and FP8 (no general kernel) is refused with
+    UNSUPPORTED.  The operands are built on the device (A is ~4.3 GiB of
+    memory, of which only M x K elements are read)."""
+    import torch
+    dt = {"f32": np.float32, "f16": np.float16, "bf16": synth.BF16, "f8": synth.F8}[kind]
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.int16, "f8": torch.uint8}[kind]
+    es = {"f32": 4, "f16": 2, "bf16": 2, "f8": 1}[kind]
+    M, N, K = 130, 272, 96
+    lda = (2 ** 31 // es) // (M - 1) + 4096  # (M-1) * lda * es > 2^31
+    lda -= lda % 16
+    A = synth.small_int(61, 0, M, K, dtype=dt)
+    B = synth.small_int(61, 1, K, N, dtype=dt)
+    host_bits = {"f32": np.float32, "f16": np.float16, "bf16": np.int16, "f8": np.uint8}[kind]
+    a_big = torch.empty((M, lda), dtype=tdt, device="cuda")
+    a_big[:, :K] = torch.from_numpy(np.ascontiguousarray(A).view(host_bits)).cuda()
+    b = torch.from_numpy(np.ascontiguousarray(B).view(host_bits)).cuda()
+    c_dt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.int16, "f8": torch.int16}[kind]
+    c = torch.zeros((M, N), dtype=c_dt, device="cuda")
+    dtype = {"f32": gemm.DTYPE_F32, "f16": gemm.DTYPE_F16, "bf16": gemm.DTYPE_BF16,
+             "f8": gemm.DTYPE_F8}[kind]
+    stream = torch.cuda.current_stream().cuda_stream
+    log(f"{kind} lda={lda} ({(M - 1) * lda * es / 2**30:.2f} GiB to the last row)")
+    st = gemm.entry(dtype)(M, N, K, a_big.data_ptr(), lda, b.data_ptr(), N, c.data_ptr(), N, stream)
+    torch.cuda.synchronize()
+    if kind == "f8":
+        assert st == gemm.GEMM_ERR_UNSUPPORTED
+        return
+    assert st == gemm.GEMM_OK, gemm.gemm_last_error()
+    out = c.cpu().numpy()
+    out = out.view(np.uint16).view(synth.BF16) if kind == "bf16" else out
+    assert exact_equal(A, B, out)
+    del a_big
