@@ -108,6 +108,11 @@ def _declare(lib):
         fn = getattr(lib, name)
         fn.argtypes = [i64, i64, i64, p, i64, p, i64, p, p, i64, p, i64]
         fn.restype = ctypes.c_int
+    for name in ("oracle_gemm_rows_trans_f32", "oracle_gemm_rows_trans_f16",
+                 "oracle_gemm_rows_trans_bf16", "oracle_gemm_rows_trans_f8"):
+        fn = getattr(lib, name)
+        fn.argtypes = [i64, i64, i64, p, i64, p, i64, ctypes.c_int, ctypes.c_int, p, p, i64, p, i64]
+        fn.restype = ctypes.c_int
     for name in ("oracle_epilogue_rows_f32", "oracle_epilogue_rows_f16",
                  "oracle_epilogue_rows_bf16"):
         fn = getattr(lib, name)
@@ -262,6 +267,44 @@ def gemm_rows_bt(A: np.ndarray, Bt: np.ndarray, rows=None, lib=None):
     rc = fn(nrows, N, K, a_ptr, lda, b_ptr, ldbt, rp, _ptr(C), N, _ptr(D), N)
     if rc != 0:
         raise RuntimeError(f"oracle_gemm_rows_bt failed with code {rc}")
+    return C, D
+
+
+def gemm_rows_trans(A: np.ndarray, B: np.ndarray, trans_a: bool, trans_b: bool, rows=None,
+                    lib=None):
+    """C_ref and D (float64) for C = op(A) @ op(B), op(X) = X.T when its
+    flag is set: A is M x K (or K x M with trans_a), B is K x N (or N x K
+    with trans_b).  Single-threaded (test sizes only)."""
+    lib = lib or load()
+    kind = _kind(A)
+    if _kind(B) != kind:
+        raise TypeError("A and B must have the same element type")
+    A, dt = _raw(A, kind)
+    B, _ = _raw(B, kind)
+    A, lda = _as_matrix(A, dt)
+    B, ldb = _as_matrix(B, dt)
+    M, K = (A.shape[1], A.shape[0]) if trans_a else A.shape
+    K2, N = (B.shape[1], B.shape[0]) if trans_b else B.shape
+    if K2 != K:
+        raise ValueError(f"inner dimensions differ: {K} vs {K2}")
+    if rows is None:
+        nrows, rp = M, None
+    else:
+        rows_arr = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        if rows_arr.size and (rows_arr.min() < 0 or rows_arr.max() >= M):
+            raise IndexError("row index out of range")
+        nrows, rp = rows_arr.size, _ptr(rows_arr)
+    C = np.zeros((nrows, N), dtype=np.float64)
+    D = np.zeros((nrows, N), dtype=np.float64)
+    if nrows == 0 or N == 0:
+        return C, D
+    a_ptr = _ptr(A) if A.size else _ptr(np.zeros(1, dt))
+    b_ptr = _ptr(B) if B.size else _ptr(np.zeros(1, dt))
+    rc = getattr(lib, f"oracle_gemm_rows_trans_{kind}")(nrows, N, K, a_ptr, lda, b_ptr, ldb,
+                                                        int(bool(trans_a)), int(bool(trans_b)),
+                                                        rp, _ptr(C), N, _ptr(D), N)
+    if rc != 0:
+        raise RuntimeError(f"oracle_gemm_rows_trans failed with code {rc}")
     return C, D
 
 

@@ -361,6 +361,54 @@ int oracle_gemm_rows_bt_f8(int64_t nrows, int64_t N, int64_t K, const uint8_t *A
 }
 
 /*
+ * Rows of C_ref and D with either operand given transposed, the four BLAS
+ * layouts: A element (i, k) is A[i*lda + k], or A[k*lda + i] when trans_a
+ * (A passed as its K x M transpose, i.e. column-major A); B element (k, j)
+ * is B[k*ldb + j], or B[j*ldb + k] when trans_b (column-major B, the layout
+ * of the lqnn.cn SGEMM article's baseline, section 3.1).  Same i-k-j order
+ * (k ascending) as oracle_gemm_rows_*.  Single-threaded (test sizes).
+ */
+static int run_rows_trans(int dtype, int64_t nrows, int64_t N, int64_t K, const void *A,
+                          int64_t lda, const void *B, int64_t ldb, int trans_a, int trans_b,
+                          const int64_t *rows, double *C, int64_t ldr, double *D, int64_t ldd)
+{
+    if (nrows < 0 || N < 0 || K < 0 || ldr < N || ldd < N)
+        return -1;
+    for (int64_t t = 0; t < nrows; ++t) {
+        const int64_t i = rows ? rows[t] : t;
+        double *acc = C + t * ldr;
+        double *den = D + t * ldd;
+        for (int64_t j = 0; j < N; ++j) {
+            acc[j] = 0.0;
+            den[j] = 0.0;
+        }
+        for (int64_t k = 0; k < K; ++k) {
+            const double a = load_elem(A, dtype, trans_a ? k * lda + i : i * lda + k);
+            for (int64_t j = 0; j < N; ++j) {
+                const double b = load_elem(B, dtype, trans_b ? j * ldb + k : k * ldb + j);
+                acc[j] += a * b;
+                den[j] += fabs(a) * fabs(b);
+            }
+        }
+    }
+    return 0;
+}
+
+#define ORACLE_TRANS(SUFFIX, DT, T)                                                            \
+    int oracle_gemm_rows_trans_##SUFFIX(int64_t nrows, int64_t N, int64_t K, const T *A,      \
+                                        int64_t lda, const T *B, int64_t ldb, int trans_a,    \
+                                        int trans_b, const int64_t *rows, double *C,          \
+                                        int64_t ldr, double *D, int64_t ldd)                  \
+    {                                                                                         \
+        return run_rows_trans(DT, nrows, N, K, A, lda, B, ldb, trans_a, trans_b, rows, C,     \
+                              ldr, D, ldd);                                                   \
+    }
+ORACLE_TRANS(f32, ORACLE_F32, float)
+ORACLE_TRANS(f16, ORACLE_F16, uint16_t)
+ORACLE_TRANS(bf16, ORACLE_BF16, uint16_t)
+ORACLE_TRANS(f8, ORACLE_E4M3, uint8_t)
+
+/*
  * Fused epilogue, applied to rows of C_ref and D produced by
  * oracle_gemm_rows_* (in place):
  *   C[t][j] <- act(alpha * C[t][j] + beta * C0[i][j] + bias[j])

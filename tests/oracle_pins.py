@@ -441,6 +441,50 @@ def pin_bt_rank1(lib):
 
 
 # --------------------------------------------------------------------------
+# Either operand transposed: C = op(A) @ op(B).
+# --------------------------------------------------------------------------
+def pin_trans_matches_materialised(lib):
+    """Each of the four layouts equals the plain product of the
+    materialised operands bit for bit (same k order), with padded leading
+    dimensions and a row subset; the transposed-B case also equals the
+    dedicated transposed-B routine."""
+    for dt in _dtypes():
+        A, B = _rand(dt, 71, 0, 11, 37), _rand(dt, 71, 1, 37, 13)
+        rows = [10, 0, 4]
+        Cp, Dp = oracle.gemm_rows(A, B, rows=rows, lib=lib)
+        for ta in (False, True):
+            for tb in (False, True):
+                a = _padded(np.ascontiguousarray(A.T), 3) if ta else _padded(A, 2)
+                b = _padded(np.ascontiguousarray(B.T), 5) if tb else _padded(B, 1)
+                C, D = oracle.gemm_rows_trans(a, b, ta, tb, rows=rows, lib=lib)
+                assert np.array_equal(C, Cp) and np.array_equal(D, Dp), f"trans {ta}{tb}"
+        Cb, _ = oracle.gemm_rows_bt(A, np.ascontiguousarray(B.T), rows=rows, lib=lib)
+        assert np.array_equal(Cb, Cp), "trans vs bt routine"
+
+
+def pin_trans_identity_rank1(lib):
+    """A^T = I gives C = B; with A^T holding one nonzero row c (A's column
+    c) and B^T one nonzero column c (B's row c), C = u v^T; a mismatched k
+    gives 0."""
+    for dt in _dtypes():
+        B = _rand(dt, 72, 1, 9, 6)
+        C, _ = oracle.gemm_rows_trans(_make(np.eye(9), dt), B, True, False, lib=lib)
+        assert np.array_equal(C, _wide(B)), "A^T = I"
+        M, N, K = 5, 6, 8
+        u = synth.small_int(73, 0, M, 1, -3, 3).ravel()
+        v = synth.small_int(73, 1, N, 1, -3, 3).ravel()
+        At, Bt = np.zeros((K, M)), np.zeros((N, K))
+        At[2, :] = u
+        Bt[:, 2] = v
+        C, _ = oracle.gemm_rows_trans(_make(At, dt), _make(Bt, dt), True, True, lib=lib)
+        assert np.array_equal(C, np.outer(u, v)), "rank-1 TT"
+        Bt2 = np.zeros((N, K))
+        Bt2[:, 3] = v
+        C2, _ = oracle.gemm_rows_trans(_make(At, dt), _make(Bt2, dt), True, True, lib=lib)
+        assert not np.any(C2), "mismatched k"
+
+
+# --------------------------------------------------------------------------
 # INT8 quantisation of epilogue values: ties to even, saturating.
 # --------------------------------------------------------------------------
 def pin_quantize_i8(lib):
@@ -473,7 +517,7 @@ PINS = [pin_identity, pin_permutation, pin_all_ones, pin_rank1, pin_k0_k1,
         pin_e4m3_decode,
         pin_error_metric, pin_epilogue_closed_form, pin_epilogue_reduces_to_plain,
         pin_epilogue_bruteforce, pin_bt_identity_permutation, pin_bt_matches_plain_transpose,
-        pin_bt_rank1, pin_quantize_i8]
+        pin_bt_rank1, pin_trans_matches_materialised, pin_trans_identity_rank1, pin_quantize_i8]
 
 
 def run_all(lib) -> list[str]:

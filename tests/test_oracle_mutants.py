@@ -59,6 +59,12 @@ MUTANTS = {
     "q8_truncate": ("    else if (frac < 0.5)\n        r = f;", "    else if (frac < 0.999)\n        r = f;"),
     "q8_no_low_saturation": ("    if (v <= -128.0)\n        return -128;", "    if (v <= -129.0)\n        return -129;"),
     "q8_high_saturation_off_by_one": ("    if (v >= 127.0)\n        return 127;", "    if (v >= 127.0)\n        return 126;"),
+    "trans_a_ignored": ("load_elem(A, dtype, trans_a ? k * lda + i : i * lda + k)",
+                        "load_elem(A, dtype, i * lda + k)"),
+    "trans_a_swapped_index": ("load_elem(A, dtype, trans_a ? k * lda + i : i * lda + k)",
+                              "load_elem(A, dtype, trans_a ? i * lda + k : k * lda + i)"),
+    "trans_b_wrong_ld": ("load_elem(B, dtype, trans_b ? j * ldb + k : k * ldb + j)",
+                         "load_elem(B, dtype, trans_b ? j * K + k : k * ldb + j)"),
     "entries_drop_k": ("for (int64_t k = 0; k < K; ++k) {",
                        "for (int64_t k = 0; k + 1 < K; ++k) {"),
     "metric_absolute": ("r = diff / den;", "r = diff;"),
