@@ -162,7 +162,7 @@ double gemm_seconds(int dtype, const Variant& v, int64_t M, int64_t N, int64_t K
 }
 
 Choice heuristic(int dtype, int64_t M, int64_t N, int64_t K, bool allow_split, bool need_epi = false,
-                 bool need_bt = false, bool need_q8 = false) {
+                 bool need_bt = false, bool need_q8 = false, bool need_at = false) {
   const auto& v = table().v[dtype];
   const double es = (double)out_bytes(dtype);
   Choice best;
@@ -171,6 +171,7 @@ Choice heuristic(int dtype, int64_t M, int64_t N, int64_t K, bool allow_split, b
     if (need_epi && !v[i].launch_epi) continue;
     if (need_bt && !v[i].launch_bt) continue;
     if (need_q8 && !v[i].launch_q8) continue;
+    if (need_at && !(need_bt ? v[i].launch_atbt : v[i].launch_at)) continue;
     const double t1 = gemm_seconds(dtype, v[i], M, N, K, 1);
     if (t1 < best.t) best = Choice{(int)i, 1, t1};
     if (!allow_split || !v[i].launch_partial || M == 0 || N == 0) continue;
@@ -190,12 +191,13 @@ Choice heuristic(int dtype, int64_t M, int64_t N, int64_t K, bool allow_split, b
 
 // Plain calls (split = false) never split; split-K calls may.
 gemm_config_t select(int dtype, int64_t M, int64_t N, int64_t K, bool split = false,
-                     bool need_epi = false, bool need_bt = false, bool need_q8 = false) {
+                     bool need_epi = false, bool need_bt = false, bool need_q8 = false,
+                     bool need_at = false) {
   {
     std::lock_guard<std::mutex> lk(g_tuning_mu);
     for (const auto& e : g_tuning)
       if (e.dtype == dtype && e.M == M && e.N == N && e.K == K && (split || e.splits <= 1) &&
-          (!need_epi || table().v[dtype][e.id].launch_epi) && !need_bt && !need_q8) {
+          (!need_epi || table().v[dtype][e.id].launch_epi) && !need_bt && !need_q8 && !need_at) {
         gemm_config_t d = table().v[dtype][e.id].desc;
         d.order = e.order;
         d.group_m = e.group_m;
@@ -203,7 +205,7 @@ gemm_config_t select(int dtype, int64_t M, int64_t N, int64_t K, bool split = fa
         return d;
       }
   }
-  const Choice c = heuristic(dtype, M, N, K, split, need_epi, need_bt, need_q8);
+  const Choice c = heuristic(dtype, M, N, K, split, need_epi, need_bt, need_q8, need_at);
   gemm_config_t d = table().v[dtype][c.id].desc;
   d.splits = (int32_t)c.splits;
   return d;
@@ -232,13 +234,15 @@ size_t span_bytes(int64_t rows, int64_t cols, int64_t ld, size_t es) {
 
 // bt: B is given transposed (Bt, N x K row-major, leading dimension ldb).
 // c_es: bytes of one C element when not the dtype's (INT8 codes: 1).
+// at: A is given transposed (At, K x M row-major, leading dimension lda).
 gemm_status_t validate(int dtype, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
                        const void* B, int64_t ldb, const void* C, int64_t ldc, bool bt = false,
-                       size_t c_es = 0) {
+                       size_t c_es = 0, bool at = false) {
   if (M < 0 || N < 0 || K < 0) return fail(GEMM_ERR_INVALID_ARG, "negative dimension");
   const int64_t lim = 0x7fffffff;
   if (M > lim || N > lim || K > lim) return fail(GEMM_ERR_INVALID_ARG, "dimension above 2^31-1");
-  if (lda < (K > 1 ? K : 1)) return fail(GEMM_ERR_INVALID_ARG, "lda < max(1, K)");
+  if (!at && lda < (K > 1 ? K : 1)) return fail(GEMM_ERR_INVALID_ARG, "lda < max(1, K)");
+  if (at && lda < (M > 1 ? M : 1)) return fail(GEMM_ERR_INVALID_ARG, "lda < max(1, M) (A transposed)");
   if (!bt && ldb < (N > 1 ? N : 1)) return fail(GEMM_ERR_INVALID_ARG, "ldb < max(1, N)");
   if (bt && ldb < (K > 1 ? K : 1)) return fail(GEMM_ERR_INVALID_ARG, "ldbt < max(1, K)");
   if (ldc < (N > 1 ? N : 1)) return fail(GEMM_ERR_INVALID_ARG, "ldc < max(1, N)");
@@ -249,7 +253,7 @@ gemm_status_t validate(int dtype, int64_t M, int64_t N, int64_t K, const void* A
   if (cdiv(M, 64) * cdiv(N, 64) > tiles_lim) return fail(GEMM_ERR_INVALID_ARG, "output too large");
   const size_t es = in_bytes(dtype);
   const size_t cb = span_bytes(M, N, ldc, c_es ? c_es : out_bytes(dtype));
-  if (overlap(C, cb, A, span_bytes(M, K, lda, es)) ||
+  if (overlap(C, cb, A, at ? span_bytes(K, M, lda, es) : span_bytes(M, K, lda, es)) ||
       overlap(C, cb, B, bt ? span_bytes(N, K, ldb, es) : span_bytes(K, N, ldb, es)))
     return fail(GEMM_ERR_ALIAS, "C overlaps A or B");
   return GEMM_OK;
@@ -261,10 +265,10 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 // selection for the shape.
 gemm_status_t resolve(int dtype, int64_t M, int64_t N, int64_t K, const gemm_config_t* forced,
                       bool split, gemm_config_t& cfg, bool need_epi = false, bool need_bt = false,
-                      bool need_q8 = false) {
+                      bool need_q8 = false, bool need_at = false) {
   const auto& v = table().v[dtype];
   if (!forced) {
-    cfg = select(dtype, M, N, K, split, need_epi, need_bt, need_q8);
+    cfg = select(dtype, M, N, K, split, need_epi, need_bt, need_q8, need_at);
     return GEMM_OK;
   }
   if (forced->id < 0 || forced->id >= (int32_t)v.size())
@@ -280,6 +284,8 @@ gemm_status_t resolve(int dtype, int64_t M, int64_t N, int64_t K, const gemm_con
     return fail(GEMM_ERR_UNSUPPORTED, "variant %s has no transposed-B form", v[forced->id].desc.name);
   if (need_q8 && !v[forced->id].launch_q8)
     return fail(GEMM_ERR_UNSUPPORTED, "variant %s has no INT8-epilogue form", v[forced->id].desc.name);
+  if (need_at && !(need_bt ? v[forced->id].launch_atbt : v[forced->id].launch_at))
+    return fail(GEMM_ERR_UNSUPPORTED, "variant %s has no transposed-A form", v[forced->id].desc.name);
   cfg = v[forced->id].desc;
   cfg.order = forced->order;
   cfg.group_m = forced->group_m;
@@ -453,6 +459,45 @@ gemm_status_t run_q8(int dtype, int64_t M, int64_t N, int64_t K, const void* A, 
   if (!vec) return unsupported();
   const TileMap map = make_map(cfg, M, N);
   const hipError_t e = table().v[dtype][cfg.id].launch_q8(p, map, vec, static_cast<hipStream_t>(stream));
+  if (e == hipErrorNotSupported) return unsupported();
+  if (e != hipSuccess) return fail(GEMM_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+  return GEMM_OK;
+}
+
+// C = op(A) op(B) for the four layouts; the two with A transposed run on
+// the LDS-direct kernels' transposed-A forms (vector layout only).
+gemm_status_t run_trans(int dtype, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                        const void* B, int64_t ldb, void* C, int64_t ldc, void* stream,
+                        const gemm_config_t* forced, int32_t trans_a, int32_t trans_b) {
+  g_err[0] = 0;
+  if ((trans_a != 0 && trans_a != 1) || (trans_b != 0 && trans_b != 1))
+    return fail(GEMM_ERR_INVALID_ARG, "trans_a and trans_b must be 0 or 1");
+  if (!trans_a) return trans_b ? run_bt(dtype, M, N, K, A, lda, B, ldb, C, ldc, stream, forced)
+                               : run(dtype, M, N, K, A, lda, B, ldb, C, ldc, stream, forced);
+  const bool bt = trans_b != 0;
+  gemm_status_t st = validate(dtype, M, N, K, A, lda, B, ldb, C, ldc, bt, 0, true);
+  if (st != GEMM_OK) return st;
+  gemm_config_t cfg;
+  st = resolve(dtype, M, N, K, forced, false, cfg, false, bt, false, true);
+  if (st != GEMM_OK) return st;
+  if (M == 0 || N == 0) return GEMM_OK;
+  Params p = make_params(dtype, A, lda, B, ldb, C, ldc, M, N, K);
+  p.bt = bt;
+  // 16-byte chunks: A^T rows of M values, B rows of N (or Bt rows of K).
+  const int64_t w = 16 / (int64_t)in_bytes(dtype), wc = 16 / (int64_t)out_bytes(dtype);
+  const bool vec = aligned16(A) && aligned16(B) && aligned16(C) && lda % w == 0 && ldb % w == 0 &&
+                   ldc % wc == 0 && M % w == 0 && (bt ? K % w == 0 : N % w == 0) && N % wc == 0;
+  auto unsupported = [] {
+    return fail(GEMM_ERR_UNSUPPORTED,
+                "A transposed needs 16-byte aligned A, B and C, M, lda, ldb and N (K when B is "
+                "transposed too) multiples of 16 bytes of elements, ldc likewise for C, and byte "
+                "offsets below 2^31");
+  };
+  if (!vec) return unsupported();
+  const Variant& var = table().v[dtype][cfg.id];
+  const TileMap map = make_map(cfg, M, N);
+  const hipError_t e =
+      (bt ? var.launch_atbt : var.launch_at)(p, map, vec, static_cast<hipStream_t>(stream));
   if (e == hipErrorNotSupported) return unsupported();
   if (e != hipSuccess) return fail(GEMM_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
   return GEMM_OK;
@@ -659,6 +704,33 @@ gemm_status_t gemm_f8_epi_q8(int64_t M, int64_t N, int64_t K, const gemm_f8_t* A
                              const gemm_f8_t* B, int64_t ldb, int8_t* Q, int64_t ldq, void* stream,
                              const gemm_config_t* cfg, const gemm_epilogue_t* epi) {
   return run_q8(GEMM_DTYPE_F8, M, N, K, A, lda, B, ldb, Q, ldq, stream, cfg, epi);
+}
+
+gemm_status_t gemm_f32_trans(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
+                             const float* B, int64_t ldb, float* C, int64_t ldc, void* stream,
+                             const gemm_config_t* cfg, int32_t trans_a, int32_t trans_b) {
+  return run_trans(GEMM_DTYPE_F32, M, N, K, A, lda, B, ldb, C, ldc, stream, cfg, trans_a, trans_b);
+}
+
+gemm_status_t gemm_f16_trans(int64_t M, int64_t N, int64_t K, const gemm_f16_t* A, int64_t lda,
+                             const gemm_f16_t* B, int64_t ldb, gemm_f16_t* C, int64_t ldc,
+                             void* stream, const gemm_config_t* cfg, int32_t trans_a,
+                             int32_t trans_b) {
+  return run_trans(GEMM_DTYPE_F16, M, N, K, A, lda, B, ldb, C, ldc, stream, cfg, trans_a, trans_b);
+}
+
+gemm_status_t gemm_bf16_trans(int64_t M, int64_t N, int64_t K, const gemm_bf16_t* A, int64_t lda,
+                              const gemm_bf16_t* B, int64_t ldb, gemm_bf16_t* C, int64_t ldc,
+                              void* stream, const gemm_config_t* cfg, int32_t trans_a,
+                              int32_t trans_b) {
+  return run_trans(GEMM_DTYPE_BF16, M, N, K, A, lda, B, ldb, C, ldc, stream, cfg, trans_a, trans_b);
+}
+
+gemm_status_t gemm_f8_trans(int64_t M, int64_t N, int64_t K, const gemm_f8_t* A, int64_t lda,
+                            const gemm_f8_t* B, int64_t ldb, gemm_bf16_t* C, int64_t ldc,
+                            void* stream, const gemm_config_t* cfg, int32_t trans_a,
+                            int32_t trans_b) {
+  return run_trans(GEMM_DTYPE_F8, M, N, K, A, lda, B, ldb, C, ldc, stream, cfg, trans_a, trans_b);
 }
 
 int64_t gemm_splitk_workspace_bytes(int32_t dtype, int64_t M, int64_t N, int64_t K, int32_t splits) {

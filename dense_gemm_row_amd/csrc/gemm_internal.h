@@ -235,6 +235,11 @@ struct Variant {
   // Launch of the INT8-quantising fused epilogue (C holds int8 codes,
   // p.epi.beta == 0), or nullptr when the kernel has no such form.
   LaunchFn launch_q8;
+  // Launches with A given transposed (p.A is At, K x M row-major), B as
+  // usual (launch_at) or also transposed (launch_atbt); nullptr when the
+  // kernel has no such form.
+  LaunchFn launch_at;
+  LaunchFn launch_atbt;
 };
 
 // Per-family registration (each kernel file defines its table).

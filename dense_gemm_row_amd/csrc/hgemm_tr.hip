@@ -96,11 +96,15 @@ __device__ __forceinline__ void static_for(F&& f, std::integer_sequence<int, I..
 // column-major B); its tile is then staged and read exactly like A's (one
 // LDS row per output column, k contiguous), with no transpose read.  TY_:
 // the element types, 0 binary16 in and out, 1 bfloat16 in and out, 2 FP8
-// E4M3 in and bfloat16 out.
+// E4M3 in and bfloat16 out.  AT_: A given transposed (At, K x M row-major,
+// i.e. column-major A): its tile is staged and read exactly like B's (k
+// rows of BM values, chunk XOR by k, transpose reads), which hands each
+// lane the same k run of its row as the direct read of row-major A.
 template <int BM_, int BN_, int WM_, int WN_, int BK_, int NS_, int MODE_ = 0, bool BT_ = false,
-          int TY_ = 0>
+          int TY_ = 0, bool AT_ = false>
 struct Shape {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BK_, NS = NS_, TY = TY_;
+  static constexpr bool AT = AT_;
   static constexpr bool PARTIAL = MODE_ == 1, EPI = MODE_ == 2 || MODE_ == 3, Q8 = MODE_ == 3, BT = BT_;
   static constexpr bool BF = TY != 0;   // C (and the epilogue's old C) is bfloat16
   static constexpr bool F8 = TY == 2;   // A and B are FP8 E4M3
@@ -114,10 +118,11 @@ struct Shape {
   static constexpr int NT = NW * 64;
   static constexpr int MB = WM / 32, NB = WN / 32, KS = BK / KW;
   static constexpr int NMMA_ = MB * NB;  // MFMAs per k step
-  static constexpr int A_ROW = BK * ES, A_CPR = A_ROW / 16;  // bytes / chunks per A row
+  // A rows: BM rows of BK k values, or (AT) BK rows of BM values.
+  static constexpr int A_ROW = AT ? BM * ES : BK * ES, A_CPR = A_ROW / 16;  // bytes / chunks
   // B rows: BK rows of BN columns, or (BT) BN rows of BK k values.
   static constexpr int B_ROW = BT ? BK * ES : BN * ES, B_CPR = B_ROW / 16;  // bytes / chunks
-  static constexpr int A_STAGE = BM * A_ROW, B_STAGE = BT ? BN * B_ROW : BK * B_ROW;
+  static constexpr int A_STAGE = AT ? BK * A_ROW : BM * A_ROW, B_STAGE = BT ? BN * B_ROW : BK * B_ROW;
   static constexpr int LDS_BYTES = NS * (A_STAGE + B_STAGE);
   static constexpr int IA = A_STAGE / 1024 / NW, IB = B_STAGE / 1024 / NW, LPS = IA + IB;
   // With three or more stages a slice's copies are spread over the k steps
@@ -141,6 +146,7 @@ struct Shape {
   static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile");
   static_assert(A_STAGE % (1024 * NW) == 0 && B_STAGE % (1024 * NW) == 0, "direct-load split");
   static_assert(BT || B_CPR >= 16, "B rows of at least 256 bytes (the k%4 chunk XOR)");
+  static_assert(!AT || A_CPR >= 16, "A^T rows of at least 256 bytes (the chunk XOR)");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
   static_assert((NS - 1) * LPS <= 63, "vmcnt field");
   static_assert(!SPREAD || (LPS % KS == 0 && PP <= NMMA_), "copies split evenly over k steps");
@@ -151,8 +157,9 @@ struct Shape {
   static_assert(P >= 1 && WM % P == 0 && RPA % 32 == 0 && RPA % EPI_RPI == 0 &&
                 RPA * EPI_ROW <= A_STAGE && RPA * EPI_ROW <= B_STAGE, "epilogue staging");
   // Fragment reads use a per-lane base plus immediate offsets (< 64 KB).
-  static_assert((MB - 1) * 32 * A_ROW < 65536 && (BK - KW + RR * (TRN - 1)) * B_ROW < 65536 &&
-                (NB - 1) * 32 * B_ROW < 65536, "immediate offsets");
+  static_assert((AT ? (BK - KW + RR * (TRN - 1)) * A_ROW : (MB - 1) * 32 * A_ROW) < 65536 &&
+                (BK - KW + RR * (TRN - 1)) * B_ROW < 65536 && (NB - 1) * 32 * B_ROW < 65536,
+                "immediate offsets");
 
   // Byte offsets within one stage array.
   __host__ __device__ static constexpr int a_byte(int r, int q) { return swz_off(r, q, A_ROW); }
@@ -190,6 +197,30 @@ struct Shape {
   __host__ __device__ static constexpr int b_frag(int wn0, int nb, int j, int jr, int l) {
     return b_byte(KW * j + (KW / 2) * (l / 32) + RR * jr + (l % 16) / (16 / RR),
                   wn0 + 32 * nb + 16 * ((l / 16) % 2) + (8 / ES) * (l % (16 / RR)));
+  }
+  // AT: A^T tile row k, value m (B's layout with BM values per row); the
+  // direct loads; the transpose read jr of k step j for row block mb
+  // (b_frag's lane map with wm0 + 32mb for wn0 + 32nb).
+  __host__ __device__ static constexpr int at_byte(int k, int m) {
+    return k * A_ROW + 16 * b_phys(k, m / CE) + ES * (m % CE);
+  }
+  __host__ __device__ static constexpr int at_dl_k(int i, int w, int l) {
+    return (1024 * (i * NW + w) + 16 * l) / A_ROW;
+  }
+  __host__ __device__ static constexpr int at_dl_c(int i, int w, int l) {
+    return ((1024 * (i * NW + w) + 16 * l) % A_ROW / 16) ^ b_swz(at_dl_k(i, w, l));
+  }
+  __host__ __device__ static constexpr int at_frag(int wm0, int mb, int j, int jr, int l) {
+    return at_byte(KW * j + (KW / 2) * (l / 32) + RR * jr + (l % 16) / (16 / RR),
+                   wm0 + 32 * mb + 16 * ((l / 16) % 2) + (8 / ES) * (l % (16 / RR)));
+  }
+  // BT direct loads: Bt rows (B_ROW bytes) placed like row-major A's rows,
+  // by B's own row length (with A transposed the two differ).
+  __host__ __device__ static constexpr int bt_dl_row(int i, int w, int l) {
+    return (1024 / B_ROW) * (i * NW + w) + l / (B_ROW / 16);
+  }
+  __host__ __device__ static constexpr int bt_dl_q(int i, int w, int l) {
+    return (l % (B_ROW / 16)) ^ swz_row(bt_dl_row(i, w, l), B_ROW);
   }
   // BT: B tile row n (one output column), 16-byte k chunk q, placed and read
   // with A's maps (B_ROW == A_ROW): lane reads column wn0 + 32nb + l%32,
@@ -258,11 +289,11 @@ __device__ __forceinline__ void issue_slice(const unsigned char* Ab, const unsig
                                             int64_t a_bytes, int64_t b_bytes, int s, bool live,
                                             const unsigned* a_vo, const unsigned* b_vo,  // this slice's
                                             unsigned char* lds_a, unsigned char* lds_b, int wave,
-                                            int ldb) {
+                                            int lda, int ldb) {
   // Slices past the last one (issued only to keep the wait counts uniform)
   // get empty descriptors: they load zeros without touching memory.
-  const int64_t ka = S::ES * (int64_t)s * S::BK;
-  const int64_t kb = S::BT ? ka : (int64_t)s * S::BK * ldb * S::ES;
+  const int64_t ka = S::AT ? (int64_t)s * S::BK * lda * S::ES : S::ES * (int64_t)s * S::BK;
+  const int64_t kb = S::BT ? S::ES * (int64_t)s * S::BK : (int64_t)s * S::BK * ldb * S::ES;
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(Ab + ka, live ? a_bytes - ka : 0);
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bb + kb, live ? b_bytes - kb : 0);
   // Copy instructions Q0 .. Q1-1 of the slice: A's IA blocks, then B's IB.
@@ -323,10 +354,11 @@ hgemm_tr_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
   const int sk = blockIdx.y;
   const int kc = p.splits > 1 ? p.kc : p.K;
   const int M = p.M, N = p.N, K = min(kc, p.K - sk * kc);
-  const unsigned char* Ab = static_cast<const unsigned char*>(p.A) + S::ES * (int64_t)sk * kc;
+  const int64_t ashift = S::AT ? S::ES * (int64_t)sk * kc * lda : S::ES * (int64_t)sk * kc;
+  const unsigned char* Ab = static_cast<const unsigned char*>(p.A) + ashift;
   const int64_t bshift = S::BT ? S::ES * (int64_t)sk * kc : S::ES * (int64_t)sk * kc * ldb;
   const unsigned char* Bb = static_cast<const unsigned char*>(p.B) + bshift;
-  a_bytes -= S::ES * (int64_t)sk * kc;
+  a_bytes -= ashift;
   b_bytes -= bshift;
 
   const int tid = threadIdx.x;
@@ -339,16 +371,23 @@ hgemm_tr_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
   unsigned a_vo[IA], a_vo_tail[IA], b_vo[IB], b_vo_tail[IB];
 #pragma unroll
   for (int i = 0; i < IA; ++i) {
-    const int r = S::a_dl_row(i, wave, l), q = S::a_dl_q(i, wave, l);
-    const bool ok = (m0 + r) < M;
-    a_vo[i] = ok ? (unsigned)S::ES * ((unsigned)(m0 + r) * (unsigned)lda + (unsigned)S::CE * q) : OOB;
-    a_vo_tail[i] = ((T - 1) * BK + S::CE * q < K) ? a_vo[i] : OOB;
+    if constexpr (S::AT) {
+      const int k = S::at_dl_k(i, wave, l), c = S::at_dl_c(i, wave, l);
+      const bool ok = (m0 + S::CE * c) < M;
+      a_vo[i] = ok ? (unsigned)S::ES * ((unsigned)k * (unsigned)lda + (unsigned)(m0 + S::CE * c)) : OOB;
+      a_vo_tail[i] = a_vo[i];  // rows past K are past the buffer's range
+    } else {
+      const int r = S::a_dl_row(i, wave, l), q = S::a_dl_q(i, wave, l);
+      const bool ok = (m0 + r) < M;
+      a_vo[i] = ok ? (unsigned)S::ES * ((unsigned)(m0 + r) * (unsigned)lda + (unsigned)S::CE * q) : OOB;
+      a_vo_tail[i] = ((T - 1) * BK + S::CE * q < K) ? a_vo[i] : OOB;
+    }
   }
 #pragma unroll
   for (int i = 0; i < IB; ++i) {
     if constexpr (S::BT) {
-      // Bt row n0 + r (output column), k chunk q: A's placement.
-      const int r = S::a_dl_row(i, wave, l), q = S::a_dl_q(i, wave, l);
+      // Bt row n0 + r (output column), k chunk q: row-major A's placement.
+      const int r = S::bt_dl_row(i, wave, l), q = S::bt_dl_q(i, wave, l);
       const bool ok = (n0 + r) < N;
       b_vo[i] = ok ? (unsigned)S::ES * ((unsigned)(n0 + r) * (unsigned)ldb + (unsigned)S::CE * q) : OOB;
       b_vo_tail[i] = ((T - 1) * BK + S::CE * q < K) ? b_vo[i] : OOB;
@@ -362,11 +401,16 @@ hgemm_tr_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
   // Fragment byte offsets: k step j of A and block nb of B; other blocks
   // and k steps are immediate offsets.
   constexpr int FR = S::FR;
-  int a_fb[KS * FR], b_fb[S::BT ? KS * FR : NB];
+  int a_fb[S::AT ? MB : KS * FR], b_fb[S::BT ? KS * FR : NB];
+  if constexpr (S::AT) {
 #pragma unroll
-  for (int j = 0; j < KS; ++j)
+    for (int mb = 0; mb < MB; ++mb) a_fb[mb] = S::at_frag(wm0, mb, 0, 0, l);
+  } else {
 #pragma unroll
-    for (int q = 0; q < FR; ++q) a_fb[j * FR + q] = S::a_frag(wm0, 0, j, l, q);
+    for (int j = 0; j < KS; ++j)
+#pragma unroll
+      for (int q = 0; q < FR; ++q) a_fb[j * FR + q] = S::a_frag(wm0, 0, j, l, q);
+  }
   if constexpr (S::BT) {
 #pragma unroll
     for (int j = 0; j < KS; ++j)
@@ -379,14 +423,14 @@ hgemm_tr_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
 
   auto issue = [&](int s, unsigned char* la, unsigned char* lb) __attribute__((always_inline)) {
     issue_slice<S>(Ab, Bb, a_bytes, b_bytes, s, s < T, s == T - 1 ? a_vo_tail : a_vo,
-                   s == T - 1 ? b_vo_tail : b_vo, la, lb, wave, ldb);
+                   s == T - 1 ? b_vo_tail : b_vo, la, lb, wave, lda, ldb);
   };
   // Part j (of KS) of slice s's copies.
   auto issue_part = [&](int s, auto J, unsigned char* la, unsigned char* lb) __attribute__((always_inline)) {
     constexpr int j = decltype(J)::value;
     issue_slice<S, j * S::PP, (j + 1) * S::PP>(Ab, Bb, a_bytes, b_bytes, s, s < T,
                                                s == T - 1 ? a_vo_tail : a_vo,
-                                               s == T - 1 ? b_vo_tail : b_vo, la, lb, wave, ldb);
+                                               s == T - 1 ? b_vo_tail : b_vo, la, lb, wave, lda, ldb);
   };
 
   // An operand: 8 16-bit or 32 8-bit values per lane.
@@ -398,44 +442,57 @@ hgemm_tr_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
     const u32x4 x0 = *(const lds_u32x4*)p0, x1 = *(const lds_u32x4*)p1;
     return __builtin_bit_cast(i32x8_t, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
   };
+  // The transpose reads of one operand from a row-major (k rows) tile at
+  // byte b, rows `row` bytes apart.
+  auto tr_operand = [](const unsigned char* b, int row) __attribute__((always_inline)) {
+    if constexpr (S::F8) {
+      const i32x2 r0 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)b);
+      const i32x2 r1 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(b + 8 * row));
+      const i32x2 r2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(b + 16 * row));
+      const i32x2 r3 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(b + 24 * row));
+      const i32x4 lo = __builtin_shufflevector(r0, r1, 0, 1, 2, 3);
+      const i32x4 hi = __builtin_shufflevector(r2, r3, 0, 1, 2, 3);
+      return Frag(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    } else {
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)b);
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(b + 4 * row));
+      return Frag(__builtin_bit_cast(f16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7)));
+    }
+  };
   auto load_frags = [&](int buf, const unsigned char* la, const unsigned char* lb, int j)
       __attribute__((always_inline)) {
-    if constexpr (S::F8) {
+    if constexpr (S::AT) {
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-        fa[buf][mb] = two_chunks(la + a_fb[2 * j] + mb * 32 * S::A_ROW, la + a_fb[2 * j + 1] + mb * 32 * S::A_ROW);
+      for (int mb = 0; mb < MB; ++mb) fa[buf][mb] = tr_operand(la + a_fb[mb] + S::KW * j * S::A_ROW, S::A_ROW);
+    }
+    if constexpr (S::F8) {
+      if constexpr (!S::AT) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+          fa[buf][mb] = two_chunks(la + a_fb[2 * j] + mb * 32 * S::A_ROW, la + a_fb[2 * j + 1] + mb * 32 * S::A_ROW);
+      }
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         if constexpr (S::BT) {
           fb[buf][nb] = two_chunks(lb + b_fb[2 * j] + nb * 32 * S::B_ROW, lb + b_fb[2 * j + 1] + nb * 32 * S::B_ROW);
         } else {
-          const unsigned char* b = lb + b_fb[nb] + S::KW * j * S::B_ROW;
-          const i32x2 r0 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)b);
-          const i32x2 r1 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(b + 8 * S::B_ROW));
-          const i32x2 r2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(b + 16 * S::B_ROW));
-          const i32x2 r3 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(b + 24 * S::B_ROW));
-          const i32x4 lo = __builtin_shufflevector(r0, r1, 0, 1, 2, 3);
-          const i32x4 hi = __builtin_shufflevector(r2, r3, 0, 1, 2, 3);
-          fb[buf][nb] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          fb[buf][nb] = tr_operand(lb + b_fb[nb] + S::KW * j * S::B_ROW, S::B_ROW);
         }
       }
       return;
     } else {
+    if constexpr (!S::AT) {
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-      fa[buf][mb] = *(const lds_f16x8*)(la + a_fb[j] + mb * 32 * S::A_ROW);
+      for (int mb = 0; mb < MB; ++mb)
+        fa[buf][mb] = *(const lds_f16x8*)(la + a_fb[j] + mb * 32 * S::A_ROW);
+    }
     if constexpr (S::BT) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
         fb[buf][nb] = *(const lds_f16x8*)(lb + b_fb[j] + nb * 32 * S::B_ROW);
     } else {
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const unsigned char* b = lb + b_fb[nb] + 16 * j * S::B_ROW;
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)b);
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(b + 4 * S::B_ROW));
-        fb[buf][nb] = __builtin_bit_cast(f16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      }
+      for (int nb = 0; nb < NB; ++nb) fb[buf][nb] = tr_operand(lb + b_fb[nb] + 16 * j * S::B_ROW, S::B_ROW);
     }
     }
   };
@@ -463,7 +520,7 @@ hgemm_tr_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
   // (The lambdas are forced inline: an out-of-line call would move the
   // accumulators to scratch memory.)
   constexpr int NMMA = MB * NB;     // MFMAs per k step
-  constexpr int NRD = MB * FR + (S::BT ? FR : S::TRN) * NB;  // LDS reads per k step
+  constexpr int NRD = MB * (S::AT ? S::TRN : FR) + (S::BT ? FR : S::TRN) * NB;  // LDS reads per k step
   // Slice t from stage c: k steps 0..KS-2 with the next step's fragments
   // in flight; wait for slice t+1; barrier; issue slice t+NS into the freed
   // stage c; last k step (registers only) under the first fragment reads of
@@ -695,15 +752,19 @@ hipError_t launch(const Params& p, const TileMap& map, bool vec, hipStream_t str
   const bool b_far = S::BT ? (int64_t)(p.N + S::BN) * p.ldb * ES > lim
                            : (int64_t)(S::BK + 2) * p.ldb * ES > lim ||
                                  ((int64_t)(p.K > 0 ? p.K - 1 : 0) * p.ldb + p.N) * ES > lim;
-  if (!vec || (int64_t)(p.M + S::BM) * p.lda * ES > lim || b_far || (int64_t)p.M * p.lda * ES > lim ||
-      (S::EPI && (int64_t)p.M * p.ldc * 2 > lim)) {
+  const bool a_far = S::AT ? (int64_t)(S::BK + 2) * p.lda * ES > lim ||
+                                 ((int64_t)(p.K > 0 ? p.K - 1 : 0) * p.lda + p.M) * ES > lim
+                           : (int64_t)(p.M + S::BM) * p.lda * ES > lim || (int64_t)p.M * p.lda * ES > lim;
+  if (!vec || a_far || b_far || (S::EPI && (int64_t)p.M * p.ldc * 2 > lim)) {
     // The general kernel has no split-K form (the caller runs unsplit) and
-    // no FP8 or INT8-output form (the caller reports the operands
-    // unsupported).
-    if (p.splits > 1 || S::F8 || S::Q8) return hipErrorNotSupported;
+    // no FP8, INT8-output or transposed-A form (the caller reports the
+    // operands unsupported).
+    if (p.splits > 1 || S::F8 || S::Q8 || S::AT) return hipErrorNotSupported;
     return hgemm_launch_shape(S::BM, S::BN, S::WM, S::WN, p, map, vec, stream);
   }
-  const int64_t a_bytes = p.K > 0 ? ((int64_t)(p.M - 1) * p.lda + p.K) * ES : 0;
+  const int64_t a_bytes = p.K <= 0 ? 0
+                          : S::AT ? ((int64_t)(p.K - 1) * p.lda + p.M) * ES
+                                  : ((int64_t)(p.M - 1) * p.lda + p.K) * ES;
   const int64_t b_bytes = p.K <= 0 ? 0
                           : S::BT ? ((int64_t)(p.N - 1) * p.ldb + p.K) * ES
                                   : ((int64_t)(p.K - 1) * p.ldb + p.N) * ES;
@@ -725,7 +786,7 @@ int layout_check_bt(int banks, int64_t* rconf) {
     for (int w = 0; w < S::NW; ++w)
       for (int l = 0; l < 64; ++l) {
         const int off = 1024 * (i * S::NW + w) + 16 * l;
-        const int r = S::a_dl_row(i, w, l), q = S::a_dl_q(i, w, l);
+        const int r = S::bt_dl_row(i, w, l), q = S::bt_dl_q(i, w, l);
         if (r >= S::BN || q >= S::B_CPR || S::bt_byte(r, q) != off) return 20;
         for (int e = 0; e < S::CE; ++e) {
           if (n_of[off + S::ES * e] != -1) return 21;
@@ -753,6 +814,58 @@ int layout_check_bt(int banks, int64_t* rconf) {
                 return 25;
           }
           *rconf += lds_conflicts(addr, 16, banks);
+        }
+  }
+  return 0;
+}
+
+// Host replay of the transposed-A form's A side: A^T rows placed by the
+// direct loads (B's maps with BM values per row) and the transpose reads of
+// each row block, checked for coverage, bounds, the element each lane must
+// see and bank conflicts (added to *rconf).  Returns 0 when valid, else a
+// code from 40.
+template <class S>
+int layout_check_at(int banks, int64_t* rconf) {
+  static_assert(S::AT, "transposed-A shape");
+  static int m_of[S::A_STAGE], k_of[S::A_STAGE];
+  for (int i = 0; i < S::A_STAGE; ++i) m_of[i] = -1;
+  for (int i = 0; i < S::IA; ++i)
+    for (int w = 0; w < S::NW; ++w)
+      for (int l = 0; l < 64; ++l) {
+        const int off = 1024 * (i * S::NW + w) + 16 * l;
+        const int k = S::at_dl_k(i, w, l), c = S::at_dl_c(i, w, l);
+        if (k >= S::BK || c >= S::A_CPR || S::at_byte(k, S::CE * c) != off) return 40;
+        for (int e = 0; e < S::CE; ++e) {
+          if (m_of[off + S::ES * e] != -1) return 41;
+          m_of[off + S::ES * e] = S::CE * c + e;
+          k_of[off + S::ES * e] = k;
+        }
+      }
+  for (int i = 0; i < S::A_STAGE; i += S::ES)
+    if (m_of[i] < 0) return 42;
+  int addr[64];
+  constexpr int LPR = 16 / S::RR;
+  for (int w = 0; w < S::NW; ++w) {
+    const int wm0 = (w / S::WAVES_N) * S::WM;
+    for (int j = 0; j < S::KS; ++j)
+      for (int mb = 0; mb < S::MB; ++mb)
+        for (int jr = 0; jr < S::TRN; ++jr) {
+          for (int l = 0; l < 64; ++l) {
+            addr[l] = S::at_frag(wm0, mb, j, jr, l);
+            if (addr[l] != S::at_frag(wm0, mb, 0, 0, l) + (S::KW * j + S::RR * jr) * S::A_ROW) return 43;
+          }
+          for (int l = 0; l < 64; ++l)
+            for (int t = 0; t < S::RR; ++t) {
+              const int g = l / 16, jj = l % 16;
+              const int src = addr[16 * g + LPR * t + jj / S::RR] + S::ES * (jj % S::RR);
+              if (src < 0 || src >= S::A_STAGE) return 44;
+              // B_op lane l, element RR*jr + t:
+              // A[m = wm0 + 32mb + l%32][k = KW j + (KW/2)(l/32) + RR jr + t].
+              if (k_of[src] != S::KW * j + (S::KW / 2) * (l / 32) + S::RR * jr + t ||
+                  m_of[src] != wm0 + 32 * mb + l % 32)
+                return 45;
+            }
+          *rconf += lds_conflicts(addr, 8, banks);
         }
   }
   return 0;
@@ -914,11 +1027,28 @@ int layout_check(int banks, int64_t out[2]) {
       rconf += lds_conflicts(addr, 16, banks);
     }
   }
-  const int rc = layout_check_bt<Shape<S::BM, S::BN, S::WM, S::WN, S::BK, S::NS, 0, true, S::TY>>(banks, &rconf);
+  int rc = layout_check_bt<Shape<S::BM, S::BN, S::WM, S::WN, S::BK, S::NS, 0, true, S::TY>>(banks, &rconf);
   if (rc != 0) return rc;
+  if constexpr (S::BM * S::ES >= 256) {
+    rc = layout_check_at<Shape<S::BM, S::BN, S::WM, S::WN, S::BK, S::NS, 0, false, S::TY, true>>(banks, &rconf);
+    if (rc != 0) return rc;
+    // Both transposed: B's side must not depend on A's row length.
+    rc = layout_check_bt<Shape<S::BM, S::BN, S::WM, S::WN, S::BK, S::NS, 0, true, S::TY, true>>(banks, &rconf);
+    if (rc != 0) return rc;
+  }
   out[0] = wconf;
   out[1] = rconf;
   return 0;
+}
+
+// The transposed-A launches, for tiles whose A^T rows (BM values) span the
+// 256 bytes the chunk XOR needs; none otherwise.
+template <int BM, int BN, int WM, int WN, int BK, int NS, int TY, bool BT>
+constexpr LaunchFn at_launch() {
+  if constexpr (BM * (TY == 2 ? 1 : 2) >= 256)
+    return &launch<Shape<BM, BN, WM, WN, BK, NS, 0, BT, TY, true>>;
+  else
+    return nullptr;
 }
 
 #define HGEMM_TR_VARIANT(TY, DT, TAG, BM, BN, WM, WN, BK, NS, EFF)                               \
@@ -933,7 +1063,9 @@ int layout_check(int banks, int64_t out[2]) {
         &launch<Shape<BM, BN, WM, WN, BK, NS, 1, false, TY>>, EFF,                           \
         &launch<Shape<BM, BN, WM, WN, BK, NS, 2, false, TY>>,                                \
         &launch<Shape<BM, BN, WM, WN, BK, NS, 0, true, TY>>,                                 \
-        &launch<Shape<BM, BN, WM, WN, BK, NS, 3, false, TY>>                                 \
+        &launch<Shape<BM, BN, WM, WN, BK, NS, 3, false, TY>>,                                \
+        at_launch<BM, BN, WM, WN, BK, NS, TY, false>(),                                      \
+        at_launch<BM, BN, WM, WN, BK, NS, TY, true>()                                        \
   }
 
 // The 16-bit LDS layouts and data path do not depend on the element type,

@@ -66,17 +66,22 @@ __device__ __forceinline__ void static_for(F&& f, std::integer_sequence<int, I..
 // holds column wn0 + NB*j + nb) so that a lane's 16-byte read gives four k
 // steps of its column and 16 lanes read 16 consecutive rows.
 // Q8_: the fused epilogue writes INT8 codes (C is int8, beta is 0).
+// AT_: A given transposed (At, K x M row-major, i.e. column-major A): its
+// tile is staged like B's, one LDS row per k with BM m values, and a lane
+// reads, per MFMA step, the MB adjacent values m = wm0 + MB*(l%32) + mb of
+// its k row (the row interleave that B's columns use), so output rows of
+// block mb are m = wm0 + MB*i + mb.
 template <int BM_, int BN_, int WM_, int WN_, int BK_, int NS_, bool EPI_ = false, bool BT_ = false,
-          bool Q8_ = false>
+          bool Q8_ = false, bool AT_ = false>
 struct Shape {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BK_, NS = NS_;
-  static constexpr bool EPI = EPI_ || Q8_, BT = BT_, Q8 = Q8_;
+  static constexpr bool EPI = EPI_ || Q8_, BT = BT_, Q8 = Q8_, AT = AT_;
   static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN, NW = WAVES_M * WAVES_N;
   static constexpr int NT = NW * 64;
   static constexpr int MB = WM / 32, NB = WN / 32, KG = BK / 8;  // k groups of 8 per slice
-  static constexpr int A_ROW = BK * 4, A_CPR = A_ROW / 16;       // bytes / chunks per A row
-  static constexpr int B_ROW = BT ? BK * 4 : BN * 4;             // bytes per B row
-  static constexpr int A_STAGE = BM * A_ROW, B_STAGE = BT ? BN * B_ROW : BK * B_ROW;
+  static constexpr int A_ROW = AT ? BM * 4 : BK * 4, A_CPR = A_ROW / 16;  // bytes / chunks per A row
+  static constexpr int B_ROW = BT ? BK * 4 : BN * 4;                      // bytes per B row
+  static constexpr int A_STAGE = AT ? BK * A_ROW : BM * A_ROW, B_STAGE = BT ? BN * B_ROW : BK * B_ROW;
   static constexpr int LDS_BYTES = NS * (A_STAGE + B_STAGE);
   static constexpr int IA = A_STAGE / 1024 / NW, IB = B_STAGE / 1024 / NW, LPS = IA + IB;
   static_assert(BK == 16 || BK == 32, "K slice");
@@ -89,7 +94,9 @@ struct Shape {
   static_assert(!BT || (NB - 1) * 32 * B_ROW < 65536, "immediate offsets (BT)");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
   static_assert((NS - 1) * LPS <= 63, "vmcnt field");
-  static_assert((MB - 1) * 32 * A_ROW < 65536 && BK * B_ROW < 65536, "immediate offsets");
+  static_assert((AT ? BK * A_ROW : (MB - 1) * 32 * A_ROW) < 65536 && BK * B_ROW < 65536,
+                "immediate offsets");
+  static_assert(!AT || A_ROW % 1024 == 0 || 1024 % A_ROW == 0, "A^T rows tile the 1 KB blocks");
 
   // Byte offsets within one stage array.
   __host__ __device__ static constexpr int a_byte(int r, int q) { return swz_off(r, q, A_ROW); }
@@ -116,6 +123,26 @@ struct Shape {
   //  B: lane reads row 8g + 4h + s, the NB columns wn0 + NB*(l%32) + nb.
   __host__ __device__ static constexpr int b_frag(int wn0, int g, int s, int l) {
     return b_byte(8 * g + 4 * (l / 32) + s, wn0 + NB * (l % 32));
+  }
+  // AT: A^T tile row k, m value m; direct loads; the fragment read of k
+  // group g, step s: row 8g + 4h + s, the MB rows wm0 + MB*(l%32) + mb.
+  __host__ __device__ static constexpr int at_byte(int k, int m) { return k * A_ROW + 4 * m; }
+  __host__ __device__ static constexpr int at_dl_k(int i, int w, int l) {
+    return (1024 * (i * NW + w) + 16 * l) / A_ROW;
+  }
+  __host__ __device__ static constexpr int at_dl_c(int i, int w, int l) {
+    return (1024 * (i * NW + w) + 16 * l) % A_ROW / 16;
+  }
+  __host__ __device__ static constexpr int at_frag(int wm0, int g, int s, int l) {
+    return at_byte(8 * g + 4 * (l / 32) + s, wm0 + MB * (l % 32));
+  }
+  // BT direct loads: Bt rows (B_ROW bytes) placed like row-major A's rows,
+  // by B's own row length (with A transposed the two differ).
+  __host__ __device__ static constexpr int bt_dl_row(int i, int w, int l) {
+    return (1024 / B_ROW) * (i * NW + w) + l / (B_ROW / 16);
+  }
+  __host__ __device__ static constexpr int bt_dl_q(int i, int w, int l) {
+    return (l % (B_ROW / 16)) ^ swz_row(bt_dl_row(i, w, l), B_ROW);
   }
   // BT: tile column held by LDS row R, the LDS placement of (row R, k
   // chunk q), and the fragment read of block nb in k group g: LDS row
@@ -174,9 +201,9 @@ __device__ __forceinline__ void issue_slice(const unsigned char* Ab, const unsig
                                             int64_t a_bytes, int64_t b_bytes, int s, bool live,
                                             const unsigned* a_vo, const unsigned* b_vo,
                                             unsigned char* lds_a, unsigned char* lds_b, int wave,
-                                            int ldb) {
-  const int64_t ka = 4 * (int64_t)s * S::BK;
-  const int64_t kb = S::BT ? ka : (int64_t)s * S::BK * ldb * 4;
+                                            int lda, int ldb) {
+  const int64_t ka = S::AT ? (int64_t)s * S::BK * lda * 4 : 4 * (int64_t)s * S::BK;
+  const int64_t kb = S::BT ? 4 * (int64_t)s * S::BK : (int64_t)s * S::BK * ldb * 4;
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(Ab + ka, live ? a_bytes - ka : 0);
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bb + kb, live ? b_bytes - kb : 0);
 #pragma unroll
@@ -229,10 +256,11 @@ sgemm_dl_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
   const int sk = blockIdx.y;
   const int kc = p.splits > 1 ? p.kc : p.K;
   const int M = p.M, N = p.N, K = min(kc, p.K - sk * kc);
-  const unsigned char* Ab = static_cast<const unsigned char*>(p.A) + 4 * (int64_t)sk * kc;
+  const int64_t ashift = S::AT ? 4 * (int64_t)sk * kc * lda : 4 * (int64_t)sk * kc;
+  const unsigned char* Ab = static_cast<const unsigned char*>(p.A) + ashift;
   const int64_t bshift = S::BT ? 4 * (int64_t)sk * kc : 4 * (int64_t)sk * kc * ldb;
   const unsigned char* Bb = static_cast<const unsigned char*>(p.B) + bshift;
-  a_bytes -= 4 * (int64_t)sk * kc;
+  a_bytes -= ashift;
   b_bytes -= bshift;
 
   const int tid = threadIdx.x;
@@ -245,16 +273,23 @@ sgemm_dl_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
   unsigned a_vo[IA], a_vo_tail[IA], b_vo[IB], b_vo_tail[IB];
 #pragma unroll
   for (int i = 0; i < IA; ++i) {
-    const int r = S::a_dl_row(i, wave, l), q = S::a_dl_q(i, wave, l);
-    const bool ok = (m0 + r) < M;
-    a_vo[i] = ok ? 4u * ((unsigned)(m0 + r) * (unsigned)lda + 4u * q) : OOB;
-    a_vo_tail[i] = ((T - 1) * BK + 4 * q < K) ? a_vo[i] : OOB;
+    if constexpr (S::AT) {
+      const int k = S::at_dl_k(i, wave, l), c = S::at_dl_c(i, wave, l);
+      const bool ok = (m0 + 4 * c) < M;
+      a_vo[i] = ok ? 4u * ((unsigned)k * (unsigned)lda + (unsigned)(m0 + 4 * c)) : OOB;
+      a_vo_tail[i] = a_vo[i];  // rows past K are past the buffer's range
+    } else {
+      const int r = S::a_dl_row(i, wave, l), q = S::a_dl_q(i, wave, l);
+      const bool ok = (m0 + r) < M;
+      a_vo[i] = ok ? 4u * ((unsigned)(m0 + r) * (unsigned)lda + 4u * q) : OOB;
+      a_vo_tail[i] = ((T - 1) * BK + 4 * q < K) ? a_vo[i] : OOB;
+    }
   }
 #pragma unroll
   for (int i = 0; i < IB; ++i) {
     if constexpr (S::BT) {
       // LDS row R holds Bt row n0 + bt_col(R); k chunk q as for A.
-      const int R = S::a_dl_row(i, wave, l), q = S::a_dl_q(i, wave, l);
+      const int R = S::bt_dl_row(i, wave, l), q = S::bt_dl_q(i, wave, l);
       const int n = n0 + S::bt_col(R);
       b_vo[i] = n < N ? 4u * ((unsigned)n * (unsigned)ldb + 4u * q) : OOB;
       b_vo_tail[i] = ((T - 1) * BK + 4 * q < K) ? b_vo[i] : OOB;
@@ -269,7 +304,8 @@ sgemm_dl_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
   // offsets), and group 0 step 0 of B (other steps and groups likewise).
   int a_fb[KG];
 #pragma unroll
-  for (int g = 0; g < KG; ++g) a_fb[g] = S::a_frag(wm0, 0, g, l);
+  for (int g = 0; g < KG; ++g) a_fb[g] = S::AT ? 0 : S::a_frag(wm0, 0, g, l);
+  const int at_fb = S::AT ? S::at_frag(wm0, 0, 0, l) : 0;
   const int b_fb = S::BT ? 0 : S::b_frag(wn0, 0, 0, l);
   int bt_fb[KG];
 #pragma unroll
@@ -277,16 +313,25 @@ sgemm_dl_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
 
   auto issue = [&](int s, unsigned char* la, unsigned char* lb) __attribute__((always_inline)) {
     issue_slice<S>(Ab, Bb, a_bytes, b_bytes, s, s < T, s == T - 1 ? a_vo_tail : a_vo,
-                   s == T - 1 ? b_vo_tail : b_vo, la, lb, wave, ldb);
+                   s == T - 1 ? b_vo_tail : b_vo, la, lb, wave, lda, ldb);
   };
 
-  f32x4 fa[2][MB];
+  typedef typename VecF<MB>::T vecMB;
+  typedef __attribute__((address_space(3))) vecMB lds_vecMB;
+  f32x4 fa[2][MB];   // A: four k steps of each row block
+  vecMB fat[2][4];   // A^T: each k step's MB rows
   vecNB fb[2][4];
   auto load_frags = [&](int buf, const unsigned char* la, const unsigned char* lb, int g)
       __attribute__((always_inline)) {
+    if constexpr (S::AT) {
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-      fa[buf][mb] = *(const lds_f32x4*)(la + a_fb[g] + mb * 32 * S::A_ROW);
+      for (int s = 0; s < 4; ++s)
+        fat[buf][s] = *(const lds_vecMB*)(la + at_fb + (8 * g + s) * S::A_ROW);
+    } else {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+        fa[buf][mb] = *(const lds_f32x4*)(la + a_fb[g] + mb * 32 * S::A_ROW);
+    }
     if constexpr (S::BT) {
       // One 16-byte read per block nb: its column's values for steps 0..3.
 #pragma unroll
@@ -319,14 +364,17 @@ sgemm_dl_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-          float bv;
+          float av, bv;
+          if constexpr (!S::AT) av = fa[buf][mb][s];
+          else if constexpr (MB == 1) av = fat[buf][s];
+          else av = fat[buf][s][mb];
           if constexpr (NB == 1) bv = fb[buf][s]; else bv = fb[buf][s][nb];
-          acc[mb][nb] = mfma(fa[buf][mb][s], bv, acc[mb][nb]);
+          acc[mb][nb] = mfma(av, bv, acc[mb][nb]);
         }
   };
 
   constexpr int NMMA = 4 * MB * NB;  // MFMAs per k group
-  constexpr int NRD = MB + (S::BT ? NB : 4);  // LDS reads per k group
+  constexpr int NRD = (S::AT ? 4 : MB) + (S::BT ? NB : 4);  // LDS reads per k group
   // (The lambdas are forced inline: a slice of the larger tiles is several
   // hundred MFMAs, past the inliner's budget, and an out-of-line call would
   // move the accumulators to scratch memory.)
@@ -383,7 +431,11 @@ sgemm_dl_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
   // lanes cover 128*NB contiguous bytes of the row).
   float* __restrict__ C = static_cast<float*>(p.C) + sk * p.c_stride;
   const int col = n0 + wn0 + NB * (l % 32);
-  auto row_of = [&](int mb, int r) { return m0 + wm0 + 32 * mb + 8 * (r / 4) + 4 * (l / 32) + (r % 4); };
+  // (A^T: block mb's row i is m = wm0 + MB*i + mb.)
+  auto row_of = [&](int mb, int r) {
+    const int i = 8 * (r / 4) + 4 * (l / 32) + (r % 4);
+    return S::AT ? m0 + wm0 + MB * i + mb : m0 + wm0 + 32 * mb + i;
+  };
   auto acc_vec = [&](int mb, int r) {
     vecNB v;
     if constexpr (NB == 1) {
@@ -491,16 +543,22 @@ template <class S>
 hipError_t launch(const Params& p, const TileMap& map, bool vec, hipStream_t stream) {
   const int64_t lim = 0x7fffffff;
   // Every offset (rows past M and K included) must fit the 31-bit range.
-  if (!vec || (int64_t)(p.M + S::BM) * p.lda * 4 > lim || (int64_t)(S::BK + 2) * p.ldb * 4 > lim ||
+  const bool a_far = S::AT ? (int64_t)(S::BK + 2) * p.lda * 4 > lim ||
+                                 ((int64_t)(p.K > 0 ? p.K - 1 : 0) * p.lda + p.M) * 4 > lim
+                           : (int64_t)(p.M + S::BM) * p.lda * 4 > lim;
+  if (!vec || a_far || (int64_t)(S::BK + 2) * p.ldb * 4 > lim ||
       (S::BT ? (int64_t)(p.N + S::BN) * p.ldb * 4 > lim
              : ((int64_t)(p.K > 0 ? p.K - 1 : 0) * p.ldb + p.N) * 4 > lim) ||
       (S::EPI && (int64_t)p.M * p.ldc * 4 > lim)) {
     // The general kernel has no split-K form (the caller runs unsplit) and
-    // no INT8 form (the caller reports the operands unsupported).
-    if (p.splits > 1 || S::Q8) return hipErrorNotSupported;
+    // no INT8 or transposed-A form (the caller reports the operands
+    // unsupported).
+    if (p.splits > 1 || S::Q8 || S::AT) return hipErrorNotSupported;
     return sgemm_launch_shape(S::BM, S::BN, S::WM, S::WN, p, map, vec, stream);
   }
-  const int64_t a_bytes = p.K > 0 ? ((int64_t)(p.M - 1) * p.lda + p.K) * 4 : 0;
+  const int64_t a_bytes = p.K <= 0 ? 0
+                          : S::AT ? ((int64_t)(p.K - 1) * p.lda + p.M) * 4
+                                  : ((int64_t)(p.M - 1) * p.lda + p.K) * 4;
   const int64_t b_bytes = p.K <= 0 ? 0
                           : S::BT ? ((int64_t)(p.N - 1) * p.ldb + p.K) * 4
                                   : ((int64_t)(p.K - 1) * p.ldb + p.N) * 4;
@@ -522,7 +580,7 @@ int layout_check_bt(int banks, int64_t* rconf) {
     for (int w = 0; w < S::NW; ++w)
       for (int l = 0; l < 64; ++l) {
         const int off = 1024 * (i * S::NW + w) + 16 * l;
-        const int R = S::a_dl_row(i, w, l), q = S::a_dl_q(i, w, l);
+        const int R = S::bt_dl_row(i, w, l), q = S::bt_dl_q(i, w, l);
         if (R >= S::BN || q >= S::BK / 4 || S::bt_byte(R, q) != off) return 20;
         for (int e = 0; e < 4; ++e) {
           if (n_of[off + 4 * e] != -1) return 21;
@@ -548,6 +606,50 @@ int layout_check_bt(int banks, int64_t* rconf) {
               return 25;
         }
         *rconf += lds_conflicts(addr, 16, banks);
+      }
+  }
+  return 0;
+}
+
+// Host replay of the transposed-A form's A side: A^T rows placed as loaded,
+// and the fragment reads checked for coverage, bounds, the element each
+// lane must see in each MFMA step, and bank conflicts (added to *rconf).
+// Returns 0 when valid, else a code from 30.
+template <class S>
+int layout_check_at(int banks, int64_t* rconf) {
+  static_assert(S::AT, "transposed-A shape");
+  static int m_of[S::A_STAGE], k_of[S::A_STAGE];
+  for (int i = 0; i < S::A_STAGE; ++i) m_of[i] = -1;
+  for (int i = 0; i < S::IA; ++i)
+    for (int w = 0; w < S::NW; ++w)
+      for (int l = 0; l < 64; ++l) {
+        const int off = 1024 * (i * S::NW + w) + 16 * l;
+        const int k = S::at_dl_k(i, w, l), c = S::at_dl_c(i, w, l);
+        if (k >= S::BK || S::at_byte(k, 4 * c) != off) return 30;
+        for (int e = 0; e < 4; ++e) {
+          if (m_of[off + 4 * e] != -1) return 31;
+          m_of[off + 4 * e] = 4 * c + e;
+          k_of[off + 4 * e] = k;
+        }
+      }
+  for (int i = 0; i < S::A_STAGE; i += 4)
+    if (m_of[i] < 0) return 32;
+  int addr[64];
+  for (int w = 0; w < S::NW; ++w) {
+    const int wm0 = (w / S::WAVES_N) * S::WM;
+    for (int g = 0; g < S::KG; ++g)
+      for (int st = 0; st < 4; ++st) {
+        for (int l = 0; l < 64; ++l) {
+          addr[l] = S::at_frag(wm0, 0, 0, l) + (8 * g + st) * S::A_ROW;
+          if (addr[l] != S::at_frag(wm0, g, st, l)) return 33;
+          if (addr[l] < 0 || addr[l] + 4 * S::MB > S::A_STAGE) return 34;
+          // Step st, block mb: A[m = wm0 + MB*(l%32) + mb][k = 8g + 4(l/32) + st].
+          for (int mb = 0; mb < S::MB; ++mb)
+            if (m_of[addr[l] + 4 * mb] != wm0 + S::MB * (l % 32) + mb ||
+                k_of[addr[l] + 4 * mb] != 8 * g + 4 * (l / 32) + st)
+              return 35;
+        }
+        *rconf += lds_conflicts(addr, 4 * S::MB, banks);
       }
   }
   return 0;
@@ -623,7 +725,12 @@ int layout_check(int banks, int64_t out[2]) {
       }
     }
   }
-  const int rc = layout_check_bt<Shape<S::BM, S::BN, S::WM, S::WN, S::BK, S::NS, false, true>>(banks, &rconf);
+  int rc = layout_check_bt<Shape<S::BM, S::BN, S::WM, S::WN, S::BK, S::NS, false, true>>(banks, &rconf);
+  if (rc != 0) return rc;
+  rc = layout_check_at<Shape<S::BM, S::BN, S::WM, S::WN, S::BK, S::NS, false, false, false, true>>(banks, &rconf);
+  if (rc != 0) return rc;
+  // Both transposed: B's side must not depend on A's row length.
+  rc = layout_check_bt<Shape<S::BM, S::BN, S::WM, S::WN, S::BK, S::NS, false, true, false, true>>(banks, &rconf);
   if (rc != 0) return rc;
   out[0] = 0;  // no LDS writes by the waves (copies are LDS-direct)
   out[1] = rconf;
@@ -640,7 +747,9 @@ int layout_check(int banks, int64_t out[2]) {
         &launch<Shape<BM, BN, WM, WN, BK, NS>>, EFF,                                        \
         &launch<Shape<BM, BN, WM, WN, BK, NS, true>>,                                       \
         &launch<Shape<BM, BN, WM, WN, BK, NS, false, true>>,                                \
-        &launch<Shape<BM, BN, WM, WN, BK, NS, false, false, true>>                          \
+        &launch<Shape<BM, BN, WM, WN, BK, NS, false, false, true>>,                         \
+        &launch<Shape<BM, BN, WM, WN, BK, NS, false, false, false, true>>,                  \
+        &launch<Shape<BM, BN, WM, WN, BK, NS, false, true, false, true>>                    \
   }
 
 const Variant kVariants[] = {

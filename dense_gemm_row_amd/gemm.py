@@ -39,7 +39,7 @@ ACT_NONE = 0
 ACT_RELU = 1
 
 TYPES = ("f32", "f16", "bf16", "f8")
-EXPORTS = [f"gemm_{t}{form}" for form in ("", "_ex", "_bt", "_epi", "_epi_q8", "_splitk")
+EXPORTS = [f"gemm_{t}{form}" for form in ("", "_ex", "_bt", "_trans", "_epi", "_epi_q8", "_splitk")
            for t in TYPES] + [
            "gemm_splitk_workspace_bytes", "gemm_select_splitk_config",
            "gemm_num_configs", "gemm_get_config", "gemm_select_config", "gemm_tile_of_block",
@@ -95,6 +95,9 @@ def _declare(lib):
         getattr(lib, name).restype = ctypes.c_int
     for name in [f"gemm_{t}_epi" for t in types] + [f"gemm_{t}_epi_q8" for t in types]:
         getattr(lib, name).argtypes = gemm_args + [cfgp, ctypes.POINTER(GemmEpilogue)]
+        getattr(lib, name).restype = ctypes.c_int
+    for name in (f"gemm_{t}_trans" for t in types):
+        getattr(lib, name).argtypes = gemm_args + [cfgp, i32, i32]
         getattr(lib, name).restype = ctypes.c_int
     for name in (f"gemm_{t}_splitk" for t in types):
         getattr(lib, name).argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, p, i64, p, cfgp]
@@ -266,10 +269,27 @@ gemm_bf16_epi_q8 = _q8("gemm_bf16_epi_q8")
 gemm_f8_epi_q8 = _q8("gemm_f8_epi_q8")
 
 
+def _trans(name):
+    def fn(M, N, K, A, lda, B, ldb, C, ldc, stream=None, cfg: GemmConfig | None = None,
+           trans_a: int = 0, trans_b: int = 0) -> int:
+        return getattr(lib(), name)(M, N, K, A, lda, B, ldb, C, ldc, stream,
+                                    ctypes.byref(cfg) if cfg is not None else None,
+                                    int(trans_a), int(trans_b))
+    fn.__name__ = name
+    return fn
+
+
+# C = op(A) op(B) in the four layouts.
+gemm_f32_trans = _trans("gemm_f32_trans")
+gemm_f16_trans = _trans("gemm_f16_trans")
+gemm_bf16_trans = _trans("gemm_bf16_trans")
+gemm_f8_trans = _trans("gemm_f8_trans")
+
+
 # Entry points per dtype code, for callers that dispatch on it.
 def entry(dtype: int, form: str = ""):
     """The binding of gemm_<type><form> (form "", "_ex", "_bt", "_epi",
-    "_epi_q8", "_splitk") for dtype DTYPE_F32 / DTYPE_F16 / DTYPE_BF16 / DTYPE_F8."""
+    "_epi_q8", "_trans", "_splitk") for dtype DTYPE_F32 / DTYPE_F16 / DTYPE_BF16 / DTYPE_F8."""
     name = {DTYPE_F32: "f32", DTYPE_F16: "f16", DTYPE_BF16: "bf16", DTYPE_F8: "f8"}[dtype]
     return globals()[f"gemm_{name}{form}"]
 

@@ -277,6 +277,42 @@ gemm_status_t gemm_f8_bt(int64_t M, int64_t N, int64_t K,
                          gemm_bf16_t *C, int64_t ldc, void *stream,
                          const gemm_config_t *cfg);
 
+/*
+ * GEMM in any of the four layouts: C = op(A) x op(B), op(X) = X^T when its
+ * flag is 1.  trans_a = 1: A is passed as its K x M transpose, row-major
+ * (column-major A; element (i, k) at A[k*lda + i], lda >= max(1, M));
+ * trans_b = 1: B as its N x K transpose (element (k, j) at B[j*ldb + k],
+ * ldb >= max(1, K), as gemm_*_bt).  C is M x N row-major as always.  These
+ * are the column-major operand layouts of the lqnn.cn SGEMM article
+ * (section 3.1), read directly by the matrix cores instead of transposed
+ * beforehand.  trans_a = 0 forms are the same calls as gemm_* / gemm_*_bt.
+ * trans_a = 1 runs on the LDS-direct kernels only and needs the vector
+ * layout: A, B, C 16-byte aligned; M, lda, ldb and N (K instead of N when
+ * trans_b) multiples of 16 bytes' worth of elements; ldc likewise for C;
+ * else UNSUPPORTED before any launch.  Flags other than 0 / 1 ->
+ * INVALID_ARG.  cfg NULL: the selection among the variants with the form.
+ */
+gemm_status_t gemm_f32_trans(int64_t M, int64_t N, int64_t K,
+                             const float *A, int64_t lda,
+                             const float *B, int64_t ldb,
+                             float *C, int64_t ldc, void *stream,
+                             const gemm_config_t *cfg, int32_t trans_a, int32_t trans_b);
+gemm_status_t gemm_f16_trans(int64_t M, int64_t N, int64_t K,
+                             const gemm_f16_t *A, int64_t lda,
+                             const gemm_f16_t *B, int64_t ldb,
+                             gemm_f16_t *C, int64_t ldc, void *stream,
+                             const gemm_config_t *cfg, int32_t trans_a, int32_t trans_b);
+gemm_status_t gemm_bf16_trans(int64_t M, int64_t N, int64_t K,
+                              const gemm_bf16_t *A, int64_t lda,
+                              const gemm_bf16_t *B, int64_t ldb,
+                              gemm_bf16_t *C, int64_t ldc, void *stream,
+                              const gemm_config_t *cfg, int32_t trans_a, int32_t trans_b);
+gemm_status_t gemm_f8_trans(int64_t M, int64_t N, int64_t K,
+                            const gemm_f8_t *A, int64_t lda,
+                            const gemm_f8_t *B, int64_t ldb,
+                            gemm_bf16_t *C, int64_t ldc, void *stream,
+                            const gemm_config_t *cfg, int32_t trans_a, int32_t trans_b);
+
 /* Activation applied by the fused epilogue. */
 typedef enum gemm_act {
     GEMM_ACT_NONE = 0,

@@ -104,7 +104,7 @@ WS_GUARD = 256  # canary floats on each side of a split-K workspace
 
 
 def run(A: np.ndarray, B: np.ndarray, cfg=None, pad=(0, 0, 0), offset=(0, 0, 0),
-        repeat: int = 1, split=None, epi=None, bt: bool = False):
+        repeat: int = 1, split=None, epi=None, bt: bool = False, at: bool = False):
     """Compute A @ B through libgemm.  Returns (C as numpy, C DevMatrix).
 
     split: None for the plain entry points; "auto" for gemm_*_splitk with
@@ -118,13 +118,16 @@ def run(A: np.ndarray, B: np.ndarray, cfg=None, pad=(0, 0, 0), offset=(0, 0, 0),
     (None: the library's choice).
 
     bt: B is given transposed (the argument is Bt, N x K) and the call is
-    gemm_*_bt; A @ Bt.T is computed."""
+    gemm_*_bt; A @ Bt.T is computed.
+
+    at: A is given transposed (the argument is At, K x M) and the call is
+    gemm_*_trans with trans_a = 1 (and trans_b = bt)."""
     kind = kind_of(A)
     ckind = oracle.out_kind(kind)  # FP8 products are BF16
     dtype = DTYPE[kind]
-    M, K = A.shape
+    K, M = A.shape if at else A.shape[::-1]
     N = B.shape[0] if bt else B.shape[1]
-    dA = DevMatrix(A, M, K, kind, pad=pad[0], offset=offset[0])
+    dA = DevMatrix(A, *((K, M) if at else (M, K)), kind, pad=pad[0], offset=offset[0])
     dB = DevMatrix(B, *((N, K) if bt else (K, N)), kind, pad=pad[1], offset=offset[1])
     dC = DevMatrix(None if epi is None else epi.get("C0"), M, N, ckind, pad=pad[2], offset=offset[2])
     bias_dev, epi_s = None, None
@@ -147,7 +150,9 @@ def run(A: np.ndarray, B: np.ndarray, cfg=None, pad=(0, 0, 0), offset=(0, 0, 0),
         ws = torch.from_numpy(host.view(np.int32)).to("cuda")
     for _ in range(repeat):
         args = (M, N, K, dA.ptr, dA.ld, dB.ptr, dB.ld, dC.ptr, dC.ld)
-        if bt:
+        if at:
+            st = gemm.entry(dtype, "_trans")(*args, stream, cfg, 1, int(bt))
+        elif bt:
             st = gemm.entry(dtype, "_bt")(*args, stream, cfg)
         elif epi is not None:
             st = gemm.entry(dtype, "_epi")(*args, stream, cfg, epi_s)

@@ -362,3 +362,27 @@ def test_q8_argument_validation(fn):
             assert fn(*base[:-1], None, c, ok) == gemm.GEMM_ERR_UNSUPPORTED, c.name
     assert fn(64, 64, 64, PA, 64, PB, 64, PC, 72, None, None, ok) == gemm.GEMM_ERR_UNSUPPORTED  # ldq % 16
     assert fn(0, 64, 64, PA, 64, PB, 64, 0, 64, None, None, ok) == gemm.GEMM_OK
+
+
+@pytest.mark.parametrize("fn", [gemm.gemm_f32_trans, gemm.gemm_f16_trans, gemm.gemm_bf16_trans,
+                                gemm.gemm_f8_trans])
+def test_trans_argument_validation(fn):
+    """Transposed layouts: flags 0/1 only; with A transposed lda is checked
+    against M and the alias check covers A^T's K x M span; variants without
+    the form are refused when forced; off-layout operands are refused; all
+    before any launch."""
+    dt = _dtype_of(fn)
+    # M=32, N=64, K=128: with trans_a, lda >= 32 suffices; without, >= 128.
+    assert fn(32, 64, 128, PA, 32, PB, 64, PC, 64, None, None, 2, 0) == gemm.GEMM_ERR_INVALID_ARG
+    assert fn(32, 64, 128, PA, 31, PB, 64, PC, 64, None, None, 1, 0) == gemm.GEMM_ERR_INVALID_ARG
+    assert fn(32, 64, 128, PA, 32, PB, 64, PC, 64, None, None, 0, 0) == gemm.GEMM_ERR_INVALID_ARG
+    es = {gemm.DTYPE_F32: 4, gemm.DTYPE_F16: 2, gemm.DTYPE_BF16: 2, gemm.DTYPE_F8: 1}[dt]
+    # C starting inside A^T's last row (127 rows of 32 plus 32) aliases.
+    assert fn(32, 64, 128, PA, 32, PB, 64, PA + (127 * 32 + 16) * es, 64, None, None, 1, 0) == \
+        gemm.GEMM_ERR_ALIAS
+    for c in gemm.configs(dt):
+        if not c.name.decode().startswith(("dl_", "tr_")):
+            assert fn(32, 64, 128, PA, 32, PB, 64, PC, 64, None, c, 1, 0) == gemm.GEMM_ERR_UNSUPPORTED
+    # M = 34 is off the vector layout for every element size.
+    assert fn(34, 64, 128, PA, 34, PB, 128, PC, 64, None, None, 1, 1) == gemm.GEMM_ERR_UNSUPPORTED
+    assert fn(0, 64, 128, PA, 32, PB, 128, 0, 64, None, None, 1, 1) == gemm.GEMM_OK
