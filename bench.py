@@ -57,6 +57,9 @@ def parse_args():
     ap.add_argument("--bt", action="store_true",
                     help="time the transposed-B entry points instead: B held as its N x K "
                          "transpose (column-major B)")
+    ap.add_argument("--at", action="store_true",
+                    help="A held as its K x M transpose (column-major A), through gemm_*_trans; "
+                         "with --bt both are transposed")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="before the steps, run a plain device copy of this many MiB (read N, "
                          "write N) three times: the reference kernel that scales HBM counters")
@@ -158,13 +161,15 @@ def main():
             return t.view(torch.int16).cpu().numpy().view(np.uint16).view(synth.BF16)
         return t.cpu().numpy()
     devbuf = {}
-    if args.bt and args.epilogue:
-        print("--bt and --epilogue are separate modes", file=sys.stderr)
+    if (args.bt or args.at) and args.epilogue:
+        print("--bt / --at and --epilogue are separate modes", file=sys.stderr)
         sys.exit(2)
     for k in kinds:
         A, B = host[k]
         if args.bt:
             B = np.ascontiguousarray(B.T)
+        if args.at:
+            A = np.ascontiguousarray(A.T)
         devbuf[k] = (to_dev(A), to_dev(B),
                      torch.empty((n, n), dtype=tdt[k], device=dev))
     cfgs = {}
@@ -197,6 +202,8 @@ def main():
         args3 = (n, n, n, a.data_ptr(), n, b.data_ptr(), n, c.data_ptr(), n, sptr, cfgs[k])
         if epi is not None:
             st = gemm.entry(dcode[k], "_epi")(*args3, epi)
+        elif args.at:
+            st = gemm.entry(dcode[k], "_trans")(*args3, 1, int(args.bt))
         elif args.bt:
             st = gemm.entry(dcode[k], "_bt")(*args3)
         else:
@@ -244,6 +251,14 @@ def main():
                              "max_rel": rep["max_rel"], "ok": rep["ok"]}
                 continue
             tol = oracle.TOL[k]
+            if args.at:
+                ref, den = oracle.gemm_rows_trans(np.ascontiguousarray(A.T),
+                                                  np.ascontiguousarray(B.T) if args.bt else B,
+                                                  True, args.bt, rows=rows)
+                rep = oracle.check(np.ascontiguousarray(C[rows]), ref, den, tol)
+                parity[k] = {"rows": len(rows), "entries": 0, "tol": tol,
+                             "max_rel": rep["max_rel"], "ok": rep["ok"]}
+                continue
             if args.bt:
                 ref, den = oracle.gemm_rows_bt(A, np.ascontiguousarray(B.T), rows=rows)
                 rep = oracle.check(np.ascontiguousarray(C[rows]), ref, den, tol)
@@ -303,7 +318,7 @@ def main():
         kk = kernels[k]
         achieved = flops / (kk["ms_mean"] * 1e-3) / 1e12
         # The counters were taken on the plain kernels.
-        traffic = None if epi is not None or args.bt else load_traffic(kk["variant"], n)
+        traffic = None if epi is not None or args.bt or args.at else load_traffic(kk["variant"], n)
         return {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS[k],
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS[k], 4),
                 "traffic": traffic, "traffic_unit": "bytes/launch", "kernel": kk["variant"],
@@ -353,6 +368,7 @@ def main():
         "config": {"workload": f"{WORKLOAD_NAME.get(tuple(kinds), '+'.join(kinds) + ' gemm')} "
                                f"{n}x{n}x{n} row-major, uniform[-1,1) seed 0"
                                + (", fused epilogue relu(AB + C + bias)" if epi is not None else "")
+                               + (", A given transposed (K x M)" if args.at else "")
                                + (", B given transposed (N x K)" if args.bt else ""),
                    "M": n, "N": n, "K": n, "step": " then ".join(STEP_NAME[k] for k in kinds)},
         "kernels": kernels,
