@@ -99,11 +99,19 @@ __device__ __forceinline__ void static_for(F&& f, std::integer_sequence<int, I..
 // E4M3 in and bfloat16 out.  AT_: A given transposed (At, K x M row-major,
 // i.e. column-major A): its tile is staged and read exactly like B's (k
 // rows of BM values, chunk XOR by k, transpose reads), which hands each
-// lane the same k run of its row as the direct read of row-major A.
+// lane the same k run of its row as the direct read of row-major A.  PW_:
+// producer waves (0: none).  With PW_ > 0 the workgroup is split by role:
+// the NW compute waves only read LDS and run MFMAs, and PW_ further waves
+// only issue the LDS-direct copies and wait for them to land; both meet at
+// the one barrier per K slice.  This is the load/compute separation that
+// "hgemm_naive_kernel explained" lists among its further directions
+// (section 10.3), with LDS-direct copies in the role that "nxbn.cn GB300
+// GEMM" (section 3.2) gives to a copy engine driven by a few threads.
 template <int BM_, int BN_, int WM_, int WN_, int BK_, int NS_, int MODE_ = 0, bool BT_ = false,
-          int TY_ = 0, bool AT_ = false>
+          int TY_ = 0, bool AT_ = false, int PW_ = 0>
 struct Shape {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BK_, NS = NS_, TY = TY_;
+  static constexpr int PW = PW_;
   static constexpr bool AT = AT_;
   static constexpr bool PARTIAL = MODE_ == 1, EPI = MODE_ == 2 || MODE_ == 3, Q8 = MODE_ == 3, BT = BT_;
   static constexpr bool BF = TY != 0;   // C (and the epilogue's old C) is bfloat16
@@ -115,7 +123,8 @@ struct Shape {
   static constexpr int TRN = F8 ? 4 : 2;   // transpose reads per B operand
   static constexpr int RR = F8 ? 8 : 4;    // k rows (elements per lane) of one transpose read
   static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN, NW = WAVES_M * WAVES_N;
-  static constexpr int NT = NW * 64;
+  // NL waves issue the copies: the producers, or every wave.
+  static constexpr int NL = PW > 0 ? PW : NW, NT = (NW + PW) * 64;
   static constexpr int MB = WM / 32, NB = WN / 32, KS = BK / KW;
   static constexpr int NMMA_ = MB * NB;  // MFMAs per k step
   // A rows: BM rows of BK k values, or (AT) BK rows of BM values.
@@ -124,11 +133,12 @@ struct Shape {
   static constexpr int B_ROW = BT ? BK * ES : BN * ES, B_CPR = B_ROW / 16;  // bytes / chunks
   static constexpr int A_STAGE = AT ? BK * A_ROW : BM * A_ROW, B_STAGE = BT ? BN * B_ROW : BK * B_ROW;
   static constexpr int LDS_BYTES = NS * (A_STAGE + B_STAGE);
-  static constexpr int IA = A_STAGE / 1024 / NW, IB = B_STAGE / 1024 / NW, LPS = IA + IB;
+  static constexpr int IA = A_STAGE / 1024 / NL, IB = B_STAGE / 1024 / NL, LPS = IA + IB;
   // With three or more stages a slice's copies are spread over the k steps
   // of the slice before (PP per step); with two they go out in one burst
   // after the barrier that frees their stage.
-  static constexpr bool SPREAD = NS >= 3;
+  // (Producer waves have nothing else to do: they issue in bursts.)
+  static constexpr bool SPREAD = NS >= 3 && PW == 0;
   static constexpr int PP = LPS / KS;
   // Epilogue: wave w stages its tile in P of the 2*NS stage arrays
   // (A arrays first), RPA rows per array.
@@ -144,7 +154,10 @@ struct Shape {
   static_assert(NS >= 2 && NS <= MAX_STAGES, "stages");
   static_assert(BM % WM == 0 && BN % WN == 0, "wave grid");
   static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile");
-  static_assert(A_STAGE % (1024 * NW) == 0 && B_STAGE % (1024 * NW) == 0, "direct-load split");
+  static_assert(A_STAGE % (1024 * NL) == 0 && B_STAGE % (1024 * NL) == 0, "direct-load split");
+  // A compute wave and a producer wave share a SIMD, so the compute waves
+  // must fit half of its 512 registers: wave tiles of at most 128 x 64.
+  static_assert(PW == 0 || (WM * WN <= 128 * 64 && NW == 4 && PW <= 4), "producer waves");
   static_assert(BT || B_CPR >= 16, "B rows of at least 256 bytes (the k%4 chunk XOR)");
   static_assert(!AT || A_CPR >= 16, "A^T rows of at least 256 bytes (the chunk XOR)");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
@@ -170,18 +183,18 @@ struct Shape {
   __host__ __device__ static constexpr int b_byte(int k, int n) {
     return k * B_ROW + 16 * b_phys(k, n / CE) + ES * (n % CE);
   }
-  // Direct loads: lane l of wave w, instruction i.
+  // Direct loads: lane l of loading wave w, instruction i.
   __host__ __device__ static constexpr int a_dl_row(int i, int w, int l) {
-    return (1024 / A_ROW) * (i * NW + w) + l / A_CPR;
+    return (1024 / A_ROW) * (i * NL + w) + l / A_CPR;
   }
   __host__ __device__ static constexpr int a_dl_q(int i, int w, int l) {
     return (l % A_CPR) ^ swz_row(a_dl_row(i, w, l), A_ROW);
   }
   __host__ __device__ static constexpr int b_dl_k(int i, int w, int l) {
-    return (1024 * (i * NW + w) + 16 * l) / B_ROW;
+    return (1024 * (i * NL + w) + 16 * l) / B_ROW;
   }
   __host__ __device__ static constexpr int b_dl_c(int i, int w, int l) {
-    return ((1024 * (i * NW + w) + 16 * l) % B_ROW / 16) ^ b_swz(b_dl_k(i, w, l));
+    return ((1024 * (i * NL + w) + 16 * l) % B_ROW / 16) ^ b_swz(b_dl_k(i, w, l));
   }
   // Fragment reads for k step j of a slice.  Lane l's operand holds k
   // KW*j + (KW/2)*(l/32) + 0 .. KW/2-1 (any k order common to both operands
@@ -205,10 +218,10 @@ struct Shape {
     return k * A_ROW + 16 * b_phys(k, m / CE) + ES * (m % CE);
   }
   __host__ __device__ static constexpr int at_dl_k(int i, int w, int l) {
-    return (1024 * (i * NW + w) + 16 * l) / A_ROW;
+    return (1024 * (i * NL + w) + 16 * l) / A_ROW;
   }
   __host__ __device__ static constexpr int at_dl_c(int i, int w, int l) {
-    return ((1024 * (i * NW + w) + 16 * l) % A_ROW / 16) ^ b_swz(at_dl_k(i, w, l));
+    return ((1024 * (i * NL + w) + 16 * l) % A_ROW / 16) ^ b_swz(at_dl_k(i, w, l));
   }
   __host__ __device__ static constexpr int at_frag(int wm0, int mb, int j, int jr, int l) {
     return at_byte(KW * j + (KW / 2) * (l / 32) + RR * jr + (l % 16) / (16 / RR),
@@ -217,7 +230,7 @@ struct Shape {
   // BT direct loads: Bt rows (B_ROW bytes) placed like row-major A's rows,
   // by B's own row length (with A transposed the two differ).
   __host__ __device__ static constexpr int bt_dl_row(int i, int w, int l) {
-    return (1024 / B_ROW) * (i * NW + w) + l / (B_ROW / 16);
+    return (1024 / B_ROW) * (i * NL + w) + l / (B_ROW / 16);
   }
   __host__ __device__ static constexpr int bt_dl_q(int i, int w, int l) {
     return (l % (B_ROW / 16)) ^ swz_row(bt_dl_row(i, w, l), B_ROW);
@@ -300,10 +313,10 @@ __device__ __forceinline__ void issue_slice(const unsigned char* Ab, const unsig
 #pragma unroll
   for (int q = Q0; q < Q1; ++q) {
     if (q < S::IA) {
-      lds_void* dst = (lds_void*)(lds_a + 1024 * (q * S::NW + wave));
+      lds_void* dst = (lds_void*)(lds_a + 1024 * (q * S::NL + wave));
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, dst, 16, a_vo[q], 0, 0, 0);
     } else {
-      lds_void* dst = (lds_void*)(lds_b + 1024 * ((q - S::IA) * S::NW + wave));
+      lds_void* dst = (lds_void*)(lds_b + 1024 * ((q - S::IA) * S::NL + wave));
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, dst, 16, b_vo[q - S::IA], 0, 0, 0);
     }
   }
@@ -365,6 +378,9 @@ hgemm_tr_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
   const int l = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm0 = (wave / S::WAVES_N) * WM, wn0 = (wave % S::WAVES_N) * WN;
+  // This wave's index among the waves that issue copies (producer waves
+  // follow the NW compute waves).
+  const int lw = S::PW > 0 ? wave - S::NW : wave;
   const int T = (K + BK - 1) / BK;
 
   // Direct-load offsets (relative to the slice's descriptor base).
@@ -372,12 +388,12 @@ hgemm_tr_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
 #pragma unroll
   for (int i = 0; i < IA; ++i) {
     if constexpr (S::AT) {
-      const int k = S::at_dl_k(i, wave, l), c = S::at_dl_c(i, wave, l);
+      const int k = S::at_dl_k(i, lw, l), c = S::at_dl_c(i, lw, l);
       const bool ok = (m0 + S::CE * c) < M;
       a_vo[i] = ok ? (unsigned)S::ES * ((unsigned)k * (unsigned)lda + (unsigned)(m0 + S::CE * c)) : OOB;
       a_vo_tail[i] = a_vo[i];  // rows past K are past the buffer's range
     } else {
-      const int r = S::a_dl_row(i, wave, l), q = S::a_dl_q(i, wave, l);
+      const int r = S::a_dl_row(i, lw, l), q = S::a_dl_q(i, lw, l);
       const bool ok = (m0 + r) < M;
       a_vo[i] = ok ? (unsigned)S::ES * ((unsigned)(m0 + r) * (unsigned)lda + (unsigned)S::CE * q) : OOB;
       a_vo_tail[i] = ((T - 1) * BK + S::CE * q < K) ? a_vo[i] : OOB;
@@ -387,12 +403,12 @@ hgemm_tr_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
   for (int i = 0; i < IB; ++i) {
     if constexpr (S::BT) {
       // Bt row n0 + r (output column), k chunk q: row-major A's placement.
-      const int r = S::bt_dl_row(i, wave, l), q = S::bt_dl_q(i, wave, l);
+      const int r = S::bt_dl_row(i, lw, l), q = S::bt_dl_q(i, lw, l);
       const bool ok = (n0 + r) < N;
       b_vo[i] = ok ? (unsigned)S::ES * ((unsigned)(n0 + r) * (unsigned)ldb + (unsigned)S::CE * q) : OOB;
       b_vo_tail[i] = ((T - 1) * BK + S::CE * q < K) ? b_vo[i] : OOB;
     } else {
-      const int k = S::b_dl_k(i, wave, l), c = S::b_dl_c(i, wave, l);
+      const int k = S::b_dl_k(i, lw, l), c = S::b_dl_c(i, lw, l);
       const bool ok = (n0 + S::CE * c) < N;
       b_vo[i] = ok ? (unsigned)S::ES * ((unsigned)k * (unsigned)ldb + (unsigned)(n0 + S::CE * c)) : OOB;
       b_vo_tail[i] = b_vo[i];  // rows past K are past the buffer's range
@@ -421,16 +437,55 @@ hgemm_tr_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
     for (int nb = 0; nb < NB; ++nb) b_fb[nb] = S::b_frag(wn0, nb, 0, 0, l);
   }
 
-  auto issue = [&](int s, unsigned char* la, unsigned char* lb) __attribute__((always_inline)) {
+  // Slice s's copies into one stage (all of them; with producer waves, the
+  // producer's share).
+  auto produce = [&](int s, unsigned char* la, unsigned char* lb) __attribute__((always_inline)) {
     issue_slice<S>(Ab, Bb, a_bytes, b_bytes, s, s < T, s == T - 1 ? a_vo_tail : a_vo,
-                   s == T - 1 ? b_vo_tail : b_vo, la, lb, wave, lda, ldb);
+                   s == T - 1 ? b_vo_tail : b_vo, la, lb, lw, lda, ldb);
+  };
+  if constexpr (S::PW > 0) {
+    if (wave >= S::NW) {
+      // Producer wave: the compute waves' schedule of copies and barriers
+      // (one barrier before the loop, one per slice, then the epilogue's),
+      // without their LDS reads and MFMAs.  All NS stages are filled first;
+      // the barrier that ends slice t's reads (once slice t+1 has landed)
+      // frees stage t % NS for slice t + NS.
+      if (T > 0) {
+        static_for([&](auto I) { produce(decltype(I)::value, A_of(I), B_of(I)); },
+                   std::make_integer_sequence<int, NS>{});
+        loop_barrier<(NS - 1) * S::LPS>();  // slice 0 landed
+        int t = 0;
+        for (; t + NS <= T; t += NS)
+          static_for([&](auto I) {
+            loop_barrier<(NS - 2) * S::LPS>();  // slice t+I+1 landed, stage I read
+            produce(t + decltype(I)::value + NS, A_of(I), B_of(I));
+          }, std::make_integer_sequence<int, NS>{});
+        static_for([&](auto I) {
+          if (t + decltype(I)::value < T) {
+            loop_barrier<(NS - 2) * S::LPS>();
+            produce(t + decltype(I)::value + NS, A_of(I), B_of(I));
+          }
+        }, std::make_integer_sequence<int, NS>{});
+        // Every copy (the zero-filled ones past T included) lands before
+        // the epilogue reuses the stages.
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+      }
+      if constexpr (!S::PARTIAL) __syncthreads();
+      if constexpr (!S::PARTIAL && !S::EPI) __syncthreads();
+      return;
+    }
+  }
+  // The compute waves' own copies (none when producer waves issue them).
+  auto issue = [&](int s, unsigned char* la, unsigned char* lb) __attribute__((always_inline)) {
+    if constexpr (S::PW == 0) produce(s, la, lb);
   };
   // Part j (of KS) of slice s's copies.
   auto issue_part = [&](int s, auto J, unsigned char* la, unsigned char* lb) __attribute__((always_inline)) {
     constexpr int j = decltype(J)::value;
-    issue_slice<S, j * S::PP, (j + 1) * S::PP>(Ab, Bb, a_bytes, b_bytes, s, s < T,
-                                               s == T - 1 ? a_vo_tail : a_vo,
-                                               s == T - 1 ? b_vo_tail : b_vo, la, lb, wave, lda, ldb);
+    if constexpr (S::PW == 0)
+      issue_slice<S, j * S::PP, (j + 1) * S::PP>(Ab, Bb, a_bytes, b_bytes, s, s < T,
+                                                 s == T - 1 ? a_vo_tail : a_vo,
+                                                 s == T - 1 ? b_vo_tail : b_vo, la, lb, wave, lda, ldb);
   };
 
   // An operand: 8 16-bit or 32 8-bit values per lane.
@@ -561,7 +616,7 @@ hgemm_tr_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
       if constexpr (S::SPREAD) {
         if (S::copy_slot(i)) SGB(SG_VMEM_RD, 1);
       } else {
-        if (i < S::LPS) SGB(SG_VMEM_RD, 1);
+        if (S::PW == 0 && i < S::LPS) SGB(SG_VMEM_RD, 1);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -783,9 +838,9 @@ int layout_check_bt(int banks, int64_t* rconf) {
   static int n_of[S::B_STAGE], k_of[S::B_STAGE];
   for (int i = 0; i < S::B_STAGE; ++i) n_of[i] = -1;
   for (int i = 0; i < S::IB; ++i)
-    for (int w = 0; w < S::NW; ++w)
+    for (int w = 0; w < S::NL; ++w)
       for (int l = 0; l < 64; ++l) {
-        const int off = 1024 * (i * S::NW + w) + 16 * l;
+        const int off = 1024 * (i * S::NL + w) + 16 * l;
         const int r = S::bt_dl_row(i, w, l), q = S::bt_dl_q(i, w, l);
         if (r >= S::BN || q >= S::B_CPR || S::bt_byte(r, q) != off) return 20;
         for (int e = 0; e < S::CE; ++e) {
@@ -830,9 +885,9 @@ int layout_check_at(int banks, int64_t* rconf) {
   static int m_of[S::A_STAGE], k_of[S::A_STAGE];
   for (int i = 0; i < S::A_STAGE; ++i) m_of[i] = -1;
   for (int i = 0; i < S::IA; ++i)
-    for (int w = 0; w < S::NW; ++w)
+    for (int w = 0; w < S::NL; ++w)
       for (int l = 0; l < 64; ++l) {
-        const int off = 1024 * (i * S::NW + w) + 16 * l;
+        const int off = 1024 * (i * S::NL + w) + 16 * l;
         const int k = S::at_dl_k(i, w, l), c = S::at_dl_c(i, w, l);
         if (k >= S::BK || c >= S::A_CPR || S::at_byte(k, S::CE * c) != off) return 40;
         for (int e = 0; e < S::CE; ++e) {
@@ -884,9 +939,9 @@ int layout_check(int banks, int64_t out[2]) {
   for (int i = 0; i < S::A_STAGE; ++i) a_row_of[i] = -1;
   for (int i = 0; i < S::B_STAGE; ++i) b_k_of[i] = -1;
   for (int i = 0; i < S::IA; ++i)
-    for (int w = 0; w < S::NW; ++w)
+    for (int w = 0; w < S::NL; ++w)
       for (int l = 0; l < 64; ++l) {
-        const int off = 1024 * (i * S::NW + w) + 16 * l;
+        const int off = 1024 * (i * S::NL + w) + 16 * l;
         const int r = S::a_dl_row(i, w, l), q = S::a_dl_q(i, w, l);
         if (r >= BM || q >= S::A_CPR || S::a_byte(r, q) != off) return 1;
         for (int e = 0; e < S::CE; ++e) {
@@ -896,9 +951,9 @@ int layout_check(int banks, int64_t out[2]) {
         }
       }
   for (int i = 0; i < S::IB; ++i)
-    for (int w = 0; w < S::NW; ++w)
+    for (int w = 0; w < S::NL; ++w)
       for (int l = 0; l < 64; ++l) {
-        const int off = 1024 * (i * S::NW + w) + 16 * l;
+        const int off = 1024 * (i * S::NL + w) + 16 * l;
         const int k = S::b_dl_k(i, w, l), c = S::b_dl_c(i, w, l);
         if (k >= BK || c >= S::B_CPR || S::b_byte(k, S::CE * c) != off) return 3;
         for (int e = 0; e < S::CE; ++e) {
@@ -1027,13 +1082,16 @@ int layout_check(int banks, int64_t out[2]) {
       rconf += lds_conflicts(addr, 16, banks);
     }
   }
-  int rc = layout_check_bt<Shape<S::BM, S::BN, S::WM, S::WN, S::BK, S::NS, 0, true, S::TY>>(banks, &rconf);
+  int rc = layout_check_bt<Shape<S::BM, S::BN, S::WM, S::WN, S::BK, S::NS, 0, true, S::TY, false, S::PW>>(
+      banks, &rconf);
   if (rc != 0) return rc;
   if constexpr (S::BM * S::ES >= 256) {
-    rc = layout_check_at<Shape<S::BM, S::BN, S::WM, S::WN, S::BK, S::NS, 0, false, S::TY, true>>(banks, &rconf);
+    rc = layout_check_at<Shape<S::BM, S::BN, S::WM, S::WN, S::BK, S::NS, 0, false, S::TY, true, S::PW>>(
+        banks, &rconf);
     if (rc != 0) return rc;
     // Both transposed: B's side must not depend on A's row length.
-    rc = layout_check_bt<Shape<S::BM, S::BN, S::WM, S::WN, S::BK, S::NS, 0, true, S::TY, true>>(banks, &rconf);
+    rc = layout_check_bt<Shape<S::BM, S::BN, S::WM, S::WN, S::BK, S::NS, 0, true, S::TY, true, S::PW>>(
+        banks, &rconf);
     if (rc != 0) return rc;
   }
   out[0] = wconf;
@@ -1043,30 +1101,33 @@ int layout_check(int banks, int64_t out[2]) {
 
 // The transposed-A launches, for tiles whose A^T rows (BM values) span the
 // 256 bytes the chunk XOR needs; none otherwise.
-template <int BM, int BN, int WM, int WN, int BK, int NS, int TY, bool BT>
+template <int BM, int BN, int WM, int WN, int BK, int NS, int TY, bool BT, int PW>
 constexpr LaunchFn at_launch() {
   if constexpr (BM * (TY == 2 ? 1 : 2) >= 256)
-    return &launch<Shape<BM, BN, WM, WN, BK, NS, 0, BT, TY, true>>;
+    return &launch<Shape<BM, BN, WM, WN, BK, NS, 0, BT, TY, true, PW>>;
   else
     return nullptr;
 }
 
-#define HGEMM_TR_VARIANT(TY, DT, TAG, BM, BN, WM, WN, BK, NS, EFF)                               \
+// PW producer waves (0: none); their count is the name's _p suffix.
+#define HGEMM_TR_VARIANT_PW(TY, DT, TAG, BM, BN, WM, WN, BK, NS, PW, SFX, EFF)                   \
   Variant {                                                                                  \
     gemm_config_t{0, DT, GEMM_FAMILY_MFMA, BM, BN, BK, WM, WN,                               \
-                  Shape<BM, BN, WM, WN, BK, NS, 0, false, TY>::NT, NS,                       \
-                  Shape<BM, BN, WM, WN, BK, NS, 0, false, TY>::LDS_BYTES,                    \
+                  Shape<BM, BN, WM, WN, BK, NS, 0, false, TY, false, PW>::NT, NS,            \
+                  Shape<BM, BN, WM, WN, BK, NS, 0, false, TY, false, PW>::LDS_BYTES,         \
                   GEMM_ORDER_XCD, 4, 1,                                                      \
-                  "tr_" TAG "_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_s" #NS},              \
-        &launch<Shape<BM, BN, WM, WN, BK, NS, 0, false, TY>>,                                \
-        &layout_check<Shape<BM, BN, WM, WN, BK, NS, 0, false, TY>>,                          \
-        &launch<Shape<BM, BN, WM, WN, BK, NS, 1, false, TY>>, EFF,                           \
-        &launch<Shape<BM, BN, WM, WN, BK, NS, 2, false, TY>>,                                \
-        &launch<Shape<BM, BN, WM, WN, BK, NS, 0, true, TY>>,                                 \
-        &launch<Shape<BM, BN, WM, WN, BK, NS, 3, false, TY>>,                                \
-        at_launch<BM, BN, WM, WN, BK, NS, TY, false>(),                                      \
-        at_launch<BM, BN, WM, WN, BK, NS, TY, true>()                                        \
+                  "tr_" TAG "_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_s" #NS SFX},          \
+        &launch<Shape<BM, BN, WM, WN, BK, NS, 0, false, TY, false, PW>>,                     \
+        &layout_check<Shape<BM, BN, WM, WN, BK, NS, 0, false, TY, false, PW>>,               \
+        &launch<Shape<BM, BN, WM, WN, BK, NS, 1, false, TY, false, PW>>, EFF,                \
+        &launch<Shape<BM, BN, WM, WN, BK, NS, 2, false, TY, false, PW>>,                     \
+        &launch<Shape<BM, BN, WM, WN, BK, NS, 0, true, TY, false, PW>>,                      \
+        &launch<Shape<BM, BN, WM, WN, BK, NS, 3, false, TY, false, PW>>,                     \
+        at_launch<BM, BN, WM, WN, BK, NS, TY, false, PW>(),                                  \
+        at_launch<BM, BN, WM, WN, BK, NS, TY, true, PW>()                                    \
   }
+#define HGEMM_TR_VARIANT(TY, DT, TAG, BM, BN, WM, WN, BK, NS, EFF) \
+  HGEMM_TR_VARIANT_PW(TY, DT, TAG, BM, BN, WM, WN, BK, NS, 0, "", EFF)
 
 // The 16-bit LDS layouts and data path do not depend on the element type,
 // so FP16 and BF16 share the tiles and the measured tile efficiencies.  FP8
@@ -1078,7 +1139,9 @@ constexpr LaunchFn at_launch() {
    HGEMM_TR_VARIANT(TY, DT, TAG, 256, 256, 128, 128, 32, 5, 0.99f), \
    HGEMM_TR_VARIANT(TY, DT, TAG, 256, 128, 128, 64, 64, 3, 0.90f),  \
    HGEMM_TR_VARIANT(TY, DT, TAG, 128, 256, 64, 128, 64, 3, 0.89f),  \
-   HGEMM_TR_VARIANT(TY, DT, TAG, 128, 128, 64, 64, 64, 2, 0.71f)}
+   HGEMM_TR_VARIANT(TY, DT, TAG, 128, 128, 64, 64, 64, 2, 0.71f),                 \
+   HGEMM_TR_VARIANT_PW(TY, DT, TAG, 256, 128, 128, 64, 64, 3, 4, "_p4", 0.895f),   \
+   HGEMM_TR_VARIANT_PW(TY, DT, TAG, 256, 128, 128, 64, 64, 3, 2, "_p2", 0.89f)}
 
 const Variant kVariants[] = HGEMM_TR_TABLE(0, GEMM_DTYPE_F16, "f16");
 const Variant kVariantsBf[] = HGEMM_TR_TABLE(1, GEMM_DTYPE_BF16, "bf16");
@@ -1086,6 +1149,7 @@ const Variant kVariantsF8[] = {
     HGEMM_TR_VARIANT(2, GEMM_DTYPE_F8, "f8", 256, 256, 128, 128, 128, 2, 1.00f),
     HGEMM_TR_VARIANT(2, GEMM_DTYPE_F8, "f8", 256, 256, 128, 128, 64, 4, 0.85f),
     HGEMM_TR_VARIANT(2, GEMM_DTYPE_F8, "f8", 128, 256, 64, 128, 128, 3, 0.89f),
+    HGEMM_TR_VARIANT_PW(2, GEMM_DTYPE_F8, "f8", 128, 256, 64, 128, 128, 3, 4, "_p4", 0.88f),
 };
 
 }  // namespace
