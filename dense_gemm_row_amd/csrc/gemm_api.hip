@@ -57,19 +57,26 @@ gemm_status_t fail(gemm_status_t st, const char* fmt, ...) {
   return st;
 }
 
-constexpr int kDtypes = 4;  // F32, F16, BF16, F8 (E4M3 in, BF16 out)
+// F32, F16, BF16, F8 (E4M3 in, BF16 out), E5M2 (E5M2 in, BF16 out)
+constexpr int kDtypes = 5;
 
-bool valid_dtype(int d) { return d >= GEMM_DTYPE_F32 && d <= GEMM_DTYPE_F8; }
+bool valid_dtype(int d) { return d >= GEMM_DTYPE_F32 && d <= GEMM_DTYPE_E5M2; }
+// Either 8-bit input type.
+bool is_f8(int d) { return d == GEMM_DTYPE_F8 || d == GEMM_DTYPE_E5M2; }
 
 const char* dtype_name(int d) {
-  return d == GEMM_DTYPE_F32 ? "f32" : d == GEMM_DTYPE_F16 ? "f16" : d == GEMM_DTYPE_BF16 ? "bf16" : "f8";
+  return d == GEMM_DTYPE_F32    ? "f32"
+         : d == GEMM_DTYPE_F16  ? "f16"
+         : d == GEMM_DTYPE_BF16 ? "bf16"
+         : d == GEMM_DTYPE_F8   ? "f8"
+                                : "e5m2";
 }
 
 // Bytes of one A / B element and of one C element.
-size_t in_bytes(int d) { return d == GEMM_DTYPE_F32 ? 4 : d == GEMM_DTYPE_F8 ? 1 : 2; }
+size_t in_bytes(int d) { return d == GEMM_DTYPE_F32 ? 4 : is_f8(d) ? 1 : 2; }
 size_t out_bytes(int d) { return d == GEMM_DTYPE_F32 ? 4 : 2; }
 // The type of C (the split-K reduction writes it).
-int out_dtype(int d) { return d == GEMM_DTYPE_F8 ? GEMM_DTYPE_BF16 : d; }
+int out_dtype(int d) { return is_f8(d) ? GEMM_DTYPE_BF16 : d; }
 
 struct Table {
   std::vector<Variant> v[kDtypes];  // per dtype
@@ -93,6 +100,8 @@ struct Table {
     v[2].insert(v[2].end(), p, p + n);
     p = hgemm_tr_variants(&n, 2);
     v[3].insert(v[3].end(), p, p + n);
+    p = hgemm_tr_variants(&n, 3);
+    v[4].insert(v[4].end(), p, p + n);
     for (int d = 0; d < kDtypes; ++d)
       for (size_t i = 0; i < v[d].size(); ++i) v[d][i].desc.id = (int32_t)i;
   }
@@ -149,7 +158,7 @@ struct Choice {
 
 double gemm_seconds(int dtype, const Variant& v, int64_t M, int64_t N, int64_t Kc, int64_t S) {
   const gemm_config_t& d = v.desc;
-  const double rate = dtype == GEMM_DTYPE_F32 ? 0.59e12 : dtype == GEMM_DTYPE_F8 ? 9.4e12 : 4.7e12;
+  const double rate = dtype == GEMM_DTYPE_F32 ? 0.59e12 : is_f8(dtype) ? 9.4e12 : 4.7e12;
   int64_t per_cu = (160 * 1024) / (d.lds_bytes > 0 ? d.lds_bytes : 1);
   per_cu = per_cu < 1 ? 1 : per_cu > 2 ? 2 : per_cu;
   const int64_t wgs = cdiv(M, d.bm) * cdiv(N, d.bn) * S;
@@ -316,7 +325,7 @@ bool vector_path(int dtype, const void* A, int64_t lda, const void* B, int64_t l
   const int64_t w = 16 / (int64_t)in_bytes(dtype);  // elements per 16 bytes
   const int64_t wc = 16 / (int64_t)(c_es ? c_es : out_bytes(dtype));
   // FP8 with K = 0 reads neither A nor B (C = 0): only C's layout matters.
-  if (dtype == GEMM_DTYPE_F8 && K == 0) return aligned16(C) && ldc % wc == 0 && N % wc == 0;
+  if (is_f8(dtype) && K == 0) return aligned16(C) && ldc % wc == 0 && N % wc == 0;
   return aligned16(A) && aligned16(B) && aligned16(C) && lda % w == 0 && ldb % w == 0 &&
          ldc % wc == 0 && K % w == 0 && N % w == 0;
 }
@@ -349,10 +358,10 @@ gemm_status_t launch_plain(int dtype, const gemm_config_t& cfg, int64_t M, int64
                            int64_t ldc, void* stream) {
   const Params p = make_params(dtype, A, lda, B, ldb, C, ldc, M, N, K);
   const bool vec = vector_path(dtype, A, lda, B, ldb, C, ldc, K, N);
-  if (dtype == GEMM_DTYPE_F8 && !vec) return f8_unsupported();
+  if (is_f8(dtype) && !vec) return f8_unsupported();
   const TileMap map = make_map(cfg, M, N);
   const hipError_t e = table().v[dtype][cfg.id].launch(p, map, vec, static_cast<hipStream_t>(stream));
-  if (e == hipErrorNotSupported && dtype == GEMM_DTYPE_F8) return f8_unsupported();
+  if (e == hipErrorNotSupported && is_f8(dtype)) return f8_unsupported();
   if (e != hipSuccess) return fail(GEMM_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
   return GEMM_OK;
 }
@@ -383,11 +392,11 @@ gemm_status_t run_bt(int dtype, int64_t M, int64_t N, int64_t K, const void* A, 
   Params p = make_params(dtype, A, lda, Bt, ldbt, C, ldc, M, N, K);
   p.bt = true;
   const bool vec = vector_path(dtype, A, lda, Bt, ldbt, C, ldc, K, N);
-  if (dtype == GEMM_DTYPE_F8 && !vec) return f8_unsupported();
+  if (is_f8(dtype) && !vec) return f8_unsupported();
   const TileMap map = make_map(cfg, M, N);
   const hipError_t e =
       table().v[dtype][cfg.id].launch_bt(p, map, vec, static_cast<hipStream_t>(stream));
-  if (e == hipErrorNotSupported && dtype == GEMM_DTYPE_F8) return f8_unsupported();
+  if (e == hipErrorNotSupported && is_f8(dtype)) return f8_unsupported();
   if (e != hipSuccess) return fail(GEMM_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
   return GEMM_OK;
 }
@@ -416,11 +425,11 @@ gemm_status_t run_epi(int dtype, int64_t M, int64_t N, int64_t K, const void* A,
   // The vector forms read the bias four floats at a time.
   const bool vec = vector_path(dtype, A, lda, B, ldb, C, ldc, K, N) &&
                    (!epi->bias || aligned16(epi->bias));
-  if (dtype == GEMM_DTYPE_F8 && !vec) return f8_unsupported();
+  if (is_f8(dtype) && !vec) return f8_unsupported();
   const TileMap map = make_map(cfg, M, N);
   const hipError_t e =
       table().v[dtype][cfg.id].launch_epi(p, map, vec, static_cast<hipStream_t>(stream));
-  if (e == hipErrorNotSupported && dtype == GEMM_DTYPE_F8) return f8_unsupported();
+  if (e == hipErrorNotSupported && is_f8(dtype)) return f8_unsupported();
   if (e != hipSuccess) return fail(GEMM_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
   return GEMM_OK;
 }
@@ -849,5 +858,51 @@ const char* gemm_status_string(gemm_status_t s) {
 const char* gemm_last_error(void) { return g_err; }
 
 const char* gemm_version(void) { return "libgemm 0.1.0 (gfx950)"; }
+
+// FP8 E5M2: the FP8 entry points with the other operand format.
+gemm_status_t gemm_e5m2(int64_t M, int64_t N, int64_t K, const gemm_e5m2_t* A, int64_t lda,
+                        const gemm_e5m2_t* B, int64_t ldb, gemm_bf16_t* C, int64_t ldc, void* stream) {
+  return run(GEMM_DTYPE_E5M2, M, N, K, A, lda, B, ldb, C, ldc, stream, nullptr);
+}
+
+gemm_status_t gemm_e5m2_ex(int64_t M, int64_t N, int64_t K, const gemm_e5m2_t* A, int64_t lda,
+                           const gemm_e5m2_t* B, int64_t ldb, gemm_bf16_t* C, int64_t ldc, void* stream,
+                           const gemm_config_t* cfg) {
+  if (!cfg) return fail(GEMM_ERR_INVALID_ARG, "cfg is NULL");
+  return run(GEMM_DTYPE_E5M2, M, N, K, A, lda, B, ldb, C, ldc, stream, cfg);
+}
+
+gemm_status_t gemm_e5m2_bt(int64_t M, int64_t N, int64_t K, const gemm_e5m2_t* A, int64_t lda,
+                           const gemm_e5m2_t* Bt, int64_t ldbt, gemm_bf16_t* C, int64_t ldc,
+                           void* stream, const gemm_config_t* cfg) {
+  return run_bt(GEMM_DTYPE_E5M2, M, N, K, A, lda, Bt, ldbt, C, ldc, stream, cfg);
+}
+
+gemm_status_t gemm_e5m2_epi(int64_t M, int64_t N, int64_t K, const gemm_e5m2_t* A, int64_t lda,
+                            const gemm_e5m2_t* B, int64_t ldb, gemm_bf16_t* C, int64_t ldc,
+                            void* stream, const gemm_config_t* cfg, const gemm_epilogue_t* epi) {
+  return run_epi(GEMM_DTYPE_E5M2, M, N, K, A, lda, B, ldb, C, ldc, stream, cfg, epi);
+}
+
+gemm_status_t gemm_e5m2_splitk(int64_t M, int64_t N, int64_t K, const gemm_e5m2_t* A, int64_t lda,
+                               const gemm_e5m2_t* B, int64_t ldb, gemm_bf16_t* C, int64_t ldc,
+                               void* workspace, int64_t workspace_bytes, void* stream,
+                               const gemm_config_t* cfg) {
+  return run_splitk(GEMM_DTYPE_E5M2, M, N, K, A, lda, B, ldb, C, ldc, workspace, workspace_bytes,
+                    stream, cfg);
+}
+
+gemm_status_t gemm_e5m2_epi_q8(int64_t M, int64_t N, int64_t K, const gemm_e5m2_t* A, int64_t lda,
+                               const gemm_e5m2_t* B, int64_t ldb, int8_t* Q, int64_t ldq, void* stream,
+                               const gemm_config_t* cfg, const gemm_epilogue_t* epi) {
+  return run_q8(GEMM_DTYPE_E5M2, M, N, K, A, lda, B, ldb, Q, ldq, stream, cfg, epi);
+}
+
+gemm_status_t gemm_e5m2_trans(int64_t M, int64_t N, int64_t K, const gemm_e5m2_t* A, int64_t lda,
+                              const gemm_e5m2_t* B, int64_t ldb, gemm_bf16_t* C, int64_t ldc,
+                              void* stream, const gemm_config_t* cfg, int32_t trans_a,
+                              int32_t trans_b) {
+  return run_trans(GEMM_DTYPE_E5M2, M, N, K, A, lda, B, ldb, C, ldc, stream, cfg, trans_a, trans_b);
+}
 
 }  // extern "C"

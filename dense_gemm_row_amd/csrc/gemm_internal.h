@@ -96,14 +96,17 @@ __device__ __forceinline__ f32x16_t mfma16(h16x8_t a, h16x8_t b, f32x16_t c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
-// FP8 E4M3 (OCP) operands, 32 per lane (k 64 per instruction):
-// v_mfma_f32_32x32x64_f8f6f4 with both format fields 0 (E4M3) and no block
-// scales (the scaled builtin with zero scale operands selects the unscaled
-// instruction; checked on the device: scale 0 and 127 both give x1).
+// FP8 operands, 32 per lane (k 64 per instruction):
+// v_mfma_f32_32x32x64_f8f6f4 with both operand-format fields FMT (0: OCP
+// E4M3, 1: OCP E5M2) and no block scales (the scaled builtin with zero
+// scale operands selects the unscaled instruction; checked on the device:
+// scale 0 and 127 both give x1).
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 
-__device__ __forceinline__ f32x16_t mfma_e4m3(i32x8_t a, i32x8_t b, f32x16_t c) {
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+template <int FMT>
+__device__ __forceinline__ f32x16_t mfma_f8(i32x8_t a, i32x8_t b, f32x16_t c) {
+  static_assert(FMT == 0 || FMT == 1, "E4M3 or E5M2");
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FMT, FMT, 0, 0, 0, 0);
 }
 
 // float -> 16-bit pattern, rounded to nearest even (v_cvt_f16_f32 or
@@ -251,6 +254,7 @@ const Variant* sgemm_simt_variants(int* count);
 // an FP8 E4M3 one (ty: 0 FP16, 1 BF16, 2 FP8 with BF16 output).
 const Variant* hgemm_mfma_variants(int* count, bool bf16 = false);
 const Variant* hgemm_pipe_variants(int* count);
+// ty: 0 FP16, 1 BF16, 2 FP8 E4M3, 3 FP8 E5M2.
 const Variant* hgemm_tr_variants(int* count, int ty = 0);
 
 // Launch the general 16-bit kernel (any alignment, 64-bit addressing; FP16

@@ -3,8 +3,9 @@
 // v_mfma_f32_32x32x16_f16, one round-to-nearest-even conversion per output.
 // The same kernel, with v_mfma_f32_32x32x16_bf16 and bfloat16 conversions,
 // is the BF16 GEMM, and with 8-bit elements, v_mfma_f32_32x32x64_f8f6f4
-// (k 64 per MFMA) and bfloat16 output it is the FP8 E4M3 GEMM (Shape's
-// TY_): the data path moves bit patterns and never looks inside them.  For
+// (k 64 per MFMA) and bfloat16 output it is the FP8 GEMM, E4M3 or E5M2 by
+// the instruction's operand format (Shape's TY_): the data path moves bit
+// patterns and never looks inside them.  For
 // FP8, a lane's operand is 32 bytes (two 16-byte A chunks; four
 // ds_read_b64_tr_b8 reads of B, the byte form of the transpose read below:
 // output lane j of a 16-lane group gets byte j%8 of the 8-byte pieces of
@@ -96,7 +97,7 @@ __device__ __forceinline__ void static_for(F&& f, std::integer_sequence<int, I..
 // column-major B); its tile is then staged and read exactly like A's (one
 // LDS row per output column, k contiguous), with no transpose read.  TY_:
 // the element types, 0 binary16 in and out, 1 bfloat16 in and out, 2 FP8
-// E4M3 in and bfloat16 out.  AT_: A given transposed (At, K x M row-major,
+// E4M3 in and bfloat16 out, 3 FP8 E5M2 in and bfloat16 out.  AT_: A given transposed (At, K x M row-major,
 // i.e. column-major A): its tile is staged and read exactly like B's (k
 // rows of BM values, chunk XOR by k, transpose reads), which hands each
 // lane the same k run of its row as the direct read of row-major A.  PW_:
@@ -115,7 +116,7 @@ struct Shape {
   static constexpr bool AT = AT_;
   static constexpr bool PARTIAL = MODE_ == 1, EPI = MODE_ == 2 || MODE_ == 3, Q8 = MODE_ == 3, BT = BT_;
   static constexpr bool BF = TY != 0;   // C (and the epilogue's old C) is bfloat16
-  static constexpr bool F8 = TY == 2;   // A and B are FP8 E4M3
+  static constexpr bool F8 = TY >= 2;   // A and B are FP8 (E4M3, or E5M2 when TY == 3)
   static constexpr int ES = F8 ? 1 : 2;    // input element bytes
   static constexpr int CE = 16 / ES;       // input elements per 16-byte chunk
   static constexpr int KW = F8 ? 64 : 16;  // k per MFMA
@@ -566,7 +567,7 @@ hgemm_tr_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
         if constexpr (S::F8)
-          acc[nb][mb] = mfma_e4m3(fb[buf][nb], fa[buf][mb], acc[nb][mb]);
+          acc[nb][mb] = mfma_f8<S::TY - 2>(fb[buf][nb], fa[buf][mb], acc[nb][mb]);
         else
           acc[nb][mb] = mfma16<S::BF>(fb[buf][nb], fa[buf][mb], acc[nb][mb]);
       }
@@ -1103,7 +1104,7 @@ int layout_check(int banks, int64_t out[2]) {
 // 256 bytes the chunk XOR needs; none otherwise.
 template <int BM, int BN, int WM, int WN, int BK, int NS, int TY, bool BT, int PW>
 constexpr LaunchFn at_launch() {
-  if constexpr (BM * (TY == 2 ? 1 : 2) >= 256)
+  if constexpr (BM * (TY >= 2 ? 1 : 2) >= 256)
     return &launch<Shape<BM, BN, WM, WN, BK, NS, 0, BT, TY, true, PW>>;
   else
     return nullptr;
@@ -1145,16 +1146,23 @@ constexpr LaunchFn at_launch() {
 
 const Variant kVariants[] = HGEMM_TR_TABLE(0, GEMM_DTYPE_F16, "f16");
 const Variant kVariantsBf[] = HGEMM_TR_TABLE(1, GEMM_DTYPE_BF16, "bf16");
-const Variant kVariantsF8[] = {
-    HGEMM_TR_VARIANT(2, GEMM_DTYPE_F8, "f8", 256, 256, 128, 128, 128, 2, 1.00f),
-    HGEMM_TR_VARIANT(2, GEMM_DTYPE_F8, "f8", 256, 256, 128, 128, 64, 4, 0.85f),
-    HGEMM_TR_VARIANT(2, GEMM_DTYPE_F8, "f8", 128, 256, 64, 128, 128, 3, 0.89f),
-    HGEMM_TR_VARIANT_PW(2, GEMM_DTYPE_F8, "f8", 128, 256, 64, 128, 128, 3, 4, "_p4", 0.88f),
-};
+// The two FP8 encodings share the tiles (the data path moves bytes; only
+// the matrix instruction's operand format differs).
+#define HGEMM_TR_F8_TABLE(TY, DT, TAG)                                              \
+  {HGEMM_TR_VARIANT(TY, DT, TAG, 256, 256, 128, 128, 128, 2, 1.00f),              \
+   HGEMM_TR_VARIANT(TY, DT, TAG, 256, 256, 128, 128, 64, 4, 0.85f),               \
+   HGEMM_TR_VARIANT(TY, DT, TAG, 128, 256, 64, 128, 128, 3, 0.89f),               \
+   HGEMM_TR_VARIANT_PW(TY, DT, TAG, 128, 256, 64, 128, 128, 3, 4, "_p4", 0.88f)}
+const Variant kVariantsF8[] = HGEMM_TR_F8_TABLE(2, GEMM_DTYPE_F8, "f8");
+const Variant kVariantsE5[] = HGEMM_TR_F8_TABLE(3, GEMM_DTYPE_E5M2, "e5m2");
 
 }  // namespace
 
 const Variant* hgemm_tr_variants(int* count, int ty) {
+  if (ty == 3) {
+    *count = sizeof(kVariantsE5) / sizeof(kVariantsE5[0]);
+    return kVariantsE5;
+  }
   const Variant* v = ty == 2 ? kVariantsF8 : ty == 1 ? kVariantsBf : kVariants;
   *count = ty == 2 ? sizeof(kVariantsF8) / sizeof(kVariantsF8[0])
                    : ty == 1 ? sizeof(kVariantsBf) / sizeof(kVariantsBf[0])

@@ -29,6 +29,7 @@ DTYPE_F32 = 0
 DTYPE_F16 = 1
 DTYPE_BF16 = 2
 DTYPE_F8 = 3  # FP8 E4M3 A and B, bfloat16 C
+DTYPE_E5M2 = 4  # FP8 E5M2 A and B, bfloat16 C
 FAMILY_MFMA = 0
 FAMILY_SIMT = 1
 ORDER_ROW = 0
@@ -38,7 +39,7 @@ ORDER_XCD = 2
 ACT_NONE = 0
 ACT_RELU = 1
 
-TYPES = ("f32", "f16", "bf16", "f8")
+TYPES = ("f32", "f16", "bf16", "f8", "e5m2")
 EXPORTS = [f"gemm_{t}{form}" for form in ("", "_ex", "_bt", "_trans", "_epi", "_epi_q8", "_splitk")
            for t in TYPES] + [
            "gemm_splitk_workspace_bytes", "gemm_select_splitk_config",
@@ -160,6 +161,10 @@ def gemm_f8(M, N, K, A, lda, B, ldb, C, ldc, stream=None) -> int:
     return lib().gemm_f8(M, N, K, A, lda, B, ldb, C, ldc, stream)
 
 
+def gemm_e5m2(M, N, K, A, lda, B, ldb, C, ldc, stream=None) -> int:
+    return lib().gemm_e5m2(M, N, K, A, lda, B, ldb, C, ldc, stream)
+
+
 def gemm_f32_ex(M, N, K, A, lda, B, ldb, C, ldc, stream, cfg: GemmConfig) -> int:
     return lib().gemm_f32_ex(M, N, K, A, lda, B, ldb, C, ldc, stream,
                              ctypes.byref(cfg) if cfg is not None else None)
@@ -180,6 +185,11 @@ def gemm_f8_ex(M, N, K, A, lda, B, ldb, C, ldc, stream, cfg: GemmConfig) -> int:
                             ctypes.byref(cfg) if cfg is not None else None)
 
 
+def gemm_e5m2_ex(M, N, K, A, lda, B, ldb, C, ldc, stream, cfg: GemmConfig) -> int:
+    return lib().gemm_e5m2_ex(M, N, K, A, lda, B, ldb, C, ldc, stream,
+                              ctypes.byref(cfg) if cfg is not None else None)
+
+
 def gemm_f32_bt(M, N, K, A, lda, Bt, ldbt, C, ldc, stream=None, cfg: GemmConfig | None = None) -> int:
     return lib().gemm_f32_bt(M, N, K, A, lda, Bt, ldbt, C, ldc, stream,
                              ctypes.byref(cfg) if cfg is not None else None)
@@ -198,6 +208,11 @@ def gemm_bf16_bt(M, N, K, A, lda, Bt, ldbt, C, ldc, stream=None, cfg: GemmConfig
 def gemm_f8_bt(M, N, K, A, lda, Bt, ldbt, C, ldc, stream=None, cfg: GemmConfig | None = None) -> int:
     return lib().gemm_f8_bt(M, N, K, A, lda, Bt, ldbt, C, ldc, stream,
                             ctypes.byref(cfg) if cfg is not None else None)
+
+
+def gemm_e5m2_bt(M, N, K, A, lda, Bt, ldbt, C, ldc, stream=None, cfg: GemmConfig | None = None) -> int:
+    return lib().gemm_e5m2_bt(M, N, K, A, lda, Bt, ldbt, C, ldc, stream,
+                              ctypes.byref(cfg) if cfg is not None else None)
 
 
 def gemm_f32_epi(M, N, K, A, lda, B, ldb, C, ldc, stream, cfg: GemmConfig | None,
@@ -228,6 +243,13 @@ def gemm_f8_epi(M, N, K, A, lda, B, ldb, C, ldc, stream, cfg: GemmConfig | None,
                              ctypes.byref(epi) if epi is not None else None)
 
 
+def gemm_e5m2_epi(M, N, K, A, lda, B, ldb, C, ldc, stream, cfg: GemmConfig | None,
+                  epi: GemmEpilogue | None) -> int:
+    return lib().gemm_e5m2_epi(M, N, K, A, lda, B, ldb, C, ldc, stream,
+                               ctypes.byref(cfg) if cfg is not None else None,
+                               ctypes.byref(epi) if epi is not None else None)
+
+
 def gemm_f32_splitk(M, N, K, A, lda, B, ldb, C, ldc, workspace, workspace_bytes, stream=None,
                     cfg: GemmConfig | None = None) -> int:
     return lib().gemm_f32_splitk(M, N, K, A, lda, B, ldb, C, ldc, workspace, workspace_bytes, stream,
@@ -252,6 +274,12 @@ def gemm_f8_splitk(M, N, K, A, lda, B, ldb, C, ldc, workspace, workspace_bytes, 
                                 stream, ctypes.byref(cfg) if cfg is not None else None)
 
 
+def gemm_e5m2_splitk(M, N, K, A, lda, B, ldb, C, ldc, workspace, workspace_bytes, stream=None,
+                     cfg: GemmConfig | None = None) -> int:
+    return lib().gemm_e5m2_splitk(M, N, K, A, lda, B, ldb, C, ldc, workspace, workspace_bytes,
+                                  stream, ctypes.byref(cfg) if cfg is not None else None)
+
+
 def _q8(name):
     def fn(M, N, K, A, lda, B, ldb, Q, ldq, stream, cfg: GemmConfig | None,
            epi: GemmEpilogue | None) -> int:
@@ -267,6 +295,7 @@ gemm_f32_epi_q8 = _q8("gemm_f32_epi_q8")
 gemm_f16_epi_q8 = _q8("gemm_f16_epi_q8")
 gemm_bf16_epi_q8 = _q8("gemm_bf16_epi_q8")
 gemm_f8_epi_q8 = _q8("gemm_f8_epi_q8")
+gemm_e5m2_epi_q8 = _q8("gemm_e5m2_epi_q8")
 
 
 def _trans(name):
@@ -284,13 +313,16 @@ gemm_f32_trans = _trans("gemm_f32_trans")
 gemm_f16_trans = _trans("gemm_f16_trans")
 gemm_bf16_trans = _trans("gemm_bf16_trans")
 gemm_f8_trans = _trans("gemm_f8_trans")
+gemm_e5m2_trans = _trans("gemm_e5m2_trans")
 
 
 # Entry points per dtype code, for callers that dispatch on it.
 def entry(dtype: int, form: str = ""):
     """The binding of gemm_<type><form> (form "", "_ex", "_bt", "_epi",
-    "_epi_q8", "_trans", "_splitk") for dtype DTYPE_F32 / DTYPE_F16 / DTYPE_BF16 / DTYPE_F8."""
-    name = {DTYPE_F32: "f32", DTYPE_F16: "f16", DTYPE_BF16: "bf16", DTYPE_F8: "f8"}[dtype]
+    "_epi_q8", "_trans", "_splitk") for dtype DTYPE_F32 / DTYPE_F16 / DTYPE_BF16 / DTYPE_F8 /
+    DTYPE_E5M2."""
+    name = {DTYPE_F32: "f32", DTYPE_F16: "f16", DTYPE_BF16: "bf16", DTYPE_F8: "f8",
+            DTYPE_E5M2: "e5m2"}[dtype]
     return globals()[f"gemm_{name}{form}"]
 
 
@@ -389,8 +421,8 @@ def matmul(a, b, out=None, config: GemmConfig | None = None, stream=None, split_
            alpha: float = 1.0, beta: float = 0.0, bias=None, act: int = ACT_NONE,
            b_transposed: bool = False):
     """C = a @ b on the GPU through libgemm.  a: M x K, b: K x N, of one
-    type (float32, float16, bfloat16, or float8_e4m3fn with a bfloat16
-    result), row-major (any row stride).  Returns ``out`` (allocated when
+    type (float32, float16, bfloat16, or float8_e4m3fn / float8_e5m2 with a
+    bfloat16 result), row-major (any row stride).  Returns ``out`` (allocated when
     None).  Raises GemmError on a non-OK status.
 
     With ``config`` None and ``split_k`` True, shapes for which the library
@@ -406,10 +438,11 @@ def matmul(a, b, out=None, config: GemmConfig | None = None, stream=None, split_
     gemm_*_epi; ``out`` must then be given when beta != 0)."""
     import torch
     dtypes = {torch.float32: DTYPE_F32, torch.float16: DTYPE_F16, torch.bfloat16: DTYPE_BF16,
-              torch.float8_e4m3fn: DTYPE_F8}
+              torch.float8_e4m3fn: DTYPE_F8, torch.float8_e5m2: DTYPE_E5M2}
     if a.dtype != b.dtype or a.dtype not in dtypes:
-        raise TypeError("a and b must both be float32, float16, bfloat16 or float8_e4m3fn")
-    c_dtype = torch.bfloat16 if a.dtype == torch.float8_e4m3fn else a.dtype
+        raise TypeError("a and b must both be float32, float16, bfloat16, float8_e4m3fn or "
+                        "float8_e5m2")
+    c_dtype = torch.bfloat16 if a.dtype in (torch.float8_e4m3fn, torch.float8_e5m2) else a.dtype
     if not (a.is_cuda and b.is_cuda):
         raise ValueError("a and b must be GPU tensors")
     M, K = a.shape

@@ -22,7 +22,8 @@ increment 0x9E3779B97F4A7C15).
   round-to-nearest-even bfloat16 value of it (:func:`to_bf16`), held as
   uint16 bit patterns under the marker dtype :data:`BF16`; FP8 inputs are
   the round-to-nearest-even OCP E4M3 value (:func:`to_e4m3`), bytes under
-  :data:`F8`.
+  :data:`F8`, or the round-to-nearest-even OCP E5M2 value
+  (:func:`to_e5m2`), bytes under :data:`E5M2`.
 
 Streams: A uses stream 0 and B stream 1.  The workloads draw i.i.d.
 uniform[-1, 1) entries from seed 0, the synthetic square and rectangular
@@ -46,6 +47,10 @@ BF16 = np.dtype([("bf16", "<u2")])
 # FP8 E4M3 (OCP) byte patterns: 1 sign, 4 exponent (bias 7), 3 fraction
 # bits, no infinities, 0x7F / 0xFF NaN, largest finite 448.
 F8 = np.dtype([("e4m3", "u1")])
+# FP8 E5M2 (OCP) byte patterns: 1 sign, 5 exponent (bias 15), 2 fraction
+# bits; exponent 31 holds the infinities (fraction 0) and NaN; largest
+# finite 57344.
+E5M2 = np.dtype([("e5m2", "u1")])
 
 
 def _e4m3_table() -> np.ndarray:
@@ -56,6 +61,16 @@ def _e4m3_table() -> np.ndarray:
 
 
 _E4M3 = _e4m3_table()
+
+
+def _e5m2_table() -> np.ndarray:
+    """float64 value of each finite non-negative code 0x00..0x7B (increasing)."""
+    codes = np.arange(0x7C)
+    e, f = codes >> 2, codes & 3
+    return np.where(e == 0, f * 2.0 ** -16, (4 + f) * 2.0 ** (e.astype(np.float64) - 17))
+
+
+_E5M2 = _e5m2_table()
 
 
 def mix64_int(z: int) -> int:
@@ -167,6 +182,36 @@ def e4m3_to_f32(b) -> np.ndarray:
     return np.where(codes & 0x80, -mag, mag).astype(np.float32)
 
 
+def to_e5m2(x) -> np.ndarray:
+    """float32 values to FP8 E5M2 byte patterns (dtype E5M2), rounding to
+    nearest with ties to even; magnitudes from 61440 (halfway above 57344)
+    become infinity, NaN becomes 0x7E with the sign."""
+    v = np.array(x, dtype=np.float64, order="C")
+    mag = np.abs(v)
+    hi = np.clip(np.searchsorted(_E5M2, mag, side="left"), 0, len(_E5M2) - 1)
+    lo = np.maximum(hi - 1, 0)
+    d_lo, d_hi = mag - _E5M2[lo], _E5M2[hi] - mag
+    pick = np.where((d_lo < d_hi) | ((d_lo == d_hi) & (lo % 2 == 0)), lo, hi)
+    pick = np.where(mag <= _E5M2[0], 0, pick)
+    pick = np.where(mag >= 61440.0, 0x7C, pick)
+    code = np.where(np.isnan(mag), 0x7E, pick).astype(np.uint8)
+    code = code | (np.signbit(v).astype(np.uint8) << np.uint8(7))
+    return code.view(E5M2)
+
+
+def e5m2_to_f32(b) -> np.ndarray:
+    """FP8 E5M2 byte patterns (E5M2 or uint8) to float32 (exact)."""
+    codes = np.array(np.asarray(b).view(np.uint8), order="C")
+    m = codes & 0x7F
+    mag = np.where(m > 0x7C, np.nan, np.where(m == 0x7C, np.inf, _E5M2[np.minimum(m, 0x7B)]))
+    return np.where(codes & 0x80, -mag, mag).astype(np.float32)
+
+
+def uniform_e5m2(seed: int, stream: int, rows: int, cols: int) -> np.ndarray:
+    """The FP32 matrix of :func:`uniform_f32` rounded to FP8 E5M2 (RNE)."""
+    return to_e5m2(uniform_f32(seed, stream, rows, cols))
+
+
 def uniform_f8(seed: int, stream: int, rows: int, cols: int) -> np.ndarray:
     """The FP32 matrix of :func:`uniform_f32` rounded to FP8 E4M3 (RNE)."""
     return to_e4m3(uniform_f32(seed, stream, rows, cols))
@@ -187,6 +232,8 @@ def small_int(seed: int, stream: int, rows: int, cols: int, lo: int = -2,
         return to_bf16(small_int(seed, stream, rows, cols, lo, hi, np.float32))
     if dtype == F8:
         return to_e4m3(small_int(seed, stream, rows, cols, lo, hi, np.float32))
+    if dtype == E5M2:
+        return to_e5m2(small_int(seed, stream, rows, cols, lo, hi, np.float32))
     if n == 0:
         return np.zeros((rows, cols), dtype=dtype)
     u = stream_u64(seed, stream, n) >> np.uint64(32)
@@ -213,4 +260,6 @@ def workload(M: int, N: int, K: int, dtype: str, seed: int = 0):
         return (uniform_bf16(seed, STREAM_A, M, K), uniform_bf16(seed, STREAM_B, K, N))
     if dtype == "f8":
         return (uniform_f8(seed, STREAM_A, M, K), uniform_f8(seed, STREAM_B, K, N))
+    if dtype == "e5m2":
+        return (uniform_e5m2(seed, STREAM_A, M, K), uniform_e5m2(seed, STREAM_B, K, N))
     raise ValueError(f"unknown dtype {dtype!r}")

@@ -84,10 +84,10 @@ def time_config(gemm, torch, fn, args, cfg, stream, warmup: int, reps: int, ws=N
 def tune_shape(gemm, torch, kind: str, M: int, N: int, K: int, orders, warmup: int,
                reps: int, splits=(1,)) -> dict:
     dtype = {"f32": gemm.DTYPE_F32, "f16": gemm.DTYPE_F16, "bf16": gemm.DTYPE_BF16,
-             "f8": gemm.DTYPE_F8}[kind]
+             "f8": gemm.DTYPE_F8, "e5m2": gemm.DTYPE_E5M2}[kind]
     tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16,
-           "f8": torch.float8_e4m3fn}[kind]
-    cdt = torch.bfloat16 if kind == "f8" else tdt  # FP8 products are BF16
+           "f8": torch.float8_e4m3fn, "e5m2": torch.float8_e5m2}[kind]
+    cdt = torch.bfloat16 if kind in ("f8", "e5m2") else tdt  # FP8 products are BF16
     dev = torch.device("cuda:0")
     gen = torch.Generator(device=dev)
     gen.manual_seed(M * 1000003 + N * 1009 + K)
@@ -146,7 +146,8 @@ def tune_shape(gemm, torch, kind: str, M: int, N: int, K: int, orders, warmup: i
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--shapes", nargs="+", type=parse_shape, required=True, help="MxNxK ...")
-    ap.add_argument("--dtypes", nargs="+", choices=["f32", "f16", "bf16", "f8"], default=["f32", "f16"])
+    ap.add_argument("--dtypes", nargs="+", choices=["f32", "f16", "bf16", "f8", "e5m2"],
+                    default=["f32", "f16"])
     ap.add_argument("--orders", nargs="+", type=parse_order,
                     default=[parse_order("xcd:4"), parse_order("xcd:8"), parse_order("grouped:8")],
                     help="tile orders to try: row | grouped:G | xcd:G")

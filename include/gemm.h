@@ -69,12 +69,17 @@ typedef uint16_t gemm_bf16_t;
 /* FP8 E4M3 byte (OCP 8-bit floating point: 1 sign, 4 exponent bits with
  * bias 7, 3 fraction bits, no infinities, largest finite 448). */
 typedef uint8_t gemm_f8_t;
+/* FP8 E5M2 byte (OCP 8-bit floating point: 1 sign, 5 exponent bits with
+ * bias 15, 2 fraction bits, infinities and NaN in exponent 31, largest
+ * finite 57344). */
+typedef uint8_t gemm_e5m2_t;
 
 typedef enum gemm_dtype {
     GEMM_DTYPE_F32 = 0,
     GEMM_DTYPE_F16 = 1,
     GEMM_DTYPE_BF16 = 2,
-    GEMM_DTYPE_F8 = 3 /* E4M3 A and B, bfloat16 C */
+    GEMM_DTYPE_F8 = 3,  /* E4M3 A and B, bfloat16 C */
+    GEMM_DTYPE_E5M2 = 4 /* E5M2 A and B, bfloat16 C */
 } gemm_dtype_t;
 
 /* Kernel families. */
@@ -405,6 +410,51 @@ gemm_status_t gemm_f8_epi_q8(int64_t M, int64_t N, int64_t K,
                              int8_t *Q, int64_t ldq, void *stream,
                              const gemm_config_t *cfg, const gemm_epilogue_t *epi);
 
+/*
+ * FP8 E5M2 GEMM: the other OCP 8-bit encoding (5 exponent bits, 2 fraction
+ * bits: FP16's exponent range, one fraction bit fewer than E4M3).  FP32
+ * accumulation, bfloat16 output rounded to nearest even; the same kernels
+ * as FP8 E4M3 with the E5M2 operand format of the matrix instruction.  Each
+ * entry point has the contract of its gemm_f8_* counterpart (vector layout
+ * only, the same forms, sizes and errors), with gemm_e5m2_t A and B;
+ * gemm_splitk_workspace_bytes takes GEMM_DTYPE_E5M2.
+ */
+gemm_status_t gemm_e5m2(int64_t M, int64_t N, int64_t K,
+                        const gemm_e5m2_t *A, int64_t lda,
+                        const gemm_e5m2_t *B, int64_t ldb,
+                        gemm_bf16_t *C, int64_t ldc, void *stream);
+gemm_status_t gemm_e5m2_ex(int64_t M, int64_t N, int64_t K,
+                           const gemm_e5m2_t *A, int64_t lda,
+                           const gemm_e5m2_t *B, int64_t ldb,
+                           gemm_bf16_t *C, int64_t ldc, void *stream,
+                           const gemm_config_t *cfg);
+gemm_status_t gemm_e5m2_splitk(int64_t M, int64_t N, int64_t K,
+                               const gemm_e5m2_t *A, int64_t lda,
+                               const gemm_e5m2_t *B, int64_t ldb,
+                               gemm_bf16_t *C, int64_t ldc,
+                               void *workspace, int64_t workspace_bytes,
+                               void *stream, const gemm_config_t *cfg);
+gemm_status_t gemm_e5m2_bt(int64_t M, int64_t N, int64_t K,
+                           const gemm_e5m2_t *A, int64_t lda,
+                           const gemm_e5m2_t *Bt, int64_t ldbt,
+                           gemm_bf16_t *C, int64_t ldc, void *stream,
+                           const gemm_config_t *cfg);
+gemm_status_t gemm_e5m2_trans(int64_t M, int64_t N, int64_t K,
+                              const gemm_e5m2_t *A, int64_t lda,
+                              const gemm_e5m2_t *B, int64_t ldb,
+                              gemm_bf16_t *C, int64_t ldc, void *stream,
+                              const gemm_config_t *cfg, int32_t trans_a, int32_t trans_b);
+gemm_status_t gemm_e5m2_epi(int64_t M, int64_t N, int64_t K,
+                            const gemm_e5m2_t *A, int64_t lda,
+                            const gemm_e5m2_t *B, int64_t ldb,
+                            gemm_bf16_t *C, int64_t ldc, void *stream,
+                            const gemm_config_t *cfg, const gemm_epilogue_t *epi);
+gemm_status_t gemm_e5m2_epi_q8(int64_t M, int64_t N, int64_t K,
+                               const gemm_e5m2_t *A, int64_t lda,
+                               const gemm_e5m2_t *B, int64_t ldb,
+                               int8_t *Q, int64_t ldq, void *stream,
+                               const gemm_config_t *cfg, const gemm_epilogue_t *epi);
+
 /* Variant table: count per dtype, and the description of variant idx. */
 int32_t gemm_num_configs(int32_t dtype);
 gemm_status_t gemm_get_config(int32_t dtype, int32_t idx, gemm_config_t *out);
@@ -435,7 +485,7 @@ gemm_status_t gemm_layout_check(int32_t dtype, int32_t idx, int32_t banks,
                                 int64_t out[2]);
 
 /* Tuning table: a text file of lines "dtype M N K name order group_m
- * [splits]" (dtype f32|f16|bf16|f8; splits defaults to 1).  Exact-shape matches
+ * [splits]" (dtype f32|f16|bf16|f8|e5m2; splits defaults to 1).  Exact-shape matches
  * override the heuristic.  Loading replaces the previous table; NULL clears
  * it.  Not safe to call concurrently with GEMM calls. */
 gemm_status_t gemm_load_tuning(const char *path);

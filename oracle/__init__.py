@@ -18,14 +18,16 @@ marshals numpy arrays:
 * :func:`f16_to_f64` -- exact IEEE binary16 decoding.
 * :func:`bf16_to_f64` -- exact bfloat16 decoding.
 * :func:`e4m3_to_f64` -- exact FP8 E4M3 decoding.
+* :func:`e5m2_to_f64` -- exact FP8 E5M2 decoding.
 * :func:`quantize_i8` and :func:`q8_allowed` -- INT8 quantisation of epilogue
   values (ties to even, saturating) and the codes a result within a given
   error of the exact value may take.
 
 Element types: float32, float16 (or uint16 binary16 bit patterns),
 bfloat16 as uint16 bit patterns viewed with the marker dtype :data:`BF16`
-(numpy has no bfloat16 type), and FP8 E4M3 as bytes under :data:`F8`.
-An FP8 product's C (and the old C of its fused epilogue) is bfloat16.
+(numpy has no bfloat16 type), FP8 E4M3 as bytes under :data:`F8` and FP8
+E5M2 as bytes under :data:`E5M2`.  An FP8 product's C (and the old C of its
+fused epilogue) is bfloat16.
 
 Parity status: pinned (see the oracle tests in ``tests/``).
 """
@@ -62,8 +64,10 @@ F8_TOL = 5e-3
 BF16 = np.dtype([("bf16", "<u2")])
 # FP8 E4M3 (OCP) byte patterns, the same way.
 F8 = np.dtype([("e4m3", "u1")])
+# FP8 E5M2 (OCP) byte patterns (products exact in FP32 too: 3 x 3 bits).
+E5M2 = np.dtype([("e5m2", "u1")])
 
-TOL = {"f32": SGEMM_TOL, "f16": HGEMM_TOL, "bf16": BF16_TOL, "f8": F8_TOL}
+TOL = {"f32": SGEMM_TOL, "f16": HGEMM_TOL, "bf16": BF16_TOL, "f8": F8_TOL, "e5m2": F8_TOL}
 
 
 def build(src: str = _SRC, out: str = _LIB, extra_flags=()) -> str:
@@ -93,23 +97,28 @@ def _declare(lib):
     lib.oracle_e4m3_to_f64.restype = ctypes.c_double
     lib.oracle_e4m3_array_to_f64.argtypes = [p, p, i64]
     lib.oracle_e4m3_array_to_f64.restype = None
+    lib.oracle_e5m2_to_f64.argtypes = [ctypes.c_uint8]
+    lib.oracle_e5m2_to_f64.restype = ctypes.c_double
+    lib.oracle_e5m2_array_to_f64.argtypes = [p, p, i64]
+    lib.oracle_e5m2_array_to_f64.restype = None
     for name in ("oracle_gemm_rows_f32", "oracle_gemm_rows_f16", "oracle_gemm_rows_bf16",
-                 "oracle_gemm_rows_f8"):
+                 "oracle_gemm_rows_f8", "oracle_gemm_rows_e5m2"):
         fn = getattr(lib, name)
         fn.argtypes = [i64, i64, i64, p, i64, p, i64, p, p, i64, p, i64, ctypes.c_int]
         fn.restype = ctypes.c_int
     for name in ("oracle_gemm_entries_f32", "oracle_gemm_entries_f16", "oracle_gemm_entries_bf16",
-                 "oracle_gemm_entries_f8"):
+                 "oracle_gemm_entries_f8", "oracle_gemm_entries_e5m2"):
         fn = getattr(lib, name)
         fn.argtypes = [i64, p, i64, p, i64, p, p, i64, p, p]
         fn.restype = ctypes.c_int
     for name in ("oracle_gemm_rows_bt_f32", "oracle_gemm_rows_bt_f16", "oracle_gemm_rows_bt_bf16",
-                 "oracle_gemm_rows_bt_f8"):
+                 "oracle_gemm_rows_bt_f8", "oracle_gemm_rows_bt_e5m2"):
         fn = getattr(lib, name)
         fn.argtypes = [i64, i64, i64, p, i64, p, i64, p, p, i64, p, i64]
         fn.restype = ctypes.c_int
     for name in ("oracle_gemm_rows_trans_f32", "oracle_gemm_rows_trans_f16",
-                 "oracle_gemm_rows_trans_bf16", "oracle_gemm_rows_trans_f8"):
+                 "oracle_gemm_rows_trans_bf16", "oracle_gemm_rows_trans_f8",
+                 "oracle_gemm_rows_trans_e5m2"):
         fn = getattr(lib, name)
         fn.argtypes = [i64, i64, i64, p, i64, p, i64, ctypes.c_int, ctypes.c_int, p, p, i64, p, i64]
         fn.restype = ctypes.c_int
@@ -175,6 +184,8 @@ def _kind(a: np.ndarray) -> str:
         return "bf16"
     if a.dtype == F8:
         return "f8"
+    if a.dtype == E5M2:
+        return "e5m2"
     raise TypeError(f"unsupported dtype {a.dtype}")
 
 
@@ -186,14 +197,14 @@ def _raw(a: np.ndarray, kind: str) -> tuple[np.ndarray, type]:
     """The array as the C routines take it (float32, uint16 or uint8 bits)."""
     if kind == "f32":
         return a, np.float32
-    if kind == "f8":
+    if kind in ("f8", "e5m2"):
         return a.view(np.uint8), np.uint8
     return _bits16(a), np.uint16
 
 
 def out_kind(kind: str) -> str:
     """The element type of C for inputs of `kind` (FP8 products are BF16)."""
-    return "bf16" if kind == "f8" else kind
+    return "bf16" if kind in ("f8", "e5m2") else kind
 
 
 def gemm_rows(A: np.ndarray, B: np.ndarray, rows=None, threads: int | None = None,
@@ -435,6 +446,17 @@ def e4m3_to_f64(bits) -> np.ndarray:
     out = np.empty(b.shape, dtype=np.float64)
     if b.size:
         lib.oracle_e4m3_array_to_f64(_ptr(b), _ptr(out), b.size)
+    return out
+
+
+def e5m2_to_f64(bits) -> np.ndarray:
+    """Exact decode of FP8 E5M2 byte patterns (:data:`E5M2` or uint8 array)."""
+    lib = load()
+    b = np.asarray(bits)
+    b = np.ascontiguousarray(b.view(np.uint8) if b.dtype == E5M2 else b.astype(np.uint8, copy=False))
+    out = np.empty(b.shape, dtype=np.float64)
+    if b.size:
+        lib.oracle_e5m2_array_to_f64(_ptr(b), _ptr(out), b.size)
     return out
 
 

@@ -34,7 +34,9 @@
  * their own; a BF16 x BF16 product carries at most 16 significant bits, so
  * it is exact in double as well.  FP8 inputs (OCP E4M3: the 8-bit type the
  * GB300 GEMM article puts a tier above FP16 in section 1.1) arrive as byte
- * patterns with a decoder of their own (4 significant bits, products exact).
+ * patterns with a decoder of their own (4 significant bits, products exact);
+ * so do FP8 E5M2 inputs (OCP E5M2, the other 8-bit encoding of that tier:
+ * 3 significant bits, products exact).
  *
  * Parity status: pinned.  The pins (identity, permutation, all-ones closed
  * form C_ij = K, rank-1 outer products, K = 0 and K = 1, brute force against
@@ -135,10 +137,37 @@ void oracle_e4m3_array_to_f64(const uint8_t *src, double *dst, int64_t n)
 }
 
 /* ---------------------------------------------------------------------- */
+/* FP8 E5M2 (OCP) -> binary64, exact.                                      */
+/* Layout: 1 sign bit, 5 exponent bits (bias 15), 2 fraction bits;         */
+/* exponent 31 holds the infinities (fraction 0) and NaN (fraction != 0);  */
+/* exponent 0 holds zeros and subnormals (fraction * 2^-16).               */
+/* ---------------------------------------------------------------------- */
+double oracle_e5m2_to_f64(uint8_t b)
+{
+    const int sign = (b >> 7) & 1;
+    const int expo = (b >> 2) & 0x1f;
+    const int frac = b & 0x3;
+    double mag;
+    if (expo == 0x1f)
+        mag = frac ? NAN : INFINITY;
+    else if (expo == 0)
+        mag = ldexp((double)frac, -16);
+    else
+        mag = ldexp((double)(0x4 | frac), expo - 17);
+    return sign ? -mag : mag;
+}
+
+void oracle_e5m2_array_to_f64(const uint8_t *src, double *dst, int64_t n)
+{
+    for (int64_t t = 0; t < n; ++t)
+        dst[t] = oracle_e5m2_to_f64(src[t]);
+}
+
+/* ---------------------------------------------------------------------- */
 /* Input access: element (i, k) of a row-major matrix with leading         */
 /* dimension ld lives at base[i * ld + k].                                  */
 /* ---------------------------------------------------------------------- */
-enum { ORACLE_F32 = 0, ORACLE_F16 = 1, ORACLE_BF16 = 2, ORACLE_E4M3 = 3 };
+enum { ORACLE_F32 = 0, ORACLE_F16 = 1, ORACLE_BF16 = 2, ORACLE_E4M3 = 3, ORACLE_E5M2 = 4 };
 
 static double load_elem(const void *base, int dtype, int64_t idx)
 {
@@ -146,6 +175,8 @@ static double load_elem(const void *base, int dtype, int64_t idx)
         return (double)((const float *)base)[idx];
     if (dtype == ORACLE_E4M3)
         return oracle_e4m3_to_f64(((const uint8_t *)base)[idx]);
+    if (dtype == ORACLE_E5M2)
+        return oracle_e5m2_to_f64(((const uint8_t *)base)[idx]);
     if (dtype == ORACLE_BF16)
         return oracle_bf16_to_f64(((const uint16_t *)base)[idx]);
     return oracle_f16_to_f64(((const uint16_t *)base)[idx]);
@@ -282,6 +313,15 @@ int oracle_gemm_rows_f8(int64_t nrows, int64_t N, int64_t K,
                     nthreads);
 }
 
+int oracle_gemm_rows_e5m2(int64_t nrows, int64_t N, int64_t K,
+                          const uint8_t *A, int64_t lda, const uint8_t *B, int64_t ldb,
+                          const int64_t *rows, double *C, int64_t ldr,
+                          double *D, int64_t ldd, int nthreads)
+{
+    return run_rows(ORACLE_E5M2, nrows, N, K, A, lda, B, ldb, rows, C, ldr, D, ldd,
+                    nthreads);
+}
+
 /*
  * Rows of C_ref and D for B given transposed: Bt is the N x K row-major
  * matrix with Bt[j][k] = B[k][j] (B column-major, the layout of the
@@ -360,6 +400,13 @@ int oracle_gemm_rows_bt_f8(int64_t nrows, int64_t N, int64_t K, const uint8_t *A
     return run_rows_bt(ORACLE_E4M3, nrows, N, K, A, lda, Bt, ldbt, rows, C, ldr, D, ldd);
 }
 
+int oracle_gemm_rows_bt_e5m2(int64_t nrows, int64_t N, int64_t K, const uint8_t *A,
+                             int64_t lda, const uint8_t *Bt, int64_t ldbt, const int64_t *rows,
+                             double *C, int64_t ldr, double *D, int64_t ldd)
+{
+    return run_rows_bt(ORACLE_E5M2, nrows, N, K, A, lda, Bt, ldbt, rows, C, ldr, D, ldd);
+}
+
 /*
  * Rows of C_ref and D with either operand given transposed, the four BLAS
  * layouts: A element (i, k) is A[i*lda + k], or A[k*lda + i] when trans_a
@@ -407,6 +454,7 @@ ORACLE_TRANS(f32, ORACLE_F32, float)
 ORACLE_TRANS(f16, ORACLE_F16, uint16_t)
 ORACLE_TRANS(bf16, ORACLE_BF16, uint16_t)
 ORACLE_TRANS(f8, ORACLE_E4M3, uint8_t)
+ORACLE_TRANS(e5m2, ORACLE_E5M2, uint8_t)
 
 /*
  * Fused epilogue, applied to rows of C_ref and D produced by
@@ -561,6 +609,13 @@ int oracle_gemm_entries_f8(int64_t K, const uint8_t *A, int64_t lda,
                            const int64_t *jj, int64_t n, double *c, double *d)
 {
     return run_entries(ORACLE_E4M3, K, A, lda, B, ldb, ii, jj, n, c, d);
+}
+
+int oracle_gemm_entries_e5m2(int64_t K, const uint8_t *A, int64_t lda,
+                             const uint8_t *B, int64_t ldb, const int64_t *ii,
+                             const int64_t *jj, int64_t n, double *c, double *d)
+{
+    return run_entries(ORACLE_E5M2, K, A, lda, B, ldb, ii, jj, n, c, d);
 }
 
 /* ---------------------------------------------------------------------- */

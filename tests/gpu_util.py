@@ -19,13 +19,18 @@ from dense_gemm_row_amd import gemm, synth
 CANARY_F32 = np.uint32(0x7FC0DEAD)  # a quiet NaN payload nobody computes
 CANARY_F16 = np.uint16(0x7E5A)
 CANARY_BF16 = np.uint16(0x7FDA)
-CANARY_F8 = np.uint8(0x7F)  # the E4M3 NaN
+CANARY_F8 = np.uint8(0x7F)  # a NaN in both E4M3 and E5M2
 CANARY_I8 = np.uint8(0x5A)  # INT8 outputs: any byte is a code, so this marks only the padding
-CANARY = {"f32": CANARY_F32, "f16": CANARY_F16, "bf16": CANARY_BF16, "f8": CANARY_F8, "i8": CANARY_I8}
-DTYPE = {"f32": gemm.DTYPE_F32, "f16": gemm.DTYPE_F16, "bf16": gemm.DTYPE_BF16, "f8": gemm.DTYPE_F8}
-VIEW = {"f32": np.float32, "f16": np.float16, "bf16": synth.BF16, "f8": synth.F8, "i8": np.int8}
-BITS = {"f32": np.uint32, "f16": np.uint16, "bf16": np.uint16, "f8": np.uint8, "i8": np.uint8}
-TORCH_BITS = {"f32": np.int32, "f16": np.int16, "bf16": np.int16, "f8": np.int8, "i8": np.int8}
+CANARY = {"f32": CANARY_F32, "f16": CANARY_F16, "bf16": CANARY_BF16, "f8": CANARY_F8,
+          "e5m2": CANARY_F8, "i8": CANARY_I8}
+DTYPE = {"f32": gemm.DTYPE_F32, "f16": gemm.DTYPE_F16, "bf16": gemm.DTYPE_BF16, "f8": gemm.DTYPE_F8,
+         "e5m2": gemm.DTYPE_E5M2}
+VIEW = {"f32": np.float32, "f16": np.float16, "bf16": synth.BF16, "f8": synth.F8,
+        "e5m2": synth.E5M2, "i8": np.int8}
+BITS = {"f32": np.uint32, "f16": np.uint16, "bf16": np.uint16, "f8": np.uint8, "e5m2": np.uint8,
+        "i8": np.uint8}
+TORCH_BITS = {"f32": np.int32, "f16": np.int16, "bf16": np.int16, "f8": np.int8, "e5m2": np.int8,
+              "i8": np.int8}
 
 
 def kind_of(a: np.ndarray) -> str:
@@ -37,6 +42,8 @@ def kind_of(a: np.ndarray) -> str:
         return "bf16"
     if a.dtype == synth.F8:
         return "f8"
+    if a.dtype == synth.E5M2:
+        return "e5m2"
     raise TypeError(f"unsupported dtype {a.dtype}")
 
 
@@ -46,6 +53,8 @@ def wide(x: np.ndarray) -> np.ndarray:
         return synth.bf16_to_f32(x).astype(np.float64)
     if x.dtype == synth.F8:
         return synth.e4m3_to_f32(x).astype(np.float64)
+    if x.dtype == synth.E5M2:
+        return synth.e5m2_to_f32(x).astype(np.float64)
     return x.astype(np.float64)
 
 
@@ -225,7 +234,7 @@ def rounded(ref: np.ndarray, kind: str) -> np.ndarray:
     assert np.array_equal(ref32.astype(np.float64), ref), "exact results must be FP32 values"
     if kind == "f32":
         return ref
-    if kind == "f8":
+    if kind in ("f8", "e5m2"):
         kind = "bf16"
     if kind == "f16":
         return ref32.astype(np.float16).astype(np.float64)

@@ -12,10 +12,10 @@ yuyanqi.com, section 1.1).  The pages print no worked matrices, so the pins
 are closed forms (identity, permutation, all-ones C_ij = K, rank-1 outer
 products, K = 0, K = 1), brute force against exact rational arithmetic, a
 float64 library matmul, and the exhaustive binary16 and bfloat16 tables.
-Every structural pin runs for FP32, FP16, BF16 and FP8 E4M3 inputs (BF16
-and FP8 as bit patterns under marker dtypes; values are built and widened
-here through the seeded-input module's conversions, which are checked
-against torch's, independently of the oracle's decoders).  An FP8
+Every structural pin runs for FP32, FP16, BF16, FP8 E4M3 and FP8 E5M2
+inputs (BF16 and FP8 as bit patterns under marker dtypes; values are built
+and widened here through the seeded-input module's conversions, which are
+checked against torch's, independently of the oracle's decoders).  An FP8
 product's C, and the old C of its epilogue, is BF16.
 """
 from __future__ import annotations
@@ -34,11 +34,12 @@ U64 = 2.0 ** -53  # unit roundoff of binary64
 
 BF16 = synth.BF16
 F8 = synth.F8
+E5M2 = synth.E5M2
 
 
 def _out(dt):
     """Element type of C for inputs of type dt."""
-    return BF16 if dt == F8 else dt
+    return BF16 if dt in (F8, E5M2) else dt
 
 
 def _make(x, dt) -> np.ndarray:
@@ -48,6 +49,8 @@ def _make(x, dt) -> np.ndarray:
         return synth.to_bf16(x.astype(np.float32))
     if dt == F8:
         return synth.to_e4m3(x.astype(np.float32))
+    if dt == E5M2:
+        return synth.to_e5m2(x.astype(np.float32))
     return x.astype(dt)
 
 
@@ -57,6 +60,8 @@ def _wide(x: np.ndarray) -> np.ndarray:
         return synth.bf16_to_f32(x).astype(np.float64)
     if x.dtype == F8:
         return synth.e4m3_to_f32(x).astype(np.float64)
+    if x.dtype == E5M2:
+        return synth.e5m2_to_f32(x).astype(np.float64)
     return x.astype(np.float64)
 
 
@@ -70,7 +75,7 @@ def _padded(x: np.ndarray, pad: int) -> np.ndarray:
 
 
 def _dtypes():
-    return (np.float32, np.float16, BF16, F8)
+    return (np.float32, np.float16, BF16, F8, E5M2)
 
 
 def _rand(dtype, seed, stream, r, c):
@@ -80,6 +85,8 @@ def _rand(dtype, seed, stream, r, c):
         return synth.uniform_bf16(seed, stream, r, c)
     if dtype == F8:
         return synth.uniform_f8(seed, stream, r, c)
+    if dtype == E5M2:
+        return synth.uniform_e5m2(seed, stream, r, c)
     return synth.uniform_f16(seed, stream, r, c)
 
 
@@ -290,6 +297,32 @@ def pin_e4m3_decode(lib):
             assert np.isnan(got), f"e4m3 decode 0x{b:02x}"
         else:
             assert got == v and np.signbit(got) == np.signbit(v), f"e4m3 decode 0x{b:02x}"
+
+
+def pin_e5m2_decode(lib):
+    """Exhaustive FP8 E5M2 decode against torch's float8_e5m2 (a library
+    routine) widened to float64; against the top byte of binary16 (E5M2 is
+    binary16 with its 8 low fraction bits dropped, so code c decodes like
+    the binary16 pattern c << 8, which numpy's float16 widens); plus the
+    hand-worked patterns of tests/golden/float8_e5m2_patterns.txt."""
+    import torch
+    bits = np.arange(256, dtype=np.uint8)
+    out = np.empty(bits.shape, dtype=np.float64)
+    lib.oracle_e5m2_array_to_f64(bits.ctypes.data, out.ctypes.data, bits.size)
+    ref = torch.from_numpy(bits).view(torch.float8_e5m2).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(out), nan), "e5m2 NaN patterns"
+    assert np.array_equal(out[~nan], ref[~nan]), "e5m2 decoded values"
+    assert np.array_equal(np.signbit(out[~nan]), np.signbit(ref[~nan])), "e5m2 signs"
+    top = (bits.astype(np.uint16) << np.uint16(8)).view(np.float16).astype(np.float64)
+    assert np.array_equal(out[~nan], top[~nan]), "e5m2 as the top byte of binary16"
+    for bits_s, val_s in golden_data.rows("float8_e5m2_patterns.txt"):
+        b, v = int(bits_s, 16), float.fromhex(val_s) if "p" in val_s else float(val_s)
+        got = lib.oracle_e5m2_to_f64(b)
+        if np.isnan(v):
+            assert np.isnan(got), f"e5m2 decode 0x{b:02x}"
+        else:
+            assert got == v and np.signbit(got) == np.signbit(v), f"e5m2 decode 0x{b:02x}"
 
 
 def _decode(lib, bits):
@@ -514,7 +547,7 @@ def pin_quantize_i8(lib):
 
 PINS = [pin_identity, pin_permutation, pin_all_ones, pin_rank1, pin_k0_k1,
         pin_bruteforce_fractions, pin_numpy_matmul, pin_f16_decode, pin_bf16_decode,
-        pin_e4m3_decode,
+        pin_e4m3_decode, pin_e5m2_decode,
         pin_error_metric, pin_epilogue_closed_form, pin_epilogue_reduces_to_plain,
         pin_epilogue_bruteforce, pin_bt_identity_permutation, pin_bt_matches_plain_transpose,
         pin_bt_rank1, pin_trans_matches_materialised, pin_trans_identity_rank1, pin_quantize_i8]

@@ -20,7 +20,8 @@ PA, PB, PC = 0x10000000, 0x20000000, 0x30000000
 def _dtype_of(fn):
     """The dtype code of a binding gemm_<type>[_form]."""
     t = fn.__name__.split("_")[1]
-    return {"f32": gemm.DTYPE_F32, "f16": gemm.DTYPE_F16, "bf16": gemm.DTYPE_BF16, "f8": gemm.DTYPE_F8}[t]
+    return {"f32": gemm.DTYPE_F32, "f16": gemm.DTYPE_F16, "bf16": gemm.DTYPE_BF16, "f8": gemm.DTYPE_F8,
+            "e5m2": gemm.DTYPE_E5M2}[t]
 
 
 def header_functions():
@@ -308,42 +309,48 @@ def test_bf16_tables_mirror_f16():
     assert c.name.decode().startswith("tr_bf16_") and c.bm * c.bn == 256 * 256
     s = gemm.gemm_select_splitk_config(gemm.DTYPE_BF16, 1024, 1024, 8192)
     assert s.splits > 1
-    assert gemm.gemm_num_configs(4) == 0
+    assert gemm.gemm_num_configs(5) == 0
     with pytest.raises(gemm.GemmError):
-        gemm.gemm_get_config(4, 0)
+        gemm.gemm_get_config(5, 0)
 
 
-def test_f8_table_and_validation():
-    """FP8 (E4M3 in, BF16 out): LDS-direct variants only, layouts valid and
-    conflict-free; operands off the vector layout are refused (UNSUPPORTED)
-    before any launch; sizes are checked with 1-byte A/B and 2-byte C."""
-    cfgs = gemm.configs(gemm.DTYPE_F8)
-    assert cfgs and all(c.name.decode().startswith("tr_f8_") and c.bk in (64, 128) for c in cfgs)
+@pytest.mark.parametrize("t", ["f8", "e5m2"])
+def test_f8_table_and_validation(t):
+    """FP8 (E4M3 or E5M2 in, BF16 out): LDS-direct variants only, layouts
+    valid and conflict-free, the two encodings on the same tiles; operands
+    off the vector layout are refused (UNSUPPORTED) before any launch; sizes
+    are checked with 1-byte A/B and 2-byte C."""
+    dt = {"f8": gemm.DTYPE_F8, "e5m2": gemm.DTYPE_E5M2}[t]
+    cfgs = gemm.configs(dt)
+    assert cfgs and all(c.name.decode().startswith(f"tr_{t}_") and c.bk in (64, 128) for c in cfgs)
     for c in cfgs:
-        assert gemm.gemm_layout_check(gemm.DTYPE_F8, c.id, 64) == (0, 0), c.name
-    sel = gemm.gemm_select_config(gemm.DTYPE_F8, 4096, 4096, 4096)
+        assert gemm.gemm_layout_check(dt, c.id, 64) == (0, 0), c.name
+    assert [c.name.decode().replace("_e5m2_", "_f8_") for c in gemm.configs(gemm.DTYPE_E5M2)] == \
+        [c.name.decode() for c in gemm.configs(gemm.DTYPE_F8)]
+    sel = gemm.gemm_select_config(dt, 4096, 4096, 4096)
     assert sel.bm * sel.bn == 256 * 256
-    assert gemm.gemm_select_splitk_config(gemm.DTYPE_F8, 1024, 1024, 8192).splits > 1
-    f = gemm.gemm_f8
+    assert gemm.gemm_select_splitk_config(dt, 1024, 1024, 8192).splits > 1
+    f = gemm.entry(dt)
     U = gemm.GEMM_ERR_UNSUPPORTED
     assert f(64, 64, 64, PA + 8, 64, PB, 64, PC, 64) == U        # A not 16-byte aligned
     assert f(64, 64, 72, PA, 72, PB, 64, PC, 64) == U            # K not a multiple of 16
     assert f(64, 72, 64, PA, 64, PB, 72, PC, 72) == U            # N not a multiple of 16
     assert f(64, 64, 64, PA, 64, PB, 64, PC, 68) == U            # ldc not a multiple of 8
     assert "FP8" in gemm.gemm_last_error()
-    assert gemm.gemm_f8_bt(64, 64, 64, PA, 64, PB, 72, PC, 64) == U
-    assert gemm.gemm_f8_splitk(64, 64, 4096, PA, 4096, PB, 64 + 8, PC, 64, PC + (1 << 20), 1 << 24) == U
+    assert gemm.entry(dt, "_bt")(64, 64, 64, PA, 64, PB, 72, PC, 64) == U
+    assert gemm.entry(dt, "_splitk")(64, 64, 4096, PA, 4096, PB, 64 + 8, PC, 64, PC + (1 << 20),
+                                     1 << 24) == U
     ok = gemm.GemmEpilogue(1.0, 0.0, None, gemm.ACT_NONE)
-    assert gemm.gemm_f8_epi(64, 64, 64, PA, 64, PB, 64, PC + 2, 64, None, None, ok) == U
+    assert gemm.entry(dt, "_epi")(64, 64, 64, PA, 64, PB, 64, PC + 2, 64, None, None, ok) == U
     # C is 2 bytes per element, A and B 1: C just past A's 64 x 64 bytes is fine,
     # C overlapping B's last row is not.
     assert f(0, 64, 64, PA, 64, PB, 64, PA + 64 * 64, 64) == gemm.GEMM_OK
     assert f(64, 64, 64, PA, 64, PB, 64, PB + 63 * 64, 64) == gemm.GEMM_ERR_ALIAS
-    assert gemm.gemm_splitk_workspace_bytes(gemm.DTYPE_F8, 10, 20, 1000, 3) == 3 * 10 * 20 * 4
+    assert gemm.gemm_splitk_workspace_bytes(dt, 10, 20, 1000, 3) == 3 * 10 * 20 * 4
 
 
 @pytest.mark.parametrize("fn", [gemm.gemm_f32_epi_q8, gemm.gemm_f16_epi_q8, gemm.gemm_bf16_epi_q8,
-                                gemm.gemm_f8_epi_q8])
+                                gemm.gemm_f8_epi_q8, gemm.gemm_e5m2_epi_q8])
 def test_q8_argument_validation(fn):
     """The INT8 epilogue: beta must be 0, the activation known, the bias not
     overlapping Q (1-byte elements), variants without an INT8 form refused
@@ -365,7 +372,7 @@ def test_q8_argument_validation(fn):
 
 
 @pytest.mark.parametrize("fn", [gemm.gemm_f32_trans, gemm.gemm_f16_trans, gemm.gemm_bf16_trans,
-                                gemm.gemm_f8_trans])
+                                gemm.gemm_f8_trans, gemm.gemm_e5m2_trans])
 def test_trans_argument_validation(fn):
     """Transposed layouts: flags 0/1 only; with A transposed lda is checked
     against M and the alias check covers A^T's K x M span; variants without
@@ -376,7 +383,8 @@ def test_trans_argument_validation(fn):
     assert fn(32, 64, 128, PA, 32, PB, 64, PC, 64, None, None, 2, 0) == gemm.GEMM_ERR_INVALID_ARG
     assert fn(32, 64, 128, PA, 31, PB, 64, PC, 64, None, None, 1, 0) == gemm.GEMM_ERR_INVALID_ARG
     assert fn(32, 64, 128, PA, 32, PB, 64, PC, 64, None, None, 0, 0) == gemm.GEMM_ERR_INVALID_ARG
-    es = {gemm.DTYPE_F32: 4, gemm.DTYPE_F16: 2, gemm.DTYPE_BF16: 2, gemm.DTYPE_F8: 1}[dt]
+    es = {gemm.DTYPE_F32: 4, gemm.DTYPE_F16: 2, gemm.DTYPE_BF16: 2, gemm.DTYPE_F8: 1,
+          gemm.DTYPE_E5M2: 1}[dt]
     # C starting inside A^T's last row (127 rows of 32 plus 32) aliases.
     assert fn(32, 64, 128, PA, 32, PB, 64, PA + (127 * 32 + 16) * es, 64, None, None, 1, 0) == \
         gemm.GEMM_ERR_ALIAS

@@ -1,17 +1,21 @@
-"""GPU parity of the FP8 GEMM (gemm_f8*, through the C-ABI) against the CPU
-oracle: FP8 E4M3 inputs, FP32 accumulation, bfloat16 output.
+"""GPU parity of the FP8 GEMMs (gemm_f8* for OCP E4M3 and gemm_e5m2* for OCP
+E5M2, through the C-ABI) against the CPU oracle: FP8 inputs, FP32
+accumulation, bfloat16 output.  Every test runs for both encodings (the
+``fmt`` fixture).
 
 * Exact inputs (small integers, identity, permutation, the rounding probe):
-  E4M3 products are exact in FP32, so the one correct output is the
+  E4M3 and E5M2 products are exact in FP32, so the one correct output is the
   oracle's exact result rounded once to bfloat16 (ties to even); every FP8
   variant must produce it on edge shapes (M ragged; N and K multiples of 16,
   the vector layout FP8 requires), padded leading dimensions, every tile
   order and every form (plain, split-K, fused epilogue, transposed B).
-* Random uniform[-1, 1) inputs rounded to E4M3: max_ij |C - C_ref| /
+* Random uniform[-1, 1) inputs rounded to E4M3 or E5M2: max_ij |C - C_ref| /
   sum_k |A_ik||B_kj| <= 5e-3 (bfloat16's unit roundoff plus the FP32
   accumulation bound), judged after the output rounding.
 * Operands off the vector layout are refused with GEMM_ERR_UNSUPPORTED.
 """
+from types import SimpleNamespace
+
 import numpy as np
 import pytest
 
@@ -22,21 +26,35 @@ from tests.gpu_util import check_full, check_rows, exact_equal, log, rounded, ru
 
 pytestmark = pytest.mark.gpu
 
-F8 = synth.F8
-DT = gemm.DTYPE_F8
-CFGS = list(range(gemm.gemm_num_configs(DT)))
+# The two encodings share their variant tables tile for tile.
+CFGS = list(range(gemm.gemm_num_configs(gemm.DTYPE_F8)))
 TOL = oracle.F8_TOL
+
+FORMATS = {
+    "f8": SimpleNamespace(name="f8", marker=synth.F8, dt=gemm.DTYPE_F8, to=synth.to_e4m3,
+                          uniform=synth.uniform_f8, rne="f8_bf16_rne_halfway.txt",
+                          torch="float8_e4m3fn"),
+    "e5m2": SimpleNamespace(name="e5m2", marker=synth.E5M2, dt=gemm.DTYPE_E5M2, to=synth.to_e5m2,
+                            uniform=synth.uniform_e5m2, rne="e5m2_bf16_rne_halfway.txt",
+                            torch="float8_e5m2"),
+}
+
+
+@pytest.fixture(params=sorted(FORMATS))
+def fmt(request):
+    return FORMATS[request.param]
 
 EDGE_SHAPES = [(1, 16, 16), (2, 16, 32), (31, 48, 16), (64, 64, 128), (127, 144, 80),
                (130, 272, 96), (257, 128, 208), (65, 304, 512)]
 
 
-def _ints(M, N, K, seed=7):
-    return synth.small_int(seed, 0, M, K, dtype=F8), synth.small_int(seed, 1, K, N, dtype=F8)
+def _ints(fmt, M, N, K, seed=7):
+    return (synth.small_int(seed, 0, M, K, dtype=fmt.marker),
+            synth.small_int(seed, 1, K, N, dtype=fmt.marker))
 
 
-def _cfg(idx, order=None, group_m=None):
-    c = gemm.gemm_get_config(DT, idx)
+def _cfg(fmt, idx, order=None, group_m=None):
+    c = gemm.gemm_get_config(fmt.dt, idx)
     if order is not None:
         c.order = order
     if group_m is not None:
@@ -48,62 +66,63 @@ def _bits(x):
     return x.view(np.uint16)
 
 
-def test_f8_table():
-    assert len(CFGS) >= 2
-    assert all(gemm.gemm_get_config(DT, i).dtype == DT for i in CFGS)
+def test_f8_table(fmt):
+    assert len(CFGS) >= 2 and gemm.gemm_num_configs(fmt.dt) == len(CFGS)
+    assert all(gemm.gemm_get_config(fmt.dt, i).dtype == fmt.dt for i in CFGS)
 
 
 @pytest.mark.parametrize("idx", CFGS)
 @pytest.mark.parametrize("shape", EDGE_SHAPES, ids=lambda s: "x".join(map(str, s)))
-def test_f8_exact_small_int(idx, shape):
+def test_f8_exact_small_int(fmt, idx, shape):
     M, N, K = shape
-    A, B = _ints(M, N, K)
-    cfg = _cfg(idx)
-    log(f"f8 exact cfg={cfg.name.decode()} shape={shape}")
+    A, B = _ints(fmt, M, N, K)
+    cfg = _cfg(fmt, idx)
+    log(f"{fmt.name} exact cfg={cfg.name.decode()} shape={shape}")
     C, _ = run(A, B, cfg)
     assert exact_equal(A, B, C)
 
 
 @pytest.mark.parametrize("order", [gemm.ORDER_ROW, gemm.ORDER_GROUPED, gemm.ORDER_XCD])
-def test_f8_tile_orders_exact(order):
+def test_f8_tile_orders_exact(fmt, order):
     M, N, K = 300, 528, 144
-    A, B = _ints(M, N, K, seed=11)
+    A, B = _ints(fmt, M, N, K, seed=11)
     for idx in CFGS:
-        cfg = _cfg(idx, order=order, group_m=3)
-        log(f"f8 order={order} cfg={cfg.name.decode()}")
+        cfg = _cfg(fmt, idx, order=order, group_m=3)
+        log(f"{fmt.name} order={order} cfg={cfg.name.decode()}")
         C, _ = run(A, B, cfg)
         assert exact_equal(A, B, C), cfg.name
 
 
 @pytest.mark.parametrize("pad", [(16, 32, 8), (48, 16, 24)])
-def test_f8_padded_leading_dimensions(pad):
+def test_f8_padded_leading_dimensions(fmt, pad):
     M, N, K = 129, 208, 272
-    A, B = _ints(M, N, K, seed=3)
+    A, B = _ints(fmt, M, N, K, seed=3)
     for idx in CFGS:
-        cfg = _cfg(idx)
-        log(f"f8 pad={pad} cfg={cfg.name.decode()}")
+        cfg = _cfg(fmt, idx)
+        log(f"{fmt.name} pad={pad} cfg={cfg.name.decode()}")
         C, _ = run(A, B, cfg, pad=pad)
         assert exact_equal(A, B, C), cfg.name
 
 
 @pytest.mark.parametrize("pad,offset", [((1, 0, 0), (0, 0, 0)), ((0, 0, 0), (1, 0, 0)),
                                         ((0, 0, 0), (0, 0, 1))])
-def test_f8_off_vector_layout_is_refused(pad, offset):
+def test_f8_off_vector_layout_is_refused(fmt, pad, offset):
     """lda not a multiple of 16, A or C misaligned: UNSUPPORTED, and C
     untouched (run's canary check)."""
-    A, B = _ints(64, 64, 64, seed=5)
-    log(f"f8 unsupported pad={pad} offset={offset}")
+    A, B = _ints(fmt, 64, 64, 64, seed=5)
+    log(f"{fmt.name} unsupported pad={pad} offset={offset}")
     with pytest.raises(gemm.GemmError) as e:
         run(A, B, None, pad=pad, offset=offset)
     assert e.value.status == gemm.GEMM_ERR_UNSUPPORTED
 
 
-def test_f8_output_rounds_to_nearest_even():
-    # Exact FP32 sums of E4M3 products halfway between two bfloat16
-    # neighbours (tests/golden/f8_bf16_rne_halfway.txt), zero-padded to
-    # K = N = 16 for the vector layout.
+def test_f8_output_rounds_to_nearest_even(fmt):
+    # Exact FP32 sums of FP8 products halfway between two bfloat16
+    # neighbours (tests/golden/f8_bf16_rne_halfway.txt for E4M3,
+    # e5m2_bf16_rne_halfway.txt for E5M2), zero-padded to K = N = 16 for
+    # the vector layout.
     mats = {}
-    for r in golden_data.rows("f8_bf16_rne_halfway.txt"):
+    for r in golden_data.rows(fmt.rne):
         mats.setdefault(r[0], []).append([int(x, 16) for x in r[2:]])
     A = np.zeros((3, 16), np.uint8)
     B = np.zeros((16, 16), np.uint8)
@@ -111,49 +130,49 @@ def test_f8_output_rounds_to_nearest_even():
     B[:3, :2] = np.array(mats["B"], np.uint8)
     expect = np.array(mats["C"], np.uint16)
     for idx in CFGS:
-        log(f"f8 RNE probe cfg={idx}")
-        C, _ = run(A.view(F8), B.view(F8), _cfg(idx))
+        log(f"{fmt.name} RNE probe cfg={idx}")
+        C, _ = run(A.view(fmt.marker), B.view(fmt.marker), _cfg(fmt, idx))
         assert np.array_equal(_bits(C)[:, :2], expect), _bits(C)[:, :2]
         assert not np.any(_bits(C)[:, 2:])
 
 
-def test_f8_k_zero_and_empty():
-    log("f8 K=0, M=0")
-    C, _ = run(synth.to_e4m3(np.zeros((70, 0), np.float32)), synth.to_e4m3(np.zeros((0, 96), np.float32)))
+def test_f8_k_zero_and_empty(fmt):
+    log(f"{fmt.name} K=0, M=0")
+    C, _ = run(fmt.to(np.zeros((70, 0), np.float32)), fmt.to(np.zeros((0, 96), np.float32)))
     assert C.shape == (70, 96) and np.all(_bits(C) == 0)
-    C, _ = run(synth.to_e4m3(np.zeros((0, 16), np.float32)), synth.to_e4m3(np.ones((16, 32), np.float32)))
+    C, _ = run(fmt.to(np.zeros((0, 16), np.float32)), fmt.to(np.ones((16, 32), np.float32)))
     assert C.shape == (0, 32)
 
 
-def test_f8_identity_and_permutation_4096():
+def test_f8_identity_and_permutation_4096(fmt):
     n = 4096
-    B = synth.uniform_f8(5, 1, n, n)
-    eye = synth.to_e4m3(np.eye(n, dtype=np.float32))
-    log("f8 identity 4096")
+    B = fmt.uniform(5, 1, n, n)
+    eye = fmt.to(np.eye(n, dtype=np.float32))
+    log(f"{fmt.name} identity 4096")
     C, _ = run(eye, B)
-    assert np.array_equal(wide(C), wide(B))  # every E4M3 value is a BF16 value
+    assert np.array_equal(wide(C), wide(B))  # every E4M3 and E5M2 value is a BF16 value
     p = synth.permutation(9, 2, n)
     P = np.zeros((n, n), np.float32)
     P[np.arange(n), p] = 1
-    log("f8 permutation 4096")
-    C, _ = run(synth.to_e4m3(P), B)
+    log(f"{fmt.name} permutation 4096")
+    C, _ = run(fmt.to(P), B)
     assert np.array_equal(wide(C), wide(B)[p])
 
 
-def test_f8_deterministic():
-    A, B = synth.workload(1024, 1024, 1024, "f8", seed=4)
-    log("f8 determinism")
+def test_f8_deterministic(fmt):
+    A, B = synth.workload(1024, 1024, 1024, fmt.name, seed=4)
+    log(f"{fmt.name} determinism")
     C1, _ = run(A, B)
     C2, _ = run(A, B, repeat=3)
     assert np.array_equal(_bits(C1), _bits(C2))
 
 
 @pytest.mark.parametrize("n", [256, 2048])
-def test_f8_random_full_check(n):
-    A, B = synth.workload(n, n, n, "f8")
+def test_f8_random_full_check(fmt, n):
+    A, B = synth.workload(n, n, n, fmt.name)
     for idx in CFGS if n == 256 else [None]:
-        cfg = None if idx is None else _cfg(idx)
-        log(f"f8 random {n}^3 cfg={'auto' if cfg is None else cfg.name.decode()}")
+        cfg = None if idx is None else _cfg(fmt, idx)
+        log(f"{fmt.name} random {n}^3 cfg={'auto' if cfg is None else cfg.name.decode()}")
         C, _ = run(A, B, cfg)
         rep = check_full(A, B, C)
         log(f"  max_rel={rep['max_rel']:.3e} max_abs={rep['max_abs']:.3e}")
@@ -164,10 +183,10 @@ SWEEP = [(4096, 4096, 4096), (8192, 8192, 1024), (4096, 11008, 4096), (4000, 400
 
 
 @pytest.mark.parametrize("shape", SWEEP, ids=lambda s: "x".join(map(str, s)))
-def test_f8_random_sampled_full_size(shape):
+def test_f8_random_sampled_full_size(fmt, shape):
     M, N, K = shape
-    A, B = synth.workload(M, N, K, "f8")
-    log(f"f8 random {shape} (auto config)")
+    A, B = synth.workload(M, N, K, fmt.name)
+    log(f"{fmt.name} random {shape} (auto config)")
     C, _ = run(A, B)
     rng = np.random.default_rng(0)
     rows = sorted(set([0, M - 1, M // 2] + rng.integers(0, M, 24).tolist()))
@@ -185,23 +204,23 @@ def test_f8_random_sampled_full_size(shape):
 # --- split-K -------------------------------------------------------------------
 @pytest.mark.parametrize("shape", [(200, 144, 1024), (130, 256, 4096), (1, 16, 256)],
                          ids=lambda s: "x".join(map(str, s)))
-def test_f8_splitk_exact_small_int(shape):
+def test_f8_splitk_exact_small_int(fmt, shape):
     M, N, K = shape
-    A, B = _ints(M, N, K, seed=11)
-    for cfg in gemm.configs(DT):
+    A, B = _ints(fmt, M, N, K, seed=11)
+    for cfg in gemm.configs(fmt.dt):
         for splits in (2, 3, 7):
             cfg.splits = splits
-            log(f"f8 split-K exact cfg={cfg.name.decode()} splits={splits} shape={shape}")
+            log(f"{fmt.name} split-K exact cfg={cfg.name.decode()} splits={splits} shape={shape}")
             C, _ = run(A, B, split=cfg)
             assert exact_equal(A, B, C), (cfg.name, splits)
 
 
-def test_f8_splitk_auto_full_size():
+def test_f8_splitk_auto_full_size(fmt):
     M, N, K = 1024, 1024, 8192
-    sel = gemm.gemm_select_splitk_config(DT, M, N, K)
+    sel = gemm.gemm_select_splitk_config(fmt.dt, M, N, K)
     assert sel.splits > 1
-    A, B = synth.workload(M, N, K, "f8")
-    log(f"f8 split-K auto {M}x{N}x{K}: {sel.name.decode()} splits={sel.splits}")
+    A, B = synth.workload(M, N, K, fmt.name)
+    log(f"{fmt.name} split-K auto {M}x{N}x{K}: {sel.name.decode()} splits={sel.splits}")
     C1, _ = run(A, B, split="auto")
     rep = check_rows(A, B, C1, [0, 1, 511, 1000, 1023])
     log(f"  rows: max_rel={rep['max_rel']:.3e}")
@@ -217,32 +236,32 @@ def _epi_ref(A, B, C0, e, bias):
 
 @pytest.mark.parametrize("shape", [(1, 16, 16), (31, 48, 32), (130, 272, 96), (257, 144, 64)],
                          ids=lambda s: "x".join(map(str, s)))
-def test_f8_epilogue_exact_small_int(shape):
+def test_f8_epilogue_exact_small_int(fmt, shape):
     M, N, K = shape
-    A, B = _ints(M, N, K, seed=13)
+    A, B = _ints(fmt, M, N, K, seed=13)
     C0 = synth.small_int(13, 2, M, N, -3, 3, dtype=synth.BF16)
     bias = synth.small_int(13, 3, 1, N, -3, 3).ravel()
     cases = [dict(alpha=2.0, beta=-1.0, act=0), dict(alpha=-1.0, beta=0.5, act=1),
              dict(alpha=1.0, beta=0.0, act=1)]
-    for cfg in gemm.configs(DT):
+    for cfg in gemm.configs(fmt.dt):
         for e in cases:
-            log(f"f8 epilogue exact cfg={cfg.name.decode()} {e} shape={shape}")
+            log(f"{fmt.name} epilogue exact cfg={cfg.name.decode()} {e} shape={shape}")
             C, _ = run(A, B, cfg, epi=dict(e, C0=C0 if e["beta"] != 0.0 else None, bias=bias))
             ref, _ = _epi_ref(A, B, C0, e, bias)
             assert np.array_equal(wide(C), rounded(ref, "bf16")), (cfg.name, e)
 
 
-def test_f8_epilogue_random_scale():
+def test_f8_epilogue_random_scale(fmt):
     """alpha as a per-tensor dequantisation scale, beta with the old C, bias
     and ReLU, within tolerance on the epilogue's error scale."""
     M, N, K = 300, 528, 704
-    A, B = synth.workload(M, N, K, "f8", seed=21)
+    A, B = synth.workload(M, N, K, fmt.name, seed=21)
     C0 = synth.uniform_bf16(21, 2, M, N)
     bias = synth.uniform_f32(21, 3, 1, N).ravel()
     e = dict(alpha=0.0625, beta=-0.3, act=1)
     ref, den = _epi_ref(A, B, C0, e, bias)
     for name, kw in (("auto", {}), ("padded", dict(pad=(16, 32, 8)))):
-        log(f"f8 epilogue random {name}")
+        log(f"{fmt.name} epilogue random {name}")
         C, _ = run(A, B, None, epi=dict(e, C0=C0, bias=bias), **kw)
         rep = oracle.check(C, ref, den, TOL)
         log(f"  max_rel={rep['max_rel']:.3e}")
@@ -252,24 +271,24 @@ def test_f8_epilogue_random_scale():
 # --- B given transposed ---------------------------------------------------------
 @pytest.mark.parametrize("shape", [(2, 16, 16), (127, 144, 80), (257, 128, 208), (65, 304, 512)],
                          ids=lambda s: "x".join(map(str, s)))
-def test_f8_bt_exact_small_int(shape):
+def test_f8_bt_exact_small_int(fmt, shape):
     M, N, K = shape
-    A = synth.small_int(29, 0, M, K, dtype=F8)
-    Bt = synth.small_int(29, 1, N, K, dtype=F8)
+    A = synth.small_int(29, 0, M, K, dtype=fmt.marker)
+    Bt = synth.small_int(29, 1, N, K, dtype=fmt.marker)
     ref, _ = oracle.gemm_rows_bt(A, Bt)
-    for cfg in gemm.configs(DT):
+    for cfg in gemm.configs(fmt.dt):
         for pad in ((0, 0, 0), (16, 32, 8)):
-            log(f"f8 bt exact cfg={cfg.name.decode()} shape={shape} pad={pad}")
+            log(f"{fmt.name} bt exact cfg={cfg.name.decode()} shape={shape} pad={pad}")
             C, _ = run(A, Bt, cfg, pad=pad, bt=True)
             assert np.array_equal(wide(C), rounded(ref, "bf16")), (cfg.name, pad)
 
 
-def test_f8_bt_full_size_sampled():
+def test_f8_bt_full_size_sampled(fmt):
     n = 4096
-    A, B = synth.workload(n, n, n, "f8", seed=5)
+    A, B = synth.workload(n, n, n, fmt.name, seed=5)
     Bt = np.ascontiguousarray(B.T)
     del B
-    log("f8 bt 4096^3")
+    log(f"{fmt.name} bt 4096^3")
     C, _ = run(A, Bt, None, bt=True)
     rows = np.array([0, 1, 255, 256, 2047, 4095])
     ref, den = oracle.gemm_rows_bt(A, Bt, rows=rows)
@@ -278,12 +297,13 @@ def test_f8_bt_full_size_sampled():
     assert rep["ok"], rep
 
 
-def test_f8_matmul_torch():
+def test_f8_matmul_torch(fmt):
     import torch
-    A, B = synth.workload(200, 272, 144, "f8", seed=37)
-    ta = torch.from_numpy(A.view(np.uint8)).cuda().view(torch.float8_e4m3fn)
-    tb = torch.from_numpy(B.view(np.uint8)).cuda().view(torch.float8_e4m3fn)
-    log("matmul f8")
+    A, B = synth.workload(200, 272, 144, fmt.name, seed=37)
+    tdt = getattr(torch, fmt.torch)
+    ta = torch.from_numpy(A.view(np.uint8)).cuda().view(tdt)
+    tb = torch.from_numpy(B.view(np.uint8)).cuda().view(tdt)
+    log(f"matmul {fmt.name}")
     out = gemm.matmul(ta, tb)
     torch.cuda.synchronize()
     assert out.dtype == torch.bfloat16

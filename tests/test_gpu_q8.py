@@ -22,7 +22,8 @@ from tests.gpu_util import log, run_q8
 pytestmark = pytest.mark.gpu
 
 KINDS = {"f32": (gemm.DTYPE_F32, np.float32), "f16": (gemm.DTYPE_F16, np.float16),
-         "bf16": (gemm.DTYPE_BF16, synth.BF16), "f8": (gemm.DTYPE_F8, synth.F8)}
+         "bf16": (gemm.DTYPE_BF16, synth.BF16), "f8": (gemm.DTYPE_F8, synth.F8),
+         "e5m2": (gemm.DTYPE_E5M2, synth.E5M2)}
 
 
 def _cfgs(kind):

@@ -19,7 +19,8 @@ from tests.gpu_util import log, rounded, run, wide
 pytestmark = pytest.mark.gpu
 
 KINDS = {"f32": (gemm.DTYPE_F32, np.float32), "f16": (gemm.DTYPE_F16, np.float16),
-         "bf16": (gemm.DTYPE_BF16, synth.BF16), "f8": (gemm.DTYPE_F8, synth.F8)}
+         "bf16": (gemm.DTYPE_BF16, synth.BF16), "f8": (gemm.DTYPE_F8, synth.F8),
+         "e5m2": (gemm.DTYPE_E5M2, synth.E5M2)}
 
 
 def _cfgs(kind):
@@ -51,7 +52,7 @@ def test_trans_a_exact_small_int(kind, tb):
                 C, _ = run(A, B, cfg, bt=tb, at=True)
             except gemm.GemmError as e:
                 # Variants whose A^T rows would be under 256 bytes have no form.
-                assert e.status == gemm.GEMM_ERR_UNSUPPORTED and kind == "f8" and cfg.bm < 256
+                assert e.status == gemm.GEMM_ERR_UNSUPPORTED and kind in ("f8", "e5m2") and cfg.bm < 256
                 continue
             assert np.array_equal(wide(C), want), (cfg.name, (M, N, K))
 
@@ -99,10 +100,12 @@ def test_trans_a0_delegates(kind):
         A, B = _operands(kind, M, N, K, False, tb, seed=3)
         want = rounded(oracle.gemm_rows_trans(A, B, False, tb)[0], kind)
         log(f"{kind} trans_a=0 trans_b={int(tb)}")
-        bits = {"f32": np.float32, "f16": np.float16, "bf16": np.int16, "f8": np.uint8}[kind]
+        bits = {"f32": np.float32, "f16": np.float16, "bf16": np.int16, "f8": np.uint8,
+                "e5m2": np.uint8}[kind]
         a = torch.from_numpy(np.ascontiguousarray(A).view(bits)).cuda()
         b = torch.from_numpy(np.ascontiguousarray(B).view(bits)).cuda()
-        cbits = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.int16, "f8": torch.int16}[kind]
+        cbits = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.int16, "f8": torch.int16,
+                 "e5m2": torch.int16}[kind]
         c = torch.zeros((M, N), dtype=cbits, device="cuda")
         st = gemm.entry(dt, "_trans")(M, N, K, a.data_ptr(), K, b.data_ptr(), K if tb else N,
                                       c.data_ptr(), N, torch.cuda.current_stream().cuda_stream, None,
@@ -110,14 +113,14 @@ def test_trans_a0_delegates(kind):
         torch.cuda.synchronize()
         assert st == gemm.GEMM_OK, gemm.gemm_last_error()
         out = c.cpu().numpy()
-        if kind in ("bf16", "f8"):
+        if kind in ("bf16", "f8", "e5m2"):
             out = out.view(np.uint16).view(synth.BF16)
         assert np.array_equal(wide(out), want)
 
 
 @pytest.mark.parametrize("kind", list(KINDS))
 def test_trans_off_layout_refused(kind):
-    w = {"f32": 4, "f16": 8, "bf16": 8, "f8": 16}[kind]
+    w = {"f32": 4, "f16": 8, "bf16": 8, "f8": 16, "e5m2": 16}[kind]
     A, B = _operands(kind, 64 + w // 2 if w > 1 else 66, 64, 64, True, False, seed=5)
     log(f"{kind} trans unsupported")
     with pytest.raises(gemm.GemmError) as e:

@@ -33,7 +33,8 @@ def test_bad_arguments(lib):
 
 
 @pytest.mark.parametrize("name,kind", [("f16_rne_halfway.txt", "f16"), ("bf16_rne_halfway.txt", "bf16"),
-                                       ("f8_bf16_rne_halfway.txt", "f8")])
+                                       ("f8_bf16_rne_halfway.txt", "f8"),
+                                       ("e5m2_bf16_rne_halfway.txt", "e5m2")])
 def test_rounding_probe_fixtures(lib, name, kind):
     """The hand-worked output-rounding fixtures: the oracle's exact sums of
     their A and B are the ties the headers describe, and the stored C
@@ -47,9 +48,9 @@ def test_rounding_probe_fixtures(lib, name, kind):
     g = {}
     for r in golden_data.rows(name):
         g.setdefault(r[0], []).append([int(x, 16) for x in r[2:]])
-    ins = np.uint8 if kind == "f8" else np.uint16
+    ins = np.uint8 if kind in ("f8", "e5m2") else np.uint16
     bits = {k: np.array(v, dtype=ins if k in "AB" else np.uint16) for k, v in g.items()}
-    view = {"f16": np.float16, "bf16": synth.BF16, "f8": synth.F8}[kind]
+    view = {"f16": np.float16, "bf16": synth.BF16, "f8": synth.F8, "e5m2": synth.E5M2}[kind]
     C, _ = oracle.gemm_rows(bits["A"].view(view), bits["B"].view(view), lib=lib)
     c32 = C.astype(np.float32)
     assert np.array_equal(c32.astype(np.float64), C), "the sums are exact in FP32"
@@ -63,4 +64,4 @@ def test_rounding_probe_fixtures(lib, name, kind):
     # Four (FP8 probe: three) of the six sums sit exactly halfway between
     # neighbours on [1, 2).
     frac = (C - 1.0) / ulp
-    assert np.sum(frac - np.floor(frac) == 0.5) == (3 if kind == "f8" else 4)
+    assert np.sum(frac - np.floor(frac) == 0.5) == (3 if kind in ("f8", "e5m2") else 4)

@@ -55,6 +55,17 @@ MUTANTS = {
     "e4m3_all_top_exponent_nan": ("if (expo == 0xf && frac == 0x7)", "if (expo == 0xf)"),
     "e4m3_decoded_as_f16": ("    if (dtype == ORACLE_E4M3)\n        return oracle_e4m3_to_f64",
                             "    if (0)\n        return oracle_e4m3_to_f64"),
+    "e5m2_bias": ("mag = ldexp((double)(0x4 | frac), expo - 17);",
+                  "mag = ldexp((double)(0x4 | frac), expo - 16);"),
+    "e5m2_no_hidden_bit": ("mag = ldexp((double)(0x4 | frac), expo - 17);",
+                           "mag = ldexp((double)frac, expo - 17);"),
+    "e5m2_subnormal": ("mag = ldexp((double)frac, -16);", "mag = ldexp((double)frac, -17);"),
+    "e5m2_fraction_width": ("const int expo = (b >> 2) & 0x1f;\n    const int frac = b & 0x3;",
+                            "const int expo = (b >> 3) & 0xf;\n    const int frac = b & 0x7;"),
+    "e5m2_infinity_as_nan": ("    if (expo == 0x1f)\n        mag = frac ? NAN : INFINITY;",
+                             "    if (expo == 0x1f)\n        mag = NAN;"),
+    "e5m2_decoded_as_e4m3": ("    if (dtype == ORACLE_E5M2)\n        return oracle_e5m2_to_f64",
+                             "    if (dtype == ORACLE_E5M2)\n        return oracle_e4m3_to_f64"),
     "q8_ties_up": ("r = (fmod(f, 2.0) == 0.0) ? f : f + 1.0;", "r = f + 1.0;"),
     "q8_truncate": ("    else if (frac < 0.5)\n        r = f;", "    else if (frac < 0.999)\n        r = f;"),
     "q8_no_low_saturation": ("    if (v <= -128.0)\n        return -128;", "    if (v <= -129.0)\n        return -129;"),

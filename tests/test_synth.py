@@ -108,3 +108,27 @@ def test_to_e4m3_matches_torch():
     assert np.array_equal(back[ok], tref[ok])
     ints = synth.small_int(4, 1, 6, 6, dtype=synth.F8)
     assert np.array_equal(synth.e4m3_to_f32(ints), synth.small_int(4, 1, 6, 6))
+
+
+def test_to_e5m2_matches_torch():
+    """RNE onto FP8 E5M2 against torch's float32 -> float8_e5m2 (a library
+    routine): the workload's values, ties (1 + 2**-3 is half an ulp above 1
+    -> 1.0; 1 + 3 * 2**-3 ties to 1.5), subnormals, the top of the range
+    (57344; from 61440 on, infinity) and signed zeros; and the decode back,
+    infinities included."""
+    import torch
+    x = np.concatenate([synth.uniform_f32(6, 0, 200, 200).ravel(),
+                        np.array([1 + 2.0 ** -3, 1 + 3 * 2.0 ** -3, -1.5, 57344.0, 61439.0, 61440.0,
+                                  -70000.0, 2.0 ** -16, 3 * 2.0 ** -17, 2.0 ** -18, 0.0, -0.0],
+                                 np.float32)])
+    mine = synth.to_e5m2(x).view(np.uint8)
+    ref = torch.from_numpy(x).to(torch.float8_e5m2).view(torch.uint8).numpy()
+    assert np.array_equal(mine, ref)
+    codes = np.arange(256, dtype=np.uint8)
+    back = synth.e5m2_to_f32(codes)
+    tref = torch.from_numpy(codes).view(torch.float8_e5m2).float().numpy()
+    assert np.array_equal(np.isnan(back), np.isnan(tref))
+    ok = ~np.isnan(tref)
+    assert np.array_equal(back[ok], tref[ok])
+    ints = synth.small_int(4, 1, 6, 6, dtype=synth.E5M2)
+    assert np.array_equal(synth.e5m2_to_f32(ints), synth.small_int(4, 1, 6, 6))
