@@ -330,10 +330,11 @@ bool vector_path(int dtype, const void* A, int64_t lda, const void* B, int64_t l
          ldc % wc == 0 && K % w == 0 && N % w == 0;
 }
 
-// FP8 runs on the LDS-direct kernels only (no general kernel).
+// FP8 operands off the vector layout run on the general 16-bit kernel
+// (widened to bfloat16 while staging); a form that it lacks is refused.
 gemm_status_t f8_unsupported() {
   return fail(GEMM_ERR_UNSUPPORTED,
-              "FP8 operands need 16-byte aligned A, B, C, K, N, lda and ldb multiples of 16, "
+              "this FP8 form needs 16-byte aligned A, B, C, K, N, lda and ldb multiples of 16, "
               "ldc a multiple of 8, and byte offsets below 2^31");
 }
 
@@ -341,6 +342,7 @@ Params make_params(int dtype, const void* A, int64_t lda, const void* B, int64_t
                    int64_t ldc, int64_t M, int64_t N, int64_t K) {
   Params p;
   p.bf16 = dtype == GEMM_DTYPE_BF16;
+  p.f8 = dtype == GEMM_DTYPE_F8 ? 1 : dtype == GEMM_DTYPE_E5M2 ? 2 : 0;
   p.A = A;
   p.B = B;
   p.C = C;
@@ -358,7 +360,6 @@ gemm_status_t launch_plain(int dtype, const gemm_config_t& cfg, int64_t M, int64
                            int64_t ldc, void* stream) {
   const Params p = make_params(dtype, A, lda, B, ldb, C, ldc, M, N, K);
   const bool vec = vector_path(dtype, A, lda, B, ldb, C, ldc, K, N);
-  if (is_f8(dtype) && !vec) return f8_unsupported();
   const TileMap map = make_map(cfg, M, N);
   const hipError_t e = table().v[dtype][cfg.id].launch(p, map, vec, static_cast<hipStream_t>(stream));
   if (e == hipErrorNotSupported && is_f8(dtype)) return f8_unsupported();
@@ -392,7 +393,6 @@ gemm_status_t run_bt(int dtype, int64_t M, int64_t N, int64_t K, const void* A, 
   Params p = make_params(dtype, A, lda, Bt, ldbt, C, ldc, M, N, K);
   p.bt = true;
   const bool vec = vector_path(dtype, A, lda, Bt, ldbt, C, ldc, K, N);
-  if (is_f8(dtype) && !vec) return f8_unsupported();
   const TileMap map = make_map(cfg, M, N);
   const hipError_t e =
       table().v[dtype][cfg.id].launch_bt(p, map, vec, static_cast<hipStream_t>(stream));
@@ -425,7 +425,6 @@ gemm_status_t run_epi(int dtype, int64_t M, int64_t N, int64_t K, const void* A,
   // The vector forms read the bias four floats at a time.
   const bool vec = vector_path(dtype, A, lda, B, ldb, C, ldc, K, N) &&
                    (!epi->bias || aligned16(epi->bias));
-  if (is_f8(dtype) && !vec) return f8_unsupported();
   const TileMap map = make_map(cfg, M, N);
   const hipError_t e =
       table().v[dtype][cfg.id].launch_epi(p, map, vec, static_cast<hipStream_t>(stream));

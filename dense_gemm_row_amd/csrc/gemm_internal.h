@@ -71,7 +71,43 @@ struct Params {
   // hold bfloat16 instead of binary16.  The general FP16 kernel reads it at
   // launch; the LDS-direct kernels have it (and FP8) in their template.
   bool bf16 = false;
+  // FP8 A and B (0: none, 1: E4M3, 2: E5M2; C is bfloat16).  The
+  // LDS-direct kernels have the format in their template; the general
+  // 16-bit kernel reads this at launch and widens each FP8 element to
+  // bfloat16 (exactly) while staging, so FP8 operands off the vector layout
+  // run there on the bf16 matrix instruction.
+  int f8 = 0;
 };
+
+// ---------------------------------------------------------------------------
+// FP8 byte -> bfloat16 bit pattern, exact (every E4M3 and E5M2 value is a
+// bfloat16 value: at most 4 significant bits, exponents within bfloat16's
+// range).  From the OCP 8-bit definitions: E4M3 has exponent bias 7,
+// subnormals fraction * 2^-9, NaN at exponent 15 with fraction 7 and no
+// infinities; E5M2 has bias 15, subnormals fraction * 2^-16, infinities and
+// NaN at exponent 31.  A subnormal fraction m with leading bit p becomes
+// the normal 2^(p - scale) * (1 + (m - 2^p) / 2^p).
+// ---------------------------------------------------------------------------
+__host__ __device__ constexpr unsigned short e4m3_to_bf16(unsigned char b) {
+  const unsigned s = (b & 0x80u) << 8, e = (b >> 3) & 0xfu, m = b & 0x7u;
+  if (e == 0xf && m == 0x7) return (unsigned short)(s | 0x7fc0u);
+  if (e == 0) {
+    if (m == 0) return (unsigned short)s;
+    const unsigned p = m >= 4 ? 2 : m >= 2 ? 1 : 0;  // m * 2^-9 = 2^(p-9) * ...
+    return (unsigned short)(s | ((p + 118u) << 7) | ((m << (7 - p)) & 0x7fu));
+  }
+  return (unsigned short)(s | ((e + 120u) << 7) | (m << 4));
+}
+__host__ __device__ constexpr unsigned short e5m2_to_bf16(unsigned char b) {
+  const unsigned s = (b & 0x80u) << 8, e = (b >> 2) & 0x1fu, m = b & 0x3u;
+  if (e == 0x1f) return (unsigned short)(s | (m ? 0x7fc0u : 0x7f80u));
+  if (e == 0) {
+    if (m == 0) return (unsigned short)s;
+    const unsigned p = m >= 2 ? 1 : 0;  // m * 2^-16 = 2^(p-16) * ...
+    return (unsigned short)(s | ((p + 111u) << 7) | ((m << (7 - p)) & 0x7fu));
+  }
+  return (unsigned short)(s | ((e + 112u) << 7) | (m << 5));
+}
 
 // ---------------------------------------------------------------------------
 // The two 16-bit element types of the half-precision kernels: binary16

@@ -30,6 +30,13 @@
 // * VEC=true: A, B, C 16-byte aligned and K, N, lda, ldb, ldc multiples of
 //   8 (whole 16-byte chunks in or out of range).  VEC=false: element loads
 //   and stores with per-element masks.
+// * FP8 operands off the LDS-direct kernels' layout (IN = 1 E4M3, 2 E5M2)
+//   run here too: the masked element loads read bytes and widen each to its
+//   bfloat16 value, which is exact (at most 4 significant bits, exponents in
+//   range), and the bf16 form computes the same FP32-accumulated product
+//   into a bfloat16 C.
+#include <type_traits>
+
 #include "gemm_internal.h"
 
 namespace gemm {
@@ -73,16 +80,28 @@ struct Shape {
   }
 };
 
+// The 16-bit pattern of input element x: itself, or an FP8 byte widened to
+// bfloat16.
+template <int IN, class T>
+__device__ __forceinline__ unsigned short in16(T x) {
+  if constexpr (IN == 1) return e4m3_to_bf16(x);
+  else if constexpr (IN == 2) return e5m2_to_bf16(x);
+  else return x;
+}
+
 // BT: B given transposed (p.bt: Bt, N x K row-major).  Its rows are already
 // k-contiguous per output column, so they are staged like A's chunks into
 // the transposed B tile (no register transpose).  BF: the elements are
 // bfloat16 (v_mfma_f32_32x32x16_bf16 and bfloat16 conversions; the staging
-// moves 16-bit patterns either way).
-template <int BM, int BN, int WM, int WN, bool VEC, bool EPI, bool BT, bool BF>
+// moves 16-bit patterns either way).  IN: 0 for 16-bit inputs, 1 / 2 for
+// FP8 E4M3 / E5M2 bytes (element loads only, widened to bfloat16).
+template <int BM, int BN, int WM, int WN, bool VEC, bool EPI, bool BT, bool BF, int IN = 0>
 __global__ void __launch_bounds__((Shape<BM, BN, WM, WN>::NT))
 hgemm_mfma_kernel(Params p, TileMap map) {
   using S = Shape<BM, BN, WM, WN>;
   constexpr int NT = S::NT, MB = S::MB, NB = S::NB, CA = S::CA, CB = S::CB;
+  static_assert(IN == 0 || (BF && !VEC), "FP8 inputs: bfloat16 compute, element loads");
+  using In = std::conditional_t<IN == 0, unsigned short, unsigned char>;
 
   __shared__ __attribute__((aligned(16))) unsigned char smem[2 * S::STAGE];
 
@@ -90,8 +109,8 @@ hgemm_mfma_kernel(Params p, TileMap map) {
   tile_of_block(blockIdx.x, map, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
   const int M = p.M, N = p.N, K = p.K;
-  const unsigned short* __restrict__ A = static_cast<const unsigned short*>(p.A);
-  const unsigned short* __restrict__ B = static_cast<const unsigned short*>(p.B);
+  const In* __restrict__ A = static_cast<const In*>(p.A);
+  const In* __restrict__ B = static_cast<const In*>(p.B);
   unsigned short* __restrict__ C = static_cast<unsigned short*>(p.C);
 
   const int tid = threadIdx.x;
@@ -100,7 +119,7 @@ hgemm_mfma_kernel(Params p, TileMap map) {
   const int wm0 = (wave / S::WAVES_N) * WM, wn0 = (wave % S::WAVES_N) * WN;
 
   // A staging: chunk (row r, k-chunk q) per slot.
-  const unsigned short* a_src[CA];
+  const In* a_src[CA];
   bool a_row_ok[CA];
   int a_k[CA], a_dst[CA];
 #pragma unroll
@@ -113,7 +132,7 @@ hgemm_mfma_kernel(Params p, TileMap map) {
     a_dst[i] = S::a_chunk(r, q);
   }
   // B staging: 8x8 block (k-group r, column chunk c) per slot.
-  const unsigned short* b_src[CB];
+  const In* b_src[CB];
   bool b_on[CB];
   int b_k[CB], b_col[CB], b_c[CB], b_r[CB];
 #pragma unroll
@@ -129,7 +148,7 @@ hgemm_mfma_kernel(Params p, TileMap map) {
   }
 
   // BT staging: Bt chunk (tile column n, k chunk q) per slot.
-  const unsigned short* bt_src[S::CBT];
+  const In* bt_src[S::CBT];
   bool bt_ok[S::CBT];
   int bt_k[S::CBT], bt_dst[S::CBT];
 #pragma unroll
@@ -150,14 +169,14 @@ hgemm_mfma_kernel(Params p, TileMap map) {
 #pragma unroll
     for (int i = 0; i < CA; ++i) {
       const int kg = k0 + a_k[i];
-      if (VEC) {
+      if constexpr (VEC) {
         u32x4 v = {0u, 0u, 0u, 0u};
         if (a_row_ok[i] && kg < K) v = *reinterpret_cast<const u32x4*>(a_src[i] + k0);
         ra[i] = v;
       } else {
         unsigned short e[8];
 #pragma unroll
-        for (int t = 0; t < 8; ++t) e[t] = (a_row_ok[i] && kg + t < K) ? a_src[i][k0 + t] : 0;
+        for (int t = 0; t < 8; ++t) e[t] = (a_row_ok[i] && kg + t < K) ? in16<IN>(a_src[i][k0 + t]) : 0;
 #pragma unroll
         for (int d = 0; d < 4; ++d) ra[i][d] = e[2 * d] | ((unsigned)e[2 * d + 1] << 16);
       }
@@ -166,14 +185,14 @@ hgemm_mfma_kernel(Params p, TileMap map) {
 #pragma unroll
       for (int i = 0; i < S::CBT; ++i) {
         const int kg = k0 + bt_k[i];
-        if (VEC) {
+        if constexpr (VEC) {
           u32x4 v = {0u, 0u, 0u, 0u};
           if (bt_ok[i] && kg < K) v = *reinterpret_cast<const u32x4*>(bt_src[i] + k0);
           rbt[i] = v;
         } else {
           unsigned short e[8];
 #pragma unroll
-          for (int t = 0; t < 8; ++t) e[t] = (bt_ok[i] && kg + t < K) ? bt_src[i][k0 + t] : 0;
+          for (int t = 0; t < 8; ++t) e[t] = (bt_ok[i] && kg + t < K) ? in16<IN>(bt_src[i][k0 + t]) : 0;
 #pragma unroll
           for (int d = 0; d < 4; ++d) rbt[i][d] = e[2 * d] | ((unsigned)e[2 * d + 1] << 16);
         }
@@ -185,15 +204,16 @@ hgemm_mfma_kernel(Params p, TileMap map) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int kg = k0 + b_k[i] + e;
-        const unsigned short* src = b_src[i] + (int64_t)(k0 + e) * p.ldb;
-        if (VEC) {
+        const In* src = b_src[i] + (int64_t)(k0 + e) * p.ldb;
+        if constexpr (VEC) {
           u32x4 v = {0u, 0u, 0u, 0u};
           if (b_on[i] && kg < K && b_col[i] < N) v = *reinterpret_cast<const u32x4*>(src);
           rb[i][e] = v;
         } else {
           unsigned short x[8];
 #pragma unroll
-          for (int t = 0; t < 8; ++t) x[t] = (b_on[i] && kg < K && b_col[i] + t < N) ? src[t] : 0;
+          for (int t = 0; t < 8; ++t)
+            x[t] = (b_on[i] && kg < K && b_col[i] + t < N) ? in16<IN>(src[t]) : 0;
 #pragma unroll
           for (int d = 0; d < 4; ++d) rb[i][e][d] = x[2 * d] | ((unsigned)x[2 * d + 1] << 16);
         }
@@ -285,7 +305,7 @@ hgemm_mfma_kernel(Params p, TileMap map) {
       const int row = m0 + wm0 + 32 * mb + 8 * (r / 4) + 4 * h + (r % 4);
       if (row >= M) continue;
       unsigned short* dst = C + (int64_t)row * p.ldc + col;
-      if (VEC) {
+      if constexpr (VEC) {
         if (col < N) {
           if constexpr (NB == 4) {
             uint2 v;
@@ -332,8 +352,26 @@ hipError_t launch_typed(const Params& p, const TileMap& map, bool vec, hipStream
 }
 
 // One launch function for both element types: p.bf16 picks the instance.
+// FP8 operands (p.f8): element loads widened to bfloat16, bf16 compute.
+template <int BM, int BN, int WM, int WN, int IN>
+hipError_t launch_f8(const Params& p, const TileMap& map, hipStream_t stream) {
+  using S = Shape<BM, BN, WM, WN>;
+  const dim3 grid(map.tiles_m * map.tiles_n), block(S::NT);
+  if (p.bt) {
+    if (p.epi.on) return hipErrorNotSupported;
+    hipLaunchKernelGGL((hgemm_mfma_kernel<BM, BN, WM, WN, false, false, true, true, IN>), grid, block, 0, stream, p, map);
+  } else if (p.epi.on) {
+    hipLaunchKernelGGL((hgemm_mfma_kernel<BM, BN, WM, WN, false, true, false, true, IN>), grid, block, 0, stream, p, map);
+  } else {
+    hipLaunchKernelGGL((hgemm_mfma_kernel<BM, BN, WM, WN, false, false, false, true, IN>), grid, block, 0, stream, p, map);
+  }
+  return hipGetLastError();
+}
+
 template <int BM, int BN, int WM, int WN>
 hipError_t launch(const Params& p, const TileMap& map, bool vec, hipStream_t stream) {
+  if (p.f8) return p.f8 == 1 ? launch_f8<BM, BN, WM, WN, 1>(p, map, stream)
+                             : launch_f8<BM, BN, WM, WN, 2>(p, map, stream);
   return p.bf16 ? launch_typed<BM, BN, WM, WN, true>(p, map, vec, stream)
                 : launch_typed<BM, BN, WM, WN, false>(p, map, vec, stream);
 }

@@ -813,9 +813,9 @@ hipError_t launch(const Params& p, const TileMap& map, bool vec, hipStream_t str
                            : (int64_t)(p.M + S::BM) * p.lda * ES > lim || (int64_t)p.M * p.lda * ES > lim;
   if (!vec || a_far || b_far || (S::EPI && (int64_t)p.M * p.ldc * 2 > lim)) {
     // The general kernel has no split-K form (the caller runs unsplit) and
-    // no FP8, INT8-output or transposed-A form (the caller reports the
-    // operands unsupported).
-    if (p.splits > 1 || S::F8 || S::Q8 || S::AT) return hipErrorNotSupported;
+    // no INT8-output or transposed-A form (the caller reports the operands
+    // unsupported); it takes FP8 operands through p.f8.
+    if (p.splits > 1 || S::Q8 || S::AT) return hipErrorNotSupported;
     return hgemm_launch_shape(S::BM, S::BN, S::WM, S::WN, p, map, vec, stream);
   }
   const int64_t a_bytes = p.K <= 0 ? 0

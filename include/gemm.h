@@ -157,10 +157,14 @@ gemm_status_t gemm_bf16(int64_t M, int64_t N, int64_t K,
  * range; bfloat16 keeps FP32's).  FP8 is the tier above FP16 that the
  * GB300 GEMM article names for the matrix units (section 1.1).  Inputs are
  * taken as they are (no scale factors; the fused-epilogue form's alpha
- * applies a per-tensor scale).  Only the vector layout is supported: A, B,
- * C 16-byte aligned, K, N, lda, ldb multiples of 16, ldc a multiple of 8
- * (else UNSUPPORTED, before any launch).  Every gemm_f16_* entry point has a
- * gemm_f8_* counterpart with gemm_f8_t A and B and gemm_bf16_t C;
+ * applies a per-tensor scale).  Any shape and alignment is accepted: the
+ * vector layout (A, B, C 16-byte aligned, K, N, lda, ldb multiples of 16,
+ * ldc a multiple of 8) runs on the 8-bit matrix instruction, anything else
+ * on the general kernel, which widens each FP8 element to its (exactly
+ * equal) bfloat16 value and computes on the bf16 instruction.  Every
+ * gemm_f16_* entry point has a gemm_f8_* counterpart with gemm_f8_t A and B
+ * and gemm_bf16_t C, with the same layout rules (the INT8 epilogue and A
+ * transposed need the vector layout, as for every type);
  * gemm_splitk_workspace_bytes takes GEMM_DTYPE_F8.
  */
 gemm_status_t gemm_f8(int64_t M, int64_t N, int64_t K,
@@ -415,8 +419,8 @@ gemm_status_t gemm_f8_epi_q8(int64_t M, int64_t N, int64_t K,
  * bits: FP16's exponent range, one fraction bit fewer than E4M3).  FP32
  * accumulation, bfloat16 output rounded to nearest even; the same kernels
  * as FP8 E4M3 with the E5M2 operand format of the matrix instruction.  Each
- * entry point has the contract of its gemm_f8_* counterpart (vector layout
- * only, the same forms, sizes and errors), with gemm_e5m2_t A and B;
+ * entry point has the contract of its gemm_f8_* counterpart (the same
+ * forms, layouts, sizes and errors), with gemm_e5m2_t A and B;
  * gemm_splitk_workspace_bytes takes GEMM_DTYPE_E5M2.
  */
 gemm_status_t gemm_e5m2(int64_t M, int64_t N, int64_t K,

@@ -12,7 +12,10 @@ accumulation, bfloat16 output.  Every test runs for both encodings (the
 * Random uniform[-1, 1) inputs rounded to E4M3 or E5M2: max_ij |C - C_ref| /
   sum_k |A_ik||B_kj| <= 5e-3 (bfloat16's unit roundoff plus the FP32
   accumulation bound), judged after the output rounding.
-* Operands off the vector layout are refused with GEMM_ERR_UNSUPPORTED.
+* Operands off the vector layout (ragged K or N, odd leading dimensions,
+  misaligned pointers) run on the general kernel, which widens each FP8
+  element to bfloat16: the same exact results, and a decode pin that sends
+  every finite code through it.
 """
 from types import SimpleNamespace
 
@@ -104,16 +107,68 @@ def test_f8_padded_leading_dimensions(fmt, pad):
         assert exact_equal(A, B, C), cfg.name
 
 
-@pytest.mark.parametrize("pad,offset", [((1, 0, 0), (0, 0, 0)), ((0, 0, 0), (1, 0, 0)),
-                                        ((0, 0, 0), (0, 0, 1))])
-def test_f8_off_vector_layout_is_refused(fmt, pad, offset):
-    """lda not a multiple of 16, A or C misaligned: UNSUPPORTED, and C
-    untouched (run's canary check)."""
-    A, B = _ints(fmt, 64, 64, 64, seed=5)
-    log(f"{fmt.name} unsupported pad={pad} offset={offset}")
-    with pytest.raises(gemm.GemmError) as e:
-        run(A, B, None, pad=pad, offset=offset)
-    assert e.value.status == gemm.GEMM_ERR_UNSUPPORTED
+GENERAL_SHAPES = [(1, 1, 1), (3, 5, 7), (33, 17, 65), (130, 70, 100), (257, 300, 129)]
+
+
+@pytest.mark.parametrize("shape", GENERAL_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_f8_general_layouts_exact(fmt, shape):
+    """K or N off the 16-element grid, odd leading dimensions, misaligned
+    A, B or C: every form that has a general kernel (plain, forced variant,
+    transposed B, fused epilogue, split-K falling back to one pass) gives
+    the exact result, and nothing outside C changes (run's canary check)."""
+    M, N, K = shape
+    A, B = _ints(fmt, M, N, K, seed=M + N + K)
+    want = np.array(rounded(oracle.gemm_rows(A, B)[0], "bf16"))
+    Bt = np.ascontiguousarray(B.T)
+    for pad, offset in (((0, 0, 0), (0, 0, 0)), ((1, 3, 5), (0, 0, 0)), ((0, 0, 0), (1, 3, 1))):
+        log(f"{fmt.name} general {shape} pad={pad} offset={offset}")
+        C, _ = run(A, B, None, pad=pad, offset=offset)
+        assert np.array_equal(wide(C), want), (pad, offset)
+        C, _ = run(A, B, _cfg(fmt, 0), pad=pad, offset=offset)
+        assert np.array_equal(wide(C), want), ("forced", pad, offset)
+        C, _ = run(A, Bt, None, pad=pad, offset=offset, bt=True)
+        assert np.array_equal(wide(C), want), ("bt", pad, offset)
+        sk = _cfg(fmt, 0)
+        sk.splits = 3
+        C, _ = run(A, B, split=sk, pad=pad, offset=offset)
+        assert np.array_equal(wide(C), want), ("split-K", pad, offset)
+    C0 = synth.small_int(3, 2, M, N, -3, 3, dtype=synth.BF16)
+    bias = synth.small_int(3, 3, 1, N, -3, 3).ravel()
+    e = dict(alpha=2.0, beta=-1.0, act=1)
+    ref, _ = _epi_ref(A, B, C0, e, bias)
+    log(f"{fmt.name} general epilogue {shape}")
+    C, _ = run(A, B, None, pad=(1, 3, 5), epi=dict(e, C0=C0, bias=bias, bias_offset=1))
+    assert np.array_equal(wide(C), rounded(ref, "bf16"))
+
+
+def test_f8_general_path_decodes_every_code(fmt):
+    """Every finite code as a row of A (K off the 16-element grid, so the
+    general kernel's byte-to-bfloat16 widening runs) times the identity:
+    C's row is the decoded codes, value for value, as the oracle decodes
+    them."""
+    codes = np.arange(256, dtype=np.uint8)
+    vals = wide(codes.view(fmt.marker))
+    finite = codes[np.isfinite(vals)]
+    K = finite.size
+    assert K % 16 != 0
+    A = finite.reshape(1, K).view(fmt.marker)
+    eye = fmt.to(np.eye(K, dtype=np.float32))
+    log(f"{fmt.name} decode every code through the general kernel (K={K})")
+    C, _ = run(A, eye)
+    dec = (oracle.e4m3_to_f64 if fmt.name == "f8" else oracle.e5m2_to_f64)(finite)
+    # (The column of -0 sums to +0: -0 plus the +0 products.)
+    assert np.array_equal(wide(C).ravel(), dec)
+
+
+def test_f8_general_random(fmt):
+    """Random inputs off the vector layout, within tolerance."""
+    M, N, K = 300, 203, 517
+    A, B = synth.workload(M, N, K, fmt.name, seed=23)
+    log(f"{fmt.name} general random {M}x{N}x{K}")
+    C, _ = run(A, B, None, pad=(3, 1, 0))
+    rep = check_full(A, B, C)
+    log(f"  max_rel={rep['max_rel']:.3e}")
+    assert rep["ok"], rep
 
 
 def test_f8_output_rounds_to_nearest_even(fmt):
