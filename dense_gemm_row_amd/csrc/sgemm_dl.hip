@@ -452,7 +452,8 @@ sgemm_dl_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = row_of(mb, r);
-        if (row < M && col < N) *reinterpret_cast<vecNB*>(C + (int64_t)row * p.ldc + col) = acc_vec(mb, r);
+        if (row < M && col < N)  // streaming store (C is written once)
+          __builtin_nontemporal_store(acc_vec(mb, r), reinterpret_cast<vecNB*>(C + (int64_t)row * p.ldc + col));
       }
   } else if constexpr (S::Q8) {
     // INT8-quantising epilogue: the lane's NB adjacent columns of a row
