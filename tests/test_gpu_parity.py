@@ -15,7 +15,7 @@ import pytest
 import oracle
 from dense_gemm_row_amd import gemm, synth
 from tests import golden_data
-from tests.gpu_util import check_full, check_rows, exact_equal, log, run
+from tests.gpu_util import check_full, check_rows, exact_equal, log, rounded, run, wide
 
 pytestmark = pytest.mark.gpu
 
@@ -487,3 +487,43 @@ def test_offsets_past_31_bits(kind):
     out = out.view(np.uint16).view(synth.BF16) if kind in ("bf16", "f8") else out
     assert exact_equal(A, B, out)
     del a_big
+
+
+# --- the largest operands the LDS-direct kernels address ---------------------------
+@pytest.mark.parametrize("kind", ["f16", "f8"])
+@pytest.mark.parametrize("M", [65024, 65536], ids=["below", "above"])
+def test_operands_at_the_31_bit_limit(kind, M):
+    """A spanning just under 2^31 bytes including the last tile's rows past
+    M (the 256 x 256 LDS-direct variant addresses it with 32-bit buffer
+    offsets: M = 65024) and just over (M = 65536: the same call runs on the
+    general kernel with 64-bit addresses).  Small-integer values drawn on
+    the device from a seeded generator; sampled rows of C against the
+    oracle, exactly."""
+    import torch
+    es = {"f16": 2, "f8": 1}[kind]
+    K, N = 32768 // es, 256
+    tdt = {"f16": torch.float16, "f8": torch.float8_e4m3fn}[kind]
+    view = {"f16": np.float16, "f8": synth.F8}[kind]
+    dtype = {"f16": gemm.DTYPE_F16, "f8": gemm.DTYPE_F8}[kind]
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(M + K)
+    a = torch.randint(-2, 3, (M, K), dtype=torch.int8, device="cuda", generator=gen)
+    a = a.to(torch.float16).to(tdt)
+    B = synth.small_int(71, 1, K, N, dtype=np.float16 if kind == "f16" else synth.F8)
+    host_bits = {"f16": np.int16, "f8": np.uint8}[kind]
+    b = torch.from_numpy(np.ascontiguousarray(B).view(host_bits)).cuda().view(tdt)
+    c = torch.zeros((M, N), dtype=torch.int16, device="cuda")
+    cfg = gemm.config_by_name(dtype, f"tr_{kind}_256x256x{64 if kind == 'f16' else 128}_w128x128_s2")
+    log(f"{kind} M={M} K={K}: A spans {M * K * es / 2**30:.3f} GiB")
+    st = gemm.entry(dtype, "_ex")(M, N, K, a.data_ptr(), K, b.data_ptr(), N, c.data_ptr(), N,
+                                  torch.cuda.current_stream().cuda_stream, cfg)
+    torch.cuda.synchronize()
+    assert st == gemm.GEMM_OK, gemm.gemm_last_error()
+    rows = [0, 1, M // 2, M - 257, M - 256, M - 1]
+    A_rows = a.view(torch.int16 if kind == "f16" else torch.uint8)[rows].cpu().numpy()
+    A_rows = A_rows.view(np.uint16).view(np.float16) if kind == "f16" else A_rows.view(synth.F8)
+    ref, _ = oracle.gemm_rows(A_rows, B)
+    got = c[rows].cpu().numpy().view(np.uint16)
+    got = got.view(np.float16) if kind == "f16" else got.view(synth.BF16)
+    assert np.array_equal(wide(got), rounded(ref, "f16" if kind == "f16" else "bf16"))
+    del a
