@@ -9,7 +9,9 @@ the JSON line also carries each kernel's own TFLOP/s and fraction of the
 MI355X matrix peak (FP32 157.3 TFLOP/s, FP16 2516.6 TFLOP/s dense).
 
 Before timing, sampled rows and entries of both products are checked
-against the CPU oracle.  After timing, the oracle itself is timed on a
+against the CPU oracle, and each kernel runs 20 launches timed one by one
+(the median and minimum per launch in the JSON line, beside the timed
+region's mean).  After timing, the oracle itself is timed on a
 bounded sample of the same workload (``cpu_baseline``).
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
@@ -282,6 +284,20 @@ def main():
                 launch(k)
         torch.cuda.synchronize()
 
+    # Per-launch statistics, before the timed region (they do not enter
+    # `value`): each launch between its own pair of events, for the median
+    # and minimum beside the timed region's mean.
+    per_launch = {}
+    n_pl = min(args.steps, 20)
+    for k in kinds:
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_pl + 1)]
+        evs[0].record(stream)
+        for j in range(n_pl):
+            launch(k)
+            evs[j + 1].record(stream)
+        torch.cuda.synchronize()
+        per_launch[k] = sorted(evs[j].elapsed_time(evs[j + 1]) for j in range(n_pl))
+
     # Timed region: K steps.  The launches of one kernel run back to back
     # (the K SGEMMs, then the K HGEMMs) between events recorded on the launch
     # stream, so each kernel's average launch duration is its block's time
@@ -306,6 +322,8 @@ def main():
         kernels[k] = {
             "variant": cfgs[k].name.decode(), "order": cfgs[k].order, "group_m": cfgs[k].group_m,
             "ms_mean": round(mean, 5),
+            "ms_median_single": round(per_launch[k][len(per_launch[k]) // 2], 5),
+            "ms_min_single": round(per_launch[k][0], 5),
             "tflops": round(flops / (mean * 1e-3) / 1e12, 2),
             "pct_peak": round(100.0 * flops / (mean * 1e-3) / 1e12 / PEAK_TFLOPS[k], 2),
             "peak_tflops": PEAK_TFLOPS[k],
