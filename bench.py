@@ -9,9 +9,9 @@ the JSON line also carries each kernel's own TFLOP/s and fraction of the
 MI355X matrix peak (FP32 157.3 TFLOP/s, FP16 2516.6 TFLOP/s dense).
 
 Before timing, sampled rows and entries of both products are checked
-against the CPU oracle, and each kernel runs 20 launches timed one by one
-(the median and minimum per launch in the JSON line, beside the timed
-region's mean).  After timing, the oracle itself is timed on a
+against the CPU oracle; the warmup steps follow, then the timed steps.
+After them each kernel runs 20 launches timed one by one (the median and
+minimum per launch in the JSON line, beside the timed region's mean).  After timing, the oracle itself is timed on a
 bounded sample of the same workload (``cpu_baseline``).
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
@@ -225,16 +225,14 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    if epi is not None:
-        # One launch from the known C0 for the parity check; the warmup
-        # follows it (the epilogue reads C, so later launches change it).
-        for k in kinds:
+    # One launch of each kernel for the parity check (with the fused
+    # epilogue, from the known C0: the epilogue reads C, so later launches
+    # change it).  The warmup follows the check, right before the timed
+    # region, so that the GPU is not idle in between.
+    for k in kinds:
+        if epi is not None:
             devbuf[k][2].copy_(to_dev(C0[k]))
-            launch(k)
-    else:
-        for _ in range(max(args.warmup, 1)):
-            for k in kinds:
-                launch(k)
+        launch(k)
     torch.cuda.synchronize()
 
     parity = {}
@@ -278,25 +276,10 @@ def main():
         if not all(p["ok"] for p in parity.values()):
             print(json.dumps({"error": "parity check failed", "parity": parity}), flush=True)
             sys.exit(1)
-    if epi is not None:
-        for _ in range(max(args.warmup, 1)):
-            for k in kinds:
-                launch(k)
-        torch.cuda.synchronize()
-
-    # Per-launch statistics, before the timed region (they do not enter
-    # `value`): each launch between its own pair of events, for the median
-    # and minimum beside the timed region's mean.
-    per_launch = {}
-    n_pl = min(args.steps, 20)
-    for k in kinds:
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_pl + 1)]
-        evs[0].record(stream)
-        for j in range(n_pl):
+    for _ in range(args.warmup):
+        for k in kinds:
             launch(k)
-            evs[j + 1].record(stream)
-        torch.cuda.synchronize()
-        per_launch[k] = sorted(evs[j].elapsed_time(evs[j + 1]) for j in range(n_pl))
+    torch.cuda.synchronize()
 
     # Timed region: K steps.  The launches of one kernel run back to back
     # (the K SGEMMs, then the K HGEMMs) between events recorded on the launch
@@ -313,6 +296,20 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     ms_per_step = wall * 1e3 / args.steps
+
+    # Per-launch statistics, after the timed region (they do not enter
+    # `value`): each launch between its own pair of events, for the median
+    # and minimum beside the timed region's mean.
+    per_launch = {}
+    n_pl = min(args.steps, 20)
+    for k in kinds:
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_pl + 1)]
+        evs[0].record(stream)
+        for j in range(n_pl):
+            launch(k)
+            evs[j + 1].record(stream)
+        torch.cuda.synchronize()
+        per_launch[k] = sorted(evs[j].elapsed_time(evs[j + 1]) for j in range(n_pl))
 
     kernels = {}
     for i, k in enumerate(kinds):
