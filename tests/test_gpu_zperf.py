@@ -1,0 +1,59 @@
+"""Performance smoke: the default kernels at 4096^3 against floors set well
+below their recorded rates on MI355X, so that a kernel silently falling off
+its fast path (a general-kernel fallback, a lost pipeline stage, a spilled
+accumulator) fails here while box-to-box spread (about 20 % in the matrix
+units' sustained clock) does not.
+
+Recorded at 4096^3 (TFLOP/s): FP32 142-149, FP16 1178-1230, BF16 1270-1323,
+FP8 2528-2668.  Floors: about 70 % of the lowest.  The library's own choice
+must be the LDS-direct variant, and the check runs after a warmup on
+device-resident operands, timing 20 launches between two events on the
+launch stream (the bench's method).
+
+Named to run after the parity tests (pytest -x stops at the first
+failure, and a slow box must not hide a parity result).
+"""
+import pytest
+import torch
+
+from dense_gemm_row_amd import gemm
+from tests.gpu_util import log
+
+pytestmark = pytest.mark.gpu
+
+N = 4096
+FLOOR = {"f32": 100.0, "f16": 820.0, "bf16": 880.0, "f8": 1750.0}
+DT = {"f32": (gemm.DTYPE_F32, torch.float32, torch.float32),
+      "f16": (gemm.DTYPE_F16, torch.float16, torch.float16),
+      "bf16": (gemm.DTYPE_BF16, torch.bfloat16, torch.bfloat16),
+      "f8": (gemm.DTYPE_F8, torch.float8_e4m3fn, torch.bfloat16)}
+PREFIX = {"f32": "dl_f32_", "f16": "tr_f16_", "bf16": "tr_bf16_", "f8": "tr_f8_"}
+
+
+@pytest.mark.parametrize("kind", list(FLOOR))
+def test_default_kernel_rate_4096(kind):
+    dt, tin, tout = DT[kind]
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7)
+    a = (torch.rand((N, N), device=dev, generator=gen) * 2 - 1).to(tin)
+    b = (torch.rand((N, N), device=dev, generator=gen) * 2 - 1).to(tin)
+    c = torch.empty((N, N), device=dev, dtype=tout)
+    cfg = gemm.gemm_select_config(dt, N, N, N)
+    assert cfg.name.decode().startswith(PREFIX[kind]), cfg.name
+    stream = torch.cuda.current_stream(dev)
+    fn = gemm.entry(dt, "_ex")
+    args = (N, N, N, a.data_ptr(), N, b.data_ptr(), N, c.data_ptr(), N, stream.cuda_stream, cfg)
+    for _ in range(5):
+        assert fn(*args) == gemm.GEMM_OK, gemm.gemm_last_error()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 20
+    e0.record(stream)
+    for _ in range(reps):
+        fn(*args)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    tflops = 2.0 * N ** 3 / (ms * 1e-3) / 1e12
+    log(f"{kind} {cfg.name.decode()}: {ms * 1e3:.1f} us, {tflops:.1f} TFLOP/s (floor {FLOOR[kind]})")
+    assert tflops >= FLOOR[kind], (kind, tflops)
