@@ -22,6 +22,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -72,20 +73,29 @@ def parse_args():
 FAMILY_SOURCE = {"dl_f32": "sgemm_dl.hip", "mfma_f32": "sgemm_mfma.hip", "simt_f32": "sgemm_simt.hip",
                  "mfma_f16": "hgemm_mfma.hip", "pipe_f16": "hgemm_pipe.hip",
                  "tr_f16": "hgemm_tr.hip", "mfma_bf16": "hgemm_mfma.hip", "tr_bf16": "hgemm_tr.hip",
-                 "tr_f8": "hgemm_tr.hip"}
+                 "tr_f8": "hgemm_tr.hip", "tr_e5m2": "hgemm_tr.hip"}
+
+
+def code_only(text: str) -> str:
+    """C/C++ source with comments removed and whitespace collapsed: what the
+    compiler sees of it, for the digest (a comment edit keeps the kernel)."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
 
 
 def kernel_digest(variant: str) -> str:
-    """Digest of the sources that define one variant's kernel: its family's
-    file plus the shared index maps and the public header."""
+    """Digest of the code that defines one variant's kernel: its family's
+    file plus the shared index maps and the public header, comments
+    excluded."""
     family = "_".join(variant.split("_")[:2])
     files = [os.path.join(ROOT, "dense_gemm_row_amd", "csrc", FAMILY_SOURCE[family]),
              os.path.join(ROOT, "dense_gemm_row_amd", "csrc", "gemm_internal.h"),
              os.path.join(ROOT, "include", "gemm.h")]
     h = hashlib.sha256()
     for path in files:
-        with open(path, "rb") as f:
-            h.update(os.path.basename(path).encode() + b"\0" + f.read())
+        with open(path, encoding="utf-8") as f:
+            h.update(os.path.basename(path).encode() + b"\0" + code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

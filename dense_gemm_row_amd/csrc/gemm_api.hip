@@ -8,6 +8,7 @@
 // sizes and leading dimensions instead of tensors.
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <mutex>
@@ -270,16 +271,62 @@ gemm_status_t validate(int dtype, int64_t M, int64_t N, int64_t K, const void* A
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-// Resolves the configuration of a call: the forced one (checked), or the
-// selection for the shape.
+// Environment, read once: GEMM_FORCE_CONFIG names a variant that replaces
+// the library's own choice in calls of that variant's element type that do
+// not force one themselves (ignored where the variant lacks the call's
+// form); GEMM_LOG (any value but "0") prints each call's shape, form and
+// configuration to stderr.
+struct Env {
+  std::string force;
+  bool log = false;
+};
+const Env& env() {
+  static const Env e = [] {
+    Env x;
+    if (const char* f = getenv("GEMM_FORCE_CONFIG")) x.force = f;
+    const char* l = getenv("GEMM_LOG");
+    x.log = l && *l && strcmp(l, "0") != 0;
+    return x;
+  }();
+  return e;
+}
+
+gemm_status_t resolve_forced(int dtype, int64_t M, int64_t N, int64_t K, const gemm_config_t* forced,
+                             bool split, gemm_config_t& cfg, bool need_epi, bool need_bt,
+                             bool need_q8, bool need_at);
+
+// Resolves the configuration of a call: the forced one (checked), the
+// GEMM_FORCE_CONFIG variant, or the selection for the shape.
 gemm_status_t resolve(int dtype, int64_t M, int64_t N, int64_t K, const gemm_config_t* forced,
                       bool split, gemm_config_t& cfg, bool need_epi = false, bool need_bt = false,
                       bool need_q8 = false, bool need_at = false) {
-  const auto& v = table().v[dtype];
-  if (!forced) {
+  gemm_status_t st = GEMM_OK;
+  if (forced) {
+    st = resolve_forced(dtype, M, N, K, forced, split, cfg, need_epi, need_bt, need_q8, need_at);
+  } else {
     cfg = select(dtype, M, N, K, split, need_epi, need_bt, need_q8, need_at);
-    return GEMM_OK;
+    const int id = env().force.empty() ? -1 : find_by_name(dtype, env().force.c_str());
+    if (id >= 0) {
+      gemm_config_t f = table().v[dtype][id].desc;
+      f.splits = 0;  // split calls: the model's best count for this variant
+      gemm_config_t g;
+      if (resolve_forced(dtype, M, N, K, &f, split, g, need_epi, need_bt, need_q8, need_at) == GEMM_OK)
+        cfg = g;
+      g_err[0] = 0;
+    }
   }
+  if (st == GEMM_OK && env().log)
+    fprintf(stderr, "libgemm: %s %lldx%lldx%lld%s%s%s%s%s -> %s order=%d group_m=%d splits=%d\n",
+            dtype_name(dtype), (long long)M, (long long)N, (long long)K, split ? " splitk" : "",
+            need_epi ? " epi" : "", need_q8 ? " q8" : "", need_at ? " at" : "", need_bt ? " bt" : "",
+            cfg.name, cfg.order, cfg.group_m, cfg.splits);
+  return st;
+}
+
+gemm_status_t resolve_forced(int dtype, int64_t M, int64_t N, int64_t K, const gemm_config_t* forced,
+                             bool split, gemm_config_t& cfg, bool need_epi, bool need_bt,
+                             bool need_q8, bool need_at) {
+  const auto& v = table().v[dtype];
   if (forced->id < 0 || forced->id >= (int32_t)v.size())
     return fail(GEMM_ERR_UNSUPPORTED, "config id %d not in the %s table", forced->id,
                 dtype_name(dtype));

@@ -488,6 +488,14 @@ gemm_status_t gemm_tile_of_block(const gemm_config_t *cfg, int64_t M, int64_t N,
 gemm_status_t gemm_layout_check(int32_t dtype, int32_t idx, int32_t banks,
                                 int64_t out[2]);
 
+/* Environment, read at the first call: GEMM_FORCE_CONFIG=<variant name>
+ * makes calls of that variant's element type that pass no cfg use it (where
+ * it has the call's form; split-K calls take the model's best split count
+ * for it), as if given to the *_ex form; gemm_select_config and
+ * gemm_select_splitk_config still report the library's own choice.
+ * GEMM_LOG (any value but "0") prints one line per call to stderr: type,
+ * shape, form and the configuration used. */
+
 /* Tuning table: a text file of lines "dtype M N K name order group_m
  * [splits]" (dtype f32|f16|bf16|f8|e5m2; splits defaults to 1).  Exact-shape matches
  * override the heuristic.  Loading replaces the previous table; NULL clears

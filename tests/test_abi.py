@@ -392,3 +392,34 @@ def test_trans_argument_validation(fn):
     # M = 34 is off the vector layout for every element size.
     assert fn(34, 64, 128, PA, 34, PB, 128, PC, 64, None, None, 1, 1) == gemm.GEMM_ERR_UNSUPPORTED
     assert fn(0, 64, 128, PA, 32, PB, 128, 0, 64, None, None, 1, 1) == gemm.GEMM_OK
+
+
+def test_environment_force_and_log():
+    """GEMM_FORCE_CONFIG replaces the library's choice for calls without a
+    cfg (where the variant has the form), GEMM_LOG prints the choice; an
+    M = 0 call resolves its configuration and returns before any launch,
+    so this runs without a GPU (in a child process: the variables are read
+    once)."""
+    import subprocess
+    import sys
+    code = (
+        "from dense_gemm_row_amd import gemm\n"
+        "P = 0x10000000\n"
+        "assert gemm.gemm_f16(0, 64, 64, P, 64, P + (1 << 20), 64, 0, 64) == gemm.GEMM_OK\n"
+        "assert gemm.gemm_f32(0, 64, 64, P, 64, P + (1 << 20), 64, 0, 64) == gemm.GEMM_OK\n"
+        "e = gemm.GemmEpilogue(1.0, 0.0, None, 0)\n"
+        "assert gemm.gemm_f16_epi(0, 64, 64, P, 64, P + (1 << 20), 64, 0, 64, None, None, e) == gemm.GEMM_OK\n"
+        "print(gemm.gemm_select_config(gemm.DTYPE_F16, 4096, 4096, 4096).name.decode())\n")
+    env = dict(os.environ, GEMM_FORCE_CONFIG="pipe_f16_128x128x64_w64x64", GEMM_LOG="1")
+    res = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True,
+                         cwd=ROOT, timeout=120)
+    assert res.returncode == 0, res.stderr
+    lines = [l for l in res.stderr.splitlines() if l.startswith("libgemm:")]
+    assert len(lines) == 3, res.stderr
+    assert lines[0].startswith("libgemm: f16 0x64x64 -> pipe_f16_128x128x64_w64x64"), lines[0]
+    assert "-> dl_f32_" in lines[1] or "-> mfma_f32_" in lines[1], lines[1]   # another type: untouched
+    assert " epi -> " in lines[2] and "pipe_f16" not in lines[2], lines[2]    # no epilogue form
+    assert res.stdout.strip().startswith("tr_f16_")                          # the library's own choice
+    res = subprocess.run([sys.executable, "-c", code], env=dict(os.environ, GEMM_LOG="0"),
+                         capture_output=True, text=True, cwd=ROOT, timeout=120)
+    assert res.returncode == 0 and "libgemm:" not in res.stderr
