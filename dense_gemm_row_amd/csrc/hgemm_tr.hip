@@ -91,23 +91,28 @@ __device__ __forceinline__ void static_for(F&& f, std::integer_sequence<int, I..
   (f(IC<I>{}), ...);
 }
 
-// MODE_: 0 the plain kernel; 1 the split-K form, whose epilogue writes FP32
-// partials; 2 the form with the fused epilogue (alpha, beta, bias,
-// activation); 3 the fused epilogue writing INT8 codes (C is int8, beta 0).  BT_: B is given transposed (Bt, N x K row-major, i.e.
-// column-major B); its tile is then staged and read exactly like A's (one
-// LDS row per output column, k contiguous), with no transpose read.  TY_:
-// the element types, 0 binary16 in and out, 1 bfloat16 in and out, 2 FP8
-// E4M3 in and bfloat16 out, 3 FP8 E5M2 in and bfloat16 out.  AT_: A given transposed (At, K x M row-major,
-// i.e. column-major A): its tile is staged and read exactly like B's (k
-// rows of BM values, chunk XOR by k, transpose reads), which hands each
-// lane the same k run of its row as the direct read of row-major A.  PW_:
-// producer waves (0: none).  With PW_ > 0 the workgroup is split by role:
-// the NW compute waves only read LDS and run MFMAs, and PW_ further waves
-// only issue the LDS-direct copies and wait for them to land; both meet at
-// the one barrier per K slice.  This is the load/compute separation that
-// "hgemm_naive_kernel explained" lists among its further directions
-// (section 10.3), with LDS-direct copies in the role that "nxbn.cn GB300
-// GEMM" (section 3.2) gives to a copy engine driven by a few threads.
+// Template parameters beyond the tile (BM x BN, wave tiles WM x WN, K slice
+// BK, NS stages):
+// * MODE_: 0 the plain kernel; 1 the split-K form, whose epilogue writes
+//   FP32 partials; 2 the form with the fused epilogue (alpha, beta, bias,
+//   activation); 3 the fused epilogue writing INT8 codes (C is int8, beta 0).
+// * BT_: B is given transposed (Bt, N x K row-major, i.e. column-major B);
+//   its tile is then staged and read exactly like A's (one LDS row per
+//   output column, k contiguous), with no transpose read.
+// * TY_: the element types, 0 binary16 in and out, 1 bfloat16 in and out,
+//   2 FP8 E4M3 in and bfloat16 out, 3 FP8 E5M2 in and bfloat16 out.
+// * AT_: A given transposed (At, K x M row-major, i.e. column-major A): its
+//   tile is staged and read exactly like B's (k rows of BM values, chunk XOR
+//   by k, transpose reads), which hands each lane the same k run of its row
+//   as the direct read of row-major A.
+// * PW_: producer waves (0: none).  With PW_ > 0 the workgroup is split by
+//   role: the NW compute waves only read LDS and run MFMAs, and PW_ further
+//   waves only issue the LDS-direct copies and wait for them to land; both
+//   meet at the one barrier per K slice.  This is the load/compute
+//   separation that "hgemm_naive_kernel explained" lists among its further
+//   directions (section 10.3), with LDS-direct copies in the role that
+//   "nxbn.cn GB300 GEMM" (section 3.2) gives to a copy engine driven by a
+//   few threads.
 template <int BM_, int BN_, int WM_, int WN_, int BK_, int NS_, int MODE_ = 0, bool BT_ = false,
           int TY_ = 0, bool AT_ = false, int PW_ = 0>
 struct Shape {
