@@ -419,7 +419,7 @@ def _ld(t) -> int:
 
 def matmul(a, b, out=None, config: GemmConfig | None = None, stream=None, split_k: bool = True,
            alpha: float = 1.0, beta: float = 0.0, bias=None, act: int = ACT_NONE,
-           b_transposed: bool = False):
+           b_transposed: bool = False, a_transposed: bool = False):
     """C = a @ b on the GPU through libgemm.  a: M x K, b: K x N, of one
     type (float32, float16, bfloat16, or float8_e4m3fn / float8_e5m2 with a
     bfloat16 result), row-major (any row stride).  Returns ``out`` (allocated when
@@ -432,6 +432,9 @@ def matmul(a, b, out=None, config: GemmConfig | None = None, stream=None, split_
 
     b_transposed: ``b`` holds B^T (N x K, row-major) and the product is
     a @ b.T (gemm_*_bt; not combined with split-K or the fused epilogue).
+    a_transposed: ``a`` holds A^T (K x M, row-major) and the product is
+    a.T @ b (or a.T @ b.T with b_transposed too), through gemm_*_trans; the
+    aligned-operand kernels only, and neither split-K nor the epilogue.
 
     alpha, beta, bias (a float32 GPU tensor of N values) and act select the
     fused epilogue out = act(alpha * (a @ b) + beta * out + bias) (through
@@ -445,7 +448,7 @@ def matmul(a, b, out=None, config: GemmConfig | None = None, stream=None, split_
     c_dtype = torch.bfloat16 if a.dtype in (torch.float8_e4m3fn, torch.float8_e5m2) else a.dtype
     if not (a.is_cuda and b.is_cuda):
         raise ValueError("a and b must be GPU tensors")
-    M, K = a.shape
+    M, K = (a.shape[1], a.shape[0]) if a_transposed else a.shape
     N, K2 = b.shape if b_transposed else (b.shape[1], b.shape[0])
     if K2 != K:
         raise ValueError(f"inner dimensions differ: {K} vs {K2}")
@@ -457,6 +460,14 @@ def matmul(a, b, out=None, config: GemmConfig | None = None, stream=None, split_
         stream = torch.cuda.current_stream(a.device).cuda_stream
     args = (M, N, K, a.data_ptr(), _ld(a), b.data_ptr(), _ld(b), out.data_ptr(), _ld(out), stream)
     dtype = dtypes[a.dtype]
+    if a_transposed:
+        if alpha != 1.0 or beta != 0.0 or bias is not None or act != ACT_NONE:
+            raise ValueError("a_transposed does not take the fused epilogue")
+        fn = entry(dtype, "_trans")
+        st = fn(*args[:9], stream, config, 1, int(b_transposed))
+        if st != GEMM_OK:
+            raise GemmError(st, fn.__name__)
+        return out
     if b_transposed:
         if alpha != 1.0 or beta != 0.0 or bias is not None or act != ACT_NONE:
             raise ValueError("b_transposed does not take the fused epilogue")

@@ -452,6 +452,20 @@ def test_matmul_b_transposed():
     assert rep["ok"], rep
 
 
+@pytest.mark.parametrize("tb", [False, True], ids=["TN", "TT"])
+def test_matmul_a_transposed(tb):
+    import torch
+    A, B = synth.workload(200, 264, 136, "f16", seed=41)
+    at = torch.from_numpy(np.ascontiguousarray(A.T)).cuda()
+    bx = torch.from_numpy(np.ascontiguousarray(B.T) if tb else B).cuda()
+    log(f"matmul f16 a_transposed b_transposed={tb}")
+    out = gemm.matmul(at, bx, a_transposed=True, b_transposed=tb)
+    torch.cuda.synchronize()
+    ref, den = oracle.gemm_rows(A, B)
+    rep = oracle.check(out.cpu().numpy(), ref, den, oracle.HGEMM_TOL)
+    assert rep["ok"], rep
+
+
 # --- very large leading dimensions (byte offsets past 2^31) -----------------------
 @pytest.mark.parametrize("kind", ["f32", "f16", "bf16", "f8"])
 def test_offsets_past_31_bits(kind):
