@@ -541,3 +541,51 @@ def test_operands_at_the_31_bit_limit(kind, M):
     got = got.view(np.float16) if kind == "f16" else got.view(synth.BF16)
     assert np.array_equal(wide(got), rounded(ref, "f16" if kind == "f16" else "bf16"))
     del a
+
+
+# --- concurrency: two host threads, two streams -------------------------------------
+def test_concurrent_calls_on_two_streams():
+    """The library keeps no per-call state: two host threads issuing GEMMs
+    on two streams at once (different types, shapes and forms) get the same
+    bits as the same calls made one at a time, and each thread's last error
+    is its own."""
+    import threading
+
+    import torch
+    jobs = []
+    for seed, kind, (M, N, K) in ((3, "f16", (300, 264, 520)), (5, "f32", (257, 136, 333))):
+        A, B = synth.workload(M, N, K, kind, seed=seed)
+        jobs.append((kind, M, N, K, A, B))
+    ref = [run(A, B)[0] for (_, _, _, _, A, B) in jobs]
+    results, errors = [None, None], [None, None]
+
+    def worker(i):
+        kind, M, N, K, A, B = jobs[i]
+        s = torch.cuda.Stream()
+        tdt = torch.float16 if kind == "f16" else torch.float32
+        a = torch.from_numpy(A).cuda()
+        b = torch.from_numpy(B).cuda()
+        c = torch.full((M, N), float("nan"), dtype=tdt, device="cuda")
+        fn = gemm.entry(gemm.DTYPE_F16 if kind == "f16" else gemm.DTYPE_F32)
+        torch.cuda.synchronize()
+        for _ in range(20):
+            st = fn(M, N, K, a.data_ptr(), K, b.data_ptr(), N, c.data_ptr(), N, s.cuda_stream)
+            assert st == gemm.GEMM_OK
+        # A refused call on this thread leaves its own error text only.
+        assert fn(-1, N, K, a.data_ptr(), K, b.data_ptr(), N, c.data_ptr(), N, s.cuda_stream) == \
+            gemm.GEMM_ERR_INVALID_ARG
+        errors[i] = gemm.gemm_last_error()
+        s.synchronize()
+        results[i] = c.cpu().numpy()
+
+    log("two threads, two streams")
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=120)
+    for i in range(2):
+        assert results[i] is not None, f"thread {i} did not finish"
+        assert np.array_equal(results[i].view(np.uint8), np.asarray(ref[i]).view(np.uint8)), i
+        assert "negative" in errors[i]
+    assert gemm.gemm_last_error() == "" or "negative" not in gemm.gemm_last_error()
