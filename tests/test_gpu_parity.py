@@ -589,3 +589,55 @@ def test_concurrent_calls_on_two_streams():
         assert np.array_equal(results[i].view(np.uint8), np.asarray(ref[i]).view(np.uint8)), i
         assert "negative" in errors[i]
     assert gemm.gemm_last_error() == "" or "negative" not in gemm.gemm_last_error()
+
+
+# --- HIP graph capture ---------------------------------------------------------------
+def test_calls_replay_in_a_hip_graph():
+    """Plain and split-K calls allocate nothing and record no memset, so a
+    HIP graph captures them: every replay (with eager work and
+    synchronisations in between) reproduces the eager result bit for bit."""
+    import torch
+    M, N, K = 520, 264, 1032
+    A16, B16 = synth.workload(M, N, K, "f16", seed=8)
+    A32, B32 = synth.workload(M, N, K, "f32", seed=9)
+    a16, b16 = torch.from_numpy(A16).cuda(), torch.from_numpy(B16).cuda()
+    a32, b32 = torch.from_numpy(A32).cuda(), torch.from_numpy(B32).cuda()
+    c16 = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    c32 = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    c16s = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    sk = gemm.gemm_get_config(gemm.DTYPE_F16, 0)
+    sk.splits = 3
+    ws = torch.empty(gemm.gemm_splitk_workspace_bytes(gemm.DTYPE_F16, M, N, K, 3), dtype=torch.uint8,
+                     device="cuda")
+
+    def calls():
+        s = torch.cuda.current_stream().cuda_stream
+        assert gemm.gemm_f16(M, N, K, a16.data_ptr(), K, b16.data_ptr(), N, c16.data_ptr(), N, s) == 0
+        assert gemm.gemm_f32(M, N, K, a32.data_ptr(), K, b32.data_ptr(), N, c32.data_ptr(), N, s) == 0
+        assert gemm.gemm_f16_splitk(M, N, K, a16.data_ptr(), K, b16.data_ptr(), N, c16s.data_ptr(), N,
+                                    ws.data_ptr(), ws.numel(), s, sk) == 0
+
+    calls()
+    torch.cuda.synchronize()
+    want = [c16.clone(), c32.clone(), c16s.clone()]
+    log("graph capture of plain and split-K calls")
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        calls()  # warm the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        calls()
+    for rep in range(5):
+        for c in (c16, c32, c16s):
+            c.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for got, ref in zip((c16, c32, c16s), want):
+            assert torch.equal(got.view(torch.uint8), ref.view(torch.uint8)), rep
+    ref16, den16 = oracle.gemm_rows(A16, B16, rows=[0, M - 1])
+    rep16 = oracle.check(c16.cpu().numpy()[[0, M - 1]], ref16, den16, oracle.HGEMM_TOL)
+    assert rep16["ok"], rep16
