@@ -143,177 +143,84 @@ def lib():
 
 
 # --------------------------------------------------------------------------
-# The C entry points, one Python function each.
+# The C entry points, one Python function each: gemm_<type><form> for every
+# type in TYPES and every form below, made by one factory per form (the
+# C signatures of a form are the same for every type).  Configurations and
+# epilogues are passed as GemmConfig / GemmEpilogue or None.
 # --------------------------------------------------------------------------
-def gemm_f32(M, N, K, A, lda, B, ldb, C, ldc, stream=None) -> int:
-    return lib().gemm_f32(M, N, K, A, lda, B, ldb, C, ldc, stream)
+def _ref(x):
+    return ctypes.byref(x) if x is not None else None
 
 
-def gemm_f16(M, N, K, A, lda, B, ldb, C, ldc, stream=None) -> int:
-    return lib().gemm_f16(M, N, K, A, lda, B, ldb, C, ldc, stream)
+def _named(fn, name):
+    fn.__name__ = fn.__qualname__ = name
+    return fn
 
 
-def gemm_bf16(M, N, K, A, lda, B, ldb, C, ldc, stream=None) -> int:
-    return lib().gemm_bf16(M, N, K, A, lda, B, ldb, C, ldc, stream)
+def _plain(name):
+    """gemm_<t>(M, N, K, A, lda, B, ldb, C, ldc, stream=None)."""
+    def fn(M, N, K, A, lda, B, ldb, C, ldc, stream=None) -> int:
+        return getattr(lib(), name)(M, N, K, A, lda, B, ldb, C, ldc, stream)
+    return _named(fn, name)
 
 
-def gemm_f8(M, N, K, A, lda, B, ldb, C, ldc, stream=None) -> int:
-    return lib().gemm_f8(M, N, K, A, lda, B, ldb, C, ldc, stream)
+def _ex(name):
+    """gemm_<t>_ex(..., stream, cfg): a forced variant and tile order."""
+    def fn(M, N, K, A, lda, B, ldb, C, ldc, stream, cfg: GemmConfig) -> int:
+        return getattr(lib(), name)(M, N, K, A, lda, B, ldb, C, ldc, stream, _ref(cfg))
+    return _named(fn, name)
 
 
-def gemm_e5m2(M, N, K, A, lda, B, ldb, C, ldc, stream=None) -> int:
-    return lib().gemm_e5m2(M, N, K, A, lda, B, ldb, C, ldc, stream)
+def _bt(name):
+    """gemm_<t>_bt(M, N, K, A, lda, Bt, ldbt, C, ldc, stream=None, cfg=None):
+    B given transposed."""
+    def fn(M, N, K, A, lda, Bt, ldbt, C, ldc, stream=None, cfg: GemmConfig | None = None) -> int:
+        return getattr(lib(), name)(M, N, K, A, lda, Bt, ldbt, C, ldc, stream, _ref(cfg))
+    return _named(fn, name)
 
 
-def gemm_f32_ex(M, N, K, A, lda, B, ldb, C, ldc, stream, cfg: GemmConfig) -> int:
-    return lib().gemm_f32_ex(M, N, K, A, lda, B, ldb, C, ldc, stream,
-                             ctypes.byref(cfg) if cfg is not None else None)
+def _epi(name):
+    """gemm_<t>_epi(..., stream, cfg, epi): the fused epilogue."""
+    def fn(M, N, K, A, lda, B, ldb, C, ldc, stream, cfg: GemmConfig | None,
+           epi: GemmEpilogue | None) -> int:
+        return getattr(lib(), name)(M, N, K, A, lda, B, ldb, C, ldc, stream, _ref(cfg), _ref(epi))
+    return _named(fn, name)
 
 
-def gemm_f16_ex(M, N, K, A, lda, B, ldb, C, ldc, stream, cfg: GemmConfig) -> int:
-    return lib().gemm_f16_ex(M, N, K, A, lda, B, ldb, C, ldc, stream,
-                             ctypes.byref(cfg) if cfg is not None else None)
-
-
-def gemm_bf16_ex(M, N, K, A, lda, B, ldb, C, ldc, stream, cfg: GemmConfig) -> int:
-    return lib().gemm_bf16_ex(M, N, K, A, lda, B, ldb, C, ldc, stream,
-                              ctypes.byref(cfg) if cfg is not None else None)
-
-
-def gemm_f8_ex(M, N, K, A, lda, B, ldb, C, ldc, stream, cfg: GemmConfig) -> int:
-    return lib().gemm_f8_ex(M, N, K, A, lda, B, ldb, C, ldc, stream,
-                            ctypes.byref(cfg) if cfg is not None else None)
-
-
-def gemm_e5m2_ex(M, N, K, A, lda, B, ldb, C, ldc, stream, cfg: GemmConfig) -> int:
-    return lib().gemm_e5m2_ex(M, N, K, A, lda, B, ldb, C, ldc, stream,
-                              ctypes.byref(cfg) if cfg is not None else None)
-
-
-def gemm_f32_bt(M, N, K, A, lda, Bt, ldbt, C, ldc, stream=None, cfg: GemmConfig | None = None) -> int:
-    return lib().gemm_f32_bt(M, N, K, A, lda, Bt, ldbt, C, ldc, stream,
-                             ctypes.byref(cfg) if cfg is not None else None)
-
-
-def gemm_f16_bt(M, N, K, A, lda, Bt, ldbt, C, ldc, stream=None, cfg: GemmConfig | None = None) -> int:
-    return lib().gemm_f16_bt(M, N, K, A, lda, Bt, ldbt, C, ldc, stream,
-                             ctypes.byref(cfg) if cfg is not None else None)
-
-
-def gemm_bf16_bt(M, N, K, A, lda, Bt, ldbt, C, ldc, stream=None, cfg: GemmConfig | None = None) -> int:
-    return lib().gemm_bf16_bt(M, N, K, A, lda, Bt, ldbt, C, ldc, stream,
-                              ctypes.byref(cfg) if cfg is not None else None)
-
-
-def gemm_f8_bt(M, N, K, A, lda, Bt, ldbt, C, ldc, stream=None, cfg: GemmConfig | None = None) -> int:
-    return lib().gemm_f8_bt(M, N, K, A, lda, Bt, ldbt, C, ldc, stream,
-                            ctypes.byref(cfg) if cfg is not None else None)
-
-
-def gemm_e5m2_bt(M, N, K, A, lda, Bt, ldbt, C, ldc, stream=None, cfg: GemmConfig | None = None) -> int:
-    return lib().gemm_e5m2_bt(M, N, K, A, lda, Bt, ldbt, C, ldc, stream,
-                              ctypes.byref(cfg) if cfg is not None else None)
-
-
-def gemm_f32_epi(M, N, K, A, lda, B, ldb, C, ldc, stream, cfg: GemmConfig | None,
-                 epi: GemmEpilogue | None) -> int:
-    return lib().gemm_f32_epi(M, N, K, A, lda, B, ldb, C, ldc, stream,
-                              ctypes.byref(cfg) if cfg is not None else None,
-                              ctypes.byref(epi) if epi is not None else None)
-
-
-def gemm_f16_epi(M, N, K, A, lda, B, ldb, C, ldc, stream, cfg: GemmConfig | None,
-                 epi: GemmEpilogue | None) -> int:
-    return lib().gemm_f16_epi(M, N, K, A, lda, B, ldb, C, ldc, stream,
-                              ctypes.byref(cfg) if cfg is not None else None,
-                              ctypes.byref(epi) if epi is not None else None)
-
-
-def gemm_bf16_epi(M, N, K, A, lda, B, ldb, C, ldc, stream, cfg: GemmConfig | None,
-                  epi: GemmEpilogue | None) -> int:
-    return lib().gemm_bf16_epi(M, N, K, A, lda, B, ldb, C, ldc, stream,
-                               ctypes.byref(cfg) if cfg is not None else None,
-                               ctypes.byref(epi) if epi is not None else None)
-
-
-def gemm_f8_epi(M, N, K, A, lda, B, ldb, C, ldc, stream, cfg: GemmConfig | None,
-                epi: GemmEpilogue | None) -> int:
-    return lib().gemm_f8_epi(M, N, K, A, lda, B, ldb, C, ldc, stream,
-                             ctypes.byref(cfg) if cfg is not None else None,
-                             ctypes.byref(epi) if epi is not None else None)
-
-
-def gemm_e5m2_epi(M, N, K, A, lda, B, ldb, C, ldc, stream, cfg: GemmConfig | None,
-                  epi: GemmEpilogue | None) -> int:
-    return lib().gemm_e5m2_epi(M, N, K, A, lda, B, ldb, C, ldc, stream,
-                               ctypes.byref(cfg) if cfg is not None else None,
-                               ctypes.byref(epi) if epi is not None else None)
-
-
-def gemm_f32_splitk(M, N, K, A, lda, B, ldb, C, ldc, workspace, workspace_bytes, stream=None,
-                    cfg: GemmConfig | None = None) -> int:
-    return lib().gemm_f32_splitk(M, N, K, A, lda, B, ldb, C, ldc, workspace, workspace_bytes, stream,
-                                 ctypes.byref(cfg) if cfg is not None else None)
-
-
-def gemm_f16_splitk(M, N, K, A, lda, B, ldb, C, ldc, workspace, workspace_bytes, stream=None,
-                    cfg: GemmConfig | None = None) -> int:
-    return lib().gemm_f16_splitk(M, N, K, A, lda, B, ldb, C, ldc, workspace, workspace_bytes, stream,
-                                 ctypes.byref(cfg) if cfg is not None else None)
-
-
-def gemm_bf16_splitk(M, N, K, A, lda, B, ldb, C, ldc, workspace, workspace_bytes, stream=None,
-                     cfg: GemmConfig | None = None) -> int:
-    return lib().gemm_bf16_splitk(M, N, K, A, lda, B, ldb, C, ldc, workspace, workspace_bytes,
-                                  stream, ctypes.byref(cfg) if cfg is not None else None)
-
-
-def gemm_f8_splitk(M, N, K, A, lda, B, ldb, C, ldc, workspace, workspace_bytes, stream=None,
-                   cfg: GemmConfig | None = None) -> int:
-    return lib().gemm_f8_splitk(M, N, K, A, lda, B, ldb, C, ldc, workspace, workspace_bytes,
-                                stream, ctypes.byref(cfg) if cfg is not None else None)
-
-
-def gemm_e5m2_splitk(M, N, K, A, lda, B, ldb, C, ldc, workspace, workspace_bytes, stream=None,
-                     cfg: GemmConfig | None = None) -> int:
-    return lib().gemm_e5m2_splitk(M, N, K, A, lda, B, ldb, C, ldc, workspace, workspace_bytes,
-                                  stream, ctypes.byref(cfg) if cfg is not None else None)
+def _splitk(name):
+    """gemm_<t>_splitk(..., workspace, workspace_bytes, stream=None, cfg=None)."""
+    def fn(M, N, K, A, lda, B, ldb, C, ldc, workspace, workspace_bytes, stream=None,
+           cfg: GemmConfig | None = None) -> int:
+        return getattr(lib(), name)(M, N, K, A, lda, B, ldb, C, ldc, workspace, workspace_bytes,
+                                    stream, _ref(cfg))
+    return _named(fn, name)
 
 
 def _q8(name):
+    """gemm_<t>_epi_q8(M, N, K, A, lda, B, ldb, Q, ldq, stream, cfg, epi): the
+    INT8-quantising epilogue, Q = sat8(rne(act(alpha * A x B + bias)))."""
     def fn(M, N, K, A, lda, B, ldb, Q, ldq, stream, cfg: GemmConfig | None,
            epi: GemmEpilogue | None) -> int:
-        return getattr(lib(), name)(M, N, K, A, lda, B, ldb, Q, ldq, stream,
-                                    ctypes.byref(cfg) if cfg is not None else None,
-                                    ctypes.byref(epi) if epi is not None else None)
-    fn.__name__ = name
-    return fn
-
-
-# The INT8-quantising epilogue: Q = sat8(rne(act(alpha * A x B + bias))).
-gemm_f32_epi_q8 = _q8("gemm_f32_epi_q8")
-gemm_f16_epi_q8 = _q8("gemm_f16_epi_q8")
-gemm_bf16_epi_q8 = _q8("gemm_bf16_epi_q8")
-gemm_f8_epi_q8 = _q8("gemm_f8_epi_q8")
-gemm_e5m2_epi_q8 = _q8("gemm_e5m2_epi_q8")
+        return getattr(lib(), name)(M, N, K, A, lda, B, ldb, Q, ldq, stream, _ref(cfg), _ref(epi))
+    return _named(fn, name)
 
 
 def _trans(name):
+    """gemm_<t>_trans(..., stream=None, cfg=None, trans_a=0, trans_b=0): C =
+    op(A) op(B) in the four layouts."""
     def fn(M, N, K, A, lda, B, ldb, C, ldc, stream=None, cfg: GemmConfig | None = None,
            trans_a: int = 0, trans_b: int = 0) -> int:
-        return getattr(lib(), name)(M, N, K, A, lda, B, ldb, C, ldc, stream,
-                                    ctypes.byref(cfg) if cfg is not None else None,
+        return getattr(lib(), name)(M, N, K, A, lda, B, ldb, C, ldc, stream, _ref(cfg),
                                     int(trans_a), int(trans_b))
-    fn.__name__ = name
-    return fn
+    return _named(fn, name)
 
 
-# C = op(A) op(B) in the four layouts.
-gemm_f32_trans = _trans("gemm_f32_trans")
-gemm_f16_trans = _trans("gemm_f16_trans")
-gemm_bf16_trans = _trans("gemm_bf16_trans")
-gemm_f8_trans = _trans("gemm_f8_trans")
-gemm_e5m2_trans = _trans("gemm_e5m2_trans")
+FORMS = {"": _plain, "_ex": _ex, "_bt": _bt, "_trans": _trans, "_epi": _epi, "_epi_q8": _q8,
+         "_splitk": _splitk}
+for _t in TYPES:
+    for _form, _make in FORMS.items():
+        globals()[f"gemm_{_t}{_form}"] = _make(f"gemm_{_t}{_form}")
+del _t, _form, _make
 
 
 # Entry points per dtype code, for callers that dispatch on it.
