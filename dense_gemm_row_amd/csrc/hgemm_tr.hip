@@ -738,7 +738,7 @@ hgemm_tr_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
 #pragma unroll
         for (int i = 0; i < BATCH; ++i) {
           const int row = m0 + wm0 + pass * (WM / 2) + (b0 + i) * RPI32 + l / CPR32;
-          off[i] = (row < M) & (col < N) ? CB * ((unsigned)row * (unsigned)p.ldc + (unsigned)col) : OOB;
+          off[i] = ((row < M) & (col < N)) ? CB * ((unsigned)row * (unsigned)p.ldc + (unsigned)col) : OOB;
           c_old[i] = v2i{0, 0};
         }
         if (!S::Q8 && p.epi.beta != 0.f) {

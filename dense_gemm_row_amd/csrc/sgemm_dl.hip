@@ -468,7 +468,7 @@ sgemm_dl_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = row_of(mb, r);
-        const unsigned off = (row < M) & (col < N) ? (unsigned)row * (unsigned)p.ldc + (unsigned)col : OOB;
+        const unsigned off = ((row < M) & (col < N)) ? (unsigned)row * (unsigned)p.ldc + (unsigned)col : OOB;
         const vecNB v = acc_vec(mb, r);
         if constexpr (NB == 4) {
           const int w = pack_i8x4(quantize_i8(epi_value(p.epi, v[0], 0.f, bias[0])),
@@ -518,7 +518,7 @@ sgemm_dl_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
 #pragma unroll
         for (int i = 0; i < BATCH; ++i) {
           const int row = row_of(mb, r0 + i);
-          off[i] = (row < M) & (col < N) ? 4u * ((unsigned)row * (unsigned)p.ldc + (unsigned)col) : OOB;
+          off[i] = ((row < M) & (col < N)) ? 4u * ((unsigned)row * (unsigned)p.ldc + (unsigned)col) : OOB;
           c_old[i] = vecNB{};
         }
         if (p.epi.beta != 0.f) {
