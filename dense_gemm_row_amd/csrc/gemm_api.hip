@@ -233,13 +233,18 @@ TileMap make_map(const gemm_config_t& c, int64_t M, int64_t N) {
 
 bool overlap(const void* a, size_t abytes, const void* b, size_t bbytes) {
   if (!a || !b || abytes == 0 || bbytes == 0) return false;
-  const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  const unsigned __int128 a0 = (uintptr_t)a, b0 = (uintptr_t)b;  // no wrap at the top
   return a0 < b0 + bbytes && b0 < a0 + abytes;
 }
 
+// Byte range of a rows x cols operand with leading dimension ld (>= 1),
+// saturated at 2^63: validate() rejects operands that reach it.
+constexpr size_t kSpanLimit = (size_t)1 << 63;
 size_t span_bytes(int64_t rows, int64_t cols, int64_t ld, size_t es) {
   if (rows <= 0 || cols <= 0) return 0;
-  return ((size_t)(rows - 1) * (size_t)ld + (size_t)cols) * es;
+  const unsigned __int128 s =
+      ((unsigned __int128)(uint64_t)(rows - 1) * (uint64_t)ld + (uint64_t)cols) * es;
+  return s >= kSpanLimit ? kSpanLimit : (size_t)s;
 }
 
 // bt: B is given transposed (Bt, N x K row-major, leading dimension ldb).
@@ -263,9 +268,11 @@ gemm_status_t validate(int dtype, int64_t M, int64_t N, int64_t K, const void* A
   if (cdiv(M, 64) * cdiv(N, 64) > tiles_lim) return fail(GEMM_ERR_INVALID_ARG, "output too large");
   const size_t es = in_bytes(dtype);
   const size_t cb = span_bytes(M, N, ldc, c_es ? c_es : out_bytes(dtype));
-  if (overlap(C, cb, A, at ? span_bytes(K, M, lda, es) : span_bytes(M, K, lda, es)) ||
-      overlap(C, cb, B, bt ? span_bytes(N, K, ldb, es) : span_bytes(K, N, ldb, es)))
-    return fail(GEMM_ERR_ALIAS, "C overlaps A or B");
+  const size_t ab = at ? span_bytes(K, M, lda, es) : span_bytes(M, K, lda, es);
+  const size_t bb = bt ? span_bytes(N, K, ldb, es) : span_bytes(K, N, ldb, es);
+  if (ab >= kSpanLimit || bb >= kSpanLimit || cb >= kSpanLimit)
+    return fail(GEMM_ERR_INVALID_ARG, "an operand's byte range reaches 2^63 (leading dimension too large)");
+  if (overlap(C, cb, A, ab) || overlap(C, cb, B, bb)) return fail(GEMM_ERR_ALIAS, "C overlaps A or B");
   return GEMM_OK;
 }
 

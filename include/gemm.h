@@ -39,6 +39,9 @@
  *              M, N or K < 0                              -> INVALID_ARG
  *              lda < max(1,K), ldb < max(1,N), ldc < max(1,N) -> INVALID_ARG
  *              NULL A (M,K > 0), B (K,N > 0) or C (M,N > 0) -> INVALID_ARG
+ *              M, N or K above 2^31-1, C of more than 2^31-1
+ *              64 x 64 tiles, or an operand whose byte range
+ *              (leading dimension included) reaches 2^63     -> INVALID_ARG
  *              byte range of C overlapping that of A or B   -> ALIAS
  *              forced configuration unknown / wrong dtype   -> UNSUPPORTED
  *              launch failure reported by the HIP runtime   -> HIP
