@@ -797,6 +797,8 @@ gemm_status_t gemm_f8_trans(int64_t M, int64_t N, int64_t K, const gemm_f8_t* A,
 
 int64_t gemm_splitk_workspace_bytes(int32_t dtype, int64_t M, int64_t N, int64_t K, int32_t splits) {
   if (!valid_dtype(dtype) || M < 0 || N < 0 || K < 0) return -1;
+  const int64_t lim = 0x7fffffff;
+  if (M > lim || N > lim || K > lim || cdiv(M, 64) * cdiv(N, 64) > lim) return -1;
   if (splits <= 0) splits = select(dtype, M, N, K, true).splits;
   int64_t S, Kc;
   split_shape(K, splits, S, Kc);

@@ -253,7 +253,9 @@ gemm_status_t gemm_f8_splitk(int64_t M, int64_t N, int64_t K,
 
 /* Workspace bytes a split-K call with `splits` requested chunks needs
  * (0 when it would not split; splits <= 0 means the library's choice for
- * the shape).  Negative sizes give -1. */
+ * the shape).  An unknown dtype, negative sizes or sizes that the GEMM
+ * calls refuse (above 2^31-1, or C of more than 2^31-1 64 x 64 tiles)
+ * give -1. */
 int64_t gemm_splitk_workspace_bytes(int32_t dtype, int64_t M, int64_t N, int64_t K,
                                     int32_t splits);
 

@@ -208,6 +208,10 @@ def test_splitk_workspace_and_selection():
     assert gemm.gemm_splitk_workspace_bytes(f32, 10, 20, 1000, 1) == 0
     assert gemm.gemm_splitk_workspace_bytes(f32, -1, 20, 1000, 2) == -1
     assert gemm.gemm_splitk_workspace_bytes(7, 1, 1, 1, 2) == -1
+    # Sizes the GEMM calls refuse: no size (and no overflow) either.
+    assert gemm.gemm_splitk_workspace_bytes(f32, 2 ** 31, 20, 1000, 2) == -1
+    assert gemm.gemm_splitk_workspace_bytes(f32, 2 ** 40, 2 ** 40, 2 ** 20, 2) == -1
+    assert gemm.gemm_splitk_workspace_bytes(f32, 2 ** 31 - 1, 2 ** 31 - 1, 1000, 2) == -1
     for dt in (f32, f16):
         assert gemm.gemm_select_splitk_config(dt, 1024, 1024, 8192).splits > 1
         assert gemm.gemm_select_splitk_config(dt, 4096, 4096, 4096).splits == 1
