@@ -11,6 +11,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -79,8 +80,74 @@ size_t out_bytes(int d) { return d == GEMM_DTYPE_F32 ? 4 : 2; }
 // The type of C (the split-K reduction writes it).
 int out_dtype(int d) { return is_f8(d) ? GEMM_DTYPE_BF16 : d; }
 
+// One workgroup with its CU to itself, measured on MI355X with 64
+// workgroups of each variant while the other CUs idle, at two K (1024 and
+// 8192; FP32 512 and 4096): eff1 = the loop's rate from the slope, relative
+// to the cost model's per-CU rate R; fixed_us = the intercept (launch,
+// pipeline fill, epilogue).  With few CUs busy the 16- and 8-bit matrix
+// instructions keep a higher clock, so eff1 exceeds the full-GPU eff of the
+// large tiles; small tiles cannot hide their latency alone and fall below
+// it.  E5M2 takes E4M3's figures (same tiles); variants not listed use eff
+// and no fixed cost.
+struct AloneRate {
+  const char* name;
+  float eff1, fixed_us;
+};
+const AloneRate kAlone[] = {
+    {"dl_f32_256x256x32_w128x128_s2", 1.017f, 10.52f},
+    {"dl_f32_256x256x16_w128x128_s4", 1.005f, 7.65f},
+    {"dl_f32_256x128x32_w128x64_s3", 0.996f, 7.40f},
+    {"dl_f32_128x256x32_w64x128_s3", 1.005f, 5.82f}, {"dl_f32_128x128x32_w64x64_s3", 0.997f, 5.18f},
+    {"mfma_f32_128x128x32_w64x64", 0.759f, 4.35f}, {"mfma_f32_128x128x16_w64x64", 0.735f, 4.51f},
+    {"mfma_f32_256x128x32_w128x64", 0.837f, 7.04f}, {"mfma_f32_256x256x32_w128x128", 0.893f, 8.31f},
+    {"mfma_f32_128x256x32_w64x128", 0.825f, 4.98f}, {"mfma_f32_64x64x32_w32x32", 0.585f, 3.17f},
+    {"mfma_f32_128x64x32_w64x32", 0.669f, 3.94f}, {"tr_f16_256x256x64_w128x128_s2", 1.556f, 8.31f},
+    {"tr_f16_256x256x32_w128x128_s4", 1.716f, 8.42f},
+    {"tr_f16_256x256x32_w128x128_s5", 1.771f, 8.69f},
+    {"tr_f16_256x128x64_w128x64_s3", 1.721f, 5.93f},
+    {"tr_f16_128x256x64_w64x128_s3", 1.691f, 6.18f}, {"tr_f16_128x128x64_w64x64_s2", 0.767f, 1.36f},
+    {"tr_f16_256x128x64_w128x64_s3_p4", 1.835f, 5.86f},
+    {"tr_f16_256x128x64_w128x64_s3_p2", 1.854f, 6.37f},
+    {"pipe_f16_256x256x64_w128x128", 1.157f, 7.29f}, {"pipe_f16_256x128x64_w128x64", 0.709f, 4.58f},
+    {"pipe_f16_128x256x64_w64x128", 0.791f, 5.90f}, {"pipe_f16_128x128x64_w64x64", 0.428f, 2.48f},
+    {"pipe_f16_256x256x64_w128x64", 1.078f, 6.55f}, {"pipe_f16_256x256x64_w64x128", 1.087f, 4.54f},
+    {"mfma_f16_256x256x64_w128x128", 0.840f, 8.11f}, {"mfma_f16_256x128x64_w128x64", 0.545f, 6.93f},
+    {"mfma_f16_128x256x64_w64x128", 0.547f, 2.75f}, {"mfma_f16_128x128x64_w64x64", 0.381f, 2.74f},
+    {"mfma_f16_64x64x64_w32x32", 0.126f, 1.30f}, {"tr_bf16_256x256x64_w128x128_s2", 1.554f, 8.22f},
+    {"tr_bf16_256x256x32_w128x128_s4", 1.746f, 8.66f},
+    {"tr_bf16_256x256x32_w128x128_s5", 1.784f, 9.04f},
+    {"tr_bf16_256x128x64_w128x64_s3", 1.721f, 6.07f},
+    {"tr_bf16_128x256x64_w64x128_s3", 1.677f, 6.24f},
+    {"tr_bf16_128x128x64_w64x64_s2", 0.770f, 1.69f},
+    {"tr_bf16_256x128x64_w128x64_s3_p4", 1.841f, 5.98f},
+    {"tr_bf16_256x128x64_w128x64_s3_p2", 1.870f, 6.54f},
+    {"mfma_bf16_256x256x64_w128x128", 0.849f, 7.43f},
+    {"mfma_bf16_256x128x64_w128x64", 0.547f, 5.94f},
+    {"mfma_bf16_128x256x64_w64x128", 0.546f, 2.76f}, {"mfma_bf16_128x128x64_w64x64", 0.381f, 2.79f},
+    {"mfma_bf16_64x64x64_w32x32", 0.126f, 1.39f}, {"tr_f8_256x256x128_w128x128_s2", 1.774f, 8.60f},
+    {"tr_f8_256x256x64_w128x128_s4", 1.597f, 8.70f},
+    {"tr_f8_128x256x128_w64x128_s3", 1.687f, 6.30f},
+    {"tr_f8_128x256x128_w64x128_s3_p4", 1.788f, 6.16f},
+};
+
+double model_rate(int dtype);
+
+// The loop rate (relative to R) of one workgroup per CU with all 256 CUs
+// busy, for a tile that fills its CU's LDS: eff with the fixed cost taken
+// out of the time eff gives for one round at K = 4096.
+double full_loop_rate(int dtype, const Variant& v, const AloneRate& a) {
+  const double eff = v.eff > 0.f ? v.eff : 0.1;
+  const double work = 2.0 * v.desc.bm * v.desc.bn * 4096.0;
+  const double inv = 1.0 / eff - a.fixed_us * 1e-6 * model_rate(dtype) / work;
+  return inv > 0.0 ? 1.0 / inv : eff;
+}
+
 struct Table {
   std::vector<Variant> v[kDtypes];  // per dtype
+  std::vector<AloneRate> alone[kDtypes];  // per variant: kAlone's figures, else {eff, 0}
+  // Loop rate with all 256 CUs busy over eff1, per dtype, from the default
+  // tile (at most 1): the matrix units' clock falls as more CUs run them.
+  double derate[kDtypes];
   Table() {
     int n = 0;
     const Variant* p = sgemm_dl_variants(&n);
@@ -103,14 +170,31 @@ struct Table {
     v[3].insert(v[3].end(), p, p + n);
     p = hgemm_tr_variants(&n, 3);
     v[4].insert(v[4].end(), p, p + n);
-    for (int d = 0; d < kDtypes; ++d)
-      for (size_t i = 0; i < v[d].size(); ++i) v[d][i].desc.id = (int32_t)i;
+    for (int d = 0; d < kDtypes; ++d) {
+      derate[d] = 1.0;
+      for (size_t i = 0; i < v[d].size(); ++i) {
+        v[d][i].desc.id = (int32_t)i;
+        std::string name = v[d][i].desc.name;
+        if (name.rfind("tr_e5m2_", 0) == 0) name = "tr_f8_" + name.substr(8);
+        AloneRate r{v[d][i].desc.name, v[d][i].eff, 0.f};
+        for (const AloneRate& a : kAlone)
+          if (name == a.name) r = AloneRate{v[d][i].desc.name, a.eff1, a.fixed_us};
+        alone[d].push_back(r);
+      }
+      if (!v[d].empty() && alone[d][0].eff1 > 0.f)
+        derate[d] = std::min(1.0, full_loop_rate(d, v[d][0], alone[d][0]) / alone[d][0].eff1);
+    }
   }
 };
 
 const Table& table() {
   static Table t;
   return t;
+}
+
+// The cost model's per-CU rate R for a dtype (FP32 matrix, 16-bit, 8-bit).
+double model_rate(int dtype) {
+  return dtype == GEMM_DTYPE_F32 ? 0.59e12 : is_f8(dtype) ? 9.4e12 : 4.7e12;
 }
 
 struct TuneEntry {
@@ -142,13 +226,20 @@ void split_shape(int64_t K, int64_t splits, int64_t& S, int64_t& Kc) {
 
 // Shape heuristic: a cost model over the matrix-core variants (a tuning
 // table entry overrides it for its exact shape).  Times in seconds:
-//   GEMM:   rounds * 2*bm*bn*Kc / (eff * R / w),  rounds = ceil(WGs / slots),
+//   GEMM, unsplit with at most one workgroup per CU (WGs <= 256):
+//           fixed + 2*bm*bn*K / (r * R), fixed and r = the workgroup's
+//           measured intercept and loop rate alone (kAlone), r lowered
+//           linearly from 64 to 256 busy CUs to its loop rate with all
+//           CUs busy;
+//   GEMM otherwise:
+//           rounds * 2*bm*bn*Kc / (eff * R / w),  rounds = ceil(WGs / slots),
 //           w = workgroups per CU (as LDS allows, at most 2; 1 when there
 //           are no more workgroups than CUs), slots = 256 w,
 //           R = per-CU rate of the best tile with the GPU full (measured
 //           on MI355X at 4096^3), eff = the variant's relative whole-GPU
 //           rate when full;
-//   split:  + (2*S*M*N*4 + M*N*es) bytes / 4 TB/s + a launch, for the
+//   split:  the partials' rounds, each with the variant's fixed cost,
+//           + (2*S*M*N*4 + M*N*es) bytes / 4 TB/s + a launch, for the
 //           partials written, read back and the result written.
 // Ties go to the earlier table entry.
 struct Choice {
@@ -159,16 +250,35 @@ struct Choice {
 
 double gemm_seconds(int dtype, const Variant& v, int64_t M, int64_t N, int64_t Kc, int64_t S) {
   const gemm_config_t& d = v.desc;
-  const double rate = dtype == GEMM_DTYPE_F32 ? 0.59e12 : is_f8(dtype) ? 9.4e12 : 4.7e12;
+  const double rate = model_rate(dtype);
   int64_t per_cu = (160 * 1024) / (d.lds_bytes > 0 ? d.lds_bytes : 1);
   per_cu = per_cu < 1 ? 1 : per_cu > 2 ? 2 : per_cu;
   const int64_t wgs = cdiv(M, d.bm) * cdiv(N, d.bn) * S;
+  if (S == 1 && wgs <= 256) {
+    // Unsplit, one workgroup per CU at most: the fixed cost plus the loop
+    // at its rate alone, eff1 with up to 64 CUs busy, linearly down to its
+    // rate with all 256 busy.  That is full_loop_rate for a tile that fills
+    // its CU's LDS (eff was measured with one workgroup per CU); for a
+    // smaller one, which eff measured two to a CU, the dtype's derate of
+    // eff1, at most eff.
+    const Table& t = table();
+    const AloneRate& a = t.alone[dtype][d.id];
+    const double e1 = a.eff1 > 0.f ? a.eff1 : 0.1;
+    const double eff = v.eff > 0.f ? v.eff : 0.1;
+    const double full = per_cu == 1 ? full_loop_rate(dtype, v, a) : std::min(eff, e1 * t.derate[dtype]);
+    const double f = wgs <= 64 ? 0.0 : (double)(wgs - 64) / 192.0;
+    const double r = e1 + (full - e1) * f;
+    return a.fixed_us * 1e-6 + 2.0 * d.bm * d.bn * (double)(Kc > 0 ? Kc : 1) / (r * rate);
+  }
   const int64_t rounds = cdiv(wgs, 256 * per_cu);
   const double eff = v.eff > 0.f ? v.eff : 0.1;
   // A CU running w workgroups at once gives each 1/w of its rate; with
-  // fewer workgroups than CUs each runs alone.
+  // fewer workgroups than CUs each runs alone.  Split partials, short K
+  // chunks, pay each round's fixed cost on top (eff, measured at K = 4096,
+  // holds it for the unsplit rounds).
   const int64_t w = wgs <= 256 ? 1 : per_cu;
-  return (double)rounds * 2.0 * d.bm * d.bn * (double)(Kc > 0 ? Kc : 1) * w / (eff * rate);
+  const double fixed = S > 1 ? (double)rounds * table().alone[dtype][d.id].fixed_us * 1e-6 : 0.0;
+  return fixed + (double)rounds * 2.0 * d.bm * d.bn * (double)(Kc > 0 ? Kc : 1) * w / (eff * rate);
 }
 
 Choice heuristic(int dtype, int64_t M, int64_t N, int64_t K, bool allow_split, bool need_epi = false,

@@ -166,6 +166,16 @@ def test_heuristic_selection():
     for dt in (gemm.DTYPE_F32, gemm.DTYPE_F16, gemm.DTYPE_BF16):
         for M, N, K in [(1, 1, 1), (4096, 11008, 4096), (1024, 1024, 8192)]:
             assert gemm.gemm_select_config(dt, M, N, K).family == gemm.FAMILY_MFMA
+    # At 4096^3 every type takes its first (default) tile: one per CU.
+    for dt in (gemm.DTYPE_F32, gemm.DTYPE_F16, gemm.DTYPE_BF16, gemm.DTYPE_F8, gemm.DTYPE_E5M2):
+        assert gemm.gemm_select_config(dt, 4096, 4096, 4096).name == gemm.gemm_get_config(dt, 0).name
+    # Few output tiles, long K, unsplit: the 16-bit types keep an LDS-direct
+    # tile (its rate alone); small tiles of the general kernel cannot hide
+    # their latency with one workgroup per CU.
+    for dt in (gemm.DTYPE_F16, gemm.DTYPE_BF16):
+        assert gemm.gemm_select_config(dt, 1024, 1024, 8192).name.startswith(b"tr_")
+        # Short K: the smallest LDS-direct tile (lowest fixed cost) wins.
+        assert gemm.gemm_select_config(dt, 1024, 1024, 1024).bm * gemm.gemm_select_config(dt, 1024, 1024, 1024).bn == 128 * 128
 
 
 def test_tuning_table(tmp_path):
