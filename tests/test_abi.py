@@ -178,6 +178,24 @@ def test_heuristic_selection():
         assert gemm.gemm_select_config(dt, 1024, 1024, 1024).bm * gemm.gemm_select_config(dt, 1024, 1024, 1024).bn == 128 * 128
 
 
+def test_every_matrix_core_variant_has_its_alone_figures():
+    # The cost model's per-variant rate and fixed cost of a lone workgroup
+    # are keyed by name in gemm_api.hip; a renamed or added variant without
+    # them would silently fall back to its full-GPU eff.
+    src = open(os.path.join(ROOT, "dense_gemm_row_amd", "csrc", "gemm_api.hip")).read()
+    body = src[src.index("const AloneRate kAlone[] = {"):]
+    body = body[:body.index("};")]
+    listed = set(re.findall(r'\{"([a-z0-9_]+)", [0-9.]+f, [0-9.]+f\}', body))
+    for dt in (gemm.DTYPE_F32, gemm.DTYPE_F16, gemm.DTYPE_BF16, gemm.DTYPE_F8):
+        for i in range(gemm.gemm_num_configs(dt)):
+            c = gemm.gemm_get_config(dt, i)
+            if c.family == gemm.FAMILY_MFMA:
+                assert c.name.decode() in listed, c.name
+    assert len(listed) == sum(1 for dt in (gemm.DTYPE_F32, gemm.DTYPE_F16, gemm.DTYPE_BF16, gemm.DTYPE_F8)
+                              for i in range(gemm.gemm_num_configs(dt))
+                              if gemm.gemm_get_config(dt, i).family == gemm.FAMILY_MFMA)
+
+
 def test_tuning_table(tmp_path):
     cfg = gemm.gemm_get_config(gemm.DTYPE_F32, 1)
     path = tmp_path / "tuned.txt"
