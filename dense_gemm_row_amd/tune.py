@@ -13,6 +13,11 @@ each with its mean launch time and TFLOP/s.
     python -m dense_gemm_row_amd.tune --shapes 4096x4096x4096 1024x1024x8192 \\
         --dtypes f32 f16 --out tuning.txt
 
+``--alone`` instead measures, per matrix-core variant, a workgroup with its
+CU to itself (64 workgroups, the other CUs idle) at two K, and prints the
+loop rate from the slope (relative to the cost model's per-CU rate) and the
+intercept in the form of the cost model's table of lone-workgroup figures.
+
 Timing: a few untimed launches, then ``--reps`` launches back to back
 between two HIP events on the launch stream (mean per launch).  Every
 candidate passes through the C-ABI with its configuration forced
@@ -81,13 +86,18 @@ def time_config(gemm, torch, fn, args, cfg, stream, warmup: int, reps: int, ws=N
     return e0.elapsed_time(e1) / reps
 
 
-def tune_shape(gemm, torch, kind: str, M: int, N: int, K: int, orders, warmup: int,
-               reps: int, splits=(1,)) -> dict:
+def _types(gemm, torch, kind: str):
+    """The dtype code, the operands' torch type and C's (FP8 products are BF16)."""
     dtype = {"f32": gemm.DTYPE_F32, "f16": gemm.DTYPE_F16, "bf16": gemm.DTYPE_BF16,
              "f8": gemm.DTYPE_F8, "e5m2": gemm.DTYPE_E5M2}[kind]
     tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16,
            "f8": torch.float8_e4m3fn, "e5m2": torch.float8_e5m2}[kind]
-    cdt = torch.bfloat16 if kind in ("f8", "e5m2") else tdt  # FP8 products are BF16
+    return dtype, tdt, (torch.bfloat16 if kind in ("f8", "e5m2") else tdt)
+
+
+def tune_shape(gemm, torch, kind: str, M: int, N: int, K: int, orders, warmup: int,
+               reps: int, splits=(1,)) -> dict:
+    dtype, tdt, cdt = _types(gemm, torch, kind)
     dev = torch.device("cuda:0")
     gen = torch.Generator(device=dev)
     gen.manual_seed(M * 1000003 + N * 1009 + K)
@@ -143,9 +153,46 @@ def tune_shape(gemm, torch, kind: str, M: int, N: int, K: int, orders, warmup: i
     return rep
 
 
+# The cost model's per-CU rate (model_rate in the C-ABI's cost model).
+MODEL_RATE = {"f32": 0.59e12, "f16": 4.7e12, "bf16": 4.7e12, "f8": 9.4e12, "e5m2": 9.4e12}
+
+
+def alone_figures(gemm, torch, kind: str, warmup: int, reps: int):
+    """(name, eff1, fixed_us) per matrix-core variant: 64 workgroups (an
+    8 x 8 grid of tiles), timed at two K; the slope gives the loop's rate,
+    the intercept the fixed cost."""
+    dt, tin, tout = _types(gemm, torch, kind)
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    fn = gemm.entry(dt, "_ex")
+    ks = (512, 4096) if kind == "f32" else (1024, 8192)
+    out = []
+    for cfg in gemm.configs(dt):
+        if cfg.family != gemm.FAMILY_MFMA:
+            continue
+        M, N = 8 * cfg.bm, 8 * cfg.bn
+        t = {}
+        for K in ks:
+            a = (torch.rand((M, K), device=dev) - 0.5).to(tin)
+            b = (torch.rand((K, N), device=dev) - 0.5).to(tin)
+            c = torch.empty((M, N), device=dev, dtype=tout)
+            ms = time_config(gemm, torch, fn, (M, N, K, a.data_ptr(), K, b.data_ptr(), N, c.data_ptr(), N),
+                             cfg, stream, warmup, reps)
+            if ms is not None:
+                t[K] = ms * 1e3
+        if len(t) < 2:
+            continue
+        slope = (t[ks[1]] - t[ks[0]]) / (ks[1] - ks[0])          # microseconds per unit of K
+        eff1 = 2.0 * cfg.bm * cfg.bn / (slope * 1e-6) / MODEL_RATE[kind]
+        out.append((cfg.name.decode(), eff1, t[ks[0]] - slope * ks[0]))
+    return out
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
-    ap.add_argument("--shapes", nargs="+", type=parse_shape, required=True, help="MxNxK ...")
+    ap.add_argument("--shapes", nargs="+", type=parse_shape, default=[], help="MxNxK ...")
+    ap.add_argument("--alone", action="store_true",
+                    help="measure each variant's lone-workgroup loop rate and fixed cost instead")
     ap.add_argument("--dtypes", nargs="+", choices=["f32", "f16", "bf16", "f8", "e5m2"],
                     default=["f32", "f16"])
     ap.add_argument("--orders", nargs="+", type=parse_order,
@@ -167,6 +214,13 @@ def main(argv=None) -> int:
         return 1
     gemm.lib()
     torch.cuda.set_device(0)
+    if args.alone:
+        for kind in args.dtypes:
+            for name, eff1, fixed in alone_figures(gemm, torch, kind, args.warmup, args.reps):
+                print(f'{{"{name}", {eff1:.3f}f, {fixed:.2f}f}},', flush=True)
+        return 0
+    if not args.shapes:
+        ap.error("--shapes is required (or --alone)")
     lines = ["# libgemm tuning table: dtype M N K variant order group_m",
              f"# written by dense_gemm_row_amd.tune on {torch.cuda.get_device_name(0)}"]
     for kind in args.dtypes:
