@@ -174,6 +174,11 @@ def test_heuristic_selection():
     # their latency with one workgroup per CU.
     for dt in (gemm.DTYPE_F16, gemm.DTYPE_BF16):
         assert gemm.gemm_select_config(dt, 1024, 1024, 8192).name.startswith(b"tr_")
+    # E5M2 shares E4M3's tiles and measured figures, so it picks the same.
+    for shape in [(1024, 1024, 8192), (2048, 2048, 2048), (512, 512, 512), (4096, 4096, 4096)]:
+        f8 = gemm.gemm_select_config(gemm.DTYPE_F8, *shape).name.decode()
+        assert gemm.gemm_select_config(gemm.DTYPE_E5M2, *shape).name.decode() == f8.replace("tr_f8_", "tr_e5m2_")
+    for dt in (gemm.DTYPE_F16, gemm.DTYPE_BF16):
         # Short K: the smallest LDS-direct tile (lowest fixed cost) wins.
         assert gemm.gemm_select_config(dt, 1024, 1024, 1024).bm * gemm.gemm_select_config(dt, 1024, 1024, 1024).bn == 128 * 128
 
