@@ -460,10 +460,10 @@ def e5m2_to_f64(bits) -> np.ndarray:
     return out
 
 
-def quantize_i8(v) -> np.ndarray:
+def quantize_i8(v, lib=None) -> np.ndarray:
     """INT8 codes of float64 values: nearest integer, ties to even,
     saturated to [-128, 127] (oracle_quantize_i8)."""
-    lib = load()
+    lib = lib or load()
     v = np.ascontiguousarray(np.asarray(v, dtype=np.float64))
     q = np.empty(v.shape, dtype=np.int8)
     if v.size:
@@ -471,11 +471,32 @@ def quantize_i8(v) -> np.ndarray:
     return q
 
 
-def q8_allowed(v: np.ndarray, err: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+def _code_of_exact_sum(a: np.ndarray, b: np.ndarray, lib=None) -> np.ndarray:
+    """INT8 code of the exact real a + b (binary64 a, b).  s = fl(a + b) and
+    its rounding error t (a + b = s + t exactly; Knuth's TwoSum) are formed
+    first.  Every half-integer below 2**52 is a binary64 value, and the
+    exact sum lies within half an ulp of s, so it sits on the same side of
+    every rounding boundary as s except s itself: the code of s, unless s
+    is a boundary n + 0.5 and t moves the exact sum off it (t > 0: n + 1,
+    t < 0: n), then saturated."""
+    s = a + b
+    bb = s - a
+    t = (a - (s - bb)) + (b - bb)
+    q = quantize_i8(s, lib=lib).astype(np.int64)
+    fl = np.floor(s)
+    tie = (s - fl) == 0.5
+    q = np.where(tie & (t > 0), fl + 1, np.where(tie & (t < 0), fl, q))
+    return np.clip(q, -128, 127).astype(np.int8)
+
+
+def q8_allowed(v: np.ndarray, err: np.ndarray, lib=None) -> tuple[np.ndarray, np.ndarray]:
     """(lo, hi) int8 bounds of the codes that a computed value within
     `err` of the exact epilogue value `v` may quantise to: quantisation is
-    monotone, so they are the codes of v - err and v + err.  A result is
-    valid when lo <= q <= hi (one code except near a rounding boundary)."""
+    monotone and steps by one code at each boundary, so the codes of the
+    reals in [v - err, v + err] are exactly lo..hi, the codes of the two
+    ends.  A result is valid when lo <= q <= hi (one code except near a
+    rounding boundary).  The ends' codes are those of the exact reals
+    v - err and v + err, not of their binary64 roundings."""
     v = np.asarray(v, dtype=np.float64)
     err = np.asarray(err, dtype=np.float64)
-    return quantize_i8(v - err), quantize_i8(v + err)
+    return _code_of_exact_sum(v, -err, lib=lib), _code_of_exact_sum(v, err, lib=lib)

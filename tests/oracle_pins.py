@@ -546,12 +546,49 @@ def pin_quantize_i8(lib):
         assert got == r, f"quantize({v}) = {got}, want {r}"
 
 
+def _q8_exact(x: Fraction) -> int:
+    """Nearest integer to a rational, ties to even, saturated to int8."""
+    f = x.numerator // x.denominator
+    frac = x - f
+    r = f + 1 if frac > Fraction(1, 2) else f if frac < Fraction(1, 2) else (f if f % 2 == 0 else f + 1)
+    return max(-128, min(127, r))
+
+
+def pin_q8_allowed(lib):
+    """The codes a value within err of v may take: for every v on a grid of
+    quarters and near-ties (both signs, past +-128) and every err (0, below
+    one binary64 ulp of v, a half, 1.3), the returned [lo, hi] equals the
+    set of codes of all reals in [v - err, v + err], found with exact
+    rational arithmetic: the codes of the interval's ends and every integer
+    between.  err = 0 gives the single code of v."""
+    vs = np.arange(-540, 541) / 4.0
+    vs = np.concatenate([vs, vs + 2.0 ** -20, vs - 2.0 ** -20])
+    for err in (0.0, 2.0 ** -60, 0.5, 1.3):
+        e = np.full(vs.shape, err)
+        lo, hi = oracle.q8_allowed(vs, e, lib=lib)
+        assert lo.shape == vs.shape and hi.shape == vs.shape
+        for v, a, b in zip(vs.tolist(), lo.tolist(), hi.tolist()):
+            x, d = Fraction(v), Fraction(err)
+            want_lo, want_hi = _q8_exact(x - d), _q8_exact(x + d)
+            # Quantisation is monotone and moves one code per boundary, so
+            # the reals of the interval reach every code between its ends.
+            assert (a, b) == (want_lo, want_hi), f"q8_allowed({v}, {err}) = {(a, b)}, want {(want_lo, want_hi)}"
+            if err == 0.0:
+                assert a == b == _q8_exact(x), f"q8_allowed({v}, 0) = {(a, b)}"
+    # Hand-worked: 2.5 +- 0.5 covers [2, 3], codes 2 (tie to even), 3, 4
+    # (3.0 + 0.5 is the tie 3.5 -> 4); 2.75 +- 0.25 covers [2.5, 3.0], codes 2..3.
+    lo, hi = oracle.q8_allowed(np.array([3.0, 2.75, -2.75, 127.2, -128.9]),
+                               np.array([0.5, 0.25, 0.25, 5.0, 0.3]), lib=lib)
+    assert lo.tolist() == [2, 2, -3, 122, -128] and hi.tolist() == [4, 3, -2, 127, -128], (lo, hi)
+
+
 PINS = [pin_identity, pin_permutation, pin_all_ones, pin_rank1, pin_k0_k1,
         pin_bruteforce_fractions, pin_numpy_matmul, pin_f16_decode, pin_bf16_decode,
         pin_e4m3_decode, pin_e5m2_decode,
         pin_error_metric, pin_epilogue_closed_form, pin_epilogue_reduces_to_plain,
         pin_epilogue_bruteforce, pin_bt_identity_permutation, pin_bt_matches_plain_transpose,
-        pin_bt_rank1, pin_trans_matches_materialised, pin_trans_identity_rank1, pin_quantize_i8]
+        pin_bt_rank1, pin_trans_matches_materialised, pin_trans_identity_rank1, pin_quantize_i8,
+        pin_q8_allowed]
 
 
 def run_all(lib) -> list[str]:

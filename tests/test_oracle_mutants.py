@@ -120,3 +120,51 @@ def test_unmutated_copy_passes(tmp_path):
     res = subprocess.run([sys.executable, os.path.join(ROOT, "tests", "_pin_runner.py"), lib],
                          capture_output=True, text=True, timeout=600)
     assert res.returncode == 0, res.stdout + res.stderr
+
+
+# Planted mistakes in the Python side of the oracle (the INT8 code bounds
+# for random-input results), each applied to a copy of oracle/__init__.py
+# that is loaded as a separate module over the same, unmutated C library.
+PY_SRC = os.path.join(ROOT, "oracle", "__init__.py")
+PY_MUTANTS = {
+    "q8_bounds_swapped": ("    return _code_of_exact_sum(v, -err, lib=lib), _code_of_exact_sum(v, err, lib=lib)",
+                          "    return _code_of_exact_sum(v, err, lib=lib), _code_of_exact_sum(v, -err, lib=lib)"),
+    "q8_lo_plus_one": ("    return _code_of_exact_sum(v, -err, lib=lib), ",
+                       "    return _code_of_exact_sum(v, -err, lib=lib) + np.int8(1), "),
+    "q8_hi_minus_one": (", _code_of_exact_sum(v, err, lib=lib)\n",
+                        ", _code_of_exact_sum(v, err, lib=lib) - np.int8(1)\n"),
+    "q8_err_doubled": ("    err = np.asarray(err, dtype=np.float64)\n    return _code",
+                       "    err = 2.0 * np.asarray(err, dtype=np.float64)\n    return _code"),
+    "q8_err_ignored": (", _code_of_exact_sum(v, err, lib=lib)\n",
+                       ", _code_of_exact_sum(v, 0.0 * err, lib=lib)\n"),
+    "q8_binary64_ends": ("    tie = (s - fl) == 0.5\n", "    tie = np.zeros(np.shape(s), dtype=bool)\n"),
+    "q8_tie_side_swapped": ("np.where(tie & (t > 0), fl + 1, np.where(tie & (t < 0), fl, q))",
+                            "np.where(tie & (t < 0), fl + 1, np.where(tie & (t > 0), fl, q))"),
+    "q8_no_saturation": ("    return np.clip(q, -128, 127).astype(np.int8)",
+                         "    return q.astype(np.int8)"),
+}
+
+
+def _mutant_module(text: str):
+    import types
+    mod = types.ModuleType("oracle_py_mutant")
+    mod.__file__ = PY_SRC  # the same directory, so the same liboracle.so
+    exec(compile(text, PY_SRC, "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name", sorted(PY_MUTANTS))
+def test_planted_python_mistake_is_caught(name, monkeypatch):
+    from tests import oracle_pins
+    old, new = PY_MUTANTS[name]
+    text = open(PY_SRC).read()
+    assert text.count(old) == 1, f"anchor for {name} not found once in oracle/__init__.py"
+    monkeypatch.setattr(oracle_pins, "oracle", _mutant_module(text.replace(old, new)))
+    with pytest.raises(AssertionError):
+        oracle_pins.pin_q8_allowed(oracle.load())
+
+
+def test_unmutated_python_copy_passes(monkeypatch):
+    from tests import oracle_pins
+    monkeypatch.setattr(oracle_pins, "oracle", _mutant_module(open(PY_SRC).read()))
+    oracle_pins.pin_q8_allowed(oracle.load())
