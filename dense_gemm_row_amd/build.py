@@ -20,7 +20,7 @@ BUILD_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libgemm.so")
 ARCH = "gfx950"
 
-SOURCES = ["gemm_api.hip", "splitk.hip", "sgemm_dl.hip", "sgemm_mfma.hip", "hgemm_mfma.hip", "hgemm_pipe.hip", "hgemm_tr.hip", "sgemm_simt.hip"]
+SOURCES = ["gemm_api.hip", "splitk.hip", "sgemm_dl.hip", "sgemm_mfma.hip", "hgemm_mfma.hip", "hgemm_tr.hip", "sgemm_simt.hip"]
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

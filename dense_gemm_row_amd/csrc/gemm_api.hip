@@ -108,9 +108,6 @@ const AloneRate kAlone[] = {
     {"tr_f16_128x256x64_w64x128_s3", 1.691f, 6.18f}, {"tr_f16_128x128x64_w64x64_s2", 0.767f, 1.36f},
     {"tr_f16_256x128x64_w128x64_s3_p4", 1.835f, 5.86f},
     {"tr_f16_256x128x64_w128x64_s3_p2", 1.854f, 6.37f},
-    {"pipe_f16_256x256x64_w128x128", 1.157f, 7.29f}, {"pipe_f16_256x128x64_w128x64", 0.709f, 4.58f},
-    {"pipe_f16_128x256x64_w64x128", 0.791f, 5.90f}, {"pipe_f16_128x128x64_w64x64", 0.428f, 2.48f},
-    {"pipe_f16_256x256x64_w128x64", 1.078f, 6.55f}, {"pipe_f16_256x256x64_w64x128", 1.087f, 4.54f},
     {"mfma_f16_256x256x64_w128x128", 0.840f, 8.11f}, {"mfma_f16_256x128x64_w128x64", 0.545f, 6.93f},
     {"mfma_f16_128x256x64_w64x128", 0.547f, 2.75f}, {"mfma_f16_128x128x64_w64x64", 0.381f, 2.74f},
     {"mfma_f16_64x64x64_w32x32", 0.126f, 1.30f}, {"tr_bf16_256x256x64_w128x128_s2", 1.554f, 8.22f},
@@ -157,8 +154,6 @@ struct Table {
     p = sgemm_simt_variants(&n);
     v[0].insert(v[0].end(), p, p + n);
     p = hgemm_tr_variants(&n);
-    v[1].insert(v[1].end(), p, p + n);
-    p = hgemm_pipe_variants(&n);
     v[1].insert(v[1].end(), p, p + n);
     p = hgemm_mfma_variants(&n);
     v[1].insert(v[1].end(), p, p + n);
@@ -214,14 +209,26 @@ int find_by_name(int dtype, const char* name) {
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Split-K chunking: Kc = roundup(ceil(K / splits), 64) (a whole number of
-// K slices for every variant, 16-byte aligned chunk bases), S = ceil(K / Kc).
-constexpr int64_t kChunkAlign = 64;
-void split_shape(int64_t K, int64_t splits, int64_t& S, int64_t& Kc) {
+// Split-K chunking: Kc = roundup(ceil(K / splits), align), S = ceil(K / Kc).
+// align is a multiple of every K slice of the dtype's variants (BK <= 64
+// for 32- and 16-bit elements, <= 128 for 8-bit ones), so every chunk but
+// the last is a whole number of slices: a slice never reaches into the next
+// chunk's rows of B, whose values could otherwise meet A's zero padding
+// (0 * Inf = NaN).  Chunk bases stay 16-byte aligned.
+int64_t chunk_align(int dtype) { return is_f8(dtype) ? 128 : 64; }
+void split_shape(int dtype, int64_t K, int64_t splits, int64_t& S, int64_t& Kc) {
   if (splits < 1) splits = 1;
-  Kc = cdiv(cdiv(K, splits), kChunkAlign) * kChunkAlign;
-  if (Kc < 1) Kc = kChunkAlign;
+  const int64_t align = chunk_align(dtype);
+  Kc = cdiv(cdiv(K, splits), align) * align;
+  if (Kc < 1) Kc = align;
   S = K > 0 ? cdiv(K, Kc) : 1;
+}
+
+// Workspace bytes of S FP32 partial planes of M x N, or -1 when the product
+// does not fit an int64.
+int64_t partial_bytes(int64_t S, int64_t M, int64_t N) {
+  const __int128 b = (__int128)S * M * N * 4;
+  return b > (__int128)INT64_MAX ? -1 : (int64_t)b;
 }
 
 // Shape heuristic: a cost model over the matrix-core variants (a tuning
@@ -297,7 +304,7 @@ Choice heuristic(int dtype, int64_t M, int64_t N, int64_t K, bool allow_split, b
     if (!allow_split || !v[i].launch_partial || M == 0 || N == 0) continue;
     for (int64_t want = 2; want <= 32; ++want) {
       int64_t S, Kc;
-      split_shape(K, want, S, Kc);
+      split_shape(dtype, K, want, S, Kc);
       if (S != want) continue;
       if (Kc < 256) break;
       const double t = gemm_seconds(dtype, v[i], M, N, Kc, S) +
@@ -336,7 +343,9 @@ TileMap make_map(const gemm_config_t& c, int64_t M, int64_t N) {
   t.tiles_m = (int)cdiv(M, c.bm);
   t.tiles_n = (int)cdiv(N, c.bn);
   t.order = c.order;
-  t.group_m = c.group_m;
+  // Bands taller than the grid are the whole grid (and keep the band
+  // width, group_m * tiles_n, within an int for any requested group_m).
+  t.group_m = c.group_m < 1 ? 1 : (int)std::min<int64_t>(c.group_m, t.tiles_m);
   t.xcds = kXcds;
   return t;
 }
@@ -469,7 +478,7 @@ gemm_status_t resolve_forced(int dtype, int64_t M, int64_t N, int64_t K, const g
     cfg.splits = 1;
     for (int64_t want = 1; want <= 32; ++want) {
       int64_t S, Kc;
-      split_shape(K, want, S, Kc);
+      split_shape(dtype, K, want, S, Kc);
       if (S != want) continue;
       if (want > 1 && (Kc < 256 || !v[forced->id].launch_partial)) break;
       const double es = (double)out_bytes(dtype);
@@ -687,12 +696,13 @@ gemm_status_t run_splitk(int dtype, int64_t M, int64_t N, int64_t K, const void*
   if (st != GEMM_OK) return st;
   if (M == 0 || N == 0) return GEMM_OK;
   int64_t S, Kc;
-  split_shape(K, cfg.splits, S, Kc);
+  split_shape(dtype, K, cfg.splits, S, Kc);
   const Variant& var = table().v[dtype][cfg.id];
   const bool vec = vector_path(dtype, A, lda, B, ldb, C, ldc, K, N);
   if (S <= 1 || K == 0 || !vec || !var.launch_partial)
     return launch_plain(dtype, cfg, M, N, K, A, lda, B, ldb, C, ldc, stream);
-  const int64_t need = S * M * N * 4;
+  const int64_t need = partial_bytes(S, M, N);
+  if (need < 0) return fail(GEMM_ERR_INVALID_ARG, "workspace size overflows int64");
   if (!ws) return fail(GEMM_ERR_INVALID_ARG, "workspace is NULL (%lld bytes needed)", (long long)need);
   if (ws_bytes < need)
     return fail(GEMM_ERR_INVALID_ARG, "workspace of %lld bytes, %lld needed", (long long)ws_bytes,
@@ -911,8 +921,8 @@ int64_t gemm_splitk_workspace_bytes(int32_t dtype, int64_t M, int64_t N, int64_t
   if (M > lim || N > lim || K > lim || cdiv(M, 64) * cdiv(N, 64) > lim) return -1;
   if (splits <= 0) splits = select(dtype, M, N, K, true).splits;
   int64_t S, Kc;
-  split_shape(K, splits, S, Kc);
-  return (S > 1 && M > 0 && N > 0) ? S * M * N * 4 : 0;
+  split_shape(dtype, K, splits, S, Kc);
+  return (S > 1 && M > 0 && N > 0) ? partial_bytes(S, M, N) : 0;
 }
 
 gemm_status_t gemm_select_splitk_config(int32_t dtype, int64_t M, int64_t N, int64_t K,
@@ -1021,6 +1031,7 @@ const char* gemm_status_string(gemm_status_t s) {
 }
 
 const char* gemm_last_error(void) { return g_err; }
+const char* gemm_last_hip_error(void) { return g_err; }
 
 const char* gemm_version(void) { return "libgemm 0.1.0 (gfx950)"; }
 

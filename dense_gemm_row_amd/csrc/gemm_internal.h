@@ -189,7 +189,8 @@ __host__ __device__ inline void tile_of_block(int b, const TileMap& t, int& tm, 
     const int q = G / t.xcds, r = G % t.xcds;
     bb = x * q + (x < r ? x : r) + b / t.xcds;
   }
-  const int gm = t.group_m < 1 ? 1 : t.group_m;
+  // A band never exceeds the grid, so width <= G fits an int for any group_m.
+  const int gm = t.group_m < 1 ? 1 : (t.group_m > t.tiles_m ? t.tiles_m : t.group_m);
   const int width = gm * t.tiles_n;  // tiles in one band
   const int band = bb / width;
   const int first_m = band * gm;
@@ -289,7 +290,6 @@ const Variant* sgemm_simt_variants(int* count);
 // bfloat16 form, a bfloat16 one (bf16 = true); the LDS-direct family also
 // an FP8 E4M3 one (ty: 0 FP16, 1 BF16, 2 FP8 with BF16 output).
 const Variant* hgemm_mfma_variants(int* count, bool bf16 = false);
-const Variant* hgemm_pipe_variants(int* count);
 // ty: 0 FP16, 1 BF16, 2 FP8 E4M3, 3 FP8 E5M2.
 const Variant* hgemm_tr_variants(int* count, int ty = 0);
 

@@ -64,7 +64,7 @@ COPY = "copy(neg)"
 _TR_TYPE = re.compile(r"Shape<(?:\d+, ){6}\d+, (?:true|false), (\d+), (?:true|false)(?:, \d+)?>")
 _PREFIX_FAMILY = {"dl_f32": "sgemm_dl", "mfma_f32": "sgemm_mfma", "simt_f32": "sgemm_simt",
                   "tr_f16": "hgemm_tr", "tr_bf16": "hgemm_tr_bf16", "tr_f8": "hgemm_tr_f8",
-                  "tr_e5m2": "hgemm_tr_e5m2", "pipe_f16": "hgemm_pipe", "mfma_f16": "hgemm_mfma"}
+                  "tr_e5m2": "hgemm_tr_e5m2", "mfma_f16": "hgemm_mfma"}
 SUMMARY_CMD = "python -m dense_gemm_row_amd.evidence <out>"
 
 
@@ -79,9 +79,8 @@ def family(kernel_name: str):
         m = _TR_TYPE.search(kernel_name)
         ty = m.group(1) if m else "0"
         return {"1": "hgemm_tr_bf16", "2": "hgemm_tr_f8", "3": "hgemm_tr_e5m2"}.get(ty, "hgemm_tr")
-    for key in ("hgemm_pipe", "hgemm_mfma"):
-        if key in kernel_name:
-            return key
+    if "hgemm_mfma" in kernel_name:
+        return "hgemm_mfma"
     if "neg_kernel" in kernel_name:
         return COPY
     return None
@@ -218,7 +217,7 @@ def counter_summaries(run_dir: str, digest=None):
           "# bytes_per_launch = fetch_kib*1024*fetch_scale + write_kib*1024*write_scale.  "
           "min_bytes = A + B + C once.",
           "# source = digest of the kernel's own file + gemm_internal.h + gemm.h, comments excluded "
-          "(bench.py kernel_digest);",
+          "(dense_gemm_row_amd.provenance.kernel_digest);",
           "# bench.py reports traffic only while that digest still matches."]
     q = [f"# MFMA utilisation and LDS bank conflicts (rocprofv3 --pmc), M=N=K={SIZE}, one MI355X.",
          f"# command (repo root): timeout -s KILL 120 rocprofv3 --pmc {SQ_PASS} --output-format csv "
@@ -326,9 +325,7 @@ def main(argv=None) -> int:
                                                   "profiles"))
     args = ap.parse_args(argv)
     R, O = args.run_dir, args.out
-    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-    sys.path.insert(0, root)
-    import bench  # the source digest that keys the traffic lines
+    from dense_gemm_row_amd.provenance import kernel_digest  # keys the traffic lines
 
     def write(name, lines):
         with open(os.path.join(O, name), "w") as f:
@@ -337,7 +334,7 @@ def main(argv=None) -> int:
     M = args.main_trace or R
     lines, tstats, bj = main_trace_summary(os.path.join(M, "kt"), os.path.join(M, "kt_bench.log"))
     write("kernel_trace_gemm4096.txt", lines)
-    traffic, sq, records = counter_summaries(R, bench.kernel_digest)
+    traffic, sq, records = counter_summaries(R, kernel_digest)
     write("hbm_traffic.txt", traffic)
     write("mfma_lds_counters_gemm4096.txt", sq)
     if os.path.isdir(os.path.join(R, "kts")):

@@ -45,7 +45,7 @@ EXPORTS = [f"gemm_{t}{form}" for form in ("", "_ex", "_bt", "_trans", "_epi", "_
            "gemm_splitk_workspace_bytes", "gemm_select_splitk_config",
            "gemm_num_configs", "gemm_get_config", "gemm_select_config", "gemm_tile_of_block",
            "gemm_layout_check", "gemm_load_tuning", "gemm_status_string",
-           "gemm_last_error", "gemm_version"]
+           "gemm_last_error", "gemm_last_hip_error", "gemm_version"]
 
 
 class GemmConfig(ctypes.Structure):
@@ -123,6 +123,8 @@ def _declare(lib):
     lib.gemm_status_string.restype = ctypes.c_char_p
     lib.gemm_last_error.argtypes = []
     lib.gemm_last_error.restype = ctypes.c_char_p
+    lib.gemm_last_hip_error.argtypes = []
+    lib.gemm_last_hip_error.restype = ctypes.c_char_p
     lib.gemm_version.argtypes = []
     lib.gemm_version.restype = ctypes.c_char_p
     return lib
@@ -293,6 +295,10 @@ def gemm_last_error() -> str:
     return lib().gemm_last_error().decode()
 
 
+def gemm_last_hip_error() -> str:
+    return lib().gemm_last_hip_error().decode()
+
+
 def gemm_version() -> str:
     return lib().gemm_version().decode()
 
@@ -363,8 +369,13 @@ def matmul(a, b, out=None, config: GemmConfig | None = None, stream=None, split_
         out = torch.empty((M, N), dtype=c_dtype, device=a.device)
     if out.shape != (M, N) or out.dtype != c_dtype:
         raise ValueError("out has the wrong shape or dtype")
+    # The launch stream: torch's current stream, a torch.cuda.Stream, or a
+    # raw hipStream_t handle.
     if stream is None:
         stream = torch.cuda.current_stream(a.device).cuda_stream
+    elif isinstance(stream, torch.cuda.Stream):
+        stream = stream.cuda_stream
+    stream = int(stream)
     args = (M, N, K, a.data_ptr(), _ld(a), b.data_ptr(), _ld(b), out.data_ptr(), _ld(out), stream)
     dtype = dtypes[a.dtype]
     if a_transposed:
@@ -399,7 +410,16 @@ def matmul(a, b, out=None, config: GemmConfig | None = None, stream=None, split_
         split_cfg = gemm_select_splitk_config(dtype, M, N, K)
     if split_cfg is not None and split_cfg.splits > 1:
         nbytes = gemm_splitk_workspace_bytes(dtype, M, N, K, split_cfg.splits)
-        ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=a.device)
+        if nbytes < 0:
+            raise GemmError(GEMM_ERR_INVALID_ARG, "gemm_splitk_workspace_bytes")
+        # The workspace is allocated on the launch stream, so that torch's
+        # caching allocator orders its reuse after the split-K kernels (a
+        # block taken from, or returned to, another stream's pool could be
+        # handed to work running concurrently with them).
+        cur = torch.cuda.current_stream(a.device)
+        on = cur if stream == cur.cuda_stream else torch.cuda.ExternalStream(stream, device=a.device)
+        with torch.cuda.stream(on):
+            ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=a.device)
         fn = entry(dtype, "_splitk")
         st = fn(*args[:9], ws.data_ptr(), ws.numel(), stream, split_cfg)
         if st != GEMM_OK:

@@ -202,8 +202,9 @@ gemm_status_t gemm_f8_ex(int64_t M, int64_t N, int64_t K,
 /*
  * Split-K GEMM: the same results contract as gemm_f32 / gemm_f16, for shapes
  * with too few output tiles to fill the GPU (e.g. M = N = 1024, K = 8192).
- * The K range is cut into S chunks of Kc = roundup(ceil(K / splits), 64)
- * (S = ceil(K / Kc) <= splits); one launch computes every chunk's FP32
+ * The K range is cut into S chunks of Kc = roundup(ceil(K / splits), a)
+ * with a = 64, or 128 for the 8-bit types (a multiple of every variant's
+ * K slice), and S = ceil(K / Kc) <= splits; one launch computes every chunk's FP32
  * partial product into `workspace` (S x M x N floats, row-major), and a
  * second launch sums the S partials of each element in chunk order and
  * writes C (FP32, or FP16 / BF16 rounded to nearest even once, after the
@@ -255,7 +256,8 @@ gemm_status_t gemm_f8_splitk(int64_t M, int64_t N, int64_t K,
  * (0 when it would not split; splits <= 0 means the library's choice for
  * the shape).  An unknown dtype, negative sizes or sizes that the GEMM
  * calls refuse (above 2^31-1, or C of more than 2^31-1 64 x 64 tiles)
- * give -1. */
+ * give -1, and so does a workspace size beyond 2^63-1 bytes (a split-K
+ * call then returns GEMM_ERR_INVALID_ARG). */
 int64_t gemm_splitk_workspace_bytes(int32_t dtype, int64_t M, int64_t N, int64_t K,
                                     int32_t splits);
 
@@ -509,6 +511,10 @@ gemm_status_t gemm_load_tuning(const char *path);
 
 const char *gemm_status_string(gemm_status_t status);
 const char *gemm_last_error(void); /* thread-local; "" when none */
+/* The same thread-local message under a second name: for GEMM_ERR_HIP it
+ * holds the HIP runtime's error text (hipGetErrorString of the launch
+ * error), for the other statuses the argument check that failed. */
+const char *gemm_last_hip_error(void);
 const char *gemm_version(void);
 
 #ifdef __cplusplus

@@ -65,6 +65,7 @@ def test_argument_validation(fn):
     for args, expect in bad:
         assert fn(*args, None) == expect, args
         assert gemm.gemm_last_error() != ""
+        assert gemm.gemm_last_hip_error() == gemm.gemm_last_error()  # the second name
 
 
 @pytest.mark.parametrize("fn", [gemm.gemm_f32, gemm.gemm_f16, gemm.gemm_bf16])
@@ -112,7 +113,8 @@ SHAPES = [(1, 1), (33, 17), (128, 128), (300, 520), (4096, 4096), (4000, 4000),
 @pytest.mark.parametrize("order", [gemm.ORDER_ROW, gemm.ORDER_GROUPED, gemm.ORDER_XCD])
 def test_tile_map_is_a_bijection(dt, order):
     for cfg in gemm.configs(dt):
-        for group_m in (1, 3, 4, 8):
+        # Bands taller than the grid (up to 2^31 - 1 rows) are the grid.
+        for group_m in (1, 3, 4, 8, 2 ** 30, 2 ** 31 - 1):
             cfg.order, cfg.group_m = order, group_m
             for M, N in SHAPES:
                 tm_n, tn_n = -(-M // cfg.bm), -(-N // cfg.bn)
@@ -227,7 +229,7 @@ def test_every_pipelined_variant_has_a_general_fallback(dt):
     cfgs = gemm.configs(dt)
     general = {(c.bm, c.bn) for c in cfgs if c.name.decode().startswith("mfma_")}
     for c in cfgs:
-        if c.name.decode().startswith(("pipe_", "tr_", "dl_")):
+        if c.name.decode().startswith(("tr_", "dl_")):
             assert (c.bm, c.bn) in general, c.name
 
 
@@ -306,7 +308,7 @@ def test_epilogue_argument_validation(fn):
     # Variants without a fused-epilogue form are refused when forced.
     for c in gemm.configs(dt):
         name = c.name.decode()
-        if name.startswith(("pipe_", "simt_")):
+        if name.startswith("simt_"):
             assert fn(*base, c, ok) == gemm.GEMM_ERR_UNSUPPORTED, name
     assert fn(0, 64, 64, PA, 64, PB, 64, 0, 64, None, None, ok) == gemm.GEMM_OK   # M == 0
 
@@ -325,7 +327,7 @@ def test_bt_argument_validation(fn):
     assert fn(64, 32, 128, PA, 128, PB, 128, PB + (31 * 128 + 100) * es, 32) == gemm.GEMM_ERR_ALIAS
     for c in gemm.configs(dt):
         name = c.name.decode()
-        if name.startswith(("pipe_", "simt_")):
+        if name.startswith("simt_"):
             assert fn(64, 32, 128, PA, 128, PB, 128, PC, 32, None, c) == gemm.GEMM_ERR_UNSUPPORTED, name
     assert fn(0, 32, 128, PA, 128, PB, 128, 0, 32) == gemm.GEMM_OK  # M == 0
 
@@ -335,7 +337,7 @@ def test_bf16_tables_mirror_f16():
     the same tiles and forms, one for one, under bf16 names; a BF16 config
     is refused by the FP16 entry points' id check only when out of range,
     and the selection picks a matrix-core variant."""
-    f16 = [c for c in gemm.configs(gemm.DTYPE_F16) if not c.name.decode().startswith("pipe_")]
+    f16 = gemm.configs(gemm.DTYPE_F16)
     bf16 = gemm.configs(gemm.DTYPE_BF16)
     assert [c.name.decode().replace("_f16_", "_bf16_") for c in f16] == [c.name.decode() for c in bf16]
     for a, b in zip(f16, bf16):
@@ -442,21 +444,21 @@ def test_environment_force_and_log():
     code = (
         "from dense_gemm_row_amd import gemm\n"
         "P = 0x10000000\n"
-        "assert gemm.gemm_f16(0, 64, 64, P, 64, P + (1 << 20), 64, 0, 64) == gemm.GEMM_OK\n"
         "assert gemm.gemm_f32(0, 64, 64, P, 64, P + (1 << 20), 64, 0, 64) == gemm.GEMM_OK\n"
+        "assert gemm.gemm_f16(0, 64, 64, P, 64, P + (1 << 20), 64, 0, 64) == gemm.GEMM_OK\n"
         "e = gemm.GemmEpilogue(1.0, 0.0, None, 0)\n"
-        "assert gemm.gemm_f16_epi(0, 64, 64, P, 64, P + (1 << 20), 64, 0, 64, None, None, e) == gemm.GEMM_OK\n"
-        "print(gemm.gemm_select_config(gemm.DTYPE_F16, 4096, 4096, 4096).name.decode())\n")
-    env = dict(os.environ, GEMM_FORCE_CONFIG="pipe_f16_128x128x64_w64x64", GEMM_LOG="1")
+        "assert gemm.gemm_f32_epi(0, 64, 64, P, 64, P + (1 << 20), 64, 0, 64, None, None, e) == gemm.GEMM_OK\n"
+        "print(gemm.gemm_select_config(gemm.DTYPE_F32, 4096, 4096, 4096).name.decode())\n")
+    env = dict(os.environ, GEMM_FORCE_CONFIG="simt_f32_128x128x16_t8x8", GEMM_LOG="1")
     res = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True,
                          cwd=ROOT, timeout=120)
     assert res.returncode == 0, res.stderr
     lines = [l for l in res.stderr.splitlines() if l.startswith("libgemm:")]
     assert len(lines) == 3, res.stderr
-    assert lines[0].startswith("libgemm: f16 0x64x64 -> pipe_f16_128x128x64_w64x64"), lines[0]
-    assert "-> dl_f32_" in lines[1] or "-> mfma_f32_" in lines[1], lines[1]   # another type: untouched
-    assert " epi -> " in lines[2] and "pipe_f16" not in lines[2], lines[2]    # no epilogue form
-    assert res.stdout.strip().startswith("tr_f16_")                          # the library's own choice
+    assert lines[0].startswith("libgemm: f32 0x64x64 -> simt_f32_128x128x16_t8x8"), lines[0]
+    assert "-> tr_f16_" in lines[1] or "-> mfma_f16_" in lines[1], lines[1]   # another type: untouched
+    assert " epi -> " in lines[2] and "simt_f32" not in lines[2], lines[2]    # no epilogue form
+    assert res.stdout.strip().startswith("dl_f32_")                          # the library's own choice
     res = subprocess.run([sys.executable, "-c", code], env=dict(os.environ, GEMM_LOG="0"),
                          capture_output=True, text=True, cwd=ROOT, timeout=120)
     assert res.returncode == 0 and "libgemm:" not in res.stderr

@@ -58,3 +58,24 @@ def test_checks_follow_the_stated_rules(dt, M, N, K, A, lda, B, ldb, C, ldc, at,
     got = fn(M, N, K, A, lda, B, ldb, C, ldc, None, None, int(at), int(bt))
     assert got == want, (got, want, gemm.gemm_last_error())
     assert (gemm.gemm_last_error() == "") == (got == OK)
+
+
+def test_workspace_size_overflow_is_refused():
+    """S x M x N x 4 beyond int64 (M = N = 2^21, K = 2^31 - 1, 2^20 chunks
+    of 2048) is refused, not wrapped to a small or zero size."""
+    for dt in sorted(IN_BYTES):
+        assert gemm.gemm_splitk_workspace_bytes(dt, 2 ** 21, 2 ** 21, LIM, 2 ** 20) == -1
+        assert gemm.gemm_splitk_workspace_bytes(dt, 2 ** 21, 2 ** 21, LIM, 2 ** 19) == -1  # 2^63
+        # 2^18 chunks of 8192 k: 2^18 * 2^42 * 4 = 2^62 bytes fits.
+        assert gemm.gemm_splitk_workspace_bytes(dt, 2 ** 21, 2 ** 21, LIM, 2 ** 18) == 2 ** 62
+
+
+def test_split_chunks_are_whole_slices_of_every_variant():
+    """Chunks are multiples of 64 k, or of 128 k for the 8-bit types (whose
+    LDS-direct slices are up to 128 k): K = 8192 with 12 requested splits
+    gives chunks of 704 (12 planes) for 32- and 16-bit types and of 768
+    (11 planes) for E4M3 and E5M2."""
+    M, N = 512, 256
+    for dt in sorted(IN_BYTES):
+        planes = 11 if dt in (gemm.DTYPE_F8, gemm.DTYPE_E5M2) else 12
+        assert gemm.gemm_splitk_workspace_bytes(dt, M, N, 8192, 12) == planes * M * N * 4, dt

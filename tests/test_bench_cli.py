@@ -6,7 +6,7 @@ import os
 import subprocess
 import sys
 
-import bench
+from dense_gemm_row_amd import provenance
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -24,12 +24,12 @@ def test_code_digest_ignores_comments_only():
     a = "int f(int x) {\n  // twice\n  return 2 * x; /* doubled */\n}\n"
     b = "int f(int x) {\n  /* a different\n     comment */ return 2 * x;\n}\n"
     c = "int f(int x) {\n  return 3 * x;\n}\n"
-    assert bench.code_only(a) == bench.code_only(b)
-    assert bench.code_only(a) != bench.code_only(c)
+    assert provenance.code_only(a) == provenance.code_only(b)
+    assert provenance.code_only(a) != provenance.code_only(c)
 
 
 def test_traffic_lookup_is_keyed_by_size_and_digest(monkeypatch):
     v = "tr_f16_256x256x64_w128x128_s2"
-    assert bench.load_traffic(v, 1234) is None           # no entry at that size
-    monkeypatch.setattr(bench, "kernel_digest", lambda variant: "0000000000000000")
-    assert bench.load_traffic(v, 4096) is None           # code changed since the counters
+    assert provenance.load_traffic(v, 1234) is None           # no entry at that size
+    monkeypatch.setattr(provenance, "kernel_digest", lambda variant: "0000000000000000")
+    assert provenance.load_traffic(v, 4096) is None           # code changed since the counters

@@ -270,6 +270,29 @@ def test_f8_splitk_exact_small_int(fmt, shape):
             assert exact_equal(A, B, C), (cfg.name, splits)
 
 
+def test_e5m2_splitk_inf_near_a_chunk_boundary():
+    """An E5M2 infinity in B's row 450 with K = 2048 and 5 requested
+    splits: chunks are whole 128-k slices (512, 4 chunks), so no slice of
+    one chunk reads B rows of the next against A's zero padding, where
+    0 * Inf would turn the column's +Inf into NaN.  Every variant, split and
+    unsplit, gives +Inf in that column and the exact sums elsewhere."""
+    fmt = FORMATS["e5m2"]
+    M, N, K = 256, 272, 2048
+    A, B = _ints(fmt, M, N, K, seed=23)
+    a8, b8 = A.view(np.uint8), B.view(np.uint8)
+    a8[:, 450] = 0x3C  # 1.0: every row meets the infinity with a positive weight
+    b8[450, 37] = 0x7C  # +Inf
+    ref, _ = oracle.gemm_rows(A, B)
+    assert np.all(np.isposinf(ref[:, 37])) and np.isfinite(np.delete(ref, 37, axis=1)).all()
+    want = rounded(ref, "e5m2")
+    for cfg in gemm.configs(fmt.dt):
+        for splits in (1, 5):
+            cfg.splits = splits
+            log(f"e5m2 split-K Inf cfg={cfg.name.decode()} splits={splits}")
+            C, _ = run(A, B, split=cfg)
+            assert np.array_equal(wide(C), want), (cfg.name, splits)
+
+
 def test_f8_splitk_auto_full_size(fmt):
     M, N, K = 1024, 1024, 8192
     sel = gemm.gemm_select_splitk_config(fmt.dt, M, N, K)

@@ -286,6 +286,37 @@ def test_matmul_uses_split_k():
     assert rep["ok"], rep
 
 
+@pytest.mark.parametrize("as_handle", [False, True], ids=["stream", "handle"])
+def test_matmul_split_k_on_a_side_stream(as_handle):
+    """matmul's split-K workspace belongs to the launch stream: a call on a
+    side stream (a torch Stream or its raw handle), followed at once by
+    allocations of the workspace's size filled with NaN on the current
+    stream, gives the same bits as the call on the current stream.  (A
+    workspace taken from the current stream's pool and dropped on return
+    would be handed to those fills while the split-K kernels still use
+    it.)"""
+    import torch
+    M = N = 1024
+    K = 8192
+    A, B = synth.workload(M, N, K, "f16", seed=19)
+    a, b = torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda()
+    ref = gemm.matmul(a, b)
+    torch.cuda.synchronize()
+    nbytes = gemm.gemm_splitk_workspace_bytes(gemm.DTYPE_F16, M, N, K, 0)
+    assert nbytes > 0
+    side = torch.cuda.Stream()
+    log(f"matmul f16 {M}x{N}x{K} split-K on a side stream ({'handle' if as_handle else 'Stream'})")
+    for _ in range(3):
+        c = torch.empty_like(ref)
+        side.wait_stream(torch.cuda.current_stream())
+        gemm.matmul(a, b, out=c, stream=side.cuda_stream if as_handle else side)
+        junk = [torch.full((nbytes // 2,), float("nan"), dtype=torch.float16, device="cuda")
+                for _ in range(4)]
+        torch.cuda.synchronize()
+        del junk
+        assert torch.equal(c.view(torch.int16), ref.view(torch.int16))
+
+
 # --------------------------------------------------------------------------
 # Fused epilogue (gemm_*_epi): act(alpha * AB + beta * C + bias).
 # --------------------------------------------------------------------------
