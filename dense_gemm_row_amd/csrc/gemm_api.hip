@@ -728,6 +728,75 @@ gemm_status_t run_splitk(int dtype, int64_t M, int64_t N, int64_t K, const void*
   return GEMM_OK;
 }
 
+// ---------------------------------------------------------------------------
+// Split-K without a caller workspace: the partial planes live in a static
+// device array.  Each GPU the library runs on holds its own copy of it
+// (kScratchBytes) until the process ends; its device address is looked up
+// once per device, with that device current, and kept.  Host code never
+// passes the array's own name to a kernel or a copy (on the host that name
+// is a stand-in, not a device address).
+constexpr int64_t kScratchBytes = GEMM_SPLITK_STATIC_MAX_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The scratch array's address on the device that runs `stream`.
+gemm_status_t scratch_for(void* stream, void** out) {
+  int dev = -1;
+  const hipError_t e0 = stream ? hipStreamGetDevice(static_cast<hipStream_t>(stream), &dev)
+                               : hipGetDevice(&dev);
+  if (e0 != hipSuccess) return fail(GEMM_ERR_HIP, "no device for the stream: %s", hipGetErrorString(e0));
+  if (dev < 0 || dev >= kMaxDevices) return fail(GEMM_ERR_UNSUPPORTED, "device %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    int cur = -1;
+    hipError_t e = hipGetDevice(&cur);
+    if (e == hipSuccess && cur != dev) e = hipSetDevice(dev);
+    void* p = nullptr;
+    if (e == hipSuccess) e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur >= 0 && cur != dev) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess || !p)
+      return fail(GEMM_ERR_HIP, "scratch address on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return GEMM_OK;
+}
+
+gemm_status_t run_splitk_static(int dtype, int64_t M, int64_t N, int64_t K, const void* A,
+                                int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc,
+                                void* stream, const gemm_config_t* forced) {
+  g_err[0] = 0;
+  if (!valid_dtype(dtype)) return fail(GEMM_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  gemm_status_t st = validate(dtype, M, N, K, A, lda, B, ldb, C, ldc);
+  if (st != GEMM_OK) return st;
+  gemm_config_t cfg;
+  st = resolve(dtype, M, N, K, forced, true, cfg);
+  if (st != GEMM_OK) return st;
+  if (M == 0 || N == 0) return GEMM_OK;
+  int64_t S, Kc;
+  split_shape(dtype, K, cfg.splits, S, Kc);
+  const bool vec = vector_path(dtype, A, lda, B, ldb, C, ldc, K, N);
+  // The same cases as the workspace form run unsplit and touch no scratch.
+  if (S <= 1 || K == 0 || !vec || !table().v[dtype][cfg.id].launch_partial)
+    return launch_plain(dtype, cfg, M, N, K, A, lda, B, ldb, C, ldc, stream);
+  const int64_t need = partial_bytes(S, M, N);
+  if (need < 0 || need > kScratchBytes)
+    return fail(GEMM_ERR_INVALID_ARG,
+                "split-K needs %lld bytes of partials (%lld chunks of %lld x %lld FP32); the static "
+                "scratch holds %lld: use the workspace form or fewer splits",
+                (long long)need, (long long)S, (long long)M, (long long)N, (long long)kScratchBytes);
+  void* ws = nullptr;
+  st = scratch_for(stream, &ws);
+  if (st != GEMM_OK) return st;
+  return run_splitk(dtype, M, N, K, A, lda, B, ldb, C, ldc, ws, kScratchBytes, stream, forced);
+}
+
 }  // namespace
 }  // namespace gemm
 
@@ -1032,6 +1101,12 @@ const char* gemm_status_string(gemm_status_t s) {
 
 const char* gemm_last_error(void) { return g_err; }
 const char* gemm_last_hip_error(void) { return g_err; }
+
+gemm_status_t gemm_splitk_static(int32_t dtype, int64_t M, int64_t N, int64_t K, const void* A,
+                                 int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc,
+                                 void* stream, const gemm_config_t* cfg) {
+  return run_splitk_static(dtype, M, N, K, A, lda, B, ldb, C, ldc, stream, cfg);
+}
 
 const char* gemm_version(void) { return "libgemm 0.1.0 (gfx950)"; }
 

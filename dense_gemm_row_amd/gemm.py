@@ -42,7 +42,7 @@ ACT_RELU = 1
 TYPES = ("f32", "f16", "bf16", "f8", "e5m2")
 EXPORTS = [f"gemm_{t}{form}" for form in ("", "_ex", "_bt", "_trans", "_epi", "_epi_q8", "_splitk")
            for t in TYPES] + [
-           "gemm_splitk_workspace_bytes", "gemm_select_splitk_config",
+           "gemm_splitk_workspace_bytes", "gemm_select_splitk_config", "gemm_splitk_static",
            "gemm_num_configs", "gemm_get_config", "gemm_select_config", "gemm_tile_of_block",
            "gemm_layout_check", "gemm_load_tuning", "gemm_status_string",
            "gemm_last_error", "gemm_last_hip_error", "gemm_version"]
@@ -103,6 +103,8 @@ def _declare(lib):
     for name in (f"gemm_{t}_splitk" for t in types):
         getattr(lib, name).argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, p, i64, p, cfgp]
         getattr(lib, name).restype = ctypes.c_int
+    lib.gemm_splitk_static.argtypes = [i32, i64, i64, i64, p, i64, p, i64, p, i64, p, cfgp]
+    lib.gemm_splitk_static.restype = ctypes.c_int
     lib.gemm_splitk_workspace_bytes.argtypes = [i32, i64, i64, i64, i32]
     lib.gemm_splitk_workspace_bytes.restype = i64
     lib.gemm_select_splitk_config.argtypes = [i32, i64, i64, i64, cfgp]
@@ -233,6 +235,17 @@ def entry(dtype: int, form: str = ""):
     name = {DTYPE_F32: "f32", DTYPE_F16: "f16", DTYPE_BF16: "bf16", DTYPE_F8: "f8",
             DTYPE_E5M2: "e5m2"}[dtype]
     return globals()[f"gemm_{name}{form}"]
+
+
+# The static scratch of gemm_splitk_static (GEMM_SPLITK_STATIC_MAX_BYTES).
+SPLITK_STATIC_MAX_BYTES = 64 << 20
+
+
+def gemm_splitk_static(dtype: int, M, N, K, A, lda, B, ldb, C, ldc, stream=None,
+                       cfg: GemmConfig | None = None) -> int:
+    """gemm_splitk_static: split-K with the partials in the library's static
+    device scratch (no workspace, no allocation)."""
+    return lib().gemm_splitk_static(dtype, M, N, K, A, lda, B, ldb, C, ldc, stream, _ref(cfg))
 
 
 def gemm_splitk_workspace_bytes(dtype: int, M: int, N: int, K: int, splits: int = 0) -> int:

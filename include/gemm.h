@@ -252,6 +252,32 @@ gemm_status_t gemm_f8_splitk(int64_t M, int64_t N, int64_t K,
                              void *workspace, int64_t workspace_bytes,
                              void *stream, const gemm_config_t *cfg);
 
+/*
+ * Split-K that allocates nothing and takes no workspace: for callers that
+ * cannot allocate device memory (code under HIP graph capture, serving
+ * loops and harnesses that forbid hipMalloc).  The same computation and
+ * results as gemm_<dtype>_splitk with the same cfg (bit for bit: same
+ * variant, chunks and reduction order), for dtype GEMM_DTYPE_F32 / F16 /
+ * BF16 / F8 / E5M2 with A, B and C of that dtype's gemm_<dtype>_splitk
+ * types (device pointers; FP8 products are BF16).  The FP32 partial planes
+ * live in a static device array of GEMM_SPLITK_STATIC_MAX_BYTES that each
+ * GPU the library runs on holds until the process ends; the call itself
+ * calls no allocator.
+ * Errors: as gemm_<dtype>_splitk; an unknown dtype, or a split whose
+ * partials (S x M x N x 4 bytes) exceed GEMM_SPLITK_STATIC_MAX_BYTES
+ * -> GEMM_ERR_INVALID_ARG before any launch (pass cfg with fewer splits,
+ * or use the workspace form).  Calls that run unsplit touch no scratch.
+ * Every call on one GPU shares that GPU's array and leaves its last
+ * partials there: calls that overlap in time on one GPU (two streams,
+ * two threads) race and must be serialised by the caller.
+ */
+#define GEMM_SPLITK_STATIC_MAX_BYTES (64ll << 20)
+gemm_status_t gemm_splitk_static(int32_t dtype, int64_t M, int64_t N, int64_t K,
+                                 const void *A, int64_t lda,
+                                 const void *B, int64_t ldb,
+                                 void *C, int64_t ldc,
+                                 void *stream, const gemm_config_t *cfg);
+
 /* Workspace bytes a split-K call with `splits` requested chunks needs
  * (0 when it would not split; splits <= 0 means the library's choice for
  * the shape).  An unknown dtype, negative sizes or sizes that the GEMM
