@@ -50,7 +50,9 @@ def parse_args():
     ap.add_argument("--group-m", type=int, default=None, help="force the band height")
     ap.add_argument("--cpu-budget", type=float, default=20.0,
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
-    ap.add_argument("--cpu-threads", type=int, default=16)
+    ap.add_argument("--cpu-threads", type=int, default=0,
+                    help="oracle threads (0 = the host cores this process may use: its CPU "
+                         "affinity, capped by OMP_NUM_THREADS when set)")
     ap.add_argument("--no-check", action="store_true", help="skip the oracle check")
     ap.add_argument("--epilogue", action="store_true",
                     help="time the fused-epilogue entry points instead: C = relu(A x B + C + bias) "
@@ -61,10 +63,146 @@ def parse_args():
     ap.add_argument("--at", action="store_true",
                     help="A held as its K x M transpose (column-major A), through gemm_*_trans; "
                          "with --bt both are transposed")
+    ap.add_argument("--no-probes", action="store_true",
+                    help="skip the clock and matrix-core ceiling probes and the SIMT ablation")
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the step: one JSON line per configuration of the measurement "
+                         "plan (256^3, 2048^3, 4096^3, 8192x8192x1024, 1024x1024x8192, "
+                         "4096x11008x4096, 4000^3) for each of --dtypes, each checked in full "
+                         "against the oracle before it is timed")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="before the steps, run a plain device copy of this many MiB (read N, "
                          "write N) three times: the reference kernel that scales HBM counters")
     return ap.parse_args()
+
+
+# The measurement plan's configurations (the pages' 2048^3 and 4096^3, the
+# correctness size 256^3, and the non-square sweep); the step uses 4096^3.
+SWEEP_SHAPES = [(256, 256, 256), (2048, 2048, 2048), (4096, 4096, 4096), (8192, 8192, 1024),
+                (1024, 1024, 8192), (4096, 11008, 4096), (4000, 4000, 4000)]
+SWEEP_ONE_THREAD = {(256, 256, 256), (2048, 2048, 2048)}
+
+
+def sweep(args):
+    """One JSON line per (configuration, dtype): the library's own choice
+    (split-K where it picks it, with a preallocated workspace), checked on
+    every element against the oracle before timing, then 5 warm-up and 50
+    timed launches (20 at 4096x11008x4096), each between its own HIP events;
+    median, mean and min, TFLOP/s from the median, the oracle's time on
+    `cpu_threads` threads (and on one for 256^3 and 2048^3), and the clock
+    over the K loop of one traced launch in a block of the kernel."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from dense_gemm_row_amd import gemm, synth
+
+    dev = torch.device("cuda:0")
+    kinds = [k for k in args.dtypes.split(",") if k]
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16, "f8": torch.bfloat16}
+    dcode = {"f32": gemm.DTYPE_F32, "f16": gemm.DTYPE_F16, "bf16": gemm.DTYPE_BF16, "f8": gemm.DTYPE_F8}
+
+    def to_dev(x):
+        if x.dtype == synth.BF16:
+            return torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+        if x.dtype == synth.F8:
+            return torch.from_numpy(x.view(np.uint8)).to(dev).view(torch.float8_e4m3fn)
+        return torch.from_numpy(x).to(dev)
+
+    def from_dev(t):
+        if t.dtype == torch.bfloat16:
+            return t.view(torch.int16).cpu().numpy().view(np.uint16).view(synth.BF16)
+        return t.cpu().numpy()
+
+    stream = torch.cuda.current_stream(dev)
+    sptr = stream.cuda_stream
+    T = args.cpu_threads
+    for (M, N, K) in SWEEP_SHAPES:
+        for k in kinds:
+            dt = dcode[k]
+            A, B = synth.workload(M, N, K, k, seed=0)
+            a, b = to_dev(A), to_dev(B)
+            c = torch.empty((M, N), dtype=tdt[k], device=dev)
+            sel = gemm.gemm_select_splitk_config(dt, M, N, K)
+            ws = None
+            if sel.splits > 1:
+                nbytes = gemm.gemm_splitk_workspace_bytes(dt, M, N, K, sel.splits)
+                ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+
+            def call():
+                args9 = (M, N, K, a.data_ptr(), K, b.data_ptr(), N, c.data_ptr(), N)
+                if ws is not None:
+                    st = gemm.entry(dt, "_splitk")(*args9, ws.data_ptr(), ws.numel(), sptr, sel)
+                else:
+                    st = gemm.entry(dt, "_ex")(*args9, sptr, sel)
+                if st != gemm.GEMM_OK:
+                    raise gemm.GemmError(st, f"gemm_{k}")
+
+            call()
+            torch.cuda.synchronize()
+            C = from_dev(c)
+            t0 = time.perf_counter()
+            ref, den = oracle.gemm_rows(A, B, threads=T)
+            oracle_s = time.perf_counter() - t0
+            rep = oracle.check(C, ref, den, oracle.TOL[k])
+            del ref, den
+            one = None
+            if (M, N, K) in SWEEP_ONE_THREAD:
+                t0 = time.perf_counter()
+                oracle.gemm_rows(A, B, threads=1)
+                one = time.perf_counter() - t0
+            line = {"dtype": k, "M": M, "N": N, "K": K, "config": sel.name.decode(),
+                    "splits": int(sel.splits), "max_rel_err": rep["max_rel"],
+                    "max_abs_err": rep["max_abs"], "tol": oracle.TOL[k], "ok": rep["ok"],
+                    "oracle_s": round(oracle_s, 3), "oracle_threads": T,
+                    "oracle_gflops": round(2.0 * M * N * K / oracle_s / 1e9, 3)}
+            if one is not None:
+                line["oracle_s_1thread"] = round(one, 3)
+            if not rep["ok"]:
+                print(json.dumps(dict(line, error="parity check failed")), flush=True)
+                sys.exit(1)
+            reps = 20 if N == 11008 else 50
+            # Warm-up: at least 5 launches and 0.2 s, so that the clocks have
+            # left the idle state of the oracle's run before the timing.
+            t0 = time.perf_counter()
+            j = 0
+            while j < 5 or time.perf_counter() - t0 < 0.2:
+                call()
+                j += 1
+                if j % 20 == 0:
+                    torch.cuda.synchronize()
+            evs = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+            evs[0].record(stream)
+            for j in range(reps):
+                call()
+                evs[j + 1].record(stream)
+            torch.cuda.synchronize()
+            ts = sorted(evs[j].elapsed_time(evs[j + 1]) for j in range(reps))
+            med, mean = ts[reps // 2], sum(ts) / reps
+            # The kernel's clock over its K loop, from one traced launch in a
+            # block of 20 (None for variants that record no trace).
+            wgs = -(-M // sel.bm) * -(-N // sel.bn) * max(1, int(sel.splits))
+            stamps = torch.zeros(8 * wgs, dtype=torch.int64, device=dev)
+            for j in range(20):
+                if j == 10:
+                    gemm.gemm_trace_set(stamps.data_ptr(), wgs)
+                call()
+                if j == 10:
+                    gemm.gemm_trace_set(None, 0)
+            torch.cuda.synchronize()
+            st = stamps.cpu().numpy()
+            clk = None
+            if (st != 0).all():
+                clk = round(float(gemm.trace_summary(st)["loop_clock_mhz"].mean()), 1)
+            flops = 2.0 * M * N * K
+            line.update({"t_median_ms": round(med, 5), "t_mean_ms": round(mean, 5), "t_min_ms": round(ts[0], 5),
+                         "tflops": round(flops / (med * 1e-3) / 1e12, 2),
+                         "pct_peak": round(100.0 * flops / (med * 1e-3) / 1e12 / PEAK_TFLOPS[k], 2),
+                         "peak_tflops": PEAK_TFLOPS[k], "reps": reps,
+                         "gpu_clock_mhz": clk})
+            print(json.dumps(line), flush=True)
+            del a, b, c, ws
+            torch.cuda.empty_cache()
 
 
 def main():
@@ -87,6 +225,11 @@ def main():
     gemm.lib()  # fails loudly if libgemm.so is missing
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.cpu_threads <= 0:
+        import oracle
+        args.cpu_threads = oracle.default_threads()
+    if args.sweep:
+        return sweep(args)
     n = args.size
     kinds = [k for k in args.dtypes.split(",") if k]
     if not kinds or any(k not in PEAK_TFLOPS for k in kinds):
@@ -203,7 +346,7 @@ def main():
             rows = sorted(set([0, n - 1] + rng.integers(0, n, 6).tolist()))
             if epi is not None:
                 ref, den = oracle.gemm_rows_epi(A, B, C0[k], 1.0, 1.0, bias_host, oracle.ACT_RELU,
-                                                rows=rows, threads=min(args.cpu_threads, 16))
+                                                rows=rows, threads=args.cpu_threads)
                 rep = oracle.check(np.ascontiguousarray(C[rows]), ref, den, oracle.TOL[k])
                 parity[k] = {"rows": len(rows), "entries": 0, "tol": rep["tol"],
                              "max_rel": rep["max_rel"], "ok": rep["ok"]}
@@ -223,7 +366,7 @@ def main():
                 parity[k] = {"rows": len(rows), "entries": 0, "tol": tol,
                              "max_rel": rep["max_rel"], "ok": rep["ok"]}
                 continue
-            ref, den = oracle.gemm_rows(A, B, rows=rows, threads=min(args.cpu_threads, 16))
+            ref, den = oracle.gemm_rows(A, B, rows=rows, threads=args.cpu_threads)
             rep = oracle.check(np.ascontiguousarray(C[rows]), ref, den, tol)
             ii, jj = rng.integers(0, n, 512), rng.integers(0, n, 512)
             ce, de = oracle.gemm_entries(A, B, ii, jj)
@@ -269,6 +412,50 @@ def main():
         torch.cuda.synchronize()
         per_launch[k] = sorted(evs[j].elapsed_time(evs[j + 1]) for j in range(n_pl))
 
+    # Probes (after the timed region; none of this enters `value`):
+    # * the kernel's own clock and timeline: one traced launch
+    #   (gemm_trace_set) in the middle of a block of 20 back-to-back
+    #   launches, so it runs under the same sustained load; its workgroups'
+    #   cycle and constant-clock stamps give the clock over the K loop, the
+    #   pipeline fill, the epilogue and the spread of the loop ends;
+    # * the matrix-core ceiling of the kernel's instruction with its
+    #   operands in registers, and the clock that ceiling ran at.
+    probes = {}
+    if not args.no_probes:
+        from dense_gemm_row_amd import probe
+        ceiling_steps = {"f32": 20000, "f16": 40000, "bf16": 40000, "f8": 20000}
+        for k in kinds:
+            wgs = -(-n // cfgs[k].bm) * -(-n // cfgs[k].bn)
+            stamps = torch.zeros(8 * wgs, dtype=torch.int64, device=dev)
+            for j in range(20):
+                if j == 10:
+                    gemm.gemm_trace_set(stamps.data_ptr(), wgs)
+                launch(k)
+                if j == 10:
+                    gemm.gemm_trace_set(None, 0)
+            torch.cuda.synchronize()
+            st = stamps.cpu().numpy()
+            rec = {}
+            if (st != 0).all():  # the variant records a trace
+                tr = gemm.trace_summary(st)
+                rec = {"clock_mhz": round(float(tr["loop_clock_mhz"].mean()), 1),
+                       "loop_kcycles": [round(float(tr["loop_kcycles"].min()), 1),
+                                        round(float(tr["loop_kcycles"].mean()), 1),
+                                        round(float(tr["loop_kcycles"].max()), 1)],
+                       "clock_mhz_min": round(float(tr["loop_clock_mhz"].min()), 1),
+                       "clock_mhz_max": round(float(tr["loop_clock_mhz"].max()), 1),
+                       "trace_us": {"fill": round(float(tr["fill_us"].mean()), 2),
+                                    "loop": round(float(tr["loop_us"].mean()), 2),
+                                    "loop_min": round(float(tr["loop_us"].min()), 2),
+                                    "loop_max": round(float(tr["loop_us"].max()), 2),
+                                    "epilogue": round(float(tr["epilogue_us"].mean()), 2),
+                                    "loop_end_spread": round(tr["loop_end_spread_us"], 2),
+                                    "span": round(tr["span_us"], 2)}}
+            ceil = probe.mfma_ceiling(dcode[k], ceiling_steps[k], repeats=2)
+            rec.update({"mfma_ceiling_tflops": round(ceil["tflops"], 2),
+                        "mfma_ceiling_clock_mhz": round(ceil["clock_mhz"], 1)})
+            probes[k] = rec
+
     kernels = {}
     for i, k in enumerate(kinds):
         mean = marks[i].elapsed_time(marks[i + 1]) / args.steps
@@ -284,6 +471,33 @@ def main():
             "peak_tflops": PEAK_TFLOPS[k],
             "min_bytes_per_launch": n * n * (2 * in_elem + elem),
         }
+        if k in probes:
+            kernels[k].update(probes[k])
+            kernels[k]["frac_of_ceiling"] = round(kernels[k]["tflops"] / probes[k]["mfma_ceiling_tflops"], 4)
+
+    # The SIMT ablation (the pages' vector-ALU kernel, re-derived for 64-lane
+    # waves) on the same FP32 operands, timed as a block of back-to-back
+    # launches like the step's kernels.
+    ablation = None
+    if "f32" in kinds and not args.no_probes and epi is None and not args.bt and not args.at:
+        simt = gemm.config_by_name(gemm.DTYPE_F32, "simt_f32_128x128x16_t8x8")
+        a, b, c = devbuf["f32"]
+        sargs = (n, n, n, a.data_ptr(), n, b.data_ptr(), n, c.data_ptr(), n, sptr, simt)
+        reps = 10
+        if gemm.gemm_f32_ex(*sargs) != gemm.GEMM_OK:
+            raise gemm.GemmError(gemm.GEMM_ERR_HIP, "SIMT ablation")
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            gemm.gemm_f32_ex(*sargs)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        tf = flops / (ms * 1e-3) / 1e12
+        ablation = {"variant": simt.name.decode(), "ms_mean": round(ms, 4), "tflops": round(tf, 2),
+                    "pct_fp32_matrix_peak": round(100 * tf / PEAK_TFLOPS["f32"], 2),
+                    "pct_fp32_vector_peak": round(100 * tf / 78.6, 2),
+                    "mfma_kernel_speedup": round(ms / kernels["f32"]["ms_mean"], 2)}
 
     dom = max(kinds, key=lambda k: kernels[k]["ms_mean"])
 
@@ -302,7 +516,7 @@ def main():
     cpu = None
     if args.cpu_budget > 0:
         import oracle
-        threads = max(1, min(args.cpu_threads, len(os.sched_getaffinity(0))))
+        threads = args.cpu_threads
         spent, done_flops, parts = 0.0, 0.0, []
         for k in kinds:
             A, B = host[k]
@@ -320,6 +534,8 @@ def main():
             done_flops += 2.0 * rows * n * n
             parts.append(f"{rows} rows of the {n}^3 {STEP_NAME[k].split(' ')[0]} {k}")
         cpu = {"value": round(done_flops / spent / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+               "affinity_cores": len(os.sched_getaffinity(0)),
+               "omp_num_threads": os.environ.get("OMP_NUM_THREADS"),
                "kind": "oracle", "seconds": round(spent, 2),
                "sample": " + ".join(parts) + " (FP64 i-k-j oracle, all columns of each row)"}
 
@@ -348,6 +564,8 @@ def main():
         "roofline": roofline(dom),
         "roofline_all": {k: roofline(k) for k in kinds},
         "cpu_baseline": cpu,
+        "gpu_clock_mhz": {k: probes[k].get("clock_mhz") for k in probes} or None,
+        "ablation": {"simt_f32": ablation} if ablation else None,
         "parity": parity,
         "input_gen_s": round(gen_s, 2),
     }

@@ -18,6 +18,9 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libgemm.so")
+# The measurement probes (include/gemm_probe.h) live in a library of their own.
+PROBE_SOURCES = ["probe.hip"]
+PROBE_LIB = os.path.join(HERE, "libgemm_probe.so")
 ARCH = "gfx950"
 
 SOURCES = ["gemm_api.hip", "splitk.hip", "sgemm_dl.hip", "sgemm_mfma.hip", "hgemm_mfma.hip", "hgemm_tr.hip", "sgemm_simt.hip"]
@@ -47,13 +50,8 @@ def _compile(src: str, extra) -> str:
     return obj
 
 
-def build(extra_flags=(), jobs: int | None = None, verbose: bool = False) -> str:
-    """Compile every source and link libgemm.so.  Always rebuilds."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    jobs = jobs or min(len(SOURCES), os.cpu_count() or 1)
-    with cf.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, list(extra_flags)), SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, out: str) -> None:
+    tmp = out + ".tmp"
     # --no-undefined: a kernel whose host-side launch stub went missing must
     # fail the build, not the first dlopen.
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,--no-undefined", *objs,
@@ -61,9 +59,21 @@ def build(extra_flags=(), jobs: int | None = None, verbose: bool = False) -> str
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stdout}\n{res.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(extra_flags=(), jobs: int | None = None, verbose: bool = False) -> str:
+    """Compile every source and link libgemm.so and libgemm_probe.so.
+    Always rebuilds."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    jobs = jobs or min(len(srcs), os.cpu_count() or 1)
+    with cf.ThreadPoolExecutor(jobs) as ex:
+        objs = list(ex.map(lambda s: _compile(s, list(extra_flags)), srcs))
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], PROBE_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PROBE_LIB}")
     return LIB
 
 

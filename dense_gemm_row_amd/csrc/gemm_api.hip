@@ -511,9 +511,15 @@ gemm_status_t f8_unsupported() {
               "ldc a multiple of 8, and byte offsets below 2^31");
 }
 
+// gemm_trace_set's buffer and capacity, per host thread.
+thread_local unsigned long long* g_trace = nullptr;
+thread_local int g_trace_cap = 0;
+
 Params make_params(int dtype, const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
                    int64_t ldc, int64_t M, int64_t N, int64_t K) {
   Params p;
+  p.trace = g_trace;
+  p.trace_cap = g_trace_cap;
   p.bf16 = dtype == GEMM_DTYPE_BF16;
   p.f8 = dtype == GEMM_DTYPE_F8 ? 1 : dtype == GEMM_DTYPE_E5M2 ? 2 : 0;
   p.A = A;
@@ -1101,6 +1107,15 @@ const char* gemm_status_string(gemm_status_t s) {
 
 const char* gemm_last_error(void) { return g_err; }
 const char* gemm_last_hip_error(void) { return g_err; }
+
+gemm_status_t gemm_trace_set(uint64_t* stamps, int64_t workgroups) {
+  g_err[0] = 0;
+  if (workgroups < 0 || workgroups > 0x7fffffff || (stamps && workgroups == 0))
+    return fail(GEMM_ERR_INVALID_ARG, "trace capacity %lld", (long long)workgroups);
+  g_trace = stamps ? reinterpret_cast<unsigned long long*>(stamps) : nullptr;
+  g_trace_cap = stamps ? (int)workgroups : 0;
+  return GEMM_OK;
+}
 
 gemm_status_t gemm_splitk_static(int32_t dtype, int64_t M, int64_t N, int64_t K, const void* A,
                                  int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc,

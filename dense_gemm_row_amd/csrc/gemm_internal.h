@@ -77,7 +77,31 @@ struct Params {
   // bfloat16 (exactly) while staging, so FP8 operands off the vector layout
   // run there on the bf16 matrix instruction.
   int f8 = 0;
+  // Per-workgroup timestamps (gemm_trace_set): when non-null, the kernels
+  // that record them write, for workgroup w = blockIdx.y * gridDim.x +
+  // blockIdx.x below trace_cap, the shader-cycle counter and the 100 MHz
+  // constant clock at four points (entry, first K slice landed, K loop
+  // done, C issued) into trace[8w + 2 * point] and trace[8w + 2 * point + 1].
+  unsigned long long* trace = nullptr;
+  int trace_cap = 0;
 };
+
+// One timestamp of gemm_trace_set's record (see Params::trace): a uniform
+// branch when tracing is off; when on, lane 0 of the workgroup's first wave
+// stores the two counters with ordinary vector stores.
+__device__ __forceinline__ void trace_stamp(const Params& p, int point) {
+  if (p.trace) {
+    const unsigned w = blockIdx.y * gridDim.x + blockIdx.x;
+    if (w < (unsigned)p.trace_cap) {
+      const unsigned long long t = __builtin_amdgcn_s_memtime();
+      const unsigned long long r = __builtin_amdgcn_s_memrealtime();
+      if (threadIdx.x == 0) {
+        p.trace[8 * w + 2 * point] = t;
+        p.trace[8 * w + 2 * point + 1] = r;
+      }
+    }
+  }
+}
 
 // ---------------------------------------------------------------------------
 // FP8 byte -> bfloat16 bit pattern, exact (every E4M3 and E5M2 value is a

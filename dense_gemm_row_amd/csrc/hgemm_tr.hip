@@ -364,6 +364,7 @@ hgemm_tr_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
     else return B_of(IC<(i - NS) % NS>{});
   };
 
+  trace_stamp(p, 0);
   int tm, tn;
   tile_of_block(blockIdx.x, map, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
@@ -641,6 +642,7 @@ hgemm_tr_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
                  std::make_integer_sequence<int, NS>{});
       loop_barrier<(NS - 1) * S::LPS>();  // slice 0 landed
     }
+    trace_stamp(p, 1);
     load_frags(0, la0, lb0, 0);
     int t = 0;
     for (; t + NS <= T; t += NS)
@@ -651,6 +653,7 @@ hgemm_tr_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
     // must land before the epilogue reuses the LDS.
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   }
+  trace_stamp(p, 2);
   if constexpr (S::PARTIAL) {
     // Split-K partial: FP32 C (the workspace) written straight from the
     // accumulators, no FP16 rounding, no LDS round trip.
@@ -671,6 +674,7 @@ hgemm_tr_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
             *reinterpret_cast<f32x4*>(Cf + (int64_t)row * p.ldc + col) = v;
           }
         }
+    trace_stamp(p, 3);
     return;
   }
   __syncthreads();
@@ -768,6 +772,7 @@ hgemm_tr_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
         }
       }
     }
+    trace_stamp(p, 3);
     return;
   }
 #pragma unroll
@@ -804,6 +809,7 @@ hgemm_tr_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
       __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(C + (int64_t)grow * p.ldc + col));
     }
   }
+  trace_stamp(p, 3);
 }
 
 // With S::PARTIAL this is the split-K partial launch (FP32 partials).

@@ -221,6 +221,7 @@ __device__ __forceinline__ void issue_slice(const unsigned char* Ab, const unsig
 template <class S>
 __global__ void __launch_bounds__(S::NT)
 sgemm_dl_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
+  trace_stamp(p, 0);
   constexpr int NS = S::NS, KG = S::KG, MB = S::MB, NB = S::NB, IA = S::IA, IB = S::IB;
   constexpr int BM = S::BM, BN = S::BN, WM = S::WM, WN = S::WN, BK = S::BK;
   typedef typename VecF<NB>::T vecNB;
@@ -414,6 +415,7 @@ sgemm_dl_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
     static_for([&](auto I) { issue(decltype(I)::value, A_of(I), B_of(I)); },
                std::make_integer_sequence<int, NS>{});
     loop_barrier<(NS - 1) * S::LPS>();  // slice 0 landed
+    trace_stamp(p, 1);
     load_frags(0, la0, lb0, 0);
     int t = 0;
     for (; t + NS <= T; t += NS)
@@ -424,6 +426,7 @@ sgemm_dl_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
     // before the workgroup ends and its LDS is handed to another.
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   }
+  trace_stamp(p, 2);
 
   // Epilogue: acc[mb][nb] register r of lane l holds C[m][n] with
   // m = wm0 + 32mb + 8(r/4) + 4(l/32) + r%4 and n = wn0 + NB*(l%32) + nb:
@@ -538,6 +541,7 @@ sgemm_dl_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
         }
       }
   }
+  trace_stamp(p, 3);
 }
 
 template <class S>

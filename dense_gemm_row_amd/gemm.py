@@ -43,6 +43,7 @@ TYPES = ("f32", "f16", "bf16", "f8", "e5m2")
 EXPORTS = [f"gemm_{t}{form}" for form in ("", "_ex", "_bt", "_trans", "_epi", "_epi_q8", "_splitk")
            for t in TYPES] + [
            "gemm_splitk_workspace_bytes", "gemm_select_splitk_config", "gemm_splitk_static",
+           "gemm_trace_set",
            "gemm_num_configs", "gemm_get_config", "gemm_select_config", "gemm_tile_of_block",
            "gemm_layout_check", "gemm_load_tuning", "gemm_status_string",
            "gemm_last_error", "gemm_last_hip_error", "gemm_version"]
@@ -103,6 +104,8 @@ def _declare(lib):
     for name in (f"gemm_{t}_splitk" for t in types):
         getattr(lib, name).argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, p, i64, p, cfgp]
         getattr(lib, name).restype = ctypes.c_int
+    lib.gemm_trace_set.argtypes = [p, i64]
+    lib.gemm_trace_set.restype = ctypes.c_int
     lib.gemm_splitk_static.argtypes = [i32, i64, i64, i64, p, i64, p, i64, p, i64, p, cfgp]
     lib.gemm_splitk_static.restype = ctypes.c_int
     lib.gemm_splitk_workspace_bytes.argtypes = [i32, i64, i64, i64, i32]
@@ -235,6 +238,31 @@ def entry(dtype: int, form: str = ""):
     name = {DTYPE_F32: "f32", DTYPE_F16: "f16", DTYPE_BF16: "bf16", DTYPE_F8: "f8",
             DTYPE_E5M2: "e5m2"}[dtype]
     return globals()[f"gemm_{name}{form}"]
+
+
+def gemm_trace_set(stamps, workgroups: int) -> int:
+    """gemm_trace_set: per-workgroup timestamps of this thread's following
+    launches of the LDS-direct kernels into the device buffer `stamps`
+    (8 uint64 per workgroup); stamps None stops."""
+    return lib().gemm_trace_set(stamps, workgroups)
+
+
+def trace_summary(stamps) -> dict:
+    """Per-workgroup intervals of a traced launch from its stamps (a CPU
+    int64/uint64 array of 8 per workgroup): entry to first slice (fill), the
+    K loop, the epilogue, and the clock over the loop (MHz), as numpy
+    arrays; plus the span of loop ends across workgroups (us)."""
+    import numpy as np
+    s = np.asarray(stamps, dtype=np.float64).reshape(-1, 8)
+    cyc, rt = s[:, 0::2], s[:, 1::2]
+    us = (rt - rt[:, :1]) / 100.0
+    loop_clock = (cyc[:, 2] - cyc[:, 1]) / np.maximum(rt[:, 2] - rt[:, 1], 1) * 100.0
+    return {"fill_us": us[:, 1], "loop_us": us[:, 2] - us[:, 1], "epilogue_us": us[:, 3] - us[:, 2],
+            "loop_kcycles": (cyc[:, 2] - cyc[:, 1]) / 1e3,
+            "loop_clock_mhz": loop_clock, "entry_us": (rt[:, 0] - rt[:, 0].min()) / 100.0,
+            "loop_end_us": (rt[:, 2] - rt[:, 0].min()) / 100.0,
+            "loop_end_spread_us": float((rt[:, 2].max() - rt[:, 2].min()) / 100.0),
+            "span_us": float((rt[:, 3].max() - rt[:, 0].min()) / 100.0)}
 
 
 # The static scratch of gemm_splitk_static (GEMM_SPLITK_STATIC_MAX_BYTES).

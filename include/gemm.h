@@ -253,6 +253,25 @@ gemm_status_t gemm_f8_splitk(int64_t M, int64_t N, int64_t K,
                              void *stream, const gemm_config_t *cfg);
 
 /*
+ * Per-workgroup timestamps of the GEMM launches that follow on the calling
+ * thread (the "trace" of a launch; tracing and profiling).  While `stamps`
+ * is set, every launch of the two LDS-direct kernel families (the default
+ * variants: names "dl_f32_*" and "tr_*") makes workgroup w =
+ * blockIdx.y * gridDim.x + blockIdx.x, for w < `workgroups`, write eight
+ * uint64 into stamps[8w .. 8w+7]: pairs (shader-cycle counter s_memtime,
+ * 100 MHz constant clock s_memrealtime) at four points: 0 kernel entry,
+ * 1 first K slice in LDS, 2 K loop done, 3 C stores issued.  The
+ * workgroup's clock over an interval is d(cycles) / d(constant clock) x
+ * 100 MHz.  Each launch overwrites the entries of its workgroups; other
+ * kernels write nothing.  `stamps` is a device buffer of at least
+ * 8 x `workgroups` uint64, owned by the caller, who keeps it alive while
+ * set; NULL stops tracing.  Bad capacity (negative, above 2^31-1, or 0
+ * with a buffer) -> GEMM_ERR_INVALID_ARG.  Tracing is not a result of the
+ * GEMM: outputs are unchanged.
+ */
+gemm_status_t gemm_trace_set(uint64_t *stamps, int64_t workgroups);
+
+/*
  * Split-K that allocates nothing and takes no workspace: for callers that
  * cannot allocate device memory (code under HIP graph capture, serving
  * loops and harnesses that forbid hipMalloc).  The same computation and

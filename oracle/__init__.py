@@ -151,10 +151,20 @@ def load(path: str | None = None):
 
 
 def default_threads() -> int:
+    """The host cores this process may use: its CPU affinity, capped by
+    OMP_NUM_THREADS when the environment sets it (a machine shared between
+    jobs grants each its share that way).  The thread count never changes a
+    result: threads split whole rows, and each row's sums keep their
+    order."""
     try:
-        return len(os.sched_getaffinity(0))
+        n = len(os.sched_getaffinity(0))
     except AttributeError:  # pragma: no cover
-        return os.cpu_count() or 1
+        n = os.cpu_count() or 1
+    try:
+        cap = int(os.environ.get("OMP_NUM_THREADS", "0"))
+    except ValueError:
+        cap = 0
+    return max(1, min(n, cap) if cap > 0 else n)
 
 
 def _ptr(a: np.ndarray) -> int:

@@ -24,10 +24,26 @@ def _dtype_of(fn):
             "e5m2": gemm.DTYPE_E5M2}[t]
 
 
-def header_functions():
-    text = open(HEADER).read()
+def header_functions(path=HEADER):
+    text = open(path).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(gemm_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_probe_library_exports_its_header():
+    """libgemm_probe exports every call include/gemm_probe.h declares, and
+    refuses bad arguments before any launch."""
+    from dense_gemm_row_amd import probe
+    L = probe.lib()
+    names = header_functions(os.path.join(ROOT, "include", "gemm_probe.h"))
+    assert names == ["gemm_probe_clock", "gemm_probe_mfma", "gemm_probe_workgroups"]
+    for name in names:
+        assert hasattr(L, name), name
+    assert L.gemm_probe_workgroups() == 256
+    assert L.gemm_probe_mfma(1, -2, 8, 8, None) == gemm.GEMM_ERR_INVALID_ARG
+    assert L.gemm_probe_mfma(1, 2, None, 8, None) == gemm.GEMM_ERR_INVALID_ARG
+    assert L.gemm_probe_mfma(9, 2, 8, 8, None) == gemm.GEMM_ERR_INVALID_ARG
+    assert L.gemm_probe_clock(-1, 8, 8, None) == gemm.GEMM_ERR_INVALID_ARG
 
 
 def test_exports_every_declared_symbol():
@@ -37,6 +53,14 @@ def test_exports_every_declared_symbol():
     for name in names:
         assert hasattr(lib, name), f"{name} declared in gemm.h but not exported"
     assert sorted(gemm.EXPORTS) == names
+
+
+def test_trace_set_checks_its_capacity():
+    assert gemm.gemm_trace_set(PC, -1) == gemm.GEMM_ERR_INVALID_ARG
+    assert gemm.gemm_trace_set(PC, 0) == gemm.GEMM_ERR_INVALID_ARG
+    assert gemm.gemm_trace_set(PC, 2 ** 31) == gemm.GEMM_ERR_INVALID_ARG
+    assert gemm.gemm_trace_set(PC, 256) == gemm.GEMM_OK
+    assert gemm.gemm_trace_set(None, 0) == gemm.GEMM_OK
 
 
 def test_version_and_status_strings():
