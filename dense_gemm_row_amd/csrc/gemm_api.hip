@@ -108,6 +108,7 @@ const AloneRate kAlone[] = {
     {"tr_f16_128x256x64_w64x128_s3", 1.691f, 6.18f}, {"tr_f16_128x128x64_w64x64_s2", 0.767f, 1.36f},
     {"tr_f16_256x128x64_w128x64_s3_p4", 1.835f, 5.86f},
     {"tr_f16_256x128x64_w128x64_s3_p2", 1.854f, 6.37f},
+    {"tr_f16_256x256x64_w128x128_s2_ps", 1.556f, 8.31f},
     {"mfma_f16_256x256x64_w128x128", 0.840f, 8.11f}, {"mfma_f16_256x128x64_w128x64", 0.545f, 6.93f},
     {"mfma_f16_128x256x64_w64x128", 0.547f, 2.75f}, {"mfma_f16_128x128x64_w64x64", 0.381f, 2.74f},
     {"mfma_f16_64x64x64_w32x32", 0.126f, 1.30f}, {"tr_bf16_256x256x64_w128x128_s2", 1.554f, 8.22f},
@@ -118,16 +119,37 @@ const AloneRate kAlone[] = {
     {"tr_bf16_128x128x64_w64x64_s2", 0.770f, 1.69f},
     {"tr_bf16_256x128x64_w128x64_s3_p4", 1.841f, 5.98f},
     {"tr_bf16_256x128x64_w128x64_s3_p2", 1.870f, 6.54f},
+    {"tr_bf16_256x256x64_w128x128_s2_ps", 1.554f, 8.22f},
     {"mfma_bf16_256x256x64_w128x128", 0.849f, 7.43f},
     {"mfma_bf16_256x128x64_w128x64", 0.547f, 5.94f},
     {"mfma_bf16_128x256x64_w64x128", 0.546f, 2.76f}, {"mfma_bf16_128x128x64_w64x64", 0.381f, 2.79f},
     {"mfma_bf16_64x64x64_w32x32", 0.126f, 1.39f}, {"tr_f8_256x256x128_w128x128_s2", 1.774f, 8.60f},
     {"tr_f8_256x256x64_w128x128_s4", 1.597f, 8.70f},
+    {"tr_f8_256x256x128_w128x128_s2_ps", 1.774f, 8.60f},
     {"tr_f8_128x256x128_w64x128_s3", 1.687f, 6.30f},
     {"tr_f8_128x256x128_w64x128_s3_p4", 1.788f, 6.16f},
 };
 
 double model_rate(int dtype);
+
+// Persistent tiles against their one-tile twin, per round of tiles (one
+// 256 x 256 tile per CU), from same-box timings at 8192 x 8192 x 1024 and
+// 4096 x 11008 x 4096 with in-kernel timestamps: saved_us, the per-tile
+// fixed cost saved (launch, pipeline fill and the epilogue's exposed part
+// overlap the neighbouring tiles' work), and slice_us, the extra loop time
+// per K slice (the previous tile's C stores share the memory path).  Per
+// round, time = twin's - saved_us + slices * slice_us: the persistent form
+// wins at short K (below about 53 slices for 16-bit, 33 for 8-bit).  E5M2
+// takes E4M3's figures.
+struct PsRate {
+  const char* name;
+  float saved_us, slice_us;
+};
+const PsRate kPs[] = {
+    {"tr_f16_256x256x64_w128x128_s2_ps", 3.7f, 0.07f},
+    {"tr_bf16_256x256x64_w128x128_s2_ps", 3.7f, 0.07f},
+    {"tr_f8_256x256x128_w128x128_s2_ps", 3.7f, 0.11f},
+};
 
 // The loop rate (relative to R) of one workgroup per CU with all 256 CUs
 // busy, for a tile that fills its CU's LDS: eff with the fixed cost taken
@@ -142,6 +164,7 @@ double full_loop_rate(int dtype, const Variant& v, const AloneRate& a) {
 struct Table {
   std::vector<Variant> v[kDtypes];  // per dtype
   std::vector<AloneRate> alone[kDtypes];  // per variant: kAlone's figures, else {eff, 0}
+  std::vector<PsRate> ps[kDtypes];        // per variant: kPs's figures, else {0, 0}
   // Loop rate with all 256 CUs busy over eff1, per dtype, from the default
   // tile (at most 1): the matrix units' clock falls as more CUs run them.
   double derate[kDtypes];
@@ -175,6 +198,10 @@ struct Table {
         for (const AloneRate& a : kAlone)
           if (name == a.name) r = AloneRate{v[d][i].desc.name, a.eff1, a.fixed_us};
         alone[d].push_back(r);
+        PsRate q{v[d][i].desc.name, 0.f, 0.f};
+        for (const PsRate& a : kPs)
+          if (name == a.name) q = PsRate{v[d][i].desc.name, a.saved_us, a.slice_us};
+        ps[d].push_back(q);
       }
       if (!v[d].empty() && alone[d][0].eff1 > 0.f)
         derate[d] = std::min(1.0, full_loop_rate(d, v[d][0], alone[d][0]) / alone[d][0].eff1);
@@ -261,6 +288,16 @@ double gemm_seconds(int dtype, const Variant& v, int64_t M, int64_t N, int64_t K
   int64_t per_cu = (160 * 1024) / (d.lds_bytes > 0 ? d.lds_bytes : 1);
   per_cu = per_cu < 1 ? 1 : per_cu > 2 ? 2 : per_cu;
   const int64_t wgs = cdiv(M, d.bm) * cdiv(N, d.bn) * S;
+  if (v.persistent) {
+    // Only several rounds of tiles give it anything to overlap; with one
+    // round (or split partials, which it has no form for) its twin runs.
+    if (S != 1 || wgs <= 256) return 1e30;
+    const PsRate& q = table().ps[dtype][d.id];
+    const int64_t rounds = cdiv(wgs, 256);
+    const double twin = (double)rounds * 2.0 * d.bm * d.bn * (double)(Kc > 0 ? Kc : 1) /
+                        ((v.eff > 0.f ? v.eff : 0.1) * rate);
+    return twin - (double)rounds * (q.saved_us - (double)cdiv(Kc, d.bk) * q.slice_us) * 1e-6;
+  }
   if (S == 1 && wgs <= 256) {
     // Unsplit, one workgroup per CU at most: the fixed cost plus the loop
     // at its rate alone, eff1 with up to 64 CUs busy, linearly down to its

@@ -304,6 +304,9 @@ struct Variant {
   // kernel has no such form.
   LaunchFn launch_at;
   LaunchFn launch_atbt;
+  // The persistent form of a tile (workgroups walk several output tiles):
+  // the cost model prices it per round against its one-tile twin.
+  bool persistent = false;
 };
 
 // Per-family registration (each kernel file defines its table).

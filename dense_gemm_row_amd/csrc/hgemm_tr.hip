@@ -151,6 +151,8 @@ struct Shape {
   static constexpr int EPI_ROW = WN * 2, EPI_SPR = WN / 4;
   static constexpr int P = (2 * NS) / NW, RPA = WM / P;
   static constexpr int EPI_CPR = WN / 8, EPI_RPI = 64 / EPI_CPR;  // store pass shape
+  // The persistent form's wave-private epilogue staging: 32 rows.
+  static constexpr int PS_EPI_BYTES = 32 * EPI_ROW;
   static_assert(F8 ? (BK == 64 || BK == 128) : (BK == 32 || BK == 64), "K slice");
   // Fragments alternate between two register sets by global k step
   // (slice * KS + step); the slice loop is unrolled NS times, so the set of
@@ -325,6 +327,36 @@ __device__ __forceinline__ void issue_slice(const unsigned char* Ab, const unsig
       lds_void* dst = (lds_void*)(lds_b + 1024 * ((q - S::IA) * S::NL + wave));
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, dst, 16, b_vo[q - S::IA], 0, 0, 0);
     }
+  }
+}
+
+// The persistent kernel's copies of slice s (row-major A and B): the same
+// copies as issue_slice, with the last slice's A tail mask given as one
+// bit per copy (bit i clear: copy i of A reads past K and is dropped), so
+// that each offset is a select, not a choice between two offset arrays.
+// (Its own function: the host pass leaves a device function template's
+// specialisation unusable for a second kernel once one kernel has
+// instantiated it.)
+template <class S>
+__device__ __forceinline__ void issue_slice_ps(const unsigned char* Ab, const unsigned char* Bb,
+                                               int64_t a_bytes, int64_t b_bytes, int s, bool live,
+                                               bool last, const unsigned* a_vo, unsigned a_tail,
+                                               const unsigned* b_vo, unsigned char* lds_a,
+                                               unsigned char* lds_b, int wave, int lda, int ldb) {
+  const int64_t ka = S::ES * (int64_t)s * S::BK;
+  const int64_t kb = (int64_t)s * S::BK * ldb * S::ES;
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(Ab + ka, live ? a_bytes - ka : 0);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bb + kb, live ? b_bytes - kb : 0);
+#pragma unroll
+  for (int q = 0; q < S::IA; ++q) {
+    lds_void* dst = (lds_void*)(lds_a + 1024 * (q * S::NL + wave));
+    const unsigned off = (last && !((a_tail >> q) & 1u)) ? OOB : a_vo[q];
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, dst, 16, off, 0, 0, 0);
+  }
+#pragma unroll
+  for (int q = 0; q < S::IB; ++q) {
+    lds_void* dst = (lds_void*)(lds_b + 1024 * (q * S::NL + wave));
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, dst, 16, b_vo[q], 0, 0, 0);
   }
 }
 
@@ -812,6 +844,299 @@ hgemm_tr_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
   trace_stamp(p, 3);
 }
 
+// Persistent form of the plain kernel (two stages, row-major A and B, no
+// producer waves).  gridDim.x workgroups (at most one per CU) walk the
+// tiles v = blockIdx.x, blockIdx.x + gridDim.x, ... in the tile map's order
+// (gridDim.x is a multiple of the XCD count, so every tile a workgroup
+// takes belongs to its own XCD's run of the map), and the slice pipeline
+// runs on across tiles: the two stages that a tile's last two slices free
+// receive the next tile's first two slices, so those copies are in flight
+// while this tile's C is written.  The C tile therefore leaves the
+// accumulators through a wave-private LDS region, not the stages: 32 rows
+// of the wave tile per round, written as 8-byte slots XOR-swizzled by row
+// (conflict-free), read back as 16-byte row chunks and stored with
+// WN/8 lanes per row segment (the coalesced write-back of "sgemm - beyond
+// cuBLAS", section 5), branch-free through a buffer descriptor over C.
+// The number of K slices must be even, so that every tile starts on stage
+// 0 (the launch runs the one-tile-per-workgroup kernel otherwise).
+//
+// The first wait of each later tile is vmcnt <= (copies of one slice):
+// the C stores were issued after the next tile's copies, and whether or
+// not stores complete in order with loads, a count that low means at least
+// one slice's worth of copies has completed beyond the stores, and copies
+// complete in order among themselves, so the tile's first slice is in LDS.
+template <class S>
+__global__ void __launch_bounds__(S::NT)
+hgemm_tr_persistent_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
+  static_assert(S::NS == 2 && S::PW == 0 && !S::BT && !S::AT && !S::PARTIAL && !S::EPI,
+                "persistent form: plain two-stage kernel");
+  constexpr int KS = S::KS, MB = S::MB, NB = S::NB, IA = S::IA, IB = S::IB;
+  constexpr int BM = S::BM, BN = S::BN, WM = S::WM, WN = S::WN, BK = S::BK;
+  __shared__ __attribute__((aligned(1024))) unsigned char la0[S::A_STAGE], lb0[S::B_STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char la1[S::A_STAGE], lb1[S::B_STAGE];
+  // Epilogue staging, one region per wave: 32 rows of EPI_ROW bytes.
+  __shared__ __attribute__((aligned(1024))) unsigned char lep[S::NW * S::PS_EPI_BYTES];
+
+  trace_stamp(p, 0);
+  const int ntiles = map.tiles_m * map.tiles_n;
+  const int M = p.M, N = p.N, K = p.K;
+  const int lda = (int)p.lda, ldb = (int)p.ldb;
+  const unsigned char* Ab = static_cast<const unsigned char*>(p.A);
+  const unsigned char* Bb = static_cast<const unsigned char*>(p.B);
+  const int tid = threadIdx.x;
+  const int l = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm0 = (wave / S::WAVES_N) * WM, wn0 = (wave % S::WAVES_N) * WN;
+  const int lw = S::PW > 0 ? wave - S::NW : wave;  // index among the copying waves
+  const int T = (K + BK - 1) / BK;
+  unsigned char* ep = lep + wave * S::PS_EPI_BYTES;
+
+  // Direct-load offsets of one tile (relative to the slice's descriptor
+  // base), as in the one-tile kernel.
+  unsigned a_vo[IA], b_vo[IB];
+  // Bit i: copy i of A stays within K in the last (partial) slice.
+  unsigned a_tail = 0;
+  // The lane index as a value the compiler cannot see through: the per-lane
+  // terms of the offsets below are then recomputed where they are used
+  // instead of being hoisted out of the tile loop and kept live across it,
+  // which spills registers to scratch memory (whose loads share the wait
+  // counter with the stage copies).
+  auto opaque_lane = [&]() __attribute__((always_inline)) {
+    int v = l;
+    asm volatile("" : "+v"(v));
+    return v;
+  };
+  // Everything per lane that the K loop needs is (re)computed at the top of
+  // each tile (and the copy offsets again for the next tile two slices
+  // before the end), so that none of it is live across the epilogue, which
+  // needs the registers.
+  auto set_tile = [&](int m0, int n0) __attribute__((always_inline)) {
+    const int l = opaque_lane();
+    a_tail = 0;
+#pragma unroll
+    for (int i = 0; i < IA; ++i)
+      a_tail |= ((T - 1) * BK + S::CE * S::a_dl_q(i, lw, l) < K) ? 1u << i : 0u;
+#pragma unroll
+    for (int i = 0; i < IA; ++i) {
+      const int r = S::a_dl_row(i, lw, l), q = S::a_dl_q(i, lw, l);
+      a_vo[i] = (m0 + r) < M ? (unsigned)S::ES * ((unsigned)(m0 + r) * (unsigned)lda + (unsigned)S::CE * q) : OOB;
+    }
+    // (B rows past K are past the buffer's range.)
+#pragma unroll
+    for (int i = 0; i < IB; ++i) {
+      const int k = S::b_dl_k(i, lw, l), c = S::b_dl_c(i, lw, l);
+      b_vo[i] = (n0 + S::CE * c) < N ? (unsigned)S::ES * ((unsigned)k * (unsigned)ldb + (unsigned)(n0 + S::CE * c))
+                                     : OOB;
+    }
+  };
+  // Fragment byte offsets (tile-independent; recomputed per tile).
+  constexpr int FR = S::FR;
+  int a_fb[KS * FR], b_fb[NB];
+  auto set_frags = [&]() __attribute__((always_inline)) {
+    const int l = opaque_lane();
+#pragma unroll
+    for (int j = 0; j < KS; ++j)
+#pragma unroll
+      for (int q = 0; q < FR; ++q) a_fb[j * FR + q] = S::a_frag(wm0, 0, j, l, q);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) b_fb[nb] = S::b_frag(wn0, nb, 0, 0, l);
+  };
+
+  // Slice s of the current tile's offsets (s >= T: zeros, no memory read).
+#define PS_PRODUCE(s_, la_, lb_)                                                              \
+  issue_slice_ps<S>(Ab, Bb, a_bytes, b_bytes, (s_), (s_) < T, (s_) == T - 1, a_vo, a_tail, b_vo, \
+                    (la_), (lb_), lw, lda, ldb)
+
+  typedef std::conditional_t<S::F8, i32x8_t, f16x8> Frag;
+  Frag fa[2][MB], fb[2][NB];
+  auto two_chunks = [](const unsigned char* p0, const unsigned char* p1) __attribute__((always_inline)) {
+    const u32x4 x0 = *(const lds_u32x4*)p0, x1 = *(const lds_u32x4*)p1;
+    return __builtin_bit_cast(i32x8_t, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  auto tr_operand = [](const unsigned char* b, int row) __attribute__((always_inline)) {
+    if constexpr (S::F8) {
+      const i32x2 r0 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)b);
+      const i32x2 r1 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(b + 8 * row));
+      const i32x2 r2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(b + 16 * row));
+      const i32x2 r3 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(b + 24 * row));
+      const i32x4 lo = __builtin_shufflevector(r0, r1, 0, 1, 2, 3);
+      const i32x4 hi = __builtin_shufflevector(r2, r3, 0, 1, 2, 3);
+      return Frag(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    } else {
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)b);
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(b + 4 * row));
+      return Frag(__builtin_bit_cast(f16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7)));
+    }
+  };
+  auto load_frags = [&](int buf, const unsigned char* la, const unsigned char* lb, int j)
+      __attribute__((always_inline)) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      if constexpr (S::F8)
+        fa[buf][mb] = two_chunks(la + a_fb[2 * j] + mb * 32 * S::A_ROW, la + a_fb[2 * j + 1] + mb * 32 * S::A_ROW);
+      else
+        fa[buf][mb] = *(const lds_f16x8*)(la + a_fb[j] + mb * 32 * S::A_ROW);
+    }
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) fb[buf][nb] = tr_operand(lb + b_fb[nb] + S::KW * j * S::B_ROW, S::B_ROW);
+  };
+  f32x16 acc[NB][MB];
+  auto zero_acc = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[nb][mb][r] = 0.f;
+  };
+  auto mma = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        if constexpr (S::F8)
+          acc[nb][mb] = mfma_f8<S::TY - 2>(fb[buf][nb], fa[buf][mb], acc[nb][mb]);
+        else
+          acc[nb][mb] = mfma16<S::BF>(fb[buf][nb], fa[buf][mb], acc[nb][mb]);
+      }
+  };
+  constexpr int NMMA = MB * NB;
+  constexpr int NRD = MB * FR + S::TRN * NB;
+
+  int v = blockIdx.x;
+  int tm, tn;
+  tile_of_block(v, map, tm, tn);
+  int m0 = tm * BM, n0 = tn * BN;
+  int vn = v + gridDim.x;
+  bool has_next = vn < ntiles;
+  int m0n = 0, n0n = 0;
+  if (has_next) {
+    tile_of_block(vn, map, tm, tn);
+    m0n = tm * BM;
+    n0n = tn * BN;
+  }
+  set_tile(m0, n0);
+
+  // Slice t of the current tile from stage c (as the one-tile kernel's
+  // two-stage slice), except that the copy issued into the freed stage is
+  // slice t+2 of this tile, or, past its last slice, slice t+2-T of the
+  // next tile (the offsets switch to the next tile at its first copy).
+  auto slice = [&](int t, auto C_) __attribute__((always_inline)) {
+    constexpr int c = decltype(C_)::value, n = (c + 1) % 2;
+    unsigned char* ca = c == 0 ? la0 : la1;
+    unsigned char* cb = c == 0 ? lb0 : lb1;
+    // Every copy of this tile is issued by now (slice T-1 went out in
+    // slice T-3): the offsets can move to the next tile.
+    if (has_next && t == T - 2) set_tile(m0n, n0n);
+    static_for([&](auto J) __attribute__((always_inline)) {
+      constexpr int j = decltype(J)::value;
+      load_frags(S::frag_set(c, j + 1), ca, cb, j + 1);
+      mma(S::frag_set(c, j));
+#pragma unroll
+      for (int i = 0; i < NMMA; ++i) {
+        SGB(SG_MFMA, 1);
+        if (i < NRD) SGB(SG_DS_RD, 1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }, std::make_integer_sequence<int, KS - 1>{});
+    loop_barrier<0>();  // slice t+1 landed (and any earlier stores done)
+    __builtin_amdgcn_sched_barrier(0);
+    {
+      const int s = has_next && t + 2 >= T ? t + 2 - T : t + 2;
+      PS_PRODUCE(s, ca, cb);
+    }
+    load_frags(S::frag_set(c + 1, 0), n == 0 ? la0 : la1, n == 0 ? lb0 : lb1, 0);
+    mma(S::frag_set(c, KS - 1));
+#pragma unroll
+    for (int i = 0; i < NMMA; ++i) {
+      SGB(SG_MFMA, 1);
+      if (i < NRD) SGB(SG_DS_RD, 1);
+      if (i < S::LPS) SGB(SG_VMEM_RD, 1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  typedef int v4i __attribute__((ext_vector_type(4)));
+  const __amdgpu_buffer_rsrc_t rc =
+      make_rsrc(static_cast<const unsigned char*>(p.C), ((int64_t)(M - 1) * p.ldc + N) * 2);
+  constexpr int CPR = S::EPI_CPR, RPI = S::EPI_RPI;
+
+  zero_acc();
+  if (T > 0) {
+    PS_PRODUCE(0, la0, lb0);
+    PS_PRODUCE(1, la1, lb1);
+  }
+  bool first = true;
+  for (;;) {
+    set_tile(m0, n0);
+    set_frags();
+    if (T > 0) {
+      // Slice 0 of this tile landed (later tiles: see the note above).
+      loop_barrier<S::LPS>();
+      if (first) trace_stamp(p, 1);
+      load_frags(0, la0, lb0, 0);
+      for (int t = 0; t < T; t += 2) {
+        slice(t, IC<0>{});
+        slice(t + 1, IC<1>{});
+      }
+    }
+    first = false;
+    // Epilogue: round mb stages rows wm0 + 32mb .. +31 of the wave tile.
+    const int l = opaque_lane();
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      // One round at a time (the scheduler would otherwise hoist every
+      // round's accumulator reads and run out of registers).
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          uint2 w;
+          w.x = round16<S::BF>(acc[nb][mb][4 * rq + 0]) | ((unsigned)round16<S::BF>(acc[nb][mb][4 * rq + 1]) << 16);
+          w.y = round16<S::BF>(acc[nb][mb][4 * rq + 2]) | ((unsigned)round16<S::BF>(acc[nb][mb][4 * rq + 3]) << 16);
+          *reinterpret_cast<uint2*>(ep + S::epi_byte(l % 32, 8 * nb + 2 * rq + l / 32)) = w;
+        }
+      // All the round's row chunks are read back first, then stored: one
+      // wait for the LDS reads instead of one per store.
+      const int col = n0 + wn0 + 8 * (l % CPR);
+      constexpr int PASSES = 32 / RPI;
+      v4i val[PASSES];
+#pragma unroll
+      for (int pass = 0; pass < PASSES; ++pass) {
+        const int r = pass * RPI + l / CPR;
+        const uint2 lo = *reinterpret_cast<const uint2*>(ep + S::epi_byte(r, 2 * (l % CPR)));
+        const uint2 hi = *reinterpret_cast<const uint2*>(ep + S::epi_byte(r, 2 * (l % CPR) + 1));
+        val[pass] = v4i{(int)lo.x, (int)lo.y, (int)hi.x, (int)hi.y};
+      }
+#pragma unroll
+      for (int pass = 0; pass < PASSES; ++pass) {
+        const int row = m0 + wm0 + 32 * mb + pass * RPI + l / CPR;
+        const unsigned off = ((row < M) & (col < N)) ? 2u * ((unsigned)row * (unsigned)p.ldc + (unsigned)col) : OOB;
+        __builtin_amdgcn_raw_buffer_store_b128(val[pass], rc, off, 0, 0);
+      }
+    }
+    if (!has_next) break;
+    v = vn;
+    m0 = m0n;
+    n0 = n0n;
+    vn = v + gridDim.x;
+    has_next = vn < ntiles;
+    if (has_next) {
+      tile_of_block(vn, map, tm, tn);
+      m0n = tm * BM;
+      n0n = tn * BN;
+    }
+    zero_acc();
+  }
+  trace_stamp(p, 2);
+  // The zero-filling copies past the last tile's last slice must land
+  // before the workgroup ends and its LDS is handed to another.
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  trace_stamp(p, 3);
+#undef PS_PRODUCE
+}
+
 // With S::PARTIAL this is the split-K partial launch (FP32 partials).
 template <class S>
 hipError_t launch(const Params& p, const TileMap& map, bool vec, hipStream_t stream) {
@@ -839,6 +1164,29 @@ hipError_t launch(const Params& p, const TileMap& map, bool vec, hipStream_t str
                                   : ((int64_t)(p.K - 1) * p.ldb + p.N) * ES;
   const dim3 grid(map.tiles_m * map.tiles_n, p.splits), block(S::NT);
   hipLaunchKernelGGL(hgemm_tr_kernel<S>, grid, block, 0, stream, p, map, a_bytes, b_bytes);
+  return hipGetLastError();
+}
+
+// The persistent form's launch: min(tiles, 256) workgroups (one per CU of
+// MI355X) when the K slices are even in number and C's offsets fit the
+// buffer store's 32 bits; the one-tile kernel otherwise (which also takes
+// the operands off the vector layout to the general kernel).
+template <class S>
+hipError_t launch_persistent(const Params& p, const TileMap& map, bool vec, hipStream_t stream) {
+  static_assert(S::LDS_BYTES + S::NW * S::PS_EPI_BYTES <= 160 * 1024, "LDS");
+  const int T = (p.K + S::BK - 1) / S::BK;
+  const int64_t lim = 0x7fffffff;
+  constexpr int ES = S::ES;
+  const bool far = (int64_t)(S::BK + 2) * p.ldb * ES > lim ||
+                   ((int64_t)(p.K > 0 ? p.K - 1 : 0) * p.ldb + p.N) * ES > lim ||
+                   (int64_t)(p.M + S::BM) * p.lda * ES > lim || (int64_t)p.M * p.lda * ES > lim ||
+                   ((int64_t)p.M * p.ldc + S::BN) * 2 > lim;
+  if (!vec || far || T == 0 || T % 2 != 0 || p.splits > 1) return launch<S>(p, map, vec, stream);
+  const int64_t a_bytes = ((int64_t)(p.M - 1) * p.lda + p.K) * ES;
+  const int64_t b_bytes = ((int64_t)(p.K - 1) * p.ldb + p.N) * ES;
+  const int tiles = map.tiles_m * map.tiles_n;
+  const dim3 grid(tiles < 256 ? tiles : 256), block(S::NT);
+  hipLaunchKernelGGL(hgemm_tr_persistent_kernel<S>, grid, block, 0, stream, p, map, a_bytes, b_bytes);
   return hipGetLastError();
 }
 
@@ -1140,6 +1488,20 @@ constexpr LaunchFn at_launch() {
         at_launch<BM, BN, WM, WN, BK, NS, TY, false, PW>(),                                  \
         at_launch<BM, BN, WM, WN, BK, NS, TY, true, PW>()                                    \
   }
+// The persistent form of a two-stage tile: the plain call only.
+#define HGEMM_TR_VARIANT_PS(TY, DT, TAG, BM, BN, WM, WN, BK, EFF)                                    \
+  Variant {                                                                                      \
+    gemm_config_t{0, DT, GEMM_FAMILY_MFMA, BM, BN, BK, WM, WN,                                   \
+                  Shape<BM, BN, WM, WN, BK, 2, 0, false, TY, false, 0>::NT, 2,                   \
+                  Shape<BM, BN, WM, WN, BK, 2, 0, false, TY, false, 0>::LDS_BYTES +              \
+                      Shape<BM, BN, WM, WN, BK, 2, 0, false, TY, false, 0>::NW *                 \
+                          Shape<BM, BN, WM, WN, BK, 2, 0, false, TY, false, 0>::PS_EPI_BYTES,    \
+                  GEMM_ORDER_XCD, 4, 1,                                                          \
+                  "tr_" TAG "_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_s2_ps"},                  \
+        &launch_persistent<Shape<BM, BN, WM, WN, BK, 2, 0, false, TY, false, 0>>,                \
+        &layout_check<Shape<BM, BN, WM, WN, BK, 2, 0, false, TY, false, 0>>, nullptr, EFF,      \
+        nullptr, nullptr, nullptr, nullptr, nullptr, true                                        \
+  }
 #define HGEMM_TR_VARIANT(TY, DT, TAG, BM, BN, WM, WN, BK, NS, EFF) \
   HGEMM_TR_VARIANT_PW(TY, DT, TAG, BM, BN, WM, WN, BK, NS, 0, "", EFF)
 
@@ -1155,7 +1517,8 @@ constexpr LaunchFn at_launch() {
    HGEMM_TR_VARIANT(TY, DT, TAG, 128, 256, 64, 128, 64, 3, 0.89f),  \
    HGEMM_TR_VARIANT(TY, DT, TAG, 128, 128, 64, 64, 64, 2, 0.71f),                 \
    HGEMM_TR_VARIANT_PW(TY, DT, TAG, 256, 128, 128, 64, 64, 3, 4, "_p4", 0.895f),   \
-   HGEMM_TR_VARIANT_PW(TY, DT, TAG, 256, 128, 128, 64, 64, 3, 2, "_p2", 0.89f)}
+   HGEMM_TR_VARIANT_PW(TY, DT, TAG, 256, 128, 128, 64, 64, 3, 2, "_p2", 0.89f),    \
+   HGEMM_TR_VARIANT_PS(TY, DT, TAG, 256, 256, 128, 128, 64, 1.00f)}
 
 const Variant kVariants[] = HGEMM_TR_TABLE(0, GEMM_DTYPE_F16, "f16");
 const Variant kVariantsBf[] = HGEMM_TR_TABLE(1, GEMM_DTYPE_BF16, "bf16");
@@ -1165,7 +1528,8 @@ const Variant kVariantsBf[] = HGEMM_TR_TABLE(1, GEMM_DTYPE_BF16, "bf16");
   {HGEMM_TR_VARIANT(TY, DT, TAG, 256, 256, 128, 128, 128, 2, 1.00f),              \
    HGEMM_TR_VARIANT(TY, DT, TAG, 256, 256, 128, 128, 64, 4, 0.85f),               \
    HGEMM_TR_VARIANT(TY, DT, TAG, 128, 256, 64, 128, 128, 3, 0.89f),               \
-   HGEMM_TR_VARIANT_PW(TY, DT, TAG, 128, 256, 64, 128, 128, 3, 4, "_p4", 0.88f)}
+   HGEMM_TR_VARIANT_PW(TY, DT, TAG, 128, 256, 64, 128, 128, 3, 4, "_p4", 0.88f),  \
+   HGEMM_TR_VARIANT_PS(TY, DT, TAG, 256, 256, 128, 128, 128, 1.00f)}
 const Variant kVariantsF8[] = HGEMM_TR_F8_TABLE(2, GEMM_DTYPE_F8, "f8");
 const Variant kVariantsE5[] = HGEMM_TR_F8_TABLE(3, GEMM_DTYPE_E5M2, "e5m2");
 

@@ -58,6 +58,13 @@ def wide(x: np.ndarray) -> np.ndarray:
     return x.astype(np.float64)
 
 
+def form_configs(dtype: int):
+    """The variants of `dtype` that have the fused-epilogue, transposed and
+    split-K forms: all but the persistent tiles (names ending in "_ps"),
+    which are plain calls only."""
+    return [c for c in gemm.configs(dtype) if not c.name.decode().endswith("_ps")]
+
+
 def log(msg: str) -> None:
     print(msg, flush=True)
     sys.stdout.flush()

@@ -18,7 +18,7 @@ import pytest
 import oracle
 from dense_gemm_row_amd import gemm, synth
 from tests import golden_data
-from tests.gpu_util import check_full, check_rows, exact_equal, log, rounded, run, wide
+from tests.gpu_util import form_configs, check_full, check_rows, exact_equal, log, rounded, run, wide
 
 pytestmark = pytest.mark.gpu
 
@@ -172,7 +172,7 @@ def test_bf16_random_sampled_full_size(shape):
 
 # --- split-K -----------------------------------------------------------------
 def _split_cfgs():
-    return [c for c in gemm.configs(DT) if c.name.decode().startswith("tr_")]
+    return [c for c in gemm.configs(DT) if c.name.decode().startswith("tr_") and not c.name.decode().endswith("_ps")]
 
 
 @pytest.mark.parametrize("shape", [(200, 136, 1000), (130, 257, 4096), (1, 8, 200)],
@@ -216,7 +216,7 @@ def test_bf16_epilogue_exact_small_int(shape):
     bias = synth.small_int(13, 3, 1, N, -3, 3).ravel()
     cases = [dict(alpha=2.0, beta=-1.0, act=0), dict(alpha=-1.0, beta=0.5, act=1),
              dict(alpha=1.0, beta=0.0, act=1)]
-    for cfg in [c for c in gemm.configs(DT)]:
+    for cfg in form_configs(DT):
         for e in cases:
             log(f"bf16 epilogue exact cfg={cfg.name.decode()} {e} shape={shape}")
             C, _ = run(A, B, cfg, epi=dict(e, C0=C0 if e["beta"] != 0.0 else None, bias=bias))
@@ -248,7 +248,7 @@ def test_bf16_bt_exact_small_int(shape):
     A = synth.small_int(29, 0, M, K, dtype=BF)
     Bt = synth.small_int(29, 1, N, K, dtype=BF)
     ref, _ = oracle.gemm_rows_bt(A, Bt)
-    for cfg in gemm.configs(DT):
+    for cfg in form_configs(DT):
         for pad in ((0, 0, 0), (3, 5, 1)):
             log(f"bf16 bt exact cfg={cfg.name.decode()} shape={shape} pad={pad}")
             C, _ = run(A, Bt, cfg, pad=pad, bt=True)

@@ -25,7 +25,7 @@ import pytest
 import oracle
 from dense_gemm_row_amd import gemm, synth
 from tests import golden_data
-from tests.gpu_util import check_full, check_rows, exact_equal, log, rounded, run, wide
+from tests.gpu_util import form_configs, check_full, check_rows, exact_equal, log, rounded, run, wide
 
 pytestmark = pytest.mark.gpu
 
@@ -262,7 +262,7 @@ def test_f8_random_sampled_full_size(fmt, shape):
 def test_f8_splitk_exact_small_int(fmt, shape):
     M, N, K = shape
     A, B = _ints(fmt, M, N, K, seed=11)
-    for cfg in gemm.configs(fmt.dt):
+    for cfg in form_configs(fmt.dt):
         for splits in (2, 3, 7):
             cfg.splits = splits
             log(f"{fmt.name} split-K exact cfg={cfg.name.decode()} splits={splits} shape={shape}")
@@ -285,7 +285,7 @@ def test_e5m2_splitk_inf_near_a_chunk_boundary():
     ref, _ = oracle.gemm_rows(A, B)
     assert np.all(np.isposinf(ref[:, 37])) and np.isfinite(np.delete(ref, 37, axis=1)).all()
     want = rounded(ref, "e5m2")
-    for cfg in gemm.configs(fmt.dt):
+    for cfg in form_configs(fmt.dt):
         for splits in (1, 5):
             cfg.splits = splits
             log(f"e5m2 split-K Inf cfg={cfg.name.decode()} splits={splits}")
@@ -321,7 +321,7 @@ def test_f8_epilogue_exact_small_int(fmt, shape):
     bias = synth.small_int(13, 3, 1, N, -3, 3).ravel()
     cases = [dict(alpha=2.0, beta=-1.0, act=0), dict(alpha=-1.0, beta=0.5, act=1),
              dict(alpha=1.0, beta=0.0, act=1)]
-    for cfg in gemm.configs(fmt.dt):
+    for cfg in form_configs(fmt.dt):
         for e in cases:
             log(f"{fmt.name} epilogue exact cfg={cfg.name.decode()} {e} shape={shape}")
             C, _ = run(A, B, cfg, epi=dict(e, C0=C0 if e["beta"] != 0.0 else None, bias=bias))
@@ -354,7 +354,7 @@ def test_f8_bt_exact_small_int(fmt, shape):
     A = synth.small_int(29, 0, M, K, dtype=fmt.marker)
     Bt = synth.small_int(29, 1, N, K, dtype=fmt.marker)
     ref, _ = oracle.gemm_rows_bt(A, Bt)
-    for cfg in gemm.configs(fmt.dt):
+    for cfg in form_configs(fmt.dt):
         for pad in ((0, 0, 0), (16, 32, 8)):
             log(f"{fmt.name} bt exact cfg={cfg.name.decode()} shape={shape} pad={pad}")
             C, _ = run(A, Bt, cfg, pad=pad, bt=True)

@@ -205,7 +205,7 @@ def _split_cfgs(kind):
     """Every variant with a split-K form (the LDS-direct families)."""
     pre = "dl_" if kind == "f32" else "tr_"
     dt = gemm.DTYPE_F32 if kind == "f32" else gemm.DTYPE_F16
-    return [c for c in gemm.configs(dt) if c.name.decode().startswith(pre)]
+    return [c for c in gemm.configs(dt) if c.name.decode().startswith(pre) and not c.name.decode().endswith("_ps")]
 
 
 SPLIT_SHAPES = [(200, 136, 1000), (64, 64, 512), (130, 257, 4096), (1, 8, 200)]
@@ -315,7 +315,8 @@ def test_matmul_split_k_on_a_side_stream(as_handle):
 # --------------------------------------------------------------------------
 def _epi_cfgs(kind):
     dt = gemm.DTYPE_F32 if kind == "f32" else gemm.DTYPE_F16
-    return [c for c in gemm.configs(dt) if c.name.decode().startswith(("dl_", "tr_", "mfma_"))]
+    return [c for c in gemm.configs(dt) if c.name.decode().startswith(("dl_", "tr_", "mfma_"))
+            and not c.name.decode().endswith("_ps")]  # the persistent form is plain-only
 
 
 EPI_CASES = [dict(alpha=2.0, beta=-1.0, act=0), dict(alpha=-1.0, beta=0.5, act=1),
@@ -403,7 +404,8 @@ def test_matmul_fused_epilogue():
 
 def _bt_cfgs(kind):
     dt = gemm.DTYPE_F32 if kind == "f32" else gemm.DTYPE_F16
-    return [c for c in gemm.configs(dt) if c.name.decode().startswith(("dl_", "tr_", "mfma_"))]
+    return [c for c in gemm.configs(dt) if c.name.decode().startswith(("dl_", "tr_", "mfma_"))
+            and not c.name.decode().endswith("_ps")]
 
 
 BT_SHAPES = [(1, 1, 1), (2, 3, 5), (31, 33, 17), (127, 129, 65), (130, 257, 96),
