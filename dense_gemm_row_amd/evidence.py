@@ -11,7 +11,7 @@ Inputs are the directories that ``rocprofv3 --output-format csv -o run
 -d <dir>`` writes, laid out under one run directory ``R``:
 
 ====================  ==========================================================
-``R/kt``              ``--kernel-trace --stats`` of ``bench.py --steps 50 --warmup 5``
+``R/kt``              ``--kernel-trace --stats`` of ``bench.py --steps 50 --warmup 5 --no-probes``
                       (``R/kt_bench.log`` holds that run's JSON line)
 ``R/pmc1``            ``--pmc FETCH_SIZE`` of the counter command below
 ``R/pmc2``            ``--pmc WRITE_SIZE TCC_HIT_sum TCC_MISS_sum``
@@ -19,10 +19,14 @@ Inputs are the directories that ``rocprofv3 --output-format csv -o run
 ``R/kts``             kernel trace of the split-K tuner run (``R/kts.log``)
 ``R/kte`` ... ``kta``  kernel traces of ``bench.py --epilogue``, ``--bt``,
                       ``--dtypes f32,bf16``, ``--dtypes f32,f8`` and ``--at``
+``R/probe_bench.log`` ``bench.py --steps 20 --warmup 5`` (with its probes)
+``R/sweep.log``       ``bench.py --sweep --dtypes f32,f16`` (checked)
+``R/ktw``             kernel trace of ``bench.py --sweep --no-check --dtypes
+                      f32,f16,bf16,f8`` (``R/ktw.log`` its lines)
 ====================  ==========================================================
 
 Counter command: ``bench.py --steps 5 --warmup 1 --cpu-budget 0 --no-check
---copy-mib 512 --dtypes f32,f16,bf16,f8``.  Its ``--copy-mib`` block runs a
+--no-probes --copy-mib 512 --dtypes f32,f16,bf16,f8``.  Its ``--copy-mib`` block runs a
 plain copy kernel (``torch.neg`` over 512 MiB of FP32) whose FETCH_SIZE and
 WRITE_SIZE calibrate the two counters to bytes.
 
@@ -46,10 +50,10 @@ SIZE = 4096
 COPY_BYTES = 512 * 2 ** 20
 XCDS, SIMDS = 8, 1024          # MI355X: GRBM_GUI_ACTIVE sums over XCDs; 256 CUs x 4 SIMDs
 HBM_PEAK = 8.0e12              # bytes/s
-COUNTER_CMD = ("python3 -u bench.py --steps 5 --warmup 1 --cpu-budget 0 --no-check --copy-mib 512 "
-               "--dtypes f32,f16,bf16,f8")
+COUNTER_CMD = ("python3 -u bench.py --steps 5 --warmup 1 --cpu-budget 0 --no-check --no-probes "
+               "--copy-mib 512 --dtypes f32,f16,bf16,f8")
 TRACE_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d <out> -o run -- "
-             "python3 -u bench.py --steps 50 --warmup 5")
+             "python3 -u bench.py --steps 50 --warmup 5 --no-probes")
 SQ_PASS = ("SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES SQ_WAVE_CYCLES SQ_INSTS_MFMA SQ_LDS_BANK_CONFLICT "
            "SQ_LDS_IDX_ACTIVE SQ_INSTS_LDS SQ_WAVES GRBM_GUI_ACTIVE")
 PASSES = ("FETCH_SIZE", "WRITE_SIZE TCC_HIT_sum TCC_MISS_sum", SQ_PASS)
@@ -286,17 +290,85 @@ def bench_trace_summary(kt_dir: str, bench_log: str, title: str, argv: str, widt
 # (subdirectory, bench log, title, bench.py arguments, output file, kernel-name width)
 BENCH_TRACES = (
     ("kte", "kte_bench.log", "fused-epilogue GEMM C = relu(A x B + C + bias) at M=N=K=4096",
-     "--epilogue --steps 50 --warmup 5 --cpu-budget 0", "kernel_trace_gemm4096_epilogue.txt", 150),
+     "--epilogue --steps 50 --warmup 5 --cpu-budget 0 --no-probes", "kernel_trace_gemm4096_epilogue.txt", 150),
     ("ktb", "ktb_bench.log", "GEMM with B given transposed (Bt N x K row-major) at M=N=K=4096 (FP32 and FP16)",
-     "--bt --steps 50 --warmup 5 --cpu-budget 0", "kernel_trace_gemm4096_bt.txt", 160),
+     "--bt --steps 50 --warmup 5 --cpu-budget 0 --no-probes", "kernel_trace_gemm4096_bt.txt", 160),
     ("ktf", "ktf_bench.log", "BF16 GEMM (bf16 in, FP32 accumulate, bf16 out) at M=N=K=4096, timed after an "
-     "SGEMM block like the headline HGEMM", "--dtypes f32,bf16 --steps 50 --warmup 5 --cpu-budget 0",
+     "SGEMM block like the headline HGEMM", "--dtypes f32,bf16 --steps 50 --warmup 5 --cpu-budget 0 --no-probes",
      "kernel_trace_bgemm4096.txt", 160),
     ("kt8", "kt8_bench.log", "FP8 E4M3 GEMM (bf16 out) at M=N=K=4096, timed after an SGEMM block like the "
-     "headline HGEMM", "--dtypes f32,f8 --steps 50 --warmup 5 --cpu-budget 0", "kernel_trace_fp8gemm4096.txt", 160),
+     "headline HGEMM", "--dtypes f32,f8 --steps 50 --warmup 5 --cpu-budget 0 --no-probes", "kernel_trace_fp8gemm4096.txt", 160),
     ("kta", "kta_bench.log", "GEMM with A given transposed (At K x M row-major) at M=N=K=4096 (FP32 and FP16)",
-     "--at --steps 50 --warmup 5 --cpu-budget 0", "kernel_trace_gemm4096_at.txt", 160),
+     "--at --steps 50 --warmup 5 --cpu-budget 0 --no-probes", "kernel_trace_gemm4096_at.txt", 160),
 )
+
+
+def probe_summary(bench_log: str) -> list:
+    """The driver's bench command with its probes: per kernel, the clock and
+    timeline of the traced launch, and the matrix-core ceiling of the same
+    instruction with no memory traffic; the SIMT ablation."""
+    bj = bench_record(bench_log)
+    out = ["# Launch traces and matrix-core ceilings at M=N=K=4096, one MI355X: bench.py's probes.",
+           "# command (repo root): python3 -u bench.py --steps 20 --warmup 5",
+           f"# summary: {SUMMARY_CMD}",
+           "# clock: d(s_memtime) / d(s_memrealtime) x 100 MHz over each workgroup's K loop in one traced",
+           "# launch (gemm_trace_set) inside a block of 20; fill = entry to first K slice in LDS; epilogue =",
+           "# loop end to C issued; spread = last minus first loop end over workgroups.  ceiling = the",
+           "# register-only matrix-core stream of the same instruction (gemm_probe_mfma) and its clock."]
+    for k, v in bj["kernels"].items():
+        t = v.get("trace_us", {})
+        out.append(f"{k} variant={v['variant']} ms_mean={v['ms_mean']} tflops={v['tflops']} "
+                   f"pct_peak={v['pct_peak']} clock_mhz={v.get('clock_mhz')} "
+                   f"(min {v.get('clock_mhz_min')} max {v.get('clock_mhz_max')}) "
+                   f"loop_kcycles(min,mean,max)={v.get('loop_kcycles')} fill_us={t.get('fill')} "
+                   f"loop_us={t.get('loop')} (min {t.get('loop_min')} max {t.get('loop_max')}) "
+                   f"epilogue_us={t.get('epilogue')} loop_end_spread_us={t.get('loop_end_spread')} "
+                   f"span_us={t.get('span')} ceiling_tflops={v.get('mfma_ceiling_tflops')} "
+                   f"ceiling_clock_mhz={v.get('mfma_ceiling_clock_mhz')} frac_of_ceiling={v.get('frac_of_ceiling')}")
+    ab = (bj.get("ablation") or {}).get("simt_f32")
+    if ab:
+        out.append(f"simt_f32 variant={ab['variant']} ms_mean={ab['ms_mean']} tflops={ab['tflops']} "
+                   f"pct_fp32_matrix_peak={ab['pct_fp32_matrix_peak']} pct_fp32_vector_peak="
+                   f"{ab['pct_fp32_vector_peak']} mfma_kernel_speedup={ab['mfma_kernel_speedup']}")
+    out.append(f"# bench value={bj['value']} {bj['unit']} ms_per_step={bj['ms_per_step']} "
+               f"cpu_baseline={json.dumps(bj.get('cpu_baseline'))}")
+    return out
+
+
+def sweep_summary(sweep_log: str, ktw_dir: str | None = None, ktw_log: str | None = None) -> list:
+    """The measurement plan's configurations: bench.py --sweep's lines (each
+    checked on every element against the oracle first), and, when given,
+    the kernel trace of an unchecked sweep."""
+    out = ["# The measurement plan's configurations, one MI355X: python3 -u bench.py --sweep --dtypes f32,f16",
+           "# (every element checked against the oracle on the host's granted cores before timing; 50 timed",
+           "# launches, 20 at 4096x11008x4096, each between its own HIP events; TFLOP/s from the median).",
+           f"# summary: {SUMMARY_CMD}",
+           "# dtype M N K config splits t_median_ms t_mean_ms t_min_ms tflops pct_peak clock_mhz max_rel_err "
+           "tol oracle_s oracle_threads oracle_s_1thread"]
+    with open(sweep_log) as f:
+        for line in f:
+            if not line.startswith("{"):
+                continue
+            d = json.loads(line)
+            out.append(" ".join(str(d.get(k)) for k in (
+                "dtype", "M", "N", "K", "config", "splits", "t_median_ms", "t_mean_ms", "t_min_ms", "tflops",
+                "pct_peak", "gpu_clock_mhz", "max_rel_err", "tol", "oracle_s", "oracle_threads",
+                "oracle_s_1thread")))
+    if ktw_dir and os.path.isdir(ktw_dir):
+        out += ["# rocprofv3 kernel-trace statistics of the unchecked sweep of all four types:",
+                "# command (repo root): rocprofv3 --kernel-trace --stats --output-format csv -d <out> -o run -- "
+                "python3 -u bench.py --sweep --no-check --dtypes f32,f16,bf16,f8",
+                f"#   {'calls':>5} {'avg_us':>10} {'min_us':>10} {'max_us':>10}  kernel"]
+        out += _stats_rows(os.path.join(ktw_dir, "run_kernel_stats.csv"), only_gemm=True, width=170)
+        if ktw_log and os.path.exists(ktw_log):
+            out.append("# that run's lines (TFLOP/s under the profiler):")
+            with open(ktw_log) as f:
+                for line in f:
+                    if line.startswith("{"):
+                        d = json.loads(line)
+                        out.append(f"#   {d['dtype']} {d['M']}x{d['N']}x{d['K']} {d['config']} splits={d['splits']} "
+                                   f"tflops={d['tflops']}")
+    return out
 
 
 def evidence_records(trace_stats: dict, bench: dict, counters: dict) -> list:
@@ -351,6 +423,11 @@ def main(argv=None) -> int:
                 tstats.setdefault(fam, launch_stats(launches))
             for k, v in bench_record(os.path.join(R, log))["kernels"].items():
                 kernels.setdefault(k, v)
+    if os.path.exists(os.path.join(R, "probe_bench.log")):
+        write("launch_trace_gemm4096.txt", probe_summary(os.path.join(R, "probe_bench.log")))
+    if os.path.exists(os.path.join(R, "sweep.log")):
+        write("sweep_gemm.txt", sweep_summary(os.path.join(R, "sweep.log"), os.path.join(R, "ktw"),
+                                              os.path.join(R, "ktw.log")))
     lines = [f"# Evidence per default kernel at M=N=K={SIZE}, one MI355X: one JSON record per line.",
              "# Time: the kernel trace's timed launches; rate: bench.py's HIP events; counters, traffic and",
              "# l2_hit: the --pmc passes of hbm_traffic.txt and mfma_lds_counters_gemm4096.txt; hbm_GBps =",
