@@ -156,6 +156,20 @@ __device__ __forceinline__ f32x16_t mfma16(h16x8_t a, h16x8_t b, f32x16_t c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
+// The 16 x 16 instruction on the same operand registers (twice the k per
+// instruction, a quarter of the accumulators): v_mfma_f32_16x16x32_f16 /
+// _bf16, picked by the accumulator type.
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+template <bool BF>
+__device__ __forceinline__ f32x4_t mfma16(h16x8_t a, h16x8_t b, f32x4_t c) {
+  if constexpr (BF)
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(b16x8_t, a),
+                                                    __builtin_bit_cast(b16x8_t, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
 // FP8 operands, 32 per lane (k 64 per instruction):
 // v_mfma_f32_32x32x64_f8f6f4 with both operand-format fields FMT (0: OCP
 // E4M3, 1: OCP E5M2) and no block scales (the scaled builtin with zero
@@ -167,6 +181,13 @@ template <int FMT>
 __device__ __forceinline__ f32x16_t mfma_f8(i32x8_t a, i32x8_t b, f32x16_t c) {
   static_assert(FMT == 0 || FMT == 1, "E4M3 or E5M2");
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FMT, FMT, 0, 0, 0, 0);
+}
+
+// The 16 x 16 form, k 128 per instruction: v_mfma_f32_16x16x128_f8f6f4.
+template <int FMT>
+__device__ __forceinline__ f32x4_t mfma_f8(i32x8_t a, i32x8_t b, f32x4_t c) {
+  static_assert(FMT == 0 || FMT == 1, "E4M3 or E5M2");
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, FMT, FMT, 0, 0, 0, 0);
 }
 
 // float -> 16-bit pattern, rounded to nearest even (v_cvt_f16_f32 or

@@ -113,25 +113,37 @@ __device__ __forceinline__ void static_for(F&& f, std::integer_sequence<int, I..
 //   directions (section 10.3), with LDS-direct copies in the role that
 //   "nxbn.cn GB300 GEMM" (section 3.2) gives to a copy engine driven by a
 //   few threads.
+// * MI_: the matrix instruction's output block, 32 (32 x 32, k 16 or 64)
+//   or 16 (16 x 16, twice the k: v_mfma_f32_16x16x32_f16 / _bf16,
+//   v_mfma_f32_16x16x128_f8f6f4).  Both take the same operand registers
+//   (8 16-bit or 32 8-bit k values per lane) and do the same work per
+//   cycle, but under MI355X's power limit the 16 x 16 stream runs at a
+//   higher clock (register-only rate on the device: FP16 about 1960 against
+//   1735 TFLOP/s, FP8 4640 against 4255).  A 16 x 16 block's operand lane l
+//   holds row (column) l%16 and k run l/16 of four; its accumulator
+//   register r holds output row 4(l/16) + r, column l%16.
 template <int BM_, int BN_, int WM_, int WN_, int BK_, int NS_, int MODE_ = 0, bool BT_ = false,
-          int TY_ = 0, bool AT_ = false, int PW_ = 0>
+          int TY_ = 0, bool AT_ = false, int PW_ = 0, int MI_ = 32>
 struct Shape {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BK_, NS = NS_, TY = TY_;
-  static constexpr int PW = PW_;
+  static constexpr int PW = PW_, MI = MI_;
   static constexpr bool AT = AT_;
   static constexpr bool PARTIAL = MODE_ == 1, EPI = MODE_ == 2 || MODE_ == 3, Q8 = MODE_ == 3, BT = BT_;
   static constexpr bool BF = TY != 0;   // C (and the epilogue's old C) is bfloat16
   static constexpr bool F8 = TY >= 2;   // A and B are FP8 (E4M3, or E5M2 when TY == 3)
   static constexpr int ES = F8 ? 1 : 2;    // input element bytes
   static constexpr int CE = 16 / ES;       // input elements per 16-byte chunk
-  static constexpr int KW = F8 ? 64 : 16;  // k per MFMA
+  static_assert(MI == 32 || MI == 16, "matrix instruction");
+  static constexpr int KW = (F8 ? 64 : 16) * (32 / MI);  // k per MFMA
+  static constexpr int LG = 64 / MI, KL = KW / LG;  // lane groups along k; k per lane
+  static constexpr int AR = MI * MI / 64, RQ = AR / 4;  // accumulators per block; 4-column groups
   static constexpr int FR = F8 ? 2 : 1;    // 16-byte chunks per lane in an A / Bt operand
   static constexpr int TRN = F8 ? 4 : 2;   // transpose reads per B operand
   static constexpr int RR = F8 ? 8 : 4;    // k rows (elements per lane) of one transpose read
   static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN, NW = WAVES_M * WAVES_N;
   // NL waves issue the copies: the producers, or every wave.
   static constexpr int NL = PW > 0 ? PW : NW, NT = (NW + PW) * 64;
-  static constexpr int MB = WM / 32, NB = WN / 32, KS = BK / KW;
+  static constexpr int MB = WM / MI, NB = WN / MI, KS = BK / KW;
   static constexpr int NMMA_ = MB * NB;  // MFMAs per k step
   // A rows: BM rows of BK k values, or (AT) BK rows of BM values.
   static constexpr int A_ROW = AT ? BM * ES : BK * ES, A_CPR = A_ROW / 16;  // bytes / chunks
@@ -154,6 +166,7 @@ struct Shape {
   // The persistent form's wave-private epilogue staging: 32 rows.
   static constexpr int PS_EPI_BYTES = 32 * EPI_ROW;
   static_assert(F8 ? (BK == 64 || BK == 128) : (BK == 32 || BK == 64), "K slice");
+  static_assert(BK % KW == 0, "whole matrix instructions per K slice");
   // Fragments alternate between two register sets by global k step
   // (slice * KS + step); the slice loop is unrolled NS times, so the set of
   // each step is static when NS * KS is even.
@@ -162,6 +175,8 @@ struct Shape {
   static_assert(NS >= 2 && NS <= MAX_STAGES, "stages");
   static_assert(BM % WM == 0 && BN % WN == 0, "wave grid");
   static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile");
+  // The 16 x 16 epilogue staging XORs 16-byte chunks by the row's low 4 bits.
+  static_assert(MI == 32 || WN * 2 >= 256, "16 x 16 blocks: wave tiles at least 128 wide");
   static_assert(A_STAGE % (1024 * NL) == 0 && B_STAGE % (1024 * NL) == 0, "direct-load split");
   // A compute wave and a producer wave share a SIMD, so the compute waves
   // must fit half of its 512 registers: wave tiles of at most 128 x 64.
@@ -178,15 +193,20 @@ struct Shape {
   static_assert(P >= 1 && WM % P == 0 && RPA % 32 == 0 && RPA % EPI_RPI == 0 &&
                 RPA * EPI_ROW <= A_STAGE && RPA * EPI_ROW <= B_STAGE, "epilogue staging");
   // Fragment reads use a per-lane base plus immediate offsets (< 64 KB).
-  static_assert((AT ? (BK - KW + RR * (TRN - 1)) * A_ROW : (MB - 1) * 32 * A_ROW) < 65536 &&
-                (BK - KW + RR * (TRN - 1)) * B_ROW < 65536 && (NB - 1) * 32 * B_ROW < 65536,
+  static_assert((AT ? (BK - KW + RR * (TRN - 1)) * A_ROW : (MB - 1) * MI * A_ROW) < 65536 &&
+                (BK - KW + RR * (TRN - 1)) * B_ROW < 65536 && (NB - 1) * MI * B_ROW < 65536,
                 "immediate offsets");
 
   // Byte offsets within one stage array.
   __host__ __device__ static constexpr int a_byte(int r, int q) { return swz_off(r, q, A_ROW); }
   // B chunk XOR: the rows one transpose read touches (4 for 16-bit, 8 for
-  // 8-bit) land on distinct 16-byte (32-byte) bank slots.
-  __host__ __device__ static constexpr int b_swz(int k) { return F8 ? 2 * (k % 8) : 4 * (k % 4); }
+  // 8-bit) land on distinct 16-byte (32-byte) bank slots.  With 16 x 16
+  // blocks the second 16 lanes of a read take the next k run (KL rows on)
+  // of the same columns instead of the next 16 columns, so the run's
+  // parity also flips one chunk-index bit.
+  __host__ __device__ static constexpr int b_swz(int k) {
+    return (F8 ? 2 * (k % 8) : 4 * (k % 4)) ^ (MI == 16 ? (F8 ? 1 : 2) * ((k / KL) % 2) : 0);
+  }
   __host__ __device__ static constexpr int b_phys(int k, int c) { return c ^ b_swz(k); }
   __host__ __device__ static constexpr int b_byte(int k, int n) {
     return k * B_ROW + 16 * b_phys(k, n / CE) + ES * (n % CE);
@@ -205,19 +225,19 @@ struct Shape {
     return ((1024 * (i * NL + w) + 16 * l) % B_ROW / 16) ^ b_swz(b_dl_k(i, w, l));
   }
   // Fragment reads for k step j of a slice.  Lane l's operand holds k
-  // KW*j + (KW/2)*(l/32) + 0 .. KW/2-1 (any k order common to both operands
+  // KW*j + KL*(l/MI) + 0 .. KL-1 (any k order common to both operands
   // gives the same product; this one keeps each lane's k run contiguous).
-  //  B_op (A values): lane reads row wm0 + 32mb + l%32, chunks
-  //  FR*(2j + l/32) + part.
+  //  B_op (A values): lane reads row wm0 + MI*mb + l%MI, chunks
+  //  FR*(LG*j + l/MI) + part.
   __host__ __device__ static constexpr int a_frag(int wm0, int mb, int j, int l, int part = 0) {
-    return a_byte(wm0 + 32 * mb + l % 32, FR * (2 * j + l / 32) + part);
+    return a_byte(wm0 + MI * mb + l % MI, FR * (LG * j + l / MI) + part);
   }
   //  A_op (B values, transpose read jr of TRN): lane LPR*t + q of 16-lane
-  //  group g (LPR = 16/RR lanes per row) points at row KW*j + (KW/2)h +
-  //  RR*jr + t, columns wn0 + 32nb + 16(g%2) + (8/ES)q.
+  //  group g (LPR = 16/RR lanes per row) points at row KW*j + KL*(l/MI) +
+  //  RR*jr + t, columns wn0 + MI*nb + 16((l%MI)/16) + (8/ES)q.
   __host__ __device__ static constexpr int b_frag(int wn0, int nb, int j, int jr, int l) {
-    return b_byte(KW * j + (KW / 2) * (l / 32) + RR * jr + (l % 16) / (16 / RR),
-                  wn0 + 32 * nb + 16 * ((l / 16) % 2) + (8 / ES) * (l % (16 / RR)));
+    return b_byte(KW * j + KL * (l / MI) + RR * jr + (l % 16) / (16 / RR),
+                  wn0 + MI * nb + 16 * ((l % MI) / 16) + (8 / ES) * (l % (16 / RR)));
   }
   // AT: A^T tile row k, value m (B's layout with BM values per row); the
   // direct loads; the transpose read jr of k step j for row block mb
@@ -232,8 +252,8 @@ struct Shape {
     return ((1024 * (i * NL + w) + 16 * l) % A_ROW / 16) ^ b_swz(at_dl_k(i, w, l));
   }
   __host__ __device__ static constexpr int at_frag(int wm0, int mb, int j, int jr, int l) {
-    return at_byte(KW * j + (KW / 2) * (l / 32) + RR * jr + (l % 16) / (16 / RR),
-                   wm0 + 32 * mb + 16 * ((l / 16) % 2) + (8 / ES) * (l % (16 / RR)));
+    return at_byte(KW * j + KL * (l / MI) + RR * jr + (l % 16) / (16 / RR),
+                   wm0 + MI * mb + 16 * ((l % MI) / 16) + (8 / ES) * (l % (16 / RR)));
   }
   // BT direct loads: Bt rows (B_ROW bytes) placed like row-major A's rows,
   // by B's own row length (with A transposed the two differ).
@@ -244,18 +264,39 @@ struct Shape {
     return (l % (B_ROW / 16)) ^ swz_row(bt_dl_row(i, w, l), B_ROW);
   }
   // BT: B tile row n (one output column), 16-byte k chunk q, placed and read
-  // with A's maps (B_ROW == A_ROW): lane reads column wn0 + 32nb + l%32,
-  // chunks FR*(2j + l/32) + part of k step j (the MFMA A operand of C^T
+  // with A's maps (B_ROW == A_ROW): lane reads column wn0 + MI*nb + l%MI,
+  // chunks FR*(LG*j + l/MI) + part of k step j (the MFMA A operand of C^T
   // directly).
   __host__ __device__ static constexpr int bt_byte(int n, int q) { return swz_off(n, q, B_ROW); }
   __host__ __device__ static constexpr int bt_frag(int wn0, int nb, int j, int l, int part = 0) {
-    return bt_byte(wn0 + 32 * nb + l % 32, FR * (2 * j + l / 32) + part);
+    return bt_byte(wn0 + MI * nb + l % MI, FR * (LG * j + l / MI) + part);
   }
+  // Accumulator block (nb, mb), register 4rq + e of lane l: C[m][n] with
+  // m = MI*mb + l%MI and n = MI*nb + 8rq + 4(l/MI) + e (wave-tile
+  // coordinates): four consecutive columns of one row per register group.
+  __host__ __device__ static constexpr int acc_row(int mb, int l) { return MI * mb + l % MI; }
+  __host__ __device__ static constexpr int acc_col(int nb, int rq, int l) { return MI * nb + 8 * rq + 4 * (l / MI); }
   // Epilogue staging: 8-byte slot s (columns 4s..4s+3) of local row m of an
-  // array, XOR-swizzled by the row so that the 32 rows written by one
-  // instruction hit 32 different bank pairs; read back 8 bytes at a time.
+  // array, XOR-swizzled by the row so that the rows written by one
+  // instruction hit different bank pairs (32 rows of one slot for 32 x 32
+  // blocks; 16 rows of two adjacent slots for 16 x 16 blocks, so there the
+  // 16-byte chunk is XORed by the row's low 4 bits); read back 8 bytes at a
+  // time.
   __host__ __device__ static constexpr int epi_byte(int m, int s) {
-    return m * EPI_ROW + 8 * (s ^ (m % EPI_SPR));
+    return MI == 32 ? m * EPI_ROW + 8 * (s ^ (m % EPI_SPR))
+                    : m * EPI_ROW + 16 * ((s / 2) ^ (m % 16)) + 8 * (s % 2);
+  }
+  // Read back 16-byte chunk c (columns 8c..8c+7) of local row m: two
+  // 8-byte slots, or with 16 x 16 blocks one 16-byte read (the slots are
+  // adjacent there).
+  __device__ static u32x4 epi_chunk(const unsigned char* base, int m, int c) {
+    if constexpr (MI == 16) {
+      return *reinterpret_cast<const u32x4*>(base + epi_byte(m, 2 * c));
+    } else {
+      const uint2 lo = *reinterpret_cast<const uint2*>(base + epi_byte(m, 2 * c));
+      const uint2 hi = *reinterpret_cast<const uint2*>(base + epi_byte(m, 2 * c + 1));
+      return u32x4{lo.x, lo.y, hi.x, hi.y};
+    }
   }
   // Fused-epilogue staging (FP32, two passes of WM/2 rows in the same
   // region): R32 rows per array, 16-byte chunk q of local row m at chunk
@@ -299,6 +340,34 @@ __device__ __forceinline__ void loop_barrier() {
 }
 #define SGB(mask, n) __builtin_amdgcn_sched_group_barrier((mask), (n), 0)
 
+// The 16 x 16 matrix instruction for 16-bit operands as inline assembly,
+// its accumulator tied in place ("+a").  With the builtin, the register
+// allocator kept reassigning the 64 four-register accumulators of a
+// 128 x 128 wave tile and moved most of them between registers on every
+// pass of the K loop (hundreds of extra instructions per slice); tied
+// operands keep each in its registers.  The compiler's hazard checks do
+// not see into the assembly, so the kernels (a) write the accumulators
+// only before a guard (mfma_guard) that precedes the first MFMA, read them
+// only after one that follows the last, and (b) feed srcA / srcB only from
+// LDS reads, whose arrival the compiler's own waits cover.
+template <int TY>
+__device__ __forceinline__ void mfma16_asm(f32x4& c, const f16x8& a, const f16x8& b) {
+  static_assert(TY == 0 || TY == 1, "16-bit operands");
+  if constexpr (TY == 0)
+    asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+  else
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
+
+// 24 wait states, with nothing scheduled across: more than any matrix-core
+// hazard of gfx950 needs (an XDL result read by a vector instruction, the
+// longest, needs under 20).
+__device__ __forceinline__ void mfma_guard() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // Issue the LDS-direct copies of K slice s into one stage.  The buffer
 // descriptors start at the slice (base moved by s*BK along k) and end at the
 // matrix end, so rows past K (and anything past the last element) load as
@@ -327,6 +396,49 @@ __device__ __forceinline__ void issue_slice(const unsigned char* Ab, const unsig
       lds_void* dst = (lds_void*)(lds_b + 1024 * ((q - S::IA) * S::NL + wave));
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, dst, 16, b_vo[q - S::IA], 0, 0, 0);
     }
+  }
+}
+
+// Copy q alone of the persistent kernel's slice s (issue_slice_ps's copy q).
+template <class S>
+__device__ __forceinline__ void issue_copy_ps(const unsigned char* Ab, const unsigned char* Bb,
+                                              int64_t a_bytes, int64_t b_bytes, int s, bool live,
+                                              bool last, const unsigned* a_vo, unsigned a_tail,
+                                              const unsigned* b_vo, unsigned char* lds_a,
+                                              unsigned char* lds_b, int wave, int lda, int ldb, int q) {
+  if (q < S::IA) {
+    const int64_t ka = S::ES * (int64_t)s * S::BK;
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(Ab + ka, live ? a_bytes - ka : 0);
+    lds_void* dst = (lds_void*)(lds_a + 1024 * (q * S::NL + wave));
+    const unsigned off = (last && !((a_tail >> q) & 1u)) ? OOB : a_vo[q];
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, dst, 16, off, 0, 0, 0);
+  } else {
+    const int64_t kb = (int64_t)s * S::BK * ldb * S::ES;
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bb + kb, live ? b_bytes - kb : 0);
+    lds_void* dst = (lds_void*)(lds_b + 1024 * ((q - S::IA) * S::NL + wave));
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, dst, 16, b_vo[q - S::IA], 0, 0, 0);
+  }
+}
+
+// Copy q alone of slice s (issue_slice's copy q), for the 16 x 16 K loop,
+// which places each copy between two MFMAs.  (Its own function: see
+// issue_slice_ps.)
+template <class S>
+__device__ __forceinline__ void issue_copy(const unsigned char* Ab, const unsigned char* Bb,
+                                           int64_t a_bytes, int64_t b_bytes, int s, bool live,
+                                           const unsigned* a_vo, const unsigned* b_vo,
+                                           unsigned char* lds_a, unsigned char* lds_b, int wave,
+                                           int lda, int ldb, int q) {
+  const int64_t ka = S::AT ? (int64_t)s * S::BK * lda * S::ES : S::ES * (int64_t)s * S::BK;
+  const int64_t kb = S::BT ? S::ES * (int64_t)s * S::BK : (int64_t)s * S::BK * ldb * S::ES;
+  if (q < S::IA) {
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(Ab + ka, live ? a_bytes - ka : 0);
+    lds_void* dst = (lds_void*)(lds_a + 1024 * (q * S::NL + wave));
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, dst, 16, a_vo[q], 0, 0, 0);
+  } else {
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bb + kb, live ? b_bytes - kb : 0);
+    lds_void* dst = (lds_void*)(lds_b + 1024 * ((q - S::IA) * S::NL + wave));
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, dst, 16, b_vo[q - S::IA], 0, 0, 0);
   }
 }
 
@@ -553,52 +665,49 @@ hgemm_tr_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
       return Frag(__builtin_bit_cast(f16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7)));
     }
   };
+  // The operands of k step j: A's row block mb, B's column block nb.
+  auto load_a = [&](int buf, const unsigned char* la, int j, int mb) __attribute__((always_inline)) {
+    if constexpr (S::AT)
+      fa[buf][mb] = tr_operand(la + a_fb[mb] + S::KW * j * S::A_ROW, S::A_ROW);
+    else if constexpr (S::F8)
+      fa[buf][mb] = two_chunks(la + a_fb[2 * j] + mb * S::MI * S::A_ROW, la + a_fb[2 * j + 1] + mb * S::MI * S::A_ROW);
+    else
+      fa[buf][mb] = *(const lds_f16x8*)(la + a_fb[j] + mb * S::MI * S::A_ROW);
+  };
+  auto load_b = [&](int buf, const unsigned char* lb, int j, int nb) __attribute__((always_inline)) {
+    if constexpr (!S::BT)
+      fb[buf][nb] = tr_operand(lb + b_fb[nb] + S::KW * j * S::B_ROW, S::B_ROW);
+    else if constexpr (S::F8)
+      fb[buf][nb] = two_chunks(lb + b_fb[2 * j] + nb * S::MI * S::B_ROW, lb + b_fb[2 * j + 1] + nb * S::MI * S::B_ROW);
+    else
+      fb[buf][nb] = *(const lds_f16x8*)(lb + b_fb[j] + nb * S::MI * S::B_ROW);
+  };
   auto load_frags = [&](int buf, const unsigned char* la, const unsigned char* lb, int j)
       __attribute__((always_inline)) {
-    if constexpr (S::AT) {
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) fa[buf][mb] = tr_operand(la + a_fb[mb] + S::KW * j * S::A_ROW, S::A_ROW);
-    }
-    if constexpr (S::F8) {
-      if constexpr (!S::AT) {
+    for (int mb = 0; mb < MB; ++mb) load_a(buf, la, j, mb);
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-          fa[buf][mb] = two_chunks(la + a_fb[2 * j] + mb * 32 * S::A_ROW, la + a_fb[2 * j + 1] + mb * 32 * S::A_ROW);
-      }
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        if constexpr (S::BT) {
-          fb[buf][nb] = two_chunks(lb + b_fb[2 * j] + nb * 32 * S::B_ROW, lb + b_fb[2 * j + 1] + nb * 32 * S::B_ROW);
-        } else {
-          fb[buf][nb] = tr_operand(lb + b_fb[nb] + S::KW * j * S::B_ROW, S::B_ROW);
-        }
-      }
-      return;
-    } else {
-    if constexpr (!S::AT) {
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-        fa[buf][mb] = *(const lds_f16x8*)(la + a_fb[j] + mb * 32 * S::A_ROW);
-    }
-    if constexpr (S::BT) {
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-        fb[buf][nb] = *(const lds_f16x8*)(lb + b_fb[j] + nb * 32 * S::B_ROW);
-    } else {
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) fb[buf][nb] = tr_operand(lb + b_fb[nb] + 16 * j * S::B_ROW, S::B_ROW);
-    }
-    }
+    for (int nb = 0; nb < NB; ++nb) load_b(buf, lb, j, nb);
   };
 
   // acc[nb][mb]: block of C^T (rows n, columns m).
-  f32x16 acc[NB][MB];
+  typedef std::conditional_t<S::MI == 32, f32x16, f32x4> Acc;
+  Acc acc[NB][MB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[nb][mb][r] = 0.f;
+      for (int r = 0; r < S::AR; ++r) acc[nb][mb][r] = 0.f;
+  // 16 x 16 blocks: the zeros are in the accumulator registers before the
+  // hazard guard, and the first MFMA comes after it (see mfma16_asm).
+  if constexpr (S::MI == 16) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) asm volatile("" : "+a"(acc[nb][mb]));
+    mfma_guard();
+  }
   auto mma = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
@@ -609,6 +718,31 @@ hgemm_tr_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
         else
           acc[nb][mb] = mfma16<S::BF>(fb[buf][nb], fa[buf][mb], acc[nb][mb]);
       }
+  };
+
+  // 16 x 16 blocks: k step `cur` as a fixed sequence, MFMA i on block
+  // (i / MB, i % MB), with scheduling barriers between them that place the
+  // next step's operand reads (rd(f) after MFMA 4f: A's MB operands first,
+  // which the next step's first MFMAs need, then B's) and the copies
+  // (cp(q) after MFMA q).  The builtin's scheduling groups cannot place
+  // inline assembly.
+  auto mma16 = [&](int cur, auto&& rd, auto&& cp) __attribute__((always_inline)) {
+    if constexpr (S::MI == 16 && !S::F8) {
+      static_for([&](auto I) __attribute__((always_inline)) {
+        constexpr int i = decltype(I)::value;
+        mfma16_asm<S::TY>(acc[i / MB][i % MB], fb[cur][i / MB], fa[cur][i % MB]);
+        if constexpr (i % 4 == 0 && i / 4 < MB + NB) rd(IC<i / 4>{});
+        cp(IC<i>{});
+        __builtin_amdgcn_sched_barrier(0);
+      }, std::make_integer_sequence<int, MB * NB>{});
+    }
+  };
+  // Operand f of k step j (f < MB: A's block f; else B's block f - MB).
+  auto rd_op = [&](int buf, const unsigned char* la, const unsigned char* lb, int j, auto F)
+      __attribute__((always_inline)) {
+    constexpr int f = decltype(F)::value;
+    if constexpr (f < MB) load_a(buf, la, j, f);
+    else load_b(buf, lb, j, f - MB);
   };
 
   // (The lambdas are forced inline: an out-of-line call would move the
@@ -623,6 +757,32 @@ hgemm_tr_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
     constexpr int c = decltype(C_)::value, n = (c + 1) % NS, f = (c + NS - 1) % NS;
     unsigned char* ca = A_of(IC<c>{});
     unsigned char* cb = B_of(IC<c>{});
+    if constexpr (S::MI == 16) {
+      static_assert(!S::SPREAD && S::PW == 0, "16 x 16 blocks: two stages, no producer waves");
+      // Steps 0..KS-2 with the next step's operands read from stage c.
+      static_for([&](auto J) __attribute__((always_inline)) {
+        constexpr int j = decltype(J)::value;
+        mma16(S::frag_set(c, j),
+              [&](auto F) __attribute__((always_inline)) { rd_op(S::frag_set(c, j + 1), ca, cb, j + 1, F); },
+              [](auto) {});
+      }, std::make_integer_sequence<int, KS - 1>{});
+      loop_barrier<(NS - 2) * S::LPS>();
+      __builtin_amdgcn_sched_barrier(0);
+      // Last step: slice t+NS's copies into stage c, one after each of the
+      // first LPS MFMAs, and the next stage's first operands.
+      mma16(S::frag_set(c, KS - 1),
+            [&](auto F) __attribute__((always_inline)) {
+              rd_op(S::frag_set(c + 1, 0), A_of(IC<n>{}), B_of(IC<n>{}), 0, F);
+            },
+            [&](auto Q) __attribute__((always_inline)) {
+              constexpr int q = decltype(Q)::value;
+              if constexpr (q < S::LPS)
+                issue_copy<S>(Ab, Bb, a_bytes, b_bytes, t + NS, t + NS < T,
+                              t + NS == T - 1 ? a_vo_tail : a_vo, t + NS == T - 1 ? b_vo_tail : b_vo,
+                              ca, cb, lw, lda, ldb, q);
+            });
+      return;
+    }
     static_for([&](auto J) __attribute__((always_inline)) {
       constexpr int j = decltype(J)::value;
       load_frags(S::frag_set(c, j + 1), ca, cb, j + 1);
@@ -679,27 +839,36 @@ hgemm_tr_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
     int t = 0;
     for (; t + NS <= T; t += NS)
       static_for([&](auto I) { slice(t + decltype(I)::value, I); }, std::make_integer_sequence<int, NS>{});
-    static_for([&](auto I) { if (t + decltype(I)::value < T) slice(t + decltype(I)::value, I); },
-               std::make_integer_sequence<int, NS>{});
+    // (16 x 16 blocks: guards wherever control flow joins after MFMAs.)
+    if constexpr (S::MI == 16) mfma_guard();
+    static_for([&](auto I) {
+      if (t + decltype(I)::value < T) {
+        slice(t + decltype(I)::value, I);
+        if constexpr (S::MI == 16) mfma_guard();
+      }
+    }, std::make_integer_sequence<int, NS>{});
     // The copies of the slices past T (out of range: they write zeros)
     // must land before the epilogue reuses the LDS.
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    if constexpr (S::MI == 16) mfma_guard();
   }
+  if constexpr (S::MI == 16) mfma_guard();  // the last MFMA's results
   trace_stamp(p, 2);
   if constexpr (S::PARTIAL) {
     // Split-K partial: FP32 C (the workspace) written straight from the
     // accumulators, no FP16 rounding, no LDS round trip.
-    // acc[nb][mb] register 4rq+e of lane l is C[m][n], m = wm0 + 32mb +
-    // l%32, n = wn0 + 32nb + 8rq + 4(l/32) + e: one 16-byte store each.
+    // acc[nb][mb] register 4rq+e of lane l is C[m][n], m = wm0 +
+    // acc_row(mb, l), n = wn0 + acc_col(nb, rq, l) + e: one 16-byte store
+    // each.
     float* __restrict__ Cf = static_cast<float*>(p.C) + sk * p.c_stride;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int rq = 0; rq < 4; ++rq) {
-          const int row = m0 + wm0 + 32 * mb + l % 32;
-          const int col = n0 + wn0 + 32 * nb + 8 * rq + 4 * (l / 32);
+        for (int rq = 0; rq < S::RQ; ++rq) {
+          const int row = m0 + wm0 + S::acc_row(mb, l);
+          const int col = n0 + wn0 + S::acc_col(nb, rq, l);
           if (row < M && col < N) {
             f32x4 v = {acc[nb][mb][4 * rq], acc[nb][mb][4 * rq + 1], acc[nb][mb][4 * rq + 2],
                        acc[nb][mb][4 * rq + 3]};
@@ -711,8 +880,8 @@ hgemm_tr_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
   }
   __syncthreads();
 
-  // Epilogue.  acc[nb][mb] register r of lane l holds C[m][n] with
-  // m = wm0 + 32mb + l%32 and n = wn0 + 32nb + 8(r/4) + 4(l/32) + r%4: four
+  // Epilogue.  acc[nb][mb] register 4rq + e of lane l holds C[m][n] with
+  // m = wm0 + acc_row(mb, l) and n = wn0 + acc_col(nb, rq, l) + e: four
   // consecutive columns per register group.  Stage the wave's FP16 tile in
   // its P arrays (row-major, 8-byte slots swizzled by row), then write it
   // out in 16-byte row chunks.
@@ -751,9 +920,9 @@ hgemm_tr_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
 #pragma unroll
         for (int mbl = 0; mbl < MB / 2; ++mbl)
 #pragma unroll
-          for (int rq = 0; rq < 4; ++rq) {
+          for (int rq = 0; rq < S::RQ; ++rq) {
             const int mb = pass * (MB / 2) + mbl;
-            const int m = 32 * mbl + l % 32, q = 8 * nb + 2 * rq + l / 32;
+            const int m = S::acc_row(mbl, l), q = S::acc_col(nb, rq, l) / 4;
             f32x4 v = {acc[nb][mb][4 * rq], acc[nb][mb][4 * rq + 1], acc[nb][mb][4 * rq + 2],
                        acc[nb][mb][4 * rq + 3]};
             *reinterpret_cast<f32x4*>(ep[m / R32] + S::epi32_byte(m % R32, q)) = v;
@@ -812,13 +981,13 @@ hgemm_tr_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
+      for (int rq = 0; rq < S::RQ; ++rq) {
         uint2 v;
         v.x = round16<S::BF>(acc[nb][mb][4 * rq + 0]) |
               ((unsigned)round16<S::BF>(acc[nb][mb][4 * rq + 1]) << 16);
         v.y = round16<S::BF>(acc[nb][mb][4 * rq + 2]) |
               ((unsigned)round16<S::BF>(acc[nb][mb][4 * rq + 3]) << 16);
-        const int row = 32 * mb + l % 32, slot = 8 * nb + 2 * rq + l / 32;
+        const int row = S::acc_row(mb, l), slot = S::acc_col(nb, rq, l) / 4;
         *reinterpret_cast<uint2*>(ep[row / S::RPA] + S::epi_byte(row % S::RPA, slot)) = v;
       }
   __syncthreads();
@@ -831,11 +1000,9 @@ hgemm_tr_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
     const int row = pass * RPI + rl;
     const unsigned char* e = ep[(pass * RPI) / S::RPA];
     const int lr = row % S::RPA;
-    const uint2 lo = *reinterpret_cast<const uint2*>(e + S::epi_byte(lr, 2 * c));
-    const uint2 hi = *reinterpret_cast<const uint2*>(e + S::epi_byte(lr, 2 * c + 1));
+    const u32x4 v = S::epi_chunk(e, lr, c);
     const int grow = m0 + wm0 + row;
     if (grow < M && col < N) {
-      u32x4 v = {lo.x, lo.y, hi.x, hi.y};
       // Streaming store: C is written once and not read back here (about
       // 1 % faster than a plain store for the end-of-kernel write burst).
       __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(C + (int64_t)grow * p.ldc + col));
@@ -860,11 +1027,11 @@ hgemm_tr_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
 // The number of K slices must be even, so that every tile starts on stage
 // 0 (the launch runs the one-tile-per-workgroup kernel otherwise).
 //
-// The first wait of each later tile is vmcnt <= (copies of one slice):
-// the C stores were issued after the next tile's copies, and whether or
-// not stores complete in order with loads, a count that low means at least
-// one slice's worth of copies has completed beyond the stores, and copies
-// complete in order among themselves, so the tile's first slice is in LDS.
+// The first wait of each later tile lets the copies of its second slice
+// and the previous tile's C stores (issued after the first slice's copies)
+// stay in flight: vector memory operations of a wave complete in issue
+// order, loads and stores alike (gfx9 has one counter for both, and the
+// compiler's own waits for this target assume the same order).
 template <class S>
 __global__ void __launch_bounds__(S::NT)
 hgemm_tr_persistent_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
@@ -968,26 +1135,31 @@ hgemm_tr_persistent_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_byt
       return Frag(__builtin_bit_cast(f16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7)));
     }
   };
+  auto load_a = [&](int buf, const unsigned char* la, int j, int mb) __attribute__((always_inline)) {
+    if constexpr (S::F8)
+      fa[buf][mb] = two_chunks(la + a_fb[2 * j] + mb * S::MI * S::A_ROW, la + a_fb[2 * j + 1] + mb * S::MI * S::A_ROW);
+    else
+      fa[buf][mb] = *(const lds_f16x8*)(la + a_fb[j] + mb * S::MI * S::A_ROW);
+  };
+  auto load_b = [&](int buf, const unsigned char* lb, int j, int nb) __attribute__((always_inline)) {
+    fb[buf][nb] = tr_operand(lb + b_fb[nb] + S::KW * j * S::B_ROW, S::B_ROW);
+  };
   auto load_frags = [&](int buf, const unsigned char* la, const unsigned char* lb, int j)
       __attribute__((always_inline)) {
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      if constexpr (S::F8)
-        fa[buf][mb] = two_chunks(la + a_fb[2 * j] + mb * 32 * S::A_ROW, la + a_fb[2 * j + 1] + mb * 32 * S::A_ROW);
-      else
-        fa[buf][mb] = *(const lds_f16x8*)(la + a_fb[j] + mb * 32 * S::A_ROW);
-    }
+    for (int mb = 0; mb < MB; ++mb) load_a(buf, la, j, mb);
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) fb[buf][nb] = tr_operand(lb + b_fb[nb] + S::KW * j * S::B_ROW, S::B_ROW);
+    for (int nb = 0; nb < NB; ++nb) load_b(buf, lb, j, nb);
   };
-  f32x16 acc[NB][MB];
+  typedef std::conditional_t<S::MI == 32, f32x16, f32x4> Acc;
+  Acc acc[NB][MB];
   auto zero_acc = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[nb][mb][r] = 0.f;
+        for (int r = 0; r < S::AR; ++r) acc[nb][mb][r] = 0.f;
   };
   auto mma = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
@@ -1002,6 +1174,35 @@ hgemm_tr_persistent_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_byt
   };
   constexpr int NMMA = MB * NB;
   constexpr int NRD = MB * FR + S::TRN * NB;
+  // 16 x 16 blocks: the one-tile kernel's fixed MFMA sequence (mma16 there).
+  auto mma16 = [&](int cur, auto&& rd, auto&& cp) __attribute__((always_inline)) {
+    if constexpr (S::MI == 16 && !S::F8) {
+      static_for([&](auto I) __attribute__((always_inline)) {
+        constexpr int i = decltype(I)::value;
+        mfma16_asm<S::TY>(acc[i / MB][i % MB], fb[cur][i / MB], fa[cur][i % MB]);
+        if constexpr (i % 4 == 0 && i / 4 < MB + NB) rd(IC<i / 4>{});
+        cp(IC<i>{});
+        __builtin_amdgcn_sched_barrier(0);
+      }, std::make_integer_sequence<int, MB * NB>{});
+    }
+  };
+  auto rd_op = [&](int buf, const unsigned char* la, const unsigned char* lb, int j, auto F)
+      __attribute__((always_inline)) {
+    constexpr int f = decltype(F)::value;
+    if constexpr (f < MB) load_a(buf, la, j, f);
+    else load_b(buf, lb, j, f - MB);
+  };
+  // The accumulators' zeros in place before the guard that precedes the
+  // next MFMA (16 x 16 blocks; see mfma16_asm).
+  auto pin_zero = [&]() __attribute__((always_inline)) {
+    if constexpr (S::MI == 16) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) asm volatile("" : "+a"(acc[nb][mb]));
+      mfma_guard();
+    }
+  };
 
   int v = blockIdx.x;
   int tm, tn;
@@ -1028,6 +1229,28 @@ hgemm_tr_persistent_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_byt
     // Every copy of this tile is issued by now (slice T-1 went out in
     // slice T-3): the offsets can move to the next tile.
     if (has_next && t == T - 2) set_tile(m0n, n0n);
+    if constexpr (S::MI == 16) {
+      static_for([&](auto J) __attribute__((always_inline)) {
+        constexpr int j = decltype(J)::value;
+        mma16(S::frag_set(c, j),
+              [&](auto F) __attribute__((always_inline)) { rd_op(S::frag_set(c, j + 1), ca, cb, j + 1, F); },
+              [](auto) {});
+      }, std::make_integer_sequence<int, KS - 1>{});
+      loop_barrier<0>();  // slice t+1 landed (and any earlier stores done)
+      __builtin_amdgcn_sched_barrier(0);
+      const int s = has_next && t + 2 >= T ? t + 2 - T : t + 2;
+      mma16(S::frag_set(c, KS - 1),
+            [&](auto F) __attribute__((always_inline)) {
+              rd_op(S::frag_set(c + 1, 0), n == 0 ? la0 : la1, n == 0 ? lb0 : lb1, 0, F);
+            },
+            [&](auto Q) __attribute__((always_inline)) {
+              constexpr int q = decltype(Q)::value;
+              if constexpr (q < S::LPS)
+                issue_copy_ps<S>(Ab, Bb, a_bytes, b_bytes, s, s < T, s == T - 1, a_vo, a_tail, b_vo, ca, cb,
+                                 lw, lda, ldb, q);
+            });
+      return;
+    }
     static_for([&](auto J) __attribute__((always_inline)) {
       constexpr int j = decltype(J)::value;
       load_frags(S::frag_set(c, j + 1), ca, cb, j + 1);
@@ -1060,8 +1283,14 @@ hgemm_tr_persistent_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_byt
   const __amdgpu_buffer_rsrc_t rc =
       make_rsrc(static_cast<const unsigned char*>(p.C), ((int64_t)(M - 1) * p.ldc + N) * 2);
   constexpr int CPR = S::EPI_CPR, RPI = S::EPI_RPI;
+  // Rounds of 32 rows (row blocks per round); store instructions of one
+  // tile's epilogue per wave.
+  constexpr int BPR = 32 / S::MI, ROUNDS = MB / BPR;
+  constexpr int PS_STORES = ROUNDS * (32 / RPI);
+  static_assert(S::LPS + PS_STORES <= 63, "vmcnt field");
 
   zero_acc();
+  pin_zero();
   if (T > 0) {
     PS_PRODUCE(0, la0, lb0);
     PS_PRODUCE(1, la1, lb1);
@@ -1071,32 +1300,43 @@ hgemm_tr_persistent_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_byt
     set_tile(m0, n0);
     set_frags();
     if (T > 0) {
-      // Slice 0 of this tile landed (later tiles: see the note above).
-      loop_barrier<S::LPS>();
-      if (first) trace_stamp(p, 1);
+      // Slice 0 of this tile landed: with slice 1's copies still in flight,
+      // and for later tiles also the previous tile's C stores (see above).
+      if (first) {
+        loop_barrier<S::LPS>();
+        trace_stamp(p, 1);
+      } else {
+        loop_barrier<S::LPS + PS_STORES>();
+      }
       load_frags(0, la0, lb0, 0);
       for (int t = 0; t < T; t += 2) {
         slice(t, IC<0>{});
         slice(t + 1, IC<1>{});
       }
+      if constexpr (S::MI == 16) mfma_guard();  // the tile's last MFMA results
     }
+    if constexpr (S::MI == 16) mfma_guard();
     first = false;
-    // Epilogue: round mb stages rows wm0 + 32mb .. +31 of the wave tile.
+    // Epilogue: round rd stages rows wm0 + 32rd .. +31 of the wave tile
+    // (BPR row blocks).
     const int l = opaque_lane();
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
+    for (int rd = 0; rd < ROUNDS; ++rd) {
       // One round at a time (the scheduler would otherwise hoist every
       // round's accumulator reads and run out of registers).
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
+      for (int mbl = 0; mbl < BPR; ++mbl)
 #pragma unroll
-        for (int rq = 0; rq < 4; ++rq) {
-          uint2 w;
-          w.x = round16<S::BF>(acc[nb][mb][4 * rq + 0]) | ((unsigned)round16<S::BF>(acc[nb][mb][4 * rq + 1]) << 16);
-          w.y = round16<S::BF>(acc[nb][mb][4 * rq + 2]) | ((unsigned)round16<S::BF>(acc[nb][mb][4 * rq + 3]) << 16);
-          *reinterpret_cast<uint2*>(ep + S::epi_byte(l % 32, 8 * nb + 2 * rq + l / 32)) = w;
-        }
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int rq = 0; rq < S::RQ; ++rq) {
+            const int mb = rd * BPR + mbl;
+            uint2 w;
+            w.x = round16<S::BF>(acc[nb][mb][4 * rq + 0]) | ((unsigned)round16<S::BF>(acc[nb][mb][4 * rq + 1]) << 16);
+            w.y = round16<S::BF>(acc[nb][mb][4 * rq + 2]) | ((unsigned)round16<S::BF>(acc[nb][mb][4 * rq + 3]) << 16);
+            *reinterpret_cast<uint2*>(ep + S::epi_byte(S::acc_row(mbl, l), S::acc_col(nb, rq, l) / 4)) = w;
+          }
       // All the round's row chunks are read back first, then stored: one
       // wait for the LDS reads instead of one per store.
       const int col = n0 + wn0 + 8 * (l % CPR);
@@ -1105,13 +1345,11 @@ hgemm_tr_persistent_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_byt
 #pragma unroll
       for (int pass = 0; pass < PASSES; ++pass) {
         const int r = pass * RPI + l / CPR;
-        const uint2 lo = *reinterpret_cast<const uint2*>(ep + S::epi_byte(r, 2 * (l % CPR)));
-        const uint2 hi = *reinterpret_cast<const uint2*>(ep + S::epi_byte(r, 2 * (l % CPR) + 1));
-        val[pass] = v4i{(int)lo.x, (int)lo.y, (int)hi.x, (int)hi.y};
+        val[pass] = __builtin_bit_cast(v4i, S::epi_chunk(ep, r, l % CPR));
       }
 #pragma unroll
       for (int pass = 0; pass < PASSES; ++pass) {
-        const int row = m0 + wm0 + 32 * mb + pass * RPI + l / CPR;
+        const int row = m0 + wm0 + 32 * rd + pass * RPI + l / CPR;
         const unsigned off = ((row < M) & (col < N)) ? 2u * ((unsigned)row * (unsigned)p.ldc + (unsigned)col) : OOB;
         __builtin_amdgcn_raw_buffer_store_b128(val[pass], rc, off, 0, 0);
       }
@@ -1128,6 +1366,7 @@ hgemm_tr_persistent_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_byt
       n0n = tn * BN;
     }
     zero_acc();
+    pin_zero();
   }
   trace_stamp(p, 2);
   // The zero-filling copies past the last tile's last slice must land
@@ -1222,12 +1461,12 @@ int layout_check_bt(int banks, int64_t* rconf) {
           for (int l = 0; l < 64; ++l) {
             addr[l] = S::bt_frag(wn0, nb, j, l, part);
             if (addr[l] < 0 || addr[l] + 16 > S::B_STAGE) return 23;
-            if (addr[l] != S::bt_frag(wn0, 0, j, l, part) + nb * 32 * S::B_ROW) return 24;
+            if (addr[l] != S::bt_frag(wn0, 0, j, l, part) + nb * S::MI * S::B_ROW) return 24;
             // A_op lane l, element e of this chunk:
-            // B[k = KW j + (KW/2)(l/32) + CE part + e][n = wn0 + 32nb + l%32].
+            // B[k = KW j + KL(l/MI) + CE part + e][n = wn0 + MI nb + l%MI].
             for (int e = 0; e < S::CE; ++e)
-              if (n_of[addr[l] + S::ES * e] != wn0 + 32 * nb + l % 32 ||
-                  k_of[addr[l] + S::ES * e] != S::KW * j + (S::KW / 2) * (l / 32) + S::CE * part + e)
+              if (n_of[addr[l] + S::ES * e] != wn0 + S::MI * nb + l % S::MI ||
+                  k_of[addr[l] + S::ES * e] != S::KW * j + S::KL * (l / S::MI) + S::CE * part + e)
                 return 25;
           }
           *rconf += lds_conflicts(addr, 16, banks);
@@ -1277,9 +1516,9 @@ int layout_check_at(int banks, int64_t* rconf) {
               const int src = addr[16 * g + LPR * t + jj / S::RR] + S::ES * (jj % S::RR);
               if (src < 0 || src >= S::A_STAGE) return 44;
               // B_op lane l, element RR*jr + t:
-              // A[m = wm0 + 32mb + l%32][k = KW j + (KW/2)(l/32) + RR jr + t].
-              if (k_of[src] != S::KW * j + (S::KW / 2) * (l / 32) + S::RR * jr + t ||
-                  m_of[src] != wm0 + 32 * mb + l % 32)
+              // A[m = wm0 + MI mb + l%MI][k = KW j + KL(l/MI) + RR jr + t].
+              if (k_of[src] != S::KW * j + S::KL * (l / S::MI) + S::RR * jr + t ||
+                  m_of[src] != wm0 + S::MI * mb + l % S::MI)
                 return 45;
             }
           *rconf += lds_conflicts(addr, 8, banks);
@@ -1338,14 +1577,14 @@ int layout_check(int banks, int64_t out[2]) {
             addr[l] = S::a_frag(wm0, mb, j, l, part);
             if (addr[l] < 0 || addr[l] + 16 > S::A_STAGE) return 15;
             // B_op lane l, element e of this chunk:
-            // A[m = wm0 + 32mb + l%32][k = KW j + (KW/2)(l/32) + CE part + e].
+            // A[m = wm0 + MI mb + l%MI][k = KW j + KL(l/MI) + CE part + e].
             for (int e = 0; e < S::CE; ++e) {
               const int b = addr[l] + S::ES * e;
-              if (a_row_of[b] != wm0 + 32 * mb + l % 32 ||
-                  a_k_of[b] != S::KW * j + (S::KW / 2) * (l / 32) + S::CE * part + e)
+              if (a_row_of[b] != wm0 + S::MI * mb + l % S::MI ||
+                  a_k_of[b] != S::KW * j + S::KL * (l / S::MI) + S::CE * part + e)
                 return 7;
             }
-            if (addr[l] != S::a_frag(wm0, 0, j, l, part) + mb * 32 * S::A_ROW) return 8;
+            if (addr[l] != S::a_frag(wm0, 0, j, l, part) + mb * S::MI * S::A_ROW) return 8;
           }
           rconf += lds_conflicts(addr, 16, banks);
         }
@@ -1365,9 +1604,9 @@ int layout_check(int banks, int64_t out[2]) {
               const int src = addr[16 * g + LPR * t + jj / S::RR] + S::ES * (jj % S::RR);
               if (src < 0 || src >= S::B_STAGE) return 14;
               // A_op lane l, element RR*jr + t:
-              // B[k = KW j + (KW/2)(l/32) + RR jr + t][n = wn0 + 32nb + l%32].
-              if (b_k_of[src] != S::KW * j + (S::KW / 2) * (l / 32) + S::RR * jr + t ||
-                  b_n_of[src] != wn0 + 32 * nb + l % 32)
+              // B[k = KW j + KL(l/MI) + RR jr + t][n = wn0 + MI nb + l%MI].
+              if (b_k_of[src] != S::KW * j + S::KL * (l / S::MI) + S::RR * jr + t ||
+                  b_n_of[src] != wn0 + S::MI * nb + l % S::MI)
                 return 10;
             }
           rconf += lds_conflicts(addr, 8, banks);
@@ -1380,34 +1619,40 @@ int layout_check(int banks, int64_t out[2]) {
   static int ep_row[S::P][EW], ep_col[S::P][EW];
   for (int a = 0; a < S::P; ++a)
     for (int i = 0; i < EW; ++i) ep_row[a][i] = -1;
+  // Accumulator register 4rq + e of lane l in block (nb, mb) holds row
+  // MI mb + l%MI, column MI nb + 8rq + 4(l/MI) + e of the wave tile (the
+  // matrix instruction's output layout, operands swapped).
+  constexpr int MI = S::MI;
   for (int nb = 0; nb < S::NB; ++nb)
     for (int mb = 0; mb < S::MB; ++mb)
-      for (int rq = 0; rq < 4; ++rq) {
+      for (int rq = 0; rq < S::RQ; ++rq) {
         for (int l = 0; l < 64; ++l) {
-          const int row = 32 * mb + l % 32, slot = 8 * nb + 2 * rq + l / 32;
+          const int row = MI * mb + l % MI, slot = (MI / 4) * nb + 2 * rq + l / MI;
           const int a = row / S::RPA;
           addr[l] = S::epi_byte(row % S::RPA, slot);
           if (a >= S::P || addr[l] < 0 || addr[l] + 8 > EW) return 13;
           for (int e = 0; e < 4; ++e) {
             if (ep_row[a][addr[l] + 2 * e] != -1) return 11;
             ep_row[a][addr[l] + 2 * e] = row;
-            ep_col[a][addr[l] + 2 * e] = 32 * nb + 8 * rq + 4 * (l / 32) + e;
+            ep_col[a][addr[l] + 2 * e] = MI * nb + 8 * rq + 4 * (l / MI) + e;
           }
         }
         wconf += lds_conflicts(addr, 8, banks);
       }
   constexpr int CPR = S::EPI_CPR, RPI = S::EPI_RPI;
   for (int pass = 0; pass < WM / RPI; ++pass)
-    for (int half = 0; half < 2; ++half) {
+    for (int half = 0; half < (MI == 16 ? 1 : 2); ++half) {
+      // 16 x 16 blocks: one 16-byte read of both slots.
+      const int width = MI == 16 ? 16 : 8;
       for (int l = 0; l < 64; ++l) {
         const int row = pass * RPI + l / CPR, c = l % CPR;
         const int a = (pass * RPI) / S::RPA;
         addr[l] = S::epi_byte(row % S::RPA, 2 * c + half);
-        for (int e = 0; e < 4; ++e)
+        for (int e = 0; e < width / 2; ++e)
           if (ep_row[a][addr[l] + 2 * e] != row || ep_col[a][addr[l] + 2 * e] != 8 * c + 4 * half + e)
             return 12;
       }
-      rconf += lds_conflicts(addr, 8, banks);
+      rconf += lds_conflicts(addr, width, banks);
     }
   // Fused-epilogue staging (one pass; both passes use the same map): FP32
   // writes cover the wave's region once, reads return the element written.
@@ -1418,16 +1663,16 @@ int layout_check(int banks, int64_t out[2]) {
       for (int i = 0; i < E32 / 4; ++i) e_row[a][i] = -1;
     for (int nb = 0; nb < S::NB; ++nb)
       for (int mbl = 0; mbl < S::MB / 2; ++mbl)
-        for (int rq = 0; rq < 4; ++rq) {
+        for (int rq = 0; rq < S::RQ; ++rq) {
           for (int l = 0; l < 64; ++l) {
-            const int m = 32 * mbl + l % 32, q = 8 * nb + 2 * rq + l / 32;
+            const int m = MI * mbl + l % MI, q = (MI / 4) * nb + 2 * rq + l / MI;
             const int a = m / R32;
             addr[l] = S::epi32_byte(m % R32, q);
             if (a >= S::P || addr[l] < 0 || addr[l] + 16 > E32) return 16;
             for (int e = 0; e < 4; ++e) {
               if (e_row[a][addr[l] / 4 + e] != -1) return 17;
               e_row[a][addr[l] / 4 + e] = m;
-              e_col[a][addr[l] / 4 + e] = 32 * nb + 8 * rq + 4 * (l / 32) + e;
+              e_col[a][addr[l] / 4 + e] = MI * nb + 8 * rq + 4 * (l / MI) + e;
             }
           }
           wconf += lds_conflicts(addr, 16, banks);
@@ -1444,15 +1689,15 @@ int layout_check(int banks, int64_t out[2]) {
       rconf += lds_conflicts(addr, 16, banks);
     }
   }
-  int rc = layout_check_bt<Shape<S::BM, S::BN, S::WM, S::WN, S::BK, S::NS, 0, true, S::TY, false, S::PW>>(
+  int rc = layout_check_bt<Shape<S::BM, S::BN, S::WM, S::WN, S::BK, S::NS, 0, true, S::TY, false, S::PW, S::MI>>(
       banks, &rconf);
   if (rc != 0) return rc;
   if constexpr (S::BM * S::ES >= 256) {
-    rc = layout_check_at<Shape<S::BM, S::BN, S::WM, S::WN, S::BK, S::NS, 0, false, S::TY, true, S::PW>>(
+    rc = layout_check_at<Shape<S::BM, S::BN, S::WM, S::WN, S::BK, S::NS, 0, false, S::TY, true, S::PW, S::MI>>(
         banks, &rconf);
     if (rc != 0) return rc;
     // Both transposed: B's side must not depend on A's row length.
-    rc = layout_check_bt<Shape<S::BM, S::BN, S::WM, S::WN, S::BK, S::NS, 0, true, S::TY, true, S::PW>>(
+    rc = layout_check_bt<Shape<S::BM, S::BN, S::WM, S::WN, S::BK, S::NS, 0, true, S::TY, true, S::PW, S::MI>>(
         banks, &rconf);
     if (rc != 0) return rc;
   }
@@ -1463,50 +1708,57 @@ int layout_check(int banks, int64_t out[2]) {
 
 // The transposed-A launches, for tiles whose A^T rows (BM values) span the
 // 256 bytes the chunk XOR needs; none otherwise.
-template <int BM, int BN, int WM, int WN, int BK, int NS, int TY, bool BT, int PW>
+template <int BM, int BN, int WM, int WN, int BK, int NS, int TY, bool BT, int PW, int MI>
 constexpr LaunchFn at_launch() {
   if constexpr (BM * (TY >= 2 ? 1 : 2) >= 256)
-    return &launch<Shape<BM, BN, WM, WN, BK, NS, 0, BT, TY, true, PW>>;
+    return &launch<Shape<BM, BN, WM, WN, BK, NS, 0, BT, TY, true, PW, MI>>;
   else
     return nullptr;
 }
 
-// PW producer waves (0: none); their count is the name's _p suffix.
-#define HGEMM_TR_VARIANT_PW(TY, DT, TAG, BM, BN, WM, WN, BK, NS, PW, SFX, EFF)                   \
+// PW producer waves (0: none); their count is the name's _p suffix.  MI:
+// the matrix instruction's block (16: the name's _mi16 suffix).
+#define HGEMM_TR_VARIANT_MI(TY, DT, TAG, BM, BN, WM, WN, BK, NS, PW, MI, SFX, EFF)               \
   Variant {                                                                                  \
     gemm_config_t{0, DT, GEMM_FAMILY_MFMA, BM, BN, BK, WM, WN,                               \
-                  Shape<BM, BN, WM, WN, BK, NS, 0, false, TY, false, PW>::NT, NS,            \
-                  Shape<BM, BN, WM, WN, BK, NS, 0, false, TY, false, PW>::LDS_BYTES,         \
+                  Shape<BM, BN, WM, WN, BK, NS, 0, false, TY, false, PW, MI>::NT, NS,        \
+                  Shape<BM, BN, WM, WN, BK, NS, 0, false, TY, false, PW, MI>::LDS_BYTES,     \
                   GEMM_ORDER_XCD, 4, 1,                                                      \
                   "tr_" TAG "_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_s" #NS SFX},          \
-        &launch<Shape<BM, BN, WM, WN, BK, NS, 0, false, TY, false, PW>>,                     \
-        &layout_check<Shape<BM, BN, WM, WN, BK, NS, 0, false, TY, false, PW>>,               \
-        &launch<Shape<BM, BN, WM, WN, BK, NS, 1, false, TY, false, PW>>, EFF,                \
-        &launch<Shape<BM, BN, WM, WN, BK, NS, 2, false, TY, false, PW>>,                     \
-        &launch<Shape<BM, BN, WM, WN, BK, NS, 0, true, TY, false, PW>>,                      \
-        &launch<Shape<BM, BN, WM, WN, BK, NS, 3, false, TY, false, PW>>,                     \
-        at_launch<BM, BN, WM, WN, BK, NS, TY, false, PW>(),                                  \
-        at_launch<BM, BN, WM, WN, BK, NS, TY, true, PW>()                                    \
+        &launch<Shape<BM, BN, WM, WN, BK, NS, 0, false, TY, false, PW, MI>>,                 \
+        &layout_check<Shape<BM, BN, WM, WN, BK, NS, 0, false, TY, false, PW, MI>>,           \
+        &launch<Shape<BM, BN, WM, WN, BK, NS, 1, false, TY, false, PW, MI>>, EFF,            \
+        &launch<Shape<BM, BN, WM, WN, BK, NS, 2, false, TY, false, PW, MI>>,                 \
+        &launch<Shape<BM, BN, WM, WN, BK, NS, 0, true, TY, false, PW, MI>>,                  \
+        &launch<Shape<BM, BN, WM, WN, BK, NS, 3, false, TY, false, PW, MI>>,                 \
+        at_launch<BM, BN, WM, WN, BK, NS, TY, false, PW, MI>(),                              \
+        at_launch<BM, BN, WM, WN, BK, NS, TY, true, PW, MI>()                                \
   }
+#define HGEMM_TR_VARIANT_PW(TY, DT, TAG, BM, BN, WM, WN, BK, NS, PW, SFX, EFF) \
+  HGEMM_TR_VARIANT_MI(TY, DT, TAG, BM, BN, WM, WN, BK, NS, PW, 32, SFX, EFF)
 // The persistent form of a two-stage tile: the plain call only.
-#define HGEMM_TR_VARIANT_PS(TY, DT, TAG, BM, BN, WM, WN, BK, EFF)                                    \
+#define HGEMM_TR_VARIANT_PS_MI(TY, DT, TAG, BM, BN, WM, WN, BK, MI, SFX, EFF)                        \
   Variant {                                                                                      \
     gemm_config_t{0, DT, GEMM_FAMILY_MFMA, BM, BN, BK, WM, WN,                                   \
-                  Shape<BM, BN, WM, WN, BK, 2, 0, false, TY, false, 0>::NT, 2,                   \
-                  Shape<BM, BN, WM, WN, BK, 2, 0, false, TY, false, 0>::LDS_BYTES +              \
-                      Shape<BM, BN, WM, WN, BK, 2, 0, false, TY, false, 0>::NW *                 \
-                          Shape<BM, BN, WM, WN, BK, 2, 0, false, TY, false, 0>::PS_EPI_BYTES,    \
+                  Shape<BM, BN, WM, WN, BK, 2, 0, false, TY, false, 0, MI>::NT, 2,               \
+                  Shape<BM, BN, WM, WN, BK, 2, 0, false, TY, false, 0, MI>::LDS_BYTES +          \
+                      Shape<BM, BN, WM, WN, BK, 2, 0, false, TY, false, 0, MI>::NW *             \
+                          Shape<BM, BN, WM, WN, BK, 2, 0, false, TY, false, 0, MI>::PS_EPI_BYTES, \
                   GEMM_ORDER_XCD, 4, 1,                                                          \
-                  "tr_" TAG "_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_s2_ps"},                  \
-        &launch_persistent<Shape<BM, BN, WM, WN, BK, 2, 0, false, TY, false, 0>>,                \
-        &layout_check<Shape<BM, BN, WM, WN, BK, 2, 0, false, TY, false, 0>>, nullptr, EFF,      \
+                  "tr_" TAG "_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_s2" SFX "_ps"},           \
+        &launch_persistent<Shape<BM, BN, WM, WN, BK, 2, 0, false, TY, false, 0, MI>>,            \
+        &layout_check<Shape<BM, BN, WM, WN, BK, 2, 0, false, TY, false, 0, MI>>, nullptr, EFF,  \
         nullptr, nullptr, nullptr, nullptr, nullptr, true                                        \
   }
+#define HGEMM_TR_VARIANT_PS(TY, DT, TAG, BM, BN, WM, WN, BK, EFF) \
+  HGEMM_TR_VARIANT_PS_MI(TY, DT, TAG, BM, BN, WM, WN, BK, 32, "", EFF)
 #define HGEMM_TR_VARIANT(TY, DT, TAG, BM, BN, WM, WN, BK, NS, EFF) \
   HGEMM_TR_VARIANT_PW(TY, DT, TAG, BM, BN, WM, WN, BK, NS, 0, "", EFF)
 
 // The 16-bit LDS layouts and data path do not depend on the element type,
-// so FP16 and BF16 share the tiles and the measured tile efficiencies.  FP8
+// so FP16 and BF16 share the tiles and the measured tile efficiencies.  The
+// 16 x 16 instruction's form of the default tile (_mi16) runs 2-9 % above
+// it with all CUs busy (FP16 4096^3 +9 %, 8192^3 +5 %; BF16 +1-5 %).  FP8
 // moves 128 k per slice in the same bytes; its B rows must span 256 bytes
 // (the 2*(k%8) chunk XOR), so its tiles are 256 columns wide.
 #define HGEMM_TR_TABLE(TY, DT, TAG)                                   \
@@ -1518,7 +1770,9 @@ constexpr LaunchFn at_launch() {
    HGEMM_TR_VARIANT(TY, DT, TAG, 128, 128, 64, 64, 64, 2, 0.71f),                 \
    HGEMM_TR_VARIANT_PW(TY, DT, TAG, 256, 128, 128, 64, 64, 3, 4, "_p4", 0.895f),   \
    HGEMM_TR_VARIANT_PW(TY, DT, TAG, 256, 128, 128, 64, 64, 3, 2, "_p2", 0.89f),    \
-   HGEMM_TR_VARIANT_PS(TY, DT, TAG, 256, 256, 128, 128, 64, 1.00f)}
+   HGEMM_TR_VARIANT_PS(TY, DT, TAG, 256, 256, 128, 128, 64, 1.00f),               \
+   HGEMM_TR_VARIANT_MI(TY, DT, TAG, 256, 256, 128, 128, 64, 2, 0, 16, "_mi16", 1.05f), \
+   HGEMM_TR_VARIANT_PS_MI(TY, DT, TAG, 256, 256, 128, 128, 64, 16, "_mi16", 1.05f)}
 
 const Variant kVariants[] = HGEMM_TR_TABLE(0, GEMM_DTYPE_F16, "f16");
 const Variant kVariantsBf[] = HGEMM_TR_TABLE(1, GEMM_DTYPE_BF16, "bf16");

@@ -60,12 +60,12 @@ PASSES = ("FETCH_SIZE", "WRITE_SIZE TCC_HIT_sum TCC_MISS_sum", SQ_PASS)
 # The default variants the counter command runs, by kernel family.
 COUNTER_VARIANTS = {
     "sgemm_dl": "dl_f32_256x256x32_w128x128_s2",
-    "hgemm_tr": "tr_f16_256x256x64_w128x128_s2",
-    "hgemm_tr_bf16": "tr_bf16_256x256x64_w128x128_s2",
+    "hgemm_tr": "tr_f16_256x256x64_w128x128_s2_mi16",
+    "hgemm_tr_bf16": "tr_bf16_256x256x64_w128x128_s2_mi16",
     "hgemm_tr_f8": "tr_f8_256x256x128_w128x128_s2",
 }
 COPY = "copy(neg)"
-_TR_TYPE = re.compile(r"Shape<(?:\d+, ){6}\d+, (?:true|false), (\d+), (?:true|false)(?:, \d+)?>")
+_TR_TYPE = re.compile(r"Shape<(?:\d+, ){6}\d+, (?:true|false), (\d+), (?:true|false)(?:, \d+)*>")
 _PREFIX_FAMILY = {"dl_f32": "sgemm_dl", "mfma_f32": "sgemm_mfma", "simt_f32": "sgemm_simt",
                   "tr_f16": "hgemm_tr", "tr_bf16": "hgemm_tr_bf16", "tr_f8": "hgemm_tr_f8",
                   "tr_e5m2": "hgemm_tr_e5m2", "mfma_f16": "hgemm_mfma"}

@@ -192,9 +192,13 @@ def test_heuristic_selection():
     for dt in (gemm.DTYPE_F32, gemm.DTYPE_F16, gemm.DTYPE_BF16):
         for M, N, K in [(1, 1, 1), (4096, 11008, 4096), (1024, 1024, 8192)]:
             assert gemm.gemm_select_config(dt, M, N, K).family == gemm.FAMILY_MFMA
-    # At 4096^3 every type takes its first (default) tile: one per CU.
-    for dt in (gemm.DTYPE_F32, gemm.DTYPE_F16, gemm.DTYPE_BF16, gemm.DTYPE_F8, gemm.DTYPE_E5M2):
+    # At 4096^3 every type takes its first (default) tile, one per CU; the
+    # 16-bit types in its 16 x 16-instruction form (faster with all CUs busy).
+    for dt in (gemm.DTYPE_F32, gemm.DTYPE_F8, gemm.DTYPE_E5M2):
         assert gemm.gemm_select_config(dt, 4096, 4096, 4096).name == gemm.gemm_get_config(dt, 0).name
+    for dt in (gemm.DTYPE_F16, gemm.DTYPE_BF16):
+        first = gemm.gemm_get_config(dt, 0).name
+        assert gemm.gemm_select_config(dt, 4096, 4096, 4096).name == first + b"_mi16"
     # Few output tiles, long K, unsplit: the 16-bit types keep an LDS-direct
     # tile (its rate alone); small tiles of the general kernel cannot hide
     # their latency with one workgroup per CU.

@@ -14,9 +14,9 @@ SG = ("void gemm::(anonymous namespace)::sgemm_dl_kernel<gemm::(anonymous namesp
       "128, 32, 2, false, false, false, false> >(gemm::Params, gemm::TileMap, long, long)")
 
 
-def tr(ty):
+def tr(ty, mi=16):
     return ("void gemm::(anonymous namespace)::hgemm_tr_kernel<gemm::(anonymous namespace)::Shape<256, 256, "
-            f"128, 128, 64, 2, 0, false, {ty}, false, 0> >(gemm::Params, gemm::TileMap, long, long)")
+            f"128, 128, 64, 2, 0, false, {ty}, false, 0, {mi}> >(gemm::Params, gemm::TileMap, long, long)")
 
 
 NEG = "void at::native::vectorized_elementwise_kernel<4, at::native::neg_kernel_cuda(at::TensorIteratorBase&)>"
@@ -25,6 +25,7 @@ NEG = "void at::native::vectorized_elementwise_kernel<4, at::native::neg_kernel_
 def test_families_of_kernel_names():
     assert ev.family(SG) == "sgemm_dl"
     assert [ev.family(tr(t)) for t in range(4)] == ["hgemm_tr", "hgemm_tr_bf16", "hgemm_tr_f8", "hgemm_tr_e5m2"]
+    assert [ev.family(tr(t, 32)) for t in range(4)] == ["hgemm_tr", "hgemm_tr_bf16", "hgemm_tr_f8", "hgemm_tr_e5m2"]
     assert ev.family(NEG) == ev.COPY
     assert ev.family("void at::native::fill_kernel") is None
     assert ev.family_of_variant("tr_bf16_256x256x64_w128x128_s2") == "hgemm_tr_bf16"
@@ -77,7 +78,7 @@ def test_timed_window_is_before_the_single_launches(tmp_path):
 def test_run_directory_to_summaries_and_json(tmp_path):
     R, O = tmp_path / "run", tmp_path / "out"
     os.makedirs(O)
-    variants = {"f32": ("dl_f32_256x256x32_w128x128_s2", SG), "f16": ("tr_f16_256x256x64_w128x128_s2", tr(0))}
+    variants = {"f32": ("dl_f32_256x256x32_w128x128_s2", SG), "f16": ("tr_f16_256x256x64_w128x128_s2_mi16", tr(0))}
     names = {"sgemm_dl": SG, "hgemm_tr": tr(0), "hgemm_tr_bf16": tr(1), "hgemm_tr_f8": tr(2)}
     # kernel trace of the default bench run: both GEMMs at 1 us except the timed ones
     seq = []

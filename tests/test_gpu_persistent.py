@@ -7,8 +7,10 @@ oracle) at grids of more than 256 tiles, so that workgroups take two tiles
 (ragged M and N, a partial last K slice, and exactly two tiles each); odd
 slice counts, which run the one-tile kernel; random inputs at 8192 x 8192 x
 1024 (1024 tiles, four per workgroup) on sampled rows; and determinism.
-Every 16-bit and 8-bit type.  (The FP16 full-size parity test checks every
-element at 8192 x 8192 x 1024, whose default pick is this form.)"""
+Every 16-bit and 8-bit type, and for 16-bit types both matrix-instruction
+block sizes (``_s2_ps`` with 32 x 32 blocks, ``_s2_mi16_ps`` with 16 x 16).
+(The FP16 full-size parity test checks every element at 8192 x 8192 x 1024,
+whose default pick is this form.)"""
 import numpy as np
 import pytest
 
@@ -26,18 +28,23 @@ SHAPES16 = [(4352, 4352, 384), (4100, 4104, 360), (8192, 4096, 128)]
 SHAPES8 = [(4352, 4352, 512), (4100, 4112, 480), (8192, 4096, 256)]
 
 
-def _ps(dt):
-    cfgs = [c for c in gemm.configs(dt) if c.name.decode().endswith("_ps")]
+# (kind, persistent variant suffix): 16-bit types have a 16 x 16 form too.
+FORMS = [(k, "_s2_ps") for k in sorted(TYPES)] + [("f16", "_s2_mi16_ps"), ("bf16", "_s2_mi16_ps")]
+FORM_IDS = [k + sfx.replace("_s2", "").replace("_ps", "") for k, sfx in FORMS]
+
+
+def _ps(dt, sfx="_s2_ps"):
+    cfgs = [c for c in gemm.configs(dt) if c.name.decode().endswith(sfx)]
     assert len(cfgs) == 1
     return cfgs[0]
 
 
-@pytest.mark.parametrize("kind", sorted(TYPES))
+@pytest.mark.parametrize("kind,sfx", FORMS, ids=FORM_IDS)
 @pytest.mark.parametrize("shape", range(3), ids=["17x17", "ragged", "2each"])
-def test_ps_exact_multi_tile(kind, shape):
+def test_ps_exact_multi_tile(kind, sfx, shape):
     dt, marker = TYPES[kind]
     M, N, K = (SHAPES8 if kind in ("f8", "e5m2") else SHAPES16)[shape]
-    cfg = _ps(dt)
+    cfg = _ps(dt, sfx)
     A = synth.small_int(17, 0, M, K, dtype=marker)
     B = synth.small_int(17, 1, K, N, dtype=marker)
     log(f"{kind} {cfg.name.decode()} exact {M}x{N}x{K}")
@@ -47,12 +54,12 @@ def test_ps_exact_multi_tile(kind, shape):
     assert np.array_equal(C.view(np.uint16), C2.view(np.uint16))
 
 
-@pytest.mark.parametrize("kind", sorted(TYPES))
-def test_ps_odd_slice_count_runs_the_one_tile_kernel(kind):
+@pytest.mark.parametrize("kind,sfx", FORMS, ids=FORM_IDS)
+def test_ps_odd_slice_count_runs_the_one_tile_kernel(kind, sfx):
     dt, marker = TYPES[kind]
     M, N = 4352, 4352
     K = 384 if kind in ("f8", "e5m2") else 192  # three slices
-    cfg = _ps(dt)
+    cfg = _ps(dt, sfx)
     A = synth.small_int(19, 0, M, K, dtype=marker)
     B = synth.small_int(19, 1, K, N, dtype=marker)
     log(f"{kind} {cfg.name.decode()} exact {M}x{N}x{K} (odd slices)")
@@ -60,11 +67,11 @@ def test_ps_odd_slice_count_runs_the_one_tile_kernel(kind):
     assert exact_equal(A, B, C)
 
 
-@pytest.mark.parametrize("kind", sorted(TYPES))
-def test_ps_random_8192x8192x1024(kind):
+@pytest.mark.parametrize("kind,sfx", FORMS, ids=FORM_IDS)
+def test_ps_random_8192x8192x1024(kind, sfx):
     dt, _ = TYPES[kind]
     M, N, K = 8192, 8192, 1024
-    cfg = _ps(dt)
+    cfg = _ps(dt, sfx)
     A, B = synth.workload(M, N, K, kind, seed=21)
     log(f"{kind} {cfg.name.decode()} random {M}x{N}x{K}")
     C, _ = run(A, B, cfg)
