@@ -453,9 +453,13 @@ def main():
                                     "epilogue": round(float(tr["epilogue_us"].mean()), 2),
                                     "loop_end_spread": round(tr["loop_end_spread_us"], 2),
                                     "span": round(tr["span_us"], 2)}}
-            ceil = probe.mfma_ceiling(dcode[k], ceiling_steps[k], repeats=2)
+            # The ceiling of the instruction the variant runs: 16 x 16 for
+            # the _mi16 tiles, 32 x 32 otherwise.
+            block = 16 if "_mi16" in cfgs[k].name.decode() else 32
+            ceil = probe.mfma_ceiling(dcode[k], ceiling_steps[k], repeats=2, block=block)
             rec.update({"mfma_ceiling_tflops": round(ceil["tflops"], 2),
-                        "mfma_ceiling_clock_mhz": round(ceil["clock_mhz"], 1)})
+                        "mfma_ceiling_clock_mhz": round(ceil["clock_mhz"], 1),
+                        "mfma_ceiling_block": block})
             probes[k] = rec
 
     kernels = {}

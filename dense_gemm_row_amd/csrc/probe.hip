@@ -9,6 +9,10 @@
 //   that the multiplier inputs change on every instruction as in a GEMM.
 //   Its rate is the ceiling of the matrix-core loop at the clock the power
 //   limit allows for that instruction and that data.
+// * gemm_probe_mfma16 runs the same stream with the 16 x 16 instructions of
+//   the 16- and 8-bit types (8 x 8 blocks of 4 accumulators per wave, the
+//   same 256 accumulator registers; the 8 + 8 fragments are all used once
+//   per k step, which is twice the 32 x 32 step's k).
 // * gemm_probe_clock spins a short dependent vector loop.
 // Both record, per workgroup, the shader-cycle counter (s_memtime) and the
 // 100 MHz constant clock (s_memrealtime) at start and end, so the clock a
@@ -89,6 +93,8 @@ __device__ __forceinline__ typename Op<TY>::T make_op(uint32_t seed) {
   }
 }
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
 template <int TY>
 __device__ __forceinline__ f32x16 mma(typename Op<TY>::T a, typename Op<TY>::T b, f32x16 c) {
   if constexpr (TY == 0) return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
@@ -141,6 +147,50 @@ __global__ void __launch_bounds__(256) probe_mfma_kernel(int64_t steps, uint64_t
   sink[blockIdx.x * 256 + threadIdx.x] = t;
 }
 
+// The 16 x 16 form (TY 1..4): per trip, one k step of 64 instructions, the
+// same flops as two 32 x 32 steps.  (No operand rotation across trips: with
+// it the compiler moved accumulators between registers inside the loop.)
+template <int TY>
+__global__ void __launch_bounds__(256) probe_mfma16_kernel(int64_t steps, uint64_t* stamps, float* sink) {
+  static_assert(TY >= 1 && TY <= 4, "16- and 8-bit types");
+  typedef typename Op<TY>::T T;
+  const uint32_t base = (blockIdx.x * 256u + threadIdx.x) * 2u * kFrags;
+  T fa[kFrags], fb[kFrags];
+#pragma unroll
+  for (int i = 0; i < kFrags; ++i) {
+    fa[i] = make_op<TY>(base + i);
+    fb[i] = make_op<TY>(base + kFrags + i);
+  }
+  f32x4 acc[8][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.f;
+  __syncthreads();
+  stamp(stamps, 0);
+  for (int64_t s = 0; s < steps; s += 2) {
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+      for (int mb = 0; mb < 8; ++mb) {
+        if constexpr (TY == 1) acc[nb][mb] = gemm::mfma16<false>(fb[nb], fa[mb], acc[nb][mb]);
+        else if constexpr (TY == 2) acc[nb][mb] = gemm::mfma16<true>(fb[nb], fa[mb], acc[nb][mb]);
+        else acc[nb][mb] = gemm::mfma_f8<TY - 3>(fb[nb], fa[mb], acc[nb][mb]);
+      }
+  }
+  stamp(stamps, 1);
+  float t = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) t += acc[i][j][r];
+  sink[blockIdx.x * 256 + threadIdx.x] = t;
+}
+
 __global__ void __launch_bounds__(64) probe_clock_kernel(int64_t iters, uint64_t* stamps, float* sink) {
   stamp(stamps, 0);
   float x = threadIdx.x * 1e-3f, y = 1.0001f;
@@ -168,6 +218,20 @@ int32_t gemm_probe_mfma(int32_t dtype, int64_t steps, uint64_t* stamps, float* s
     case GEMM_DTYPE_BF16: hipLaunchKernelGGL(probe_mfma_kernel<2>, grid, block, 0, s, steps, stamps, sink); break;
     case GEMM_DTYPE_F8: hipLaunchKernelGGL(probe_mfma_kernel<3>, grid, block, 0, s, steps, stamps, sink); break;
     case GEMM_DTYPE_E5M2: hipLaunchKernelGGL(probe_mfma_kernel<4>, grid, block, 0, s, steps, stamps, sink); break;
+    default: return GEMM_ERR_INVALID_ARG;
+  }
+  return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
+}
+
+int32_t gemm_probe_mfma16(int32_t dtype, int64_t steps, uint64_t* stamps, float* sink, void* stream) {
+  if (steps < 0 || !stamps || !sink) return GEMM_ERR_INVALID_ARG;
+  const dim3 grid(256), block(256);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  switch (dtype) {
+    case GEMM_DTYPE_F16: hipLaunchKernelGGL(probe_mfma16_kernel<1>, grid, block, 0, s, steps, stamps, sink); break;
+    case GEMM_DTYPE_BF16: hipLaunchKernelGGL(probe_mfma16_kernel<2>, grid, block, 0, s, steps, stamps, sink); break;
+    case GEMM_DTYPE_F8: hipLaunchKernelGGL(probe_mfma16_kernel<3>, grid, block, 0, s, steps, stamps, sink); break;
+    case GEMM_DTYPE_E5M2: hipLaunchKernelGGL(probe_mfma16_kernel<4>, grid, block, 0, s, steps, stamps, sink); break;
     default: return GEMM_ERR_INVALID_ARG;
   }
   return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;

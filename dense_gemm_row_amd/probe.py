@@ -30,6 +30,8 @@ def lib():
         L.gemm_probe_workgroups.restype = i32
         L.gemm_probe_mfma.argtypes = [i32, i64, p, p, p]
         L.gemm_probe_mfma.restype = i32
+        L.gemm_probe_mfma16.argtypes = [i32, i64, p, p, p]
+        L.gemm_probe_mfma16.restype = i32
         L.gemm_probe_clock.argtypes = [i64, p, p, p]
         L.gemm_probe_clock.restype = i32
         _lib = L
@@ -45,10 +47,12 @@ def _clocks(stamps):
     return mhz, rt / 100.0
 
 
-def mfma_ceiling(dtype: int, steps: int, repeats: int = 3) -> dict:
-    """Register-only matrix-core rate of dtype's instruction: TFLOP/s from
-    HIP events (best of `repeats` launches after one warm-up) and the
-    clock the workgroups ran at (mean, min, max over workgroups, MHz)."""
+def mfma_ceiling(dtype: int, steps: int, repeats: int = 3, block: int = 32) -> dict:
+    """Register-only matrix-core rate of dtype's instruction (`block` 32:
+    the 32 x 32 form, 16: the 16 x 16 form of the 16- and 8-bit types):
+    TFLOP/s from HIP events (best of `repeats` launches after one warm-up)
+    and the clock the workgroups ran at (mean, min, max over workgroups,
+    MHz)."""
     import torch
     L = lib()
     wg = L.gemm_probe_workgroups()
@@ -57,18 +61,21 @@ def mfma_ceiling(dtype: int, steps: int, repeats: int = 3) -> dict:
     stream = torch.cuda.current_stream()
     steps += steps % 2
     flops = wg * 4 * steps * 16 * 2 * 32 * 32 * K_PER_MFMA[dtype]
+    if block not in (32, 16):
+        raise ValueError("block must be 32 or 16")
+    fn = L.gemm_probe_mfma if block == 32 else L.gemm_probe_mfma16
     best = None
     for i in range(repeats + 1):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        st = L.gemm_probe_mfma(dtype, steps, stamps.data_ptr(), sink.data_ptr(), stream.cuda_stream)
+        st = fn(dtype, steps, stamps.data_ptr(), sink.data_ptr(), stream.cuda_stream)
         e1.record(stream)
         if st != 0:
-            raise RuntimeError(f"gemm_probe_mfma returned {st}")
+            raise RuntimeError(f"probe (block {block}) returned {st}")
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1)
         mhz, _ = _clocks(stamps.cpu())
-        rec = {"tflops": flops / (ms * 1e-3) / 1e12, "ms": ms, "clock_mhz": float(mhz.mean()),
+        rec = {"block": block, "tflops": flops / (ms * 1e-3) / 1e12, "ms": ms, "clock_mhz": float(mhz.mean()),
                "clock_mhz_min": float(mhz.min()), "clock_mhz_max": float(mhz.max())}
         if i > 0 and (best is None or rec["tflops"] > best["tflops"]):
             best = rec

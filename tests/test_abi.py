@@ -36,13 +36,15 @@ def test_probe_library_exports_its_header():
     from dense_gemm_row_amd import probe
     L = probe.lib()
     names = header_functions(os.path.join(ROOT, "include", "gemm_probe.h"))
-    assert names == ["gemm_probe_clock", "gemm_probe_mfma", "gemm_probe_workgroups"]
+    assert names == ["gemm_probe_clock", "gemm_probe_mfma", "gemm_probe_mfma16", "gemm_probe_workgroups"]
     for name in names:
         assert hasattr(L, name), name
     assert L.gemm_probe_workgroups() == 256
     assert L.gemm_probe_mfma(1, -2, 8, 8, None) == gemm.GEMM_ERR_INVALID_ARG
     assert L.gemm_probe_mfma(1, 2, None, 8, None) == gemm.GEMM_ERR_INVALID_ARG
     assert L.gemm_probe_mfma(9, 2, 8, 8, None) == gemm.GEMM_ERR_INVALID_ARG
+    assert L.gemm_probe_mfma16(0, 2, 8, 8, None) == gemm.GEMM_ERR_INVALID_ARG  # no FP32 16 x 16 form
+    assert L.gemm_probe_mfma16(1, -2, 8, 8, None) == gemm.GEMM_ERR_INVALID_ARG
     assert L.gemm_probe_clock(-1, 8, 8, None) == gemm.GEMM_ERR_INVALID_ARG
 
 

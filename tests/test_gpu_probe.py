@@ -20,10 +20,10 @@ def test_clock_probe_reads_a_plausible_clock():
     assert r["span_us"] > 1.0
 
 
-@pytest.mark.parametrize("dt", sorted(PEAK))
-def test_mfma_ceiling_is_bounded_by_the_nominal_peak(dt):
-    r = probe.mfma_ceiling(dt, 2000, repeats=1)
-    log(f"mfma ceiling dtype {dt}: {r}")
+@pytest.mark.parametrize("dt,block", [(d, 32) for d in sorted(PEAK)] + [(d, 16) for d in sorted(PEAK) if d != gemm.DTYPE_F32])
+def test_mfma_ceiling_is_bounded_by_the_nominal_peak(dt, block):
+    r = probe.mfma_ceiling(dt, 2000, repeats=1, block=block)
+    log(f"mfma ceiling dtype {dt} block {block}: {r}")
     # The nominal peak assumes 2.4 GHz: the measured rate cannot beat the
     # peak scaled to the clock the workgroups reported (plus timing slack).
     assert 0.2 * PEAK[dt] < r["tflops"] <= PEAK[dt] * r["clock_mhz_max"] / 2400.0 * 1.05
