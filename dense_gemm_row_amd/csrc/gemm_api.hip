@@ -87,9 +87,7 @@ int out_dtype(int d) { return is_f8(d) ? GEMM_DTYPE_BF16 : d; }
 // pipeline fill, epilogue).  With few CUs busy the 16- and 8-bit matrix
 // instructions keep a higher clock, so eff1 exceeds the full-GPU eff of the
 // large tiles; small tiles cannot hide their latency alone and fall below
-// it.  The 16 x 16 instruction's tiles (_mi16) need more cycles per slice
-// and win only where the power limit sets the clock: below the 32 x 32
-// tile alone, above it with the GPU full.  E5M2 takes E4M3's figures (same tiles); variants not listed use eff
+// it.  E5M2 takes E4M3's figures (same tiles); variants not listed use eff
 // and no fixed cost.
 struct AloneRate {
   const char* name;
@@ -111,8 +109,8 @@ const AloneRate kAlone[] = {
     {"tr_f16_256x128x64_w128x64_s3_p4", 1.835f, 5.86f},
     {"tr_f16_256x128x64_w128x64_s3_p2", 1.854f, 6.37f},
     {"tr_f16_256x256x64_w128x128_s2_ps", 1.556f, 8.31f},
-    {"tr_f16_256x256x64_w128x128_s2_mi16", 1.477f, 7.80f},
-    {"tr_f16_256x256x64_w128x128_s2_mi16_ps", 1.422f, 9.43f},
+    {"tr_f16_256x256x64_w128x128_s2_mi16", 1.859f, 8.60f},
+    {"tr_f16_256x256x64_w128x128_s2_mi16_ps", 1.625f, 9.82f},
     {"mfma_f16_256x256x64_w128x128", 0.840f, 8.11f}, {"mfma_f16_256x128x64_w128x64", 0.545f, 6.93f},
     {"mfma_f16_128x256x64_w64x128", 0.547f, 2.75f}, {"mfma_f16_128x128x64_w64x64", 0.381f, 2.74f},
     {"mfma_f16_64x64x64_w32x32", 0.126f, 1.30f}, {"tr_bf16_256x256x64_w128x128_s2", 1.554f, 8.22f},
@@ -124,8 +122,8 @@ const AloneRate kAlone[] = {
     {"tr_bf16_256x128x64_w128x64_s3_p4", 1.841f, 5.98f},
     {"tr_bf16_256x128x64_w128x64_s3_p2", 1.870f, 6.54f},
     {"tr_bf16_256x256x64_w128x128_s2_ps", 1.554f, 8.22f},
-    {"tr_bf16_256x256x64_w128x128_s2_mi16", 1.474f, 8.16f},
-    {"tr_bf16_256x256x64_w128x128_s2_mi16_ps", 1.421f, 9.62f},
+    {"tr_bf16_256x256x64_w128x128_s2_mi16", 1.862f, 8.94f},
+    {"tr_bf16_256x256x64_w128x128_s2_mi16_ps", 1.629f, 9.97f},
     {"mfma_bf16_256x256x64_w128x128", 0.849f, 7.43f},
     {"mfma_bf16_256x128x64_w128x64", 0.547f, 5.94f},
     {"mfma_bf16_128x256x64_w64x128", 0.546f, 2.76f}, {"mfma_bf16_128x128x64_w64x64", 0.381f, 2.79f},
@@ -145,8 +143,9 @@ double model_rate(int dtype);
 // overlap the neighbouring tiles' work), and slice_us, the extra loop time
 // per K slice (the previous tile's C stores share the memory path).  Per
 // round, time = twin's - saved_us + slices * slice_us: the persistent form
-// wins at short K (below about 53 slices for 16-bit, 33 for 8-bit).  E5M2
-// takes E4M3's figures.
+// wins at short K (below about 53 slices for 16-bit, 33 for 8-bit; for the
+// 16 x 16 tiles, whose one-tile form already overlaps more of a tile's
+// fixed cost, 17).  E5M2 takes E4M3's figures.
 struct PsRate {
   const char* name;
   float saved_us, slice_us;
@@ -154,8 +153,8 @@ struct PsRate {
 const PsRate kPs[] = {
     {"tr_f16_256x256x64_w128x128_s2_ps", 3.7f, 0.07f},
     {"tr_bf16_256x256x64_w128x128_s2_ps", 3.7f, 0.07f},
-    {"tr_f16_256x256x64_w128x128_s2_mi16_ps", 3.7f, 0.07f},
-    {"tr_bf16_256x256x64_w128x128_s2_mi16_ps", 3.7f, 0.07f},
+    {"tr_f16_256x256x64_w128x128_s2_mi16_ps", 1.2f, 0.07f},
+    {"tr_bf16_256x256x64_w128x128_s2_mi16_ps", 1.2f, 0.07f},
     {"tr_f8_256x256x128_w128x128_s2_ps", 3.7f, 0.11f},
 };
 

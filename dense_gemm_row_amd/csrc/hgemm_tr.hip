@@ -271,6 +271,26 @@ struct Shape {
   __host__ __device__ static constexpr int bt_frag(int wn0, int nb, int j, int l, int part = 0) {
     return bt_byte(wn0 + MI * nb + l % MI, FR * (LG * j + l / MI) + part);
   }
+  // 16 x 16 K loop: each k step is a fixed sequence of the MB x NB MFMAs;
+  // the next step's operand read f (A's MB operands, then B's NB) is
+  // placed after MFMA rd_after(f), the slice's copy q after MFMA
+  // cp_after(q) (at most one of each after any MFMA).  The copies go one
+  // per four MFMAs (one per 64 cycles of the matrix core): packed one per
+  // MFMA they stalled the MFMA stream (2.9 K against 2.3 K cycles per
+  // slice at 4096^3; every second MFMA, 2.6 K), LDS-direct copies stalling
+  // at issue while the vector memory path is busy.
+  __host__ __device__ static constexpr int rd_after(int f) { return 4 * f; }
+  __host__ __device__ static constexpr int cp_after(int q) { return 4 * q + 2; }
+  __host__ __device__ static constexpr int rd_at(int i) {
+    for (int f = 0; f < MB + NB; ++f)
+      if (rd_after(f) == i) return f;
+    return -1;
+  }
+  __host__ __device__ static constexpr int cp_at(int i) {
+    for (int q = 0; q < LPS; ++q)
+      if (cp_after(q) == i) return q;
+    return -1;
+  }
   // Accumulator block (nb, mb), register 4rq + e of lane l: C[m][n] with
   // m = MI*mb + l%MI and n = MI*nb + 8rq + 4(l/MI) + e (wave-tile
   // coordinates): four consecutive columns of one row per register group.
@@ -722,17 +742,19 @@ hgemm_tr_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
 
   // 16 x 16 blocks: k step `cur` as a fixed sequence, MFMA i on block
   // (i / MB, i % MB), with scheduling barriers between them that place the
-  // next step's operand reads (rd(f) after MFMA 4f: A's MB operands first,
-  // which the next step's first MFMAs need, then B's) and the copies
-  // (cp(q) after MFMA q).  The builtin's scheduling groups cannot place
-  // inline assembly.
+  // next step's operand reads (rd(f) after MFMA rd_after(f): A's MB
+  // operands first, which the next step's first MFMAs need, then B's) and
+  // the copies (cp(q) after MFMA cp_after(q)).  The builtin's scheduling
+  // groups cannot place inline assembly.
   auto mma16 = [&](int cur, auto&& rd, auto&& cp) __attribute__((always_inline)) {
     if constexpr (S::MI == 16 && !S::F8) {
+      static_assert(S::rd_after(MB + NB - 1) < MB * NB && S::cp_after(S::LPS - 1) < MB * NB,
+                    "every operand read and copy has its MFMA");
       static_for([&](auto I) __attribute__((always_inline)) {
         constexpr int i = decltype(I)::value;
         mfma16_asm<S::TY>(acc[i / MB][i % MB], fb[cur][i / MB], fa[cur][i % MB]);
-        if constexpr (i % 4 == 0 && i / 4 < MB + NB) rd(IC<i / 4>{});
-        cp(IC<i>{});
+        if constexpr (S::rd_at(i) >= 0) rd(IC<S::rd_at(i)>{});
+        if constexpr (S::cp_at(i) >= 0) cp(IC<S::cp_at(i)>{});
         __builtin_amdgcn_sched_barrier(0);
       }, std::make_integer_sequence<int, MB * NB>{});
     }
@@ -1177,11 +1199,13 @@ hgemm_tr_persistent_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_byt
   // 16 x 16 blocks: the one-tile kernel's fixed MFMA sequence (mma16 there).
   auto mma16 = [&](int cur, auto&& rd, auto&& cp) __attribute__((always_inline)) {
     if constexpr (S::MI == 16 && !S::F8) {
+      static_assert(S::rd_after(MB + NB - 1) < MB * NB && S::cp_after(S::LPS - 1) < MB * NB,
+                    "every operand read and copy has its MFMA");
       static_for([&](auto I) __attribute__((always_inline)) {
         constexpr int i = decltype(I)::value;
         mfma16_asm<S::TY>(acc[i / MB][i % MB], fb[cur][i / MB], fa[cur][i % MB]);
-        if constexpr (i % 4 == 0 && i / 4 < MB + NB) rd(IC<i / 4>{});
-        cp(IC<i>{});
+        if constexpr (S::rd_at(i) >= 0) rd(IC<S::rd_at(i)>{});
+        if constexpr (S::cp_at(i) >= 0) cp(IC<S::cp_at(i)>{});
         __builtin_amdgcn_sched_barrier(0);
       }, std::make_integer_sequence<int, MB * NB>{});
     }
@@ -1757,8 +1781,8 @@ constexpr LaunchFn at_launch() {
 
 // The 16-bit LDS layouts and data path do not depend on the element type,
 // so FP16 and BF16 share the tiles and the measured tile efficiencies.  The
-// 16 x 16 instruction's form of the default tile (_mi16) runs 2-9 % above
-// it with all CUs busy (FP16 4096^3 +9 %, 8192^3 +5 %; BF16 +1-5 %).  FP8
+// 16 x 16 instruction's form of the default tile (_mi16) runs 13-16 % above
+// it with all CUs busy (FP16 4096^3 +15 %, BF16 +13 %).  FP8
 // moves 128 k per slice in the same bytes; its B rows must span 256 bytes
 // (the 2*(k%8) chunk XOR), so its tiles are 256 columns wide.
 #define HGEMM_TR_TABLE(TY, DT, TAG)                                   \
@@ -1771,8 +1795,8 @@ constexpr LaunchFn at_launch() {
    HGEMM_TR_VARIANT_PW(TY, DT, TAG, 256, 128, 128, 64, 64, 3, 4, "_p4", 0.895f),   \
    HGEMM_TR_VARIANT_PW(TY, DT, TAG, 256, 128, 128, 64, 64, 3, 2, "_p2", 0.89f),    \
    HGEMM_TR_VARIANT_PS(TY, DT, TAG, 256, 256, 128, 128, 64, 1.00f),               \
-   HGEMM_TR_VARIANT_MI(TY, DT, TAG, 256, 256, 128, 128, 64, 2, 0, 16, "_mi16", 1.05f), \
-   HGEMM_TR_VARIANT_PS_MI(TY, DT, TAG, 256, 256, 128, 128, 64, 16, "_mi16", 1.05f)}
+   HGEMM_TR_VARIANT_MI(TY, DT, TAG, 256, 256, 128, 128, 64, 2, 0, 16, "_mi16", 1.14f), \
+   HGEMM_TR_VARIANT_PS_MI(TY, DT, TAG, 256, 256, 128, 128, 64, 16, "_mi16", 1.14f)}
 
 const Variant kVariants[] = HGEMM_TR_TABLE(0, GEMM_DTYPE_F16, "f16");
 const Variant kVariantsBf[] = HGEMM_TR_TABLE(1, GEMM_DTYPE_BF16, "bf16");
