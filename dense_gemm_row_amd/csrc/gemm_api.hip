@@ -130,6 +130,8 @@ const AloneRate kAlone[] = {
     {"mfma_bf16_64x64x64_w32x32", 0.126f, 1.39f}, {"tr_f8_256x256x128_w128x128_s2", 1.774f, 8.60f},
     {"tr_f8_256x256x64_w128x128_s4", 1.597f, 8.70f},
     {"tr_f8_256x256x128_w128x128_s2_ps", 1.774f, 8.60f},
+    {"tr_f8_256x256x128_w128x128_s2_mi16", 1.778f, 9.00f},
+    {"tr_f8_256x256x128_w128x128_s2_mi16_ps", 1.663f, 9.72f},
     {"tr_f8_128x256x128_w64x128_s3", 1.687f, 6.30f},
     {"tr_f8_128x256x128_w64x128_s3_p4", 1.788f, 6.16f},
 };

@@ -279,8 +279,31 @@ struct Shape {
   // MFMA they stalled the MFMA stream (2.9 K against 2.3 K cycles per
   // slice at 4096^3; every second MFMA, 2.6 K), LDS-direct copies stalling
   // at issue while the vector memory path is busy.
-  __host__ __device__ static constexpr int rd_after(int f) { return 4 * f; }
-  __host__ __device__ static constexpr int cp_after(int q) { return 4 * q + 2; }
+  // With 8-bit operands (32 bytes per lane) the B operands have one
+  // register set (FBS): B's block nb is re-read right after the last MFMA
+  // that uses it (MB*nb + MB-1), 56 MFMAs before the next step needs it,
+  // and only A's operands alternate between two sets; the A reads go early
+  // (after MFMA 2f), since the next step's first MFMAs need all of them.
+  static constexpr int FBS = (MI == 16 && F8) ? 1 : 2;
+  __host__ __device__ static constexpr int fb_set(int buf) { return FBS == 1 ? 0 : buf; }
+  // With one k step per slice (FP8's 128-k slices), the slice's barrier
+  // sits inside the step, after MFMA BAR_AFTER, so that the previous step's
+  // last operand reads (issued after its last MFMA) land meanwhile; the
+  // reads from the next stage and the copies come after it.
+  static constexpr int BAR_AFTER = (MI == 16 && KS == 1) ? 15 : -1;
+  __host__ __device__ static constexpr int rd_after(int f) {
+    return FBS == 1 ? (f < MB ? BAR_AFTER + 1 + 2 * f
+                              : (MB * (f - MB) + MB - 1 > BAR_AFTER + 1 + 2 * MB + 4 * (f - MB)
+                                     ? MB * (f - MB) + MB - 1
+                                     : BAR_AFTER + 1 + 2 * MB + 4 * (f - MB)))
+                    : BAR_AFTER + 1 + 4 * f;
+  }
+  // (One copy per 64 matrix-core cycles: every fourth 16-cycle 16-bit MFMA,
+  // every second 32-cycle FP8 one; FP8's copies land before the next
+  // slice's barrier, 32 MFMAs after the last one.)
+  __host__ __device__ static constexpr int cp_after(int q) {
+    return BAR_AFTER >= 0 ? BAR_AFTER + 2 + (F8 ? 2 : 4) * q : 4 * q + 2;
+  }
   __host__ __device__ static constexpr int rd_at(int i) {
     for (int f = 0; f < MB + NB; ++f)
       if (rd_after(f) == i) return f;
@@ -360,8 +383,8 @@ __device__ __forceinline__ void loop_barrier() {
 }
 #define SGB(mask, n) __builtin_amdgcn_sched_group_barrier((mask), (n), 0)
 
-// The 16 x 16 matrix instruction for 16-bit operands as inline assembly,
-// its accumulator tied in place ("+a").  With the builtin, the register
+// The 16 x 16 matrix instruction as inline assembly (16-bit operands: k 32;
+// FP8: k 128), its accumulator tied in place ("+a").  With the builtin, the register
 // allocator kept reassigning the 64 four-register accumulators of a
 // 128 x 128 wave tile and moved most of them between registers on every
 // pass of the K loop (hundreds of extra instructions per slice); tied
@@ -370,13 +393,20 @@ __device__ __forceinline__ void loop_barrier() {
 // only before a guard (mfma_guard) that precedes the first MFMA, read them
 // only after one that follows the last, and (b) feed srcA / srcB only from
 // LDS reads, whose arrival the compiler's own waits cover.
-template <int TY>
-__device__ __forceinline__ void mfma16_asm(f32x4& c, const f16x8& a, const f16x8& b) {
-  static_assert(TY == 0 || TY == 1, "16-bit operands");
+template <int TY, class Frag>
+__device__ __forceinline__ void mfma16_asm(f32x4& c, const Frag& a, const Frag& b) {
+  // (Device pass only: the host pass checks asm operand constraints against
+  // the host target, which has no 256-bit "v" registers.)
+#if defined(__HIP_DEVICE_COMPILE__)
   if constexpr (TY == 0)
     asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
-  else
+  else if constexpr (TY == 1)
     asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+  else if constexpr (TY == 2)  // E4M3 operands (format fields 0)
+    asm volatile("v_mfma_f32_16x16x128_f8f6f4 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+  else  // E5M2 operands (format fields 1)
+    asm volatile("v_mfma_f32_16x16x128_f8f6f4 %0, %1, %2, %0 cbsz:1 blgp:1" : "+a"(c) : "v"(a), "v"(b));
+#endif
 }
 
 // 24 wait states, with nothing scheduled across: more than any matrix-core
@@ -661,7 +691,7 @@ hgemm_tr_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
 
   // An operand: 8 16-bit or 32 8-bit values per lane.
   typedef std::conditional_t<S::F8, i32x8_t, f16x8> Frag;
-  Frag fa[2][MB], fb[2][NB];
+  Frag fa[2][MB], fb[S::FBS][NB];
   // Two 16-byte chunks of one lane's FP8 operand (positions differ by the
   // row's XOR).
   auto two_chunks = [](const unsigned char* p0, const unsigned char* p1) __attribute__((always_inline)) {
@@ -696,11 +726,11 @@ hgemm_tr_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
   };
   auto load_b = [&](int buf, const unsigned char* lb, int j, int nb) __attribute__((always_inline)) {
     if constexpr (!S::BT)
-      fb[buf][nb] = tr_operand(lb + b_fb[nb] + S::KW * j * S::B_ROW, S::B_ROW);
+      fb[S::fb_set(buf)][nb] = tr_operand(lb + b_fb[nb] + S::KW * j * S::B_ROW, S::B_ROW);
     else if constexpr (S::F8)
-      fb[buf][nb] = two_chunks(lb + b_fb[2 * j] + nb * S::MI * S::B_ROW, lb + b_fb[2 * j + 1] + nb * S::MI * S::B_ROW);
+      fb[S::fb_set(buf)][nb] = two_chunks(lb + b_fb[2 * j] + nb * S::MI * S::B_ROW, lb + b_fb[2 * j + 1] + nb * S::MI * S::B_ROW);
     else
-      fb[buf][nb] = *(const lds_f16x8*)(lb + b_fb[j] + nb * S::MI * S::B_ROW);
+      fb[S::fb_set(buf)][nb] = *(const lds_f16x8*)(lb + b_fb[j] + nb * S::MI * S::B_ROW);
   };
   auto load_frags = [&](int buf, const unsigned char* la, const unsigned char* lb, int j)
       __attribute__((always_inline)) {
@@ -746,13 +776,18 @@ hgemm_tr_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
   // operands first, which the next step's first MFMAs need, then B's) and
   // the copies (cp(q) after MFMA cp_after(q)).  The builtin's scheduling
   // groups cannot place inline assembly.
-  auto mma16 = [&](int cur, auto&& rd, auto&& cp) __attribute__((always_inline)) {
-    if constexpr (S::MI == 16 && !S::F8) {
+  auto mma16 = [&](int cur, auto&& rd, auto&& cp, auto&& bar) __attribute__((always_inline)) {
+    if constexpr (S::MI == 16) {
       static_assert(S::rd_after(MB + NB - 1) < MB * NB && S::cp_after(S::LPS - 1) < MB * NB,
                     "every operand read and copy has its MFMA");
       static_for([&](auto I) __attribute__((always_inline)) {
         constexpr int i = decltype(I)::value;
-        mfma16_asm<S::TY>(acc[i / MB][i % MB], fb[cur][i / MB], fa[cur][i % MB]);
+        mfma16_asm<S::TY>(acc[i / MB][i % MB], fb[S::fb_set(cur)][i / MB], fa[cur][i % MB]);
+        if constexpr (i == S::BAR_AFTER) {
+          __builtin_amdgcn_sched_barrier(0);
+          bar();
+          __builtin_amdgcn_sched_barrier(0);
+        }
         if constexpr (S::rd_at(i) >= 0) rd(IC<S::rd_at(i)>{});
         if constexpr (S::cp_at(i) >= 0) cp(IC<S::cp_at(i)>{});
         __builtin_amdgcn_sched_barrier(0);
@@ -786,12 +821,17 @@ hgemm_tr_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
         constexpr int j = decltype(J)::value;
         mma16(S::frag_set(c, j),
               [&](auto F) __attribute__((always_inline)) { rd_op(S::frag_set(c, j + 1), ca, cb, j + 1, F); },
-              [](auto) {});
+              [](auto) {}, [] {});
       }, std::make_integer_sequence<int, KS - 1>{});
-      loop_barrier<(NS - 2) * S::LPS>();
-      __builtin_amdgcn_sched_barrier(0);
-      // Last step: slice t+NS's copies into stage c, one after each of the
-      // first LPS MFMAs, and the next stage's first operands.
+      // Slice t+1 landed and stage c read by every wave: before the last
+      // step, or inside it (BAR_AFTER).
+      auto bar = [&]() __attribute__((always_inline)) { loop_barrier<(NS - 2) * S::LPS>(); };
+      if constexpr (S::BAR_AFTER < 0) {
+        bar();
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // Last step: slice t+NS's copies into stage c and the next stage's
+      // first operands (after cp_after / rd_after).
       mma16(S::frag_set(c, KS - 1),
             [&](auto F) __attribute__((always_inline)) {
               rd_op(S::frag_set(c + 1, 0), A_of(IC<n>{}), B_of(IC<n>{}), 0, F);
@@ -802,6 +842,9 @@ hgemm_tr_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
                 issue_copy<S>(Ab, Bb, a_bytes, b_bytes, t + NS, t + NS < T,
                               t + NS == T - 1 ? a_vo_tail : a_vo, t + NS == T - 1 ? b_vo_tail : b_vo,
                               ca, cb, lw, lda, ldb, q);
+            },
+            [&]() __attribute__((always_inline)) {
+              if constexpr (S::BAR_AFTER >= 0) bar();
             });
       return;
     }
@@ -1137,7 +1180,7 @@ hgemm_tr_persistent_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_byt
                     (la_), (lb_), lw, lda, ldb)
 
   typedef std::conditional_t<S::F8, i32x8_t, f16x8> Frag;
-  Frag fa[2][MB], fb[2][NB];
+  Frag fa[2][MB], fb[S::FBS][NB];
   auto two_chunks = [](const unsigned char* p0, const unsigned char* p1) __attribute__((always_inline)) {
     const u32x4 x0 = *(const lds_u32x4*)p0, x1 = *(const lds_u32x4*)p1;
     return __builtin_bit_cast(i32x8_t, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -1164,7 +1207,7 @@ hgemm_tr_persistent_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_byt
       fa[buf][mb] = *(const lds_f16x8*)(la + a_fb[j] + mb * S::MI * S::A_ROW);
   };
   auto load_b = [&](int buf, const unsigned char* lb, int j, int nb) __attribute__((always_inline)) {
-    fb[buf][nb] = tr_operand(lb + b_fb[nb] + S::KW * j * S::B_ROW, S::B_ROW);
+    fb[S::fb_set(buf)][nb] = tr_operand(lb + b_fb[nb] + S::KW * j * S::B_ROW, S::B_ROW);
   };
   auto load_frags = [&](int buf, const unsigned char* la, const unsigned char* lb, int j)
       __attribute__((always_inline)) {
@@ -1197,13 +1240,18 @@ hgemm_tr_persistent_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_byt
   constexpr int NMMA = MB * NB;
   constexpr int NRD = MB * FR + S::TRN * NB;
   // 16 x 16 blocks: the one-tile kernel's fixed MFMA sequence (mma16 there).
-  auto mma16 = [&](int cur, auto&& rd, auto&& cp) __attribute__((always_inline)) {
-    if constexpr (S::MI == 16 && !S::F8) {
+  auto mma16 = [&](int cur, auto&& rd, auto&& cp, auto&& bar) __attribute__((always_inline)) {
+    if constexpr (S::MI == 16) {
       static_assert(S::rd_after(MB + NB - 1) < MB * NB && S::cp_after(S::LPS - 1) < MB * NB,
                     "every operand read and copy has its MFMA");
       static_for([&](auto I) __attribute__((always_inline)) {
         constexpr int i = decltype(I)::value;
-        mfma16_asm<S::TY>(acc[i / MB][i % MB], fb[cur][i / MB], fa[cur][i % MB]);
+        mfma16_asm<S::TY>(acc[i / MB][i % MB], fb[S::fb_set(cur)][i / MB], fa[cur][i % MB]);
+        if constexpr (i == S::BAR_AFTER) {
+          __builtin_amdgcn_sched_barrier(0);
+          bar();
+          __builtin_amdgcn_sched_barrier(0);
+        }
         if constexpr (S::rd_at(i) >= 0) rd(IC<S::rd_at(i)>{});
         if constexpr (S::cp_at(i) >= 0) cp(IC<S::cp_at(i)>{});
         __builtin_amdgcn_sched_barrier(0);
@@ -1258,10 +1306,15 @@ hgemm_tr_persistent_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_byt
         constexpr int j = decltype(J)::value;
         mma16(S::frag_set(c, j),
               [&](auto F) __attribute__((always_inline)) { rd_op(S::frag_set(c, j + 1), ca, cb, j + 1, F); },
-              [](auto) {});
+              [](auto) {}, [] {});
       }, std::make_integer_sequence<int, KS - 1>{});
-      loop_barrier<0>();  // slice t+1 landed (and any earlier stores done)
-      __builtin_amdgcn_sched_barrier(0);
+      // Slice t+1 landed (and any earlier stores done): before the last
+      // step, or inside it (BAR_AFTER).
+      auto bar = [&]() __attribute__((always_inline)) { loop_barrier<0>(); };
+      if constexpr (S::BAR_AFTER < 0) {
+        bar();
+        __builtin_amdgcn_sched_barrier(0);
+      }
       const int s = has_next && t + 2 >= T ? t + 2 - T : t + 2;
       mma16(S::frag_set(c, KS - 1),
             [&](auto F) __attribute__((always_inline)) {
@@ -1272,6 +1325,9 @@ hgemm_tr_persistent_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_byt
               if constexpr (q < S::LPS)
                 issue_copy_ps<S>(Ab, Bb, a_bytes, b_bytes, s, s < T, s == T - 1, a_vo, a_tail, b_vo, ca, cb,
                                  lw, lda, ldb, q);
+            },
+            [&]() __attribute__((always_inline)) {
+              if constexpr (S::BAR_AFTER >= 0) bar();
             });
       return;
     }
@@ -1807,7 +1863,9 @@ const Variant kVariantsBf[] = HGEMM_TR_TABLE(1, GEMM_DTYPE_BF16, "bf16");
    HGEMM_TR_VARIANT(TY, DT, TAG, 256, 256, 128, 128, 64, 4, 0.85f),               \
    HGEMM_TR_VARIANT(TY, DT, TAG, 128, 256, 64, 128, 128, 3, 0.89f),               \
    HGEMM_TR_VARIANT_PW(TY, DT, TAG, 128, 256, 64, 128, 128, 3, 4, "_p4", 0.88f),  \
-   HGEMM_TR_VARIANT_PS(TY, DT, TAG, 256, 256, 128, 128, 128, 1.00f)}
+   HGEMM_TR_VARIANT_PS(TY, DT, TAG, 256, 256, 128, 128, 128, 1.00f),              \
+   HGEMM_TR_VARIANT_MI(TY, DT, TAG, 256, 256, 128, 128, 128, 2, 0, 16, "_mi16", 1.00f), \
+   HGEMM_TR_VARIANT_PS_MI(TY, DT, TAG, 256, 256, 128, 128, 128, 16, "_mi16", 1.00f)}
 const Variant kVariantsF8[] = HGEMM_TR_F8_TABLE(2, GEMM_DTYPE_F8, "f8");
 const Variant kVariantsE5[] = HGEMM_TR_F8_TABLE(3, GEMM_DTYPE_E5M2, "e5m2");
 

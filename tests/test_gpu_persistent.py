@@ -7,8 +7,8 @@ oracle) at grids of more than 256 tiles, so that workgroups take two tiles
 (ragged M and N, a partial last K slice, and exactly two tiles each); odd
 slice counts, which run the one-tile kernel; random inputs at 8192 x 8192 x
 1024 (1024 tiles, four per workgroup) on sampled rows; and determinism.
-Every 16-bit and 8-bit type, and for 16-bit types both matrix-instruction
-block sizes (``_s2_ps`` with 32 x 32 blocks, ``_s2_mi16_ps`` with 16 x 16).
+Every 16-bit and 8-bit type, each with both matrix-instruction block
+sizes (``_s2_ps`` with 32 x 32 blocks, ``_s2_mi16_ps`` with 16 x 16).
 (The FP16 full-size parity test checks every element at 8192 x 8192 x 1024,
 whose default pick is this form.)"""
 import numpy as np
@@ -28,8 +28,8 @@ SHAPES16 = [(4352, 4352, 384), (4100, 4104, 360), (8192, 4096, 128)]
 SHAPES8 = [(4352, 4352, 512), (4100, 4112, 480), (8192, 4096, 256)]
 
 
-# (kind, persistent variant suffix): 16-bit types have a 16 x 16 form too.
-FORMS = [(k, "_s2_ps") for k in sorted(TYPES)] + [("f16", "_s2_mi16_ps"), ("bf16", "_s2_mi16_ps")]
+# (kind, persistent variant suffix): both instruction block sizes.
+FORMS = [(k, "_s2_ps") for k in sorted(TYPES)] + [(k, "_s2_mi16_ps") for k in sorted(TYPES)]
 FORM_IDS = [k + sfx.replace("_s2", "").replace("_ps", "") for k, sfx in FORMS]
 
 

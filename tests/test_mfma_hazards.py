@@ -26,7 +26,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 LIB = os.path.join(ROOT, "dense_gemm_row_amd", "libgemm.so")
 OBJDUMP = shutil.which("llvm-objdump") or "/opt/rocm/llvm/bin/llvm-objdump"
-MNEMONIC = re.compile(r"v_mfma_f32_16x16x32_(f16|bf16)\b")
+MNEMONIC = re.compile(r"v_mfma_f32_16x16x(32_f16|32_bf16|128_f8f6f4)\b")
 BEFORE, AFTER = 4, 20
 
 
@@ -126,5 +126,5 @@ def test_inline_matrix_instructions_keep_hazard_distances(tmp_path):
             bad = findings(ins)
             assert not bad, (m.group(1), bad[:3])
             checked += 1
-    # Every 16-bit type's one-tile kernel forms and the persistent form.
-    assert checked >= 8, checked
+    # Every 16- and 8-bit type's one-tile kernel forms and the persistent form.
+    assert checked >= 16, checked
