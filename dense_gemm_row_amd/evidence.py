@@ -314,7 +314,8 @@ def probe_summary(bench_log: str) -> list:
            "# clock: d(s_memtime) / d(s_memrealtime) x 100 MHz over each workgroup's K loop in one traced",
            "# launch (gemm_trace_set) inside a block of 20; fill = entry to first K slice in LDS; epilogue =",
            "# loop end to C issued; spread = last minus first loop end over workgroups.  ceiling = the",
-           "# register-only matrix-core stream of the same instruction (gemm_probe_mfma) and its clock."]
+           "# register-only matrix-core stream of the same instruction (gemm_probe_mfma; gemm_probe_mfma16 for",
+           "# the 16 x 16 tiles, ceiling_block=16) and its clock."]
     for k, v in bj["kernels"].items():
         t = v.get("trace_us", {})
         out.append(f"{k} variant={v['variant']} ms_mean={v['ms_mean']} tflops={v['tflops']} "
@@ -324,7 +325,8 @@ def probe_summary(bench_log: str) -> list:
                    f"loop_us={t.get('loop')} (min {t.get('loop_min')} max {t.get('loop_max')}) "
                    f"epilogue_us={t.get('epilogue')} loop_end_spread_us={t.get('loop_end_spread')} "
                    f"span_us={t.get('span')} ceiling_tflops={v.get('mfma_ceiling_tflops')} "
-                   f"ceiling_clock_mhz={v.get('mfma_ceiling_clock_mhz')} frac_of_ceiling={v.get('frac_of_ceiling')}")
+                   f"ceiling_clock_mhz={v.get('mfma_ceiling_clock_mhz')} ceiling_block={v.get('mfma_ceiling_block', 32)} "
+                   f"frac_of_ceiling={v.get('frac_of_ceiling')}")
     ab = (bj.get("ablation") or {}).get("simt_f32")
     if ab:
         out.append(f"simt_f32 variant={ab['variant']} ms_mean={ab['ms_mean']} tflops={ab['tflops']} "
