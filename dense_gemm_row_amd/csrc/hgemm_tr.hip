@@ -285,7 +285,7 @@ struct Shape {
   // and only A's operands alternate between two sets; the A reads go early
   // (after MFMA 2f), since the next step's first MFMAs need all of them.
   static constexpr int FBS = (MI == 16 && F8) ? 1 : 2;
-  __host__ __device__ static constexpr int fb_set(int buf) { return FBS == 1 ? 0 : buf; }
+  __host__ __device__ static constexpr int fb_set(int buf, int nb) { return FBS == 1 ? 0 * nb : buf; }
   // With one k step per slice (FP8's 128-k slices), the slice's barrier
   // sits inside the step, after MFMA BAR_AFTER, so that the previous step's
   // last operand reads (issued after its last MFMA) land meanwhile; the
@@ -303,6 +303,25 @@ struct Shape {
   // slice's barrier, 32 MFMAs after the last one.)
   __host__ __device__ static constexpr int cp_after(int q) {
     return BAR_AFTER >= 0 ? BAR_AFTER + 2 + (F8 ? 2 : 4) * q : 4 * q + 2;
+  }
+  // Every operand read and copy has its own slot among the step's MFMAs,
+  // a single-set B operand is re-read only after its last MFMA, and with
+  // the barrier inside the step everything reads or writes after it.
+  __host__ __device__ static constexpr bool schedule_ok() {
+    for (int a = 0; a < MB + NB; ++a) {
+      const int x = rd_after(a);
+      if (x < 0 || x >= MB * NB || x <= BAR_AFTER) return false;
+      if (a >= MB && fb_set(1, a - MB) == 0 && x < MB * (a - MB) + MB - 1) return false;
+      for (int b = a + 1; b < MB + NB; ++b)
+        if (rd_after(b) == x) return false;
+    }
+    for (int a = 0; a < LPS; ++a) {
+      const int x = cp_after(a);
+      if (x < 0 || x >= MB * NB || x <= BAR_AFTER) return false;
+      for (int b = a + 1; b < LPS; ++b)
+        if (cp_after(b) == x) return false;
+    }
+    return true;
   }
   __host__ __device__ static constexpr int rd_at(int i) {
     for (int f = 0; f < MB + NB; ++f)
@@ -726,11 +745,11 @@ hgemm_tr_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
   };
   auto load_b = [&](int buf, const unsigned char* lb, int j, int nb) __attribute__((always_inline)) {
     if constexpr (!S::BT)
-      fb[S::fb_set(buf)][nb] = tr_operand(lb + b_fb[nb] + S::KW * j * S::B_ROW, S::B_ROW);
+      fb[S::fb_set(buf, nb)][nb] = tr_operand(lb + b_fb[nb] + S::KW * j * S::B_ROW, S::B_ROW);
     else if constexpr (S::F8)
-      fb[S::fb_set(buf)][nb] = two_chunks(lb + b_fb[2 * j] + nb * S::MI * S::B_ROW, lb + b_fb[2 * j + 1] + nb * S::MI * S::B_ROW);
+      fb[S::fb_set(buf, nb)][nb] = two_chunks(lb + b_fb[2 * j] + nb * S::MI * S::B_ROW, lb + b_fb[2 * j + 1] + nb * S::MI * S::B_ROW);
     else
-      fb[S::fb_set(buf)][nb] = *(const lds_f16x8*)(lb + b_fb[j] + nb * S::MI * S::B_ROW);
+      fb[S::fb_set(buf, nb)][nb] = *(const lds_f16x8*)(lb + b_fb[j] + nb * S::MI * S::B_ROW);
   };
   auto load_frags = [&](int buf, const unsigned char* la, const unsigned char* lb, int j)
       __attribute__((always_inline)) {
@@ -778,11 +797,10 @@ hgemm_tr_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_bytes) {
   // groups cannot place inline assembly.
   auto mma16 = [&](int cur, auto&& rd, auto&& cp, auto&& bar) __attribute__((always_inline)) {
     if constexpr (S::MI == 16) {
-      static_assert(S::rd_after(MB + NB - 1) < MB * NB && S::cp_after(S::LPS - 1) < MB * NB,
-                    "every operand read and copy has its MFMA");
+      static_assert(S::schedule_ok(), "16 x 16 step schedule");
       static_for([&](auto I) __attribute__((always_inline)) {
         constexpr int i = decltype(I)::value;
-        mfma16_asm<S::TY>(acc[i / MB][i % MB], fb[S::fb_set(cur)][i / MB], fa[cur][i % MB]);
+        mfma16_asm<S::TY>(acc[i / MB][i % MB], fb[S::fb_set(cur, i / MB)][i / MB], fa[cur][i % MB]);
         if constexpr (i == S::BAR_AFTER) {
           __builtin_amdgcn_sched_barrier(0);
           bar();
@@ -1207,7 +1225,7 @@ hgemm_tr_persistent_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_byt
       fa[buf][mb] = *(const lds_f16x8*)(la + a_fb[j] + mb * S::MI * S::A_ROW);
   };
   auto load_b = [&](int buf, const unsigned char* lb, int j, int nb) __attribute__((always_inline)) {
-    fb[S::fb_set(buf)][nb] = tr_operand(lb + b_fb[nb] + S::KW * j * S::B_ROW, S::B_ROW);
+    fb[S::fb_set(buf, nb)][nb] = tr_operand(lb + b_fb[nb] + S::KW * j * S::B_ROW, S::B_ROW);
   };
   auto load_frags = [&](int buf, const unsigned char* la, const unsigned char* lb, int j)
       __attribute__((always_inline)) {
@@ -1242,11 +1260,10 @@ hgemm_tr_persistent_kernel(Params p, TileMap map, int64_t a_bytes, int64_t b_byt
   // 16 x 16 blocks: the one-tile kernel's fixed MFMA sequence (mma16 there).
   auto mma16 = [&](int cur, auto&& rd, auto&& cp, auto&& bar) __attribute__((always_inline)) {
     if constexpr (S::MI == 16) {
-      static_assert(S::rd_after(MB + NB - 1) < MB * NB && S::cp_after(S::LPS - 1) < MB * NB,
-                    "every operand read and copy has its MFMA");
+      static_assert(S::schedule_ok(), "16 x 16 step schedule");
       static_for([&](auto I) __attribute__((always_inline)) {
         constexpr int i = decltype(I)::value;
-        mfma16_asm<S::TY>(acc[i / MB][i % MB], fb[S::fb_set(cur)][i / MB], fa[cur][i % MB]);
+        mfma16_asm<S::TY>(acc[i / MB][i % MB], fb[S::fb_set(cur, i / MB)][i / MB], fa[cur][i % MB]);
         if constexpr (i == S::BAR_AFTER) {
           __builtin_amdgcn_sched_barrier(0);
           bar();
