@@ -147,12 +147,12 @@ __global__ void __launch_bounds__(256) probe_mfma_kernel(int64_t steps, uint64_t
   sink[blockIdx.x * 256 + threadIdx.x] = t;
 }
 
-// The 16 x 16 form (TY 1..4): per trip, one k step of 64 instructions, the
-// same flops as two 32 x 32 steps.  (No operand rotation across trips: with
+// The 16 x 16 form: per trip, one k step of 64 instructions, the same
+// flops as two 32 x 32 steps (FP32: v_mfma_f32_16x16x4_f32, k 4 against
+// the 32 x 32 form's 2; the others twice the 32 x 32 form's k).  (No operand rotation across trips: with
 // it the compiler moved accumulators between registers inside the loop.)
 template <int TY>
 __global__ void __launch_bounds__(256) probe_mfma16_kernel(int64_t steps, uint64_t* stamps, float* sink) {
-  static_assert(TY >= 1 && TY <= 4, "16- and 8-bit types");
   typedef typename Op<TY>::T T;
   const uint32_t base = (blockIdx.x * 256u + threadIdx.x) * 2u * kFrags;
   T fa[kFrags], fb[kFrags];
@@ -175,7 +175,8 @@ __global__ void __launch_bounds__(256) probe_mfma16_kernel(int64_t steps, uint64
     for (int nb = 0; nb < 8; ++nb)
 #pragma unroll
       for (int mb = 0; mb < 8; ++mb) {
-        if constexpr (TY == 1) acc[nb][mb] = gemm::mfma16<false>(fb[nb], fa[mb], acc[nb][mb]);
+        if constexpr (TY == 0) acc[nb][mb] = __builtin_amdgcn_mfma_f32_16x16x4f32(fb[nb], fa[mb], acc[nb][mb], 0, 0, 0);
+        else if constexpr (TY == 1) acc[nb][mb] = gemm::mfma16<false>(fb[nb], fa[mb], acc[nb][mb]);
         else if constexpr (TY == 2) acc[nb][mb] = gemm::mfma16<true>(fb[nb], fa[mb], acc[nb][mb]);
         else acc[nb][mb] = gemm::mfma_f8<TY - 3>(fb[nb], fa[mb], acc[nb][mb]);
       }
@@ -228,6 +229,7 @@ int32_t gemm_probe_mfma16(int32_t dtype, int64_t steps, uint64_t* stamps, float*
   const dim3 grid(256), block(256);
   hipStream_t s = static_cast<hipStream_t>(stream);
   switch (dtype) {
+    case GEMM_DTYPE_F32: hipLaunchKernelGGL(probe_mfma16_kernel<0>, grid, block, 0, s, steps, stamps, sink); break;
     case GEMM_DTYPE_F16: hipLaunchKernelGGL(probe_mfma16_kernel<1>, grid, block, 0, s, steps, stamps, sink); break;
     case GEMM_DTYPE_BF16: hipLaunchKernelGGL(probe_mfma16_kernel<2>, grid, block, 0, s, steps, stamps, sink); break;
     case GEMM_DTYPE_F8: hipLaunchKernelGGL(probe_mfma16_kernel<3>, grid, block, 0, s, steps, stamps, sink); break;

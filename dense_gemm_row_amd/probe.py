@@ -49,7 +49,7 @@ def _clocks(stamps):
 
 def mfma_ceiling(dtype: int, steps: int, repeats: int = 3, block: int = 32) -> dict:
     """Register-only matrix-core rate of dtype's instruction (`block` 32:
-    the 32 x 32 form, 16: the 16 x 16 form of the 16- and 8-bit types):
+    the 32 x 32 form, 16: the 16 x 16 form):
     TFLOP/s from HIP events (best of `repeats` launches after one warm-up)
     and the clock the workgroups ran at (mean, min, max over workgroups,
     MHz)."""

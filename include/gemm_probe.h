@@ -38,11 +38,11 @@ int32_t gemm_probe_workgroups(void);
  * 16 x 2 x 32 x 32 x k, with k = 2, 16, 16, 64, 64. */
 int32_t gemm_probe_mfma(int32_t dtype, int64_t steps, uint64_t *stamps, float *sink, void *stream);
 
-/* The same stream with the 16 x 16 instructions (dtype 1..4 only:
+/* The same stream with the 16 x 16 instructions (v_mfma_f32_16x16x4_f32,
  * v_mfma_f32_16x16x32_f16 / _bf16, v_mfma_f32_16x16x128_f8f6f4): 8 x 8
  * blocks of 4 accumulators per wave, one k step of 64 instructions per two
  * `steps`, so the flops are those of gemm_probe_mfma with the same `steps`;
- * `steps` even.  FP32 (dtype 0) has no 16 x 16 probe: -1. */
+ * `steps` even. */
 int32_t gemm_probe_mfma16(int32_t dtype, int64_t steps, uint64_t *stamps, float *sink, void *stream);
 
 /* A dependent FMA loop of `iters` trips per lane (64 lanes per workgroup):

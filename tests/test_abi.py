@@ -43,7 +43,7 @@ def test_probe_library_exports_its_header():
     assert L.gemm_probe_mfma(1, -2, 8, 8, None) == gemm.GEMM_ERR_INVALID_ARG
     assert L.gemm_probe_mfma(1, 2, None, 8, None) == gemm.GEMM_ERR_INVALID_ARG
     assert L.gemm_probe_mfma(9, 2, 8, 8, None) == gemm.GEMM_ERR_INVALID_ARG
-    assert L.gemm_probe_mfma16(0, 2, 8, 8, None) == gemm.GEMM_ERR_INVALID_ARG  # no FP32 16 x 16 form
+    assert L.gemm_probe_mfma16(9, 2, 8, 8, None) == gemm.GEMM_ERR_INVALID_ARG
     assert L.gemm_probe_mfma16(1, -2, 8, 8, None) == gemm.GEMM_ERR_INVALID_ARG
     assert L.gemm_probe_clock(-1, 8, 8, None) == gemm.GEMM_ERR_INVALID_ARG
 
