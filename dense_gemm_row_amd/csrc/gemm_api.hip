@@ -98,6 +98,7 @@ const AloneRate kAlone[] = {
     {"dl_f32_256x256x16_w128x128_s4", 1.005f, 7.65f},
     {"dl_f32_256x128x32_w128x64_s3", 0.996f, 7.40f},
     {"dl_f32_128x256x32_w64x128_s3", 1.005f, 5.82f}, {"dl_f32_128x128x32_w64x64_s3", 0.997f, 5.18f},
+    {"dl_f32_64x64x32_w32x32_s4", 0.886f, 3.79f},
     {"mfma_f32_128x128x32_w64x64", 0.759f, 4.35f}, {"mfma_f32_128x128x16_w64x64", 0.735f, 4.51f},
     {"mfma_f32_256x128x32_w128x64", 0.837f, 7.04f}, {"mfma_f32_256x256x32_w128x128", 0.893f, 8.31f},
     {"mfma_f32_128x256x32_w64x128", 0.825f, 4.98f}, {"mfma_f32_64x64x32_w32x32", 0.585f, 3.17f},
@@ -275,9 +276,9 @@ int64_t partial_bytes(int64_t S, int64_t M, int64_t N) {
 //           linearly from 64 to 256 busy CUs to its loop rate with all
 //           CUs busy;
 //   GEMM otherwise:
-//           rounds * 2*bm*bn*Kc / (eff * R / w),  rounds = ceil(WGs / slots),
-//           w = workgroups per CU (as LDS allows, at most 2; 1 when there
-//           are no more workgroups than CUs), slots = 256 w,
+//           ceil(WGs / 256) * 2*bm*bn*Kc / (eff * R): the busiest CU's
+//           tiles at the CU's rate, which its w concurrent workgroups
+//           share (w as LDS allows, at most 2),
 //           R = per-CU rate of the best tile with the GPU full (measured
 //           on MI355X at 4096^3), eff = the variant's relative whole-GPU
 //           rate when full;
@@ -325,13 +326,14 @@ double gemm_seconds(int dtype, const Variant& v, int64_t M, int64_t N, int64_t K
   }
   const int64_t rounds = cdiv(wgs, 256 * per_cu);
   const double eff = v.eff > 0.f ? v.eff : 0.1;
-  // A CU running w workgroups at once gives each 1/w of its rate; with
-  // fewer workgroups than CUs each runs alone.  Split partials, short K
-  // chunks, pay each round's fixed cost on top (eff, measured at K = 4096,
-  // holds it for the unsplit rounds).
-  const int64_t w = wgs <= 256 ? 1 : per_cu;
+  // A CU running w workgroups at once gives each 1/w of its rate, so the
+  // busiest CU, with ceil(WGs / 256) workgroups, takes that many tiles'
+  // work at the CU's rate (a CU whose last workgroup runs alone runs it at
+  // least that fast).  Split partials, short K chunks, pay each round's
+  // fixed cost on top (eff, measured at K = 4096, holds it for the unsplit
+  // rounds).
   const double fixed = S > 1 ? (double)rounds * table().alone[dtype][d.id].fixed_us * 1e-6 : 0.0;
-  return fixed + (double)rounds * 2.0 * d.bm * d.bn * (double)(Kc > 0 ? Kc : 1) * w / (eff * rate);
+  return fixed + (double)cdiv(wgs, 256) * 2.0 * d.bm * d.bn * (double)(Kc > 0 ? Kc : 1) / (eff * rate);
 }
 
 Choice heuristic(int dtype, int64_t M, int64_t N, int64_t K, bool allow_split, bool need_epi = false,

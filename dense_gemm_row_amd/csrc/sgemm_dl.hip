@@ -763,6 +763,7 @@ const Variant kVariants[] = {
     SGEMM_DL_VARIANT(256, 128, 128, 64, 32, 3, 8, 0.97f),
     SGEMM_DL_VARIANT(128, 256, 64, 128, 32, 3, 8, 0.97f),
     SGEMM_DL_VARIANT(128, 128, 64, 64, 32, 3, 8, 0.95f),
+    SGEMM_DL_VARIANT(64, 64, 32, 32, 32, 4, 8, 0.92f),
 };
 
 }  // namespace

@@ -277,19 +277,25 @@ def test_splitk_workspace_and_selection():
     assert gemm.gemm_splitk_workspace_bytes(f32, 2 ** 31, 20, 1000, 2) == -1
     assert gemm.gemm_splitk_workspace_bytes(f32, 2 ** 40, 2 ** 40, 2 ** 20, 2) == -1
     assert gemm.gemm_splitk_workspace_bytes(f32, 2 ** 31 - 1, 2 ** 31 - 1, 1000, 2) == -1
-    for dt in (f32, f16):
-        assert gemm.gemm_select_splitk_config(dt, 1024, 1024, 8192).splits > 1
+    # Shapes with few output tiles and long K: FP32 512 x 512 x 8192 (64
+    # tiles of its smallest LDS-direct tile), 16-bit 1024 x 1024 x 8192 (64
+    # of 128 x 128).
+    for dt, (M, N, K) in ((f32, (512, 512, 8192)), (f16, (1024, 1024, 8192))):
+        assert gemm.gemm_select_splitk_config(dt, M, N, K).splits > 1
         assert gemm.gemm_select_splitk_config(dt, 4096, 4096, 4096).splits == 1
-        assert gemm.gemm_select_config(dt, 1024, 1024, 8192).splits == 1
-        auto = gemm.gemm_splitk_workspace_bytes(dt, 1024, 1024, 8192, 0)
-        assert auto == gemm.gemm_select_splitk_config(dt, 1024, 1024, 8192).splits * 1024 * 1024 * 4
+        assert gemm.gemm_select_config(dt, M, N, K).splits == 1
+        auto = gemm.gemm_splitk_workspace_bytes(dt, M, N, K, 0)
+        assert auto == gemm.gemm_select_splitk_config(dt, M, N, K).splits * M * N * 4
+    # FP32 1024 x 1024 x 8192 fills the chip with 64 x 64 tiles, unsplit.
+    c = gemm.gemm_select_splitk_config(f32, 1024, 1024, 8192)
+    assert c.splits == 1 and c.bm * c.bn == 64 * 64
 
 
 @pytest.mark.parametrize("fn", [gemm.gemm_f32_splitk, gemm.gemm_f16_splitk, gemm.gemm_bf16_splitk])
 def test_splitk_argument_validation(fn):
     # A shape that splits (aligned fake pointers): workspace problems are
     # caught on the host before any launch.
-    M, N, K = 1024, 1024, 8192
+    M, N, K = (512, 512, 8192) if fn is gemm.gemm_f32_splitk else (1024, 1024, 8192)
     cfg = gemm.gemm_select_splitk_config(_dtype_of(fn),
                                          M, N, K)
     A, B, C = 0x100000000, 0x200000000, 0x300000000

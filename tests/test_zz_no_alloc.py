@@ -41,9 +41,10 @@ def _bits(C):
 @pytest.mark.parametrize("kind", KINDS)
 def test_static_matches_workspace_form_twice(kind):
     dt = DTYPE[kind]
-    # First: the library's own split of 1024 x 1024 x 8192; second: a smaller
-    # product with a forced 3-way split of the library's variant for it.
-    big = (1024, 1024, 8192)
+    # First: the library's own split of a few-tile, long-K product (FP32
+    # 512 x 512 x 8192, else 1024 x 1024 x 8192); second: a smaller product
+    # with a forced 3-way split of the library's variant for it.
+    big = (512, 512, 8192) if kind == "f32" else (1024, 1024, 8192)
     small = (200, 144, 4096)
     cfg_big = gemm.gemm_select_splitk_config(dt, *big)
     assert cfg_big.splits > 1
