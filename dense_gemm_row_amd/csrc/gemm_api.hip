@@ -98,7 +98,7 @@ const AloneRate kAlone[] = {
     {"dl_f32_256x256x16_w128x128_s4", 1.005f, 7.65f},
     {"dl_f32_256x128x32_w128x64_s3", 0.996f, 7.40f},
     {"dl_f32_128x256x32_w64x128_s3", 1.005f, 5.82f}, {"dl_f32_128x128x32_w64x64_s3", 0.997f, 5.18f},
-    {"dl_f32_64x64x32_w32x32_s4", 0.886f, 3.79f},
+    {"dl_f32_64x64x64_w32x32_s2", 0.906f, 3.74f},
     {"mfma_f32_128x128x32_w64x64", 0.759f, 4.35f}, {"mfma_f32_128x128x16_w64x64", 0.735f, 4.51f},
     {"mfma_f32_256x128x32_w128x64", 0.837f, 7.04f}, {"mfma_f32_256x256x32_w128x128", 0.893f, 8.31f},
     {"mfma_f32_128x256x32_w64x128", 0.825f, 4.98f}, {"mfma_f32_64x64x32_w32x32", 0.585f, 3.17f},

@@ -84,7 +84,7 @@ struct Shape {
   static constexpr int A_STAGE = AT ? BK * A_ROW : BM * A_ROW, B_STAGE = BT ? BN * B_ROW : BK * B_ROW;
   static constexpr int LDS_BYTES = NS * (A_STAGE + B_STAGE);
   static constexpr int IA = A_STAGE / 1024 / NW, IB = B_STAGE / 1024 / NW, LPS = IA + IB;
-  static_assert(BK == 16 || BK == 32, "K slice");
+  static_assert(BK == 16 || BK == 32 || BK == 64, "K slice");
   static_assert(KG % 2 == 0, "fragment double buffer alternates within a slice");
   static_assert(NS >= 2 && NS <= MAX_STAGES, "stages");
   static_assert(BM % WM == 0 && BN % WN == 0, "wave grid");
@@ -763,7 +763,7 @@ const Variant kVariants[] = {
     SGEMM_DL_VARIANT(256, 128, 128, 64, 32, 3, 8, 0.97f),
     SGEMM_DL_VARIANT(128, 256, 64, 128, 32, 3, 8, 0.97f),
     SGEMM_DL_VARIANT(128, 128, 64, 64, 32, 3, 8, 0.95f),
-    SGEMM_DL_VARIANT(64, 64, 32, 32, 32, 4, 8, 0.92f),
+    SGEMM_DL_VARIANT(64, 64, 32, 32, 64, 2, 8, 0.92f),
 };
 
 }  // namespace
