@@ -4,14 +4,20 @@ its fast path (a general-kernel fallback, a lost pipeline stage, a spilled
 accumulator) fails here while box-to-box spread (about 20 % in the matrix
 units' sustained clock) does not.
 
-Recorded at 4096^3 (TFLOP/s): FP32 142-149, FP16 1178-1230, BF16 1270-1323,
-FP8 2528-2668.  Floors: about 70 % of the lowest.  The plain (unsplit) FP16
-and BF16 calls at 1024x1024x8192, 16 output tiles of 256^2 for 256 CUs,
-recorded 255-262 with the library's pick (an LDS-direct tile with producer
-waves); the general kernel's small tiles gave 150, so the floor is 190.  The library's own choice
-must be the LDS-direct variant, and the check runs after a warmup on
-device-resident operands, timing 20 launches between two events on the
-launch stream (the bench's method).
+Recorded at 4096^3 (TFLOP/s): FP32 139-150, FP16 1380-1455, BF16 1476-1539,
+FP8 2610-2770 (FP16 and BF16 on the 16 x 16 instruction; the 32 x 32 tiles
+gave 1178-1230 and 1270-1323).  Floors: about 70 % of the lowest rates of
+the 32 x 32 tiles.  The plain (unsplit) FP16 and BF16 calls at
+1024x1024x8192, 16 output tiles of 256^2 for 256 CUs, recorded 255-262 with
+the library's pick (an LDS-direct tile with producer waves); the general
+kernel's small tiles gave 150, so the floor is 190.  FP32 fills the CUs with
+its 64 x 64 LDS-direct tile: 1024x1024x8192 recorded 127-132 (the previous
+picks, the general kernel's 64 x 64 unsplit or 128 x 128 in 4 chunks, gave
+83-86 and 124-131), 1024^3 recorded 99-103 (the previous picks 71-78);
+floors 100 and 80.  The library's own choice must be the LDS-direct
+variant, and the check runs after a warmup on device-resident operands,
+timing 20 launches between two events on the launch stream (the bench's
+method).
 
 Named to run after the parity tests (pytest -x stops at the first
 failure, and a slow box must not hide a parity result).
@@ -91,3 +97,34 @@ def test_unsplit_small_grid_rate(kind):
     tflops = 2.0 * M * N * K / (ms * 1e-3) / 1e12
     log(f"{kind} plain 1024x1024x8192 {cfg.name.decode()}: {ms * 1e3:.1f} us, {tflops:.1f} TFLOP/s (floor 190)")
     assert tflops >= 190.0, (kind, tflops)
+
+
+@pytest.mark.parametrize("shape,floor", [((1024, 1024, 8192), 100.0), ((1024, 1024, 1024), 80.0)],
+                         ids=["1024x1024x8192", "1024^3"])
+def test_f32_small_grid_rate(shape, floor):
+    dt, tin, tout = DT["f32"]
+    M, N_, K = shape
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(13)
+    a = (torch.rand((M, K), device=dev, generator=gen) * 2 - 1).to(tin)
+    b = (torch.rand((K, N_), device=dev, generator=gen) * 2 - 1).to(tin)
+    c = torch.empty((M, N_), device=dev, dtype=tout)
+    cfg = gemm.gemm_select_config(dt, M, N_, K)
+    assert cfg.name.decode().startswith("dl_f32_64x64"), cfg.name
+    stream = torch.cuda.current_stream(dev)
+    fn = gemm.entry(dt)
+    args = (M, N_, K, a.data_ptr(), K, b.data_ptr(), N_, c.data_ptr(), N_, stream.cuda_stream)
+    for _ in range(5):
+        assert fn(*args) == gemm.GEMM_OK, gemm.gemm_last_error()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 20
+    e0.record(stream)
+    for _ in range(reps):
+        fn(*args)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    tflops = 2.0 * M * N_ * K / (ms * 1e-3) / 1e12
+    log(f"f32 plain {M}x{N_}x{K} {cfg.name.decode()}: {ms * 1e3:.1f} us, {tflops:.1f} TFLOP/s (floor {floor})")
+    assert tflops >= floor, (shape, tflops)
