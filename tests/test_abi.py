@@ -210,6 +210,14 @@ def test_heuristic_selection():
     for shape in [(1024, 1024, 8192), (2048, 2048, 2048), (512, 512, 512), (4096, 4096, 4096)]:
         f8 = gemm.gemm_select_config(gemm.DTYPE_F8, *shape).name.decode()
         assert gemm.gemm_select_config(gemm.DTYPE_E5M2, *shape).name.decode() == f8.replace("tr_f8_", "tr_e5m2_")
+    # FP32 grids that leave CUs idle with larger tiles take the 64 x 64
+    # LDS-direct tile (two per CU; the busiest CU's tiles price it); 2048^3
+    # (256 tiles of 128 x 128) and 4096^3 keep the larger tiles.
+    for shape in [(256, 256, 256), (1024, 1024, 1024), (1536, 1536, 1536), (1024, 1024, 8192),
+                  (3000, 3000, 3000)]:
+        assert gemm.gemm_select_config(gemm.DTYPE_F32, *shape).name == b"dl_f32_64x64x64_w32x32_s2", shape
+    assert gemm.gemm_select_config(gemm.DTYPE_F32, 2048, 2048, 2048).bm == 128
+    assert gemm.gemm_select_config(gemm.DTYPE_F32, 4096, 4096, 4096).bm == 256
     for dt in (gemm.DTYPE_F16, gemm.DTYPE_BF16):
         # Short K: the smallest LDS-direct tile (lowest fixed cost) wins.
         assert gemm.gemm_select_config(dt, 1024, 1024, 1024).bm * gemm.gemm_select_config(dt, 1024, 1024, 1024).bn == 128 * 128
