@@ -17,7 +17,9 @@ import os
 import threading
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libgemm.so")
+# GEMM_LIBRARY names another build of the same library (for instance the
+# host-sanitizer build of dense_gemm_row_amd.build.build_host_asan).
+LIB_PATH = os.environ.get("GEMM_LIBRARY") or os.path.join(HERE, "libgemm.so")
 
 GEMM_OK = 0
 GEMM_ERR_INVALID_ARG = -1
