@@ -88,7 +88,7 @@ def asan_runtime() -> str | None:
 def build_host_asan(out: str) -> str:
     """libgemm with the C-ABI's host code (argument checks, the cost model,
     the tuning-table parser: gemm_api.hip) instrumented by AddressSanitizer
-    on the host only (every -fsanitize= behind -Xarch_host; the device code
+    and UndefinedBehaviorSanitizer (fatal) on the host only (every -fsanitize= behind -Xarch_host; the device code
     is the regular build's), linked with the regular objects of the other
     sources into `out`.  Needs the objects of a previous build()."""
     objs = [os.path.join(BUILD_DIR, os.path.splitext(s)[0] + ".o") for s in SOURCES if s != "gemm_api.hip"]
@@ -96,13 +96,15 @@ def build_host_asan(out: str) -> str:
     if missing:
         raise RuntimeError(f"run build() first: missing {missing}")
     api = out + ".gemm_api.o"
-    san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer"]
+    san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+           "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
     cmd = [hipcc(), *HIPCC_FLAGS, "-O1", "-g", *san, "-c", os.path.join(CSRC, "gemm_api.hip"), "-o", api]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed on gemm_api.hip (host ASan):\n{res.stdout}\n{res.stderr}")
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Xarch_host", "-fsanitize=address",
-           "-shared-libasan", api, *objs, "-o", out, "-L/opt/rocm/lib", "-lamdhip64"]
+           "-Xarch_host", "-fsanitize=undefined", "-shared-libasan", api, *objs, "-o", out,
+           "-L/opt/rocm/lib", "-lamdhip64"]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed (host ASan):\n{res.stdout}\n{res.stderr}")

@@ -1,10 +1,11 @@
-"""The C-ABI's host code under AddressSanitizer, on the CPU: the argument
-checks, the cost model, the tuning-table parser, the tile maps and the LDS
-layout replay (everything the ABI tests reach without a GPU) run in a build
-whose host side is instrumented (dense_gemm_row_amd.build.build_host_asan),
-in a child process with the sanitizer's runtime preloaded; any invalid
-memory access ends it with a report.  Skipped where the runtime or a prior
-build's objects are missing."""
+"""The C-ABI's host code under AddressSanitizer and UndefinedBehaviorSanitizer,
+on the CPU: the argument checks, the cost model, the tuning-table parser,
+the tile maps and the LDS layout replay (everything the ABI tests reach
+without a GPU) run in a build whose host side is instrumented
+(dense_gemm_row_amd.build.build_host_asan), in a child process with the
+sanitizer's runtime preloaded; any invalid memory access or undefined
+operation (signed overflow, bad shift, ...) ends it with a report.  Skipped
+where the runtime or a prior build's objects are missing."""
 import os
 import subprocess
 import sys
@@ -28,7 +29,7 @@ def test_abi_tests_pass_under_host_asan(tmp_path):
         raise
     # The host code is instrumented: the library calls the sanitizer's checks.
     syms = subprocess.run(["nm", "-D", "--undefined-only", lib], capture_output=True, text=True).stdout
-    assert "__asan_report_load" in syms
+    assert "__asan_report_load" in syms and "__ubsan_handle_" in syms
     env = dict(os.environ, GEMM_LIBRARY=lib, LD_PRELOAD=rt,
                ASAN_OPTIONS="detect_leaks=0:halt_on_error=1")
     res = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
