@@ -43,6 +43,9 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
+# ORACLE_LIBRARY names another build of oracle.c to load (the tests'
+# sanitizer build); it is used as given, never rebuilt.
+_LIB_OVERRIDE = os.environ.get("ORACLE_LIBRARY")
 # No -ffast-math: the summation order is the definition's, k ascending.
 CFLAGS = ["-O3", "-std=c11", "-fPIC", "-shared", "-pthread",
           "-fno-fast-math", "-ffp-contract=off", "-Wall", "-Wextra"]
@@ -143,6 +146,9 @@ def load(path: str | None = None):
         return _declare(ctypes.CDLL(path))
     with _lock:
         if _lib is None:
+            if _LIB_OVERRIDE:
+                _lib = _declare(ctypes.CDLL(_LIB_OVERRIDE))
+                return _lib
             if (not os.path.exists(_LIB)
                     or os.path.getmtime(_LIB) < os.path.getmtime(_SRC)):
                 build()
