@@ -77,38 +77,56 @@ def build(extra_flags=(), jobs: int | None = None, verbose: bool = False) -> str
     return LIB
 
 
-def asan_runtime() -> str | None:
-    """The compiler's AddressSanitizer runtime (a process that loads a
-    host-sanitized library must preload it), or None."""
+def sanitizer_runtime(name: str = "asan") -> str | None:
+    """The compiler's runtime of a sanitizer ("asan", "tsan"; a process that
+    loads a host-sanitized library must preload it), or None."""
     import glob
-    hits = sorted(glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    hits = sorted(glob.glob(f"/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.{name}-x86_64.so"))
     return hits[-1] if hits else None
 
 
-def build_host_asan(out: str) -> str:
+def asan_runtime() -> str | None:
+    return sanitizer_runtime("asan")
+
+
+def build_host_sanitized(out: str, sanitizers=("address", "undefined")) -> str:
     """libgemm with the C-ABI's host code (argument checks, the cost model,
-    the tuning-table parser: gemm_api.hip) instrumented by AddressSanitizer
-    and UndefinedBehaviorSanitizer (fatal) on the host only (every -fsanitize= behind -Xarch_host; the device code
-    is the regular build's), linked with the regular objects of the other
-    sources into `out`.  Needs the objects of a previous build()."""
+    the tuning-table parser: gemm_api.hip) instrumented by the given
+    sanitizers on the host only (every -fsanitize= behind -Xarch_host; the
+    device code is the regular build's; undefined behaviour is fatal),
+    linked with the regular objects of the other sources into `out`.  Needs
+    the objects of a previous build()."""
     objs = [os.path.join(BUILD_DIR, os.path.splitext(s)[0] + ".o") for s in SOURCES if s != "gemm_api.hip"]
     missing = [o for o in objs if not os.path.exists(o)]
     if missing:
         raise RuntimeError(f"run build() first: missing {missing}")
     api = out + ".gemm_api.o"
-    san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
-           "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
-    cmd = [hipcc(), *HIPCC_FLAGS, "-O1", "-g", *san, "-c", os.path.join(CSRC, "gemm_api.hip"), "-o", api]
+    san = []
+    for name in sanitizers:
+        san += ["-Xarch_host", f"-fsanitize={name}"]
+    if "undefined" in sanitizers:
+        san += ["-Xarch_host", "-fno-sanitize-recover=undefined"]
+    cmd = [hipcc(), *HIPCC_FLAGS, "-O1", "-g", *san, "-Xarch_host", "-fno-omit-frame-pointer",
+           "-c", os.path.join(CSRC, "gemm_api.hip"), "-o", api]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed on gemm_api.hip (host ASan):\n{res.stdout}\n{res.stderr}")
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Xarch_host", "-fsanitize=address",
-           "-Xarch_host", "-fsanitize=undefined", "-shared-libasan", api, *objs, "-o", out,
+        raise RuntimeError(f"hipcc failed on gemm_api.hip (host sanitizers):\n{res.stdout}\n{res.stderr}")
+    link = []
+    for name in sanitizers:
+        link += ["-Xarch_host", f"-fsanitize={name}"]
+    if "address" in sanitizers:
+        link.append("-shared-libasan")
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *link, api, *objs, "-o", out,
            "-L/opt/rocm/lib", "-lamdhip64"]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
-        raise RuntimeError(f"link failed (host ASan):\n{res.stdout}\n{res.stderr}")
+        raise RuntimeError(f"link failed (host sanitizers):\n{res.stdout}\n{res.stderr}")
     return out
+
+
+def build_host_asan(out: str) -> str:
+    """build_host_sanitized with AddressSanitizer and UndefinedBehaviorSanitizer."""
+    return build_host_sanitized(out, ("address", "undefined"))
 
 
 if __name__ == "__main__":
