@@ -270,8 +270,9 @@ int64_t partial_bytes(int64_t S, int64_t M, int64_t N) {
 
 // Shape heuristic: a cost model over the matrix-core variants (a tuning
 // table entry overrides it for its exact shape).  Times in seconds:
-//   GEMM, unsplit with at most one workgroup per CU (WGs <= 256):
-//           fixed + 2*bm*bn*K / (r * R), fixed and r = the workgroup's
+//   a launch of at most one workgroup per CU (WGs <= 256, unsplit or a
+//   split's partials):
+//           fixed + 2*bm*bn*Kc / (r * R), fixed and r = the workgroup's
 //           measured intercept and loop rate alone (kAlone), r lowered
 //           linearly from 64 to 256 busy CUs to its loop rate with all
 //           CUs busy;
@@ -282,9 +283,10 @@ int64_t partial_bytes(int64_t S, int64_t M, int64_t N) {
 //           R = per-CU rate of the best tile with the GPU full (measured
 //           on MI355X at 4096^3), eff = the variant's relative whole-GPU
 //           rate when full;
-//   split:  the partials' rounds, each with the variant's fixed cost,
-//           + (2*S*M*N*4 + M*N*es) bytes / 4 TB/s + a launch, for the
-//           partials written, read back and the result written.
+//   split:  the partials' launch as above (several rounds: each with the
+//           variant's fixed cost) + (2*S*M*N*4 + M*N*es) bytes / 4 TB/s +
+//           a launch, for the partials written, read back and the result
+//           written.
 // Ties go to the earlier table entry.
 struct Choice {
   int id = -1;
@@ -308,18 +310,20 @@ double gemm_seconds(int dtype, const Variant& v, int64_t M, int64_t N, int64_t K
                         ((v.eff > 0.f ? v.eff : 0.1) * rate);
     return twin - (double)rounds * (q.saved_us - (double)cdiv(Kc, d.bk) * q.slice_us) * 1e-6;
   }
-  if (S == 1 && wgs <= 256) {
-    // Unsplit, one workgroup per CU at most: the fixed cost plus the loop
-    // at its rate alone, eff1 with up to 64 CUs busy, linearly down to its
-    // rate with all 256 busy.  That is full_loop_rate for a tile that fills
-    // its CU's LDS (eff was measured with one workgroup per CU); for a
-    // smaller one, which eff measured two to a CU, the dtype's derate of
-    // eff1, at most eff.
+  if (wgs <= 256) {
+    // One workgroup per CU at most (unsplit, or a split's partials): the
+    // fixed cost plus the loop at its rate alone, eff1 with up to 64 CUs
+    // busy, linearly down to its rate with all 256 busy.  That is
+    // full_loop_rate for a tile that fills its CU's LDS (eff was measured
+    // with one workgroup per CU); for a smaller one, which eff measured two
+    // to a CU, eff for a split's partials and, unsplit, the dtype's derate
+    // of eff1, at most eff.
     const Table& t = table();
     const AloneRate& a = t.alone[dtype][d.id];
     const double e1 = a.eff1 > 0.f ? a.eff1 : 0.1;
     const double eff = v.eff > 0.f ? v.eff : 0.1;
-    const double full = per_cu == 1 ? full_loop_rate(dtype, v, a) : std::min(eff, e1 * t.derate[dtype]);
+    const double full = per_cu == 1 ? full_loop_rate(dtype, v, a)
+                                    : S > 1 ? eff : std::min(eff, e1 * t.derate[dtype]);
     const double f = wgs <= 64 ? 0.0 : (double)(wgs - 64) / 192.0;
     const double r = e1 + (full - e1) * f;
     return a.fixed_us * 1e-6 + 2.0 * d.bm * d.bn * (double)(Kc > 0 ? Kc : 1) / (r * rate);
